@@ -1,0 +1,192 @@
+"""Benchmark of the fine-grained FP8 hot path on one MI355X.
+
+Default workload: the dense Fprop GEMM shaped like a DeepSeek-V3 MoE
+down-projection, M=4096 tokens, K=2048, N=7168, BF16 output.  One step is the
+whole path on one batch: online 1x128 quantization of the fp32 activations,
+online 128x128 quantization of the fp32 weights (training re-quantizes its
+master weights every step), and the block-scaled FP8 GEMM.  Four independent
+input sets rotate from step to step so that no step finds its inputs in the
+256 MB last-level cache; all inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  `value` = GEMM FLOPs / step time (TFLOPS, whole step).
+`roofline` describes the GEMM kernel alone, timed with HIP events recorded
+around its launches on the launch stream inside the timed region.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+METRIC = "FP8 block-scaled GEMM TFLOPS + % of MI355X FP8 MFMA peak (dense, MoE grouped)"
+GEMM_SRC = os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_dense_4096x7168x2048_traffic.md")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--sets", type=int, default=4, help="rotating input sets")
+    p.add_argument("--cpu-rows", type=int, default=512, help="rows of the oracle's timed sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def source_hash():
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(flops_unit_bytes):
+    """HBM bytes per GEMM launch from the committed counter summary, if it was
+    taken on the current kernel source; otherwise None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_src = re.search(r"kernel source sha256/16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"HBM bytes per launch \(calibrated\):\s*([0-9.eE+]+)", text)
+    if not (m_src and m_b) or m_src.group(1) != source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(x, w, rows):
+    """The oracle, untouched, on the first `rows` rows of one input set: 1x128
+    quantization of those rows, 128x128 quantization of the whole weight
+    (every output row needs all of it), exact dequantization and the float64
+    GEMM plus |A||B| bound term.  Rate reported in the GEMM's FLOP units."""
+    from oracle import gemm, quant, e4m3
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    t0 = time.perf_counter()
+    qa, sa = quant.quant_act_1x128(x[:rows])
+    qb, sb = quant.quant_weight_128x128(w)
+    c, s = gemm.gemm_blockscaled_ref(qa, sa, qb, sb)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.shape[0] * w.shape[1]
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS", "cores": max(blas, e4m3._threads()),
+            "kind": "oracle",
+            "sample": f"{rows} of 4096 activation rows (1x128 quantization), the full 7168x2048 weight "
+                      f"(128x128 quantization), float64 GEMM and |A||B| on those rows; {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    import fp8_fine_grained_amd as fp8
+    import workloads
+
+    fp8.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M, N, K = 4096, 7168, 2048
+    sets = []
+    host0 = None
+    for i in range(args.sets):
+        x, w = workloads.dense_fprop(seed_offset=i)
+        if i == 0:
+            host0 = (x, w)
+        xs = torch.from_numpy(x).to(dev)
+        ws = torch.from_numpy(w).to(dev)
+        sets.append(dict(
+            x=xs, w=ws,
+            qa=torch.empty((M, K), dtype=torch.uint8, device=dev),
+            sa=torch.empty((K // 128, M), dtype=torch.float32, device=dev),
+            qb=torch.empty((N, K), dtype=torch.uint8, device=dev),
+            sb=torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev),
+            c=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        fp8.fp8_quant_act_1x128(s["x"], q=s["qa"], s=s["sa"])
+        if ev is not None:
+            ev[1].record(stream)
+        fp8.fp8_quant_weight_128x128(s["w"], q=s["qb"], s=s["sb"])
+        if ev is not None:
+            ev[2].record(stream)
+        fp8.fp8_gemm_blockscaled(s["qa"], s["sa"], s["qb"], s["sb"], fp8.BSCALE_128x128, torch.bfloat16, out=s["c"])
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    t_act = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    t_w = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    t_gemm = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+
+    flops = 2.0 * M * N * K
+    value = flops / (ms_step * 1e-3) / 1e12
+    gemm_tflops = flops / (t_gemm * 1e-3) / 1e12
+    act_bytes = M * K * 5 + (K // 128) * M * 4
+    w_bytes = N * K * 5 + (N // 128) * (K // 128) * 4
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded: activations N(0,1) with 0.1% outlier channels x100, weights N(0,0.02))",
+        "config": {"workload": "dense_fprop: M=4096 N=7168 K=2048, 1x128 activation / 128x128 weight scales, "
+                               "BF16 out; step = quant_act_1x128 + quant_weight_128x128 + gemm_blockscaled",
+                   "M": M, "N": N, "K": K, "rotating_input_sets": args.sets},
+        "pct_of_fp8_peak_step": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "kernels_us": {"quant_act_1x128": round(t_act * 1e3, 2), "quant_weight_128x128": round(t_w * 1e3, 2),
+                       "gemm_blockscaled": round(t_gemm * 1e3, 2)},
+        "quant_gbs": {"act": round(act_bytes / (t_act * 1e-3) / 1e9, 1),
+                      "weight": round(w_bytes / (t_w * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": stored_traffic(flops),
+                     "kernel": "gemm_bs_kernel (dense, 128x128 B scales, BF16 out)",
+                     "kernel_source": source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(host0[0], host0[1], args.cpu_rows)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+"""Python binding of libfp8fg.so: fine-grained FP8 quantization and block-scaled
+FP8 GEMM for AMD MI355X (gfx950).
+
+The functions below carry the names of the C entry points declared in
+include/fp8fg.h and only marshal arguments: they take torch tensors that live
+on the GPU, check dtypes and shapes, pass raw device pointers and the current
+HIP stream to the library, and raise Fp8fgError on a non-zero status.  Every
+step of the computation runs in the library's HIP kernels; there is no other
+implementation behind these names.  Outputs are allocated here with torch
+unless the caller passes them in (``out=``/``q=``/``s=``).
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8fg.so")
+
+BSCALE_128x128 = 0
+BSCALE_1x128 = 1
+OUT_BF16 = 0
+OUT_FP32 = 1
+
+EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
+           "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
+           "fp8fg_status_string", "fp8fg_abi_version")
+
+
+class Fp8fgError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load (once) and return the ctypes handle of libfp8fg.so; raise if missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                          "or `python fp8_fine_grained_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.fp8_quant_act_1x128.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    lib.fp8_quant_weight_128x128.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    lib.fp8_gemm_blockscaled.argtypes = [vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp]
+    lib.fp8_grouped_gemm_contiguous.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
+    lib.fp8_grouped_gemm_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
+    for name in EXPORTS[:5]:
+        getattr(lib, name).restype = ctypes.c_int
+    lib.fp8fg_status_string.argtypes = [ctypes.c_int]
+    lib.fp8fg_status_string.restype = ctypes.c_char_p
+    lib.fp8fg_abi_version.argtypes = []
+    lib.fp8fg_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().fp8fg_status_string(int(status)).decode()
+
+
+def abi_version():
+    return load_library().fp8fg_abi_version()
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Fp8fgError(fn, status)
+
+
+def _need(t, dtype, shape, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def fp8_quant_act_1x128(x, transpose_out=False, q=None, s=None):
+    """1x128 activation quantization of x f32 [M][K].
+    transpose_out=False -> (q u8 [M][K], s f32 [K/128][M]);
+    transpose_out=True  -> (q u8 [K][M], s f32 [M/128][K]) (tiles along M)."""
+    M, K = x.shape
+    _need(x, torch.float32, (M, K), "x")
+    qs = (K, M) if transpose_out else (M, K)
+    ss = (M // 128, K) if transpose_out else (K // 128, M)
+    q = _empty(qs, torch.uint8, x) if q is None else q
+    s = _empty(ss, torch.float32, x) if s is None else s
+    _need(q, torch.uint8, qs, "q")
+    _need(s, torch.float32, ss, "s")
+    _check("fp8_quant_act_1x128", load_library().fp8_quant_act_1x128(
+        _ptr(x), M, K, int(bool(transpose_out)), _ptr(q), _ptr(s), _stream(x)))
+    return q, s
+
+
+def fp8_quant_weight_128x128(w, transpose_out=False, q=None, s=None):
+    """128x128 weight quantization of w f32 [N][K] -> (q u8 [N][K], s f32 [N/128][K/128]),
+    or the transposed codes and scales when transpose_out=True."""
+    N, K = w.shape
+    _need(w, torch.float32, (N, K), "w")
+    qs = (K, N) if transpose_out else (N, K)
+    ss = (K // 128, N // 128) if transpose_out else (N // 128, K // 128)
+    q = _empty(qs, torch.uint8, w) if q is None else q
+    s = _empty(ss, torch.float32, w) if s is None else s
+    _need(q, torch.uint8, qs, "q")
+    _need(s, torch.float32, ss, "s")
+    _check("fp8_quant_weight_128x128", load_library().fp8_quant_weight_128x128(
+        _ptr(w), N, K, int(bool(transpose_out)), _ptr(q), _ptr(s), _stream(w)))
+    return q, s
+
+
+def _out_dtype(out_dtype):
+    return {torch.bfloat16: OUT_BF16, torch.float32: OUT_FP32}[out_dtype]
+
+
+def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind=BSCALE_128x128, out_dtype=torch.bfloat16, out=None):
+    """C[M][N] = A[M][K] . B[N][K]^T with 1x128 A scales and 128x128 (or 1x128) B scales."""
+    M, K = a.shape
+    N = b.shape[0]
+    _need(a, torch.uint8, (M, K), "a")
+    _need(sa, torch.float32, (K // 128, M), "sa")
+    _need(b, torch.uint8, (N, K), "b")
+    _need(sb, torch.float32, (N // 128, K // 128) if bscale_kind == BSCALE_128x128 else (K // 128, N), "sb")
+    out = _empty((M, N), out_dtype, a) if out is None else out
+    _need(out, out_dtype, (M, N), "out")
+    _check("fp8_gemm_blockscaled", load_library().fp8_gemm_blockscaled(
+        _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), int(bscale_kind), _ptr(out), _out_dtype(out_dtype),
+        M, N, K, _stream(a)))
+    return out
+
+
+def fp8_grouped_gemm_contiguous(a, sa, b, sb, group_offsets, out_dtype=torch.bfloat16, out=None):
+    """Contiguous MoE layout: expert g owns rows [off[g], off[g+1]) of a; off is device int32 [G+1]."""
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    _need(a, torch.uint8, (M_total, K), "a")
+    _need(sa, torch.float32, (K // 128, M_total), "sa")
+    _need(b, torch.uint8, (G, N, K), "b")
+    _need(sb, torch.float32, (G, N // 128, K // 128), "sb")
+    _need(group_offsets, torch.int32, (G + 1,), "group_offsets")
+    out = _empty((M_total, N), out_dtype, a) if out is None else out
+    _need(out, out_dtype, (M_total, N), "out")
+    _check("fp8_grouped_gemm_contiguous", load_library().fp8_grouped_gemm_contiguous(
+        _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(group_offsets), G, M_total, N, K, _ptr(out),
+        _out_dtype(out_dtype), _stream(a)))
+    return out
+
+
+def fp8_grouped_gemm_masked(a, sa, b, sb, masked_m, out_dtype=torch.bfloat16, out=None):
+    """Masked MoE layout: a u8 [G][M_max][K]; rows >= masked_m[g] of out are not written."""
+    G, M_max, K = a.shape
+    N = b.shape[1]
+    _need(a, torch.uint8, (G, M_max, K), "a")
+    _need(sa, torch.float32, (G, K // 128, M_max), "sa")
+    _need(b, torch.uint8, (G, N, K), "b")
+    _need(sb, torch.float32, (G, N // 128, K // 128), "sb")
+    _need(masked_m, torch.int32, (G,), "masked_m")
+    out = _empty((G, M_max, N), out_dtype, a) if out is None else out
+    _need(out, out_dtype, (G, M_max, N), "out")
+    _check("fp8_grouped_gemm_masked", load_library().fp8_grouped_gemm_masked(
+        _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(masked_m), G, M_max, N, K, _ptr(out),
+        _out_dtype(out_dtype), _stream(a)))
+    return out

@@ -1,0 +1,120 @@
+// C entry points of libfp8fg.so (declared in include/fp8fg.h).
+//
+// Every argument is checked on the host before anything is enqueued, in this
+// order: NULL pointers, sizes and multiple-of-128 rules, 16-byte alignment,
+// enum values.  A zero-sized problem returns FP8FG_OK without touching the
+// HIP runtime, so these checks can be exercised on a machine without a GPU.
+#include "fp8fg.h"
+#include "launch.hpp"
+
+#include <stdint.h>
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? FP8FG_OK : FP8FG_ERR_HIP; }
+
+inline bool valid_out(int out_dtype) { return out_dtype == FP8FG_OUT_BF16 || out_dtype == FP8FG_OUT_FP32; }
+
+}  // namespace
+
+extern "C" {
+
+int fp8fg_abi_version(void) { return FP8FG_ABI_VERSION; }
+
+const char* fp8fg_status_string(int status) {
+    switch (status) {
+        case FP8FG_OK: return "ok";
+        case FP8FG_ERR_NULL: return "null pointer argument";
+        case FP8FG_ERR_SHAPE: return "invalid shape (negative size or not a multiple of 128)";
+        case FP8FG_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case FP8FG_ERR_UNSUPPORTED: return "unsupported argument value or size";
+        case FP8FG_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+int fp8_quant_act_1x128(const float* x, int64_t M, int64_t K, int transpose_out, uint8_t* q, float* s,
+                        void* stream) {
+    if (!x || !q || !s) return FP8FG_ERR_NULL;
+    if (M < 0 || K < 0) return FP8FG_ERR_SHAPE;
+    if (transpose_out != 0 && transpose_out != 1) return FP8FG_ERR_UNSUPPORTED;
+    if (transpose_out == 0 && K % 128 != 0) return FP8FG_ERR_SHAPE;
+    if (transpose_out == 1 && M % 128 != 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return FP8FG_ERR_ALIGN;
+    if (M > kMaxDim || K > kMaxDim || (M > 0 && K > kMaxElems / M)) return FP8FG_ERR_UNSUPPORTED;
+    if (transpose_out == 1 && ((K + 63) / 64 > 65535)) return FP8FG_ERR_UNSUPPORTED;
+    if (M == 0 || K == 0) return FP8FG_OK;
+    return hip_status(fp8fg::launch_quant_act(x, M, K, transpose_out, q, s, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_quant_weight_128x128(const float* w, int64_t N, int64_t K, int transpose_out, uint8_t* q, float* s,
+                             void* stream) {
+    if (!w || !q || !s) return FP8FG_ERR_NULL;
+    if (N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8FG_ERR_SHAPE;
+    if (transpose_out != 0 && transpose_out != 1) return FP8FG_ERR_UNSUPPORTED;
+    if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return FP8FG_ERR_ALIGN;
+    if (N > kMaxDim || K > kMaxDim || (N > 0 && K > kMaxElems / N)) return FP8FG_ERR_UNSUPPORTED;
+    if (N / 128 > 65535) return FP8FG_ERR_UNSUPPORTED;
+    if (N == 0 || K == 0) return FP8FG_OK;
+    return hip_status(fp8fg::launch_quant_weight(w, N, K, transpose_out, q, s, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int bscale_kind,
+                         void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!a || !sa || !b || !sb || !c) return FP8FG_ERR_NULL;
+    if (M < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8FG_ERR_SHAPE;
+    if (K == 0 && M > 0 && N > 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(c)) return FP8FG_ERR_ALIGN;
+    if (bscale_kind != FP8FG_BSCALE_128x128 && bscale_kind != FP8FG_BSCALE_1x128) return FP8FG_ERR_UNSUPPORTED;
+    if (!valid_out(out_dtype)) return FP8FG_ERR_UNSUPPORTED;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if (((M + 127) / 128) * (N / 128) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return FP8FG_OK;
+    fp8fg::GemmArgs args{a, sa, b, sb, c, nullptr, M, N, K, 1};
+    return hip_status(fp8fg::launch_gemm(fp8fg::GemmMode::Dense, bscale_kind == FP8FG_BSCALE_1x128,
+                                         out_dtype == FP8FG_OUT_FP32, args, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                const int32_t* group_offsets, int64_t G, int64_t M_total, int64_t N, int64_t K,
+                                void* c, int out_dtype, void* stream) {
+    if (!a || !sa || !b || !sb || !group_offsets || !c) return FP8FG_ERR_NULL;
+    if (G < 0 || M_total < 0 || N < 0 || K < 0 || M_total % 128 != 0 || N % 128 != 0 || K % 128 != 0)
+        return FP8FG_ERR_SHAPE;
+    if (K == 0 && M_total > 0 && N > 0 && G > 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(c) ||
+        !aligned16(group_offsets))
+        return FP8FG_ERR_ALIGN;
+    if (!valid_out(out_dtype)) return FP8FG_ERR_UNSUPPORTED;
+    if (M_total > kMaxDim || N > kMaxDim || K > kMaxDim || G > kMaxDim - 1) return FP8FG_ERR_UNSUPPORTED;
+    if ((M_total / 128) * (N / 128) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if (G == 0 || M_total == 0 || N == 0) return FP8FG_OK;
+    fp8fg::GemmArgs args{a, sa, b, sb, c, group_offsets, M_total, N, K, G};
+    return hip_status(fp8fg::launch_gemm(fp8fg::GemmMode::Contig, 0, out_dtype == FP8FG_OUT_FP32, args,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int fp8_grouped_gemm_masked(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                            const int32_t* masked_m, int64_t G, int64_t M_max, int64_t N, int64_t K, void* c,
+                            int out_dtype, void* stream) {
+    if (!a || !sa || !b || !sb || !masked_m || !c) return FP8FG_ERR_NULL;
+    if (G < 0 || M_max < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8FG_ERR_SHAPE;
+    if (K == 0 && M_max > 0 && N > 0 && G > 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(c) || !aligned16(masked_m))
+        return FP8FG_ERR_ALIGN;
+    if (!valid_out(out_dtype)) return FP8FG_ERR_UNSUPPORTED;
+    if (M_max > kMaxDim || N > kMaxDim || K > kMaxDim || G > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    const int64_t tiles_per_group = ((M_max + 127) / 128) * (N / 128);
+    if (tiles_per_group > 0 && G > kMaxDim / tiles_per_group) return FP8FG_ERR_UNSUPPORTED;
+    if (G == 0 || M_max == 0 || N == 0) return FP8FG_OK;
+    fp8fg::GemmArgs args{a, sa, b, sb, c, masked_m, M_max, N, K, G};
+    return hip_status(fp8fg::launch_gemm(fp8fg::GemmMode::Masked, 0, out_dtype == FP8FG_OUT_FP32, args,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Internal launchers (host side).  Arguments are validated by the C entry
+// points before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8fg {
+
+hipError_t launch_quant_act(const float* x, int64_t M, int64_t K, int transpose_out, uint8_t* q,
+                            float* s, hipStream_t stream);
+hipError_t launch_quant_weight(const float* w, int64_t N, int64_t K, int transpose_out, uint8_t* q,
+                               float* s, hipStream_t stream);
+
+enum class GemmMode : int { Dense = 0, Contig = 1, Masked = 2 };
+
+struct GemmArgs {
+    const uint8_t* a;       // A codes (group 0)
+    const float* sa;        // A scales, kb-major
+    const uint8_t* b;       // B codes (group 0)
+    const float* sb;        // B scales
+    void* c;                // output (group 0)
+    const int32_t* aux;     // group_offsets (contiguous) or masked_m (masked)
+    int64_t M;              // rows: dense M, contiguous M_total, masked M_max (per group)
+    int64_t N, K;
+    int64_t G;              // groups (1 for dense)
+};
+
+hipError_t launch_gemm(GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
+                       hipStream_t stream);
+
+}  // namespace fp8fg

@@ -1,0 +1,201 @@
+// Online fine-grained FP8 quantizers for gfx950.
+//
+// Method: "The Insider Secrets Of Deepseek Discovered", passage on Figure 7(a)
+// (1x128 activation tiles, 128x128 weight blocks, scale from each group's
+// max-abs); DeepSeek-V3 FP8 knowledge-base page (codingmall.com), section on
+// online quantization (scales computed from the current data).  Per group:
+//   amax = max|x|,  s = RN32(amax / 448),  code = E4M3_RNE_SAT(RN32(x / s)).
+// Both divisions are IEEE fp32 divisions (the compiler's correctly rounded
+// sequence), so every byte and scale is reproducible bit for bit.
+//
+// All three kernels are HBM-bound: 4 bytes read and 1 byte written per
+// element, plus 4 bytes of scale per group.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp8fg {
+
+// ---------------------------------------------------------------------------
+// 1x128 tiles along K.  Row-major x [M][K] with K % 128 == 0 is a flat
+// sequence of tiles: tile t = m * (K/128) + kb starts at element t * 128, and
+// so do its codes.  A half-wave (32 lanes x float4) owns one tile at a time;
+// each half-wave takes U consecutive tiles per pass so that U independent
+// 16-byte loads per lane are in flight before the first reduction.
+// Scales go to s[kb][m].
+template <int U>
+__global__ __launch_bounds__(256) void quant_act_rows_kernel(const float* __restrict__ x, int64_t M,
+                                                             int64_t kbs, uint8_t* __restrict__ q,
+                                                             float* __restrict__ s) {
+    const int64_t ntiles = M * kbs;
+    const int lane = threadIdx.x & 31;
+    const int64_t hw = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 5;
+    const int64_t nhw = (int64_t(gridDim.x) * blockDim.x) >> 5;
+    for (int64_t base = hw * U; base < ntiles; base += nhw * U) {
+        v4f v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = base + u;
+            v[u] = t < ntiles ? ld<v4f>(x + t * kBlock + lane * 4) : v4f{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = base + u;
+            const float amax = halfwave_max(abs_max4(v[u]));
+            const float sc = amax / 448.0f;
+            const uint32_t codes = encode4(v[u], sc);
+            if (t < ntiles) {
+                *reinterpret_cast<uint32_t*>(q + t * kBlock + lane * 4) = codes;
+                if (lane == 0) {
+                    const int64_t m = t / kbs, kb = t - m * kbs;
+                    s[kb * M + m] = sc;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 tiles along M (tokens), codes written transposed: q [K][M],
+// s [M/128][K].  A workgroup owns 128 tokens x 64 channels: it stages the
+// fp32 block in LDS (row pitch 65 floats so that column walks do not collide
+// on banks), each wave reduces one quarter of the tokens per channel, the
+// four partial maxima meet in LDS, and every lane then writes 32 consecutive
+// token codes of its channel (two 16-byte stores).
+constexpr int kTokCh = 64;
+
+__global__ __launch_bounds__(256) void quant_act_tokens_kernel(const float* __restrict__ x, int64_t M,
+                                                               int64_t K, uint8_t* __restrict__ q,
+                                                               float* __restrict__ s) {
+    __shared__ float tile[kBlock][kTokCh + 1];
+    __shared__ float part[4][kTokCh];
+    const int t = threadIdx.x;
+    const int64_t mb = blockIdx.x;
+    const int64_t k0 = int64_t(blockIdx.y) * kTokCh;
+    const float* xb = x + mb * kBlock * K + k0;
+    const bool vec = ((K & 3) == 0);
+    const int c4 = (t & 15) * 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = (t >> 4) + 16 * i;
+        const float* p = xb + int64_t(r) * K + c4;
+        float e[4];
+        if (vec && k0 + c4 + 4 <= K) {
+            const v4f v = ld<v4f>(p);
+            e[0] = v[0]; e[1] = v[1]; e[2] = v[2]; e[3] = v[3];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) e[j] = (k0 + c4 + j < K) ? p[j] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tile[r][c4 + j] = e[j];
+    }
+    __syncthreads();
+
+    const int c = t & 63;           // channel within the block
+    const int quarter = t >> 6;     // tokens quarter*32 .. +32
+    float v[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        v[i] = tile[quarter * 32 + i][c];
+        amax = fmaxf(amax, fabsf(v[i]));
+    }
+    part[quarter][c] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(part[0][c], part[1][c]), fmaxf(part[2][c], part[3][c]));
+    const float sc = amax / 448.0f;
+    const int64_t k = k0 + c;
+    if (k < K) {
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            w[i] = encode4(v4f{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]}, sc);
+        uint8_t* dst = q + k * M + mb * kBlock + quarter * 32;
+        st<u32x4>(dst, u32x4{w[0], w[1], w[2], w[3]});
+        st<u32x4>(dst + 16, u32x4{w[4], w[5], w[6], w[7]});
+        if (quarter == 0) s[mb * K + k] = sc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 weight blocks: one workgroup per block.  Each thread holds 16
+// float4 (rows t/32 + 8i, columns 4*(t%32)..+3), the block max-abs is
+// reduced across the wave and then across the four waves in LDS.  The
+// transposed variant stages the codes in LDS as [column][row] and writes
+// 16-byte pieces of the rows of q^T.
+__global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restrict__ w, int64_t N,
+                                                           int64_t K, int transpose_out,
+                                                           uint8_t* __restrict__ q,
+                                                           float* __restrict__ s) {
+    __shared__ float red[4];
+    __shared__ __align__(16) uint8_t qt[kBlock][kBlock + 16];
+    const int t = threadIdx.x;
+    const int64_t nb = blockIdx.y, kb = blockIdx.x;
+    const int c4 = (t & 31) * 4;
+    const int r0 = t >> 5;
+    const float* wb = w + nb * kBlock * K + kb * kBlock + c4;
+    v4f v[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        v[i] = ld<v4f>(wb + int64_t(r0 + 8 * i) * K);
+        amax = fmaxf(amax, abs_max4(v[i]));
+    }
+    amax = wave_max(amax);
+    if ((t & 63) == 0) red[t >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float sc = amax / 448.0f;
+    if (!transpose_out) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t row = nb * kBlock + r0 + 8 * i;
+            *reinterpret_cast<uint32_t*>(q + row * K + kb * kBlock + c4) = encode4(v[i], sc);
+        }
+        if (t == 0) s[nb * (K / kBlock) + kb] = sc;
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t cw = encode4(v[i], sc);
+        const int r = r0 + 8 * i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qt[c4 + j][r] = uint8_t(cw >> (8 * j));
+    }
+    __syncthreads();
+    // row kr of the transposed block: 128 bytes, written by 8 threads x 16 B
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int piece = t + 256 * i;          // 1024 pieces of 16 B
+        const int kr = piece >> 3, off = (piece & 7) * 16;
+        st<u32x4>(q + (kb * kBlock + kr) * N + nb * kBlock + off, ld<u32x4>(&qt[kr][off]));
+    }
+    if (t == 0) s[kb * (N / kBlock) + nb] = sc;
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_quant_act(const float* x, int64_t M, int64_t K, int transpose_out, uint8_t* q,
+                            float* s, hipStream_t stream) {
+    if (!transpose_out) {
+        constexpr int U = 4;
+        const int64_t ntiles = M * (K / kBlock);
+        const int64_t per_block = 8 * U;               // 8 half-waves per 256-thread block
+        int64_t blocks = (ntiles + per_block - 1) / per_block;
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(quant_act_rows_kernel<U>, dim3(unsigned(blocks)), dim3(256), 0, stream, x, M,
+                           K / kBlock, q, s);
+    } else {
+        const dim3 grid(unsigned(M / kBlock), unsigned((K + kTokCh - 1) / kTokCh));
+        hipLaunchKernelGGL(quant_act_tokens_kernel, grid, dim3(256), 0, stream, x, M, K, q, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weight(const float* w, int64_t N, int64_t K, int transpose_out, uint8_t* q,
+                               float* s, hipStream_t stream) {
+    const dim3 grid(unsigned(K / kBlock), unsigned(N / kBlock));
+    hipLaunchKernelGGL(quant_weight_kernel, grid, dim3(256), 0, stream, w, N, K, transpose_out, q, s);
+    return hipGetLastError();
+}
+
+}  // namespace fp8fg

@@ -1,0 +1,153 @@
+/*
+ * fp8fg.h -- fine-grained FP8 quantization and block-scaled FP8 GEMM on AMD
+ * Instinct MI355X (gfx950).  C ABI of libfp8fg.so.
+ *
+ * The method (DeepSeek-V3's FP8 recipe, as retold by the pages this library
+ * follows):
+ *   - "The Insider Secrets Of Deepseek Discovered", passage on Figure 7(a):
+ *     activations are scaled per 1x128 tile (one token, 128 channels) and
+ *     weights per 128x128 block; passage on Figure 7(b): partial GEMM sums are
+ *     promoted to FP32 at a fixed K interval and the scales are applied there;
+ *     passage on Figure 6: Fprop, Dgrad and Wgrad of a Linear all run in FP8.
+ *   - DeepSeek-V3 FP8 knowledge-base page (codingmall.com), sections on
+ *     fine-grained quantization, online quantization (scales from the current
+ *     tile's max-abs), increased accumulation precision and unified E4M3.
+ *   - DeepGEMM launch article (itstec.com.br), "Principais caracteristicas":
+ *     dense GEMMs plus two MoE grouped layouts, contiguous and masked.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a DEVICE pointer owned by the caller, 16-byte aligned.
+ *     The library allocates, frees and synchronizes nothing; it keeps no state
+ *     between calls and is reentrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously on it; the call returns before it runs.
+ *   - Codes are OCP E4M3 bytes ("E4M3FN": bias 7, max 448, NaN = 0x7F/0xFF,
+ *     no infinities).  Scales are FP32 DEQUANTIZATION multipliers:
+ *     value ~= decode(code) * scale, with scale = RN32(amax / 448) and the
+ *     code = E4M3 round-to-nearest-even-saturating of RN32(x / scale), IEEE
+ *     division throughout.  A group whose amax is 0 gets scale 0 and signed
+ *     zero codes.  Inputs must be finite (NaN/Inf: unspecified output).
+ *   - Return value: FP8FG_OK, or a negative fp8fg_status.  Argument errors are
+ *     detected on the host BEFORE anything is enqueued (no partial work);
+ *     FP8FG_ERR_HIP means the kernel launch itself failed.  A zero-sized
+ *     problem (M == 0, G == 0, ...) is a successful no-op.
+ *   - Scale layouts.  A 1x128-scaled operand of logical shape [R][K] (K = the
+ *     axis the 128-element groups run along) stores codes u8 [R][K] row-major
+ *     and scales f32 [K/128][R] ("kb-major").  A 128x128-scaled [N][K] operand
+ *     stores codes u8 [N][K] and scales f32 [N/128][K/128].
+ *   - GEMM: C[M][N] = A[M][K] . B[N][K]^T, both operands K-major (a Linear
+ *     layer y = x . W^T with W [out][in]).  Each 128-wide K-block is summed
+ *     by FP8 MFMA into a fresh FP32 partial, then folded into an FP32
+ *     accumulator as acc += partial * (sA * sB).  Output row-major [M][N],
+ *     BF16 (round-to-nearest-even) or FP32.  Results are deterministic
+ *     (no atomics, no split-K).
+ */
+#ifndef FP8FG_H
+#define FP8FG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8FG_ABI_VERSION 1
+
+enum fp8fg_status {
+    FP8FG_OK = 0,
+    FP8FG_ERR_NULL = -1,         /* a required pointer is NULL                 */
+    FP8FG_ERR_SHAPE = -2,        /* negative size or a multiple-of-128 rule    */
+    FP8FG_ERR_ALIGN = -3,        /* a pointer is not 16-byte aligned           */
+    FP8FG_ERR_UNSUPPORTED = -4,  /* unknown enum value or size beyond limits   */
+    FP8FG_ERR_HIP = -5           /* the HIP runtime refused the launch         */
+};
+
+enum fp8fg_out { FP8FG_OUT_BF16 = 0, FP8FG_OUT_FP32 = 1 };
+
+enum fp8fg_bscale {
+    FP8FG_BSCALE_128x128 = 0,    /* sb f32 [N/128][K/128]   (weights: Fprop, Dgrad) */
+    FP8FG_BSCALE_1x128 = 1       /* sb f32 [K/128][N]       (token-wise operand: Wgrad) */
+};
+
+/*
+ * Online 1x128 activation quantization.
+ * x: f32 [M][K] row-major (M tokens, K channels).
+ * transpose_out = 0: tiles run along K (one token x 128 channels).
+ *     q: u8 [M][K], s: f32 [K/128][M].          Requires K % 128 == 0.
+ * transpose_out = 1: tiles run along M (128 tokens x one channel), the
+ *     operand layout of the Wgrad GEMM, whose contraction runs over tokens.
+ *     q: u8 [K][M] (transposed), s: f32 [M/128][K].  Requires M % 128 == 0.
+ * Sizes: M, K >= 0 and M * K < 2^40.
+ */
+int fp8_quant_act_1x128(const float* x, int64_t M, int64_t K, int transpose_out,
+                        uint8_t* q, float* s, void* stream);
+
+/*
+ * Online 128x128 weight quantization.
+ * w: f32 [N][K] row-major (N output channels, K input channels).
+ * transpose_out = 0: q u8 [N][K], s f32 [N/128][K/128].
+ * transpose_out = 1: q u8 [K][N] = the codes of w, transposed, with
+ *     s f32 [K/128][N/128]: the B operand of the Dgrad GEMM.  Square blocks
+ *     make this identical to quantizing w^T.
+ * Requires N % 128 == 0 and K % 128 == 0; N * K < 2^40.
+ */
+int fp8_quant_weight_128x128(const float* w, int64_t N, int64_t K, int transpose_out,
+                             uint8_t* q, float* s, void* stream);
+
+/*
+ * Dense block-scaled FP8 GEMM: C[M][N] = A[M][K] . B[N][K]^T.
+ * a: u8 [M][K] with sa f32 [K/128][M] (1x128 along K).
+ * b: u8 [N][K] with sb laid out per bscale_kind (fp8fg_bscale).
+ * c: [M][N], BF16 (uint16 bit patterns) or FP32 per out_dtype (fp8fg_out).
+ * Requires M >= 0 (any value, ragged tails allowed), N % 128 == 0,
+ * K % 128 == 0, K > 0 when M*N > 0; M, N, K < 2^31.
+ */
+int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                         int bscale_kind, void* c, int out_dtype,
+                         int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * MoE grouped GEMM, contiguous layout (training / prefill).
+ * The rows of all G local experts are concatenated: expert g owns rows
+ * [group_offsets[g], group_offsets[g+1]) of a / c.
+ * group_offsets: DEVICE int32 [G+1], non-decreasing, group_offsets[0] = 0,
+ *     group_offsets[G] = M_total, every entry a multiple of 128 (each expert's
+ *     rows padded to whole 128-row tiles).  Read only on the device, so the
+ *     host never waits for routing results.  A 128-row tile of a that lies
+ *     outside [0, group_offsets[G]) is not computed and its rows of c are not
+ *     written.  Padding rows are computed like any other row.
+ * a: u8 [M_total][K], sa f32 [K/128][M_total];
+ * b: u8 [G][N][K], sb f32 [G][N/128][K/128] (128x128 blocks per expert);
+ * c: [M_total][N] BF16 or FP32.
+ * Requires M_total % 128 == 0, N % 128 == 0, K % 128 == 0, K > 0, G >= 0.
+ */
+int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                const int32_t* group_offsets, int64_t G, int64_t M_total,
+                                int64_t N, int64_t K, void* c, int out_dtype, void* stream);
+
+/*
+ * MoE grouped GEMM, masked layout (decode).
+ * Expert g has a padded buffer of M_max rows of which the first masked_m[g]
+ * are valid.
+ * masked_m: DEVICE int32 [G]; each value is clamped to [0, M_max] on the
+ *     device.  Rows at or beyond masked_m[g] of c are NOT written.
+ * a: u8 [G][M_max][K], sa f32 [G][K/128][M_max];
+ * b: u8 [G][N][K], sb f32 [G][N/128][K/128];
+ * c: [G][M_max][N] BF16 or FP32.
+ * Requires M_max >= 0, N % 128 == 0, K % 128 == 0, K > 0, G >= 0.
+ */
+int fp8_grouped_gemm_masked(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                            const int32_t* masked_m, int64_t G, int64_t M_max,
+                            int64_t N, int64_t K, void* c, int out_dtype, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fp8fg_status_string(int status);
+
+/* FP8FG_ABI_VERSION of the loaded library. */
+int fp8fg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8FG_H */

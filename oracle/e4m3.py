@@ -13,6 +13,9 @@ finite non-negative magnitudes, ties going to the code whose mantissa LSB is
 -0 and small negatives that round to zero give 0x80).
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 MAX_FINITE = 448.0
@@ -40,14 +43,41 @@ MAGNITUDES = decode(np.arange(CODE_MAX + 1, dtype=np.uint8))
 MIDPOINTS = (MAGNITUDES[:-1] + MAGNITUDES[1:]) / 2.0
 
 
+_CHUNK = 1 << 20
+
+
+def _threads():
+    n = os.environ.get("OMP_NUM_THREADS")
+    try:
+        n = int(n) if n else len(os.sched_getaffinity(0))
+    except (ValueError, AttributeError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 32))
+
+
 def encode(y):
     """Round float32 values to E4M3 codes: nearest, ties to even, saturate at 448.
 
     ``y`` is taken as float32 (the method scales in float32 before casting).
     Non-finite input is outside the contract: NaN and +-inf both come out as
-    the saturated code.
+    the saturated code.  Large arrays are split into independent chunks that
+    are encoded on a thread pool (each element is computed the same way).
     """
-    y32 = np.asarray(y, dtype=np.float32)
+    y32 = np.ascontiguousarray(y, dtype=np.float32)
+    if y32.size <= 2 * _CHUNK:
+        return _encode_flat(y32)
+    flat = y32.reshape(-1)
+    out = np.empty(flat.shape, np.uint8)
+
+    def job(start):
+        out[start:start + _CHUNK] = _encode_flat(flat[start:start + _CHUNK])
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(job, range(0, flat.size, _CHUNK)))
+    return out.reshape(y32.shape)
+
+
+def _encode_flat(y32):
     a = np.abs(y32).astype(np.float64)
     # i = number of midpoints strictly below |y|: the nearest magnitude's code
     # unless |y| sits exactly on midpoint i (a tie between codes i and i+1).

@@ -1,0 +1,92 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_fine_grained_amd as fp8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8fg.h")
+
+OK, ENULL, ESHAPE, EALIGN, EUNSUP = 0, -1, -2, -3, -4
+P = ctypes.c_void_p(0x10000)          # a fake, 16-byte aligned "device" pointer (never dereferenced)
+P2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10004)        # misaligned
+NUL = ctypes.c_void_p(0)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:const char\*|int)\s+(\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = fp8.load_library()
+    names = header_functions()
+    assert set(names) == set(fp8.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert fp8.abi_version() == 1
+    assert fp8.status_string(0) == "ok"
+    for code in (-1, -2, -3, -4, -5):
+        assert fp8.status_string(code) not in ("ok", "unknown status")
+    assert fp8.status_string(7) == "unknown status"
+
+
+def test_quant_argument_errors():
+    lib = fp8.load_library()
+    q = lib.fp8_quant_act_1x128
+    assert q(NUL, 128, 128, 0, P, P2, NUL) == ENULL
+    assert q(P, 128, 100, 0, P, P2, NUL) == ESHAPE          # K % 128
+    assert q(P, 100, 128, 1, P, P2, NUL) == ESHAPE          # tokens % 128 when transposed
+    assert q(P, -1, 128, 0, P, P2, NUL) == ESHAPE
+    assert q(MIS, 128, 128, 0, P, P2, NUL) == EALIGN
+    assert q(P, 128, 128, 2, P, P2, NUL) == EUNSUP
+    assert q(P, 0, 128, 0, P, P2, NUL) == OK                # empty: no launch
+    assert q(P, 128, 0, 1, P, P2, NUL) == OK
+    w = lib.fp8_quant_weight_128x128
+    assert w(P, 128, 64, 0, P, P2, NUL) == ESHAPE
+    assert w(P, 64, 128, 0, P, P2, NUL) == ESHAPE
+    assert w(P, 128, 128, 0, NUL, P2, NUL) == ENULL
+    assert w(P, 128, 128, 0, P, MIS, NUL) == EALIGN
+    assert w(P, 0, 128, 1, P, P2, NUL) == OK
+
+
+def test_gemm_argument_errors():
+    g = fp8.load_library().fp8_gemm_blockscaled
+    assert g(P, P, P, NUL, 0, P, 0, 1, 128, 128, NUL) == ENULL
+    assert g(P, P, P, P, 0, P, 0, 1, 100, 128, NUL) == ESHAPE     # N % 128
+    assert g(P, P, P, P, 0, P, 0, 1, 128, 100, NUL) == ESHAPE     # K % 128
+    assert g(P, P, P, P, 0, P, 0, 1, 128, 0, NUL) == ESHAPE       # empty contraction
+    assert g(P, P, MIS, P, 0, P, 0, 1, 128, 128, NUL) == EALIGN
+    assert g(P, P, P, P, 5, P, 0, 1, 128, 128, NUL) == EUNSUP     # bscale kind
+    assert g(P, P, P, P, 0, P, 9, 1, 128, 128, NUL) == EUNSUP     # out dtype
+    assert g(P, P, P, P, 0, P, 0, 0, 128, 128, NUL) == OK          # M = 0
+    assert g(P, P, P, P, 1, P, 1, 5, 0, 128, NUL) == OK            # N = 0
+
+
+def test_grouped_argument_errors():
+    lib = fp8.load_library()
+    c = lib.fp8_grouped_gemm_contiguous
+    assert c(P, P, P, P, NUL, 4, 512, 128, 128, P, 0, NUL) == ENULL
+    assert c(P, P, P, P, P, 4, 500, 128, 128, P, 0, NUL) == ESHAPE   # M_total % 128
+    assert c(P, P, P, P, MIS, 4, 512, 128, 128, P, 0, NUL) == EALIGN
+    assert c(P, P, P, P, P, 4, 512, 128, 128, P, 3, NUL) == EUNSUP
+    assert c(P, P, P, P, P, 0, 512, 128, 128, P, 0, NUL) == OK       # G = 0
+    m = lib.fp8_grouped_gemm_masked
+    assert m(P, P, P, P, NUL, 4, 128, 128, 128, P, 0, NUL) == ENULL
+    assert m(P, P, P, P, P, 4, 128, 128, 130, P, 0, NUL) == ESHAPE
+    assert m(P, P, P, P, P, -1, 128, 128, 128, P, 0, NUL) == ESHAPE
+    assert m(P, P, P, P, P, 4, 0, 128, 128, P, 0, NUL) == OK
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        fp8.fp8_quant_act_1x128(torch.zeros(4, 128))

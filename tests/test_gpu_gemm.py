@@ -1,0 +1,280 @@
+"""GPU parity of the block-scaled GEMMs against the CPU oracle.
+
+Inputs are quantized by the oracle on the host and copied to the GPU, so no
+GEMM input and no expected value comes from the HIP path.  Outputs must satisfy
+the element-wise bound of oracle.gemm.bound (u = 2^-14); the exact special
+cases must match bit for bit.  Full-size workloads are checked on sampled rows
+(the oracle computes those rows exactly); everything else on all outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_fine_grained_amd as fp8
+from oracle import e4m3, gemm, quant
+from tests.goldens import gemm_hand_case
+import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+OUT = {"bf16": torch.bfloat16, "fp32": torch.float32}
+BS = {"128x128": fp8.BSCALE_128x128, "1x128": fp8.BSCALE_1x128}
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host64(t):
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check(c_gpu, c_ref, s_abs, out, what):
+    err = np.abs(c_gpu - c_ref)
+    lim = gemm.bound(c_ref, s_abs, out)
+    bad = np.argwhere(err > lim)
+    ratio = float(np.max(err / np.maximum(lim, 1e-300))) if err.size else 0.0
+    assert bad.size == 0, f"{what}: {len(bad)} outputs outside the bound (max err/bound {ratio:.3g}), first {bad[:3].tolist()}"
+    return ratio
+
+
+def quant_b(b, kind):
+    return quant.quant_weight_128x128(b) if kind == "128x128" else quant.quant_act_1x128(b)
+
+
+def run_dense(qa, sa, qb, sb, kind, out):
+    return fp8.fp8_gemm_blockscaled(dev(qa), dev(sa), dev(qb), dev(sb), BS[kind], OUT[out])
+
+
+def test_hand_worked_case():
+    a, b, exp = gemm_hand_case()
+    qa, sa = quant.quant_act_1x128(a)
+    qb, sb = quant.quant_weight_128x128(b)
+    for out in ("fp32", "bf16"):
+        c = host64(run_dense(qa, sa, qb, sb, "128x128", out))
+        assert c[0, 0] == exp[(out, "n0")] and np.all(c[0, 1:] == exp[(out, "n_other")]), out
+
+
+def test_exact_integer_case():
+    """Tiles of small E4M3 integers with one 448 each: scales are exactly 1,
+    every partial sum is an integer below 2^24, so FP32 output is exact and
+    BF16 output is the round-to-nearest-even of the exact value."""
+    rng = np.random.default_rng(40)
+    M, N, K = 130, 256, 512
+    ints = np.array([-16, -12, -8, -5, -3, -2, -1, 0, 1, 2, 3, 4, 6, 9, 13, 16], np.float32)
+    a = rng.choice(ints, size=(M, K)).astype(np.float32)
+    b = rng.choice(ints, size=(N, K)).astype(np.float32)
+    a[:, ::128] = 448.0
+    b[::128, ::128] = 448.0
+    qa, sa = quant.quant_act_1x128(a)
+    qb, sb = quant.quant_weight_128x128(b)
+    assert np.all(sa == 1) and np.all(sb == 1)
+    c_ref, _ = gemm.gemm_blockscaled_ref(qa, sa, qb, sb)
+    assert np.all(np.abs(c_ref) < 2 ** 24)
+    c32 = host64(run_dense(qa, sa, qb, sb, "128x128", "fp32"))
+    assert np.array_equal(c32, c_ref)
+    cbf = host64(run_dense(qa, sa, qb, sb, "128x128", "bf16"))
+    ref_bf = torch.from_numpy(c_ref.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(cbf, ref_bf)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 256, 256), (128, 256, 512), (130, 384, 384),
+                                   (257, 128, 1024), (300, 512, 2048)])
+@pytest.mark.parametrize("kind", ["128x128", "1x128"])
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_dense_random(M, N, K, kind, out):
+    rng = np.random.default_rng(M * 31 + N * 7 + K)
+    a = workloads.activations(rng, M, K, 0.01, 50.0)
+    b = workloads.weights(rng, N, K) if kind == "128x128" else workloads.activations(rng, N, K, 0.0, 1.0, 1e-3)
+    qa, sa = quant.quant_act_1x128(a)
+    qb, sb = quant_b(b, kind)
+    c = host64(run_dense(qa, sa, qb, sb, kind, out))
+    c_ref, s_abs = gemm.gemm_blockscaled_ref(qa, sa, qb, sb, kind)
+    check(c, c_ref, s_abs, out, f"dense {M}x{N}x{K} {kind} {out}")
+
+
+def test_dense_small_workload():
+    """128x256x512 with 0.5% outlier channels x50, BF16 out: every output checked."""
+    a, b = workloads.dense_small()
+    qa, sa = quant.quant_act_1x128(a)
+    qb, sb = quant.quant_weight_128x128(b)
+    c = host64(run_dense(qa, sa, qb, sb, "128x128", "bf16"))
+    c_ref, s_abs = gemm.gemm_blockscaled_ref(qa, sa, qb, sb)
+    check(c, c_ref, s_abs, "bf16", "dense_small")
+
+
+def test_determinism_and_scale_linearity():
+    rng = np.random.default_rng(41)
+    a = workloads.activations(rng, 256, 1024, 0.01, 100.0)
+    b = workloads.weights(rng, 384, 1024)
+    qa, sa = quant.quant_act_1x128(a)
+    qb, sb = quant.quant_weight_128x128(b)
+    c1 = run_dense(qa, sa, qb, sb, "128x128", "fp32")
+    c2 = run_dense(qa, sa, qb, sb, "128x128", "fp32")
+    c4 = run_dense(qa, sa * np.float32(4.0), qb, sb, "128x128", "fp32")
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    assert torch.equal(c4, c1 * 4)
+
+
+def sample_rows(M, rng, n=64):
+    rows = np.concatenate([np.arange(min(M, 16)), np.arange(max(0, M - 16), M), rng.integers(0, M, n)])
+    return np.unique(rows)
+
+
+@pytest.mark.timeout(600)
+def test_dense_fprop_full_size():
+    """M=4096 N=7168 K=2048, BF16 out: sampled rows against the oracle."""
+    x, w = workloads.dense_fprop()
+    qa, sa = quant.quant_act_1x128(x)
+    qb, sb = quant.quant_weight_128x128(w)
+    c = run_dense(qa, sa, qb, sb, "128x128", "bf16")
+    rows = sample_rows(4096, np.random.default_rng(42))
+    c = host64(c[torch.from_numpy(rows).to(DEV)])
+    c_ref, s_abs = gemm.gemm_blockscaled_ref(qa, sa, qb, sb, rows=rows)
+    check(c, c_ref, s_abs, "bf16", "dense_fprop")
+
+
+@pytest.mark.timeout(600)
+def test_linear_trio_full_size():
+    """Fprop / Dgrad / Wgrad of a 7168->2048 linear at 8192 tokens."""
+    x, w, dy = workloads.linear_trio()
+    rng = np.random.default_rng(43)
+    # Fprop: Y = X . W^T   (M=8192 N=2048 K=7168)
+    qx, sx = quant.quant_act_1x128(x)
+    qw, sw = quant.quant_weight_128x128(w)
+    c = run_dense(qx, sx, qw, sw, "128x128", "bf16")
+    rows = sample_rows(8192, rng, 48)
+    cr, s_abs = gemm.gemm_blockscaled_ref(qx, sx, qw, sw, rows=rows)
+    check(host64(c[torch.from_numpy(rows).to(DEV)]), cr, s_abs, "bf16", "fprop")
+    # Dgrad: dX = dY . W    (M=8192 N=7168 K=2048), B = transposed weight codes
+    qd, sd = quant.quant_act_1x128(dy)
+    qwt, swt = quant.quant_weight_128x128(w, transpose_out=True)
+    c = run_dense(qd, sd, qwt, swt, "128x128", "bf16")
+    cr, s_abs = gemm.gemm_blockscaled_ref(qd, sd, qwt, swt, rows=rows)
+    check(host64(c[torch.from_numpy(rows).to(DEV)]), cr, s_abs, "bf16", "dgrad")
+    # Wgrad: dW = dY^T . X  (M=2048 N=7168 K=8192), both operands 1x128 along tokens, FP32 out
+    qdt, sdt = quant.quant_act_1x128_tokenwise(dy)
+    qxt, sxt = quant.quant_act_1x128_tokenwise(x)
+    c = run_dense(qdt, sdt, qxt, sxt, "1x128", "fp32")
+    rows = sample_rows(2048, rng, 32)
+    cr, s_abs = gemm.gemm_blockscaled_ref(qdt, sdt, qxt, sxt, "1x128", rows=rows)
+    check(host64(c[torch.from_numpy(rows).to(DEV)]), cr, s_abs, "fp32", "wgrad")
+
+
+_EXPERT_CACHE = {}
+
+
+def _experts(kind, G, N, K):
+    """Oracle-quantized expert weights (cached: the full-size layers are shared
+    by the contiguous and masked tests)."""
+    key = (kind, G, N, K)
+    if key not in _EXPERT_CACHE:
+        qs, ss = [], []
+        for g in range(G):
+            q, s = quant.quant_weight_128x128(workloads.expert_weight(kind, g, N, K))
+            qs.append(q)
+            ss.append(s)
+        _EXPERT_CACHE.clear()
+        _EXPERT_CACHE[key] = (np.stack(qs), np.stack(ss))
+    return _EXPERT_CACHE[key]
+
+
+def _layer(N, K):
+    return "moe_gate_up" if (N, K) == (4096, 7168) else "moe_down"
+
+
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_contiguous_small_and_equal_to_dense(out):
+    rng = np.random.default_rng(44)
+    counts = np.array([5, 0, 300, 128, 1])
+    off = workloads.pad_offsets(counts)
+    G, N, K = 5, 256, 384
+    a = workloads.activations(rng, int(off[-1]), K, 0.01, 100.0)
+    qa, sa = quant.quant_act_1x128(a)
+    qb, sb = _experts("moe_contig", G, N, K)
+    c = fp8.fp8_grouped_gemm_contiguous(dev(qa), dev(sa), dev(qb), dev(sb), dev(off.astype(np.int32)), OUT[out])
+    rows, cr, s_abs = gemm.grouped_contiguous_ref(qa, sa, qb, sb, off)
+    check(host64(c), cr, s_abs, out, "contiguous small")
+    for g in range(G):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi > lo:
+            cd = run_dense(qa[lo:hi], sa[:, lo:hi], qb[g], sb[g], "128x128", out)
+            torch.cuda.synchronize()
+            assert torch.equal(cd, c[lo:hi]), g
+
+
+def test_contiguous_rows_outside_offsets_untouched():
+    rng = np.random.default_rng(45)
+    off = np.array([0, 128, 256], np.int32)          # M_total = 512: last two tiles belong to no group
+    G, N, K = 2, 128, 256
+    qa, sa = quant.quant_act_1x128(workloads.activations(rng, 512, K))
+    qb, sb = _experts("moe_contig", G, N, K)
+    c = torch.full((512, N), 7.0, dtype=torch.float32, device=DEV)
+    fp8.fp8_grouped_gemm_contiguous(dev(qa), dev(sa), dev(qb), dev(sb), dev(off), torch.float32, out=c)
+    torch.cuda.synchronize()
+    assert torch.all(c[256:] == 7.0)
+    assert not torch.any(c[:256] == 7.0)
+
+
+@pytest.mark.timeout(900)
+def test_contiguous_moe_full_size():
+    """32 experts, 65536 Zipf-routed rows padded per expert, K=7168 N=4096, BF16."""
+    counts, off = workloads.moe_contig_layout()
+    G, N, K = 32, 4096, 7168
+    a = workloads.moe_contig_rows(counts, off, K)
+    qa, sa = quant.quant_act_1x128(a)
+    del a
+    qb, sb = _experts(_layer(N, K), G, N, K)
+    c = fp8.fp8_grouped_gemm_contiguous(dev(qa), dev(sa), dev(qb), dev(sb), dev(off.astype(np.int32)))
+    rng = np.random.default_rng(46)
+    rows = [np.arange(off[g], min(off[g] + 4, off[g + 1])) for g in range(G) if off[g + 1] > off[g]]
+    rows += [np.arange(max(off[g], off[g + 1] - 4), off[g + 1]) for g in range(G) if off[g + 1] > off[g]]
+    rows = np.unique(np.concatenate(rows + [rng.integers(0, int(off[-1]), 256)]))
+    sel, cr, s_abs = gemm.grouped_contiguous_ref(qa, sa, qb, sb, off, rows=rows)
+    check(host64(c[torch.from_numpy(sel).to(DEV)]), cr, s_abs, "bf16", "contiguous full")
+
+
+def _masked_case(N, K, G=32, M_max=128):
+    mm, a = workloads.moe_masked_inputs(N, K, G, M_max)
+    qs, ss = zip(*[quant.quant_act_1x128(a[g]) for g in range(G)])
+    return mm, np.stack(qs), np.stack(ss)
+
+
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_masked_small_with_sentinel(out):
+    G, M_max, N, K = 4, 96, 256, 256
+    rng = np.random.default_rng(47)
+    mm = np.array([1, 0, 96, 37], np.int32)
+    a = np.stack([workloads.activations(rng, M_max, K, 0.01, 100.0) for _ in range(G)])
+    qa, sa = zip(*[quant.quant_act_1x128(a[g]) for g in range(G)])
+    qa, sa = np.stack(qa), np.stack(sa)
+    qb, sb = _experts("moe_masked", G, N, K)
+    c = torch.full((G, M_max, N), -3.0, dtype=OUT[out], device=DEV)
+    fp8.fp8_grouped_gemm_masked(dev(qa), dev(sa), dev(qb), dev(sb), dev(mm), OUT[out], out=c)
+    res = gemm.grouped_masked_ref(qa, sa, qb, sb, mm)
+    ch = host64(c)
+    for g in range(G):
+        check(ch[g, :mm[g]], res[g][0], res[g][1], out, f"masked g={g}")
+        assert np.all(ch[g, mm[g]:] == -3.0)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("N,K", [(4096, 7168), (7168, 2048)])
+def test_masked_moe_full_size(N, K):
+    """32 experts, 128-row buffers, valid rows U{1..64}: sampled valid rows per
+    expert against the oracle; every row past masked_m keeps its sentinel."""
+    G, M_max = 32, 128
+    mm, qa, sa = _masked_case(N, K, G, M_max)
+    qb, sb = _experts(_layer(N, K), G, N, K)
+    c = torch.full((G, M_max, N), 5.0, dtype=torch.bfloat16, device=DEV)
+    fp8.fp8_grouped_gemm_masked(dev(qa), dev(sa), dev(qb), dev(sb), dev(mm.astype(np.int32)), out=c)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(48)
+    for g in range(G):
+        m = int(mm[g])
+        assert bool(torch.all(c[g, m:] == 5.0)), g
+        rows = np.unique(np.concatenate([[0, m - 1], rng.integers(0, m, 4)]))
+        cr, s_abs = gemm.gemm_blockscaled_ref(qa[g], sa[g], qb[g], sb[g], rows=rows)
+        check(host64(c[g][torch.from_numpy(rows).to(DEV)]), cr, s_abs, "bf16", f"masked full g={g}")

@@ -1,0 +1,132 @@
+"""GPU parity of the quantizers against the CPU oracle: codes and scales must be
+bit-identical.  All calls go through the C ABI (ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_fine_grained_amd as fp8
+from oracle import e4m3, quant
+from tests.goldens import quant_tile_cases
+import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_same(gq, gs, oq, os_, what):
+    gq, gs = host(gq), host(gs)
+    bad = np.argwhere(gq != oq)
+    assert bad.size == 0, f"{what}: {len(bad)} code mismatches, first at {bad[:3].tolist()}"
+    assert np.array_equal(gs.view(np.uint32), np.asarray(os_, np.float32).view(np.uint32)), f"{what}: scales differ"
+
+
+def test_golden_tiles_on_gpu():
+    for name, tile, scale, codes in quant_tile_cases():
+        x = np.tile(tile, (3, 2))
+        q, s = fp8.fp8_quant_act_1x128(dev(x))
+        q, s = host(q), host(s)
+        assert np.all(s.view(np.uint32) == np.float32(scale).view(np.uint32)), name
+        for r in range(3):
+            for kb in range(2):
+                assert np.array_equal(q[r, kb * 128:(kb + 1) * 128], codes), name
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 256), (128, 512), (257, 384), (1000, 1024)])
+def test_act_rowwise_random(M, K):
+    rng = np.random.default_rng(M * 7 + K)
+    x = workloads.activations(rng, M, K, 0.01, 100.0)
+    q, s = fp8.fp8_quant_act_1x128(dev(x))
+    assert_same(q, s, *quant.quant_act_1x128(x), f"rowwise {M}x{K}")
+
+
+@pytest.mark.parametrize("M,K", [(128, 1), (128, 64), (256, 100), (384, 517), (128, 2048)])
+def test_act_tokenwise_random(M, K):
+    rng = np.random.default_rng(M + 13 * K)
+    x = workloads.activations(rng, M, K, 0.01, 100.0)
+    q, s = fp8.fp8_quant_act_1x128(dev(x), transpose_out=True)
+    assert_same(q, s, *quant.quant_act_1x128_tokenwise(x), f"tokenwise {M}x{K}")
+
+
+@pytest.mark.parametrize("N,K", [(128, 128), (256, 384), (1024, 512)])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_weight_random(N, K, transpose):
+    rng = np.random.default_rng(N + K)
+    w = workloads.weights(rng, N, K)
+    w[5, 7] = 3.0                                      # one block with an outlier
+    q, s = fp8.fp8_quant_weight_128x128(dev(w), transpose_out=transpose)
+    assert_same(q, s, *quant.quant_weight_128x128(w, transpose_out=transpose), f"weight {N}x{K} T={transpose}")
+
+
+def test_special_tiles():
+    """Zero tiles, -0, fp32 subnormals, amax whose scale underflows, ties."""
+    x = np.zeros((6, 256), np.float32)
+    x[0, 3] = -0.0
+    x[1, :128] = np.float32(1e-40) * np.arange(128, dtype=np.float32)     # subnormal amax
+    x[2, 0] = np.float32(2e-45)                                            # scale underflows to 0
+    x[2, 1] = -np.float32(1.4e-45)
+    x[3, :128] = np.linspace(-448, 448, 128, dtype=np.float32)
+    x[4, 128:] = np.float32(3.4e38) * np.linspace(-1, 1, 128, dtype=np.float32)
+    x[5, :] = np.float32(2.0 ** -10) * np.arange(256) / 7
+    q, s = fp8.fp8_quant_act_1x128(dev(x))
+    assert_same(q, s, *quant.quant_act_1x128(x), "special tiles")
+    xt = np.ascontiguousarray(np.tile(x, (22, 1))[:128])
+    q, s = fp8.fp8_quant_act_1x128(dev(xt), transpose_out=True)
+    assert_same(q, s, *quant.quant_act_1x128_tokenwise(xt), "special tiles, token-wise")
+
+
+def _binade(e):
+    base = np.uint32((e + 127) << 23)
+    return (np.arange(1 << 23, dtype=np.uint32) + base).view(np.float32)
+
+
+def test_exhaustive_encoder_through_unit_scale_tiles():
+    """Every fp32 with exponent -11..8 up to 448 (both signs) goes through the
+    GPU quantizer in a tile whose max-abs is 448, so the scale is exactly 1 and
+    the code is the plain E4M3 encoding of the value: compared with the
+    oracle's encoder on all of them."""
+    for e in range(-11, 9):
+        v = _binade(e)
+        v = v[v <= 448.0]
+        n_tiles = (v.size + 126) // 127
+        x = np.zeros((n_tiles, 128), np.float32)
+        x[:, 0] = 448.0
+        flat = x[:, 1:].reshape(-1)
+        flat[:v.size] = v
+        x[:, 1:] = flat.reshape(n_tiles, 127)
+        x[1::2] *= -1.0
+        q, s = fp8.fp8_quant_act_1x128(dev(x))
+        q, s = host(q), host(s)
+        assert np.all(s == 1.0), e
+        exp = e4m3.encode(x)
+        bad = np.argwhere(q != exp)
+        assert bad.size == 0, (e, bad[:3].tolist(), x[tuple(bad[0])] if bad.size else None)
+
+
+def test_full_size_quantizers_dense_fprop():
+    """The 4096x2048 activations and 7168x2048 weights of the dense Fprop workload."""
+    x, w = workloads.dense_fprop()
+    q, s = fp8.fp8_quant_act_1x128(dev(x))
+    assert_same(q, s, *quant.quant_act_1x128(x), "dense_fprop activations")
+    q, s = fp8.fp8_quant_weight_128x128(dev(w))
+    assert_same(q, s, *quant.quant_weight_128x128(w), "dense_fprop weights")
+
+
+def test_full_size_quantizers_linear_trio():
+    x, w, dy = workloads.linear_trio()
+    for name, arr in (("X", x), ("dY", dy)):
+        q, s = fp8.fp8_quant_act_1x128(dev(arr))
+        assert_same(q, s, *quant.quant_act_1x128(arr), f"trio {name} rowwise")
+        q, s = fp8.fp8_quant_act_1x128(dev(arr), transpose_out=True)
+        assert_same(q, s, *quant.quant_act_1x128_tokenwise(arr), f"trio {name} token-wise")
+    for t in (False, True):
+        q, s = fp8.fp8_quant_weight_128x128(dev(w), transpose_out=t)
+        assert_same(q, s, *quant.quant_weight_128x128(w, transpose_out=t), f"trio W T={t}")

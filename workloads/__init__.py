@@ -23,7 +23,7 @@ without replacement; the whole column is multiplied by the factor.
 import numpy as np
 
 SEEDS = {"dense_small": 101, "dense_fprop": 102, "linear_trio": 103,
-         "moe_contig": 104, "moe_masked": 105}
+         "moe_contig": 104, "moe_masked": 105, "moe_gate_up": 106, "moe_down": 107}
 
 SHAPES = {
     "dense_small": dict(M=128, N=256, K=512, outlier_frac=0.005, outlier_mult=50.0),
@@ -128,7 +128,10 @@ def moe_contig_rows(counts, offsets, K, seed_stream=1):
 
 
 def expert_weight(kind, g, N, K):
-    """Weights of expert g for workload `kind`, ~ N(0,0.02), drawn per expert."""
+    """Weights [N][K] of expert g, ~ N(0,0.02), drawn per expert.  `kind` names
+    the layer: 'moe_gate_up' (N=4096, K=7168) and 'moe_down' (N=7168, K=2048)
+    are shared by the contiguous and masked workloads; any other SEEDS key
+    gives an independent set."""
     (rw,) = rngs(SEEDS[kind] * 1000 + 7 + g, 1)
     return weights(rw, N, K)
 
