@@ -2,25 +2,41 @@
 //
 // Method: "The Insider Secrets Of Deepseek Discovered", passages on limited
 // Tensor Core accumulation and on promotion (Figure 7(b)): each 128-wide
-// K-block is accumulated on its own, then promoted into an FP32 accumulator
-// with the product of the two group scales applied at that moment.  On gfx950
-// one v_mfma_f32_16x16x128_f8f6f4 covers exactly one K-block of a 16x16 output
-// tile, so the per-K-block partial is the result of a single MFMA started from
-// zero, and the promotion is one FP32 FMA per output element:
+// K-block is accumulated on its own and then promoted into an FP32
+// accumulator, the product of the two group scales being applied at that
+// moment:
 //     acc += P_kb * (sA[kb][m] * sB[nb][kb])        (or sB[kb][n] for 1x128 B)
 // Layouts (DeepGEMM launch article, "Principais caracteristicas": dense plus
 // contiguous and masked MoE groupings): A codes [rows][K], B codes [N][K],
 // both K-major; A scales [K/128][rows]; C [rows][N].
 //
-// Tiling: a 256-thread workgroup computes a 128x128 tile of C; its four waves
-// each own 64 (m) x 64 (n).  A and B K-block tiles (128 rows x 128 bytes each)
-// are double-buffered in LDS; 16-byte chunks are XOR-swizzled by row so that
-// the fragment reads of 16 consecutive rows spread over the banks.  The MFMA is
-// issued with B's fragment as its first operand and A's as its second, so each
-// lane ends up holding four consecutive n of one row m: one A scale per lane
-// and fragment, and 8- or 16-byte output stores.
+// Two engines compute P_kb:
+//   exact   (default) -- the FP8 codes are widened to BF16 (exact: BF16 holds
+//           every E4M3 value) while a K-block is staged into LDS, and four
+//           chained v_mfma_f32_16x16x32_bf16 form P_kb.  This MFMA sums exact
+//           products with IEEE FP32 round-to-nearest, so P_kb is an FP32-
+//           accurate block sum, which is what the promotion scheme assumes.
+//   fp8mfma -- one v_mfma_f32_16x16x128_f8f6f4 per K-block straight from the
+//           FP8 codes, at twice the MFMA rate.  On gfx950 that instruction
+//           adds its products in groups of eight consecutive K, truncating each
+//           product to 13 fractional bits below the group's largest exponent
+//           (about 14 significant bits: the same kind of limited accumulation
+//           the pages measured on H800, here inside a single instruction), so
+//           promotion every 128 cannot restore FP32 accuracy and its results
+//           need a looser error bound.  Chosen with FP8FG_GEMM_ENGINE=fp8mfma.
+//
+// Tiling (both engines): a 256-thread workgroup computes a 128x128 tile of C;
+// its four waves each own 64 (m) x 64 (n).  K-block tiles of A and B are
+// double-buffered in LDS with 16-byte chunks XOR-swizzled by row, so that the
+// fragment reads of 16 consecutive rows fall on distinct banks.  Every MFMA
+// takes B's fragment as its first operand and A's as its second, so each lane
+// holds four consecutive n of one row m: one A scale per lane and fragment,
+// and 8- or 16-byte output stores.
 #include "device_common.hpp"
 #include "launch.hpp"
+
+#include <stdlib.h>
+#include <string.h>
 
 namespace fp8fg {
 
@@ -28,24 +44,304 @@ namespace {
 
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int kThreads = 256;
-constexpr int kTileBytes = BM * BK;        // one operand tile per K-block (A and B alike)
 
-// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row` in LDS.
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// One MFMA operand fragment: rows `row0 + lane%16`, 32 bytes starting at byte
-// 32*(lane/16) of the K-block.  A and B fragments use the same byte mapping,
-// so whatever K order the instruction assigns to (lane, byte) is shared by
-// both operands and the contraction is over matching k.
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row0, int lane) {
+// ---------------------------------------------------------------------------
+// Tile -> (group, rows, operand pointers)
+struct Tile {
+    int64_t m0;           // first row of the tile in its group's row space
+    int64_t rows_valid;   // rows [0, rows_valid) of that row space are real
+    int64_t lda_s;        // row count of the A scale array (stride between K-blocks)
+    int64_t c_base;       // element offset of the group's C block
+    const uint8_t* A;
+    const float* SA;
+    const uint8_t* B;
+    const float* SB;
+    int bn;
+    bool live;
+};
+
+template <int MODE>
+__device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile) {
+    Tile t;
+    const int n_tiles = int(args.N / BN);
+    const int64_t kbs = args.K / BK;
+    t.bn = int(tile % n_tiles);
+    tile /= n_tiles;
+    t.A = args.a;
+    t.SA = args.sa;
+    t.B = args.b;
+    t.SB = args.sb;
+    t.c_base = 0;
+    t.live = true;
+    int64_t g = 0;
+    if (MODE == int(GemmMode::Dense)) {
+        t.m0 = tile * BM;
+        t.rows_valid = args.M;
+        t.lda_s = args.M;
+    } else if (MODE == int(GemmMode::Contig)) {
+        t.m0 = tile * BM;
+        int lo = 0, hi = int(args.G) - 1;          // largest g with offsets[g] <= m0
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (args.aux[mid] <= t.m0) lo = mid; else hi = mid - 1;
+        }
+        g = lo;
+        const int64_t g_end = args.aux[g + 1];
+        if (args.aux[g] > t.m0 || t.m0 >= g_end || g_end > args.M) t.live = false;
+        t.rows_valid = g_end;
+        t.lda_s = args.M;
+    } else {
+        const int64_t m_tiles = (args.M + BM - 1) / BM;
+        g = tile / m_tiles;
+        t.m0 = (tile - g * m_tiles) * BM;
+        int64_t mm = args.aux[g];
+        t.rows_valid = mm < 0 ? 0 : (mm > args.M ? args.M : mm);
+        t.lda_s = args.M;
+        t.A += g * args.M * args.K;
+        t.SA += g * kbs * args.M;
+        t.c_base = g * args.M * args.N;
+    }
+    if (t.m0 >= t.rows_valid) t.live = false;
+    if (MODE != int(GemmMode::Dense)) {
+        t.B += g * args.N * args.K;
+        t.SB += g * (args.N / BN) * kbs;
+    }
+    return t;
+}
+
+// Per-lane scale state of one K-block: A scales for the four 16-row fragments
+// and either one B block scale or four column scales per n-fragment.
+template <int BSCALE_1x128>
+struct Scales {
+    float sa[4];
+    float sb_blk;
+    v4f sb_col[4];
+};
+
+template <int BSCALE_1x128>
+__device__ __forceinline__ Scales<BSCALE_1x128> load_scales(const Tile& t, const int64_t (&sa_row)[4], int64_t kb,
+                                                             int64_t kbs, int64_t N, int64_t n0, int n_lane) {
+    Scales<BSCALE_1x128> s;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) s.sa[mi] = t.SA[kb * t.lda_s + sa_row[mi]];
+    s.sb_blk = 0.f;
+    if (BSCALE_1x128) {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) s.sb_col[ni] = ld<v4f>(t.SB + kb * N + n0 + n_lane + ni * 16);
+    } else {
+        s.sb_blk = t.SB[int64_t(t.bn) * kbs + kb];
+    }
+    return s;
+}
+
+// The promotion: acc += P * (sA * sB), one FP32 FMA per output element.
+template <int BSCALE_1x128>
+__device__ __forceinline__ void fold(v4f (&acc)[4][4], const v4f (&p)[4][4], const Scales<BSCALE_1x128>& s) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            if (BSCALE_1x128) acc[mi][ni] = p[mi][ni] * (s.sa[mi] * s.sb_col[ni]) + acc[mi][ni];
+            else acc[mi][ni] = p[mi][ni] * (s.sa[mi] * s.sb_blk) + acc[mi][ni];
+        }
+}
+
+// lane holds C[m][n .. n+3] for each (mi, ni)
+template <int OUT_FP32>
+__device__ __forceinline__ void store_tile(const GemmArgs& args, const Tile& t, const v4f (&acc)[4][4], int wm,
+                                           int lane, int64_t n0, int n_lane) {
+    const int64_t N = args.N;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int64_t m = t.m0 + wm * 64 + mi * 16 + (lane & 15);
+        if (m >= t.rows_valid) continue;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 16;
+            const v4f v = acc[mi][ni];
+            if (OUT_FP32) {
+                st<v4f>(static_cast<float*>(args.c) + idx, v);
+            } else {
+                const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+                const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+                st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
+            }
+        }
+    }
+}
+
+// Global-load assignment shared by both engines: thread tid copies 16 bytes
+// (16 consecutive k) of rows tid/8 + 32*i, i = 0..3, from A and from B.
+struct Loader {
+    const uint8_t* a_src[4];
+    const uint8_t* b_src[4];
+    int row[4];
+    int chunk;
+};
+
+__device__ __forceinline__ Loader make_loader(const Tile& t, int tid, int64_t K, int64_t n0) {
+    Loader L;
+    L.chunk = tid & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        int64_t ar = t.m0 + r;
+        if (ar >= t.rows_valid) ar = t.rows_valid - 1;     // clamp: loaded, never stored
+        L.a_src[i] = t.A + ar * K + L.chunk * 16;
+        L.b_src[i] = t.B + (n0 + r) * K + L.chunk * 16;
+        L.row[i] = r;
+    }
+    return L;
+}
+
+// ===========================================================================
+// Engine "exact": BF16 MFMA on exactly widened FP8 codes.
+//
+// LDS tile row = 128 k x 2 bytes = 16 chunks of 16 bytes (8 bf16 each); chunk
+// c of row r lives at r*256 + ((c ^ (r & 15)) << 4).  MFMA fragment for k-step
+// ks (32 k): lane l reads chunk 4*ks + l/16 of row row0 + l%16.
+__device__ __forceinline__ int xoff(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+
+// bytes 0,1 (HI = false) or 2,3 (HI = true) of w -> two BF16 values, exactly
+template <bool HI>
+__device__ __forceinline__ uint32_t bf16x2_of_fp8(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.0f, HI));
+}
+
+// 16 FP8 codes -> 16 BF16 values (two 16-byte LDS chunks)
+__device__ __forceinline__ void widen16(u32x4 in, u32x4& lo, u32x4& hi) {
+    lo = u32x4{bf16x2_of_fp8<false>(in[0]), bf16x2_of_fp8<true>(in[0]),
+               bf16x2_of_fp8<false>(in[1]), bf16x2_of_fp8<true>(in[1])};
+    hi = u32x4{bf16x2_of_fp8<false>(in[2]), bf16x2_of_fp8<true>(in[2]),
+               bf16x2_of_fp8<false>(in[3]), bf16x2_of_fp8<true>(in[3])};
+}
+
+__device__ __forceinline__ v8bf read_frag_bf16(const uint8_t* tile, int row0, int ks, int lane) {
+    const int row = row0 + (lane & 15);
+    return ld<v8bf>(tile + xoff(row, ks * 4 + (lane >> 4)));
+}
+
+template <int BSCALE_1x128, int OUT_FP32, int MODE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_exact_kernel(GemmArgs args) {
+    constexpr int kTile = BM * BK * 2;                       // bytes of one bf16 operand tile
+    __shared__ __align__(16) uint8_t lds[2][2][kTile];        // [buffer][A, B]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t N = args.N, K = args.K, kbs = K / BK;
+    const Tile t = map_tile<MODE>(args, blockIdx.x);
+    if (!t.live) return;
+    const int64_t n0 = int64_t(t.bn) * BN;
+    const Loader L = make_loader(t, tid, K, n0);
+    int st_off[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        st_off[i][0] = xoff(L.row[i], 2 * L.chunk);
+        st_off[i][1] = xoff(L.row[i], 2 * L.chunk + 1);
+    }
+    int64_t sa_row[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int64_t r = t.m0 + wm * 64 + mi * 16 + (lane & 15);
+        sa_row[mi] = r < t.rows_valid ? r : t.rows_valid - 1;
+    }
+    const int n_lane = wn * 64 + (lane >> 4) * 4;
+    // a wave whose 64 rows are all past the valid rows skips its MFMAs
+    const bool wave_live = t.m0 + wm * 64 < t.rows_valid;
+
+    u32x4 ra[4], rb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ra[i] = ld<u32x4>(L.a_src[i]);
+        rb[i] = ld<u32x4>(L.b_src[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        u32x4 lo, hi;
+        widen16(ra[i], lo, hi);
+        st<u32x4>(&lds[0][0][st_off[i][0]], lo);
+        st<u32x4>(&lds[0][0][st_off[i][1]], hi);
+        widen16(rb[i], lo, hi);
+        st<u32x4>(&lds[0][1][st_off[i][0]], lo);
+        st<u32x4>(&lds[0][1][st_off[i][1]], hi);
+    }
+    __syncthreads();
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t kb = 0; kb < kbs; ++kb) {
+        const int cur = int(kb & 1);
+        const int64_t koff = (kb + 1 < kbs ? kb + 1 : kb) * BK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ra[i] = ld<u32x4>(L.a_src[i] + koff);
+            rb[i] = ld<u32x4>(L.b_src[i] + koff);
+        }
+        const Scales<BSCALE_1x128> sc = load_scales<BSCALE_1x128>(t, sa_row, kb, kbs, N, n0, n_lane);
+        if (wave_live) {
+            const uint8_t* ta = lds[cur][0];
+            const uint8_t* tb = lds[cur][1];
+            v4f p[4][4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) p[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                v8bf af[4], bf[4];
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) af[mi] = read_frag_bf16(ta, wm * 64 + mi * 16, ks, lane);
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) bf[ni] = read_frag_bf16(tb, wn * 64 + ni * 16, ks, lane);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+                        p[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[ni], af[mi], p[mi][ni], 0, 0, 0);
+            }
+            fold<BSCALE_1x128>(acc, p, sc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u32x4 lo, hi;
+            widen16(ra[i], lo, hi);
+            st<u32x4>(&lds[cur ^ 1][0][st_off[i][0]], lo);
+            st<u32x4>(&lds[cur ^ 1][0][st_off[i][1]], hi);
+            widen16(rb[i], lo, hi);
+            st<u32x4>(&lds[cur ^ 1][1][st_off[i][0]], lo);
+            st<u32x4>(&lds[cur ^ 1][1][st_off[i][1]], hi);
+        }
+        __syncthreads();
+    }
+    if (wave_live) store_tile<OUT_FP32>(args, t, acc, wm, lane, n0, n_lane);
+}
+
+// ===========================================================================
+// Engine "fp8mfma": one FP8 MFMA per K-block.
+//
+// LDS tile row = 128 bytes = 8 chunks of 16; chunk c of row r lives at
+// r*128 + ((c ^ (r & 7)) << 4).  Fragment: rows row0 + lane%16, 32 bytes from
+// byte 32*(lane/16) of the K-block; A and B use the same byte mapping, so the
+// instruction's own (lane, byte) -> k assignment is shared by both operands.
+__device__ __forceinline__ int foff(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ v8i read_frag_fp8(const uint8_t* tile, int row0, int lane) {
     const int row = row0 + (lane & 15);
     const int ch = (lane >> 4) * 2;
-    const u32x4 lo = ld<u32x4>(tile + lds_off(row, ch));
-    const u32x4 hi = ld<u32x4>(tile + lds_off(row, ch + 1));
+    const u32x4 lo = ld<u32x4>(tile + foff(row, ch));
+    const u32x4 hi = ld<u32x4>(tile + foff(row, ch + 1));
     return v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
 }
 
-__device__ __forceinline__ v4f mfma_kblock(v8i bfrag, v8i afrag) {
+__device__ __forceinline__ v4f mfma_fp8_kblock(v8i bfrag, v8i afrag) {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     // operand formats 0/0 = E4M3 x E4M3; zero scale operands select the plain
     // (unscaled) instruction
@@ -54,94 +350,34 @@ __device__ __forceinline__ v4f mfma_kblock(v8i bfrag, v8i afrag) {
 
 template <int BSCALE_1x128, int OUT_FP32, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_bs_kernel(GemmArgs args) {
-    __shared__ __align__(16) uint8_t lds[2][2][kTileBytes];   // [buffer][A, B]
+void gemm_fp8mfma_kernel(GemmArgs args) {
+    constexpr int kTile = BM * BK;
+    __shared__ __align__(16) uint8_t lds[2][2][kTile];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t N = args.N, K = args.K;
-    const int n_tiles = int(N / BN);
-    const int64_t kbs = K / BK;
-
-    // ---- tile -> (group, rows) ------------------------------------------
-    int64_t tile = blockIdx.x;
-    const int bn = int(tile % n_tiles);
-    tile /= n_tiles;
-    int64_t m0;               // first row of the tile within its group's row space
-    int64_t rows_valid;       // rows [0, rows_valid) of that row space exist
-    int64_t lda_s;            // row count of the scale array (stride between K-blocks)
-    const uint8_t* A = args.a;
-    const float* SA = args.sa;
-    const uint8_t* B = args.b;
-    const float* SB = args.sb;
-    int64_t g = 0;
-    if (MODE == int(GemmMode::Dense)) {
-        m0 = tile * BM;
-        rows_valid = args.M;
-        lda_s = args.M;
-    } else if (MODE == int(GemmMode::Contig)) {
-        m0 = tile * BM;
-        // largest g with offsets[g] <= m0
-        int lo = 0, hi = int(args.G) - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (args.aux[mid] <= m0) lo = mid; else hi = mid - 1;
-        }
-        g = lo;
-        const int64_t g_end = args.aux[g + 1];
-        if (args.aux[g] > m0 || m0 >= g_end || g_end > args.M) return;
-        rows_valid = g_end;
-        lda_s = args.M;
-    } else {
-        const int64_t m_tiles = (args.M + BM - 1) / BM;
-        g = tile / m_tiles;
-        m0 = (tile - g * m_tiles) * BM;
-        int64_t mm = args.aux[g];
-        mm = mm < 0 ? 0 : (mm > args.M ? args.M : mm);
-        rows_valid = mm;
-        lda_s = args.M;
-        A += g * args.M * K;
-        SA += g * kbs * args.M;
-    }
-    if (m0 >= rows_valid) return;
-    if (MODE != int(GemmMode::Dense)) {
-        B += g * N * K;
-        SB += g * (N / BN) * kbs;
-    }
-    const int64_t n0 = int64_t(bn) * BN;
-
-    // ---- global -> LDS copy assignment: rows tid/8 + 32*i, chunk tid%8 -----
-    const int ld_chunk = tid & 7;
-    const int ld_row = tid >> 3;
-    const uint8_t* a_src[4];
-    const uint8_t* b_src[4];
+    const int64_t N = args.N, K = args.K, kbs = K / BK;
+    const Tile t = map_tile<MODE>(args, blockIdx.x);
+    if (!t.live) return;
+    const int64_t n0 = int64_t(t.bn) * BN;
+    const Loader L = make_loader(t, tid, K, n0);
     int st_off[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = ld_row + 32 * i;
-        int64_t ar = m0 + r;
-        if (ar >= rows_valid) ar = rows_valid - 1;     // clamp: loaded, never stored
-        a_src[i] = A + ar * K + ld_chunk * 16;
-        b_src[i] = B + (n0 + r) * K + ld_chunk * 16;
-        st_off[i] = lds_off(r, ld_chunk);
-    }
-
-    // rows of this lane's A scales, one per 16-row fragment (clamped like the loads)
+    for (int i = 0; i < 4; ++i) st_off[i] = foff(L.row[i], L.chunk);
     int64_t sa_row[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-        int64_t r = m0 + wm * 64 + mi * 16 + (lane & 15);
-        sa_row[mi] = r < rows_valid ? r : rows_valid - 1;
+        const int64_t r = t.m0 + wm * 64 + mi * 16 + (lane & 15);
+        sa_row[mi] = r < t.rows_valid ? r : t.rows_valid - 1;
     }
-    const int n_lane = wn * 64 + (lane >> 4) * 4;      // + ni*16: first of this lane's 4 columns
+    const int n_lane = wn * 64 + (lane >> 4) * 4;
+    const bool wave_live = t.m0 + wm * 64 < t.rows_valid;
 
     u32x4 ra[4], rb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        ra[i] = ld<u32x4>(a_src[i]);
-        rb[i] = ld<u32x4>(b_src[i]);
+        ra[i] = ld<u32x4>(L.a_src[i]);
+        rb[i] = ld<u32x4>(L.b_src[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -158,51 +394,27 @@ void gemm_bs_kernel(GemmArgs args) {
 
     for (int64_t kb = 0; kb < kbs; ++kb) {
         const int cur = int(kb & 1);
-        // prefetch the next K-block (the last iteration re-reads its own block;
-        // the copy lands in the idle buffer and is never read)
         const int64_t koff = (kb + 1 < kbs ? kb + 1 : kb) * BK;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            ra[i] = ld<u32x4>(a_src[i] + koff);
-            rb[i] = ld<u32x4>(b_src[i] + koff);
+            ra[i] = ld<u32x4>(L.a_src[i] + koff);
+            rb[i] = ld<u32x4>(L.b_src[i] + koff);
         }
-        // scales of this K-block
-        float sa[4];
+        const Scales<BSCALE_1x128> sc = load_scales<BSCALE_1x128>(t, sa_row, kb, kbs, N, n0, n_lane);
+        if (wave_live) {
+            const uint8_t* ta = lds[cur][0];
+            const uint8_t* tb = lds[cur][1];
+            v8i af[4], bf[4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) sa[mi] = SA[kb * lda_s + sa_row[mi]];
-        float sb_blk = 0.f;
-        v4f sb_col[4];
-        if (BSCALE_1x128) {
+            for (int mi = 0; mi < 4; ++mi) af[mi] = read_frag_fp8(ta, wm * 64 + mi * 16, lane);
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) sb_col[ni] = ld<v4f>(SB + kb * N + n0 + n_lane + ni * 16);
-        } else {
-            sb_blk = SB[int64_t(bn) * kbs + kb];
-        }
-
-        const uint8_t* ta = lds[cur][0];
-        const uint8_t* tb = lds[cur][1];
-        v8i af[4], bf[4];
+            for (int ni = 0; ni < 4; ++ni) bf[ni] = read_frag_fp8(tb, wn * 64 + ni * 16, lane);
+            v4f p[4][4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) af[mi] = read_frag(ta, wm * 64 + mi * 16, lane);
+            for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) bf[ni] = read_frag(tb, wn * 64 + ni * 16, lane);
-        // all 16 partials of this K-block first (independent registers, so the
-        // MFMA pipe never waits on the fold), then the promotion FMAs
-        v4f p[4][4];
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) p[mi][ni] = mfma_kblock(bf[ni], af[mi]);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                if (BSCALE_1x128) {
-                    acc[mi][ni] = p[mi][ni] * (sa[mi] * sb_col[ni]) + acc[mi][ni];
-                } else {
-                    acc[mi][ni] = p[mi][ni] * (sa[mi] * sb_blk) + acc[mi][ni];
-                }
-            }
+                for (int mi = 0; mi < 4; ++mi) p[mi][ni] = mfma_fp8_kblock(bf[ni], af[mi]);
+            fold<BSCALE_1x128>(acc, p, sc);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -211,34 +423,42 @@ void gemm_bs_kernel(GemmArgs args) {
         }
         __syncthreads();
     }
-
-    // ---- epilogue: lane holds C[m][n .. n+3] for each (mi, ni) -------------
-    int64_t c_base = 0;
-    if (MODE == int(GemmMode::Masked)) c_base = g * args.M * N;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        const int64_t m = m0 + wm * 64 + mi * 16 + (lane & 15);
-        if (m >= rows_valid) continue;
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const int64_t idx = c_base + m * N + n0 + n_lane + ni * 16;
-            const v4f v = acc[mi][ni];
-            if (OUT_FP32) {
-                st<v4f>(static_cast<float*>(args.c) + idx, v);
-            } else {
-                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-                const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-                st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
-            }
-        }
-    }
+    if (wave_live) store_tile<OUT_FP32>(args, t, acc, wm, lane, n0, n_lane);
 }
 
-template <int BS, int OF, int MODE>
+template <int ENGINE, int BS, int OF, int MODE>
 hipError_t launch_one(const GemmArgs& args, int64_t tiles, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_bs_kernel<BS, OF, MODE>), dim3(unsigned(tiles)), dim3(kThreads), 0, stream, args);
+    if (ENGINE == 0)
+        hipLaunchKernelGGL((gemm_exact_kernel<BS, OF, MODE>), dim3(unsigned(tiles)), dim3(kThreads), 0, stream, args);
+    else
+        hipLaunchKernelGGL((gemm_fp8mfma_kernel<BS, OF, MODE>), dim3(unsigned(tiles)), dim3(kThreads), 0, stream, args);
     return hipGetLastError();
+}
+
+template <int ENGINE>
+hipError_t dispatch(GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args, int64_t tiles,
+                    hipStream_t stream) {
+    switch (mode) {
+        case GemmMode::Dense:
+            if (bscale_1x128)
+                return out_fp32 ? launch_one<ENGINE, 1, 1, 0>(args, tiles, stream)
+                                : launch_one<ENGINE, 1, 0, 0>(args, tiles, stream);
+            return out_fp32 ? launch_one<ENGINE, 0, 1, 0>(args, tiles, stream)
+                            : launch_one<ENGINE, 0, 0, 0>(args, tiles, stream);
+        case GemmMode::Contig:
+            return out_fp32 ? launch_one<ENGINE, 0, 1, 1>(args, tiles, stream)
+                            : launch_one<ENGINE, 0, 0, 1>(args, tiles, stream);
+        case GemmMode::Masked:
+            return out_fp32 ? launch_one<ENGINE, 0, 1, 2>(args, tiles, stream)
+                            : launch_one<ENGINE, 0, 0, 2>(args, tiles, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+// FP8FG_GEMM_ENGINE: unset or "exact" -> 0, "fp8mfma" -> 1 (read at every call)
+int engine_from_env() {
+    const char* e = getenv("FP8FG_GEMM_ENGINE");
+    return (e && strcmp(e, "fp8mfma") == 0) ? 1 : 0;
 }
 
 }  // namespace
@@ -250,16 +470,8 @@ hipError_t launch_gemm(GemmMode mode, int bscale_1x128, int out_fp32, const Gemm
     if (mode == GemmMode::Masked) tiles = args.G * ((args.M + BM - 1) / BM) * n_tiles;
     else tiles = ((args.M + BM - 1) / BM) * n_tiles;
     if (tiles == 0) return hipSuccess;
-    switch (mode) {
-        case GemmMode::Dense:
-            if (bscale_1x128) return out_fp32 ? launch_one<1, 1, 0>(args, tiles, stream) : launch_one<1, 0, 0>(args, tiles, stream);
-            return out_fp32 ? launch_one<0, 1, 0>(args, tiles, stream) : launch_one<0, 0, 0>(args, tiles, stream);
-        case GemmMode::Contig:
-            return out_fp32 ? launch_one<0, 1, 1>(args, tiles, stream) : launch_one<0, 0, 1>(args, tiles, stream);
-        case GemmMode::Masked:
-            return out_fp32 ? launch_one<0, 1, 2>(args, tiles, stream) : launch_one<0, 0, 2>(args, tiles, stream);
-    }
-    return hipErrorInvalidValue;
+    if (engine_from_env() == 1) return dispatch<1>(mode, bscale_1x128, out_fp32, args, tiles, stream);
+    return dispatch<0>(mode, bscale_1x128, out_fp32, args, tiles, stream);
 }
 
 }  // namespace fp8fg
