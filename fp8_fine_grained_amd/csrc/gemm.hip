@@ -11,30 +11,44 @@
 // both K-major; A scales [K/128][rows]; C [rows][N].
 //
 // Two engines compute P_kb:
-//   exact   (default) -- the FP8 codes are widened to BF16 (exact: BF16 holds
-//           every E4M3 value) while a K-block is staged into LDS, and four
-//           chained v_mfma_f32_16x16x32_bf16 form P_kb.  This MFMA sums exact
-//           products with IEEE FP32 round-to-nearest, so P_kb is an FP32-
-//           accurate block sum, which is what the promotion scheme assumes.
-//   fp8mfma -- one v_mfma_f32_16x16x128_f8f6f4 per K-block straight from the
-//           FP8 codes, at twice the MFMA rate.  On gfx950 that instruction
-//           adds its products in groups of eight consecutive K, truncating each
-//           product to 13 fractional bits below the group's largest exponent
-//           (about 14 significant bits: the same kind of limited accumulation
-//           the pages measured on H800, here inside a single instruction), so
-//           promotion every 128 cannot restore FP32 accuracy and its results
-//           need a looser error bound.  Chosen with FP8FG_GEMM_ENGINE=fp8mfma.
+//   exact   (default) -- each FP8 fragment is widened to BF16 in registers
+//           (exact: BF16 holds every E4M3 value) and eight chained
+//           v_mfma_f32_32x32x16_bf16 form P_kb.  This MFMA adds exact
+//           products with IEEE FP32 round-to-nearest, so P_kb is an
+//           FP32-accurate block sum, which is what the promotion assumes.
+//   fp8mfma -- two chained v_mfma_f32_32x32x64_f8f6f4 per K-block straight
+//           from the FP8 codes, at twice the MFMA rate.  gfx950's FP8 MFMAs
+//           add their products in groups of eight consecutive K, truncating
+//           each product to 13 fractional bits below the group's largest
+//           exponent (about 14 significant bits: the kind of limited
+//           accumulation the pages measured on H800, here inside a single
+//           instruction), so promotion every 128 cannot restore FP32 accuracy
+//           and this engine is held to a looser bound.  Chosen with
+//           FP8FG_GEMM_ENGINE=fp8mfma.
 //
-// Tiling (both engines): a 256-thread workgroup computes a 128x128 tile of C;
-// its four waves each own 64 (m) x 64 (n).  K-block tiles of A and B are
-// double-buffered in LDS with 16-byte chunks XOR-swizzled by row, so that the
-// fragment reads of 16 consecutive rows fall on distinct banks.  Every MFMA
-// takes B's fragment as its first operand and A's as its second, so each lane
-// holds four consecutive n of one row m: one A scale per lane and fragment,
-// and 8- or 16-byte output stores.
+// Work decomposition (both engines).  A 512-thread workgroup computes a
+// 256 (m) x 128 (n) tile of C; each of its eight waves (two per SIMD) owns a
+// 64 x 64 sub-tile = 2 x 2 MFMA tiles of 32 x 32.  K-blocks stream through a
+// three-stage ring in LDS filled by direct-to-LDS loads
+// (global_load_lds_dwordx4: the data never passes through registers), so two
+// K-blocks are in flight while a third is multiplied.  A stage holds the FP8
+// A tile (256 x 128 B), the FP8 B tile (128 x 128 B), the tile's 256 A
+// scales and, for 1x128-scaled B, its 128 column scales.  Rows of 128 bytes
+// are stored as eight 16-byte chunks, chunk c of row r at slot
+// c ^ ((r >> 1) & 7), so the 16 rows read together by a fragment load hit 16
+// distinct 16-byte bank groups.  One barrier per K-block: after it, the
+// stage read in the previous iteration is refilled.
+//
+// MFMA operands: lane l of a 32x32 fragment holds row l%32 and, per 16-byte
+// LDS chunk, 16 consecutive k; A and B use the same (lane, byte) -> k map, so
+// the contraction pairs matching k whatever order the instruction gives to
+// (lane, element).  B's fragment is the instruction's first operand, so lane
+// l ends with m = l%32 and n = 8*(i/4) + 4*(l/32) + i%4 for result i: four
+// runs of four consecutive n (one A scale per lane, 8- or 16-byte stores).
 #include "device_common.hpp"
 #include "launch.hpp"
 
+#include <stddef.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -42,11 +56,25 @@ namespace fp8fg {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int kThreads = 256;
+constexpr int BM = 256, BN = 128, BK = 128;
+constexpr int kThreads = 512;
+constexpr int kStages = 3;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+struct alignas(16) Stage {
+    uint8_t a[BM * BK];      // FP8 A tile, swizzled rows
+    uint8_t b[BN * BK];      // FP8 B tile, swizzled rows
+    float sa[BM];            // A scales of this K-block for the tile's rows
+    float sb[BN];            // B column scales (1x128 B), or the B block scale x64 (128x128 B)
+    float dummy[64];         // target of the padding scale load (never read)
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 // ---------------------------------------------------------------------------
 // Tile -> (group, rows, operand pointers)
@@ -76,30 +104,37 @@ __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile) {
     t.SB = args.sb;
     t.c_base = 0;
     t.live = true;
+    t.lda_s = args.M;
     int64_t g = 0;
     if (MODE == int(GemmMode::Dense)) {
         t.m0 = tile * BM;
         t.rows_valid = args.M;
-        t.lda_s = args.M;
     } else if (MODE == int(GemmMode::Contig)) {
-        t.m0 = tile * BM;
-        int lo = 0, hi = int(args.G) - 1;          // largest g with offsets[g] <= m0
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (args.aux[mid] <= t.m0) lo = mid; else hi = mid - 1;
+        // walk the groups, counting ceil(rows / BM) tiles per group, until the
+        // tile's index falls inside one; the grid is sized M_total/BM + G, an
+        // upper bound of the total, and the surplus tiles find no group
+        int64_t base = 0;
+        t.live = false;
+        t.m0 = 0;
+        t.rows_valid = 0;
+        for (int64_t gg = 0; gg < args.G; ++gg) {
+            const int64_t lo = args.aux[gg], hi = args.aux[gg + 1];
+            const int64_t n = hi > lo ? (hi - lo + BM - 1) / BM : 0;
+            if (tile < base + n) {
+                g = gg;
+                t.m0 = lo + (tile - base) * BM;
+                t.rows_valid = hi < args.M ? hi : args.M;
+                t.live = lo >= 0;
+                break;
+            }
+            base += n;
         }
-        g = lo;
-        const int64_t g_end = args.aux[g + 1];
-        if (args.aux[g] > t.m0 || t.m0 >= g_end || g_end > args.M) t.live = false;
-        t.rows_valid = g_end;
-        t.lda_s = args.M;
     } else {
         const int64_t m_tiles = (args.M + BM - 1) / BM;
         g = tile / m_tiles;
         t.m0 = (tile - g * m_tiles) * BM;
         int64_t mm = args.aux[g];
         t.rows_valid = mm < 0 ? 0 : (mm > args.M ? args.M : mm);
-        t.lda_s = args.M;
         t.A += g * args.M * args.K;
         t.SA += g * kbs * args.M;
         t.c_base = g * args.M * args.N;
@@ -112,247 +147,174 @@ __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile) {
     return t;
 }
 
-// Per-lane scale state of one K-block: A scales for the four 16-row fragments
-// and either one B block scale or four column scales per n-fragment.
-template <int BSCALE_1x128>
-struct Scales {
-    float sa[4];
-    float sb_blk;
-    v4f sb_col[4];
+// ---------------------------------------------------------------------------
+// Direct-to-LDS copy of one K-block into a stage.  Every wave issues exactly
+// seven load instructions per K-block (so one vmcnt value fits all waves):
+// four 1 KB pieces of A (8 rows each), two of B, and one 256-byte scale piece
+// -- waves 0-3 the A scales, waves 4-5 the B column scales when B is
+// 1x128-scaled, or wave 4 alone 64 copies of the B block scale when it is
+// 128x128-scaled, the rest a padding load into Stage::dummy.  Keeping every
+// scale on this path leaves vmcnt counting nothing but the ring.
+struct Copier {
+    const uint8_t* a_row[4];   // this lane's A row for each of its four A pieces (+ chunk offset)
+    const uint8_t* b_row[2];
+    int a_lds[4], b_lds[2];    // wave-uniform LDS byte offsets of the pieces
+    const float* s_src;        // this lane's scale source for K-block 0
+    int64_t s_stride;          // scale source stride between K-blocks
+    int s_lds;                 // wave-uniform LDS byte offset of the scale piece
 };
 
 template <int BSCALE_1x128>
-__device__ __forceinline__ Scales<BSCALE_1x128> load_scales(const Tile& t, const int64_t (&sa_row)[4], int64_t kb,
-                                                             int64_t kbs, int64_t N, int64_t n0, int n_lane) {
-    Scales<BSCALE_1x128> s;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) s.sa[mi] = t.SA[kb * t.lda_s + sa_row[mi]];
-    s.sb_blk = 0.f;
-    if (BSCALE_1x128) {
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) s.sb_col[ni] = ld<v4f>(t.SB + kb * N + n0 + n_lane + ni * 16);
-    } else {
-        s.sb_blk = t.SB[int64_t(t.bn) * kbs + kb];
-    }
-    return s;
-}
-
-// The promotion: acc += P * (sA * sB), one FP32 FMA per output element.
-template <int BSCALE_1x128>
-__device__ __forceinline__ void fold(v4f (&acc)[4][4], const v4f (&p)[4][4], const Scales<BSCALE_1x128>& s) {
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            if (BSCALE_1x128) acc[mi][ni] = p[mi][ni] * (s.sa[mi] * s.sb_col[ni]) + acc[mi][ni];
-            else acc[mi][ni] = p[mi][ni] * (s.sa[mi] * s.sb_blk) + acc[mi][ni];
-        }
-}
-
-// lane holds C[m][n .. n+3] for each (mi, ni)
-template <int OUT_FP32>
-__device__ __forceinline__ void store_tile(const GemmArgs& args, const Tile& t, const v4f (&acc)[4][4], int wm,
-                                           int lane, int64_t n0, int n_lane) {
-    const int64_t N = args.N;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        const int64_t m = t.m0 + wm * 64 + mi * 16 + (lane & 15);
-        if (m >= t.rows_valid) continue;
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 16;
-            const v4f v = acc[mi][ni];
-            if (OUT_FP32) {
-                st<v4f>(static_cast<float*>(args.c) + idx, v);
-            } else {
-                const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-                const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-                st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
-            }
-        }
-    }
-}
-
-// Global-load assignment shared by both engines: thread tid copies 16 bytes
-// (16 consecutive k) of rows tid/8 + 32*i, i = 0..3, from A and from B.
-struct Loader {
-    const uint8_t* a_src[4];
-    const uint8_t* b_src[4];
-    int row[4];
-    int chunk;
-};
-
-__device__ __forceinline__ Loader make_loader(const Tile& t, int tid, int64_t K, int64_t n0) {
-    Loader L;
-    L.chunk = tid & 7;
+__device__ __forceinline__ Copier make_copier(const Tile& t, int wave, int lane, int64_t K, int64_t N, int64_t n0) {
+    Copier c;
+    const int sub = lane >> 3;            // row within an 8-row piece
+    const int slot = lane & 7;            // 16-byte slot within the row (as stored)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        int64_t ar = t.m0 + r;
-        if (ar >= t.rows_valid) ar = t.rows_valid - 1;     // clamp: loaded, never stored
-        L.a_src[i] = t.A + ar * K + L.chunk * 16;
-        L.b_src[i] = t.B + (n0 + r) * K + L.chunk * 16;
-        L.row[i] = r;
+        const int r0 = (wave * 4 + i) * 8, r = r0 + sub;
+        const int chunk = slot ^ ((r >> 1) & 7);
+        int64_t row = t.m0 + r;
+        if (row >= t.rows_valid) row = t.rows_valid - 1;      // clamp: loaded, never stored
+        c.a_row[i] = t.A + row * K + chunk * 16;
+        c.a_lds[i] = int(offsetof(Stage, a)) + r0 * BK;
     }
-    return L;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r0 = (wave * 2 + i) * 8, r = r0 + sub;
+        const int chunk = slot ^ ((r >> 1) & 7);
+        c.b_row[i] = t.B + (n0 + r) * K + chunk * 16;
+        c.b_lds[i] = int(offsetof(Stage, b)) + r0 * BK;
+    }
+    if (wave < 4) {
+        int64_t row = t.m0 + wave * 64 + lane;
+        if (row >= t.rows_valid) row = t.rows_valid - 1;
+        c.s_src = t.SA + row;
+        c.s_stride = t.lda_s;
+        c.s_lds = int(offsetof(Stage, sa)) + wave * 64 * 4;
+    } else if (BSCALE_1x128 && wave < 6) {
+        c.s_src = t.SB + n0 + (wave - 4) * 64 + lane;
+        c.s_stride = N;
+        c.s_lds = int(offsetof(Stage, sb)) + (wave - 4) * 64 * 4;
+    } else if (!BSCALE_1x128 && wave == 4) {
+        c.s_src = t.SB + int64_t(t.bn) * (K / BK);
+        c.s_stride = 1;
+        c.s_lds = int(offsetof(Stage, sb));
+    } else {
+        c.s_src = t.SA + (t.rows_valid - 1);
+        c.s_stride = t.lda_s;
+        c.s_lds = int(offsetof(Stage, dummy));
+    }
+    return c;
 }
 
-// ===========================================================================
-// Engine "exact": BF16 MFMA on exactly widened FP8 codes.
-//
-// LDS tile row = 128 k x 2 bytes = 16 chunks of 16 bytes (8 bf16 each); chunk
-// c of row r lives at r*256 + ((c ^ (r & 15)) << 4).  MFMA fragment for k-step
-// ks (32 k): lane l reads chunk 4*ks + l/16 of row row0 + l%16.
-__device__ __forceinline__ int xoff(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+__device__ __forceinline__ void copy_kblock(const Copier& c, uint8_t* stage, int64_t kb) {
+    const int64_t koff = kb * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(c.a_row[i] + koff, (lds_ptr_t)(stage + c.a_lds[i]), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(c.b_row[i] + koff, (lds_ptr_t)(stage + c.b_lds[i]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(c.s_src + kb * c.s_stride, (lds_ptr_t)(stage + c.s_lds), 4, 0, 0);
+}
 
+// ---------------------------------------------------------------------------
 // bytes 0,1 (HI = false) or 2,3 (HI = true) of w -> two BF16 values, exactly
 template <bool HI>
 __device__ __forceinline__ uint32_t bf16x2_of_fp8(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.0f, HI));
 }
 
-// 16 FP8 codes -> 16 BF16 values (two 16-byte LDS chunks)
-__device__ __forceinline__ void widen16(u32x4 in, u32x4& lo, u32x4& hi) {
-    lo = u32x4{bf16x2_of_fp8<false>(in[0]), bf16x2_of_fp8<true>(in[0]),
-               bf16x2_of_fp8<false>(in[1]), bf16x2_of_fp8<true>(in[1])};
-    hi = u32x4{bf16x2_of_fp8<false>(in[2]), bf16x2_of_fp8<true>(in[2]),
-               bf16x2_of_fp8<false>(in[3]), bf16x2_of_fp8<true>(in[3])};
+// 8 FP8 codes (two words) -> 8 BF16 values, an MFMA operand
+__device__ __forceinline__ v8bf widen8(uint32_t w0, uint32_t w1) {
+    const u32x4 v{bf16x2_of_fp8<false>(w0), bf16x2_of_fp8<true>(w0), bf16x2_of_fp8<false>(w1),
+                  bf16x2_of_fp8<true>(w1)};
+    return __builtin_bit_cast(v8bf, v);
 }
 
-__device__ __forceinline__ v8bf read_frag_bf16(const uint8_t* tile, int row0, int ks, int lane) {
-    const int row = row0 + (lane & 15);
-    return ld<v8bf>(tile + xoff(row, ks * 4 + (lane >> 4)));
+__device__ __forceinline__ u32x4 read_chunk(const uint8_t* tile, int row, int chunk) {
+    return ld<u32x4>(tile + swz(row, chunk));
 }
 
-template <int BSCALE_1x128, int OUT_FP32, int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_exact_kernel(GemmArgs args) {
-    constexpr int kTile = BM * BK * 2;                       // bytes of one bf16 operand tile
-    __shared__ __align__(16) uint8_t lds[2][2][kTile];        // [buffer][A, B]
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t N = args.N, K = args.K, kbs = K / BK;
-    const Tile t = map_tile<MODE>(args, blockIdx.x);
-    if (!t.live) return;
-    const int64_t n0 = int64_t(t.bn) * BN;
-    const Loader L = make_loader(t, tid, K, n0);
-    int st_off[4][2];
+// P_kb for the wave's 2 x 2 MFMA tiles from one stage.
+template <int ENGINE>
+__device__ __forceinline__ void kblock_partials(const uint8_t* ta, const uint8_t* tb, int lane, v16f (&p)[2][2]) {
+    const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        st_off[i][0] = xoff(L.row[i], 2 * L.chunk);
-        st_off[i][1] = xoff(L.row[i], 2 * L.chunk + 1);
-    }
-    int64_t sa_row[4];
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        const int64_t r = t.m0 + wm * 64 + mi * 16 + (lane & 15);
-        sa_row[mi] = r < t.rows_valid ? r : t.rows_valid - 1;
-    }
-    const int n_lane = wn * 64 + (lane >> 4) * 4;
-    // a wave whose 64 rows are all past the valid rows skips its MFMAs
-    const bool wave_live = t.m0 + wm * 64 < t.rows_valid;
-
-    u32x4 ra[4], rb[4];
+        for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ra[i] = ld<u32x4>(L.a_src[i]);
-        rb[i] = ld<u32x4>(L.b_src[i]);
-    }
+            for (int i = 0; i < 16; ++i) p[mi][ni][i] = 0.f;
+    if (ENGINE == 0) {
+        // four chunk columns j: chunk 2j + h holds k = 32j + 16h .. +15; its
+        // first 8 bytes feed k-step 2j, the last 8 bytes k-step 2j + 1
+        u32x4 fa[2], fb[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        u32x4 lo, hi;
-        widen16(ra[i], lo, hi);
-        st<u32x4>(&lds[0][0][st_off[i][0]], lo);
-        st<u32x4>(&lds[0][0][st_off[i][1]], hi);
-        widen16(rb[i], lo, hi);
-        st<u32x4>(&lds[0][1][st_off[i][0]], lo);
-        st<u32x4>(&lds[0][1][st_off[i][1]], hi);
-    }
-    __syncthreads();
-
-    v4f acc[4][4];
+        for (int mi = 0; mi < 2; ++mi) fa[mi] = read_chunk(ta, mi * 32 + r, h);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+        for (int ni = 0; ni < 2; ++ni) fb[ni] = read_chunk(tb, ni * 32 + r, h);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    for (int64_t kb = 0; kb < kbs; ++kb) {
-        const int cur = int(kb & 1);
-        const int64_t koff = (kb + 1 < kbs ? kb + 1 : kb) * BK;
+        for (int j = 0; j < 4; ++j) {
+            u32x4 na[2], nb[2];
+            if (j + 1 < 4) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = ld<u32x4>(L.a_src[i] + koff);
-            rb[i] = ld<u32x4>(L.b_src[i] + koff);
-        }
-        const Scales<BSCALE_1x128> sc = load_scales<BSCALE_1x128>(t, sa_row, kb, kbs, N, n0, n_lane);
-        if (wave_live) {
-            const uint8_t* ta = lds[cur][0];
-            const uint8_t* tb = lds[cur][1];
-            v4f p[4][4];
+                for (int mi = 0; mi < 2; ++mi) na[mi] = read_chunk(ta, mi * 32 + r, 2 * (j + 1) + h);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) p[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                v8bf af[4], bf[4];
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi) af[mi] = read_frag_bf16(ta, wm * 64 + mi * 16, ks, lane);
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) bf[ni] = read_frag_bf16(tb, wn * 64 + ni * 16, ks, lane);
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni)
-                        p[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[ni], af[mi], p[mi][ni], 0, 0, 0);
+                for (int ni = 0; ni < 2; ++ni) nb[ni] = read_chunk(tb, ni * 32 + r, 2 * (j + 1) + h);
             }
-            fold<BSCALE_1x128>(acc, p, sc);
-        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            u32x4 lo, hi;
-            widen16(ra[i], lo, hi);
-            st<u32x4>(&lds[cur ^ 1][0][st_off[i][0]], lo);
-            st<u32x4>(&lds[cur ^ 1][0][st_off[i][1]], hi);
-            widen16(rb[i], lo, hi);
-            st<u32x4>(&lds[cur ^ 1][1][st_off[i][0]], lo);
-            st<u32x4>(&lds[cur ^ 1][1][st_off[i][1]], hi);
+            for (int half = 0; half < 2; ++half) {
+                v8bf a8[2], b8[2];
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi) a8[mi] = widen8(fa[mi][2 * half], fa[mi][2 * half + 1]);
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) b8[ni] = widen8(fb[ni][2 * half], fb[ni][2 * half + 1]);
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+                        p[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8[ni], a8[mi], p[mi][ni], 0, 0, 0);
+            }
+            if (j + 1 < 4) {
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi) fa[mi] = na[mi];
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) fb[ni] = nb[ni];
+            }
         }
-        __syncthreads();
+    } else {
+        // two k-steps q of 64: lane supplies chunks 4q + 2h and 4q + 2h + 1
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            v8i a8[2], b8[2];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) {
+                const u32x4 lo = read_chunk(ta, mi * 32 + r, 4 * q + 2 * h);
+                const u32x4 hi = read_chunk(ta, mi * 32 + r, 4 * q + 2 * h + 1);
+                a8[mi] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+            }
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                const u32x4 lo = read_chunk(tb, ni * 32 + r, 4 * q + 2 * h);
+                const u32x4 hi = read_chunk(tb, ni * 32 + r, 4 * q + 2 * h + 1);
+                b8[ni] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+            }
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    // formats 0/0 = E4M3 x E4M3; zero scale operands select the
+                    // plain (unscaled) instruction
+                    p[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8[ni], a8[mi], p[mi][ni], 0, 0, 0,
+                                                                                0, 0, 0);
+        }
     }
-    if (wave_live) store_tile<OUT_FP32>(args, t, acc, wm, lane, n0, n_lane);
 }
 
-// ===========================================================================
-// Engine "fp8mfma": one FP8 MFMA per K-block.
-//
-// LDS tile row = 128 bytes = 8 chunks of 16; chunk c of row r lives at
-// r*128 + ((c ^ (r & 7)) << 4).  Fragment: rows row0 + lane%16, 32 bytes from
-// byte 32*(lane/16) of the K-block; A and B use the same byte mapping, so the
-// instruction's own (lane, byte) -> k assignment is shared by both operands.
-__device__ __forceinline__ int foff(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
-
-__device__ __forceinline__ v8i read_frag_fp8(const uint8_t* tile, int row0, int lane) {
-    const int row = row0 + (lane & 15);
-    const int ch = (lane >> 4) * 2;
-    const u32x4 lo = ld<u32x4>(tile + foff(row, ch));
-    const u32x4 hi = ld<u32x4>(tile + foff(row, ch + 1));
-    return v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
-}
-
-__device__ __forceinline__ v4f mfma_fp8_kblock(v8i bfrag, v8i afrag) {
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    // operand formats 0/0 = E4M3 x E4M3; zero scale operands select the plain
-    // (unscaled) instruction
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfrag, afrag, zero, 0, 0, 0, 0, 0, 0);
-}
-
-template <int BSCALE_1x128, int OUT_FP32, int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_fp8mfma_kernel(GemmArgs args) {
-    constexpr int kTile = BM * BK;
-    __shared__ __align__(16) uint8_t lds[2][2][kTile];
+template <int ENGINE, int BSCALE_1x128, int OUT_FP32, int MODE>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args) {
+    __shared__ Stage ring[kStages];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -360,78 +322,92 @@ void gemm_fp8mfma_kernel(GemmArgs args) {
     const Tile t = map_tile<MODE>(args, blockIdx.x);
     if (!t.live) return;
     const int64_t n0 = int64_t(t.bn) * BN;
-    const Loader L = make_loader(t, tid, K, n0);
-    int st_off[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st_off[i] = foff(L.row[i], L.chunk);
-    int64_t sa_row[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        const int64_t r = t.m0 + wm * 64 + mi * 16 + (lane & 15);
-        sa_row[mi] = r < t.rows_valid ? r : t.rows_valid - 1;
-    }
-    const int n_lane = wn * 64 + (lane >> 4) * 4;
+    const Copier cp = make_copier<BSCALE_1x128>(t, wave, lane, K, N, n0);
     const bool wave_live = t.m0 + wm * 64 < t.rows_valid;
+    const int n_lane = wn * 64 + 4 * (lane >> 5);    // + ni*32 + 8*j: first n of each run of four
 
-    u32x4 ra[4], rb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ra[i] = ld<u32x4>(L.a_src[i]);
-        rb[i] = ld<u32x4>(L.b_src[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        st<u32x4>(&lds[0][0][st_off[i]], ra[i]);
-        st<u32x4>(&lds[0][1][st_off[i]], rb[i]);
-    }
-    __syncthreads();
+    copy_kblock(cp, reinterpret_cast<uint8_t*>(&ring[0]), 0);
+    if (kbs > 1) copy_kblock(cp, reinterpret_cast<uint8_t*>(&ring[1]), 1);
 
-    v4f acc[4][4];
+    v16f acc[2][2];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
 
+    int cur = 0;
     for (int64_t kb = 0; kb < kbs; ++kb) {
-        const int cur = int(kb & 1);
-        const int64_t koff = (kb + 1 < kbs ? kb + 1 : kb) * BK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = ld<u32x4>(L.a_src[i] + koff);
-            rb[i] = ld<u32x4>(L.b_src[i] + koff);
+        // this wave's copy of K-block kb has landed once at most the seven
+        // loads of K-block kb+1 are outstanding; the barrier extends that to
+        // every wave and also retires all reads of the stage refilled below
+        if (kb + 1 < kbs) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        if (kb + 2 < kbs) {
+            const int nxt = cur == 0 ? 2 : cur - 1;        // (kb + 2) % 3
+            copy_kblock(cp, reinterpret_cast<uint8_t*>(&ring[nxt]), kb + 2);
         }
-        const Scales<BSCALE_1x128> sc = load_scales<BSCALE_1x128>(t, sa_row, kb, kbs, N, n0, n_lane);
+        const Stage& sg = ring[cur];
         if (wave_live) {
-            const uint8_t* ta = lds[cur][0];
-            const uint8_t* tb = lds[cur][1];
-            v8i af[4], bf[4];
+            v16f p[2][2];
+            kblock_partials<ENGINE>(sg.a + wm * 64 * BK, sg.b + wn * 64 * BK, lane, p);
+            float sa[2];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) af[mi] = read_frag_fp8(ta, wm * 64 + mi * 16, lane);
+            for (int mi = 0; mi < 2; ++mi) sa[mi] = sg.sa[wm * 64 + mi * 32 + (lane & 31)];
+            if (BSCALE_1x128) {
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) bf[ni] = read_frag_fp8(tb, wn * 64 + ni * 16, lane);
-            v4f p[4][4];
+                for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
+                    for (int j = 0; j < 4; ++j) {
+                        const v4f sbv = ld<v4f>(&sg.sb[n_lane + ni * 32 + 8 * j]);
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi) p[mi][ni] = mfma_fp8_kblock(bf[ni], af[mi]);
-            fold<BSCALE_1x128>(acc, p, sc);
+                        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                acc[mi][ni][4 * j + e] = fmaf(p[mi][ni][4 * j + e], sa[mi] * sbv[e], acc[mi][ni][4 * j + e]);
+                    }
+            } else {
+                const float sb = sg.sb[0];
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi) {
+                    const float sc = sa[mi] * sb;
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) acc[mi][ni][i] = fmaf(p[mi][ni][i], sc, acc[mi][ni][i]);
+                }
+            }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            st<u32x4>(&lds[cur ^ 1][0][st_off[i]], ra[i]);
-            st<u32x4>(&lds[cur ^ 1][1][st_off[i]], rb[i]);
-        }
-        __syncthreads();
+        cur = cur == 2 ? 0 : cur + 1;
     }
-    if (wave_live) store_tile<OUT_FP32>(args, t, acc, wm, lane, n0, n_lane);
+    if (!wave_live) return;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const int64_t m = t.m0 + wm * 64 + mi * 32 + (lane & 31);
+        if (m >= t.rows_valid) continue;
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
+                const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
+                                  acc[mi][ni][4 * j + 3]};
+                if (OUT_FP32) {
+                    st<v4f>(static_cast<float*>(args.c) + idx, v);
+                } else {
+                    const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+                    const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+                    st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
+                }
+            }
+    }
 }
 
 template <int ENGINE, int BS, int OF, int MODE>
 hipError_t launch_one(const GemmArgs& args, int64_t tiles, hipStream_t stream) {
-    if (ENGINE == 0)
-        hipLaunchKernelGGL((gemm_exact_kernel<BS, OF, MODE>), dim3(unsigned(tiles)), dim3(kThreads), 0, stream, args);
-    else
-        hipLaunchKernelGGL((gemm_fp8mfma_kernel<BS, OF, MODE>), dim3(unsigned(tiles)), dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((gemm_kernel<ENGINE, BS, OF, MODE>), dim3(unsigned(tiles)), dim3(kThreads), 0, stream, args);
     return hipGetLastError();
 }
 
@@ -468,6 +444,7 @@ hipError_t launch_gemm(GemmMode mode, int bscale_1x128, int out_fp32, const Gemm
     const int64_t n_tiles = args.N / BN;
     int64_t tiles;
     if (mode == GemmMode::Masked) tiles = args.G * ((args.M + BM - 1) / BM) * n_tiles;
+    else if (mode == GemmMode::Contig) tiles = (args.M / BM + args.G) * n_tiles;
     else tiles = ((args.M + BM - 1) / BM) * n_tiles;
     if (tiles == 0) return hipSuccess;
     if (engine_from_env() == 1) return dispatch<1>(mode, bscale_1x128, out_fp32, args, tiles, stream);
