@@ -75,14 +75,39 @@ __device__ __forceinline__ float abs_max4(v4f v) {
     return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 }
 
-// Codes of x / s for a group with scale s (s == 0 only for an all-zero group,
-// whose elements are signed zeros and encode as such).
-__device__ __forceinline__ uint32_t encode4(v4f v, float s) {
-    if (s == 0.0f) {
-        return pack4(e4m3_from_f32(v[0]), e4m3_from_f32(v[1]), e4m3_from_f32(v[2]), e4m3_from_f32(v[3]));
+// Four E4M3 codes (RNE, saturating) of four floats, packed little-endian, by
+// the hardware conversion.  v_cvt_pk_fp8_f32 was compared with e4m3_from_f32
+// above on every 32-bit pattern whose value is finite with |y| <= 464 and
+// agreed on all of them (signed zeros, subnormals, ties, saturation); the
+// quantizers only ever convert |y| <= 448 * (1 + 2^-23).
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true));
+}
+
+// Codes of RN32(x / s) for four elements of one group, bit for bit, with
+// r = RN32(1 / s) computed once per group (r is +inf only when s is
+// subnormal enough for 1/s to overflow; s == 0 only for an all-zero group).
+//
+// y' = RN32(x * r) differs from x / s by less than 2^-23 |y'|, and RN32(x / s)
+// lies within half an ulp of x / s, so both lie inside
+// [y' - 2^-21 |y'|, y' + 2^-21 |y'|] (the bracket ends' own rounding costs less
+// than an ulp of the 4 ulps of margin).  Rounding to E4M3 is monotone, so when
+// both ends of the bracket give the same code every value inside -- RN32(x/s)
+// included -- has that code.  Otherwise (the bracket straddles a rounding
+// boundary: about 2^-16 of elements) the IEEE quotient is computed.
+__device__ __forceinline__ uint32_t encode4(v4f x, float s, float r) {
+    if (s == 0.0f) return cvt4(x[0], x[1], x[2], x[3]);       // signed zeros
+    if (r < __builtin_inff()) {
+        const v4f y = x * r;
+        constexpr float e = 0x1p-21f;
+        const uint32_t lo = cvt4(__builtin_fmaf(-__builtin_fabsf(y[0]), e, y[0]), __builtin_fmaf(-__builtin_fabsf(y[1]), e, y[1]),
+                                 __builtin_fmaf(-__builtin_fabsf(y[2]), e, y[2]), __builtin_fmaf(-__builtin_fabsf(y[3]), e, y[3]));
+        const uint32_t hi = cvt4(__builtin_fmaf(__builtin_fabsf(y[0]), e, y[0]), __builtin_fmaf(__builtin_fabsf(y[1]), e, y[1]),
+                                 __builtin_fmaf(__builtin_fabsf(y[2]), e, y[2]), __builtin_fmaf(__builtin_fabsf(y[3]), e, y[3]));
+        if (lo == hi) return lo;
     }
-    return pack4(e4m3_from_f32(v[0] / s), e4m3_from_f32(v[1] / s),
-                 e4m3_from_f32(v[2] / s), e4m3_from_f32(v[3] / s));
+    return cvt4(x[0] / s, x[1] / s, x[2] / s, x[3] / s);
 }
 
 }  // namespace fp8fg

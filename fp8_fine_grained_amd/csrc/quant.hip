@@ -5,8 +5,10 @@
 // max-abs); DeepSeek-V3 FP8 knowledge-base page (codingmall.com), section on
 // online quantization (scales computed from the current data).  Per group:
 //   amax = max|x|,  s = RN32(amax / 448),  code = E4M3_RNE_SAT(RN32(x / s)).
-// Both divisions are IEEE fp32 divisions (the compiler's correctly rounded
-// sequence), so every byte and scale is reproducible bit for bit.
+// The scale is an IEEE fp32 division; the per-element quotient RN32(x / s)
+// is never formed in the common case: encode4() proves from x * RN32(1/s)
+// which E4M3 code it rounds to and divides only when that cannot be decided,
+// so every byte and scale is reproducible bit for bit.
 //
 // All three kernels are HBM-bound: 4 bytes read and 1 byte written per
 // element, plus 4 bytes of scale per group.
@@ -16,40 +18,32 @@
 namespace fp8fg {
 
 // ---------------------------------------------------------------------------
-// 1x128 tiles along K.  Row-major x [M][K] with K % 128 == 0 is a flat
-// sequence of tiles: tile t = m * (K/128) + kb starts at element t * 128, and
-// so do its codes.  A half-wave (32 lanes x float4) owns one tile at a time;
-// each half-wave takes U consecutive tiles per pass so that U independent
-// 16-byte loads per lane are in flight before the first reduction.
-// Scales go to s[kb][m].
+// 1x128 tiles along K.  A workgroup of eight half-waves (32 lanes x float4
+// each) owns eight rows and U consecutive K-blocks of them: half-wave h takes
+// row blockIdx.y*8 + h (grid-strided over rows) and tiles kb0 .. kb0+U-1 with
+// kb0 = blockIdx.x*U, so U independent 16-byte loads per lane are in flight
+// before the first reduction and no index needs a division.  Scales go to
+// s[kb][m].
 template <int U>
-__global__ __launch_bounds__(256) void quant_act_rows_kernel(const float* __restrict__ x, int64_t M,
-                                                             int64_t kbs, uint8_t* __restrict__ q,
-                                                             float* __restrict__ s) {
-    const int64_t ntiles = M * kbs;
+__global__ __launch_bounds__(256) void quant_act_rows_kernel(const float* __restrict__ x, int64_t M, int64_t K,
+                                                             uint8_t* __restrict__ q, float* __restrict__ s) {
     const int lane = threadIdx.x & 31;
-    const int64_t hw = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 5;
-    const int64_t nhw = (int64_t(gridDim.x) * blockDim.x) >> 5;
-    for (int64_t base = hw * U; base < ntiles; base += nhw * U) {
+    const int64_t kbs = K / kBlock;
+    const int64_t kb0 = int64_t(blockIdx.x) * U;
+    for (int64_t m = int64_t(blockIdx.y) * 8 + (threadIdx.x >> 5); m < M; m += int64_t(gridDim.y) * 8) {
+        const float* xr = x + m * K + kb0 * kBlock + lane * 4;
+        uint8_t* qr = q + m * K + kb0 * kBlock + lane * 4;
         v4f v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t t = base + u;
-            v[u] = t < ntiles ? ld<v4f>(x + t * kBlock + lane * 4) : v4f{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int u = 0; u < U; ++u) v[u] = kb0 + u < kbs ? ld<v4f>(xr + u * kBlock) : v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t t = base + u;
+            if (kb0 + u >= kbs) break;
             const float amax = halfwave_max(abs_max4(v[u]));
             const float sc = amax / 448.0f;
-            const uint32_t codes = encode4(v[u], sc);
-            if (t < ntiles) {
-                *reinterpret_cast<uint32_t*>(q + t * kBlock + lane * 4) = codes;
-                if (lane == 0) {
-                    const int64_t m = t / kbs, kb = t - m * kbs;
-                    s[kb * M + m] = sc;
-                }
-            }
+            const float rc = 1.0f / sc;
+            st<uint32_t>(qr + u * kBlock, encode4(v[u], sc, rc));
+            if (lane == 0) s[(kb0 + u) * M + m] = sc;
         }
     }
 }
@@ -104,12 +98,13 @@ __global__ __launch_bounds__(256) void quant_act_tokens_kernel(const float* __re
     __syncthreads();
     amax = fmaxf(fmaxf(part[0][c], part[1][c]), fmaxf(part[2][c], part[3][c]));
     const float sc = amax / 448.0f;
+    const float rc = 1.0f / sc;
     const int64_t k = k0 + c;
     if (k < K) {
         uint32_t w[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            w[i] = encode4(v4f{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]}, sc);
+            w[i] = encode4(v4f{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]}, sc, rc);
         uint8_t* dst = q + k * M + mb * kBlock + quarter * 32;
         st<u32x4>(dst, u32x4{w[0], w[1], w[2], w[3]});
         st<u32x4>(dst + 16, u32x4{w[4], w[5], w[6], w[7]});
@@ -146,18 +141,19 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restri
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float sc = amax / 448.0f;
+    const float rc = 1.0f / sc;
     if (!transpose_out) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int64_t row = nb * kBlock + r0 + 8 * i;
-            *reinterpret_cast<uint32_t*>(q + row * K + kb * kBlock + c4) = encode4(v[i], sc);
+            *reinterpret_cast<uint32_t*>(q + row * K + kb * kBlock + c4) = encode4(v[i], sc, rc);
         }
         if (t == 0) s[nb * (K / kBlock) + kb] = sc;
         return;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const uint32_t cw = encode4(v[i], sc);
+        const uint32_t cw = encode4(v[i], sc, rc);
         const int r = r0 + 8 * i;
 #pragma unroll
         for (int j = 0; j < 4; ++j) qt[c4 + j][r] = uint8_t(cw >> (8 * j));
@@ -178,12 +174,11 @@ hipError_t launch_quant_act(const float* x, int64_t M, int64_t K, int transpose_
                             float* s, hipStream_t stream) {
     if (!transpose_out) {
         constexpr int U = 4;
-        const int64_t ntiles = M * (K / kBlock);
-        const int64_t per_block = 8 * U;               // 8 half-waves per 256-thread block
-        int64_t blocks = (ntiles + per_block - 1) / per_block;
-        if (blocks > 65536) blocks = 65536;
-        hipLaunchKernelGGL(quant_act_rows_kernel<U>, dim3(unsigned(blocks)), dim3(256), 0, stream, x, M,
-                           K / kBlock, q, s);
+        const int64_t chunks = (K / kBlock + U - 1) / U;
+        int64_t row_groups = (M + 7) / 8;
+        if (row_groups > 65535) row_groups = 65535;      // the kernel strides over the rest
+        hipLaunchKernelGGL(quant_act_rows_kernel<U>, dim3(unsigned(chunks), unsigned(row_groups)), dim3(256), 0,
+                           stream, x, M, K, q, s);
     } else {
         const dim3 grid(unsigned(M / kBlock), unsigned((K + kTokCh - 1) / kTokCh));
         hipLaunchKernelGGL(quant_act_tokens_kernel, grid, dim3(256), 0, stream, x, M, K, q, s);
