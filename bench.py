@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--sets", type=int, default=4, help="rotating input sets")
     p.add_argument("--cpu-rows", type=int, default=512, help="rows of the oracle's timed sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--workload", default="dense_fprop",
+                   choices=["dense_fprop", "dense_small", "linear_trio", "moe_contig", "moe_masked"],
+                   help="dense_fprop is the headline step; the others print one line per measured kernel")
     return p.parse_args()
 
 
@@ -86,11 +89,159 @@ def cpu_baseline(x, w, rows):
                       f"(128x128 quantization), float64 GEMM and |A||B| on those rows; {dt:.2f} s"}
 
 
+def time_launches(fn, steps, warmup, stream):
+    """Average duration (ms) of fn() from HIP events recorded around each
+    launch on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def extra_line(workload, kernel, ms, flops=None, nbytes=None, args=None, config=None):
+    line = {"metric": METRIC if flops else "HBM GB/s of " + kernel, "workload": workload, "kernel": kernel,
+            "us": round(ms * 1e3, 2), "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "data": "synthetic, seeded (drawn on the GPU)", "config": config or {}}
+    if flops:
+        tf = flops / (ms * 1e-3) / 1e12
+        line.update({"value": round(tf, 2), "unit": "TFLOPS",
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                  "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2)}})
+    if nbytes:
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        line.setdefault("value", round(gbs, 1))
+        line.setdefault("unit", "GB/s")
+        line["hbm"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": int(nbytes)}
+    print(json.dumps(line), flush=True)
+
+
+def gpu_acts(gen, rows, K, frac, mult, sigma=1.0):
+    """N(0, sigma) activations with whole outlier channels, drawn on the GPU."""
+    import torch
+    x = torch.randn((rows, K), generator=gen, device="cuda") * sigma
+    if frac > 0:
+        n = max(1, int(round(frac * K)))
+        idx = torch.randperm(K, generator=gen, device="cuda")[:n]
+        x[:, idx] *= mult
+    return x
+
+
+def run_extra(args):
+    import torch
+    import fp8_fine_grained_amd as fp8
+    import workloads
+    fp8.load_library()
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda").manual_seed(workloads.SEEDS.get(args.workload, 1))
+    T, W = args.steps, args.warmup
+    if args.workload == "dense_small":
+        M, N, K = 128, 256, 512
+        x = gpu_acts(gen, M, K, 0.005, 50.0)
+        w = torch.randn((N, K), generator=gen, device="cuda") * 0.02
+        qa, sa = fp8.fp8_quant_act_1x128(x)
+        qb, sb = fp8.fp8_quant_weight_128x128(w)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled(qa, sa, qb, sb, 0, torch.bfloat16, out=c), T, W, stream)
+        extra_line("dense_small 128x256x512", "gemm_blockscaled", ms, flops=2.0 * M * N * K, args=args,
+                   config={"M": M, "N": N, "K": K, "note": "launch-latency bound"})
+    elif args.workload == "linear_trio":
+        TOK, IN, OUT = 8192, 7168, 2048
+        x = gpu_acts(gen, TOK, IN, 0.001, 100.0)
+        w = torch.randn((OUT, IN), generator=gen, device="cuda") * 0.02
+        dy = torch.randn((TOK, OUT), generator=gen, device="cuda") * 1e-3
+        qx, sx = fp8.fp8_quant_act_1x128(x)
+        qw, sw = fp8.fp8_quant_weight_128x128(w)
+        qwt, swt = fp8.fp8_quant_weight_128x128(w, transpose_out=True)
+        qd, sd = fp8.fp8_quant_act_1x128(dy)
+        qdt, sdt = fp8.fp8_quant_act_1x128(dy, transpose_out=True)
+        qxt, sxt = fp8.fp8_quant_act_1x128(x, transpose_out=True)
+        cfg = {"tokens": TOK, "in": IN, "out": OUT}
+        for name, src, tr in (("quant_act_1x128 X rowwise", x, False), ("quant_act_1x128 X token-wise", x, True),
+                              ("quant_act_1x128 dY rowwise", dy, False), ("quant_act_1x128 dY token-wise", dy, True)):
+            ms = time_launches(lambda i, src=src, tr=tr: fp8.fp8_quant_act_1x128(src, transpose_out=tr), T, W, stream)
+            n = src.numel()
+            extra_line("linear_trio", name, ms, nbytes=n * 5 + (n // 128) * 4, args=args, config=cfg)
+        for name, tr in (("quant_weight_128x128 W", False), ("quant_weight_128x128 W transposed", True)):
+            ms = time_launches(lambda i, tr=tr: fp8.fp8_quant_weight_128x128(w, transpose_out=tr), T, W, stream)
+            extra_line("linear_trio", name, ms, nbytes=w.numel() * 5, args=args, config=cfg)
+        yb = torch.empty((TOK, OUT), dtype=torch.bfloat16, device="cuda")
+        dxb = torch.empty((TOK, IN), dtype=torch.bfloat16, device="cuda")
+        dwf = torch.empty((OUT, IN), dtype=torch.float32, device="cuda")
+        fl = 2.0 * TOK * IN * OUT
+        ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled(qx, sx, qw, sw, 0, torch.bfloat16, out=yb), T, W, stream)
+        extra_line("linear_trio", "gemm Fprop 8192x2048x7168 BF16", ms, flops=fl, args=args, config=cfg)
+        ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled(qd, sd, qwt, swt, 0, torch.bfloat16, out=dxb), T, W, stream)
+        extra_line("linear_trio", "gemm Dgrad 8192x7168x2048 BF16", ms, flops=fl, args=args, config=cfg)
+        ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled(qdt, sdt, qxt, sxt, 1, torch.float32, out=dwf), T, W, stream)
+        extra_line("linear_trio", "gemm Wgrad 2048x7168x8192 FP32 (1x128 B)", ms, flops=fl, args=args, config=cfg)
+    elif args.workload == "moe_contig":
+        G, N, K = 32, 4096, 7168
+        counts, off = workloads.moe_contig_layout()
+        mt = int(off[-1])
+        a = torch.zeros((mt, K), device="cuda")
+        xa = gpu_acts(gen, int(counts.sum()), K, 0.001, 100.0)
+        pos = 0
+        for g in range(G):
+            a[int(off[g]):int(off[g]) + int(counts[g])] = xa[pos:pos + int(counts[g])]
+            pos += int(counts[g])
+        del xa
+        qa, sa = fp8.fp8_quant_act_1x128(a)
+        qb = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+        sb = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device="cuda")
+        for g in range(G):
+            wg = torch.randn((N, K), generator=gen, device="cuda") * 0.02
+            fp8.fp8_quant_weight_128x128(wg, q=qb[g], s=sb[g])
+        offs = torch.from_numpy(off.astype(np.int32)).cuda()
+        c = torch.empty((mt, N), dtype=torch.bfloat16, device="cuda")
+        cfg = {"experts": G, "routed_rows": int(counts.sum()), "padded_rows": mt, "N": N, "K": K}
+        ms = time_launches(lambda i: fp8.fp8_quant_act_1x128(a, q=qa, s=sa), T, W, stream)
+        extra_line("moe_contig", "quant_act_1x128 A rows", ms, nbytes=a.numel() * 5 + (a.numel() // 128) * 4,
+                   args=args, config=cfg)
+        ms = time_launches(lambda i: fp8.fp8_grouped_gemm_contiguous(qa, sa, qb, sb, offs, out=c), T, W, stream)
+        extra_line("moe_contig", "grouped_gemm_contiguous gate+up", ms, flops=2.0 * int(counts.sum()) * N * K,
+                   args=args, config=dict(cfg, flops_counted="valid rows only"))
+    elif args.workload == "moe_masked":
+        G, MMAX = 32, 128
+        for (N, K) in ((4096, 7168), (7168, 2048)):
+            mm, _ = workloads.moe_masked_inputs(N, 128, G, MMAX)
+            a = gpu_acts(gen, G * MMAX, K, 0.001, 100.0).reshape(G, MMAX, K).contiguous()
+            qa = torch.empty((G, MMAX, K), dtype=torch.uint8, device="cuda")
+            sa = torch.empty((G, K // 128, MMAX), dtype=torch.float32, device="cuda")
+            for g in range(G):
+                fp8.fp8_quant_act_1x128(a[g], q=qa[g], s=sa[g])
+            qb = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+            sb = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device="cuda")
+            for g in range(G):
+                wg = torch.randn((N, K), generator=gen, device="cuda") * 0.02
+                fp8.fp8_quant_weight_128x128(wg, q=qb[g], s=sb[g])
+            mmt = torch.from_numpy(mm.astype(np.int32)).cuda()
+            c = torch.empty((G, MMAX, N), dtype=torch.bfloat16, device="cuda")
+            valid = int(mm.sum())
+            nbytes = G * N * K + G * (N // 128) * (K // 128) * 4 + valid * K + valid * (K // 128) * 4 + valid * N * 2
+            ms = time_launches(lambda i: fp8.fp8_grouped_gemm_masked(qa, sa, qb, sb, mmt, out=c), T, W, stream)
+            extra_line("moe_masked", f"grouped_gemm_masked N={N} K={K}", ms, nbytes=nbytes, args=args,
+                       config={"experts": G, "M_max": MMAX, "valid_rows": valid, "N": N, "K": K,
+                               "bytes": "all expert weights + scales + valid A rows + valid C rows"})
+            del qb, sb, c
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
         sys.exit(2)
+    if args.workload != "dense_fprop":
+        run_extra(args)
+        return
 
     import torch
     import fp8_fine_grained_amd as fp8

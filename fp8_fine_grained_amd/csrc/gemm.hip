@@ -54,11 +54,32 @@
 
 namespace fp8fg {
 
-namespace {
+namespace gemm_detail {
 
-constexpr int BM = 256, BN = 128, BK = 128;
-constexpr int kThreads = 512;
-constexpr int kStages = 3;
+constexpr int BK = 128;           // K-block = quantization group length
+constexpr int kThreads = 512;     // eight waves
+
+// Tile shape: WAVES_M x WAVES_N waves (8 in all), each owning FM x FN MFMA
+// tiles of 32 x 32.  A workgroup tile is BM x BN.
+template <int WAVES_M_, int WAVES_N_, int FM_, int FN_, int STAGES_ = 3>
+struct Cfg {
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, FM = FM_, FN = FN_, STAGES = STAGES_;
+    static constexpr int BM = WAVES_M * FM * 32, BN = WAVES_N * FN * 32;
+    static constexpr int A_PER_WAVE = BM * BK / 1024 / 8;   // 1 KB direct-to-LDS pieces per wave
+    static constexpr int B_PER_WAVE = BN * BK / 1024 / 8;
+    static constexpr int LOADS_PER_WAVE = A_PER_WAVE + B_PER_WAVE + 1;   // + one scale piece
+    static_assert(WAVES_M * WAVES_N == 8, "eight waves");
+    static_assert(A_PER_WAVE * 8 * 1024 == BM * BK && B_PER_WAVE * 8 * 1024 == BN * BK, "whole pieces per wave");
+    static_assert(BM / 64 + BN / 64 <= 8, "scale pieces fit in eight waves");
+    static_assert(STAGES >= 3 && STAGES <= 6, "ring depth");
+};
+// Dense and contiguous layouts: 256 x 128 tiles, waves 4 x 2 of 64 x 64.
+typedef Cfg<4, 2, 2, 2> BigTile;
+
+// Masked (decode) layout: 64 x 128 tiles, waves 2 x 4 of 32 x 32 -- few
+// valid rows per expert, so the tile is short in m and the weights stream
+// through with an eighth of the big tile's A traffic.
+typedef Cfg<2, 4, 1, 1, 3> DecodeTile;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -66,12 +87,14 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+template <class C>
 struct alignas(16) Stage {
-    uint8_t a[BM * BK];      // FP8 A tile, swizzled rows
-    uint8_t b[BN * BK];      // FP8 B tile, swizzled rows
-    float sa[BM];            // A scales of this K-block for the tile's rows
-    float sb[BN];            // B column scales (1x128 B), or the B block scale x64 (128x128 B)
-    float dummy[64];         // target of the padding scale load (never read)
+    uint8_t a[C::BM * BK];   // FP8 A tile, swizzled rows
+    uint8_t b[C::BN * BK];   // FP8 B tile, swizzled rows
+    float sa[C::BM];         // A scales of this K-block for the tile's rows
+    float sb[C::BN < 128 ? 128 : C::BN];   // B column scales (1x128 B), or per 128-wide n-block
+                                           // 64 copies of its block scale (128x128 B)
+    float dummy[64];         // target of the padding scale loads (never read)
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4); }
@@ -91,8 +114,9 @@ struct Tile {
     bool live;
 };
 
-template <int MODE>
+template <class C, int MODE>
 __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile) {
+    constexpr int BM = C::BM, BN = C::BN;
     Tile t;
     const int n_tiles = int(args.N / BN);
     const int64_t kbs = args.K / BK;
@@ -142,80 +166,89 @@ __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile) {
     if (t.m0 >= t.rows_valid) t.live = false;
     if (MODE != int(GemmMode::Dense)) {
         t.B += g * args.N * args.K;
-        t.SB += g * (args.N / BN) * kbs;
+        t.SB += g * (args.N / 128) * kbs;        // 128x128 scales [G][N/128][K/128]
     }
     return t;
 }
 
 // ---------------------------------------------------------------------------
 // Direct-to-LDS copy of one K-block into a stage.  Every wave issues exactly
-// seven load instructions per K-block (so one vmcnt value fits all waves):
-// four 1 KB pieces of A (8 rows each), two of B, and one 256-byte scale piece
-// -- waves 0-3 the A scales, waves 4-5 the B column scales when B is
-// 1x128-scaled, or wave 4 alone 64 copies of the B block scale when it is
-// 128x128-scaled, the rest a padding load into Stage::dummy.  Keeping every
+// C::LOADS_PER_WAVE load instructions per K-block (so one vmcnt value fits
+// all waves): its 1 KB pieces of A and of B (8 rows each) and one 256-byte
+// scale piece.  Scale pieces: the first BM/64 waves load the A scales; then,
+// when B is 1x128-scaled, BN/64 waves its column scales, or, when it is
+// 128x128-scaled, one wave per 128-wide n-block 64 copies of that block's
+// scale; the remaining waves a padding load into Stage::dummy.  Keeping every
 // scale on this path leaves vmcnt counting nothing but the ring.
+template <class C>
 struct Copier {
-    const uint8_t* a_row[4];   // this lane's A row for each of its four A pieces (+ chunk offset)
-    const uint8_t* b_row[2];
-    int a_lds[4], b_lds[2];    // wave-uniform LDS byte offsets of the pieces
+    const uint8_t* a_row[C::A_PER_WAVE];   // this lane's A row (+ chunk offset) per piece
+    const uint8_t* b_row[C::B_PER_WAVE];
+    int a_lds[C::A_PER_WAVE], b_lds[C::B_PER_WAVE];   // wave-uniform LDS byte offsets
     const float* s_src;        // this lane's scale source for K-block 0
     int64_t s_stride;          // scale source stride between K-blocks
     int s_lds;                 // wave-uniform LDS byte offset of the scale piece
+
+    // issue this wave's loads of K-block kb into `stage`
+    __device__ __forceinline__ void copy(uint8_t* stage, int64_t kb) const {
+        const int64_t koff = kb * BK;
+#pragma unroll
+        for (int i = 0; i < C::A_PER_WAVE; ++i)
+            __builtin_amdgcn_global_load_lds(a_row[i] + koff, (lds_ptr_t)(stage + a_lds[i]), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < C::B_PER_WAVE; ++i)
+            __builtin_amdgcn_global_load_lds(b_row[i] + koff, (lds_ptr_t)(stage + b_lds[i]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(s_src + kb * s_stride, (lds_ptr_t)(stage + s_lds), 4, 0, 0);
+    }
 };
 
-template <int BSCALE_1x128>
-__device__ __forceinline__ Copier make_copier(const Tile& t, int wave, int lane, int64_t K, int64_t N, int64_t n0) {
-    Copier c;
+template <class C, int BSCALE_1x128>
+__device__ __forceinline__ Copier<C> make_copier(const Tile& t, int wave, int lane, int64_t K, int64_t N,
+                                                 int64_t n0) {
+    typedef Stage<C> S;
+    Copier<C> c;
     const int sub = lane >> 3;            // row within an 8-row piece
     const int slot = lane & 7;            // 16-byte slot within the row (as stored)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r0 = (wave * 4 + i) * 8, r = r0 + sub;
+    for (int i = 0; i < C::A_PER_WAVE; ++i) {
+        const int r0 = (wave * C::A_PER_WAVE + i) * 8, r = r0 + sub;
         const int chunk = slot ^ ((r >> 1) & 7);
         int64_t row = t.m0 + r;
         if (row >= t.rows_valid) row = t.rows_valid - 1;      // clamp: loaded, never stored
         c.a_row[i] = t.A + row * K + chunk * 16;
-        c.a_lds[i] = int(offsetof(Stage, a)) + r0 * BK;
+        c.a_lds[i] = int(offsetof(S, a)) + r0 * BK;
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r0 = (wave * 2 + i) * 8, r = r0 + sub;
+    for (int i = 0; i < C::B_PER_WAVE; ++i) {
+        const int r0 = (wave * C::B_PER_WAVE + i) * 8, r = r0 + sub;
         const int chunk = slot ^ ((r >> 1) & 7);
         c.b_row[i] = t.B + (n0 + r) * K + chunk * 16;
-        c.b_lds[i] = int(offsetof(Stage, b)) + r0 * BK;
+        c.b_lds[i] = int(offsetof(S, b)) + r0 * BK;
     }
-    if (wave < 4) {
+    constexpr int a_waves = C::BM / 64;
+    constexpr int b_waves = BSCALE_1x128 ? C::BN / 64 : (C::BN + 127) / 128;
+    if (wave < a_waves) {
         int64_t row = t.m0 + wave * 64 + lane;
         if (row >= t.rows_valid) row = t.rows_valid - 1;
         c.s_src = t.SA + row;
         c.s_stride = t.lda_s;
-        c.s_lds = int(offsetof(Stage, sa)) + wave * 64 * 4;
-    } else if (BSCALE_1x128 && wave < 6) {
-        c.s_src = t.SB + n0 + (wave - 4) * 64 + lane;
-        c.s_stride = N;
-        c.s_lds = int(offsetof(Stage, sb)) + (wave - 4) * 64 * 4;
-    } else if (!BSCALE_1x128 && wave == 4) {
-        c.s_src = t.SB + int64_t(t.bn) * (K / BK);
-        c.s_stride = 1;
-        c.s_lds = int(offsetof(Stage, sb));
+        c.s_lds = int(offsetof(S, sa)) + wave * 64 * 4;
+    } else if (wave < a_waves + b_waves) {
+        const int j = wave - a_waves;
+        if (BSCALE_1x128) {
+            c.s_src = t.SB + n0 + j * 64 + lane;
+            c.s_stride = N;
+        } else {
+            c.s_src = t.SB + (n0 / 128 + j) * (K / BK);
+            c.s_stride = 1;
+        }
+        c.s_lds = int(offsetof(S, sb)) + j * 64 * 4;
     } else {
         c.s_src = t.SA + (t.rows_valid - 1);
         c.s_stride = t.lda_s;
-        c.s_lds = int(offsetof(Stage, dummy));
+        c.s_lds = int(offsetof(S, dummy));
     }
     return c;
-}
-
-__device__ __forceinline__ void copy_kblock(const Copier& c, uint8_t* stage, int64_t kb) {
-    const int64_t koff = kb * BK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds(c.a_row[i] + koff, (lds_ptr_t)(stage + c.a_lds[i]), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(c.b_row[i] + koff, (lds_ptr_t)(stage + c.b_lds[i]), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(c.s_src + kb * c.s_stride, (lds_ptr_t)(stage + c.s_lds), 4, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -236,159 +269,194 @@ __device__ __forceinline__ u32x4 read_chunk(const uint8_t* tile, int row, int ch
     return ld<u32x4>(tile + swz(row, chunk));
 }
 
-// P_kb for the wave's 2 x 2 MFMA tiles from one stage.
-template <int ENGINE>
-__device__ __forceinline__ void kblock_partials(const uint8_t* ta, const uint8_t* tb, int lane, v16f (&p)[2][2]) {
+// P_kb for the wave's FM x FN MFMA tiles from one stage.  `mlive` = number of
+// leading 32-row m-tiles that hold valid rows (the others are skipped).
+template <int ENGINE, int FM, int FN>
+__device__ __forceinline__ void kblock_partials(const uint8_t* ta, const uint8_t* tb, int lane, int mlive,
+                                                v16f (&p)[FM][FN]) {
     const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) p[mi][ni][i] = 0.f;
     if (ENGINE == 0) {
         // four chunk columns j: chunk 2j + h holds k = 32j + 16h .. +15; its
         // first 8 bytes feed k-step 2j, the last 8 bytes k-step 2j + 1
-        u32x4 fa[2], fb[2];
+        u32x4 fa[FM], fb[FN];
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) fa[mi] = read_chunk(ta, mi * 32 + r, h);
+        for (int mi = 0; mi < FM; ++mi) fa[mi] = read_chunk(ta, mi * 32 + r, h);
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) fb[ni] = read_chunk(tb, ni * 32 + r, h);
+        for (int ni = 0; ni < FN; ++ni) fb[ni] = read_chunk(tb, ni * 32 + r, h);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            u32x4 na[2], nb[2];
+            u32x4 na[FM], nb[FN];
             if (j + 1 < 4) {
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi) na[mi] = read_chunk(ta, mi * 32 + r, 2 * (j + 1) + h);
+                for (int mi = 0; mi < FM; ++mi) na[mi] = read_chunk(ta, mi * 32 + r, 2 * (j + 1) + h);
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) nb[ni] = read_chunk(tb, ni * 32 + r, 2 * (j + 1) + h);
+                for (int ni = 0; ni < FN; ++ni) nb[ni] = read_chunk(tb, ni * 32 + r, 2 * (j + 1) + h);
             }
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                v8bf a8[2], b8[2];
+                v8bf a8[FM], b8[FN];
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi) a8[mi] = widen8(fa[mi][2 * half], fa[mi][2 * half + 1]);
+                for (int mi = 0; mi < FM; ++mi) a8[mi] = widen8(fa[mi][2 * half], fa[mi][2 * half + 1]);
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) b8[ni] = widen8(fb[ni][2 * half], fb[ni][2 * half + 1]);
+                for (int ni = 0; ni < FN; ++ni) b8[ni] = widen8(fb[ni][2 * half], fb[ni][2 * half + 1]);
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
+                for (int mi = 0; mi < FM; ++mi) {
+                    if (mi >= mlive) break;
 #pragma unroll
-                    for (int ni = 0; ni < 2; ++ni)
+                    for (int ni = 0; ni < FN; ++ni)
                         p[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8[ni], a8[mi], p[mi][ni], 0, 0, 0);
+                }
             }
             if (j + 1 < 4) {
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi) fa[mi] = na[mi];
+                for (int mi = 0; mi < FM; ++mi) fa[mi] = na[mi];
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) fb[ni] = nb[ni];
+                for (int ni = 0; ni < FN; ++ni) fb[ni] = nb[ni];
             }
         }
     } else {
         // two k-steps q of 64: lane supplies chunks 4q + 2h and 4q + 2h + 1
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            v8i a8[2], b8[2];
+            v8i a8[FM], b8[FN];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) {
+            for (int mi = 0; mi < FM; ++mi) {
                 const u32x4 lo = read_chunk(ta, mi * 32 + r, 4 * q + 2 * h);
                 const u32x4 hi = read_chunk(ta, mi * 32 + r, 4 * q + 2 * h + 1);
                 a8[mi] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
             }
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
+            for (int ni = 0; ni < FN; ++ni) {
                 const u32x4 lo = read_chunk(tb, ni * 32 + r, 4 * q + 2 * h);
                 const u32x4 hi = read_chunk(tb, ni * 32 + r, 4 * q + 2 * h + 1);
                 b8[ni] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
             }
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+            for (int mi = 0; mi < FM; ++mi) {
+                if (mi >= mlive) break;
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
+                for (int ni = 0; ni < FN; ++ni)
                     // formats 0/0 = E4M3 x E4M3; zero scale operands select the
                     // plain (unscaled) instruction
                     p[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8[ni], a8[mi], p[mi][ni], 0, 0, 0,
                                                                                 0, 0, 0);
+            }
         }
     }
 }
 
-template <int ENGINE, int BSCALE_1x128, int OUT_FP32, int MODE>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args) {
-    __shared__ Stage ring[kStages];
+// s_waitcnt vmcnt(N) with N an immediate
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most `later` K-blocks' worth of this wave's copies are outstanding
+template <class C>
+__device__ __forceinline__ void wait_copies(int later) {
+    constexpr int L = C::LOADS_PER_WAVE;
+    switch (later) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<L>(); break;
+        case 2: wait_vmcnt<2 * L>(); break;
+        case 3: wait_vmcnt<3 * L>(); break;
+        default: wait_vmcnt<4 * L>(); break;
+    }
+}
+
+template <int WAVES_M, int WAVES_N, int FM_, int FN_, int STAGES_, int ENGINE, int BSCALE_1x128, int OUT_FP32, int MODE>
+__device__ __forceinline__ void gemm_body(const GemmArgs& args) {
+    typedef Cfg<WAVES_M, WAVES_N, FM_, FN_, STAGES_> C;
+    constexpr int FM = C::FM, FN = C::FN;
+    typedef Stage<C> S;
+    constexpr int STAGES = C::STAGES;
+    __shared__ __align__(16) uint8_t lds_raw[STAGES * sizeof(S)];
+    S* ring = reinterpret_cast<S*>(lds_raw);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int64_t N = args.N, K = args.K, kbs = K / BK;
-    const Tile t = map_tile<MODE>(args, blockIdx.x);
+    const Tile t = map_tile<C, MODE>(args, blockIdx.x);
     if (!t.live) return;
-    const int64_t n0 = int64_t(t.bn) * BN;
-    const Copier cp = make_copier<BSCALE_1x128>(t, wave, lane, K, N, n0);
-    const bool wave_live = t.m0 + wm * 64 < t.rows_valid;
-    const int n_lane = wn * 64 + 4 * (lane >> 5);    // + ni*32 + 8*j: first n of each run of four
+    const int64_t n0 = int64_t(t.bn) * C::BN;
+    const Copier<C> cp = make_copier<C, BSCALE_1x128>(t, wave, lane, K, N, n0);
+    // 32-row m-tiles of this wave that hold valid rows (0 .. FM)
+    const int64_t wrow0 = t.m0 + wm * FM * 32;
+    const int64_t left = t.rows_valid - wrow0;
+    const int mlive = left <= 0 ? 0 : (left >= FM * 32 ? FM : int((left + 31) / 32));
+    const int n_lane = wn * FN * 32 + 4 * (lane >> 5);    // + ni*32 + 8*j: first n of each run of four
 
-    copy_kblock(cp, reinterpret_cast<uint8_t*>(&ring[0]), 0);
-    if (kbs > 1) copy_kblock(cp, reinterpret_cast<uint8_t*>(&ring[1]), 1);
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (st < kbs) cp.copy(reinterpret_cast<uint8_t*>(&ring[st]), st);
 
-    v16f acc[2][2];
+    v16f acc[FM][FN];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
 
     int cur = 0;
     for (int64_t kb = 0; kb < kbs; ++kb) {
-        // this wave's copy of K-block kb has landed once at most the seven
-        // loads of K-block kb+1 are outstanding; the barrier extends that to
-        // every wave and also retires all reads of the stage refilled below
-        if (kb + 1 < kbs) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // this wave's copy of K-block kb has landed once only the loads of the
+        // K-blocks issued after it (up to STAGES-2 of them) are outstanding;
+        // the barrier extends that to every wave and retires all reads of the
+        // stage refilled below
+        const int64_t later = kbs - 1 - kb;
+        wait_copies<C>(int(later < STAGES - 2 ? later : STAGES - 2));
         __builtin_amdgcn_s_barrier();
-        if (kb + 2 < kbs) {
-            const int nxt = cur == 0 ? 2 : cur - 1;        // (kb + 2) % 3
-            copy_kblock(cp, reinterpret_cast<uint8_t*>(&ring[nxt]), kb + 2);
+        if (kb + STAGES - 1 < kbs) {
+            const int nxt = cur == 0 ? STAGES - 1 : cur - 1;        // (kb + STAGES - 1) % STAGES
+            cp.copy(reinterpret_cast<uint8_t*>(&ring[nxt]), kb + STAGES - 1);
         }
-        const Stage& sg = ring[cur];
-        if (wave_live) {
-            v16f p[2][2];
-            kblock_partials<ENGINE>(sg.a + wm * 64 * BK, sg.b + wn * 64 * BK, lane, p);
-            float sa[2];
+        const S& sg = ring[cur];
+        if (mlive > 0) {
+            v16f p[FM][FN];
+            kblock_partials<ENGINE, FM, FN>(sg.a + wm * FM * 32 * BK, sg.b + wn * FN * 32 * BK, lane, mlive, p);
+            float sa[FM];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) sa[mi] = sg.sa[wm * 64 + mi * 32 + (lane & 31)];
-            if (BSCALE_1x128) {
+            for (int mi = 0; mi < FM; ++mi) sa[mi] = sg.sa[wm * FM * 32 + mi * 32 + (lane & 31)];
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
+            for (int ni = 0; ni < FN; ++ni) {
+                if (BSCALE_1x128) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const v4f sbv = ld<v4f>(&sg.sb[n_lane + ni * 32 + 8 * j]);
 #pragma unroll
-                        for (int mi = 0; mi < 2; ++mi)
+                        for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                acc[mi][ni][4 * j + e] = fmaf(p[mi][ni][4 * j + e], sa[mi] * sbv[e], acc[mi][ni][4 * j + e]);
+                                acc[mi][ni][4 * j + e] =
+                                    fmaf(p[mi][ni][4 * j + e], sa[mi] * sbv[e], acc[mi][ni][4 * j + e]);
                     }
-            } else {
-                const float sb = sg.sb[0];
+                } else {
+                    // the 128-wide n-block of this n-tile (tiles never straddle one)
+                    const float sb = sg.sb[((wn * FN * 32 + ni * 32) / 128) * 64];
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi) {
-                    const float sc = sa[mi] * sb;
-#pragma unroll
-                    for (int ni = 0; ni < 2; ++ni)
+                    for (int mi = 0; mi < FM; ++mi) {
+                        const float sc = sa[mi] * sb;
 #pragma unroll
                         for (int i = 0; i < 16; ++i) acc[mi][ni][i] = fmaf(p[mi][ni][i], sc, acc[mi][ni][i]);
+                    }
                 }
             }
         }
-        cur = cur == 2 ? 0 : cur + 1;
+        cur = cur == STAGES - 1 ? 0 : cur + 1;
     }
-    if (!wave_live) return;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-        const int64_t m = t.m0 + wm * 64 + mi * 32 + (lane & 31);
+    for (int mi = 0; mi < FM; ++mi) {
+        const int64_t m = wrow0 + mi * 32 + (lane & 31);
         if (m >= t.rows_valid) continue;
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
@@ -405,28 +473,68 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args) {
     }
 }
 
-template <int ENGINE, int BS, int OF, int MODE>
-hipError_t launch_one(const GemmArgs& args, int64_t tiles, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_kernel<ENGINE, BS, OF, MODE>), dim3(unsigned(tiles)), dim3(kThreads), 0, stream, args);
-    return hipGetLastError();
+// One plain __global__ function per instantiation (kernel templates whose
+// instantiations differ only in the tile shape lost their host stubs).
+// tile id: 0 = BigTile, 1 = DecodeTile
+#define FP8FG_GEMM_KERNELS(X)                                              \
+    X(big_e0_b0_o0_dense, 0, 4, 2, 2, 2, 3, 0, 0, 0, 0)                    \
+    X(big_e0_b0_o1_dense, 0, 4, 2, 2, 2, 3, 0, 0, 1, 0)                    \
+    X(big_e0_b1_o0_dense, 0, 4, 2, 2, 2, 3, 0, 1, 0, 0)                    \
+    X(big_e0_b1_o1_dense, 0, 4, 2, 2, 2, 3, 0, 1, 1, 0)                    \
+    X(big_e0_b0_o0_contig, 0, 4, 2, 2, 2, 3, 0, 0, 0, 1)                   \
+    X(big_e0_b0_o1_contig, 0, 4, 2, 2, 2, 3, 0, 0, 1, 1)                   \
+    X(big_e0_b0_o0_masked, 0, 4, 2, 2, 2, 3, 0, 0, 0, 2)                   \
+    X(big_e0_b0_o1_masked, 0, 4, 2, 2, 2, 3, 0, 0, 1, 2)                   \
+    X(dec_e0_b0_o0_masked, 1, 2, 4, 1, 1, 3, 0, 0, 0, 2)                   \
+    X(dec_e0_b0_o1_masked, 1, 2, 4, 1, 1, 3, 0, 0, 1, 2)                   \
+    X(big_e1_b0_o0_dense, 0, 4, 2, 2, 2, 3, 1, 0, 0, 0)                    \
+    X(big_e1_b0_o1_dense, 0, 4, 2, 2, 2, 3, 1, 0, 1, 0)                    \
+    X(big_e1_b1_o0_dense, 0, 4, 2, 2, 2, 3, 1, 1, 0, 0)                    \
+    X(big_e1_b1_o1_dense, 0, 4, 2, 2, 2, 3, 1, 1, 1, 0)                    \
+    X(big_e1_b0_o0_contig, 0, 4, 2, 2, 2, 3, 1, 0, 0, 1)                   \
+    X(big_e1_b0_o1_contig, 0, 4, 2, 2, 2, 3, 1, 0, 1, 1)                   \
+    X(big_e1_b0_o0_masked, 0, 4, 2, 2, 2, 3, 1, 0, 0, 2)                   \
+    X(big_e1_b0_o1_masked, 0, 4, 2, 2, 2, 3, 1, 0, 1, 2)                   \
+    X(dec_e1_b0_o0_masked, 1, 2, 4, 1, 1, 3, 1, 0, 0, 2)                   \
+    X(dec_e1_b0_o1_masked, 1, 2, 4, 1, 1, 3, 1, 0, 1, 2)
+
+#define FP8FG_DEFINE_KERNEL(NAME, TILE, WM, WN, FM, FN, ST, E, BS, OF, MODE)                  \
+    __global__ __launch_bounds__(kThreads) void gemm_##NAME(GemmArgs args) {                  \
+        gemm_body<WM, WN, FM, FN, ST, E, BS, OF, MODE>(args);                                 \
+    }
+FP8FG_GEMM_KERNELS(FP8FG_DEFINE_KERNEL)
+#undef FP8FG_DEFINE_KERNEL
+
+struct KernelEntry {
+    void (*fn)(GemmArgs);
+    int tile, engine, bscale, out_fp32, mode;
+};
+
+#define FP8FG_ENTRY(NAME, TILE, WM, WN, FM, FN, ST, E, BS, OF, MODE) {gemm_##NAME, TILE, E, BS, OF, MODE},
+const KernelEntry kKernels[] = {FP8FG_GEMM_KERNELS(FP8FG_ENTRY)};
+#undef FP8FG_ENTRY
+
+template <class C>
+int64_t tile_count(GemmMode mode, const GemmArgs& args) {
+    const int64_t n_tiles = args.N / C::BN;
+    if (mode == GemmMode::Masked) return args.G * ((args.M + C::BM - 1) / C::BM) * n_tiles;
+    if (mode == GemmMode::Contig) return (args.M / C::BM + args.G) * n_tiles;
+    return ((args.M + C::BM - 1) / C::BM) * n_tiles;
 }
 
-template <int ENGINE>
-hipError_t dispatch(GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args, int64_t tiles,
+hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                     hipStream_t stream) {
-    switch (mode) {
-        case GemmMode::Dense:
-            if (bscale_1x128)
-                return out_fp32 ? launch_one<ENGINE, 1, 1, 0>(args, tiles, stream)
-                                : launch_one<ENGINE, 1, 0, 0>(args, tiles, stream);
-            return out_fp32 ? launch_one<ENGINE, 0, 1, 0>(args, tiles, stream)
-                            : launch_one<ENGINE, 0, 0, 0>(args, tiles, stream);
-        case GemmMode::Contig:
-            return out_fp32 ? launch_one<ENGINE, 0, 1, 1>(args, tiles, stream)
-                            : launch_one<ENGINE, 0, 0, 1>(args, tiles, stream);
-        case GemmMode::Masked:
-            return out_fp32 ? launch_one<ENGINE, 0, 1, 2>(args, tiles, stream)
-                            : launch_one<ENGINE, 0, 0, 2>(args, tiles, stream);
+    // decode-sized masked buffers stream the weights with 64-row tiles;
+    // everything else uses the big tile
+    const int tile = (mode == GemmMode::Masked && args.M <= 128) ? 1 : 0;
+    const int64_t tiles = tile == 0 ? tile_count<BigTile>(mode, args) : tile_count<DecodeTile>(mode, args);
+    if (tiles == 0) return hipSuccess;
+    for (const KernelEntry& k : kKernels) {
+        if (k.tile == tile && k.engine == engine && k.bscale == bscale_1x128 && k.out_fp32 == out_fp32 &&
+            k.mode == int(mode)) {
+            hipLaunchKernelGGL(k.fn, dim3(unsigned(tiles)), dim3(kThreads), 0, stream, args);
+            return hipGetLastError();
+        }
     }
     return hipErrorInvalidValue;
 }
@@ -437,18 +545,11 @@ int engine_from_env() {
     return (e && strcmp(e, "fp8mfma") == 0) ? 1 : 0;
 }
 
-}  // namespace
+}  // namespace gemm_detail
 
 hipError_t launch_gemm(GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                        hipStream_t stream) {
-    const int64_t n_tiles = args.N / BN;
-    int64_t tiles;
-    if (mode == GemmMode::Masked) tiles = args.G * ((args.M + BM - 1) / BM) * n_tiles;
-    else if (mode == GemmMode::Contig) tiles = (args.M / BM + args.G) * n_tiles;
-    else tiles = ((args.M + BM - 1) / BM) * n_tiles;
-    if (tiles == 0) return hipSuccess;
-    if (engine_from_env() == 1) return dispatch<1>(mode, bscale_1x128, out_fp32, args, tiles, stream);
-    return dispatch<0>(mode, bscale_1x128, out_fp32, args, tiles, stream);
+    return gemm_detail::dispatch(gemm_detail::engine_from_env(), mode, bscale_1x128, out_fp32, args, stream);
 }
 
 }  // namespace fp8fg
