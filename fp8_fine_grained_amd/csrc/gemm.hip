@@ -473,6 +473,338 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Wide exact kernel (128x128-scaled B): the promotion folded into the MFMA
+// accumulator.
+//
+// A 64 x 64 wave tile spends more VALU time widening FP8 to BF16 (one cvt per
+// two codes of both operands) and folding P_kb into the accumulator (one FMA
+// per output) than its MFMAs take, and a larger wave tile leaves no registers
+// for a separate P_kb next to the accumulator.  So this kernel gives each wave
+// a 64 x 128 tile (2 x 4 MFMA tiles; the workgroup tile is 256 x 256) and
+// lets the MFMA add every block straight into the accumulator, which is kept
+// in a unit that changes at each K-block:
+//     s = sA[kb][m] * sB[nb][kb] = (ma * 2^ta) * (mb * 2^tb)
+//     the widening cvt multiplies A codes by 2^ta and B codes by 2^tb
+//     (its scale operand contributes only its exponent: exact), so the
+//     MFMAs of K-block kb add  P_kb * 2^(ta + tb)  to the accumulator;
+//     the accumulator holds  acc / u_kb  with  u_kb = ma * mb,  so before
+//     K-block kb it is multiplied by u_(kb-1) / u_kb, and at the end by u.
+// The per-element work is one multiply per K-block, as with the fold, and
+// the cvts per MFMA drop by a third.  ta and tb are the scales' exponents,
+// clamped only to the range where the cvt is exact, so the mantissa parts
+// are at least 1 for every normal scale: the accumulator then never exceeds
+// |C| and cannot overflow where C does not (subnormal scales give parts down
+// to 2^-25).  Products of two widened codes are the true products times
+// 2^-(log2 u): they fall below FP32's normal range only when the scale
+// product itself is below about 2^-108, i.e. for blocks whose every
+// contribution is smaller than 2^-80 in magnitude.
+//
+// Stages hold half a K-block (64 K: rows of 64 bytes, four 16-byte chunks,
+// chunk c of row r at slot c ^ ((r >> 2) & 3)); four of them (135 KB) keep
+// three half-blocks in flight.  The scales of K-block kb ride with both of
+// its halves; the first half applies them.  Copies are buffer-to-LDS loads
+// whose per-lane offsets are fixed for the whole tile, the K position riding
+// in the scalar offset, and each half-block is one straight-line block of
+// fragment reads, cvts and MFMAs.  A row whose A scale (or the block's B
+// scale) is zero reads its codes from a zeroed 64-byte line after the ring,
+// so its products are +0 whatever the codes hold.
+//
+// Measured on this kernel: a SIMD runs its two waves' MFMAs and VALU
+// instructions essentially one after the other (only about two VALU
+// instructions per 32x32x16 MFMA hide under it), so the loop costs MFMA time
+// plus VALU time; the cvts (3 per MFMA) and the rescale (2 per MFMA) are most
+// of the latter.
+struct WideTile {
+    static constexpr int WAVES_M = 4, WAVES_N = 2, FM = 2, FN = 4;
+    static constexpr int BM = 256, BN = 256, KS = 64, STAGES = 4;
+    static constexpr int ROWS_PER_PIECE = 1024 / KS;                  // 16 rows per 1 KB load
+    static constexpr int A_PER_WAVE = BM / ROWS_PER_PIECE / 8;        // 2
+    static constexpr int B_PER_WAVE = BN / ROWS_PER_PIECE / 8;        // 2
+    static constexpr int LOADS_PER_WAVE = A_PER_WAVE + B_PER_WAVE + 1;
+};
+
+struct alignas(16) WideStage {
+    uint8_t a[WideTile::BM * WideTile::KS];
+    uint8_t b[WideTile::BN * WideTile::KS];
+    float sa[WideTile::BM];   // A scales of the stage's K-block
+    float sb[128];            // 64 copies of each of the two n-blocks' scales
+    float dummy[64];
+};
+
+// scale s -> (2^t with t = s's exponent clamped to [-124, 118], the range in
+// which the widening cvt scales every code exactly; s / 2^t), with s == 0
+// giving mantissa part 1 (its rows read the zero line instead).  The mantissa part
+// is in [1, 2) for every normal s below 2^119 and never below 2^-25.
+struct ScaleSplit {
+    float pow2;
+    float mant;
+};
+__device__ __forceinline__ ScaleSplit split_scale(float s) {
+    const uint32_t e = (__builtin_bit_cast(uint32_t, s) >> 23) & 0xFF;
+    const uint32_t ec = e < 3u ? 3u : (e > 245u ? 245u : e);
+    ScaleSplit r;
+    r.pow2 = __builtin_bit_cast(float, ec << 23);
+    r.mant = s == 0.0f ? 1.0f : s * __builtin_bit_cast(float, (254u - ec) << 23);
+    return r;
+}
+
+__device__ __forceinline__ float clamp_unit(float u) {
+    return fminf(fmaxf(u, 0x1p-126f), 0x1p126f);
+}
+
+// 8 FP8 codes -> 8 BF16 values times 2^(exponent of p2)
+__device__ __forceinline__ v8bf widen8_scaled(uint32_t w0, uint32_t w1, float p2) {
+    const u32x4 v{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w0), p2, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w0), p2, true)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w1), p2, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w1), p2, true))};
+    return __builtin_bit_cast(v8bf, v);
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit dwords
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), kRsrcFlags);
+}
+
+struct WideBufCopier {
+    rsrc_t ra, rb, rs;
+    uint32_t va[WideTile::A_PER_WAVE], vb[WideTile::B_PER_WAVE], vs;   // per-lane byte offsets
+    uint32_t s_step;           // scale byte offset per K-block
+    int a_lds[WideTile::A_PER_WAVE], b_lds[WideTile::B_PER_WAVE], s_lds;
+
+    __device__ __forceinline__ void copy(uint8_t* stage, int64_t h) const {
+        const uint32_t koff = uint32_t(h) * WideTile::KS;
+#pragma unroll
+        for (int i = 0; i < WideTile::A_PER_WAVE; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + a_lds[i]), 16, va[i], koff, 0, 0);
+#pragma unroll
+        for (int i = 0; i < WideTile::B_PER_WAVE; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i]), 16, vb[i], koff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs, uint32_t(h >> 1) * s_step, 0, 0);
+    }
+};
+
+__device__ __forceinline__ WideBufCopier make_wide_buf_copier(const Tile& t, int wave, int lane, int64_t K,
+                                                              int64_t n0) {
+    typedef WideTile W;
+    WideBufCopier c;
+    const int sub = lane >> 2, slot = lane & 3;
+    const int64_t tile_rows = t.rows_valid - t.m0 < W::BM ? t.rows_valid - t.m0 : W::BM;   // >= 1
+    c.ra = make_rsrc(t.A + t.m0 * K, uint32_t(tile_rows * K));
+    c.rb = make_rsrc(t.B + n0 * K, uint32_t(W::BN * K));
+#pragma unroll
+    for (int i = 0; i < W::A_PER_WAVE; ++i) {
+        const int r0 = (wave * W::A_PER_WAVE + i) * W::ROWS_PER_PIECE, r = r0 + sub;
+        const int chunk = slot ^ ((r >> 2) & 3);
+        const int64_t row = r < tile_rows ? r : tile_rows - 1;      // clamp: loaded, never stored
+        c.va[i] = uint32_t(row * K + chunk * 16);
+        c.a_lds[i] = int(offsetof(WideStage, a)) + r0 * W::KS;
+    }
+#pragma unroll
+    for (int i = 0; i < W::B_PER_WAVE; ++i) {
+        const int r0 = (wave * W::B_PER_WAVE + i) * W::ROWS_PER_PIECE, r = r0 + sub;
+        const int chunk = slot ^ ((r >> 2) & 3);
+        c.vb[i] = uint32_t(int64_t(r) * K + chunk * 16);
+        c.b_lds[i] = int(offsetof(WideStage, b)) + r0 * W::KS;
+    }
+    const int64_t kbs = K / BK;
+    if (wave < 4) {                       // A scales of rows 64 wave .. +63 (clamped)
+        const int64_t rr = int64_t(wave) * 64 + lane;
+        const int64_t row = rr < tile_rows ? rr : tile_rows - 1;
+        c.rs = make_rsrc(t.SA + t.m0, uint32_t(((kbs - 1) * t.lda_s + tile_rows) * 4));
+        c.vs = uint32_t(row * 4);
+        c.s_step = uint32_t(t.lda_s * 4);
+        c.s_lds = int(offsetof(WideStage, sa)) + wave * 64 * 4;
+    } else if (wave < 6) {                // 64 copies of the scale of n-block n0 / 128 + (wave - 4)
+        const float* base = t.SB + (n0 / 128 + (wave - 4)) * kbs;
+        c.rs = make_rsrc(base, uint32_t(kbs * 4));
+        c.vs = 0;
+        c.s_step = 4;
+        c.s_lds = int(offsetof(WideStage, sb)) + (wave - 4) * 64 * 4;
+    } else {                              // padding: the tile's first A scale again
+        c.rs = make_rsrc(t.SA + t.m0, uint32_t(((kbs - 1) * t.lda_s + 1) * 4));
+        c.vs = 0;
+        c.s_step = uint32_t(t.lda_s * 4);
+        c.s_lds = int(offsetof(WideStage, dummy));
+    }
+    return c;
+}
+
+// what a K-block's scales turn into for one wave
+struct WideScales {
+    float pa[2], pb;         // cvt scale operands (exponent parts)
+    float unit[2];           // mantissa-part products: the accumulator unit
+    int zero[2];             // 1 if the row's codes must read as +0 (its A scale or the B scale is 0)
+};
+
+__device__ __forceinline__ WideScales wide_scales(const WideStage& sg, int wm, int wn, int r) {
+    WideScales w;
+    const float sb = sg.sb[wn * 64];
+    const ScaleSplit b = split_scale(sb);
+    w.pb = b.pow2;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const float sa = sg.sa[wm * 64 + mi * 32 + r];
+        const ScaleSplit a = split_scale(sa);
+        w.pa[mi] = a.pow2;
+        w.unit[mi] = clamp_unit(a.mant * b.mant);
+        w.zero[mi] = (sa == 0.0f || sb == 0.0f) ? 1 : 0;
+    }
+    return w;
+}
+
+// LDS byte offsets (from the ring base) of this lane's fragment chunk column j
+// of stage slot `slot`: A rows (two m-tiles, or the zero line) and B rows
+struct FragAddr {
+    uint32_t a[2], b;
+};
+__device__ __forceinline__ FragAddr frag_addr(int slot, int j, int wm, int wn, int r, int h, const int (&zero)[2],
+                                              uint32_t zero_line) {
+    FragAddr f;
+    const uint32_t base = uint32_t(slot) * uint32_t(sizeof(WideStage));
+    const uint32_t chunk = uint32_t(((2 * j + h) ^ ((r >> 2) & 3)) << 4);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const uint32_t a = base + uint32_t(offsetof(WideStage, a)) + uint32_t((wm * 64 + mi * 32 + r) * 64) + chunk;
+        f.a[mi] = zero[mi] ? zero_line + chunk : a;
+    }
+    f.b = base + uint32_t(offsetof(WideStage, b)) + uint32_t((wn * 128 + r) * 64) + chunk;
+    return f;
+}
+
+struct Frags {
+    u32x4 a[2], b[4];
+};
+__device__ __forceinline__ Frags read_frags(const uint8_t* lds, const FragAddr& f) {
+    Frags x;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) x.a[mi] = ld<u32x4>(lds + f.a[mi]);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) x.b[ni] = ld<u32x4>(lds + f.b + ni * 32 * 64);
+    return x;
+}
+
+// the two k-steps of one chunk column
+__device__ __forceinline__ void mfma_column(const Frags& x, const WideScales& w, v16f (&acc)[2][4]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        v8bf a8[2], b8[4];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) a8[mi] = widen8_scaled(x.a[mi][2 * half], x.a[mi][2 * half + 1], w.pa[mi]);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) b8[ni] = widen8_scaled(x.b[ni][2 * half], x.b[ni][2 * half + 1], w.pb);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8[ni], a8[mi], acc[mi][ni], 0, 0, 0);
+    }
+}
+
+// One half-block: both chunk columns' fragments, then their four k-steps.
+__device__ __forceinline__ void wide_half_compute(const uint8_t* lds, int slot, int wm, int wn, int r, int h,
+                                                   const WideScales& w, uint32_t zero_line, v16f (&acc)[2][4]) {
+    Frags f[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) f[j] = read_frags(lds, frag_addr(slot, j, wm, wn, r, h, w.zero, zero_line));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) mfma_column(f[j], w, acc);
+}
+
+template <int OUT_FP32, int MODE>
+__device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
+    typedef WideTile W;
+    constexpr int FM = W::FM, FN = W::FN, STAGES = W::STAGES;
+    static_assert(STAGES == 4, "ring index arithmetic below assumes four stages");
+    constexpr uint32_t kZeroLine = STAGES * sizeof(WideStage);
+    __shared__ __align__(16) uint8_t lds_raw[kZeroLine + 64];
+    WideStage* ring = reinterpret_cast<WideStage*>(lds_raw);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps wave-derived values scalar
+    const int wm = wave / W::WAVES_N, wn = wave % W::WAVES_N;
+    const int64_t N = args.N, K = args.K;
+    const int halves = int(2 * (K / BK));
+    const Tile t = map_tile<W, MODE>(args, blockIdx.x);
+    if (!t.live) return;
+    const int64_t n0 = int64_t(t.bn) * W::BN;
+    const WideBufCopier cp = make_wide_buf_copier(t, wave, lane, K, n0);
+    const int64_t wrow0 = t.m0 + wm * FM * 32;
+    const bool wave_live = wrow0 < t.rows_valid;
+    const int r = lane & 31, h = lane >> 5;
+    constexpr int L = W::LOADS_PER_WAVE;
+
+    if (tid < 4) st<u32x4>(lds_raw + kZeroLine + tid * 16, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        cp.copy(reinterpret_cast<uint8_t*>(&ring[st]), st < halves ? st : halves - 1);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the zero line is written before the first barrier
+
+    v16f acc[FM][FN];
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
+    WideScales w;
+    w.pa[0] = w.pa[1] = w.pb = 1.0f;
+    w.unit[0] = w.unit[1] = 1.0f;
+    w.zero[0] = w.zero[1] = 0;
+
+    for (int hb = 0; hb < halves; hb += 2) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int cur = hb + e;
+            wait_vmcnt<2 * L>();              // this wave's copy of half-block cur has landed
+            __builtin_amdgcn_s_barrier();     // ... every wave's; slot cur - 1 is free
+            const int fill = cur + STAGES - 1;
+            cp.copy(reinterpret_cast<uint8_t*>(&ring[fill & 3]), fill < halves ? fill : halves - 1);
+            if (wave_live) {
+                if (e == 0) {
+                    const WideScales nw = wide_scales(ring[cur & 3], wm, wn, r);
+#pragma unroll
+                    for (int mi = 0; mi < FM; ++mi) {
+                        const float ratio = clamp_unit(w.unit[mi] * __builtin_amdgcn_rcpf(nw.unit[mi]));
+#pragma unroll
+                        for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) acc[mi][ni][i] *= ratio;
+                    }
+                    w = nw;
+                }
+                wide_half_compute(lds_raw, cur & 3, wm, wn, r, h, w, kZeroLine, acc);
+            }
+        }
+    }
+    wait_vmcnt<0>();   // no copy may land after the workgroup's LDS is handed on
+
+    const int n_lane = wn * FN * 32 + 4 * h;
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) {
+        const int64_t m = wrow0 + mi * 32 + r;
+        if (m >= t.rows_valid) continue;
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
+                const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
+                                  acc[mi][ni][4 * j + 3]} * w.unit[mi];
+                if (OUT_FP32) {
+                    st<v4f>(static_cast<float*>(args.c) + idx, v);
+                } else {
+                    const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+                    const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+                    st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
+                }
+            }
+    }
+}
+
 // One plain __global__ function per instantiation (kernel templates whose
 // instantiations differ only in the tile shape lost their host stubs).
 // tile id: 0 = BigTile, 1 = DecodeTile
@@ -514,6 +846,22 @@ struct KernelEntry {
 const KernelEntry kKernels[] = {FP8FG_GEMM_KERNELS(FP8FG_ENTRY)};
 #undef FP8FG_ENTRY
 
+// wide exact kernels (tile id 2): exact engine, 128x128 B scales, N a multiple of 256
+#define FP8FG_WIDE_KERNELS(X) \
+    X(wide_o0_dense, 0, 0)    \
+    X(wide_o1_dense, 1, 0)    \
+    X(wide_o0_contig, 0, 1)   \
+    X(wide_o1_contig, 1, 1)   \
+    X(wide_o0_masked, 0, 2)   \
+    X(wide_o1_masked, 1, 2)
+#define FP8FG_DEFINE_WIDE(NAME, OF, MODE) \
+    __global__ __launch_bounds__(kThreads) void gemm_##NAME(GemmArgs args) { gemm_wide_body<OF, MODE>(args); }
+FP8FG_WIDE_KERNELS(FP8FG_DEFINE_WIDE)
+#undef FP8FG_DEFINE_WIDE
+#define FP8FG_WIDE_ENTRY(NAME, OF, MODE) {gemm_##NAME, 2, 0, 0, OF, MODE},
+const KernelEntry kWideKernels[] = {FP8FG_WIDE_KERNELS(FP8FG_WIDE_ENTRY)};
+#undef FP8FG_WIDE_ENTRY
+
 template <class C>
 int64_t tile_count(GemmMode mode, const GemmArgs& args) {
     const int64_t n_tiles = args.N / C::BN;
@@ -522,20 +870,48 @@ int64_t tile_count(GemmMode mode, const GemmArgs& args) {
     return ((args.M + C::BM - 1) / C::BM) * n_tiles;
 }
 
+// The wide kernel addresses its operands through buffer descriptors with
+// 32-bit byte ranges: a 256-row slice of A or B (256 K bytes) and the A scale
+// array ((K / 128) * rows * 4 bytes) must each stay below 4 GiB, and its n-tile
+// is 256 wide.
+bool wide_fits(const GemmArgs& args) {
+    if (args.N % WideTile::BN != 0 || args.K >= (int64_t(1) << 24)) return false;
+    return (args.K / BK) * args.M * 4 <= int64_t(0xFFFFFFFF);
+}
+
+// FP8FG_GEMM_WIDE=0 keeps the big tile for everything (comparison runs)
+bool wide_enabled() {
+    const char* e = getenv("FP8FG_GEMM_WIDE");
+    return !(e && e[0] == '0');
+}
+
 hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                     hipStream_t stream) {
-    // decode-sized masked buffers stream the weights with 64-row tiles;
-    // everything else uses the big tile
-    const int tile = (mode == GemmMode::Masked && args.M <= 128) ? 1 : 0;
-    const int64_t tiles = tile == 0 ? tile_count<BigTile>(mode, args) : tile_count<DecodeTile>(mode, args);
+    // decode-sized masked buffers stream the weights with 64-row tiles; the
+    // exact engine on 128x128-scaled B with N a multiple of 256 runs the wide
+    // kernel; the rest (1x128 B scales, the FP8-MFMA engine, N = 128 mod 256)
+    // the big tile
+    int tile = 0;
+    if (mode == GemmMode::Masked && args.M <= 128)
+        tile = 1;
+    else if (engine == 0 && !bscale_1x128 && wide_fits(args) && wide_enabled())
+        tile = 2;
+    const int64_t tiles = tile == 0   ? tile_count<BigTile>(mode, args)
+                          : tile == 1 ? tile_count<DecodeTile>(mode, args)
+                                      : tile_count<WideTile>(mode, args);
     if (tiles == 0) return hipSuccess;
-    for (const KernelEntry& k : kKernels) {
+    auto launch = [&](const KernelEntry& k) -> bool {
         if (k.tile == tile && k.engine == engine && k.bscale == bscale_1x128 && k.out_fp32 == out_fp32 &&
             k.mode == int(mode)) {
             hipLaunchKernelGGL(k.fn, dim3(unsigned(tiles)), dim3(kThreads), 0, stream, args);
-            return hipGetLastError();
+            return true;
         }
-    }
+        return false;
+    };
+    for (const KernelEntry& k : kKernels)
+        if (launch(k)) return hipGetLastError();
+    for (const KernelEntry& k : kWideKernels)
+        if (launch(k)) return hipGetLastError();
     return hipErrorInvalidValue;
 }
 

@@ -136,6 +136,45 @@ def test_determinism_and_scale_linearity():
     assert torch.equal(c4, c1 * 4)
 
 
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_scales_across_many_binades(out):
+    """Tile scales spread over 2^-64 .. 2^64 (A) and 2^-24 .. 2^24 (B), with
+    one subnormal A scale: the promotion must hold for any scale pair, not
+    just for quantizer-sized ones (the kernel splits scales into powers of two
+    and mantissa parts, so this crosses all of its clamps)."""
+    rng = np.random.default_rng(50)
+    M, N, K = 300, 512, 1024
+    qa, sa = quant.quant_act_1x128(workloads.activations(rng, M, K, 0.01, 50.0))
+    qb, sb = quant.quant_weight_128x128(workloads.weights(rng, N, K))
+    sa = (sa * np.exp2(rng.integers(-64, 65, sa.shape))).astype(np.float32)
+    sb = (sb * np.exp2(rng.integers(-24, 25, sb.shape))).astype(np.float32)
+    sa[3, 7] = np.float32(2.0 ** -140)
+    c = host64(run_dense(qa, sa, qb, sb, "128x128", out))
+    c_ref, s_abs = gemm.gemm_blockscaled_ref(qa, sa, qb, sb)
+    assert np.all(np.isfinite(c))
+    check(c, c_ref, s_abs, out, f"scales across binades {out}")
+
+
+def test_zero_scales_with_nonzero_codes():
+    """A zero scale removes its block's products whatever the codes say: some
+    A tiles and B blocks get scale 0 over nonzero codes, and row 5 has only
+    zero scales, so its outputs must be exactly zero."""
+    rng = np.random.default_rng(51)
+    M, N, K = 130, 512, 768
+    qa, sa = quant.quant_act_1x128(workloads.activations(rng, M, K, 0.01, 50.0))
+    qb, sb = quant.quant_weight_128x128(workloads.weights(rng, N, K))
+    sa = sa.copy()
+    sb = sb.copy()
+    sa[rng.random(sa.shape) < 0.15] = 0.0
+    sa[:, 5] = 0.0
+    sb[rng.random(sb.shape) < 0.2] = 0.0
+    for out in ("fp32", "bf16"):
+        c = host64(run_dense(qa, sa, qb, sb, "128x128", out))
+        c_ref, s_abs = gemm.gemm_blockscaled_ref(qa, sa, qb, sb)
+        check(c, c_ref, s_abs, out, f"zero scales {out}")
+        assert np.all(c[5] == 0.0)
+
+
 def sample_rows(M, rng, n=64):
     rows = np.concatenate([np.arange(min(M, 16)), np.arange(max(0, M - 16), M), rng.integers(0, M, n)])
     return np.unique(rows)
@@ -275,6 +314,26 @@ def test_masked_small_with_sentinel(out):
     ch = host64(c)
     for g in range(G):
         check(ch[g, :mm[g]], res[g][0], res[g][1], out, f"masked g={g}")
+        assert np.all(ch[g, mm[g]:] == -3.0)
+
+
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_masked_buffers_over_128_rows(out):
+    """Masked buffers longer than 128 rows take the 256-row tile: ragged,
+    empty and full experts, sentinel kept past masked_m."""
+    G, M_max, N, K = 3, 300, 256, 384
+    rng = np.random.default_rng(52)
+    mm = np.array([300, 0, 129], np.int32)
+    a = np.stack([workloads.activations(rng, M_max, K, 0.01, 100.0) for _ in range(G)])
+    qa, sa = zip(*[quant.quant_act_1x128(a[g]) for g in range(G)])
+    qa, sa = np.stack(qa), np.stack(sa)
+    qb, sb = _experts("moe_masked", G, N, K)
+    c = torch.full((G, M_max, N), -3.0, dtype=OUT[out], device=DEV)
+    fp8.fp8_grouped_gemm_masked(dev(qa), dev(sa), dev(qb), dev(sb), dev(mm), OUT[out], out=c)
+    res = gemm.grouped_masked_ref(qa, sa, qb, sb, mm)
+    ch = host64(c)
+    for g in range(G):
+        check(ch[g, :mm[g]], res[g][0], res[g][1], out, f"masked>128 g={g}")
         assert np.all(ch[g, mm[g]:] == -3.0)
 
 
