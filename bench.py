@@ -46,6 +46,10 @@ def parse():
     p.add_argument("--sets", type=int, default=4, help="rotating input sets")
     p.add_argument("--cpu-rows", type=int, default=512, help="rows of the oracle's timed sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--profile-kernel", choices=["gemm", "quant_act", "quant_weight", "copy"],
+                   help="counter-collection driver: launch only this kernel `steps` times on the "
+                        "dense_fprop inputs (copy: a 1 GiB device-to-device copy, the byte-counter "
+                        "calibration); prints no JSON")
     p.add_argument("--workload", default="dense_fprop",
                    choices=["dense_fprop", "dense_small", "linear_trio", "moe_contig", "moe_masked"],
                    help="dense_fprop is the headline step; the others print one line per measured kernel")
@@ -272,6 +276,28 @@ def main():
             c=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
+
+    if args.profile_kernel:
+        s = sets[0]
+        fp8.fp8_quant_act_1x128(s["x"], q=s["qa"], s=s["sa"])
+        fp8.fp8_quant_weight_128x128(s["w"], q=s["qb"], s=s["sb"])
+        if args.profile_kernel == "copy":
+            src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            if args.profile_kernel == "gemm":
+                fp8.fp8_gemm_blockscaled(s["qa"], s["sa"], s["qb"], s["sb"], fp8.BSCALE_128x128, torch.bfloat16,
+                                         out=s["c"])
+            elif args.profile_kernel == "quant_act":
+                fp8.fp8_quant_act_1x128(s["x"], q=s["qa"], s=s["sa"])
+            elif args.profile_kernel == "quant_weight":
+                fp8.fp8_quant_weight_128x128(s["w"], q=s["qb"], s=s["sb"])
+            else:
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"profiled {args.profile_kernel} x{args.steps}", flush=True)
+        return
 
     def step(i, ev=None):
         s = sets[i % len(sets)]

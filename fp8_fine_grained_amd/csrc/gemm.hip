@@ -114,6 +114,57 @@ struct Tile {
     bool live;
 };
 
+// Masked layout: the p-th (expert, m-tile) pair in order of decreasing work --
+// the number of valid 32-row sub-tiles in the pair's m-range -- or -1 for a
+// pair without valid rows (those come last).  Workgroups start in index
+// order as CUs free up, so the longest ones start first and the short ones
+// fill in behind them.  Every wave computes the same answer: one lane per
+// pair, ballots count and locate.  Past 4096 pairs the natural order is kept.
+template <int BM>
+__device__ __forceinline__ int64_t masked_pair_by_work(const GemmArgs& args, int64_t p) {
+    constexpr int NC = BM / 32 + 1;              // classes 0 (no valid rows) .. BM / 32
+    const int lane = threadIdx.x & 63;
+    const int64_t m_tiles = (args.M + BM - 1) / BM, pairs = args.G * m_tiles;
+    auto cls = [&](int64_t pair) -> int {
+        const int64_t g = pair / m_tiles, mt = pair - g * m_tiles;
+        int64_t mm = args.aux[g];
+        mm = mm < 0 ? 0 : (mm > args.M ? args.M : mm);
+        const int64_t rows = mm - mt * BM;
+        return rows <= 0 ? 0 : int(((rows < BM ? rows : BM) + 31) / 32);
+    };
+    if (pairs > 4096) return cls(p) > 0 ? p : -1;
+    int64_t count[NC];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) count[k] = 0;
+    for (int64_t base = 0; base < pairs; base += 64) {
+        const int64_t pair = base + lane;
+        const int c = pair < pairs ? cls(pair) : -1;
+#pragma unroll
+        for (int k = 1; k < NC; ++k) count[k] += __builtin_popcountll(__builtin_amdgcn_ballot_w64(c == k));
+    }
+    int target = 0;
+#pragma unroll
+    for (int k = NC - 1; k >= 1; --k) {
+        if (target == 0) {
+            if (p < count[k]) target = k;
+            else p -= count[k];
+        }
+    }
+    if (target == 0) return -1;
+    for (int64_t base = 0; base < pairs; base += 64) {
+        const int64_t pair = base + lane;
+        const int c = pair < pairs ? cls(pair) : -1;
+        uint64_t m = __builtin_amdgcn_ballot_w64(c == target);
+        const int64_t n = __builtin_popcountll(m);
+        if (p < n) {
+            for (int64_t i = 0; i < p; ++i) m &= m - 1;   // drop the p lowest set bits
+            return base + __builtin_ctzll(m);
+        }
+        p -= n;
+    }
+    return -1;
+}
+
 template <class C, int MODE>
 __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile) {
     constexpr int BM = C::BM, BN = C::BN;
@@ -155,8 +206,13 @@ __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile) {
         }
     } else {
         const int64_t m_tiles = (args.M + BM - 1) / BM;
-        g = tile / m_tiles;
-        t.m0 = (tile - g * m_tiles) * BM;
+        const int64_t pair = masked_pair_by_work<BM>(args, tile);
+        if (pair < 0) {
+            t.live = false;
+            return t;
+        }
+        g = pair / m_tiles;
+        t.m0 = (pair - g * m_tiles) * BM;
         int64_t mm = args.aux[g];
         t.rows_valid = mm < 0 ? 0 : (mm > args.M ? args.M : mm);
         t.A += g * args.M * args.K;
@@ -515,20 +571,38 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
 // instructions per 32x32x16 MFMA hide under it), so the loop costs MFMA time
 // plus VALU time; the cvts (3 per MFMA) and the rescale (2 per MFMA) are most
 // of the latter.
-struct WideTile {
-    static constexpr int WAVES_M = 4, WAVES_N = 2, FM = 2, FN = 4;
-    static constexpr int BM = 256, BN = 256, KS = 64, STAGES = 4;
-    static constexpr int ROWS_PER_PIECE = 1024 / KS;                  // 16 rows per 1 KB load
-    static constexpr int A_PER_WAVE = BM / ROWS_PER_PIECE / 8;        // 2
-    static constexpr int B_PER_WAVE = BN / ROWS_PER_PIECE / 8;        // 2
+// Tile configurations of the kernel: WAVES_M x WAVES_N waves, each owning
+// FM x FN MFMA tiles of 32 x 32, STAGES half-block stages.
+template <int WAVES_M_, int WAVES_N_, int FM_, int FN_, int STAGES_>
+struct WCfg {
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, FM = FM_, FN = FN_, STAGES = STAGES_;
+    static constexpr int NW = WAVES_M * WAVES_N, THREADS = NW * 64;
+    static constexpr int BM = WAVES_M * FM * 32, BN = WAVES_N * FN * 32, KS = 64;
+    static constexpr int ROWS_PER_PIECE = 1024 / KS;                   // 16 rows per 1 KB load
+    static constexpr int A_PER_WAVE = BM / ROWS_PER_PIECE / NW;
+    static constexpr int B_PER_WAVE = BN / ROWS_PER_PIECE / NW;
+    static constexpr int A_SCALE_WAVES = BM / 64, B_SCALE_WAVES = BN / 128;
     static constexpr int LOADS_PER_WAVE = A_PER_WAVE + B_PER_WAVE + 1;
+    static_assert(A_PER_WAVE * ROWS_PER_PIECE * NW == BM && B_PER_WAVE * ROWS_PER_PIECE * NW == BN,
+                  "whole 1 KB pieces per wave");
+    static_assert(A_SCALE_WAVES * 64 == BM && B_SCALE_WAVES * 128 == BN, "scale pieces");
+    static_assert(A_SCALE_WAVES + B_SCALE_WAVES <= NW, "a scale piece per wave at most");
+    static_assert(FN * 32 <= 128 && 128 % (FN * 32) == 0, "a wave's columns lie in one 128-wide n-block");
+    static_assert(FM == 1 || FM == 2, "live m-tile paths exist for FM = 1, 2");
+    static_assert(STAGES >= 3 && STAGES <= 5, "ring depth");
 };
+// dense / contiguous / long masked buffers: 256 x 256, waves 4 x 2 of 64 x 128
+typedef WCfg<4, 2, 2, 4, 4> WideTile;
+// decode-sized masked buffers: 64 x 256, waves 1 x 4 of 64 x 64, two
+// workgroups per CU; every B code is widened once
+typedef WCfg<1, 4, 2, 2, 3> WideDecodeTile;
 
-struct alignas(16) WideStage {
-    uint8_t a[WideTile::BM * WideTile::KS];
-    uint8_t b[WideTile::BN * WideTile::KS];
-    float sa[WideTile::BM];   // A scales of the stage's K-block
-    float sb[128];            // 64 copies of each of the two n-blocks' scales
+template <class W>
+struct alignas(16) WStage {
+    uint8_t a[W::BM * W::KS];
+    uint8_t b[W::BN * W::KS];
+    float sa[W::BM];                    // A scales of the stage's K-block
+    float sb[W::B_SCALE_WAVES * 64];    // 64 copies of each n-block's scale
     float dummy[64];
 };
 
@@ -569,28 +643,30 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), kRsrcFlags);
 }
 
+template <class W>
 struct WideBufCopier {
     rsrc_t ra, rb, rs;
-    uint32_t va[WideTile::A_PER_WAVE], vb[WideTile::B_PER_WAVE], vs;   // per-lane byte offsets
+    uint32_t va[W::A_PER_WAVE], vb[W::B_PER_WAVE], vs;   // per-lane byte offsets
     uint32_t s_step;           // scale byte offset per K-block
-    int a_lds[WideTile::A_PER_WAVE], b_lds[WideTile::B_PER_WAVE], s_lds;
+    int a_lds[W::A_PER_WAVE], b_lds[W::B_PER_WAVE], s_lds;
 
-    __device__ __forceinline__ void copy(uint8_t* stage, int64_t h) const {
-        const uint32_t koff = uint32_t(h) * WideTile::KS;
+    __device__ __forceinline__ void copy(uint8_t* stage, int h) const {
+        const uint32_t koff = uint32_t(h) * W::KS;
 #pragma unroll
-        for (int i = 0; i < WideTile::A_PER_WAVE; ++i)
+        for (int i = 0; i < W::A_PER_WAVE; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + a_lds[i]), 16, va[i], koff, 0, 0);
 #pragma unroll
-        for (int i = 0; i < WideTile::B_PER_WAVE; ++i)
+        for (int i = 0; i < W::B_PER_WAVE; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i]), 16, vb[i], koff, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs, uint32_t(h >> 1) * s_step, 0, 0);
     }
 };
 
-__device__ __forceinline__ WideBufCopier make_wide_buf_copier(const Tile& t, int wave, int lane, int64_t K,
-                                                              int64_t n0) {
-    typedef WideTile W;
-    WideBufCopier c;
+template <class W>
+__device__ __forceinline__ WideBufCopier<W> make_wide_buf_copier(const Tile& t, int wave, int lane, int64_t K,
+                                                                 int64_t n0) {
+    typedef WStage<W> S;
+    WideBufCopier<W> c;
     const int sub = lane >> 2, slot = lane & 3;
     const int64_t tile_rows = t.rows_valid - t.m0 < W::BM ? t.rows_valid - t.m0 : W::BM;   // >= 1
     c.ra = make_rsrc(t.A + t.m0 * K, uint32_t(tile_rows * K));
@@ -601,53 +677,55 @@ __device__ __forceinline__ WideBufCopier make_wide_buf_copier(const Tile& t, int
         const int chunk = slot ^ ((r >> 2) & 3);
         const int64_t row = r < tile_rows ? r : tile_rows - 1;      // clamp: loaded, never stored
         c.va[i] = uint32_t(row * K + chunk * 16);
-        c.a_lds[i] = int(offsetof(WideStage, a)) + r0 * W::KS;
+        c.a_lds[i] = int(offsetof(S, a)) + r0 * W::KS;
     }
 #pragma unroll
     for (int i = 0; i < W::B_PER_WAVE; ++i) {
         const int r0 = (wave * W::B_PER_WAVE + i) * W::ROWS_PER_PIECE, r = r0 + sub;
         const int chunk = slot ^ ((r >> 2) & 3);
         c.vb[i] = uint32_t(int64_t(r) * K + chunk * 16);
-        c.b_lds[i] = int(offsetof(WideStage, b)) + r0 * W::KS;
+        c.b_lds[i] = int(offsetof(S, b)) + r0 * W::KS;
     }
     const int64_t kbs = K / BK;
-    if (wave < 4) {                       // A scales of rows 64 wave .. +63 (clamped)
+    if (wave < W::A_SCALE_WAVES) {        // A scales of rows 64 wave .. +63 (clamped)
         const int64_t rr = int64_t(wave) * 64 + lane;
         const int64_t row = rr < tile_rows ? rr : tile_rows - 1;
         c.rs = make_rsrc(t.SA + t.m0, uint32_t(((kbs - 1) * t.lda_s + tile_rows) * 4));
         c.vs = uint32_t(row * 4);
         c.s_step = uint32_t(t.lda_s * 4);
-        c.s_lds = int(offsetof(WideStage, sa)) + wave * 64 * 4;
-    } else if (wave < 6) {                // 64 copies of the scale of n-block n0 / 128 + (wave - 4)
-        const float* base = t.SB + (n0 / 128 + (wave - 4)) * kbs;
-        c.rs = make_rsrc(base, uint32_t(kbs * 4));
+        c.s_lds = int(offsetof(S, sa)) + wave * 64 * 4;
+    } else if (wave < W::A_SCALE_WAVES + W::B_SCALE_WAVES) {   // 64 copies of an n-block's scale
+        const int j = wave - W::A_SCALE_WAVES;
+        c.rs = make_rsrc(t.SB + (n0 / 128 + j) * kbs, uint32_t(kbs * 4));
         c.vs = 0;
         c.s_step = 4;
-        c.s_lds = int(offsetof(WideStage, sb)) + (wave - 4) * 64 * 4;
+        c.s_lds = int(offsetof(S, sb)) + j * 64 * 4;
     } else {                              // padding: the tile's first A scale again
         c.rs = make_rsrc(t.SA + t.m0, uint32_t(((kbs - 1) * t.lda_s + 1) * 4));
         c.vs = 0;
         c.s_step = uint32_t(t.lda_s * 4);
-        c.s_lds = int(offsetof(WideStage, dummy));
+        c.s_lds = int(offsetof(S, dummy));
     }
     return c;
 }
 
 // what a K-block's scales turn into for one wave
+template <int FM>
 struct WideScales {
-    float pa[2], pb;         // cvt scale operands (exponent parts)
-    float unit[2];           // mantissa-part products: the accumulator unit
-    int zero[2];             // 1 if the row's codes must read as +0 (its A scale or the B scale is 0)
+    float pa[FM], pb;        // cvt scale operands (exponent parts)
+    float unit[FM];          // mantissa-part products: the accumulator unit
+    int zero[FM];            // 1 if the row's codes must read as +0 (its A scale or the B scale is 0)
 };
 
-__device__ __forceinline__ WideScales wide_scales(const WideStage& sg, int wm, int wn, int r) {
-    WideScales w;
-    const float sb = sg.sb[wn * 64];
+template <class W>
+__device__ __forceinline__ WideScales<W::FM> wide_scales(const WStage<W>& sg, int wm, int wn, int r) {
+    WideScales<W::FM> w;
+    const float sb = sg.sb[((wn * W::FN * 32) / 128) * 64];
     const ScaleSplit b = split_scale(sb);
     w.pb = b.pow2;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-        const float sa = sg.sa[wm * 64 + mi * 32 + r];
+    for (int mi = 0; mi < W::FM; ++mi) {
+        const float sa = sg.sa[wm * W::FM * 32 + mi * 32 + r];
         const ScaleSplit a = split_scale(sa);
         w.pa[mi] = a.pow2;
         w.unit[mi] = clamp_unit(a.mant * b.mant);
@@ -656,72 +734,82 @@ __device__ __forceinline__ WideScales wide_scales(const WideStage& sg, int wm, i
     return w;
 }
 
-// LDS byte offsets (from the ring base) of this lane's fragment chunk column j
-// of stage slot `slot`: A rows (two m-tiles, or the zero line) and B rows
-struct FragAddr {
-    uint32_t a[2], b;
+template <int FM, int FN>
+struct Frags {
+    u32x4 a[FM], b[FN];
 };
-__device__ __forceinline__ FragAddr frag_addr(int slot, int j, int wm, int wn, int r, int h, const int (&zero)[2],
-                                              uint32_t zero_line) {
-    FragAddr f;
-    const uint32_t base = uint32_t(slot) * uint32_t(sizeof(WideStage));
+
+// this lane's fragments of chunk column j (32 K) of stage slot `slot`: A rows
+// of the first ML m-tiles (or the zero line) and B rows of the FN n-tiles
+template <class W, int ML>
+__device__ __forceinline__ Frags<W::FM, W::FN> read_frags(const uint8_t* lds, int slot, int j, int wm, int wn,
+                                                          int r, int h, const WideScales<W::FM>& w,
+                                                          uint32_t zero_line) {
+    Frags<W::FM, W::FN> x;
+    const uint32_t base = uint32_t(slot) * uint32_t(sizeof(WStage<W>));
     const uint32_t chunk = uint32_t(((2 * j + h) ^ ((r >> 2) & 3)) << 4);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-        const uint32_t a = base + uint32_t(offsetof(WideStage, a)) + uint32_t((wm * 64 + mi * 32 + r) * 64) + chunk;
-        f.a[mi] = zero[mi] ? zero_line + chunk : a;
+    for (int mi = 0; mi < ML; ++mi) {
+        const uint32_t a = base + uint32_t(offsetof(WStage<W>, a)) +
+                           uint32_t((wm * W::FM * 32 + mi * 32 + r) * W::KS) + chunk;
+        x.a[mi] = ld<u32x4>(lds + (w.zero[mi] ? zero_line + chunk : a));
     }
-    f.b = base + uint32_t(offsetof(WideStage, b)) + uint32_t((wn * 128 + r) * 64) + chunk;
-    return f;
-}
-
-struct Frags {
-    u32x4 a[2], b[4];
-};
-__device__ __forceinline__ Frags read_frags(const uint8_t* lds, const FragAddr& f) {
-    Frags x;
+    const uint32_t b = base + uint32_t(offsetof(WStage<W>, b)) + uint32_t((wn * W::FN * 32 + r) * W::KS) + chunk;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) x.a[mi] = ld<u32x4>(lds + f.a[mi]);
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) x.b[ni] = ld<u32x4>(lds + f.b + ni * 32 * 64);
+    for (int ni = 0; ni < W::FN; ++ni) x.b[ni] = ld<u32x4>(lds + b + ni * 32 * W::KS);
     return x;
 }
 
-// the two k-steps of one chunk column
-__device__ __forceinline__ void mfma_column(const Frags& x, const WideScales& w, v16f (&acc)[2][4]) {
+// the two k-steps of one chunk column, first ML m-tiles
+template <int FM, int FN, int ML>
+__device__ __forceinline__ void mfma_column(const Frags<FM, FN>& x, const WideScales<FM>& w, v16f (&acc)[FM][FN]) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-        v8bf a8[2], b8[4];
+        v8bf a8[FM], b8[FN];
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) a8[mi] = widen8_scaled(x.a[mi][2 * half], x.a[mi][2 * half + 1], w.pa[mi]);
+        for (int mi = 0; mi < ML; ++mi) a8[mi] = widen8_scaled(x.a[mi][2 * half], x.a[mi][2 * half + 1], w.pa[mi]);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) b8[ni] = widen8_scaled(x.b[ni][2 * half], x.b[ni][2 * half + 1], w.pb);
+        for (int ni = 0; ni < FN; ++ni) b8[ni] = widen8_scaled(x.b[ni][2 * half], x.b[ni][2 * half + 1], w.pb);
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < ML; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
+            for (int ni = 0; ni < FN; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8[ni], a8[mi], acc[mi][ni], 0, 0, 0);
     }
 }
 
 // One half-block: both chunk columns' fragments, then their four k-steps.
+template <class W, int ML>
 __device__ __forceinline__ void wide_half_compute(const uint8_t* lds, int slot, int wm, int wn, int r, int h,
-                                                   const WideScales& w, uint32_t zero_line, v16f (&acc)[2][4]) {
-    Frags f[2];
+                                                  const WideScales<W::FM>& w, uint32_t zero_line,
+                                                  v16f (&acc)[W::FM][W::FN]) {
+    Frags<W::FM, W::FN> f[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) f[j] = read_frags(lds, frag_addr(slot, j, wm, wn, r, h, w.zero, zero_line));
+    for (int j = 0; j < 2; ++j) f[j] = read_frags<W, ML>(lds, slot, j, wm, wn, r, h, w, zero_line);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) mfma_column(f[j], w, acc);
+    for (int j = 0; j < 2; ++j) mfma_column<W::FM, W::FN, ML>(f[j], w, acc);
 }
 
-template <int OUT_FP32, int MODE>
+// move the first ML m-tiles' accumulators from unit w to unit nw
+template <int FM, int FN, int ML>
+__device__ __forceinline__ void rescale(v16f (&acc)[FM][FN], const WideScales<FM>& w, const WideScales<FM>& nw) {
+#pragma unroll
+    for (int mi = 0; mi < ML; ++mi) {
+        const float ratio = clamp_unit(w.unit[mi] * __builtin_amdgcn_rcpf(nw.unit[mi]));
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] *= ratio;
+    }
+}
+
+template <class W, int OUT_FP32, int MODE>
 __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
-    typedef WideTile W;
+    typedef WStage<W> S;
     constexpr int FM = W::FM, FN = W::FN, STAGES = W::STAGES;
-    static_assert(STAGES == 4, "ring index arithmetic below assumes four stages");
-    constexpr uint32_t kZeroLine = STAGES * sizeof(WideStage);
+    constexpr uint32_t kZeroLine = STAGES * sizeof(S);
     __shared__ __align__(16) uint8_t lds_raw[kZeroLine + 64];
-    WideStage* ring = reinterpret_cast<WideStage*>(lds_raw);
+    S* ring = reinterpret_cast<S*>(lds_raw);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps wave-derived values scalar
@@ -731,13 +819,17 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
     const Tile t = map_tile<W, MODE>(args, blockIdx.x);
     if (!t.live) return;
     const int64_t n0 = int64_t(t.bn) * W::BN;
-    const WideBufCopier cp = make_wide_buf_copier(t, wave, lane, K, n0);
+    const WideBufCopier<W> cp = make_wide_buf_copier<W>(t, wave, lane, K, n0);
     const int64_t wrow0 = t.m0 + wm * FM * 32;
-    const bool wave_live = wrow0 < t.rows_valid;
+    const int64_t left = t.rows_valid - wrow0;
+    // m-tiles of this wave holding valid rows (uniform): 0, 1 or FM
+    const int mlive = left <= 0 ? 0 : (left >= FM * 32 ? FM : int((left + 31) / 32));
     const int r = lane & 31, h = lane >> 5;
     constexpr int L = W::LOADS_PER_WAVE;
 
     if (tid < 4) st<u32x4>(lds_raw + kZeroLine + tid * 16, u32x4{0u, 0u, 0u, 0u});
+    // half-blocks past the end reload the last one (into slots never read
+    // again), so every iteration issues the same loads and waits the same
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
         cp.copy(reinterpret_cast<uint8_t*>(&ring[st]), st < halves ? st : halves - 1);
@@ -750,34 +842,40 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
         for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
-    WideScales w;
-    w.pa[0] = w.pa[1] = w.pb = 1.0f;
-    w.unit[0] = w.unit[1] = 1.0f;
-    w.zero[0] = w.zero[1] = 0;
+    WideScales<FM> w;
+    w.pb = 1.0f;
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) {
+        w.pa[mi] = 1.0f;
+        w.unit[mi] = 1.0f;
+        w.zero[mi] = 0;
+    }
 
+    int slot = 0, fill_slot = STAGES - 1;   // ring slots of half-blocks cur and cur + STAGES - 1
     for (int hb = 0; hb < halves; hb += 2) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int cur = hb + e;
-            wait_vmcnt<2 * L>();              // this wave's copy of half-block cur has landed
-            __builtin_amdgcn_s_barrier();     // ... every wave's; slot cur - 1 is free
+            wait_vmcnt<(STAGES - 2) * L>();   // this wave's copy of half-block cur has landed
+            __builtin_amdgcn_s_barrier();     // ... every wave's; the slot of cur - 1 is free
             const int fill = cur + STAGES - 1;
-            cp.copy(reinterpret_cast<uint8_t*>(&ring[fill & 3]), fill < halves ? fill : halves - 1);
-            if (wave_live) {
+            cp.copy(reinterpret_cast<uint8_t*>(&ring[fill_slot]), fill < halves ? fill : halves - 1);
+            if (mlive > 0) {
                 if (e == 0) {
-                    const WideScales nw = wide_scales(ring[cur & 3], wm, wn, r);
-#pragma unroll
-                    for (int mi = 0; mi < FM; ++mi) {
-                        const float ratio = clamp_unit(w.unit[mi] * __builtin_amdgcn_rcpf(nw.unit[mi]));
-#pragma unroll
-                        for (int ni = 0; ni < FN; ++ni)
-#pragma unroll
-                            for (int i = 0; i < 16; ++i) acc[mi][ni][i] *= ratio;
-                    }
+                    const WideScales<FM> nw = wide_scales<W>(ring[slot], wm, wn, r);
+                    if (FM == 1 || mlive == FM)
+                        rescale<FM, FN, FM>(acc, w, nw);
+                    else
+                        rescale<FM, FN, 1>(acc, w, nw);
                     w = nw;
                 }
-                wide_half_compute(lds_raw, cur & 3, wm, wn, r, h, w, kZeroLine, acc);
+                if (FM == 1 || mlive == FM)
+                    wide_half_compute<W, FM>(lds_raw, slot, wm, wn, r, h, w, kZeroLine, acc);
+                else
+                    wide_half_compute<W, 1>(lds_raw, slot, wm, wn, r, h, w, kZeroLine, acc);
             }
+            slot = slot == STAGES - 1 ? 0 : slot + 1;
+            fill_slot = fill_slot == STAGES - 1 ? 0 : fill_slot + 1;
         }
     }
     wait_vmcnt<0>();   // no copy may land after the workgroup's LDS is handed on
@@ -839,26 +937,31 @@ FP8FG_GEMM_KERNELS(FP8FG_DEFINE_KERNEL)
 
 struct KernelEntry {
     void (*fn)(GemmArgs);
-    int tile, engine, bscale, out_fp32, mode;
+    int tile, engine, bscale, out_fp32, mode, threads;
 };
 
-#define FP8FG_ENTRY(NAME, TILE, WM, WN, FM, FN, ST, E, BS, OF, MODE) {gemm_##NAME, TILE, E, BS, OF, MODE},
+#define FP8FG_ENTRY(NAME, TILE, WM, WN, FM, FN, ST, E, BS, OF, MODE) {gemm_##NAME, TILE, E, BS, OF, MODE, kThreads},
 const KernelEntry kKernels[] = {FP8FG_GEMM_KERNELS(FP8FG_ENTRY)};
 #undef FP8FG_ENTRY
 
-// wide exact kernels (tile id 2): exact engine, 128x128 B scales, N a multiple of 256
-#define FP8FG_WIDE_KERNELS(X) \
-    X(wide_o0_dense, 0, 0)    \
-    X(wide_o1_dense, 1, 0)    \
-    X(wide_o0_contig, 0, 1)   \
-    X(wide_o1_contig, 1, 1)   \
-    X(wide_o0_masked, 0, 2)   \
-    X(wide_o1_masked, 1, 2)
-#define FP8FG_DEFINE_WIDE(NAME, OF, MODE) \
-    __global__ __launch_bounds__(kThreads) void gemm_##NAME(GemmArgs args) { gemm_wide_body<OF, MODE>(args); }
+// wide exact kernels, exact engine, 128x128 B scales, N a multiple of 256:
+// tile id 2 = WideTile, 3 = WideDecodeTile
+#define FP8FG_WIDE_KERNELS(X)                       \
+    X(wide_o0_dense, WideTile, 2, 0, 0)             \
+    X(wide_o1_dense, WideTile, 2, 1, 0)             \
+    X(wide_o0_contig, WideTile, 2, 0, 1)            \
+    X(wide_o1_contig, WideTile, 2, 1, 1)            \
+    X(wide_o0_masked, WideTile, 2, 0, 2)            \
+    X(wide_o1_masked, WideTile, 2, 1, 2)            \
+    X(wdec_o0_masked, WideDecodeTile, 3, 0, 2)      \
+    X(wdec_o1_masked, WideDecodeTile, 3, 1, 2)
+#define FP8FG_DEFINE_WIDE(NAME, CFG, TILE, OF, MODE)                                   \
+    __global__ __launch_bounds__(CFG::THREADS) void gemm_##NAME(GemmArgs args) {       \
+        gemm_wide_body<CFG, OF, MODE>(args);                                           \
+    }
 FP8FG_WIDE_KERNELS(FP8FG_DEFINE_WIDE)
 #undef FP8FG_DEFINE_WIDE
-#define FP8FG_WIDE_ENTRY(NAME, OF, MODE) {gemm_##NAME, 2, 0, 0, OF, MODE},
+#define FP8FG_WIDE_ENTRY(NAME, CFG, TILE, OF, MODE) {gemm_##NAME, TILE, 0, 0, OF, MODE, CFG::THREADS},
 const KernelEntry kWideKernels[] = {FP8FG_WIDE_KERNELS(FP8FG_WIDE_ENTRY)};
 #undef FP8FG_WIDE_ENTRY
 
@@ -887,23 +990,26 @@ bool wide_enabled() {
 
 hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                     hipStream_t stream) {
-    // decode-sized masked buffers stream the weights with 64-row tiles; the
-    // exact engine on 128x128-scaled B with N a multiple of 256 runs the wide
-    // kernel; the rest (1x128 B scales, the FP8-MFMA engine, N = 128 mod 256)
-    // the big tile
+    // the exact engine on 128x128-scaled B with N a multiple of 256 runs the
+    // wide kernel: 64 x 256 tiles for decode-sized masked buffers (at most
+    // 128 rows), 256 x 256 tiles otherwise.  The rest (1x128 B scales, the
+    // FP8-MFMA engine, N = 128 mod 256) runs the fold kernel: 64 x 128 tiles
+    // for decode-sized masked buffers, 256 x 128 tiles otherwise.
+    const bool wide = engine == 0 && !bscale_1x128 && wide_fits(args) && wide_enabled();
     int tile = 0;
     if (mode == GemmMode::Masked && args.M <= 128)
-        tile = 1;
-    else if (engine == 0 && !bscale_1x128 && wide_fits(args) && wide_enabled())
+        tile = wide ? 3 : 1;
+    else if (wide)
         tile = 2;
     const int64_t tiles = tile == 0   ? tile_count<BigTile>(mode, args)
                           : tile == 1 ? tile_count<DecodeTile>(mode, args)
-                                      : tile_count<WideTile>(mode, args);
+                          : tile == 2 ? tile_count<WideTile>(mode, args)
+                                      : tile_count<WideDecodeTile>(mode, args);
     if (tiles == 0) return hipSuccess;
     auto launch = [&](const KernelEntry& k) -> bool {
         if (k.tile == tile && k.engine == engine && k.bscale == bscale_1x128 && k.out_fp32 == out_fp32 &&
             k.mode == int(mode)) {
-            hipLaunchKernelGGL(k.fn, dim3(unsigned(tiles)), dim3(kThreads), 0, stream, args);
+            hipLaunchKernelGGL(k.fn, dim3(unsigned(tiles)), dim3(k.threads), 0, stream, args);
             return true;
         }
         return false;

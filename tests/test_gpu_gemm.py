@@ -337,6 +337,29 @@ def test_masked_buffers_over_128_rows(out):
         assert np.all(ch[g, mm[g]:] == -3.0)
 
 
+def test_masked_many_experts_every_row_once():
+    """70 experts (140 expert/m-tile pairs: the kernel orders workgroups by the
+    pairs' valid rows over several 64-pair chunks), counts covering 0, 1, 32,
+    33, 64, 65, 127 and 128 rows: every valid row is computed, every other row
+    keeps its sentinel."""
+    G, M_max, N, K = 70, 128, 256, 256
+    rng = np.random.default_rng(53)
+    mm = rng.integers(0, M_max + 1, G).astype(np.int32)
+    mm[:8] = [0, 1, 32, 33, 64, 65, 127, 128]
+    a = np.stack([workloads.activations(rng, M_max, K, 0.01, 20.0) for _ in range(G)])
+    qa, sa = zip(*[quant.quant_act_1x128(a[g]) for g in range(G)])
+    qa, sa = np.stack(qa), np.stack(sa)
+    qb, sb = _experts("moe_masked", G, N, K)
+    for out in ("bf16", "fp32"):
+        c = torch.full((G, M_max, N), -7.0, dtype=OUT[out], device=DEV)
+        fp8.fp8_grouped_gemm_masked(dev(qa), dev(sa), dev(qb), dev(sb), dev(mm), OUT[out], out=c)
+        res = gemm.grouped_masked_ref(qa, sa, qb, sb, mm)
+        ch = host64(c)
+        for g in range(G):
+            check(ch[g, :mm[g]], res[g][0], res[g][1], out, f"many experts g={g} rows={mm[g]}")
+            assert np.all(ch[g, mm[g]:] == -7.0), g
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("N,K", [(4096, 7168), (7168, 2048)])
 def test_masked_moe_full_size(N, K):
