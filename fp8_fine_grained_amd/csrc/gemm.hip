@@ -822,8 +822,12 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
     const WideBufCopier<W> cp = make_wide_buf_copier<W>(t, wave, lane, K, n0);
     const int64_t wrow0 = t.m0 + wm * FM * 32;
     const int64_t left = t.rows_valid - wrow0;
-    // m-tiles of this wave holding valid rows (uniform): 0, 1 or FM
+    // m-tiles of this wave holding valid rows (uniform): 0, 1 or FM.  Only the
+    // masked layout, whose tiles are mostly part-filled, takes the one-m-tile
+    // path: elsewhere partial m-tiles occur at edges only, and a second path
+    // would cost register copies where the two meet in every iteration.
     const int mlive = left <= 0 ? 0 : (left >= FM * 32 ? FM : int((left + 31) / 32));
+    constexpr bool full = FM == 1 || MODE != int(GemmMode::Masked);
     const int r = lane & 31, h = lane >> 5;
     constexpr int L = W::LOADS_PER_WAVE;
 
@@ -863,13 +867,13 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
             if (mlive > 0) {
                 if (e == 0) {
                     const WideScales<FM> nw = wide_scales<W>(ring[slot], wm, wn, r);
-                    if (FM == 1 || mlive == FM)
+                    if (full || mlive == FM)
                         rescale<FM, FN, FM>(acc, w, nw);
                     else
                         rescale<FM, FN, 1>(acc, w, nw);
                     w = nw;
                 }
-                if (FM == 1 || mlive == FM)
+                if (full || mlive == FM)
                     wide_half_compute<W, FM>(lds_raw, slot, wm, wn, r, h, w, kZeroLine, acc);
                 else
                     wide_half_compute<W, 1>(lds_raw, slot, wm, wn, r, h, w, kZeroLine, acc);
