@@ -53,15 +53,21 @@ __global__ __launch_bounds__(256) void quant_act_rows_kernel(const float* __rest
 // s [M/128][K].  A workgroup owns 128 tokens x 64 channels: it stages the
 // fp32 block in LDS (row pitch 65 floats so that column walks do not collide
 // on banks), each wave reduces one quarter of the tokens per channel, the
-// four partial maxima meet in LDS, and every lane then writes 32 consecutive
-// token codes of its channel (two 16-byte stores).
+// four partial maxima meet in LDS, every lane encodes 32 consecutive tokens of
+// its channel, and the codes return through LDS so that q^T is written in
+// whole 128-byte row segments.
 constexpr int kTokCh = 64;
 
 __global__ __launch_bounds__(256) void quant_act_tokens_kernel(const float* __restrict__ x, int64_t M,
                                                                int64_t K, uint8_t* __restrict__ q,
                                                                float* __restrict__ s) {
-    __shared__ float tile[kBlock][kTokCh + 1];
+    __shared__ __align__(16) float tile[kBlock][kTokCh + 1];
     __shared__ float part[4][kTokCh];
+    // the codes reuse the tile's memory: every read of the tile precedes the
+    // barrier after the partial maxima
+    typedef uint8_t CodeRow[kBlock + 16];
+    CodeRow* codes = reinterpret_cast<CodeRow*>(&tile[0][0]);
+    static_assert(sizeof(tile) >= kTokCh * sizeof(CodeRow), "codes fit in the tile");
     const int t = threadIdx.x;
     const int64_t mb = blockIdx.x;
     const int64_t k0 = int64_t(blockIdx.y) * kTokCh;
@@ -100,40 +106,65 @@ __global__ __launch_bounds__(256) void quant_act_tokens_kernel(const float* __re
     const float sc = amax / 448.0f;
     const float rc = 1.0f / sc;
     const int64_t k = k0 + c;
-    if (k < K) {
-        uint32_t w[8];
+    uint32_t w[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            w[i] = encode4(v4f{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]}, sc, rc);
-        uint8_t* dst = q + k * M + mb * kBlock + quarter * 32;
-        st<u32x4>(dst, u32x4{w[0], w[1], w[2], w[3]});
-        st<u32x4>(dst + 16, u32x4{w[4], w[5], w[6], w[7]});
-        if (quarter == 0) s[mb * K + k] = sc;
+    for (int i = 0; i < 8; ++i) w[i] = encode4(v4f{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]}, sc, rc);
+    // the codes go through LDS as [channel][token], so that each store
+    // instruction below writes eight whole 128-byte row segments of q^T
+    // instead of 64 scattered 16-byte pieces
+    st<u32x4>(&codes[c][quarter * 32], u32x4{w[0], w[1], w[2], w[3]});
+    st<u32x4>(&codes[c][quarter * 32 + 16], u32x4{w[4], w[5], w[6], w[7]});
+    if (quarter == 0 && k < K) s[mb * K + k] = sc;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int piece = t + 256 * i;             // 64 rows x 8 pieces of 16 bytes
+        const int row = piece >> 3, off = (piece & 7) * 16;
+        if (k0 + row < K) st<u32x4>(q + (k0 + row) * M + mb * kBlock + off, ld<u32x4>(&codes[row][off]));
     }
 }
 
 // ---------------------------------------------------------------------------
-// 128x128 weight blocks: one workgroup per block.  Each thread holds 16
-// float4 (rows t/32 + 8i, columns 4*(t%32)..+3), the block max-abs is
+// 128x128 weight blocks: one workgroup per block.  Thread t holds 16
+// float4: rows 16*(t/32) .. +15, columns 4*(t%32) .. +3.  The block max-abs is
 // reduced across the wave and then across the four waves in LDS.  The
-// transposed variant stages the codes in LDS as [column][row] and writes
-// 16-byte pieces of the rows of q^T.
+// transposed variant turns each 4x4 group of codes around in registers
+// (byte permutes) and stages the block in LDS as [column][row], 16-byte
+// column groups XOR-swizzled by row, then writes whole 16-byte pieces of the
+// rows of q^T.
+__device__ __forceinline__ int qt_off(int row, int col) {
+    return row * (kBlock + 16) + ((((col >> 4) ^ (row & 7))) << 4) + (col & 15);
+}
+
+// in[i] holds codes of row i (byte j = column j); out[j] the codes of column
+// j (byte i = row i)
+__device__ __forceinline__ void transpose4x4(const uint32_t (&in)[4], uint32_t (&out)[4]) {
+    const uint32_t a = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);   // r0c0 r1c0 r0c1 r1c1
+    const uint32_t b = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);   // r0c2 r1c2 r0c3 r1c3
+    const uint32_t c = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);   // r2c0 r3c0 r2c1 r3c1
+    const uint32_t d = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);   // r2c2 r3c2 r2c3 r3c3
+    out[0] = __builtin_amdgcn_perm(c, a, 0x05040100u);
+    out[1] = __builtin_amdgcn_perm(c, a, 0x07060302u);
+    out[2] = __builtin_amdgcn_perm(d, b, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
+}
+
 __global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restrict__ w, int64_t N,
                                                            int64_t K, int transpose_out,
                                                            uint8_t* __restrict__ q,
                                                            float* __restrict__ s) {
     __shared__ float red[4];
-    __shared__ __align__(16) uint8_t qt[kBlock][kBlock + 16];
+    __shared__ __align__(16) uint8_t qt[kBlock * (kBlock + 16)];
     const int t = threadIdx.x;
     const int64_t nb = blockIdx.y, kb = blockIdx.x;
     const int c4 = (t & 31) * 4;
-    const int r0 = t >> 5;
+    const int r0 = (t >> 5) * 16;
     const float* wb = w + nb * kBlock * K + kb * kBlock + c4;
     v4f v[16];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        v[i] = ld<v4f>(wb + int64_t(r0 + 8 * i) * K);
+        v[i] = ld<v4f>(wb + int64_t(r0 + i) * K);
         amax = fmaxf(amax, abs_max4(v[i]));
     }
     amax = wave_max(amax);
@@ -145,18 +176,20 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restri
     if (!transpose_out) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int64_t row = nb * kBlock + r0 + 8 * i;
+            const int64_t row = nb * kBlock + r0 + i;
             *reinterpret_cast<uint32_t*>(q + row * K + kb * kBlock + c4) = encode4(v[i], sc, rc);
         }
         if (t == 0) s[nb * (K / kBlock) + kb] = sc;
         return;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t cw = encode4(v[i], sc, rc);
-        const int r = r0 + 8 * i;
+    for (int g = 0; g < 4; ++g) {
+        uint32_t in[4], out[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) qt[c4 + j][r] = uint8_t(cw >> (8 * j));
+        for (int i = 0; i < 4; ++i) in[i] = encode4(v[4 * g + i], sc, rc);
+        transpose4x4(in, out);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st<uint32_t>(&qt[qt_off(c4 + j, r0 + 4 * g)], out[j]);
     }
     __syncthreads();
     // row kr of the transposed block: 128 bytes, written by 8 threads x 16 B
@@ -164,7 +197,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restri
     for (int i = 0; i < 4; ++i) {
         const int piece = t + 256 * i;          // 1024 pieces of 16 B
         const int kr = piece >> 3, off = (piece & 7) * 16;
-        st<u32x4>(q + (kb * kBlock + kr) * N + nb * kBlock + off, ld<u32x4>(&qt[kr][off]));
+        st<u32x4>(q + (kb * kBlock + kr) * N + nb * kBlock + off, ld<u32x4>(&qt[qt_off(kr, off)]));
     }
     if (t == 0) s[kb * (N / kBlock) + nb] = sc;
 }
