@@ -181,6 +181,18 @@ def run_extra(args):
         for name, tr in (("quant_weight_128x128 W", False), ("quant_weight_128x128 W transposed", True)):
             ms = time_launches(lambda i, tr=tr: fp8.fp8_quant_weight_128x128(w, transpose_out=tr), T, W, stream)
             extra_line("linear_trio", name, ms, nbytes=w.numel() * 5, args=args, config=cfg)
+        xh, dyh, wh = x.to(torch.bfloat16), dy.to(torch.bfloat16), w.to(torch.bfloat16)
+        for name, src, tr in (("quant_act_1x128_bf16 X rowwise", xh, False),
+                              ("quant_act_1x128_bf16 X token-wise", xh, True),
+                              ("quant_act_1x128_bf16 dY token-wise", dyh, True)):
+            ms = time_launches(lambda i, src=src, tr=tr: fp8.fp8_quant_act_1x128_bf16(src, transpose_out=tr),
+                               T, W, stream)
+            n = src.numel()
+            extra_line("linear_trio", name, ms, nbytes=n * 3 + (n // 128) * 4, args=args, config=cfg)
+        for name, tr in (("quant_weight_128x128_bf16 W", False), ("quant_weight_128x128_bf16 W transposed", True)):
+            ms = time_launches(lambda i, tr=tr: fp8.fp8_quant_weight_128x128_bf16(wh, transpose_out=tr), T, W, stream)
+            extra_line("linear_trio", name, ms, nbytes=wh.numel() * 3, args=args, config=cfg)
+        del xh, dyh, wh
         yb = torch.empty((TOK, OUT), dtype=torch.bfloat16, device="cuda")
         dxb = torch.empty((TOK, IN), dtype=torch.bfloat16, device="cuda")
         dwf = torch.empty((OUT, IN), dtype=torch.float32, device="cuda")

@@ -22,9 +22,12 @@ BSCALE_1x128 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
 
+ABI_VERSION = 2
 EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
            "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
+           "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16",
            "fp8fg_status_string", "fp8fg_abi_version")
+_COMPUTE = EXPORTS[:7]
 
 
 class Fp8fgError(RuntimeError):
@@ -51,7 +54,9 @@ def load_library(path=LIB_PATH):
     lib.fp8_gemm_blockscaled.argtypes = [vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp]
     lib.fp8_grouped_gemm_contiguous.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     lib.fp8_grouped_gemm_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
-    for name in EXPORTS[:5]:
+    lib.fp8_quant_act_1x128_bf16.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    lib.fp8_quant_weight_128x128_bf16.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    for name in _COMPUTE:
         getattr(lib, name).restype = ctypes.c_int
     lib.fp8fg_status_string.argtypes = [ctypes.c_int]
     lib.fp8fg_status_string.restype = ctypes.c_char_p
@@ -97,37 +102,53 @@ def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
-def fp8_quant_act_1x128(x, transpose_out=False, q=None, s=None):
-    """1x128 activation quantization of x f32 [M][K].
-    transpose_out=False -> (q u8 [M][K], s f32 [K/128][M]);
-    transpose_out=True  -> (q u8 [K][M], s f32 [M/128][K]) (tiles along M)."""
+def _quant_act(fn, x, dtype, transpose_out, q, s):
     M, K = x.shape
-    _need(x, torch.float32, (M, K), "x")
+    _need(x, dtype, (M, K), "x")
     qs = (K, M) if transpose_out else (M, K)
     ss = (M // 128, K) if transpose_out else (K // 128, M)
     q = _empty(qs, torch.uint8, x) if q is None else q
     s = _empty(ss, torch.float32, x) if s is None else s
     _need(q, torch.uint8, qs, "q")
     _need(s, torch.float32, ss, "s")
-    _check("fp8_quant_act_1x128", load_library().fp8_quant_act_1x128(
-        _ptr(x), M, K, int(bool(transpose_out)), _ptr(q), _ptr(s), _stream(x)))
+    _check(fn, getattr(load_library(), fn)(_ptr(x), M, K, int(bool(transpose_out)), _ptr(q), _ptr(s), _stream(x)))
     return q, s
 
 
-def fp8_quant_weight_128x128(w, transpose_out=False, q=None, s=None):
-    """128x128 weight quantization of w f32 [N][K] -> (q u8 [N][K], s f32 [N/128][K/128]),
-    or the transposed codes and scales when transpose_out=True."""
+def _quant_weight(fn, w, dtype, transpose_out, q, s):
     N, K = w.shape
-    _need(w, torch.float32, (N, K), "w")
+    _need(w, dtype, (N, K), "w")
     qs = (K, N) if transpose_out else (N, K)
     ss = (K // 128, N // 128) if transpose_out else (N // 128, K // 128)
     q = _empty(qs, torch.uint8, w) if q is None else q
     s = _empty(ss, torch.float32, w) if s is None else s
     _need(q, torch.uint8, qs, "q")
     _need(s, torch.float32, ss, "s")
-    _check("fp8_quant_weight_128x128", load_library().fp8_quant_weight_128x128(
-        _ptr(w), N, K, int(bool(transpose_out)), _ptr(q), _ptr(s), _stream(w)))
+    _check(fn, getattr(load_library(), fn)(_ptr(w), N, K, int(bool(transpose_out)), _ptr(q), _ptr(s), _stream(w)))
     return q, s
+
+
+def fp8_quant_act_1x128(x, transpose_out=False, q=None, s=None):
+    """1x128 activation quantization of x f32 [M][K].
+    transpose_out=False -> (q u8 [M][K], s f32 [K/128][M]);
+    transpose_out=True  -> (q u8 [K][M], s f32 [M/128][K]) (tiles along M)."""
+    return _quant_act("fp8_quant_act_1x128", x, torch.float32, transpose_out, q, s)
+
+
+def fp8_quant_act_1x128_bf16(x, transpose_out=False, q=None, s=None):
+    """fp8_quant_act_1x128 for x bf16 [M][K] (quantizes the exactly widened values)."""
+    return _quant_act("fp8_quant_act_1x128_bf16", x, torch.bfloat16, transpose_out, q, s)
+
+
+def fp8_quant_weight_128x128(w, transpose_out=False, q=None, s=None):
+    """128x128 weight quantization of w f32 [N][K] -> (q u8 [N][K], s f32 [N/128][K/128]),
+    or the transposed codes and scales when transpose_out=True."""
+    return _quant_weight("fp8_quant_weight_128x128", w, torch.float32, transpose_out, q, s)
+
+
+def fp8_quant_weight_128x128_bf16(w, transpose_out=False, q=None, s=None):
+    """fp8_quant_weight_128x128 for w bf16 [N][K] (quantizes the exactly widened values)."""
+    return _quant_weight("fp8_quant_weight_128x128_bf16", w, torch.bfloat16, transpose_out, q, s)
 
 
 def _out_dtype(out_dtype):

@@ -38,8 +38,9 @@ const char* fp8fg_status_string(int status) {
     }
 }
 
-int fp8_quant_act_1x128(const float* x, int64_t M, int64_t K, int transpose_out, uint8_t* q, float* s,
-                        void* stream) {
+// the quantizers' checks, shared by the fp32 and bf16 entry points
+static int quant_act(const void* x, int bf16, int64_t M, int64_t K, int transpose_out, uint8_t* q, float* s,
+                     void* stream) {
     if (!x || !q || !s) return FP8FG_ERR_NULL;
     if (M < 0 || K < 0) return FP8FG_ERR_SHAPE;
     if (transpose_out != 0 && transpose_out != 1) return FP8FG_ERR_UNSUPPORTED;
@@ -49,11 +50,11 @@ int fp8_quant_act_1x128(const float* x, int64_t M, int64_t K, int transpose_out,
     if (M > kMaxDim || K > kMaxDim || (M > 0 && K > kMaxElems / M)) return FP8FG_ERR_UNSUPPORTED;
     if (transpose_out == 1 && ((K + 63) / 64 > 65535)) return FP8FG_ERR_UNSUPPORTED;
     if (M == 0 || K == 0) return FP8FG_OK;
-    return hip_status(fp8fg::launch_quant_act(x, M, K, transpose_out, q, s, static_cast<hipStream_t>(stream)));
+    return hip_status(fp8fg::launch_quant_act(x, bf16, M, K, transpose_out, q, s, static_cast<hipStream_t>(stream)));
 }
 
-int fp8_quant_weight_128x128(const float* w, int64_t N, int64_t K, int transpose_out, uint8_t* q, float* s,
-                             void* stream) {
+static int quant_weight(const void* w, int bf16, int64_t N, int64_t K, int transpose_out, uint8_t* q, float* s,
+                        void* stream) {
     if (!w || !q || !s) return FP8FG_ERR_NULL;
     if (N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8FG_ERR_SHAPE;
     if (transpose_out != 0 && transpose_out != 1) return FP8FG_ERR_UNSUPPORTED;
@@ -61,7 +62,28 @@ int fp8_quant_weight_128x128(const float* w, int64_t N, int64_t K, int transpose
     if (N > kMaxDim || K > kMaxDim || (N > 0 && K > kMaxElems / N)) return FP8FG_ERR_UNSUPPORTED;
     if (N / 128 > 65535) return FP8FG_ERR_UNSUPPORTED;
     if (N == 0 || K == 0) return FP8FG_OK;
-    return hip_status(fp8fg::launch_quant_weight(w, N, K, transpose_out, q, s, static_cast<hipStream_t>(stream)));
+    return hip_status(
+        fp8fg::launch_quant_weight(w, bf16, N, K, transpose_out, q, s, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_quant_act_1x128(const float* x, int64_t M, int64_t K, int transpose_out, uint8_t* q, float* s,
+                        void* stream) {
+    return quant_act(x, 0, M, K, transpose_out, q, s, stream);
+}
+
+int fp8_quant_act_1x128_bf16(const uint16_t* x, int64_t M, int64_t K, int transpose_out, uint8_t* q, float* s,
+                             void* stream) {
+    return quant_act(x, 1, M, K, transpose_out, q, s, stream);
+}
+
+int fp8_quant_weight_128x128(const float* w, int64_t N, int64_t K, int transpose_out, uint8_t* q, float* s,
+                             void* stream) {
+    return quant_weight(w, 0, N, K, transpose_out, q, s, stream);
+}
+
+int fp8_quant_weight_128x128_bf16(const uint16_t* w, int64_t N, int64_t K, int transpose_out, uint8_t* q, float* s,
+                                  void* stream) {
+    return quant_weight(w, 1, N, K, transpose_out, q, s, stream);
 }
 
 int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int bscale_kind,

@@ -19,6 +19,19 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __device__ __forceinline__ T ld(const void* p) { return *reinterpret_cast<const T*>(p); }
+
+// Quantizer inputs: fp32, or bf16 carried as its 16-bit pattern (uint16_t).
+// A bf16 value widens to fp32 exactly: its bits become the high half.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float f32_of(float v) { return v; }
+__device__ __forceinline__ float f32_of(uint16_t b) { return __builtin_bit_cast(float, uint32_t(b) << 16); }
+// 4 consecutive elements (16-byte or 8-byte aligned)
+__device__ __forceinline__ v4f load4(const float* p) { return ld<v4f>(p); }
+__device__ __forceinline__ v4f load4(const uint16_t* p) {
+    const u32x2_t w = ld<u32x2_t>(p);
+    return v4f{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xFFFF0000u),
+               __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xFFFF0000u)};
+}
 template <typename T>
 __device__ __forceinline__ void st(void* p, T v) { *reinterpret_cast<T*>(p) = v; }
 

@@ -7,9 +7,10 @@
 
 namespace fp8fg {
 
-hipError_t launch_quant_act(const float* x, int64_t M, int64_t K, int transpose_out, uint8_t* q,
+// x / w: fp32, or bf16 bit patterns when bf16 != 0
+hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, int transpose_out, uint8_t* q,
                             float* s, hipStream_t stream);
-hipError_t launch_quant_weight(const float* w, int64_t N, int64_t K, int transpose_out, uint8_t* q,
+hipError_t launch_quant_weight(const void* w, int bf16, int64_t N, int64_t K, int transpose_out, uint8_t* q,
                                float* s, hipStream_t stream);
 
 enum class GemmMode : int { Dense = 0, Contig = 1, Masked = 2 };

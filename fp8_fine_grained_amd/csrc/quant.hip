@@ -10,8 +10,9 @@
 // which E4M3 code it rounds to and divides only when that cannot be decided,
 // so every byte and scale is reproducible bit for bit.
 //
-// All three kernels are HBM-bound: 4 bytes read and 1 byte written per
-// element, plus 4 bytes of scale per group.
+// All three kernels are HBM-bound: 4 bytes (fp32 input) or 2 bytes (bf16
+// input, widened exactly) read and 1 byte written per element, plus 4 bytes of
+// scale per group.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -24,18 +25,18 @@ namespace fp8fg {
 // kb0 = blockIdx.x*U, so U independent 16-byte loads per lane are in flight
 // before the first reduction and no index needs a division.  Scales go to
 // s[kb][m].
-template <int U>
-__global__ __launch_bounds__(256) void quant_act_rows_kernel(const float* __restrict__ x, int64_t M, int64_t K,
-                                                             uint8_t* __restrict__ q, float* __restrict__ s) {
+template <int U, class T>
+__device__ __forceinline__ void quant_act_rows_body(const T* __restrict__ x, int64_t M, int64_t K,
+                                                    uint8_t* __restrict__ q, float* __restrict__ s) {
     const int lane = threadIdx.x & 31;
     const int64_t kbs = K / kBlock;
     const int64_t kb0 = int64_t(blockIdx.x) * U;
     for (int64_t m = int64_t(blockIdx.y) * 8 + (threadIdx.x >> 5); m < M; m += int64_t(gridDim.y) * 8) {
-        const float* xr = x + m * K + kb0 * kBlock + lane * 4;
+        const T* xr = x + m * K + kb0 * kBlock + lane * 4;
         uint8_t* qr = q + m * K + kb0 * kBlock + lane * 4;
         v4f v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = kb0 + u < kbs ? ld<v4f>(xr + u * kBlock) : v4f{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < U; ++u) v[u] = kb0 + u < kbs ? load4(xr + u * kBlock) : v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (kb0 + u >= kbs) break;
@@ -58,9 +59,9 @@ __global__ __launch_bounds__(256) void quant_act_rows_kernel(const float* __rest
 // whole 128-byte row segments.
 constexpr int kTokCh = 64;
 
-__global__ __launch_bounds__(256) void quant_act_tokens_kernel(const float* __restrict__ x, int64_t M,
-                                                               int64_t K, uint8_t* __restrict__ q,
-                                                               float* __restrict__ s) {
+template <class T>
+__device__ __forceinline__ void quant_act_tokens_body(const T* __restrict__ x, int64_t M, int64_t K,
+                                                      uint8_t* __restrict__ q, float* __restrict__ s) {
     __shared__ __align__(16) float tile[kBlock][kTokCh + 1];
     __shared__ float part[4][kTokCh];
     // the codes reuse the tile's memory: every read of the tile precedes the
@@ -71,20 +72,20 @@ __global__ __launch_bounds__(256) void quant_act_tokens_kernel(const float* __re
     const int t = threadIdx.x;
     const int64_t mb = blockIdx.x;
     const int64_t k0 = int64_t(blockIdx.y) * kTokCh;
-    const float* xb = x + mb * kBlock * K + k0;
+    const T* xb = x + mb * kBlock * K + k0;
     const bool vec = ((K & 3) == 0);
     const int c4 = (t & 15) * 4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = (t >> 4) + 16 * i;
-        const float* p = xb + int64_t(r) * K + c4;
+        const T* p = xb + int64_t(r) * K + c4;
         float e[4];
         if (vec && k0 + c4 + 4 <= K) {
-            const v4f v = ld<v4f>(p);
+            const v4f v = load4(p);
             e[0] = v[0]; e[1] = v[1]; e[2] = v[2]; e[3] = v[3];
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) e[j] = (k0 + c4 + j < K) ? p[j] : 0.0f;
+            for (int j = 0; j < 4; ++j) e[j] = (k0 + c4 + j < K) ? f32_of(p[j]) : 0.0f;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) tile[r][c4 + j] = e[j];
@@ -149,22 +150,21 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&in)[4], uint32_t (
     out[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
 }
 
-__global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restrict__ w, int64_t N,
-                                                           int64_t K, int transpose_out,
-                                                           uint8_t* __restrict__ q,
-                                                           float* __restrict__ s) {
+template <class T>
+__device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64_t N, int64_t K, int transpose_out,
+                                                  uint8_t* __restrict__ q, float* __restrict__ s) {
     __shared__ float red[4];
     __shared__ __align__(16) uint8_t qt[kBlock * (kBlock + 16)];
     const int t = threadIdx.x;
     const int64_t nb = blockIdx.y, kb = blockIdx.x;
     const int c4 = (t & 31) * 4;
     const int r0 = (t >> 5) * 16;
-    const float* wb = w + nb * kBlock * K + kb * kBlock + c4;
+    const T* wb = w + nb * kBlock * K + kb * kBlock + c4;
     v4f v[16];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        v[i] = ld<v4f>(wb + int64_t(r0 + i) * K);
+        v[i] = load4(wb + int64_t(r0 + i) * K);
         amax = fmaxf(amax, abs_max4(v[i]));
     }
     amax = wave_max(amax);
@@ -203,26 +203,63 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restri
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_quant_act(const float* x, int64_t M, int64_t K, int transpose_out, uint8_t* q,
-                            float* s, hipStream_t stream) {
+// One plain kernel per element type (fp32, bf16 bits).
+#define FP8FG_QUANT_KERNELS(T, SUFFIX)                                                                     \
+    __global__ __launch_bounds__(256) void quant_act_rows_##SUFFIX(const T* __restrict__ x, int64_t M,      \
+                                                                   int64_t K, uint8_t* __restrict__ q,     \
+                                                                   float* __restrict__ s) {                \
+        quant_act_rows_body<4>(x, M, K, q, s);                                                             \
+    }                                                                                                      \
+    __global__ __launch_bounds__(256) void quant_act_tokens_##SUFFIX(const T* __restrict__ x, int64_t M,    \
+                                                                     int64_t K, uint8_t* __restrict__ q,   \
+                                                                     float* __restrict__ s) {              \
+        quant_act_tokens_body(x, M, K, q, s);                                                              \
+    }                                                                                                      \
+    __global__ __launch_bounds__(256) void quant_weight_##SUFFIX(const T* __restrict__ w, int64_t N,        \
+                                                                 int64_t K, int transpose_out,             \
+                                                                 uint8_t* __restrict__ q,                  \
+                                                                 float* __restrict__ s) {                  \
+        quant_weight_body(w, N, K, transpose_out, q, s);                                                   \
+    }
+FP8FG_QUANT_KERNELS(float, f32)
+FP8FG_QUANT_KERNELS(uint16_t, bf16)
+#undef FP8FG_QUANT_KERNELS
+
+template <class T>
+static hipError_t launch_act(const T* x, int64_t M, int64_t K, int transpose_out, uint8_t* q, float* s,
+                             hipStream_t stream, void (*rows)(const T*, int64_t, int64_t, uint8_t*, float*),
+                             void (*tokens)(const T*, int64_t, int64_t, uint8_t*, float*)) {
     if (!transpose_out) {
         constexpr int U = 4;
         const int64_t chunks = (K / kBlock + U - 1) / U;
         int64_t row_groups = (M + 7) / 8;
         if (row_groups > 65535) row_groups = 65535;      // the kernel strides over the rest
-        hipLaunchKernelGGL(quant_act_rows_kernel<U>, dim3(unsigned(chunks), unsigned(row_groups)), dim3(256), 0,
-                           stream, x, M, K, q, s);
+        hipLaunchKernelGGL(rows, dim3(unsigned(chunks), unsigned(row_groups)), dim3(256), 0, stream, x, M, K, q, s);
     } else {
         const dim3 grid(unsigned(M / kBlock), unsigned((K + kTokCh - 1) / kTokCh));
-        hipLaunchKernelGGL(quant_act_tokens_kernel, grid, dim3(256), 0, stream, x, M, K, q, s);
+        hipLaunchKernelGGL(tokens, grid, dim3(256), 0, stream, x, M, K, q, s);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_quant_weight(const float* w, int64_t N, int64_t K, int transpose_out, uint8_t* q,
+hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, int transpose_out, uint8_t* q,
+                            float* s, hipStream_t stream) {
+    if (bf16)
+        return launch_act(static_cast<const uint16_t*>(x), M, K, transpose_out, q, s, stream, quant_act_rows_bf16,
+                          quant_act_tokens_bf16);
+    return launch_act(static_cast<const float*>(x), M, K, transpose_out, q, s, stream, quant_act_rows_f32,
+                      quant_act_tokens_f32);
+}
+
+hipError_t launch_quant_weight(const void* w, int bf16, int64_t N, int64_t K, int transpose_out, uint8_t* q,
                                float* s, hipStream_t stream) {
     const dim3 grid(unsigned(K / kBlock), unsigned(N / kBlock));
-    hipLaunchKernelGGL(quant_weight_kernel, grid, dim3(256), 0, stream, w, N, K, transpose_out, q, s);
+    if (bf16)
+        hipLaunchKernelGGL(quant_weight_bf16, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(w), N, K,
+                           transpose_out, q, s);
+    else
+        hipLaunchKernelGGL(quant_weight_f32, grid, dim3(256), 0, stream, static_cast<const float*>(w), N, K,
+                           transpose_out, q, s);
     return hipGetLastError();
 }
 

@@ -36,11 +36,19 @@
  *     and scales f32 [K/128][R] ("kb-major").  A 128x128-scaled [N][K] operand
  *     stores codes u8 [N][K] and scales f32 [N/128][K/128].
  *   - GEMM: C[M][N] = A[M][K] . B[N][K]^T, both operands K-major (a Linear
- *     layer y = x . W^T with W [out][in]).  Each 128-wide K-block is summed
- *     by FP8 MFMA into a fresh FP32 partial, then folded into an FP32
- *     accumulator as acc += partial * (sA * sB).  Output row-major [M][N],
- *     BF16 (round-to-nearest-even) or FP32.  Results are deterministic
- *     (no atomics, no split-K).
+ *     layer y = x . W^T with W [out][in]).  C is the sum over k of
+ *     decode(a) * sA * decode(b) * sB, the scales of each 128-wide K-block
+ *     applied once per block in FP32 (promotion at a fixed K interval).
+ *     Output row-major [M][N], BF16 (round-to-nearest-even) or FP32.
+ *     Accuracy contract, element by element, against the exact real-number
+ *     result C*:  |C - C*| <= 2^-14 * S  (FP32 out), with
+ *     S = sum_k |decode(a) sA decode(b) sB|, plus one BF16 rounding of C*
+ *     for BF16 out.  The codes are widened exactly to BF16 and multiplied on
+ *     the BF16 matrix cores (exact products, FP32 sums).  The environment
+ *     variable FP8FG_GEMM_ENGINE=fp8mfma (read at every call) selects the
+ *     FP8 matrix-core engine instead: faster, but held only to 2^-9 * S,
+ *     because gfx950's FP8 MFMA keeps about 14 bits when it sums each group
+ *     of 8 products.  Results are deterministic (no atomics, no split-K).
  */
 #ifndef FP8FG_H
 #define FP8FG_H
@@ -51,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 1
+#define FP8FG_ABI_VERSION 2
 
 enum fp8fg_status {
     FP8FG_OK = 0,
@@ -93,6 +101,22 @@ int fp8_quant_act_1x128(const float* x, int64_t M, int64_t K, int transpose_out,
  */
 int fp8_quant_weight_128x128(const float* w, int64_t N, int64_t K, int transpose_out,
                              uint8_t* q, float* s, void* stream);
+
+/*
+ * The same two quantizations with BF16 inputs: x / w hold bf16 bit patterns
+ * (u16, same shapes and layouts as above).  The tensors around the FP8 GEMMs
+ * stay in a wider format (DeepSeek-V3 FP8 knowledge-base page, section on
+ * the mixed-precision framework), and BF16 is the one named beside FP8 ("The
+ * Insider Secrets Of Deepseek Discovered", passage on FP8 and BF16 modes).
+ * Each bf16 value widens to fp32 exactly, so codes and scales are identical to
+ * those of the fp32 entry points on the widened tensor; the reads are half as
+ * many bytes.  Sizes, alignment (16 bytes for every pointer), errors and
+ * layouts as for the fp32 calls.
+ */
+int fp8_quant_act_1x128_bf16(const uint16_t* x, int64_t M, int64_t K, int transpose_out,
+                             uint8_t* q, float* s, void* stream);
+int fp8_quant_weight_128x128_bf16(const uint16_t* w, int64_t N, int64_t K, int transpose_out,
+                                  uint8_t* q, float* s, void* stream);
 
 /*
  * Dense block-scaled FP8 GEMM: C[M][N] = A[M][K] . B[N][K]^T.

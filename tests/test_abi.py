@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fp8.abi_version() == 1
+    assert fp8.abi_version() == fp8.ABI_VERSION == 2
     assert fp8.status_string(0) == "ok"
     for code in (-1, -2, -3, -4, -5):
         assert fp8.status_string(code) not in ("ok", "unknown status")
@@ -56,6 +56,23 @@ def test_quant_argument_errors():
     assert w(P, 128, 128, 0, NUL, P2, NUL) == ENULL
     assert w(P, 128, 128, 0, P, MIS, NUL) == EALIGN
     assert w(P, 0, 128, 1, P, P2, NUL) == OK
+
+
+def test_bf16_quant_argument_errors():
+    lib = fp8.load_library()
+    q = lib.fp8_quant_act_1x128_bf16
+    assert q(NUL, 128, 128, 0, P, P2, NUL) == ENULL
+    assert q(P, 128, 100, 0, P, P2, NUL) == ESHAPE
+    assert q(P, 100, 128, 1, P, P2, NUL) == ESHAPE
+    assert q(MIS, 128, 128, 1, P, P2, NUL) == EALIGN
+    assert q(P, 128, 128, -1, P, P2, NUL) == EUNSUP
+    assert q(P, 0, 128, 1, P, P2, NUL) == OK
+    w = lib.fp8_quant_weight_128x128_bf16
+    assert w(P, 128, 64, 1, P, P2, NUL) == ESHAPE
+    assert w(P, 128, 128, 0, P, NUL, NUL) == ENULL
+    assert w(MIS, 128, 128, 0, P, P2, NUL) == EALIGN
+    assert w(P, 128, 128, 3, P, P2, NUL) == EUNSUP
+    assert w(P, 128, 0, 0, P, P2, NUL) == OK
 
 
 def test_gemm_argument_errors():
@@ -90,3 +107,5 @@ def test_python_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         fp8.fp8_quant_act_1x128(torch.zeros(4, 128))
+    with pytest.raises(ValueError):
+        fp8.fp8_quant_act_1x128_bf16(torch.zeros(4, 128, dtype=torch.bfloat16))

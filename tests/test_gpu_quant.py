@@ -130,3 +130,77 @@ def test_full_size_quantizers_linear_trio():
     for t in (False, True):
         q, s = fp8.fp8_quant_weight_128x128(dev(w), transpose_out=t)
         assert_same(q, s, *quant.quant_weight_128x128(w, transpose_out=t), f"trio W T={t}")
+
+
+# ---------------------------------------------------------------------------
+# bf16 inputs: the entry points widen each bf16 exactly to fp32, so their codes
+# and scales must equal the oracle's on the widened values.  Inputs are made
+# bf16-representable by clearing the low 16 bits of fp32 values.
+
+def bf16_pair(x):
+    bits = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    widened = (bits & np.uint32(0xFFFF0000)).view(np.float32)
+    top = (bits >> np.uint32(16)).astype(np.uint16)
+    return torch.from_numpy(top).to(DEV).view(torch.bfloat16), widened
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (5, 384), (257, 1024)])
+def test_bf16_act_rowwise(M, K):
+    rng = np.random.default_rng(3 * M + K)
+    xb, x = bf16_pair(workloads.activations(rng, M, K, 0.01, 100.0))
+    q, s = fp8.fp8_quant_act_1x128_bf16(xb)
+    assert_same(q, s, *quant.quant_act_1x128(x), f"bf16 rowwise {M}x{K}")
+
+
+@pytest.mark.parametrize("M,K", [(128, 1), (128, 6), (256, 100), (384, 516), (128, 2048)])
+def test_bf16_act_tokenwise(M, K):
+    rng = np.random.default_rng(5 * M + K)
+    xb, x = bf16_pair(workloads.activations(rng, M, K, 0.01, 100.0))
+    q, s = fp8.fp8_quant_act_1x128_bf16(xb, transpose_out=True)
+    assert_same(q, s, *quant.quant_act_1x128_tokenwise(x), f"bf16 tokenwise {M}x{K}")
+
+
+@pytest.mark.parametrize("N,K", [(128, 128), (384, 256)])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_bf16_weight(N, K, transpose):
+    rng = np.random.default_rng(N * 3 + K)
+    w = workloads.weights(rng, N, K)
+    w[N - 1, 9] = -2.5
+    wb, w = bf16_pair(w)
+    q, s = fp8.fp8_quant_weight_128x128_bf16(wb, transpose_out=transpose)
+    assert_same(q, s, *quant.quant_weight_128x128(w, transpose_out=transpose), f"bf16 weight {N}x{K} T={transpose}")
+
+
+def test_bf16_special_tiles():
+    """bf16 subnormals, -0, a scale that underflows, the largest bf16 values."""
+    x = np.zeros((6, 256), np.float32)
+    x[0, 3] = -0.0
+    x[1, :128] = np.float32(2.0 ** -133) * np.arange(128, dtype=np.float32)
+    x[2, 0] = np.float32(2.0 ** -133)
+    x[3, :128] = np.linspace(-448, 448, 128, dtype=np.float32)
+    x[4, 128:] = np.float32(3.38e38) * np.linspace(-1, 1, 128, dtype=np.float32)
+    x[5, :] = np.float32(2.0 ** -10) * np.arange(256) / 7
+    xb, xw = bf16_pair(x)
+    q, s = fp8.fp8_quant_act_1x128_bf16(xb)
+    assert_same(q, s, *quant.quant_act_1x128(xw), "bf16 special tiles")
+    xb, xw = bf16_pair(np.tile(x, (22, 1))[:128])
+    q, s = fp8.fp8_quant_act_1x128_bf16(xb, transpose_out=True)
+    assert_same(q, s, *quant.quant_act_1x128_tokenwise(xw), "bf16 special tiles, token-wise")
+    wb, ww = bf16_pair(np.tile(x[:, :128], (22, 1))[:128])
+    for t in (False, True):
+        q, s = fp8.fp8_quant_weight_128x128_bf16(wb, transpose_out=t)
+        assert_same(q, s, *quant.quant_weight_128x128(ww, transpose_out=t), f"bf16 special weight T={t}")
+
+
+def test_bf16_full_size_linear_trio():
+    x, w, dy = workloads.linear_trio()
+    for name, arr in (("X", x), ("dY", dy)):
+        ab, aw = bf16_pair(arr)
+        q, s = fp8.fp8_quant_act_1x128_bf16(ab)
+        assert_same(q, s, *quant.quant_act_1x128(aw), f"bf16 trio {name} rowwise")
+        q, s = fp8.fp8_quant_act_1x128_bf16(ab, transpose_out=True)
+        assert_same(q, s, *quant.quant_act_1x128_tokenwise(aw), f"bf16 trio {name} token-wise")
+    wb, ww = bf16_pair(w)
+    for t in (False, True):
+        q, s = fp8.fp8_quant_weight_128x128_bf16(wb, transpose_out=t)
+        assert_same(q, s, *quant.quant_weight_128x128(ww, transpose_out=t), f"bf16 trio W T={t}")
