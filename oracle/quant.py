@@ -106,3 +106,23 @@ def dequant_weight(q, s):
 def dequant32(q, s_full):
     """RN32(dec(q) * s) with s already expanded per element (for idempotence checks)."""
     return (e4m3.decode(q).astype(np.float32) * np.asarray(s_full, np.float32)).astype(np.float32)
+
+
+def requant_act_tokenwise(q, s):
+    """FP8 activation cache for backward.
+
+    "The Insider Secrets Of Deepseek Discovered", passage on Figure 6: with
+    Wgrad in FP8, a Linear's input can be kept in FP8 for the backward pass.
+    The Fprop operand is cached as rowwise 1x128 codes q u8 [R][K] with scales
+    s f32 [K/128][R]; the Wgrad operand is 1x128 along tokens.  Steps:
+        x'[r][k] = RN32(dec(q[r][k]) * s[k/128][r])   (fp32 dequantization)
+        (qt, st) = 1x128 quantization of x' along tokens, transposed out
+    Returns (qt u8 [K][R], st f32 [R/128][K]).  R and K multiples of 128.
+    """
+    q = np.asarray(q, dtype=np.uint8)
+    s = np.asarray(s, dtype=np.float32)
+    R, K = q.shape
+    assert R % 128 == 0 and K % 128 == 0, "R and K must be multiples of 128"
+    assert s.shape == (K // 128, R)
+    x = dequant32(q, np.repeat(s.T, 128, axis=1))
+    return quant_act_1x128_tokenwise(x)
