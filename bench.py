@@ -181,6 +181,10 @@ def run_extra(args):
         for name, tr in (("quant_weight_128x128 W", False), ("quant_weight_128x128 W transposed", True)):
             ms = time_launches(lambda i, tr=tr: fp8.fp8_quant_weight_128x128(w, transpose_out=tr), T, W, stream)
             extra_line("linear_trio", name, ms, nbytes=w.numel() * 5, args=args, config=cfg)
+        ms = time_launches(lambda i: fp8.fp8_requant_act_tokenwise(qx, sx, qt=qxt, st=sxt), T, W, stream)
+        n = x.numel()
+        extra_line("linear_trio", "requant_act_tokenwise X (rowwise FP8 cache -> token-wise)", ms,
+                   nbytes=n * 2 + (n // 128) * 8, args=args, config=cfg)
         xh, dyh, wh = x.to(torch.bfloat16), dy.to(torch.bfloat16), w.to(torch.bfloat16)
         for name, src, tr in (("quant_act_1x128_bf16 X rowwise", xh, False),
                               ("quant_act_1x128_bf16 X token-wise", xh, True),

@@ -22,12 +22,12 @@ BSCALE_1x128 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
            "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
-           "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16",
+           "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16", "fp8_requant_act_tokenwise",
            "fp8fg_status_string", "fp8fg_abi_version")
-_COMPUTE = EXPORTS[:7]
+_COMPUTE = EXPORTS[:8]
 
 
 class Fp8fgError(RuntimeError):
@@ -56,6 +56,7 @@ def load_library(path=LIB_PATH):
     lib.fp8_grouped_gemm_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     lib.fp8_quant_act_1x128_bf16.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.fp8_quant_weight_128x128_bf16.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    lib.fp8_requant_act_tokenwise.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     for name in _COMPUTE:
         getattr(lib, name).restype = ctypes.c_int
     lib.fp8fg_status_string.argtypes = [ctypes.c_int]
@@ -149,6 +150,21 @@ def fp8_quant_weight_128x128(w, transpose_out=False, q=None, s=None):
 def fp8_quant_weight_128x128_bf16(w, transpose_out=False, q=None, s=None):
     """fp8_quant_weight_128x128 for w bf16 [N][K] (quantizes the exactly widened values)."""
     return _quant_weight("fp8_quant_weight_128x128_bf16", w, torch.bfloat16, transpose_out, q, s)
+
+
+def fp8_requant_act_tokenwise(q, s, qt=None, st=None):
+    """Rowwise FP8 cache (q u8 [M][K], s f32 [K/128][M]) -> the token-wise
+    operand (qt u8 [K][M], st f32 [M/128][K]) of RN32(decode(q) * s)."""
+    M, K = q.shape
+    _need(q, torch.uint8, (M, K), "q")
+    _need(s, torch.float32, (K // 128, M), "s")
+    qt = _empty((K, M), torch.uint8, q) if qt is None else qt
+    st = _empty((M // 128, K), torch.float32, q) if st is None else st
+    _need(qt, torch.uint8, (K, M), "qt")
+    _need(st, torch.float32, (M // 128, K), "st")
+    _check("fp8_requant_act_tokenwise",
+           load_library().fp8_requant_act_tokenwise(_ptr(q), _ptr(s), M, K, _ptr(qt), _ptr(st), _stream(q)))
+    return qt, st
 
 
 def _out_dtype(out_dtype):

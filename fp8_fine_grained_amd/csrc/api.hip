@@ -86,6 +86,17 @@ int fp8_quant_weight_128x128_bf16(const uint16_t* w, int64_t N, int64_t K, int t
     return quant_weight(w, 1, N, K, transpose_out, q, s, stream);
 }
 
+int fp8_requant_act_tokenwise(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt, float* st,
+                              void* stream) {
+    if (!q || !s || !qt || !st) return FP8FG_ERR_NULL;
+    if (M < 0 || K < 0 || M % 128 != 0 || K % 128 != 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(s) || !aligned16(qt) || !aligned16(st)) return FP8FG_ERR_ALIGN;
+    if (M > kMaxDim || K > kMaxDim || (M > 0 && K > kMaxElems / M)) return FP8FG_ERR_UNSUPPORTED;
+    if (K / 64 > 65535 || M / 128 > 0x7FFFFFFF) return FP8FG_ERR_UNSUPPORTED;
+    if (M == 0 || K == 0) return FP8FG_OK;
+    return hip_status(fp8fg::launch_requant_act_tokens(q, s, M, K, qt, st, static_cast<hipStream_t>(stream)));
+}
+
 int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int bscale_kind,
                          void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
     if (!a || !sa || !b || !sb || !c) return FP8FG_ERR_NULL;

@@ -15,6 +15,7 @@ namespace fp8fg {
 // of HIP's struct-based uint4/float4.
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>

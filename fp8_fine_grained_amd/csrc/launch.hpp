@@ -10,6 +10,8 @@ namespace fp8fg {
 // x / w: fp32, or bf16 bit patterns when bf16 != 0
 hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, int transpose_out, uint8_t* q,
                             float* s, hipStream_t stream);
+hipError_t launch_requant_act_tokens(const uint8_t* qr, const float* sr, int64_t M, int64_t K, uint8_t* q, float* s,
+                                     hipStream_t stream);
 hipError_t launch_quant_weight(const void* w, int bf16, int64_t N, int64_t K, int transpose_out, uint8_t* q,
                                float* s, hipStream_t stream);
 

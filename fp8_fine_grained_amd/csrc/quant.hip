@@ -56,12 +56,47 @@ __device__ __forceinline__ void quant_act_rows_body(const T* __restrict__ x, int
 // on banks), each wave reduces one quarter of the tokens per channel, the
 // four partial maxima meet in LDS, every lane encodes 32 consecutive tokens of
 // its channel, and the codes return through LDS so that q^T is written in
-// whole 128-byte row segments.
+// whole 128-byte row segments.  The fp32 values come from a source: a dense
+// fp32 / bf16 tensor, or the rowwise FP8 cache (DenseSrc, CacheSrc).
 constexpr int kTokCh = 64;
 
+// four consecutive channels k .. k+3 of token m of a dense [M][K] tensor
+// (channels past K read as 0)
 template <class T>
-__device__ __forceinline__ void quant_act_tokens_body(const T* __restrict__ x, int64_t M, int64_t K,
-                                                      uint8_t* __restrict__ q, float* __restrict__ s) {
+struct DenseSrc {
+    const T* x;
+    int64_t K;
+    __device__ __forceinline__ void load4(int64_t m, int64_t k, float (&e)[4]) const {
+        const T* p = x + m * K + k;
+        if ((K & 3) == 0 && k + 4 <= K) {
+            const v4f v = fp8fg::load4(p);
+            e[0] = v[0]; e[1] = v[1]; e[2] = v[2]; e[3] = v[3];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) e[j] = (k + j < K) ? f32_of(p[j]) : 0.0f;
+        }
+    }
+};
+
+// The rowwise FP8 cache of a tensor (codes q [M][K], scales s [K/128][M]),
+// dequantized element by element as RN32(decode(code) * s): the decode is
+// exact (every E4M3 value is an fp32), the product rounds once.
+struct CacheSrc {
+    const uint8_t* q;
+    const float* s;
+    int64_t M, K;
+    __device__ __forceinline__ void load4(int64_t m, int64_t k, float (&e)[4]) const {
+        const uint32_t w = ld<uint32_t>(q + m * K + k);
+        const float sc = s[(k / kBlock) * M + m];
+        const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+        const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+        e[0] = lo[0] * sc; e[1] = lo[1] * sc; e[2] = hi[0] * sc; e[3] = hi[1] * sc;
+    }
+};
+
+template <class Src>
+__device__ __forceinline__ void quant_tokens_core(const Src& src, int64_t M, int64_t K, uint8_t* __restrict__ q,
+                                                  float* __restrict__ s) {
     __shared__ __align__(16) float tile[kBlock][kTokCh + 1];
     __shared__ float part[4][kTokCh];
     // the codes reuse the tile's memory: every read of the tile precedes the
@@ -72,21 +107,12 @@ __device__ __forceinline__ void quant_act_tokens_body(const T* __restrict__ x, i
     const int t = threadIdx.x;
     const int64_t mb = blockIdx.x;
     const int64_t k0 = int64_t(blockIdx.y) * kTokCh;
-    const T* xb = x + mb * kBlock * K + k0;
-    const bool vec = ((K & 3) == 0);
     const int c4 = (t & 15) * 4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = (t >> 4) + 16 * i;
-        const T* p = xb + int64_t(r) * K + c4;
         float e[4];
-        if (vec && k0 + c4 + 4 <= K) {
-            const v4f v = load4(p);
-            e[0] = v[0]; e[1] = v[1]; e[2] = v[2]; e[3] = v[3];
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) e[j] = (k0 + c4 + j < K) ? f32_of(p[j]) : 0.0f;
-        }
+        src.load4(mb * kBlock + r, k0 + c4, e);
 #pragma unroll
         for (int j = 0; j < 4; ++j) tile[r][c4 + j] = e[j];
     }
@@ -213,7 +239,7 @@ __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64
     __global__ __launch_bounds__(256) void quant_act_tokens_##SUFFIX(const T* __restrict__ x, int64_t M,    \
                                                                      int64_t K, uint8_t* __restrict__ q,   \
                                                                      float* __restrict__ s) {              \
-        quant_act_tokens_body(x, M, K, q, s);                                                              \
+        quant_tokens_core(DenseSrc<T>{x, K}, M, K, q, s);                                                  \
     }                                                                                                      \
     __global__ __launch_bounds__(256) void quant_weight_##SUFFIX(const T* __restrict__ w, int64_t N,        \
                                                                  int64_t K, int transpose_out,             \
@@ -224,6 +250,13 @@ __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64
 FP8FG_QUANT_KERNELS(float, f32)
 FP8FG_QUANT_KERNELS(uint16_t, bf16)
 #undef FP8FG_QUANT_KERNELS
+
+// FP8 activation cache -> token-wise Wgrad operand
+__global__ __launch_bounds__(256) void requant_act_tokens(const uint8_t* __restrict__ qr, const float* __restrict__ sr,
+                                                          int64_t M, int64_t K, uint8_t* __restrict__ q,
+                                                          float* __restrict__ s) {
+    quant_tokens_core(CacheSrc{qr, sr, M, K}, M, K, q, s);
+}
 
 template <class T>
 static hipError_t launch_act(const T* x, int64_t M, int64_t K, int transpose_out, uint8_t* q, float* s,
@@ -249,6 +282,13 @@ hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, int t
                           quant_act_tokens_bf16);
     return launch_act(static_cast<const float*>(x), M, K, transpose_out, q, s, stream, quant_act_rows_f32,
                       quant_act_tokens_f32);
+}
+
+hipError_t launch_requant_act_tokens(const uint8_t* qr, const float* sr, int64_t M, int64_t K, uint8_t* q, float* s,
+                                     hipStream_t stream) {
+    const dim3 grid(unsigned(M / kBlock), unsigned(K / kTokCh));
+    hipLaunchKernelGGL(requant_act_tokens, grid, dim3(256), 0, stream, qr, sr, M, K, q, s);
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_weight(const void* w, int bf16, int64_t N, int64_t K, int transpose_out, uint8_t* q,

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 2
+#define FP8FG_ABI_VERSION 3
 
 enum fp8fg_status {
     FP8FG_OK = 0,
@@ -117,6 +117,22 @@ int fp8_quant_act_1x128_bf16(const uint16_t* x, int64_t M, int64_t K, int transp
                              uint8_t* q, float* s, void* stream);
 int fp8_quant_weight_128x128_bf16(const uint16_t* w, int64_t N, int64_t K, int transpose_out,
                                   uint8_t* q, float* s, void* stream);
+
+/*
+ * FP8 activation cache for backward ("The Insider Secrets Of Deepseek
+ * Discovered", passage on Figure 6: with Wgrad in FP8, the input of a Linear
+ * can be kept in FP8 for the backward pass).  Builds the Wgrad operand from
+ * the cached Fprop operand without its fp32 source:
+ *   q: u8 [M][K] with s: f32 [K/128][M]  -- 1x128 codes along K (the output
+ *      of fp8_quant_act_1x128 with transpose_out = 0);
+ *   x'[m][k] = RN32(decode(q[m][k]) * s[k/128][m])  (fp32, one rounding);
+ *   qt: u8 [K][M], st: f32 [M/128][K]  -- 1x128 codes of x' along tokens,
+ *      transposed: exactly fp8_quant_act_1x128(x', transpose_out = 1).
+ * Requires M % 128 == 0 and K % 128 == 0; M * K < 2^40.  Codes 0x7F / 0xFF
+ * (NaN) in q give unspecified output.
+ */
+int fp8_requant_act_tokenwise(const uint8_t* q, const float* s, int64_t M, int64_t K,
+                              uint8_t* qt, float* st, void* stream);
 
 /*
  * Dense block-scaled FP8 GEMM: C[M][N] = A[M][K] . B[N][K]^T.

@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fp8.abi_version() == fp8.ABI_VERSION == 2
+    declared = int(re.search(r"#define FP8FG_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert fp8.abi_version() == fp8.ABI_VERSION == declared
     assert fp8.status_string(0) == "ok"
     for code in (-1, -2, -3, -4, -5):
         assert fp8.status_string(code) not in ("ok", "unknown status")
@@ -73,6 +74,18 @@ def test_bf16_quant_argument_errors():
     assert w(MIS, 128, 128, 0, P, P2, NUL) == EALIGN
     assert w(P, 128, 128, 3, P, P2, NUL) == EUNSUP
     assert w(P, 128, 0, 0, P, P2, NUL) == OK
+
+
+def test_requant_argument_errors():
+    r = fp8.load_library().fp8_requant_act_tokenwise
+    assert r(NUL, P, 128, 128, P, P2, NUL) == ENULL
+    assert r(P, P, 128, 128, P, NUL, NUL) == ENULL
+    assert r(P, P, 100, 128, P, P2, NUL) == ESHAPE       # tokens % 128
+    assert r(P, P, 128, 64, P, P2, NUL) == ESHAPE        # channels % 128
+    assert r(P, P, -128, 128, P, P2, NUL) == ESHAPE
+    assert r(P, MIS, 128, 128, P, P2, NUL) == EALIGN
+    assert r(P, P, 0, 128, P, P2, NUL) == OK
+    assert r(P, P, 128, 0, P, P2, NUL) == OK
 
 
 def test_gemm_argument_errors():

@@ -204,3 +204,45 @@ def test_bf16_full_size_linear_trio():
     for t in (False, True):
         q, s = fp8.fp8_quant_weight_128x128_bf16(wb, transpose_out=t)
         assert_same(q, s, *quant.quant_weight_128x128(ww, transpose_out=t), f"bf16 trio W T={t}")
+
+
+# ---------------------------------------------------------------------------
+# FP8 activation cache -> token-wise operand: bit-exact against the oracle.
+
+def _cache(rng, R, K):
+    q = rng.integers(0, 256, size=(R, K), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] ^= 0x01                          # no NaN codes
+    s = np.exp(rng.uniform(np.log(1e-8), np.log(1e4), size=(K // 128, R))).astype(np.float32)
+    s[0, 1] = 0.0
+    s[-1, 2] = np.float32(7e-41)
+    return q, s
+
+
+@pytest.mark.parametrize("M,K", [(128, 128), (256, 384), (384, 1024)])
+def test_requant_random(M, K):
+    rng = np.random.default_rng(M * 3 + K * 5)
+    q, s = _cache(rng, M, K)
+    qt, st = fp8.fp8_requant_act_tokenwise(dev(q), dev(s))
+    assert_same(qt, st, *quant.requant_act_tokenwise(q, s), f"requant {M}x{K}")
+
+
+def test_requant_every_code():
+    """All 254 non-NaN codes, each in every token position class, under unit,
+    power-of-two and general row scales."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    q = np.resize(codes, (256, 512)).astype(np.uint8)
+    q[1::2] = np.roll(q[1::2], 37, axis=1)
+    s = np.ones((4, 256), np.float32)
+    s[1] = 2.0 ** -7
+    s[2] = np.float32(1.0 / 3.0)
+    s[3] = np.linspace(1e-3, 10, 256, dtype=np.float32)
+    qt, st = fp8.fp8_requant_act_tokenwise(dev(q), dev(s))
+    assert_same(qt, st, *quant.requant_act_tokenwise(q, s), "requant every code")
+
+
+def test_requant_full_size_linear_trio():
+    """The Wgrad operand of the 8192x7168 activations, from their rowwise cache."""
+    x, _, _ = workloads.linear_trio()
+    q, s = quant.quant_act_1x128(x)
+    qt, st = fp8.fp8_requant_act_tokenwise(dev(q), dev(s))
+    assert_same(qt, st, *quant.requant_act_tokenwise(q, s), "requant trio X")
