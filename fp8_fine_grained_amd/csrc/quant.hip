@@ -49,6 +49,46 @@ __device__ __forceinline__ void quant_act_rows_body(const T* __restrict__ x, int
     }
 }
 
+// bf16 rows: 16 lanes x 8 elements (one 16-byte load each) per group, so that
+// every load moves as many bytes as the fp32 kernel's and the same number of
+// loads keeps twice the elements in flight.  A workgroup of sixteen
+// quarter-waves owns sixteen rows.
+__device__ __forceinline__ float quarterwave_max(float v) {
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ v4f widen_bf16x4(uint32_t w0, uint32_t w1) {
+    return v4f{__builtin_bit_cast(float, w0 << 16), __builtin_bit_cast(float, w0 & 0xFFFF0000u),
+               __builtin_bit_cast(float, w1 << 16), __builtin_bit_cast(float, w1 & 0xFFFF0000u)};
+}
+
+template <int U>
+__device__ __forceinline__ void quant_act_rows_bf16_body(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                         uint8_t* __restrict__ q, float* __restrict__ s) {
+    const int lane = threadIdx.x & 15;
+    const int64_t kbs = K / kBlock;
+    const int64_t kb0 = int64_t(blockIdx.x) * U;
+    for (int64_t m = int64_t(blockIdx.y) * 16 + (threadIdx.x >> 4); m < M; m += int64_t(gridDim.y) * 16) {
+        const uint16_t* xr = x + m * K + kb0 * kBlock + lane * 8;
+        uint8_t* qr = q + m * K + kb0 * kBlock + lane * 8;
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = kb0 + u < kbs ? ld<u32x4>(xr + u * kBlock) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (kb0 + u >= kbs) break;
+            const v4f lo = widen_bf16x4(v[u][0], v[u][1]), hi = widen_bf16x4(v[u][2], v[u][3]);
+            const float amax = quarterwave_max(fmaxf(abs_max4(lo), abs_max4(hi)));
+            const float sc = amax / 448.0f;
+            const float rc = 1.0f / sc;
+            st<u32x2_t>(qr + u * kBlock, u32x2_t{encode4(lo, sc, rc), encode4(hi, sc, rc)});
+            if (lane == 0) s[(kb0 + u) * M + m] = sc;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 1x128 tiles along M (tokens), codes written transposed: q [K][M],
 // s [M/128][K].  A workgroup owns 128 tokens x 64 channels: it stages the
@@ -60,37 +100,68 @@ __device__ __forceinline__ void quant_act_rows_body(const T* __restrict__ x, int
 // fp32 / bf16 tensor, or the rowwise FP8 cache (DenseSrc, CacheSrc).
 constexpr int kTokCh = 64;
 
-// four consecutive channels k .. k+3 of token m of a dense [M][K] tensor
-// (channels past K read as 0)
+// E consecutive channels k .. k+E-1 of token m of a dense [M][K] tensor
+// (channels past K read as 0): four per 16-byte load for fp32, eight for bf16
 template <class T>
 struct DenseSrc {
+    static constexpr int E = sizeof(T) == 4 ? 4 : 8;
     const T* x;
     int64_t K;
-    __device__ __forceinline__ void load4(int64_t m, int64_t k, float (&e)[4]) const {
+    // every channel of the workgroup's block exists and rows are 16-byte aligned
+    __device__ __forceinline__ bool full(int64_t k0) const { return (K & (E - 1)) == 0 && k0 + kTokCh <= K; }
+    __device__ __forceinline__ void load_fast(int64_t m, int64_t k, float (&e)[E]) const {
         const T* p = x + m * K + k;
-        if ((K & 3) == 0 && k + 4 <= K) {
-            const v4f v = fp8fg::load4(p);
-            e[0] = v[0]; e[1] = v[1]; e[2] = v[2]; e[3] = v[3];
+        {
+            if constexpr (E == 4) {
+                const v4f v = ld<v4f>(p);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) e[j] = v[j];
+            } else {
+                // (a bit_cast of a vector element would read element 0: shift
+                // and mask work on values)
+                const u32x4 w = ld<u32x4>(p);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    e[2 * j] = __builtin_bit_cast(float, w[j] << 16);
+                    e[2 * j + 1] = __builtin_bit_cast(float, w[j] & 0xFFFF0000u);
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void load(int64_t m, int64_t k, float (&e)[E]) const {
+        const T* p = x + m * K + k;
+        if ((K & (E - 1)) == 0 && k + E <= K) {
+            load_fast(m, k, e);
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) e[j] = (k + j < K) ? f32_of(p[j]) : 0.0f;
+            for (int j = 0; j < E; ++j) e[j] = (k + j < K) ? f32_of(p[j]) : 0.0f;
         }
     }
 };
 
 // The rowwise FP8 cache of a tensor (codes q [M][K], scales s [K/128][M]),
 // dequantized element by element as RN32(decode(code) * s): the decode is
-// exact (every E4M3 value is an fp32), the product rounds once.
+// exact (every E4M3 value is an fp32), the product rounds once.  Eight codes
+// per load.
 struct CacheSrc {
+    static constexpr int E = 8;
     const uint8_t* q;
     const float* s;
     int64_t M, K;
-    __device__ __forceinline__ void load4(int64_t m, int64_t k, float (&e)[4]) const {
-        const uint32_t w = ld<uint32_t>(q + m * K + k);
+    __device__ __forceinline__ bool full(int64_t) const { return true; }   // K is a multiple of 128
+    __device__ __forceinline__ void load(int64_t m, int64_t k, float (&e)[E]) const { load_fast(m, k, e); }
+    __device__ __forceinline__ void load_fast(int64_t m, int64_t k, float (&e)[E]) const {
+        const u32x2_t w = ld<u32x2_t>(q + m * K + k);
         const float sc = s[(k / kBlock) * M + m];
-        const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
-        const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
-        e[0] = lo[0] * sc; e[1] = lo[1] * sc; e[2] = hi[0] * sc; e[3] = hi[1] * sc;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 1.0f, false);
+            const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 1.0f, true);
+            e[4 * j] = lo[0] * sc;
+            e[4 * j + 1] = lo[1] * sc;
+            e[4 * j + 2] = hi[0] * sc;
+            e[4 * j + 3] = hi[1] * sc;
+        }
     }
 };
 
@@ -107,14 +178,27 @@ __device__ __forceinline__ void quant_tokens_core(const Src& src, int64_t M, int
     const int t = threadIdx.x;
     const int64_t mb = blockIdx.x;
     const int64_t k0 = int64_t(blockIdx.y) * kTokCh;
-    const int c4 = (t & 15) * 4;
+    // thread t loads E channels of rows t / (64 / E) + i * (256 E / 64)
+    constexpr int E = Src::E, TPR = kTokCh / E, RSTEP = 256 / TPR;
+    constexpr int NI = kBlock / RSTEP;
+    const int ce = (t % TPR) * E;
+    if (src.full(k0)) {             // uniform: all loads in flight before the first use
+        float e[NI][E];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = (t >> 4) + 16 * i;
-        float e[4];
-        src.load4(mb * kBlock + r, k0 + c4, e);
+        for (int i = 0; i < NI; ++i) src.load_fast(mb * kBlock + t / TPR + RSTEP * i, k0 + ce, e[i]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) tile[r][c4 + j] = e[j];
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int j = 0; j < E; ++j) tile[t / TPR + RSTEP * i][ce + j] = e[i][j];
+    } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int r = t / TPR + RSTEP * i;
+            float e[E];
+            src.load(mb * kBlock + r, k0 + ce, e);
+#pragma unroll
+            for (int j = 0; j < E; ++j) tile[r][ce + j] = e[j];
+        }
     }
     __syncthreads();
 
@@ -228,13 +312,23 @@ __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64
     if (t == 0) s[kb * (N / kBlock) + nb] = sc;
 }
 
+template <int U>
+__device__ __forceinline__ void quant_act_rows_dispatch(const float* x, int64_t M, int64_t K, uint8_t* q, float* s) {
+    quant_act_rows_body<U>(x, M, K, q, s);
+}
+template <int U>
+__device__ __forceinline__ void quant_act_rows_dispatch(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
+                                                        float* s) {
+    quant_act_rows_bf16_body<U>(x, M, K, q, s);
+}
+
 // ---------------------------------------------------------------------------
 // One plain kernel per element type (fp32, bf16 bits).
 #define FP8FG_QUANT_KERNELS(T, SUFFIX)                                                                     \
     __global__ __launch_bounds__(256) void quant_act_rows_##SUFFIX(const T* __restrict__ x, int64_t M,      \
                                                                    int64_t K, uint8_t* __restrict__ q,     \
                                                                    float* __restrict__ s) {                \
-        quant_act_rows_body<4>(x, M, K, q, s);                                                             \
+        quant_act_rows_dispatch<4>(x, M, K, q, s);                                                         \
     }                                                                                                      \
     __global__ __launch_bounds__(256) void quant_act_tokens_##SUFFIX(const T* __restrict__ x, int64_t M,    \
                                                                      int64_t K, uint8_t* __restrict__ q,   \
@@ -264,8 +358,9 @@ static hipError_t launch_act(const T* x, int64_t M, int64_t K, int transpose_out
                              void (*tokens)(const T*, int64_t, int64_t, uint8_t*, float*)) {
     if (!transpose_out) {
         constexpr int U = 4;
+        constexpr int rows_per_group = sizeof(T) == 4 ? 8 : 16;   // half-waves (fp32) or quarter-waves (bf16)
         const int64_t chunks = (K / kBlock + U - 1) / U;
-        int64_t row_groups = (M + 7) / 8;
+        int64_t row_groups = (M + rows_per_group - 1) / rows_per_group;
         if (row_groups > 65535) row_groups = 65535;      // the kernel strides over the rest
         hipLaunchKernelGGL(rows, dim3(unsigned(chunks), unsigned(row_groups)), dim3(256), 0, stream, x, M, K, q, s);
     } else {
