@@ -9,7 +9,7 @@ passage: per-tensor max-abs scaling is sensitive to activation outliers.
 This module measures, on the linear-layer workload (X [T][7168] with outlier
 channels, W [2048][7168], dY [T][2048]; the first T tokens), the relative
 error that quantization alone puts into the three GEMMs of the layer --
-Fprop Y = X W^T, Dgrad dX = dY W, Wgrad dW = dY^T X -- under four schemes:
+Fprop Y = X W^T, Dgrad dX = dY W, Wgrad dW = dY^T X -- under five schemes:
 
   fine_e4m3     the method: 1x128 tiles for X and dY (along channels for
                 Fprop / Dgrad, along tokens for Wgrad), 128x128 blocks for W,
@@ -18,6 +18,8 @@ Fprop Y = X W^T, Dgrad dX = dY W, Wgrad dW = dY^T X -- under four schemes:
   tensor_e4m3   one max-abs scale per tensor, E4M3 everywhere
   tensor_hybrid one scale per tensor, X and W in E4M3, dY in E5M2 (the
                 earlier practice)
+  mx_e4m3       microscaling (oracle/mx.py): blocks of 32 along each GEMM's
+                contraction axis with power-of-two (E8M0) scales, E4M3
 
 Each GEMM is computed exactly (float64) on the dequantized operands and
 compared with the float64 GEMM of the unquantized operands, so the numbers
@@ -27,9 +29,9 @@ Run ``python -m oracle.study`` for the table.
 
 import numpy as np
 
-from . import e4m3, e5m2, quant
+from . import e4m3, e5m2, mx, quant
 
-SCHEMES = ("fine_e4m3", "fine_hybrid", "tensor_e4m3", "tensor_hybrid")
+SCHEMES = ("fine_e4m3", "fine_hybrid", "tensor_e4m3", "tensor_hybrid", "mx_e4m3")
 GEMMS = ("fprop", "dgrad", "wgrad")
 
 
@@ -67,8 +69,20 @@ def _fine_act_tokens(x, fmt):
     return _fine_act_rows(np.ascontiguousarray(np.asarray(x, np.float32).T), fmt).T
 
 
+def _mx_rows(x):
+    """MX quantize-dequantize of each row (blocks of 32 along the last axis)."""
+    return mx.dequant_mx(*mx.quant_mx_1x32(np.ascontiguousarray(x, dtype=np.float32)))
+
+
 def operands(x, w, dy, scheme):
     """Dequantized float64 operands (A, B) of each GEMM, C = A . B^T."""
+    if scheme == "mx_e4m3":
+        x32, w32, d32 = (np.asarray(v, np.float32) for v in (x, w, dy))
+        return {
+            "fprop": (_mx_rows(x32), _mx_rows(w32)),
+            "dgrad": (_mx_rows(d32), _mx_rows(w32.T)),
+            "wgrad": (_mx_rows(d32.T), _mx_rows(x32.T)),
+        }
     if scheme.startswith("fine"):
         g = "e5m2" if scheme == "fine_hybrid" else "e4m3"
         wq = quant.dequant_weight(*quant.quant_weight_128x128(w))
