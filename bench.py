@@ -51,7 +51,7 @@ def parse():
                         "dense_fprop inputs (copy: a 1 GiB device-to-device copy, the byte-counter "
                         "calibration); prints no JSON")
     p.add_argument("--workload", default="dense_fprop",
-                   choices=["dense_fprop", "dense_small", "linear_trio", "moe_contig", "moe_masked"],
+                   choices=["dense_fprop", "dense_small", "linear_trio", "moe_contig", "moe_masked", "dense_mx"],
                    help="dense_fprop is the headline step; the others print one line per measured kernel")
     return p.parse_args()
 
@@ -120,15 +120,16 @@ def time_launches(fn, steps, warmup, stream):
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
-def extra_line(workload, kernel, ms, flops=None, nbytes=None, args=None, config=None):
+def extra_line(workload, kernel, ms, flops=None, nbytes=None, args=None, config=None, peak=None):
     line = {"metric": METRIC if flops else "HBM GB/s of " + kernel, "workload": workload, "kernel": kernel,
             "us": round(ms * 1e3, 2), "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "data": "synthetic, seeded (drawn on the GPU)", "config": config or {}}
     if flops:
         tf = flops / (ms * 1e-3) / 1e12
+        pk = peak or PEAK_BF16_TFLOPS
         line.update({"value": round(tf, 2), "unit": "TFLOPS",
-                     "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
-                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": pk,
+                                  "unit": "TFLOP/s", "frac": round(tf / pk, 4),
                                   "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2)}})
     if nbytes:
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -168,6 +169,23 @@ def run_extra(args):
         ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled(qa, sa, qb, sb, 0, torch.bfloat16, out=c), T, W, stream)
         extra_line("dense_small 128x256x512", "gemm_blockscaled", ms, flops=2.0 * M * N * K, args=args,
                    config={"M": M, "N": N, "K": K, "note": "launch-latency bound"})
+    elif args.workload == "dense_mx":
+        # the MX variant on the dense Fprop shapes: 1x32 blocks with E8M0 scales,
+        # scales applied inside the FP8 MFMA, so its peak is the FP8 one
+        M, N, K = 4096, 7168, 2048
+        x = gpu_acts(gen, M, K, 0.001, 100.0)
+        w = torch.randn((N, K), generator=gen, device="cuda") * 0.02
+        qa, ea = fp8.fp8_quant_mx_1x32(x)
+        qb, eb = fp8.fp8_quant_mx_1x32(w)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        cfg = {"M": M, "N": N, "K": K, "scales": "E8M0 per 1x32 block"}
+        ms = time_launches(lambda i: fp8.fp8_quant_mx_1x32(x, q=qa, e=ea), T, W, stream)
+        extra_line("dense_mx", "quant_mx_1x32 X", ms, nbytes=M * K * 5 + M * K // 32, args=args, config=cfg)
+        ms = time_launches(lambda i: fp8.fp8_quant_mx_1x32(w, q=qb, e=eb), T, W, stream)
+        extra_line("dense_mx", "quant_mx_1x32 W", ms, nbytes=N * K * 5 + N * K // 32, args=args, config=cfg)
+        ms = time_launches(lambda i: fp8.fp8_gemm_mx(qa, ea, qb, eb, torch.bfloat16, out=c), T, W, stream)
+        extra_line("dense_mx", "gemm_mx 4096x7168x2048 BF16", ms, flops=2.0 * M * N * K, args=args, config=cfg,
+                   peak=PEAK_FP8_TFLOPS)
     elif args.workload == "linear_trio":
         TOK, IN, OUT = 8192, 7168, 2048
         x = gpu_acts(gen, TOK, IN, 0.001, 100.0)

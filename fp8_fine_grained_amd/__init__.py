@@ -22,12 +22,13 @@ BSCALE_1x128 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
            "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
            "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16", "fp8_requant_act_tokenwise",
+           "fp8_quant_mx_1x32", "fp8_gemm_mx",
            "fp8fg_status_string", "fp8fg_abi_version")
-_COMPUTE = EXPORTS[:8]
+_COMPUTE = EXPORTS[:10]
 
 
 class Fp8fgError(RuntimeError):
@@ -57,6 +58,8 @@ def load_library(path=LIB_PATH):
     lib.fp8_quant_act_1x128_bf16.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.fp8_quant_weight_128x128_bf16.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.fp8_requant_act_tokenwise.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    lib.fp8_quant_mx_1x32.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.fp8_gemm_mx.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     for name in _COMPUTE:
         getattr(lib, name).restype = ctypes.c_int
     lib.fp8fg_status_string.argtypes = [ctypes.c_int]
@@ -165,6 +168,33 @@ def fp8_requant_act_tokenwise(q, s, qt=None, st=None):
     _check("fp8_requant_act_tokenwise",
            load_library().fp8_requant_act_tokenwise(_ptr(q), _ptr(s), M, K, _ptr(qt), _ptr(st), _stream(q)))
     return qt, st
+
+
+def fp8_quant_mx_1x32(x, q=None, e=None):
+    """MX quantization of x f32 [R][K]: (codes u8 [R][K], E8M0 scale bytes u8 [K/32][R])."""
+    R, K = x.shape
+    _need(x, torch.float32, (R, K), "x")
+    q = _empty((R, K), torch.uint8, x) if q is None else q
+    e = _empty((K // 32, R), torch.uint8, x) if e is None else e
+    _need(q, torch.uint8, (R, K), "q")
+    _need(e, torch.uint8, (K // 32, R), "e")
+    _check("fp8_quant_mx_1x32", load_library().fp8_quant_mx_1x32(_ptr(x), R, K, _ptr(q), _ptr(e), _stream(x)))
+    return q, e
+
+
+def fp8_gemm_mx(a, ea, b, eb, out_dtype=torch.bfloat16, out=None):
+    """C = A . B^T of MX operands: a u8 [M][K] / ea u8 [K/32][M], b u8 [N][K] / eb u8 [K/32][N]."""
+    M, K = a.shape
+    N = b.shape[0]
+    _need(a, torch.uint8, (M, K), "a")
+    _need(ea, torch.uint8, (K // 32, M), "ea")
+    _need(b, torch.uint8, (N, K), "b")
+    _need(eb, torch.uint8, (K // 32, N), "eb")
+    out = _empty((M, N), out_dtype, a) if out is None else out
+    _need(out, out_dtype, (M, N), "out")
+    _check("fp8_gemm_mx", load_library().fp8_gemm_mx(_ptr(a), _ptr(ea), _ptr(b), _ptr(eb), _ptr(out),
+                                                      _out_dtype(out_dtype), M, N, K, _stream(a)))
+    return out
 
 
 def _out_dtype(out_dtype):

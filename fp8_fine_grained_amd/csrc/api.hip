@@ -97,6 +97,31 @@ int fp8_requant_act_tokenwise(const uint8_t* q, const float* s, int64_t M, int64
     return hip_status(fp8fg::launch_requant_act_tokens(q, s, M, K, qt, st, static_cast<hipStream_t>(stream)));
 }
 
+int fp8_quant_mx_1x32(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e, void* stream) {
+    if (!x || !q || !e) return FP8FG_ERR_NULL;
+    if (R < 0 || K < 0 || K % 32 != 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(e)) return FP8FG_ERR_ALIGN;
+    if (R > kMaxDim || K > kMaxDim || (R > 0 && K > kMaxElems / R)) return FP8FG_ERR_UNSUPPORTED;
+    if (R == 0 || K == 0) return FP8FG_OK;
+    return hip_status(fp8fg::launch_quant_mx(x, R, K, q, e, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_gemm_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb, void* c, int out_dtype,
+                int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!a || !ea || !b || !eb || !c) return FP8FG_ERR_NULL;
+    if (M < 0 || N < 0 || K < 0 || M % 4 != 0 || N % 256 != 0 || K % 64 != 0) return FP8FG_ERR_SHAPE;
+    if (K == 0 && M > 0 && N > 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(ea) || !aligned16(b) || !aligned16(eb) || !aligned16(c)) return FP8FG_ERR_ALIGN;
+    if (!valid_out(out_dtype)) return FP8FG_ERR_UNSUPPORTED;
+    if (M > kMaxDim || N > kMaxDim || K >= (int64_t(1) << 24)) return FP8FG_ERR_UNSUPPORTED;
+    if ((K / 32) * M > int64_t(0xFFFFFF00) || (K / 32) * N > int64_t(0xFFFFFF00)) return FP8FG_ERR_UNSUPPORTED;
+    if (((M + 255) / 256) * (N / 256) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return FP8FG_OK;
+    fp8fg::GemmArgs args{a, reinterpret_cast<const float*>(ea), b, reinterpret_cast<const float*>(eb), c,
+                         nullptr, M, N, K, 1};
+    return hip_status(fp8fg::launch_gemm_mx(out_dtype == FP8FG_OUT_FP32, args, static_cast<hipStream_t>(stream)));
+}
+
 int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int bscale_kind,
                          void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
     if (!a || !sa || !b || !sb || !c) return FP8FG_ERR_NULL;

@@ -907,6 +907,214 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// MX GEMM (microscaled operands: E4M3 codes with one power-of-two E8M0 scale
+// per 32 consecutive K; the MX variant of the method, see quant.hip).
+// C = A . B^T, A codes [M][K] with scale bytes [K/32][M], B codes [N][K] with
+// [K/32][N].  gfx950's v_mfma_scale_f32_32x32x64_f8f6f4 applies both scales
+// itself, so there is no promotion step and no VALU work per K: the K loop
+// is fragment reads and MFMAs into one FP32 accumulator.  Like every FP8
+// MFMA on gfx950 it sums each group of products with limited width, so the
+// result is held to the FP8-MFMA engine's bound.
+//
+// Operand layout of the scaled instruction (measured): lane (r, h) of a
+// 64-K step gives row r, K 16h .. 16h+15 in dwords 0-3 and K 32+16h .. +15 in
+// dwords 4-7, and the scale of row r's 32-K block j is taken from lane
+// r + 32 j; so lane (r, h) supplies the scale of block h of the step.
+//
+// Work decomposition as in the wide kernel: 256 x 256 tiles, 4 x 2 waves of
+// 64 x 128, a four-stage ring of 64-K stages (rows of 64 bytes, chunk c at
+// slot c ^ ((r >> 2) & 3)) filled by buffer-to-LDS loads; the scale bytes of
+// a stage (two 256-byte runs for A and for B) ride with it.
+struct MxTile {
+    static constexpr int WAVES_M = 4, WAVES_N = 2, FM = 2, FN = 4, STAGES = 4;
+    static constexpr int NW = 8, THREADS = 512, BM = 256, BN = 256, KS = 64;
+    static constexpr int LOADS_PER_WAVE = 5;   // two A pieces, two B pieces, one scale run
+};
+
+struct alignas(16) MxStage {
+    uint8_t a[MxTile::BM * MxTile::KS];
+    uint8_t b[MxTile::BN * MxTile::KS];
+    uint8_t sa[2][MxTile::BM];    // scale bytes of the stage's two 32-K blocks
+    uint8_t sb[2][MxTile::BN];
+    uint8_t dummy[256];
+};
+
+struct MxCopier {
+    rsrc_t ra, rb, rs;
+    uint32_t va[2], vb[2], vs, s_base, s_step;
+    int a_lds[2], b_lds[2], s_lds;
+
+    __device__ __forceinline__ void copy(uint8_t* stage, int st) const {
+        const uint32_t koff = uint32_t(st) * MxTile::KS;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + a_lds[i]), 16, va[i], koff, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i]), 16, vb[i], koff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs,
+                                                 s_base + uint32_t(2 * st) * s_step, 0, 0);
+    }
+};
+
+// Waves 0-1 copy the A scale runs of blocks 2 st + w, waves 2-3 those of B,
+// waves 4-7 repeat wave 0's run into the dummy line (equal load counts).
+__device__ __forceinline__ MxCopier make_mx_copier(const GemmArgs& args, const Tile& t, int wave, int lane,
+                                                   int64_t n0) {
+    typedef MxTile W;
+    const int64_t K = args.K, M = args.M, N = args.N;
+    MxCopier c;
+    const int sub = lane >> 2, slot = lane & 3;
+    const int64_t tile_rows = t.rows_valid - t.m0 < W::BM ? t.rows_valid - t.m0 : W::BM;   // >= 1
+    c.ra = make_rsrc(t.A + t.m0 * K, uint32_t(tile_rows * K));
+    c.rb = make_rsrc(t.B + n0 * K, uint32_t(W::BN * K));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r0 = (wave * 2 + i) * 16, r = r0 + sub;
+        const int chunk = slot ^ ((r >> 2) & 3);
+        const int64_t row = r < tile_rows ? r : tile_rows - 1;      // clamp: loaded, never stored
+        c.va[i] = uint32_t(row * K + chunk * 16);
+        c.vb[i] = uint32_t(int64_t(r) * K + chunk * 16);
+        c.a_lds[i] = int(offsetof(MxStage, a)) + r0 * W::KS;
+        c.b_lds[i] = int(offsetof(MxStage, b)) + r0 * W::KS;
+    }
+    const int64_t kblocks = K / 32;
+    const uint8_t* ea = reinterpret_cast<const uint8_t*>(args.sa);
+    const uint8_t* eb = reinterpret_cast<const uint8_t*>(args.sb);
+    if (wave < 2) {           // A: bytes of rows m0 + 4 lane .. +3 in block 2 st + wave
+        c.rs = make_rsrc(ea, uint32_t(kblocks * M));
+        c.vs = uint32_t(t.m0 + 4 * lane);
+        c.s_base = uint32_t(wave * M);
+        c.s_step = uint32_t(M);
+        c.s_lds = int(offsetof(MxStage, sa)) + wave * W::BM;
+    } else if (wave < 4) {    // B: rows n0 + 4 lane .. +3 in block 2 st + wave - 2
+        c.rs = make_rsrc(eb, uint32_t(kblocks * N));
+        c.vs = uint32_t(n0 + 4 * lane);
+        c.s_base = uint32_t((wave - 2) * N);
+        c.s_step = uint32_t(N);
+        c.s_lds = int(offsetof(MxStage, sb)) + (wave - 2) * W::BN;
+    } else {
+        c.rs = make_rsrc(ea, uint32_t(kblocks * M));
+        c.vs = uint32_t(t.m0 + 4 * lane);
+        c.s_base = 0;
+        c.s_step = uint32_t(M);
+        c.s_lds = int(offsetof(MxStage, dummy));
+    }
+    return c;
+}
+
+template <int OUT_FP32>
+__device__ __forceinline__ void gemm_mx_body(const GemmArgs& args) {
+    typedef MxTile W;
+    constexpr int FM = W::FM, FN = W::FN, STAGES = W::STAGES, L = W::LOADS_PER_WAVE;
+    __shared__ __align__(16) uint8_t lds_raw[STAGES * sizeof(MxStage)];
+    MxStage* ring = reinterpret_cast<MxStage*>(lds_raw);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / W::WAVES_N, wn = wave % W::WAVES_N;
+    const int64_t N = args.N, K = args.K;
+    const int stages = int(K / W::KS);
+    const Tile t = map_tile<W, int(GemmMode::Dense)>(args, blockIdx.x);
+    if (!t.live) return;
+    const int64_t n0 = int64_t(t.bn) * W::BN;
+    const MxCopier cp = make_mx_copier(args, t, wave, lane, n0);
+    const int64_t wrow0 = t.m0 + wm * FM * 32;
+    const bool live = wrow0 < t.rows_valid;
+    const int r = lane & 31, h = lane >> 5;
+    // per-lane LDS offsets within a stage: chunks h and 2 + h of the lane's rows
+    uint32_t oa[FM][2], ob[FN][2], osa[FM], osb[FN];
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) {
+        const int row = wm * FM * 32 + mi * 32 + r;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            oa[mi][c] = uint32_t(offsetof(MxStage, a)) + uint32_t(row * W::KS + (((2 * c + h) ^ ((row >> 2) & 3)) << 4));
+        osa[mi] = uint32_t(offsetof(MxStage, sa)) + uint32_t(h * W::BM + row);
+    }
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+        const int row = wn * FN * 32 + ni * 32 + r;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            ob[ni][c] = uint32_t(offsetof(MxStage, b)) + uint32_t(row * W::KS + (((2 * c + h) ^ ((row >> 2) & 3)) << 4));
+        osb[ni] = uint32_t(offsetof(MxStage, sb)) + uint32_t(h * W::BN + row);
+    }
+
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        cp.copy(reinterpret_cast<uint8_t*>(&ring[st]), st < stages ? st : stages - 1);
+
+    v16f acc[FM][FN];
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
+
+    int slot = 0, fill_slot = STAGES - 1;
+    for (int cur = 0; cur < stages; ++cur) {
+        wait_vmcnt<(STAGES - 2) * L>();   // this wave's copy of stage cur has landed
+        __builtin_amdgcn_s_barrier();     // ... every wave's; the slot of cur - 1 is free
+        const int fill = cur + STAGES - 1;
+        cp.copy(reinterpret_cast<uint8_t*>(&ring[fill_slot]), fill < stages ? fill : stages - 1);
+        if (live) {
+            const uint8_t* sg = lds_raw + uint32_t(slot) * uint32_t(sizeof(MxStage));
+            v8i a8[FM], b8[FN];
+            int ea[FM], eb[FN];
+#pragma unroll
+            for (int mi = 0; mi < FM; ++mi) {
+                const u32x4 lo = ld<u32x4>(sg + oa[mi][0]), hi = ld<u32x4>(sg + oa[mi][1]);
+                a8[mi] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+                ea[mi] = sg[osa[mi]];
+            }
+#pragma unroll
+            for (int ni = 0; ni < FN; ++ni) {
+                const u32x4 lo = ld<u32x4>(sg + ob[ni][0]), hi = ld<u32x4>(sg + ob[ni][1]);
+                b8[ni] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+                eb[ni] = sg[osb[ni]];
+            }
+#pragma unroll
+            for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < FN; ++ni)
+                    // formats 0/0 = E4M3 x E4M3; B is the instruction's first operand
+                    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8[ni], a8[mi], acc[mi][ni], 0, 0,
+                                                                                  0, eb[ni], 0, ea[mi]);
+        }
+        slot = slot == STAGES - 1 ? 0 : slot + 1;
+        fill_slot = fill_slot == STAGES - 1 ? 0 : fill_slot + 1;
+    }
+    wait_vmcnt<0>();   // no copy may land after the workgroup's LDS is handed on
+
+    const int n_lane = wn * FN * 32 + 4 * h;
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) {
+        const int64_t m = wrow0 + mi * 32 + r;
+        if (m >= t.rows_valid) continue;
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t idx = m * N + n0 + n_lane + ni * 32 + 8 * j;
+                const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
+                                  acc[mi][ni][4 * j + 3]};
+                if (OUT_FP32) {
+                    st<v4f>(static_cast<float*>(args.c) + idx, v);
+                } else {
+                    const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+                    const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+                    st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
+                }
+            }
+    }
+}
+
+__global__ __launch_bounds__(MxTile::THREADS) void gemm_mx_o0_dense(GemmArgs args) { gemm_mx_body<0>(args); }
+__global__ __launch_bounds__(MxTile::THREADS) void gemm_mx_o1_dense(GemmArgs args) { gemm_mx_body<1>(args); }
+
 // One plain __global__ function per instantiation (kernel templates whose
 // instantiations differ only in the tile shape lost their host stubs).
 // tile id: 0 = BigTile, 1 = DecodeTile
@@ -1031,7 +1239,19 @@ int engine_from_env() {
     return (e && strcmp(e, "fp8mfma") == 0) ? 1 : 0;
 }
 
+hipError_t launch_mx(int out_fp32, const GemmArgs& args, hipStream_t stream) {
+    const int64_t tiles = ((args.M + MxTile::BM - 1) / MxTile::BM) * (args.N / MxTile::BN);
+    if (tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(out_fp32 ? gemm_mx_o1_dense : gemm_mx_o0_dense, dim3(unsigned(tiles)), dim3(MxTile::THREADS),
+                       0, stream, args);
+    return hipGetLastError();
+}
+
 }  // namespace gemm_detail
+
+hipError_t launch_gemm_mx(int out_fp32, const GemmArgs& args, hipStream_t stream) {
+    return gemm_detail::launch_mx(out_fp32, args, stream);
+}
 
 hipError_t launch_gemm(GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                        hipStream_t stream) {

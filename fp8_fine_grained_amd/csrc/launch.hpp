@@ -12,6 +12,7 @@ hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, int t
                             float* s, hipStream_t stream);
 hipError_t launch_requant_act_tokens(const uint8_t* qr, const float* sr, int64_t M, int64_t K, uint8_t* q, float* s,
                                      hipStream_t stream);
+hipError_t launch_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e, hipStream_t stream);
 hipError_t launch_quant_weight(const void* w, int bf16, int64_t N, int64_t K, int transpose_out, uint8_t* q,
                                float* s, hipStream_t stream);
 
@@ -29,6 +30,8 @@ struct GemmArgs {
     int64_t G;              // groups (1 for dense)
 };
 
+// MX GEMM: args.sa / args.sb carry the E8M0 scale bytes ([K/32][M], [K/32][N])
+hipError_t launch_gemm_mx(int out_fp32, const GemmArgs& args, hipStream_t stream);
 hipError_t launch_gemm(GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                        hipStream_t stream);
 

@@ -323,6 +323,60 @@ __device__ __forceinline__ void quant_act_rows_dispatch(const uint16_t* x, int64
 }
 
 // ---------------------------------------------------------------------------
+// MX quantization (microscaling: blocks of 32 along K, power-of-two E8M0
+// scale).  "The Insider Secrets Of Deepseek Discovered", passage after
+// Figure 7, relates the method to microscaling formats; the block rule is the
+// OCP MX one for E4M3 elements:
+//   s = clamp(floor(log2(amax)) - 8, -127, 127),  code = E4M3_RNE_SAT(x * 2^-s),
+//   scale byte = s + 127  (amax = 0 gives s = -127).
+// For a normal amax floor(log2) is its exponent field minus 127, and every
+// amax below 2^-119 (subnormals and zero included) clamps to s = -127, so
+// s = max(field - 135, -127).  x * 2^-s rounds once (only when it falls below
+// fp32's normal range) and |x * 2^-s| < 512; clamping to +-448 before the
+// conversion is the saturation.  A half-wave holds eight blocks of one row,
+// 4 lanes x 8 elements each; codes q [R][K], scale bytes e [K/32][R].
+constexpr int kMxBlock = 32;
+
+__global__ __launch_bounds__(256) void quant_mx_rows(const float* __restrict__ x, int64_t R, int64_t K,
+                                                     uint8_t* __restrict__ q, uint8_t* __restrict__ e) {
+    const int lane = threadIdx.x & 31;
+    const int64_t k = int64_t(blockIdx.x) * 256 + lane * 8;      // first of this lane's 8 elements
+    const bool valid = k < K;                                      // K % 32 == 0: whole blocks
+    for (int64_t m = int64_t(blockIdx.y) * 8 + (threadIdx.x >> 5); m < R; m += int64_t(gridDim.y) * 8) {
+        v4f v0 = v4f{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+        if (valid) {
+            v0 = ld<v4f>(x + m * K + k);
+            v1 = ld<v4f>(x + m * K + k + 4);
+        }
+        float amax = fmaxf(abs_max4(v0), abs_max4(v1));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+        const int field = int((__float_as_uint(amax) >> 23) & 0xFF);
+        const int sh = field - 135 < -127 ? -127 : field - 135;   // at most 254 - 135 = 119
+        const float mul = __uint_as_float(uint32_t(127 - sh) << 23);   // 2^-s, a normal float
+        v4f y0 = v0 * mul, y1 = v1 * mul;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            y0[j] = fmaxf(fminf(y0[j], 448.0f), -448.0f);
+            y1[j] = fmaxf(fminf(y1[j], 448.0f), -448.0f);
+        }
+        if (valid) {
+            st<u32x2_t>(q + m * K + k, u32x2_t{cvt4(y0[0], y0[1], y0[2], y0[3]), cvt4(y1[0], y1[1], y1[2], y1[3])});
+            if ((lane & 3) == 0) e[(k / kMxBlock) * R + m] = uint8_t(sh + 127);
+        }
+    }
+}
+
+hipError_t launch_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e, hipStream_t stream) {
+    const int64_t chunks = (K + 255) / 256;
+    int64_t row_groups = (R + 7) / 8;
+    if (row_groups > 65535) row_groups = 65535;      // the kernel strides over the rest
+    hipLaunchKernelGGL(quant_mx_rows, dim3(unsigned(chunks), unsigned(row_groups)), dim3(256), 0, stream, x, R, K,
+                       q, e);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // One plain kernel per element type (fp32, bf16 bits).
 #define FP8FG_QUANT_KERNELS(T, SUFFIX)                                                                     \
     __global__ __launch_bounds__(256) void quant_act_rows_##SUFFIX(const T* __restrict__ x, int64_t M,      \

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 3
+#define FP8FG_ABI_VERSION 4
 
 enum fp8fg_status {
     FP8FG_OK = 0,
@@ -133,6 +133,30 @@ int fp8_quant_weight_128x128_bf16(const uint16_t* w, int64_t N, int64_t K, int t
  */
 int fp8_requant_act_tokenwise(const uint8_t* q, const float* s, int64_t M, int64_t K,
                               uint8_t* qt, float* st, void* stream);
+
+/*
+ * MX variant (microscaling).  "The Insider Secrets Of Deepseek Discovered",
+ * passage after Figure 7: the method is consistent with microscaling
+ * formats.  Reading (the pages define no MX rule): the OCP MX rule for E4M3
+ * elements, one power-of-two scale per block of 32 consecutive K, stored as
+ * an E8M0 byte.  This is a different numeric contract from the calls above
+ * (power-of-two scales, 32-element blocks, no FP32 scale), offered beside
+ * them for comparison; gfx950 applies these scales inside the MFMA.
+ *
+ * fp8_quant_mx_1x32: x f32 [R][K] -> codes q u8 [R][K] and scale bytes
+ *   e u8 [K/32][R]:  s = clamp(floor(log2(amax)) - 8, -127, 127) per block
+ *   (amax = 0 gives -127), code = E4M3_RNE_SAT(RN32(x * 2^-s)), e = s + 127.
+ *   Requires K % 32 == 0; R * K < 2^40.
+ * fp8_gemm_mx: C[M][N] = sum_k decode(a) 2^(ea-127) decode(b) 2^(eb-127) with
+ *   a u8 [M][K], ea u8 [K/32][M], b u8 [N][K], eb u8 [K/32][N]; c BF16 or FP32
+ *   [M][N].  Accuracy: |C - C*| <= 2^-9 * S (S = sum_k |a_k b_k| of the
+ *   dequantized operands) plus the BF16 rounding: gfx950's FP8 MFMA sums its
+ *   products with limited width.  Requires M % 4 == 0, N % 256 == 0,
+ *   K % 64 == 0, K > 0 when M * N > 0, K < 2^24, (K / 32) * max(M, N) < 2^32.
+ */
+int fp8_quant_mx_1x32(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e, void* stream);
+int fp8_gemm_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb,
+                void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * Dense block-scaled FP8 GEMM: C[M][N] = A[M][K] . B[N][K]^T.

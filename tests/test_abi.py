@@ -88,6 +88,24 @@ def test_requant_argument_errors():
     assert r(P, P, 128, 0, P, P2, NUL) == OK
 
 
+def test_mx_argument_errors():
+    lib = fp8.load_library()
+    q = lib.fp8_quant_mx_1x32
+    assert q(NUL, 4, 64, P, P2, NUL) == ENULL
+    assert q(P, 4, 48, P, P2, NUL) == ESHAPE            # K % 32
+    assert q(MIS, 4, 64, P, P2, NUL) == EALIGN
+    assert q(P, 0, 64, P, P2, NUL) == OK
+    g = lib.fp8_gemm_mx
+    assert g(P, P, P, NUL, P, 0, 4, 256, 64, NUL) == ENULL
+    assert g(P, P, P, P, P, 0, 6, 256, 64, NUL) == ESHAPE     # M % 4
+    assert g(P, P, P, P, P, 0, 4, 128, 64, NUL) == ESHAPE     # N % 256
+    assert g(P, P, P, P, P, 0, 4, 256, 32, NUL) == ESHAPE     # K % 64
+    assert g(P, P, P, P, P, 0, 4, 256, 0, NUL) == ESHAPE
+    assert g(P, MIS, P, P, P, 0, 4, 256, 64, NUL) == EALIGN
+    assert g(P, P, P, P, P, 7, 4, 256, 64, NUL) == EUNSUP
+    assert g(P, P, P, P, P, 0, 0, 256, 64, NUL) == OK
+
+
 def test_gemm_argument_errors():
     g = fp8.load_library().fp8_gemm_blockscaled
     assert g(P, P, P, NUL, 0, P, 0, 1, 128, 128, NUL) == ENULL
