@@ -22,7 +22,17 @@ Scale layouts (shared with the library's C interface):
     1x128, tiles along K : q [R][K],  s [K/128][R]       ("kb-major")
     1x128, tiles along R : q [K][R],  s [R/128][K]       (token-wise, transposed out)
     128x128              : q [N][K],  s [N/128][K/128]   (or q^T, s^T)
+
+Partial tiles (reading; the pages only use whole groups): when the grouped
+axis is not a multiple of 128 the last group is shorter, and it is treated as
+the group zero-padded to 128 -- its max-abs runs over the elements that exist,
+the padding's codes are dropped.  Scale counts round up: K/128 above means
+ceil(K/128).  Computed exactly that way here: pad with zeros, quantize, slice.
 """
+
+
+def _ceil128(n):
+    return -(-n // 128) * 128
 
 import numpy as np
 
@@ -43,10 +53,12 @@ def _scale_and_cast(groups, amax):
 
 
 def quant_act_1x128(x):
-    """1x128 tiles along K.  x float32 [R][K] -> (q u8 [R][K], s f32 [K/128][R])."""
+    """1x128 tiles along K.  x float32 [R][K] -> (q u8 [R][K], s f32 [ceil(K/128)][R])."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     R, K = x.shape
-    assert K % 128 == 0, "K must be a multiple of 128"
+    if K % 128:
+        q, s = quant_act_1x128(np.pad(x, ((0, 0), (0, _ceil128(K) - K))))
+        return np.ascontiguousarray(q[:, :K]), s
     t = x.reshape(R, K // 128, 128)
     amax = np.max(np.abs(t), axis=2, keepdims=True) if R else np.zeros((0, K // 128, 1), np.float32)
     q, s = _scale_and_cast(t, amax)
@@ -61,17 +73,21 @@ def quant_act_1x128_tokenwise(x):
     of x^T, which is how it is computed here.
     """
     x = np.asarray(x, dtype=np.float32)
-    R, K = x.shape
-    assert R % 128 == 0, "token count must be a multiple of 128"
     return quant_act_1x128(np.ascontiguousarray(x.T))
 
 
 def quant_weight_128x128(w, transpose_out=False):
     """128x128 blocks.  w float32 [N][K] ->
-    (q u8 [N][K], s f32 [N/128][K/128]), or (q^T [K][N], s^T [K/128][N/128])."""
+    (q u8 [N][K], s f32 [N/128][K/128]), or (q^T [K][N], s^T [K/128][N/128])
+    (block counts rounded up)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     N, K = w.shape
-    assert N % 128 == 0 and K % 128 == 0, "N and K must be multiples of 128"
+    if N % 128 or K % 128:
+        q, s = quant_weight_128x128(np.pad(w, ((0, _ceil128(N) - N), (0, _ceil128(K) - K))))
+        q = np.ascontiguousarray(q[:N, :K])
+        if transpose_out:
+            return np.ascontiguousarray(q.T), np.ascontiguousarray(s.T)
+        return q, s
     t = w.reshape(N // 128, 128, K // 128, 128)
     amax = np.max(np.abs(t), axis=(1, 3), keepdims=True)
     q, s = _scale_and_cast(t, amax)
@@ -92,15 +108,17 @@ def quant_per_tensor(x):
 
 
 def dequant_act(q, s):
-    """Exact float64 values of 1x128-quantized rows: q u8 [R][K], s [K/128][R]."""
+    """Exact float64 values of 1x128-quantized rows: q u8 [R][K], s [ceil(K/128)][R]."""
     s = np.asarray(s, dtype=np.float32).astype(np.float64)
-    return e4m3.decode(q) * np.repeat(s.T, 128, axis=1)
+    K = np.asarray(q).shape[1]
+    return e4m3.decode(q) * np.repeat(s.T, 128, axis=1)[:, :K]
 
 
 def dequant_weight(q, s):
-    """Exact float64 values of 128x128-quantized blocks: q u8 [N][K], s [N/128][K/128]."""
+    """Exact float64 values of 128x128-quantized blocks: q u8 [N][K], s [ceil(N/128)][ceil(K/128)]."""
     s = np.asarray(s, dtype=np.float32).astype(np.float64)
-    return e4m3.decode(q) * np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
+    N, K = np.asarray(q).shape
+    return e4m3.decode(q) * np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)[:N, :K]
 
 
 def dequant32(q, s_full):
@@ -117,12 +135,11 @@ def requant_act_tokenwise(q, s):
     s f32 [K/128][R]; the Wgrad operand is 1x128 along tokens.  Steps:
         x'[r][k] = RN32(dec(q[r][k]) * s[k/128][r])   (fp32 dequantization)
         (qt, st) = 1x128 quantization of x' along tokens, transposed out
-    Returns (qt u8 [K][R], st f32 [R/128][K]).  R and K multiples of 128.
+    Returns (qt u8 [K][R], st f32 [ceil(R/128)][K]).
     """
     q = np.asarray(q, dtype=np.uint8)
     s = np.asarray(s, dtype=np.float32)
     R, K = q.shape
-    assert R % 128 == 0 and K % 128 == 0, "R and K must be multiples of 128"
-    assert s.shape == (K // 128, R)
-    x = dequant32(q, np.repeat(s.T, 128, axis=1))
+    assert s.shape == (-(-K // 128), R)
+    x = dequant32(q, np.repeat(s.T, 128, axis=1)[:, :K])
     return quant_act_1x128_tokenwise(x)

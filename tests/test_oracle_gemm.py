@@ -32,12 +32,13 @@ def _brute_force(qa, sa, qb, sb, bscale_kind, cols):
     return C
 
 
+@pytest.mark.parametrize("K", [256, 176])
 @pytest.mark.parametrize("bscale_kind", ["128x128", "1x128"])
-def test_reference_against_exact_rationals(bscale_kind):
+def test_reference_against_exact_rationals(bscale_kind, K):
     """Tiny shapes: the float64 reference agrees with exact rational arithmetic
-    to within K * 2^-53 * S."""
-    rng = np.random.default_rng(20)
-    M, N, K = 3, (128 if bscale_kind == "128x128" else 4), 256
+    to within K * 2^-53 * S (K = 176: a partial last K-block of 48)."""
+    rng = np.random.default_rng(20 + K)
+    M, N = 3, (128 if bscale_kind == "128x128" else 4)
     a = workloads.activations(rng, M, K, 0.01, 50.0)
     if bscale_kind == "128x128":
         qb, sb = quant.quant_weight_128x128(workloads.weights(rng, N, K))

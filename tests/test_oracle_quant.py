@@ -153,3 +153,45 @@ def test_fine_grained_beats_per_tensor_on_outliers():
     rel_coarse = np.abs(e4m3.decode(qt) * np.float64(st) - x)[:, normal] / np.abs(x[:, normal])
     assert np.median(rel_fine) < 2.0 ** -4
     assert rel_coarse.mean() > 4 * rel_fine.mean()
+
+
+# ---------------------------------------------------------------------------
+# Partial groups (axis length not a multiple of 128): the last group is the
+# elements that exist; pinned against the exact rational group quantizer.
+from tests.bruteforce import quant_group  # noqa: E402
+
+
+def test_partial_row_groups_brute_force():
+    x = _outlier_acts(3, 208, 21)                     # groups of 128 and 80
+    x[1, 128:] *= 1e-3
+    q, s = quant.quant_act_1x128(x)
+    assert q.shape == (3, 208) and s.shape == (2, 3)
+    for r in range(3):
+        for kb, (lo, hi) in enumerate(((0, 128), (128, 208))):
+            bs, bc = quant_group(x[r, lo:hi])
+            assert s[kb, r].view(np.uint32) == bs.view(np.uint32), (r, kb)
+            assert q[r, lo:hi].tolist() == bc, (r, kb)
+
+
+def test_partial_token_groups_brute_force():
+    x = _outlier_acts(144, 16, 22)                    # token groups of 128 and 16
+    q, s = quant.quant_act_1x128_tokenwise(x)
+    assert q.shape == (16, 144) and s.shape == (2, 16)
+    for k in range(16):
+        for tb, (lo, hi) in enumerate(((0, 128), (128, 144))):
+            bs, bc = quant_group(x[lo:hi, k])
+            assert s[tb, k].view(np.uint32) == bs.view(np.uint32)
+            assert q[k, lo:hi].tolist() == bc
+
+
+def test_partial_weight_blocks_brute_force():
+    rng = np.random.default_rng(23)
+    w = workloads.weights(rng, 128, 160)              # blocks 128x128 and 128x32
+    w[7, 150] = -0.5
+    q, s = quant.quant_weight_128x128(w)
+    qt, st = quant.quant_weight_128x128(w, transpose_out=True)
+    assert s.shape == (1, 2) and np.array_equal(qt, q.T) and np.array_equal(st, s.T)
+    for kb, (lo, hi) in enumerate(((0, 128), (128, 160))):
+        bs, bc = quant_group(w[:, lo:hi].reshape(-1))
+        assert s[0, kb].view(np.uint32) == bs.view(np.uint32)
+        assert q[:, lo:hi].reshape(-1).tolist() == bc
