@@ -102,6 +102,11 @@ def _need(t, dtype, shape, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _nb(n):
+    """Number of 128-wide groups along an axis of length n (a last partial group counts)."""
+    return (n + 127) // 128
+
+
 def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
@@ -110,7 +115,7 @@ def _quant_act(fn, x, dtype, transpose_out, q, s):
     M, K = x.shape
     _need(x, dtype, (M, K), "x")
     qs = (K, M) if transpose_out else (M, K)
-    ss = (M // 128, K) if transpose_out else (K // 128, M)
+    ss = (_nb(M), K) if transpose_out else (_nb(K), M)
     q = _empty(qs, torch.uint8, x) if q is None else q
     s = _empty(ss, torch.float32, x) if s is None else s
     _need(q, torch.uint8, qs, "q")
@@ -123,7 +128,7 @@ def _quant_weight(fn, w, dtype, transpose_out, q, s):
     N, K = w.shape
     _need(w, dtype, (N, K), "w")
     qs = (K, N) if transpose_out else (N, K)
-    ss = (K // 128, N // 128) if transpose_out else (N // 128, K // 128)
+    ss = (_nb(K), N // 128) if transpose_out else (N // 128, _nb(K))
     q = _empty(qs, torch.uint8, w) if q is None else q
     s = _empty(ss, torch.float32, w) if s is None else s
     _need(q, torch.uint8, qs, "q")
@@ -160,11 +165,11 @@ def fp8_requant_act_tokenwise(q, s, qt=None, st=None):
     operand (qt u8 [K][M], st f32 [M/128][K]) of RN32(decode(q) * s)."""
     M, K = q.shape
     _need(q, torch.uint8, (M, K), "q")
-    _need(s, torch.float32, (K // 128, M), "s")
+    _need(s, torch.float32, (_nb(K), M), "s")
     qt = _empty((K, M), torch.uint8, q) if qt is None else qt
-    st = _empty((M // 128, K), torch.float32, q) if st is None else st
+    st = _empty((_nb(M), K), torch.float32, q) if st is None else st
     _need(qt, torch.uint8, (K, M), "qt")
-    _need(st, torch.float32, (M // 128, K), "st")
+    _need(st, torch.float32, (_nb(M), K), "st")
     _check("fp8_requant_act_tokenwise",
            load_library().fp8_requant_act_tokenwise(_ptr(q), _ptr(s), M, K, _ptr(qt), _ptr(st), _stream(q)))
     return qt, st
@@ -206,9 +211,9 @@ def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind=BSCALE_128x128, out_dtype=tor
     M, K = a.shape
     N = b.shape[0]
     _need(a, torch.uint8, (M, K), "a")
-    _need(sa, torch.float32, (K // 128, M), "sa")
+    _need(sa, torch.float32, (_nb(K), M), "sa")
     _need(b, torch.uint8, (N, K), "b")
-    _need(sb, torch.float32, (N // 128, K // 128) if bscale_kind == BSCALE_128x128 else (K // 128, N), "sb")
+    _need(sb, torch.float32, (N // 128, _nb(K)) if bscale_kind == BSCALE_128x128 else (_nb(K), N), "sb")
     out = _empty((M, N), out_dtype, a) if out is None else out
     _need(out, out_dtype, (M, N), "out")
     _check("fp8_gemm_blockscaled", load_library().fp8_gemm_blockscaled(
@@ -222,9 +227,9 @@ def fp8_grouped_gemm_contiguous(a, sa, b, sb, group_offsets, out_dtype=torch.bfl
     M_total, K = a.shape
     G, N, _ = b.shape
     _need(a, torch.uint8, (M_total, K), "a")
-    _need(sa, torch.float32, (K // 128, M_total), "sa")
+    _need(sa, torch.float32, (_nb(K), M_total), "sa")
     _need(b, torch.uint8, (G, N, K), "b")
-    _need(sb, torch.float32, (G, N // 128, K // 128), "sb")
+    _need(sb, torch.float32, (G, N // 128, _nb(K)), "sb")
     _need(group_offsets, torch.int32, (G + 1,), "group_offsets")
     out = _empty((M_total, N), out_dtype, a) if out is None else out
     _need(out, out_dtype, (M_total, N), "out")
@@ -239,9 +244,9 @@ def fp8_grouped_gemm_masked(a, sa, b, sb, masked_m, out_dtype=torch.bfloat16, ou
     G, M_max, K = a.shape
     N = b.shape[1]
     _need(a, torch.uint8, (G, M_max, K), "a")
-    _need(sa, torch.float32, (G, K // 128, M_max), "sa")
+    _need(sa, torch.float32, (G, _nb(K), M_max), "sa")
     _need(b, torch.uint8, (G, N, K), "b")
-    _need(sb, torch.float32, (G, N // 128, K // 128), "sb")
+    _need(sb, torch.float32, (G, N // 128, _nb(K)), "sb")
     _need(masked_m, torch.int32, (G,), "masked_m")
     out = _empty((G, M_max, N), out_dtype, a) if out is None else out
     _need(out, out_dtype, (G, M_max, N), "out")

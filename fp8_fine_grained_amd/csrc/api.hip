@@ -44,8 +44,9 @@ static int quant_act(const void* x, int bf16, int64_t M, int64_t K, int transpos
     if (!x || !q || !s) return FP8FG_ERR_NULL;
     if (M < 0 || K < 0) return FP8FG_ERR_SHAPE;
     if (transpose_out != 0 && transpose_out != 1) return FP8FG_ERR_UNSUPPORTED;
-    if (transpose_out == 0 && K % 128 != 0) return FP8FG_ERR_SHAPE;
-    if (transpose_out == 1 && M % 128 != 0) return FP8FG_ERR_SHAPE;
+    // the grouped axis: a multiple of 16 (a last partial group is allowed)
+    if (transpose_out == 0 && K % 16 != 0) return FP8FG_ERR_SHAPE;
+    if (transpose_out == 1 && M % 16 != 0) return FP8FG_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return FP8FG_ERR_ALIGN;
     if (M > kMaxDim || K > kMaxDim || (M > 0 && K > kMaxElems / M)) return FP8FG_ERR_UNSUPPORTED;
     if (transpose_out == 1 && ((K + 63) / 64 > 65535)) return FP8FG_ERR_UNSUPPORTED;
@@ -56,7 +57,7 @@ static int quant_act(const void* x, int bf16, int64_t M, int64_t K, int transpos
 static int quant_weight(const void* w, int bf16, int64_t N, int64_t K, int transpose_out, uint8_t* q, float* s,
                         void* stream) {
     if (!w || !q || !s) return FP8FG_ERR_NULL;
-    if (N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8FG_ERR_SHAPE;
+    if (N < 0 || K < 0 || N % 128 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
     if (transpose_out != 0 && transpose_out != 1) return FP8FG_ERR_UNSUPPORTED;
     if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return FP8FG_ERR_ALIGN;
     if (N > kMaxDim || K > kMaxDim || (N > 0 && K > kMaxElems / N)) return FP8FG_ERR_UNSUPPORTED;
@@ -89,7 +90,7 @@ int fp8_quant_weight_128x128_bf16(const uint16_t* w, int64_t N, int64_t K, int t
 int fp8_requant_act_tokenwise(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt, float* st,
                               void* stream) {
     if (!q || !s || !qt || !st) return FP8FG_ERR_NULL;
-    if (M < 0 || K < 0 || M % 128 != 0 || K % 128 != 0) return FP8FG_ERR_SHAPE;
+    if (M < 0 || K < 0 || M % 16 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(s) || !aligned16(qt) || !aligned16(st)) return FP8FG_ERR_ALIGN;
     if (M > kMaxDim || K > kMaxDim || (M > 0 && K > kMaxElems / M)) return FP8FG_ERR_UNSUPPORTED;
     if (K / 64 > 65535 || M / 128 > 0x7FFFFFFF) return FP8FG_ERR_UNSUPPORTED;
@@ -125,7 +126,7 @@ int fp8_gemm_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uin
 int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int bscale_kind,
                          void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
     if (!a || !sa || !b || !sb || !c) return FP8FG_ERR_NULL;
-    if (M < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8FG_ERR_SHAPE;
+    if (M < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
     if (K == 0 && M > 0 && N > 0) return FP8FG_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(c)) return FP8FG_ERR_ALIGN;
     if (bscale_kind != FP8FG_BSCALE_128x128 && bscale_kind != FP8FG_BSCALE_1x128) return FP8FG_ERR_UNSUPPORTED;
@@ -142,7 +143,7 @@ int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t
                                 const int32_t* group_offsets, int64_t G, int64_t M_total, int64_t N, int64_t K,
                                 void* c, int out_dtype, void* stream) {
     if (!a || !sa || !b || !sb || !group_offsets || !c) return FP8FG_ERR_NULL;
-    if (G < 0 || M_total < 0 || N < 0 || K < 0 || M_total % 128 != 0 || N % 128 != 0 || K % 128 != 0)
+    if (G < 0 || M_total < 0 || N < 0 || K < 0 || M_total % 128 != 0 || N % 128 != 0 || K % 16 != 0)
         return FP8FG_ERR_SHAPE;
     if (K == 0 && M_total > 0 && N > 0 && G > 0) return FP8FG_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(c) ||
@@ -161,7 +162,7 @@ int fp8_grouped_gemm_masked(const uint8_t* a, const float* sa, const uint8_t* b,
                             const int32_t* masked_m, int64_t G, int64_t M_max, int64_t N, int64_t K, void* c,
                             int out_dtype, void* stream) {
     if (!a || !sa || !b || !sb || !masked_m || !c) return FP8FG_ERR_NULL;
-    if (G < 0 || M_max < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8FG_ERR_SHAPE;
+    if (G < 0 || M_max < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
     if (K == 0 && M_max > 0 && N > 0 && G > 0) return FP8FG_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(c) || !aligned16(masked_m))
         return FP8FG_ERR_ALIGN;

@@ -170,7 +170,7 @@ __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile) {
     constexpr int BM = C::BM, BN = C::BN;
     Tile t;
     const int n_tiles = int(args.N / BN);
-    const int64_t kbs = args.K / BK;
+    const int64_t kbs = (args.K + BK - 1) / BK;
     t.bn = int(tile % n_tiles);
     tile /= n_tiles;
     t.A = args.a;
@@ -238,23 +238,43 @@ __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile) {
 // scale on this path leaves vmcnt counting nothing but the ring.
 template <class C>
 struct Copier {
-    const uint8_t* a_row[C::A_PER_WAVE];   // this lane's A row (+ chunk offset) per piece
+    const uint8_t* a_row[C::A_PER_WAVE];   // this lane's A row start per piece
     const uint8_t* b_row[C::B_PER_WAVE];
+    int a_c16[C::A_PER_WAVE], b_c16[C::B_PER_WAVE];   // the lane's chunk offset within a K-block (bytes)
     int a_lds[C::A_PER_WAVE], b_lds[C::B_PER_WAVE];   // wave-uniform LDS byte offsets
     const float* s_src;        // this lane's scale source for K-block 0
     int64_t s_stride;          // scale source stride between K-blocks
     int s_lds;                 // wave-uniform LDS byte offset of the scale piece
+    int64_t K;
 
-    // issue this wave's loads of K-block kb into `stage`
+    // issue this wave's loads of K-block kb into `stage`; a chunk past K (a
+    // partial last K-block) reads the row's first chunk instead, never memory
+    // past the row, and is zeroed in LDS by zero_tail
     __device__ __forceinline__ void copy(uint8_t* stage, int64_t kb) const {
         const int64_t koff = kb * BK;
 #pragma unroll
+        for (int i = 0; i < C::A_PER_WAVE; ++i) {
+            const int64_t off = koff + a_c16[i];
+            __builtin_amdgcn_global_load_lds(a_row[i] + (off < K ? off : 0), (lds_ptr_t)(stage + a_lds[i]), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::B_PER_WAVE; ++i) {
+            const int64_t off = koff + b_c16[i];
+            __builtin_amdgcn_global_load_lds(b_row[i] + (off < K ? off : 0), (lds_ptr_t)(stage + b_lds[i]), 16, 0, 0);
+        }
+        __builtin_amdgcn_global_load_lds(s_src + kb * s_stride, (lds_ptr_t)(stage + s_lds), 4, 0, 0);
+    }
+
+    // after this wave's loads of K-block kb have landed: zero its 16-byte
+    // slots that lie past K, so those k contribute nothing
+    __device__ __forceinline__ void zero_tail(uint8_t* stage, int64_t kb, int lane) const {
+        const int64_t koff = kb * BK;
+#pragma unroll
         for (int i = 0; i < C::A_PER_WAVE; ++i)
-            __builtin_amdgcn_global_load_lds(a_row[i] + koff, (lds_ptr_t)(stage + a_lds[i]), 16, 0, 0);
+            if (koff + a_c16[i] >= K) st<u32x4>(stage + a_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
         for (int i = 0; i < C::B_PER_WAVE; ++i)
-            __builtin_amdgcn_global_load_lds(b_row[i] + koff, (lds_ptr_t)(stage + b_lds[i]), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(s_src + kb * s_stride, (lds_ptr_t)(stage + s_lds), 4, 0, 0);
+            if (koff + b_c16[i] >= K) st<u32x4>(stage + b_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
     }
 };
 
@@ -263,6 +283,7 @@ __device__ __forceinline__ Copier<C> make_copier(const Tile& t, int wave, int la
                                                  int64_t n0) {
     typedef Stage<C> S;
     Copier<C> c;
+    c.K = K;
     const int sub = lane >> 3;            // row within an 8-row piece
     const int slot = lane & 7;            // 16-byte slot within the row (as stored)
 #pragma unroll
@@ -271,14 +292,16 @@ __device__ __forceinline__ Copier<C> make_copier(const Tile& t, int wave, int la
         const int chunk = slot ^ ((r >> 1) & 7);
         int64_t row = t.m0 + r;
         if (row >= t.rows_valid) row = t.rows_valid - 1;      // clamp: loaded, never stored
-        c.a_row[i] = t.A + row * K + chunk * 16;
+        c.a_row[i] = t.A + row * K;
+        c.a_c16[i] = chunk * 16;
         c.a_lds[i] = int(offsetof(S, a)) + r0 * BK;
     }
 #pragma unroll
     for (int i = 0; i < C::B_PER_WAVE; ++i) {
         const int r0 = (wave * C::B_PER_WAVE + i) * 8, r = r0 + sub;
         const int chunk = slot ^ ((r >> 1) & 7);
-        c.b_row[i] = t.B + (n0 + r) * K + chunk * 16;
+        c.b_row[i] = t.B + (n0 + r) * K;
+        c.b_c16[i] = chunk * 16;
         c.b_lds[i] = int(offsetof(S, b)) + r0 * BK;
     }
     constexpr int a_waves = C::BM / 64;
@@ -295,7 +318,7 @@ __device__ __forceinline__ Copier<C> make_copier(const Tile& t, int wave, int la
             c.s_src = t.SB + n0 + j * 64 + lane;
             c.s_stride = N;
         } else {
-            c.s_src = t.SB + (n0 / 128 + j) * (K / BK);
+            c.s_src = t.SB + (n0 / 128 + j) * ((K + BK - 1) / BK);
             c.s_stride = 1;
         }
         c.s_lds = int(offsetof(S, sb)) + j * 64 * 4;
@@ -437,7 +460,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const int64_t N = args.N, K = args.K, kbs = K / BK;
+    const int64_t N = args.N, K = args.K, kbs = (K + BK - 1) / BK;   // the last K-block may be partial
     const Tile t = map_tile<C, MODE>(args, blockIdx.x);
     if (!t.live) return;
     const int64_t n0 = int64_t(t.bn) * C::BN;
@@ -468,6 +491,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
         // stage refilled below
         const int64_t later = kbs - 1 - kb;
         wait_copies<C>(int(later < STAGES - 2 ? later : STAGES - 2));
+        if ((kb + 1) * BK > K) {                  // partial last K-block (uniform)
+            cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[cur]), kb, lane);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
         __builtin_amdgcn_s_barrier();
         if (kb + STAGES - 1 < kbs) {
             const int nxt = cur == 0 ? STAGES - 1 : cur - 1;        // (kb + STAGES - 1) % STAGES
@@ -649,6 +676,22 @@ struct WideBufCopier {
     uint32_t va[W::A_PER_WAVE], vb[W::B_PER_WAVE], vs;   // per-lane byte offsets
     uint32_t s_step;           // scale byte offset per K-block
     int a_lds[W::A_PER_WAVE], b_lds[W::B_PER_WAVE], s_lds;
+    int a_c16[W::A_PER_WAVE], b_c16[W::B_PER_WAVE];       // the lane's chunk offset within a stage (bytes)
+    int64_t K;
+
+    // After this wave's loads of half-block h have landed: zero its 16-byte
+    // slots past K (a partial last K-block).  Those loads read whatever lies
+    // there -- the next row, or zeros past the buffer's range -- never
+    // outside the operand.
+    __device__ __forceinline__ void zero_tail(uint8_t* stage, int h, int lane) const {
+        const int64_t koff = int64_t(h) * W::KS;
+#pragma unroll
+        for (int i = 0; i < W::A_PER_WAVE; ++i)
+            if (koff + a_c16[i] >= K) st<u32x4>(stage + a_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+        for (int i = 0; i < W::B_PER_WAVE; ++i)
+            if (koff + b_c16[i] >= K) st<u32x4>(stage + b_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
+    }
 
     __device__ __forceinline__ void copy(uint8_t* stage, int h) const {
         const uint32_t koff = uint32_t(h) * W::KS;
@@ -667,6 +710,7 @@ __device__ __forceinline__ WideBufCopier<W> make_wide_buf_copier(const Tile& t, 
                                                                  int64_t n0) {
     typedef WStage<W> S;
     WideBufCopier<W> c;
+    c.K = K;
     const int sub = lane >> 2, slot = lane & 3;
     const int64_t tile_rows = t.rows_valid - t.m0 < W::BM ? t.rows_valid - t.m0 : W::BM;   // >= 1
     c.ra = make_rsrc(t.A + t.m0 * K, uint32_t(tile_rows * K));
@@ -677,6 +721,7 @@ __device__ __forceinline__ WideBufCopier<W> make_wide_buf_copier(const Tile& t, 
         const int chunk = slot ^ ((r >> 2) & 3);
         const int64_t row = r < tile_rows ? r : tile_rows - 1;      // clamp: loaded, never stored
         c.va[i] = uint32_t(row * K + chunk * 16);
+        c.a_c16[i] = chunk * 16;
         c.a_lds[i] = int(offsetof(S, a)) + r0 * W::KS;
     }
 #pragma unroll
@@ -684,9 +729,10 @@ __device__ __forceinline__ WideBufCopier<W> make_wide_buf_copier(const Tile& t, 
         const int r0 = (wave * W::B_PER_WAVE + i) * W::ROWS_PER_PIECE, r = r0 + sub;
         const int chunk = slot ^ ((r >> 2) & 3);
         c.vb[i] = uint32_t(int64_t(r) * K + chunk * 16);
+        c.b_c16[i] = chunk * 16;
         c.b_lds[i] = int(offsetof(S, b)) + r0 * W::KS;
     }
-    const int64_t kbs = K / BK;
+    const int64_t kbs = (K + BK - 1) / BK;
     if (wave < W::A_SCALE_WAVES) {        // A scales of rows 64 wave .. +63 (clamped)
         const int64_t rr = int64_t(wave) * 64 + lane;
         const int64_t row = rr < tile_rows ? rr : tile_rows - 1;
@@ -815,7 +861,7 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps wave-derived values scalar
     const int wm = wave / W::WAVES_N, wn = wave % W::WAVES_N;
     const int64_t N = args.N, K = args.K;
-    const int halves = int(2 * (K / BK));
+    const int halves = int(2 * ((K + BK - 1) / BK));   // the last K-block may be partial
     const Tile t = map_tile<W, MODE>(args, blockIdx.x);
     if (!t.live) return;
     const int64_t n0 = int64_t(t.bn) * W::BN;
@@ -861,6 +907,10 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
         for (int e = 0; e < 2; ++e) {
             const int cur = hb + e;
             wait_vmcnt<(STAGES - 2) * L>();   // this wave's copy of half-block cur has landed
+            if ((cur + 1) * W::KS > K) {      // partial last K-block (uniform)
+                cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[slot]), cur, lane);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
             __builtin_amdgcn_s_barrier();     // ... every wave's; the slot of cur - 1 is free
             const int fill = cur + STAGES - 1;
             cp.copy(reinterpret_cast<uint8_t*>(&ring[fill_slot]), fill < halves ? fill : halves - 1);
@@ -1191,7 +1241,7 @@ int64_t tile_count(GemmMode mode, const GemmArgs& args) {
 // is 256 wide.
 bool wide_fits(const GemmArgs& args) {
     if (args.N % WideTile::BN != 0 || args.K >= (int64_t(1) << 24)) return false;
-    return (args.K / BK) * args.M * 4 <= int64_t(0xFFFFFFFF);
+    return ((args.K + BK - 1) / BK) * args.M * 4 <= int64_t(0xFFFFFFFF);
 }
 
 // FP8FG_GEMM_WIDE=0 keeps the big tile for everything (comparison runs)

@@ -29,21 +29,22 @@ template <int U, class T>
 __device__ __forceinline__ void quant_act_rows_body(const T* __restrict__ x, int64_t M, int64_t K,
                                                     uint8_t* __restrict__ q, float* __restrict__ s) {
     const int lane = threadIdx.x & 31;
-    const int64_t kbs = K / kBlock;
+    const int64_t kbs = (K + kBlock - 1) / kBlock;     // a last partial group holds K % 128 elements
     const int64_t kb0 = int64_t(blockIdx.x) * U;
     for (int64_t m = int64_t(blockIdx.y) * 8 + (threadIdx.x >> 5); m < M; m += int64_t(gridDim.y) * 8) {
         const T* xr = x + m * K + kb0 * kBlock + lane * 4;
         uint8_t* qr = q + m * K + kb0 * kBlock + lane * 4;
         v4f v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = kb0 + u < kbs ? load4(xr + u * kBlock) : v4f{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < U; ++u)
+            v[u] = (kb0 + u) * kBlock + lane * 4 < K ? load4(xr + u * kBlock) : v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (kb0 + u >= kbs) break;
             const float amax = halfwave_max(abs_max4(v[u]));
             const float sc = amax / 448.0f;
             const float rc = 1.0f / sc;
-            st<uint32_t>(qr + u * kBlock, encode4(v[u], sc, rc));
+            if ((kb0 + u) * kBlock + lane * 4 < K) st<uint32_t>(qr + u * kBlock, encode4(v[u], sc, rc));
             if (lane == 0) s[(kb0 + u) * M + m] = sc;
         }
     }
@@ -68,14 +69,15 @@ template <int U>
 __device__ __forceinline__ void quant_act_rows_bf16_body(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                          uint8_t* __restrict__ q, float* __restrict__ s) {
     const int lane = threadIdx.x & 15;
-    const int64_t kbs = K / kBlock;
+    const int64_t kbs = (K + kBlock - 1) / kBlock;     // a last partial group holds K % 128 elements
     const int64_t kb0 = int64_t(blockIdx.x) * U;
     for (int64_t m = int64_t(blockIdx.y) * 16 + (threadIdx.x >> 4); m < M; m += int64_t(gridDim.y) * 16) {
         const uint16_t* xr = x + m * K + kb0 * kBlock + lane * 8;
         uint8_t* qr = q + m * K + kb0 * kBlock + lane * 8;
         u32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = kb0 + u < kbs ? ld<u32x4>(xr + u * kBlock) : u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < U; ++u)
+            v[u] = (kb0 + u) * kBlock + lane * 8 < K ? ld<u32x4>(xr + u * kBlock) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (kb0 + u >= kbs) break;
@@ -83,7 +85,8 @@ __device__ __forceinline__ void quant_act_rows_bf16_body(const uint16_t* __restr
             const float amax = quarterwave_max(fmaxf(abs_max4(lo), abs_max4(hi)));
             const float sc = amax / 448.0f;
             const float rc = 1.0f / sc;
-            st<u32x2_t>(qr + u * kBlock, u32x2_t{encode4(lo, sc, rc), encode4(hi, sc, rc)});
+            if ((kb0 + u) * kBlock + lane * 8 < K)
+                st<u32x2_t>(qr + u * kBlock, u32x2_t{encode4(lo, sc, rc), encode4(hi, sc, rc)});
             if (lane == 0) s[(kb0 + u) * M + m] = sc;
         }
     }
@@ -148,8 +151,15 @@ struct CacheSrc {
     const uint8_t* q;
     const float* s;
     int64_t M, K;
-    __device__ __forceinline__ bool full(int64_t) const { return true; }   // K is a multiple of 128
-    __device__ __forceinline__ void load(int64_t m, int64_t k, float (&e)[E]) const { load_fast(m, k, e); }
+    __device__ __forceinline__ bool full(int64_t k0) const { return k0 + kTokCh <= K; }
+    __device__ __forceinline__ void load(int64_t m, int64_t k, float (&e)[E]) const {
+        if (k < K) {                        // K % 8 == 0: the eight channels exist together
+            load_fast(m, k, e);
+        } else {
+#pragma unroll
+            for (int j = 0; j < E; ++j) e[j] = 0.0f;
+        }
+    }
     __device__ __forceinline__ void load_fast(int64_t m, int64_t k, float (&e)[E]) const {
         const u32x2_t w = ld<u32x2_t>(q + m * K + k);
         const float sc = s[(k / kBlock) * M + m];
@@ -182,7 +192,7 @@ __device__ __forceinline__ void quant_tokens_core(const Src& src, int64_t M, int
     constexpr int E = Src::E, TPR = kTokCh / E, RSTEP = 256 / TPR;
     constexpr int NI = kBlock / RSTEP;
     const int ce = (t % TPR) * E;
-    if (src.full(k0)) {             // uniform: all loads in flight before the first use
+    if (src.full(k0) && (mb + 1) * kBlock <= M) {   // uniform: all loads in flight before the first use
         float e[NI][E];
 #pragma unroll
         for (int i = 0; i < NI; ++i) src.load_fast(mb * kBlock + t / TPR + RSTEP * i, k0 + ce, e[i]);
@@ -195,7 +205,12 @@ __device__ __forceinline__ void quant_tokens_core(const Src& src, int64_t M, int
         for (int i = 0; i < NI; ++i) {
             const int r = t / TPR + RSTEP * i;
             float e[E];
-            src.load(mb * kBlock + r, k0 + ce, e);
+            if (mb * kBlock + r < M) {      // a last partial tile of M % 128 tokens
+                src.load(mb * kBlock + r, k0 + ce, e);
+            } else {
+#pragma unroll
+                for (int j = 0; j < E; ++j) e[j] = 0.0f;
+            }
 #pragma unroll
             for (int j = 0; j < E; ++j) tile[r][ce + j] = e[j];
         }
@@ -231,7 +246,8 @@ __device__ __forceinline__ void quant_tokens_core(const Src& src, int64_t M, int
     for (int i = 0; i < 2; ++i) {
         const int piece = t + 256 * i;             // 64 rows x 8 pieces of 16 bytes
         const int row = piece >> 3, off = (piece & 7) * 16;
-        if (k0 + row < K) st<u32x4>(q + (k0 + row) * M + mb * kBlock + off, ld<u32x4>(&codes[row][off]));
+        if (k0 + row < K && mb * kBlock + off < M)   // M % 16 == 0: whole 16-byte pieces
+            st<u32x4>(q + (k0 + row) * M + mb * kBlock + off, ld<u32x4>(&codes[row][off]));
     }
 }
 
@@ -270,11 +286,13 @@ __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64
     const int c4 = (t & 31) * 4;
     const int r0 = (t >> 5) * 16;
     const T* wb = w + nb * kBlock * K + kb * kBlock + c4;
+    const bool cvalid = kb * kBlock + c4 < K;     // K % 16 == 0: a last partial block of K % 128 columns
+    const int64_t kbs = (K + kBlock - 1) / kBlock;
     v4f v[16];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        v[i] = load4(wb + int64_t(r0 + i) * K);
+        v[i] = cvalid ? load4(wb + int64_t(r0 + i) * K) : v4f{0.f, 0.f, 0.f, 0.f};
         amax = fmaxf(amax, abs_max4(v[i]));
     }
     amax = wave_max(amax);
@@ -287,9 +305,9 @@ __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int64_t row = nb * kBlock + r0 + i;
-            *reinterpret_cast<uint32_t*>(q + row * K + kb * kBlock + c4) = encode4(v[i], sc, rc);
+            if (cvalid) *reinterpret_cast<uint32_t*>(q + row * K + kb * kBlock + c4) = encode4(v[i], sc, rc);
         }
-        if (t == 0) s[nb * (K / kBlock) + kb] = sc;
+        if (t == 0) s[nb * kbs + kb] = sc;
         return;
     }
 #pragma unroll
@@ -307,7 +325,8 @@ __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64
     for (int i = 0; i < 4; ++i) {
         const int piece = t + 256 * i;          // 1024 pieces of 16 B
         const int kr = piece >> 3, off = (piece & 7) * 16;
-        st<u32x4>(q + (kb * kBlock + kr) * N + nb * kBlock + off, ld<u32x4>(&qt[qt_off(kr, off)]));
+        if (kb * kBlock + kr < K)
+            st<u32x4>(q + (kb * kBlock + kr) * N + nb * kBlock + off, ld<u32x4>(&qt[qt_off(kr, off)]));
     }
     if (t == 0) s[kb * (N / kBlock) + nb] = sc;
 }
@@ -413,12 +432,12 @@ static hipError_t launch_act(const T* x, int64_t M, int64_t K, int transpose_out
     if (!transpose_out) {
         constexpr int U = 4;
         constexpr int rows_per_group = sizeof(T) == 4 ? 8 : 16;   // half-waves (fp32) or quarter-waves (bf16)
-        const int64_t chunks = (K / kBlock + U - 1) / U;
+        const int64_t chunks = ((K + kBlock - 1) / kBlock + U - 1) / U;
         int64_t row_groups = (M + rows_per_group - 1) / rows_per_group;
         if (row_groups > 65535) row_groups = 65535;      // the kernel strides over the rest
         hipLaunchKernelGGL(rows, dim3(unsigned(chunks), unsigned(row_groups)), dim3(256), 0, stream, x, M, K, q, s);
     } else {
-        const dim3 grid(unsigned(M / kBlock), unsigned((K + kTokCh - 1) / kTokCh));
+        const dim3 grid(unsigned((M + kBlock - 1) / kBlock), unsigned((K + kTokCh - 1) / kTokCh));
         hipLaunchKernelGGL(tokens, grid, dim3(256), 0, stream, x, M, K, q, s);
     }
     return hipGetLastError();
@@ -435,14 +454,14 @@ hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, int t
 
 hipError_t launch_requant_act_tokens(const uint8_t* qr, const float* sr, int64_t M, int64_t K, uint8_t* q, float* s,
                                      hipStream_t stream) {
-    const dim3 grid(unsigned(M / kBlock), unsigned(K / kTokCh));
+    const dim3 grid(unsigned((M + kBlock - 1) / kBlock), unsigned((K + kTokCh - 1) / kTokCh));
     hipLaunchKernelGGL(requant_act_tokens, grid, dim3(256), 0, stream, qr, sr, M, K, q, s);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_weight(const void* w, int bf16, int64_t N, int64_t K, int transpose_out, uint8_t* q,
                                float* s, hipStream_t stream) {
-    const dim3 grid(unsigned(K / kBlock), unsigned(N / kBlock));
+    const dim3 grid(unsigned((K + kBlock - 1) / kBlock), unsigned(N / kBlock));
     if (bf16)
         hipLaunchKernelGGL(quant_weight_bf16, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(w), N, K,
                            transpose_out, q, s);

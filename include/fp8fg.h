@@ -35,6 +35,12 @@
  *     axis the 128-element groups run along) stores codes u8 [R][K] row-major
  *     and scales f32 [K/128][R] ("kb-major").  A 128x128-scaled [N][K] operand
  *     stores codes u8 [N][K] and scales f32 [N/128][K/128].
+ *   - Partial groups.  The grouped axis (K, or the token axis of the
+ *     token-wise layout) need only be a multiple of 16: the last group then
+ *     holds fewer than 128 elements and is quantized as that group padded
+ *     with zeros (its max-abs runs over the elements that exist).  Every
+ *     count "K/128" in this header means ceil(K/128).  N stays a multiple of
+ *     128.
  *   - GEMM: C[M][N] = A[M][K] . B[N][K]^T, both operands K-major (a Linear
  *     layer y = x . W^T with W [out][in]).  C is the sum over k of
  *     decode(a) * sA * decode(b) * sB, the scales of each 128-wide K-block
@@ -81,10 +87,10 @@ enum fp8fg_bscale {
  * Online 1x128 activation quantization.
  * x: f32 [M][K] row-major (M tokens, K channels).
  * transpose_out = 0: tiles run along K (one token x 128 channels).
- *     q: u8 [M][K], s: f32 [K/128][M].          Requires K % 128 == 0.
+ *     q: u8 [M][K], s: f32 [K/128][M].          Requires K % 16 == 0.
  * transpose_out = 1: tiles run along M (128 tokens x one channel), the
  *     operand layout of the Wgrad GEMM, whose contraction runs over tokens.
- *     q: u8 [K][M] (transposed), s: f32 [M/128][K].  Requires M % 128 == 0.
+ *     q: u8 [K][M] (transposed), s: f32 [M/128][K].  Requires M % 16 == 0.
  * Sizes: M, K >= 0 and M * K < 2^40.
  */
 int fp8_quant_act_1x128(const float* x, int64_t M, int64_t K, int transpose_out,
@@ -97,7 +103,7 @@ int fp8_quant_act_1x128(const float* x, int64_t M, int64_t K, int transpose_out,
  * transpose_out = 1: q u8 [K][N] = the codes of w, transposed, with
  *     s f32 [K/128][N/128]: the B operand of the Dgrad GEMM.  Square blocks
  *     make this identical to quantizing w^T.
- * Requires N % 128 == 0 and K % 128 == 0; N * K < 2^40.
+ * Requires N % 128 == 0 and K % 16 == 0; N * K < 2^40.
  */
 int fp8_quant_weight_128x128(const float* w, int64_t N, int64_t K, int transpose_out,
                              uint8_t* q, float* s, void* stream);
@@ -128,7 +134,7 @@ int fp8_quant_weight_128x128_bf16(const uint16_t* w, int64_t N, int64_t K, int t
  *   x'[m][k] = RN32(decode(q[m][k]) * s[k/128][m])  (fp32, one rounding);
  *   qt: u8 [K][M], st: f32 [M/128][K]  -- 1x128 codes of x' along tokens,
  *      transposed: exactly fp8_quant_act_1x128(x', transpose_out = 1).
- * Requires M % 128 == 0 and K % 128 == 0; M * K < 2^40.  Codes 0x7F / 0xFF
+ * Requires M % 16 == 0 and K % 16 == 0; M * K < 2^40.  Codes 0x7F / 0xFF
  * (NaN) in q give unspecified output.
  */
 int fp8_requant_act_tokenwise(const uint8_t* q, const float* s, int64_t M, int64_t K,
@@ -164,7 +170,8 @@ int fp8_gemm_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uin
  * b: u8 [N][K] with sb laid out per bscale_kind (fp8fg_bscale).
  * c: [M][N], BF16 (uint16 bit patterns) or FP32 per out_dtype (fp8fg_out).
  * Requires M >= 0 (any value, ragged tails allowed), N % 128 == 0,
- * K % 128 == 0, K > 0 when M*N > 0; M, N, K < 2^31.
+ * K % 16 == 0 (a last partial K-block is allowed), K > 0 when M*N > 0;
+ * M, N, K < 2^31.
  */
 int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                          int bscale_kind, void* c, int out_dtype,
@@ -183,7 +190,7 @@ int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, co
  * a: u8 [M_total][K], sa f32 [K/128][M_total];
  * b: u8 [G][N][K], sb f32 [G][N/128][K/128] (128x128 blocks per expert);
  * c: [M_total][N] BF16 or FP32.
- * Requires M_total % 128 == 0, N % 128 == 0, K % 128 == 0, K > 0, G >= 0.
+ * Requires M_total % 128 == 0, N % 128 == 0, K % 16 == 0, K > 0, G >= 0.
  */
 int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                                 const int32_t* group_offsets, int64_t G, int64_t M_total,
@@ -198,7 +205,7 @@ int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t
  * a: u8 [G][M_max][K], sa f32 [G][K/128][M_max];
  * b: u8 [G][N][K], sb f32 [G][N/128][K/128];
  * c: [G][M_max][N] BF16 or FP32.
- * Requires M_max >= 0, N % 128 == 0, K % 128 == 0, K > 0, G >= 0.
+ * Requires M_max >= 0, N % 128 == 0, K % 16 == 0, K > 0, G >= 0.
  */
 int fp8_grouped_gemm_masked(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                             const int32_t* masked_m, int64_t G, int64_t M_max,

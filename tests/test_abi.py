@@ -44,15 +44,15 @@ def test_quant_argument_errors():
     lib = fp8.load_library()
     q = lib.fp8_quant_act_1x128
     assert q(NUL, 128, 128, 0, P, P2, NUL) == ENULL
-    assert q(P, 128, 100, 0, P, P2, NUL) == ESHAPE          # K % 128
-    assert q(P, 100, 128, 1, P, P2, NUL) == ESHAPE          # tokens % 128 when transposed
+    assert q(P, 128, 100, 0, P, P2, NUL) == ESHAPE          # K % 16
+    assert q(P, 100, 128, 1, P, P2, NUL) == ESHAPE          # tokens % 16 when transposed
     assert q(P, -1, 128, 0, P, P2, NUL) == ESHAPE
     assert q(MIS, 128, 128, 0, P, P2, NUL) == EALIGN
     assert q(P, 128, 128, 2, P, P2, NUL) == EUNSUP
     assert q(P, 0, 128, 0, P, P2, NUL) == OK                # empty: no launch
     assert q(P, 128, 0, 1, P, P2, NUL) == OK
     w = lib.fp8_quant_weight_128x128
-    assert w(P, 128, 64, 0, P, P2, NUL) == ESHAPE
+    assert w(P, 128, 72, 0, P, P2, NUL) == ESHAPE          # K % 16
     assert w(P, 64, 128, 0, P, P2, NUL) == ESHAPE
     assert w(P, 128, 128, 0, NUL, P2, NUL) == ENULL
     assert w(P, 128, 128, 0, P, MIS, NUL) == EALIGN
@@ -69,7 +69,7 @@ def test_bf16_quant_argument_errors():
     assert q(P, 128, 128, -1, P, P2, NUL) == EUNSUP
     assert q(P, 0, 128, 1, P, P2, NUL) == OK
     w = lib.fp8_quant_weight_128x128_bf16
-    assert w(P, 128, 64, 1, P, P2, NUL) == ESHAPE
+    assert w(P, 128, 72, 1, P, P2, NUL) == ESHAPE
     assert w(P, 128, 128, 0, P, NUL, NUL) == ENULL
     assert w(MIS, 128, 128, 0, P, P2, NUL) == EALIGN
     assert w(P, 128, 128, 3, P, P2, NUL) == EUNSUP
@@ -80,8 +80,8 @@ def test_requant_argument_errors():
     r = fp8.load_library().fp8_requant_act_tokenwise
     assert r(NUL, P, 128, 128, P, P2, NUL) == ENULL
     assert r(P, P, 128, 128, P, NUL, NUL) == ENULL
-    assert r(P, P, 100, 128, P, P2, NUL) == ESHAPE       # tokens % 128
-    assert r(P, P, 128, 64, P, P2, NUL) == ESHAPE        # channels % 128
+    assert r(P, P, 100, 128, P, P2, NUL) == ESHAPE       # tokens % 16
+    assert r(P, P, 128, 72, P, P2, NUL) == ESHAPE        # channels % 16
     assert r(P, P, -128, 128, P, P2, NUL) == ESHAPE
     assert r(P, MIS, 128, 128, P, P2, NUL) == EALIGN
     assert r(P, P, 0, 128, P, P2, NUL) == OK
@@ -110,7 +110,7 @@ def test_gemm_argument_errors():
     g = fp8.load_library().fp8_gemm_blockscaled
     assert g(P, P, P, NUL, 0, P, 0, 1, 128, 128, NUL) == ENULL
     assert g(P, P, P, P, 0, P, 0, 1, 100, 128, NUL) == ESHAPE     # N % 128
-    assert g(P, P, P, P, 0, P, 0, 1, 128, 100, NUL) == ESHAPE     # K % 128
+    assert g(P, P, P, P, 0, P, 0, 1, 128, 100, NUL) == ESHAPE     # K % 16
     assert g(P, P, P, P, 0, P, 0, 1, 128, 0, NUL) == ESHAPE       # empty contraction
     assert g(P, P, MIS, P, 0, P, 0, 1, 128, 128, NUL) == EALIGN
     assert g(P, P, P, P, 5, P, 0, 1, 128, 128, NUL) == EUNSUP     # bscale kind
