@@ -228,6 +228,11 @@ def run_extra(args):
         fl = 2.0 * TOK * IN * OUT
         ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled(qx, sx, qw, sw, 0, torch.bfloat16, out=yb), T, W, stream)
         extra_line("linear_trio", "gemm Fprop 8192x2048x7168 BF16", ms, flops=fl, args=args, config=cfg)
+        qy = torch.empty((TOK, OUT), dtype=torch.uint8, device="cuda")
+        sy = torch.empty((OUT // 128, TOK), dtype=torch.float32, device="cuda")
+        ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled_fp8out(qx, sx, qw, sw, q=qy, s=sy), T, W, stream)
+        extra_line("linear_trio", "gemm Fprop 8192x2048x7168, FP8 out (fused 1x128 quantization)", ms, flops=fl,
+                   args=args, config=cfg)
         ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled(qd, sd, qwt, swt, 0, torch.bfloat16, out=dxb), T, W, stream)
         extra_line("linear_trio", "gemm Dgrad 8192x7168x2048 BF16", ms, flops=fl, args=args, config=cfg)
         ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled(qdt, sdt, qxt, sxt, 1, torch.float32, out=dwf), T, W, stream)
@@ -385,6 +390,10 @@ def main():
     t_act = back_to_back(lambda s: fp8.fp8_quant_act_1x128(s["x"], q=s["qa"], s=s["sa"]))
     t_w = back_to_back(lambda s: fp8.fp8_quant_weight_128x128(s["w"], q=s["qb"], s=s["sb"]))
     t_gemm = gemm_back_to_back()
+    # the same GEMM with the next layer's 1x128 quantization fused into its epilogue
+    qy = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    sy = torch.empty((N // 128, M), dtype=torch.float32, device=dev)
+    t_fp8out = back_to_back(lambda s: fp8.fp8_gemm_blockscaled_fp8out(s["qa"], s["sa"], s["qb"], s["sb"], q=qy, s=sy))
     # the opt-in FP8-MFMA engine (looser error bound), GEMM alone, for comparison
     os.environ["FP8FG_GEMM_ENGINE"] = "fp8mfma"
     t_fp8mfma = gemm_back_to_back()
@@ -427,6 +436,10 @@ def main():
                      "duration_source": "mean of `steps` back-to-back launches on the bench stream between two "
                                         "HIP events, right after the timed steps",
                      "kernel_source": source_hash()},
+        "fp8_out_fused": {"gemm_us": round(t_fp8out * 1e3, 2),
+                          "tflops": round(flops / (t_fp8out * 1e-3) / 1e12, 2),
+                          "note": "same GEMM writing FP8 codes + 1x128 scales along N (the next layer's A "
+                                  "operand) instead of BF16; not the timed step"},
         "fp8mfma_engine": {"gemm_us": round(t_fp8mfma * 1e3, 2),
                            "tflops": round(flops / (t_fp8mfma * 1e-3) / 1e12, 2),
                            "pct_of_fp8_peak": round(100 * flops / (t_fp8mfma * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),

@@ -22,13 +22,13 @@ BSCALE_1x128 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
            "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
            "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16", "fp8_requant_act_tokenwise",
-           "fp8_quant_mx_1x32", "fp8_gemm_mx",
+           "fp8_quant_mx_1x32", "fp8_gemm_mx", "fp8_gemm_blockscaled_fp8out",
            "fp8fg_status_string", "fp8fg_abi_version")
-_COMPUTE = EXPORTS[:10]
+_COMPUTE = EXPORTS[:11]
 
 
 class Fp8fgError(RuntimeError):
@@ -60,6 +60,7 @@ def load_library(path=LIB_PATH):
     lib.fp8_requant_act_tokenwise.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     lib.fp8_quant_mx_1x32.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.fp8_gemm_mx.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    lib.fp8_gemm_blockscaled_fp8out.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
     for name in _COMPUTE:
         getattr(lib, name).restype = ctypes.c_int
     lib.fp8fg_status_string.argtypes = [ctypes.c_int]
@@ -220,6 +221,24 @@ def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind=BSCALE_128x128, out_dtype=tor
         _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), int(bscale_kind), _ptr(out), _out_dtype(out_dtype),
         M, N, K, _stream(a)))
     return out
+
+
+def fp8_gemm_blockscaled_fp8out(a, sa, b, sb, q=None, s=None):
+    """C = A . B^T (128x128 B scales) quantized 1x128 along N in the epilogue:
+    returns (q u8 [M][N], s f32 [N/128][M]) -- the next layer's A operand."""
+    M, K = a.shape
+    N = b.shape[0]
+    _need(a, torch.uint8, (M, K), "a")
+    _need(sa, torch.float32, (_nb(K), M), "sa")
+    _need(b, torch.uint8, (N, K), "b")
+    _need(sb, torch.float32, (N // 128, _nb(K)), "sb")
+    q = _empty((M, N), torch.uint8, a) if q is None else q
+    s = _empty((N // 128, M), torch.float32, a) if s is None else s
+    _need(q, torch.uint8, (M, N), "q")
+    _need(s, torch.float32, (N // 128, M), "s")
+    _check("fp8_gemm_blockscaled_fp8out", load_library().fp8_gemm_blockscaled_fp8out(
+        _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(q), _ptr(s), M, N, K, _stream(a)))
+    return q, s
 
 
 def fp8_grouped_gemm_contiguous(a, sa, b, sb, group_offsets, out_dtype=torch.bfloat16, out=None):

@@ -139,6 +139,21 @@ int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, co
                                          out_dtype == FP8FG_OUT_FP32, args, static_cast<hipStream_t>(stream)));
 }
 
+int fp8_gemm_blockscaled_fp8out(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, uint8_t* q,
+                                float* s, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!a || !sa || !b || !sb || !q || !s) return FP8FG_ERR_NULL;
+    if (M < 0 || N < 0 || K < 0 || N % 256 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
+    if (K == 0 && M > 0 && N > 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(q) || !aligned16(s))
+        return FP8FG_ERR_ALIGN;
+    if (M > kMaxDim || N > kMaxDim || K >= (int64_t(1) << 24)) return FP8FG_ERR_UNSUPPORTED;
+    if (((K + 127) / 128) * M * 4 > int64_t(0xFFFFFFFF)) return FP8FG_ERR_UNSUPPORTED;
+    if (((M + 255) / 256) * (N / 256) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return FP8FG_OK;
+    fp8fg::GemmArgs args{a, sa, b, sb, q, nullptr, M, N, K, 1, s};
+    return hip_status(fp8fg::launch_gemm(fp8fg::GemmMode::Dense, 0, 2, args, static_cast<hipStream_t>(stream)));
+}
+
 int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                                 const int32_t* group_offsets, int64_t G, int64_t M_total, int64_t N, int64_t K,
                                 void* c, int out_dtype, void* stream) {

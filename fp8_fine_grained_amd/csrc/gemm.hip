@@ -849,7 +849,8 @@ __device__ __forceinline__ void rescale(v16f (&acc)[FM][FN], const WideScales<FM
     }
 }
 
-template <class W, int OUT_FP32, int MODE>
+// OUT: 0 = BF16, 1 = FP32, 2 = FP8 codes + 1x128 scales along N (dense only)
+template <class W, int OUT, int MODE>
 __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
     typedef WStage<W> S;
     constexpr int FM = W::FM, FN = W::FN, STAGES = W::STAGES;
@@ -935,6 +936,38 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
     wait_vmcnt<0>();   // no copy may land after the workgroup's LDS is handed on
 
     const int n_lane = wn * FN * 32 + 4 * h;
+    if constexpr (OUT == 2) {
+        // Fused 1x128 quantization of C along N for the next layer: the
+        // wave's 128 columns are one group (they start on a multiple of 128),
+        // and row m's 128 values sit in lanes r and r + 32.  The values are the
+        // FP32 output's, bit for bit; the group is quantized exactly as the
+        // 1x128 activation quantizer does (amax / 448, RN32(x / s), E4M3).
+        static_assert(FN * 32 == 128, "one 128-column group per wave");
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(acc[mi][ni][i] * w.unit[mi]));
+            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+            const float sc = amax / 448.0f;
+            const float rc = 1.0f / sc;
+            const int64_t m = wrow0 + mi * 32 + r;
+            if (m >= t.rows_valid) continue;
+#pragma unroll
+            for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
+                                      acc[mi][ni][4 * j + 3]} * w.unit[mi];
+                    st<uint32_t>(static_cast<uint8_t*>(args.c) + m * N + n0 + n_lane + ni * 32 + 8 * j,
+                                 encode4(v, sc, rc));
+                }
+            if (h == 0) args.cs[(n0 / 128 + wn) * args.M + m] = sc;
+        }
+        return;
+    }
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi) {
         const int64_t m = wrow0 + mi * 32 + r;
@@ -946,7 +979,7 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
                 const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
                 const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
                                   acc[mi][ni][4 * j + 3]} * w.unit[mi];
-                if (OUT_FP32) {
+                if (OUT == 1) {
                     st<v4f>(static_cast<float*>(args.c) + idx, v);
                 } else {
                     const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
@@ -1216,7 +1249,8 @@ const KernelEntry kKernels[] = {FP8FG_GEMM_KERNELS(FP8FG_ENTRY)};
     X(wide_o0_masked, WideTile, 2, 0, 2)            \
     X(wide_o1_masked, WideTile, 2, 1, 2)            \
     X(wdec_o0_masked, WideDecodeTile, 3, 0, 2)      \
-    X(wdec_o1_masked, WideDecodeTile, 3, 1, 2)
+    X(wdec_o1_masked, WideDecodeTile, 3, 1, 2)      \
+    X(wide_o2_dense, WideTile, 2, 2, 0)
 #define FP8FG_DEFINE_WIDE(NAME, CFG, TILE, OF, MODE)                                   \
     __global__ __launch_bounds__(CFG::THREADS) void gemm_##NAME(GemmArgs args) {       \
         gemm_wide_body<CFG, OF, MODE>(args);                                           \
@@ -1257,7 +1291,10 @@ hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, c
     // 128 rows), 256 x 256 tiles otherwise.  The rest (1x128 B scales, the
     // FP8-MFMA engine, N = 128 mod 256) runs the fold kernel: 64 x 128 tiles
     // for decode-sized masked buffers, 256 x 128 tiles otherwise.
-    const bool wide = engine == 0 && !bscale_1x128 && wide_fits(args) && wide_enabled();
+    // the FP8 output mode exists only in the wide exact kernel (the entry point
+    // checks that it fits)
+    const bool wide = out_fp32 == 2 || (engine == 0 && !bscale_1x128 && wide_fits(args) && wide_enabled());
+    if (out_fp32 == 2) engine = 0;
     int tile = 0;
     if (mode == GemmMode::Masked && args.M <= 128)
         tile = wide ? 3 : 1;

@@ -28,6 +28,7 @@ struct GemmArgs {
     int64_t M;              // rows: dense M, contiguous M_total, masked M_max (per group)
     int64_t N, K;
     int64_t G;              // groups (1 for dense)
+    float* cs;              // output scales [N/128][M] of the FP8 output mode (else unused)
 };
 
 // MX GEMM: args.sa / args.sb carry the E8M0 scale bytes ([K/32][M], [K/32][N])

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 4
+#define FP8FG_ABI_VERSION 5
 
 enum fp8fg_status {
     FP8FG_OK = 0,
@@ -176,6 +176,21 @@ int fp8_gemm_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uin
 int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                          int bscale_kind, void* c, int out_dtype,
                          int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Dense GEMM with the next layer's quantization fused into the epilogue
+ * ("The Insider Secrets Of Deepseek Discovered", passage on Figure 6: with
+ * every Linear in FP8, a layer's output is quantized again before it feeds
+ * the next one).  Computes the FP32 C of fp8_gemm_blockscaled (128x128 B
+ * scales) and writes, instead of C, its 1x128 quantization along N:
+ *   q: u8 [M][N], s: f32 [N/128][M] -- exactly fp8_quant_act_1x128 applied to
+ *   the FP32 C that out_dtype = FP8FG_OUT_FP32 would write (same values, bit
+ *   for bit), i.e. the A operand layout of a following GEMM with K = N.
+ * Always the exact engine.  Requires N % 256 == 0, K % 16 == 0, K > 0 when
+ * M * N > 0, K < 2^24, ceil(K/128) * M * 4 < 2^32.
+ */
+int fp8_gemm_blockscaled_fp8out(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                uint8_t* q, float* s, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * MoE grouped GEMM, contiguous layout (training / prefill).

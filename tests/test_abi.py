@@ -119,6 +119,16 @@ def test_gemm_argument_errors():
     assert g(P, P, P, P, 1, P, 1, 5, 0, 128, NUL) == OK            # N = 0
 
 
+def test_fp8out_argument_errors():
+    f = fp8.load_library().fp8_gemm_blockscaled_fp8out
+    assert f(P, P, P, P, P, NUL, 4, 256, 128, NUL) == ENULL
+    assert f(P, P, P, P, P, P2, 4, 128, 128, NUL) == ESHAPE     # N % 256
+    assert f(P, P, P, P, P, P2, 4, 256, 72, NUL) == ESHAPE      # K % 16
+    assert f(P, P, P, P, P, P2, 4, 256, 0, NUL) == ESHAPE
+    assert f(P, P, P, P, MIS, P2, 4, 256, 128, NUL) == EALIGN
+    assert f(P, P, P, P, P, P2, 0, 256, 128, NUL) == OK
+
+
 def test_grouped_argument_errors():
     lib = fp8.load_library()
     c = lib.fp8_grouped_gemm_contiguous
