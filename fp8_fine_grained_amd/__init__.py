@@ -129,7 +129,7 @@ def _quant_weight(fn, w, dtype, transpose_out, q, s):
     N, K = w.shape
     _need(w, dtype, (N, K), "w")
     qs = (K, N) if transpose_out else (N, K)
-    ss = (_nb(K), N // 128) if transpose_out else (N // 128, _nb(K))
+    ss = (_nb(K), _nb(N)) if transpose_out else (_nb(N), _nb(K))
     q = _empty(qs, torch.uint8, w) if q is None else q
     s = _empty(ss, torch.float32, w) if s is None else s
     _need(q, torch.uint8, qs, "q")
@@ -214,7 +214,7 @@ def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind=BSCALE_128x128, out_dtype=tor
     _need(a, torch.uint8, (M, K), "a")
     _need(sa, torch.float32, (_nb(K), M), "sa")
     _need(b, torch.uint8, (N, K), "b")
-    _need(sb, torch.float32, (N // 128, _nb(K)) if bscale_kind == BSCALE_128x128 else (_nb(K), N), "sb")
+    _need(sb, torch.float32, (_nb(N), _nb(K)) if bscale_kind == BSCALE_128x128 else (_nb(K), N), "sb")
     out = _empty((M, N), out_dtype, a) if out is None else out
     _need(out, out_dtype, (M, N), "out")
     _check("fp8_gemm_blockscaled", load_library().fp8_gemm_blockscaled(
@@ -248,7 +248,7 @@ def fp8_grouped_gemm_contiguous(a, sa, b, sb, group_offsets, out_dtype=torch.bfl
     _need(a, torch.uint8, (M_total, K), "a")
     _need(sa, torch.float32, (_nb(K), M_total), "sa")
     _need(b, torch.uint8, (G, N, K), "b")
-    _need(sb, torch.float32, (G, N // 128, _nb(K)), "sb")
+    _need(sb, torch.float32, (G, _nb(N), _nb(K)), "sb")
     _need(group_offsets, torch.int32, (G + 1,), "group_offsets")
     out = _empty((M_total, N), out_dtype, a) if out is None else out
     _need(out, out_dtype, (M_total, N), "out")
@@ -265,7 +265,7 @@ def fp8_grouped_gemm_masked(a, sa, b, sb, masked_m, out_dtype=torch.bfloat16, ou
     _need(a, torch.uint8, (G, M_max, K), "a")
     _need(sa, torch.float32, (G, _nb(K), M_max), "sa")
     _need(b, torch.uint8, (G, N, K), "b")
-    _need(sb, torch.float32, (G, N // 128, _nb(K)), "sb")
+    _need(sb, torch.float32, (G, _nb(N), _nb(K)), "sb")
     _need(masked_m, torch.int32, (G,), "masked_m")
     out = _empty((G, M_max, N), out_dtype, a) if out is None else out
     _need(out, out_dtype, (G, M_max, N), "out")

@@ -57,11 +57,11 @@ static int quant_act(const void* x, int bf16, int64_t M, int64_t K, int transpos
 static int quant_weight(const void* w, int bf16, int64_t N, int64_t K, int transpose_out, uint8_t* q, float* s,
                         void* stream) {
     if (!w || !q || !s) return FP8FG_ERR_NULL;
-    if (N < 0 || K < 0 || N % 128 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
+    if (N < 0 || K < 0 || N % 16 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
     if (transpose_out != 0 && transpose_out != 1) return FP8FG_ERR_UNSUPPORTED;
     if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return FP8FG_ERR_ALIGN;
     if (N > kMaxDim || K > kMaxDim || (N > 0 && K > kMaxElems / N)) return FP8FG_ERR_UNSUPPORTED;
-    if (N / 128 > 65535) return FP8FG_ERR_UNSUPPORTED;
+    if ((N + 127) / 128 > 65535) return FP8FG_ERR_UNSUPPORTED;
     if (N == 0 || K == 0) return FP8FG_OK;
     return hip_status(
         fp8fg::launch_quant_weight(w, bf16, N, K, transpose_out, q, s, static_cast<hipStream_t>(stream)));
@@ -126,13 +126,13 @@ int fp8_gemm_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uin
 int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int bscale_kind,
                          void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
     if (!a || !sa || !b || !sb || !c) return FP8FG_ERR_NULL;
-    if (M < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
+    if (M < 0 || N < 0 || K < 0 || N % 16 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
     if (K == 0 && M > 0 && N > 0) return FP8FG_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(c)) return FP8FG_ERR_ALIGN;
     if (bscale_kind != FP8FG_BSCALE_128x128 && bscale_kind != FP8FG_BSCALE_1x128) return FP8FG_ERR_UNSUPPORTED;
     if (!valid_out(out_dtype)) return FP8FG_ERR_UNSUPPORTED;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
-    if (((M + 127) / 128) * (N / 128) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return FP8FG_OK;
     fp8fg::GemmArgs args{a, sa, b, sb, c, nullptr, M, N, K, 1};
     return hip_status(fp8fg::launch_gemm(fp8fg::GemmMode::Dense, bscale_kind == FP8FG_BSCALE_1x128,
@@ -158,7 +158,7 @@ int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t
                                 const int32_t* group_offsets, int64_t G, int64_t M_total, int64_t N, int64_t K,
                                 void* c, int out_dtype, void* stream) {
     if (!a || !sa || !b || !sb || !group_offsets || !c) return FP8FG_ERR_NULL;
-    if (G < 0 || M_total < 0 || N < 0 || K < 0 || M_total % 128 != 0 || N % 128 != 0 || K % 16 != 0)
+    if (G < 0 || M_total < 0 || N < 0 || K < 0 || M_total % 128 != 0 || N % 16 != 0 || K % 16 != 0)
         return FP8FG_ERR_SHAPE;
     if (K == 0 && M_total > 0 && N > 0 && G > 0) return FP8FG_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(c) ||
@@ -166,7 +166,7 @@ int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t
         return FP8FG_ERR_ALIGN;
     if (!valid_out(out_dtype)) return FP8FG_ERR_UNSUPPORTED;
     if (M_total > kMaxDim || N > kMaxDim || K > kMaxDim || G > kMaxDim - 1) return FP8FG_ERR_UNSUPPORTED;
-    if ((M_total / 128) * (N / 128) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if ((M_total / 128) * ((N + 127) / 128) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
     if (G == 0 || M_total == 0 || N == 0) return FP8FG_OK;
     fp8fg::GemmArgs args{a, sa, b, sb, c, group_offsets, M_total, N, K, G};
     return hip_status(fp8fg::launch_gemm(fp8fg::GemmMode::Contig, 0, out_dtype == FP8FG_OUT_FP32, args,
@@ -177,13 +177,13 @@ int fp8_grouped_gemm_masked(const uint8_t* a, const float* sa, const uint8_t* b,
                             const int32_t* masked_m, int64_t G, int64_t M_max, int64_t N, int64_t K, void* c,
                             int out_dtype, void* stream) {
     if (!a || !sa || !b || !sb || !masked_m || !c) return FP8FG_ERR_NULL;
-    if (G < 0 || M_max < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
+    if (G < 0 || M_max < 0 || N < 0 || K < 0 || N % 16 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
     if (K == 0 && M_max > 0 && N > 0 && G > 0) return FP8FG_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(c) || !aligned16(masked_m))
         return FP8FG_ERR_ALIGN;
     if (!valid_out(out_dtype)) return FP8FG_ERR_UNSUPPORTED;
     if (M_max > kMaxDim || N > kMaxDim || K > kMaxDim || G > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
-    const int64_t tiles_per_group = ((M_max + 127) / 128) * (N / 128);
+    const int64_t tiles_per_group = ((M_max + 127) / 128) * ((N + 127) / 128);
     if (tiles_per_group > 0 && G > kMaxDim / tiles_per_group) return FP8FG_ERR_UNSUPPORTED;
     if (G == 0 || M_max == 0 || N == 0) return FP8FG_OK;
     fp8fg::GemmArgs args{a, sa, b, sb, c, masked_m, M_max, N, K, G};

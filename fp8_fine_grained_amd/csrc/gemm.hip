@@ -169,7 +169,7 @@ template <class C, int MODE>
 __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile) {
     constexpr int BM = C::BM, BN = C::BN;
     Tile t;
-    const int n_tiles = int(args.N / BN);
+    const int n_tiles = int((args.N + BN - 1) / BN);   // a last partial n-tile when N % BN != 0
     const int64_t kbs = (args.K + BK - 1) / BK;
     t.bn = int(tile % n_tiles);
     tile /= n_tiles;
@@ -222,7 +222,7 @@ __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile) {
     if (t.m0 >= t.rows_valid) t.live = false;
     if (MODE != int(GemmMode::Dense)) {
         t.B += g * args.N * args.K;
-        t.SB += g * (args.N / 128) * kbs;        // 128x128 scales [G][N/128][K/128]
+        t.SB += g * ((args.N + 127) / 128) * kbs;   // 128x128 scales [G][ceil(N/128)][ceil(K/128)]
     }
     return t;
 }
@@ -300,7 +300,8 @@ __device__ __forceinline__ Copier<C> make_copier(const Tile& t, int wave, int la
     for (int i = 0; i < C::B_PER_WAVE; ++i) {
         const int r0 = (wave * C::B_PER_WAVE + i) * 8, r = r0 + sub;
         const int chunk = slot ^ ((r >> 1) & 7);
-        c.b_row[i] = t.B + (n0 + r) * K;
+        const int64_t brow = n0 + r < N ? n0 + r : N - 1;       // clamp: loaded, never stored
+        c.b_row[i] = t.B + brow * K;
         c.b_c16[i] = chunk * 16;
         c.b_lds[i] = int(offsetof(S, b)) + r0 * BK;
     }
@@ -315,7 +316,8 @@ __device__ __forceinline__ Copier<C> make_copier(const Tile& t, int wave, int la
     } else if (wave < a_waves + b_waves) {
         const int j = wave - a_waves;
         if (BSCALE_1x128) {
-            c.s_src = t.SB + n0 + j * 64 + lane;
+            const int64_t col = n0 + j * 64 + lane;
+            c.s_src = t.SB + (col < N ? col : N - 1);
             c.s_stride = N;
         } else {
             c.s_src = t.SB + (n0 / 128 + j) * ((K + BK - 1) / BK);
@@ -542,6 +544,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
         for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                // a run of four columns starts on a multiple of 4 and N % 16 == 0:
+                // the run lies wholly before N or wholly after it
+                if (n0 + n_lane + ni * 32 + 8 * j >= N) continue;
                 const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
                 const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
                                   acc[mi][ni][4 * j + 3]};
@@ -1263,7 +1268,7 @@ const KernelEntry kWideKernels[] = {FP8FG_WIDE_KERNELS(FP8FG_WIDE_ENTRY)};
 
 template <class C>
 int64_t tile_count(GemmMode mode, const GemmArgs& args) {
-    const int64_t n_tiles = args.N / C::BN;
+    const int64_t n_tiles = (args.N + C::BN - 1) / C::BN;
     if (mode == GemmMode::Masked) return args.G * ((args.M + C::BM - 1) / C::BM) * n_tiles;
     if (mode == GemmMode::Contig) return (args.M / C::BM + args.G) * n_tiles;
     return ((args.M + C::BM - 1) / C::BM) * n_tiles;

@@ -285,6 +285,7 @@ __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64
     const int64_t nb = blockIdx.y, kb = blockIdx.x;
     const int c4 = (t & 31) * 4;
     const int r0 = (t >> 5) * 16;
+    const int64_t nbs = (N + kBlock - 1) / kBlock;    // N % 16 == 0: a last partial block of N % 128 rows
     const T* wb = w + nb * kBlock * K + kb * kBlock + c4;
     const bool cvalid = kb * kBlock + c4 < K;     // K % 16 == 0: a last partial block of K % 128 columns
     const int64_t kbs = (K + kBlock - 1) / kBlock;
@@ -292,7 +293,7 @@ __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        v[i] = cvalid ? load4(wb + int64_t(r0 + i) * K) : v4f{0.f, 0.f, 0.f, 0.f};
+        v[i] = cvalid && nb * kBlock + r0 + i < N ? load4(wb + int64_t(r0 + i) * K) : v4f{0.f, 0.f, 0.f, 0.f};
         amax = fmaxf(amax, abs_max4(v[i]));
     }
     amax = wave_max(amax);
@@ -305,7 +306,8 @@ __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int64_t row = nb * kBlock + r0 + i;
-            if (cvalid) *reinterpret_cast<uint32_t*>(q + row * K + kb * kBlock + c4) = encode4(v[i], sc, rc);
+            if (cvalid && row < N)
+                *reinterpret_cast<uint32_t*>(q + row * K + kb * kBlock + c4) = encode4(v[i], sc, rc);
         }
         if (t == 0) s[nb * kbs + kb] = sc;
         return;
@@ -325,10 +327,10 @@ __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64
     for (int i = 0; i < 4; ++i) {
         const int piece = t + 256 * i;          // 1024 pieces of 16 B
         const int kr = piece >> 3, off = (piece & 7) * 16;
-        if (kb * kBlock + kr < K)
+        if (kb * kBlock + kr < K && nb * kBlock + off < N)
             st<u32x4>(q + (kb * kBlock + kr) * N + nb * kBlock + off, ld<u32x4>(&qt[qt_off(kr, off)]));
     }
-    if (t == 0) s[kb * (N / kBlock) + nb] = sc;
+    if (t == 0) s[kb * nbs + nb] = sc;
 }
 
 template <int U>
@@ -461,7 +463,7 @@ hipError_t launch_requant_act_tokens(const uint8_t* qr, const float* sr, int64_t
 
 hipError_t launch_quant_weight(const void* w, int bf16, int64_t N, int64_t K, int transpose_out, uint8_t* q,
                                float* s, hipStream_t stream) {
-    const dim3 grid(unsigned((K + kBlock - 1) / kBlock), unsigned(N / kBlock));
+    const dim3 grid(unsigned((K + kBlock - 1) / kBlock), unsigned((N + kBlock - 1) / kBlock));
     if (bf16)
         hipLaunchKernelGGL(quant_weight_bf16, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(w), N, K,
                            transpose_out, q, s);

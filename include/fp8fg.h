@@ -39,8 +39,9 @@
  *     token-wise layout) need only be a multiple of 16: the last group then
  *     holds fewer than 128 elements and is quantized as that group padded
  *     with zeros (its max-abs runs over the elements that exist).  Every
- *     count "K/128" in this header means ceil(K/128).  N stays a multiple of
- *     128.
+ *     count "K/128" in this header means ceil(K/128).  Likewise N, the
+ *     output channels (rows of B), need only be a multiple of 16 where stated:
+ *     "N/128" then means ceil(N/128).
  *   - GEMM: C[M][N] = A[M][K] . B[N][K]^T, both operands K-major (a Linear
  *     layer y = x . W^T with W [out][in]).  C is the sum over k of
  *     decode(a) * sA * decode(b) * sB, the scales of each 128-wide K-block
@@ -103,7 +104,8 @@ int fp8_quant_act_1x128(const float* x, int64_t M, int64_t K, int transpose_out,
  * transpose_out = 1: q u8 [K][N] = the codes of w, transposed, with
  *     s f32 [K/128][N/128]: the B operand of the Dgrad GEMM.  Square blocks
  *     make this identical to quantizing w^T.
- * Requires N % 128 == 0 and K % 16 == 0; N * K < 2^40.
+ * Requires N % 16 == 0 and K % 16 == 0 (partial blocks at either end);
+ * N * K < 2^40.
  */
 int fp8_quant_weight_128x128(const float* w, int64_t N, int64_t K, int transpose_out,
                              uint8_t* q, float* s, void* stream);
@@ -169,7 +171,7 @@ int fp8_gemm_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uin
  * a: u8 [M][K] with sa f32 [K/128][M] (1x128 along K).
  * b: u8 [N][K] with sb laid out per bscale_kind (fp8fg_bscale).
  * c: [M][N], BF16 (uint16 bit patterns) or FP32 per out_dtype (fp8fg_out).
- * Requires M >= 0 (any value, ragged tails allowed), N % 128 == 0,
+ * Requires M >= 0 (any value, ragged tails allowed), N % 16 == 0,
  * K % 16 == 0 (a last partial K-block is allowed), K > 0 when M*N > 0;
  * M, N, K < 2^31.
  */
@@ -205,7 +207,7 @@ int fp8_gemm_blockscaled_fp8out(const uint8_t* a, const float* sa, const uint8_t
  * a: u8 [M_total][K], sa f32 [K/128][M_total];
  * b: u8 [G][N][K], sb f32 [G][N/128][K/128] (128x128 blocks per expert);
  * c: [M_total][N] BF16 or FP32.
- * Requires M_total % 128 == 0, N % 128 == 0, K % 16 == 0, K > 0, G >= 0.
+ * Requires M_total % 128 == 0, N % 16 == 0, K % 16 == 0, K > 0, G >= 0.
  */
 int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                                 const int32_t* group_offsets, int64_t G, int64_t M_total,
@@ -220,7 +222,7 @@ int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t
  * a: u8 [G][M_max][K], sa f32 [G][K/128][M_max];
  * b: u8 [G][N][K], sb f32 [G][N/128][K/128];
  * c: [G][M_max][N] BF16 or FP32.
- * Requires M_max >= 0, N % 128 == 0, K % 16 == 0, K > 0, G >= 0.
+ * Requires M_max >= 0, N % 16 == 0, K % 16 == 0, K > 0, G >= 0.
  */
 int fp8_grouped_gemm_masked(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                             const int32_t* masked_m, int64_t G, int64_t M_max,

@@ -53,7 +53,7 @@ def test_quant_argument_errors():
     assert q(P, 128, 0, 1, P, P2, NUL) == OK
     w = lib.fp8_quant_weight_128x128
     assert w(P, 128, 72, 0, P, P2, NUL) == ESHAPE          # K % 16
-    assert w(P, 64, 128, 0, P, P2, NUL) == ESHAPE
+    assert w(P, 72, 128, 0, P, P2, NUL) == ESHAPE          # N % 16
     assert w(P, 128, 128, 0, NUL, P2, NUL) == ENULL
     assert w(P, 128, 128, 0, P, MIS, NUL) == EALIGN
     assert w(P, 0, 128, 1, P, P2, NUL) == OK
@@ -109,7 +109,7 @@ def test_mx_argument_errors():
 def test_gemm_argument_errors():
     g = fp8.load_library().fp8_gemm_blockscaled
     assert g(P, P, P, NUL, 0, P, 0, 1, 128, 128, NUL) == ENULL
-    assert g(P, P, P, P, 0, P, 0, 1, 100, 128, NUL) == ESHAPE     # N % 128
+    assert g(P, P, P, P, 0, P, 0, 1, 100, 128, NUL) == ESHAPE     # N % 16
     assert g(P, P, P, P, 0, P, 0, 1, 128, 100, NUL) == ESHAPE     # K % 16
     assert g(P, P, P, P, 0, P, 0, 1, 128, 0, NUL) == ESHAPE       # empty contraction
     assert g(P, P, MIS, P, 0, P, 0, 1, 128, 128, NUL) == EALIGN

@@ -1,5 +1,5 @@
 """GPU parity with partial groups: the grouped axis (K, or the token axis of
-the token-wise layout) a multiple of 16 but not of 128.  Quantizers bit for
+the token-wise layout) or N a multiple of 16 but not of 128.  Quantizers bit for
 bit against the oracle (which quantizes the zero-padded group); GEMMs within
 the usual bounds, on every kernel family (wide, decode, fold, the FP8-MFMA
 engine, 1x128-scaled B, both grouped layouts)."""
@@ -166,3 +166,84 @@ def test_full_size_mla_like_k():
     check(cg, *gemm.gemm_blockscaled_ref(qa, sa, qb, sb, "128x128", rows=rows), "bf16", "K=576")
     gq, gs = fp8.fp8_quant_act_1x128(dev(a))
     same(gq, gs, qa, sa, "K=576 activations")
+
+
+# ---------------------------------------------------------------------------
+# N (output channels, rows of B) a multiple of 16 but not of 128: partial
+# 128x128 blocks along N, and the fold kernels' last n-tile holds fewer
+# columns (no column past N is written).
+
+@pytest.mark.parametrize("N,K", [(16, 128), (144, 208), (400, 1040)])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_weight_partial_n(N, K, transpose):
+    w = workloads.weights(np.random.default_rng(7 * N + K), N, K)
+    w[N - 1, 0] = -2.0
+    same(*fp8.fp8_quant_weight_128x128(dev(w), transpose_out=transpose),
+         *quant.quant_weight_128x128(w, transpose_out=transpose), f"weight N={N} K={K} T={transpose}")
+    wb, ww = bf16_pair(w)
+    same(*fp8.fp8_quant_weight_128x128_bf16(wb, transpose_out=transpose),
+         *quant.quant_weight_128x128(ww, transpose_out=transpose), f"bf16 weight N={N} K={K} T={transpose}")
+
+
+@pytest.mark.parametrize("M,N,K", [(100, 208, 256), (257, 400, 1040), (64, 16, 128)])
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_dense_partial_n(M, N, K, out):
+    rng = np.random.default_rng(M + 3 * N + K)
+    qa, sa = quant.quant_act_1x128(workloads.activations(rng, M, K, 0.01, 50.0))
+    qb, sb = quant.quant_weight_128x128(workloads.weights(rng, N, K))
+    c = torch.full((M + 1, N), 9.0, dtype=OUT[out], device=DEV)        # one guard row after C
+    fp8.fp8_gemm_blockscaled(dev(qa), dev(sa), dev(qb), dev(sb), fp8.BSCALE_128x128, OUT[out], out=c[:M])
+    cg = host64(c)
+    check(cg[:M], *gemm.gemm_blockscaled_ref(qa, sa, qb, sb, "128x128"), out, f"dense N={N} {M}x{N}x{K}")
+    assert np.all(cg[M] == 9.0)
+
+
+def test_wgrad_partial_n_and_tokens():
+    """1x128-scaled B with 144 output columns (in-features) and 208 tokens."""
+    rng = np.random.default_rng(144)
+    T, OUTF, INF = 208, 256, 144
+    dy = workloads.activations(rng, T, OUTF, 0.0, 1.0, 1e-3)
+    x = workloads.activations(rng, T, INF, 0.01, 50.0)
+    qa, sa = quant.quant_act_1x128_tokenwise(dy)
+    qb, sb = quant.quant_act_1x128_tokenwise(x)
+    c = fp8.fp8_gemm_blockscaled(dev(qa), dev(sa), dev(qb), dev(sb), fp8.BSCALE_1x128, torch.float32)
+    check(host64(c), *gemm.gemm_blockscaled_ref(qa, sa, qb, sb, "1x128"), "fp32", "wgrad N=144")
+
+
+def test_fp8mfma_engine_partial_n(monkeypatch):
+    monkeypatch.setenv("FP8FG_GEMM_ENGINE", "fp8mfma")
+    rng = np.random.default_rng(88)
+    M, N, K = 130, 176, 256
+    qa, sa = quant.quant_act_1x128(workloads.activations(rng, M, K, 0.01, 50.0))
+    qb, sb = quant.quant_weight_128x128(workloads.weights(rng, N, K))
+    c = fp8.fp8_gemm_blockscaled(dev(qa), dev(sa), dev(qb), dev(sb), fp8.BSCALE_128x128, torch.float32)
+    check(host64(c), *gemm.gemm_blockscaled_ref(qa, sa, qb, sb, "128x128"), "fp32", "fp8mfma N=176",
+          u=2.0 ** -9)
+
+
+def test_grouped_partial_n():
+    rng = np.random.default_rng(208)
+    G, N, K = 3, 208, 256
+    counts = np.array([256, 128, 0])
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    qa, sa = quant.quant_act_1x128(workloads.activations(rng, int(off[-1]), K, 0.01, 50.0))
+    qbs = [quant.quant_weight_128x128(workloads.weights(rng, N, K)) for _ in range(G)]
+    qb = np.stack([q for q, _ in qbs])
+    sb = np.stack([s for _, s in qbs])
+    c = fp8.fp8_grouped_gemm_contiguous(dev(qa), dev(sa), dev(qb), dev(sb), dev(off), torch.float32)
+    rows, cr, sr = gemm.grouped_contiguous_ref(qa, sa, qb, sb, off)
+    check(host64(c)[rows], cr, sr, "fp32", "contig N=208")
+    for M_max, mm in ((128, [3, 128, 64]), (256, [256, 17, 0])):
+        am = workloads.activations(rng, G * M_max, K, 0.01, 50.0).reshape(G, M_max, K)
+        qs = [quant.quant_act_1x128(am[g]) for g in range(G)]
+        qam = np.stack([q for q, _ in qs])
+        sam = np.stack([s for _, s in qs])
+        out = torch.full((G, M_max, N), 7.0, dtype=torch.float32, device=DEV)
+        fp8.fp8_grouped_gemm_masked(dev(qam), dev(sam), dev(qb), dev(sb), dev(np.array(mm, np.int32)),
+                                    torch.float32, out=out)
+        o = host64(out)
+        for g in range(G):
+            if mm[g]:
+                cr, sr = gemm.gemm_blockscaled_ref(qam[g][:mm[g]], sam[g][:, :mm[g]], qb[g], sb[g], "128x128")
+                check(o[g, :mm[g]], cr, sr, "fp32", f"masked N=208 M_max={M_max} g={g}")
+            assert np.all(o[g, mm[g]:] == 7.0)
