@@ -150,3 +150,33 @@ def test_python_binding_refuses_cpu_tensors():
         fp8.fp8_quant_act_1x128(torch.zeros(4, 128))
     with pytest.raises(ValueError):
         fp8.fp8_quant_act_1x128_bf16(torch.zeros(4, 128, dtype=torch.bfloat16))
+
+
+def test_plain_c_program_links_and_runs(tmp_path):
+    """The header is valid C99 and a C program links libfp8fg.so directly:
+    it reads the ABI version and gets host-side argument errors (no GPU work)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use_fp8fg.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include "fp8fg.h"
+int main(void) {
+    int v = fp8fg_abi_version();
+    int e1 = fp8_quant_act_1x128((const float*)0, 128, 128, 0, (uint8_t*)0, (float*)0, (void*)0);
+    int e2 = fp8_gemm_blockscaled((const uint8_t*)16, (const float*)16, (const uint8_t*)16, (const float*)16,
+                                  FP8FG_BSCALE_128x128, (void*)16, FP8FG_OUT_BF16, 4, 100, 128, (void*)0);
+    printf("%d %d %d %s\n", v, e1, e2, fp8fg_status_string(e2));
+    return v == FP8FG_ABI_VERSION && e1 == FP8FG_ERR_NULL && e2 == FP8FG_ERR_SHAPE ? 0 : 1;
+}
+""")
+    libdir = os.path.dirname(fp8.LIB_PATH)
+    exe = tmp_path / "use_fp8fg"
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-L", libdir, "-lfp8fg", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert out.stdout.split()[0] == str(fp8.ABI_VERSION)
