@@ -614,7 +614,6 @@ struct WCfg {
     static constexpr int A_PER_WAVE = BM / ROWS_PER_PIECE / NW;
     static constexpr int B_PER_WAVE = BN / ROWS_PER_PIECE / NW;
     static constexpr int A_SCALE_WAVES = BM / 64, B_SCALE_WAVES = BN / 128;
-    static constexpr int LOADS_PER_WAVE = A_PER_WAVE + B_PER_WAVE + 1;
     static_assert(A_PER_WAVE * ROWS_PER_PIECE * NW == BM && B_PER_WAVE * ROWS_PER_PIECE * NW == BN,
                   "whole 1 KB pieces per wave");
     static_assert(A_SCALE_WAVES * 64 == BM && B_SCALE_WAVES * 128 == BN, "scale pieces");
@@ -637,6 +636,9 @@ struct alignas(16) WStage {
     float sb[W::B_SCALE_WAVES * 64];    // 64 copies of each n-block's scale
     float dummy[64];
 };
+
+// how many of the n positions after one of parity e are even
+constexpr int later_even(int n, int e) { return n % 2 == 0 ? n / 2 : (e == 1 ? (n + 1) / 2 : (n - 1) / 2); }
 
 // scale s -> (2^t with t = s's exponent clamped to [-124, 118], the range in
 // which the widening cvt scales every code exactly; s / 2^t), with s == 0
@@ -683,6 +685,7 @@ struct WideBufCopier {
     int a_lds[W::A_PER_WAVE], b_lds[W::B_PER_WAVE], s_lds;
     int a_c16[W::A_PER_WAVE], b_c16[W::B_PER_WAVE];       // the lane's chunk offset within a stage (bytes)
     int64_t K;
+    bool has_scale;            // uniform: this wave copies a scale piece (not the dummy)
 
     // After this wave's loads of half-block h have landed: zero its 16-byte
     // slots past K (a partial last K-block).  Those loads read whatever lies
@@ -698,7 +701,14 @@ struct WideBufCopier {
             if (koff + b_c16[i] >= K) st<u32x4>(stage + b_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
     }
 
-    __device__ __forceinline__ void copy(uint8_t* stage, int h) const {
+    // Half-block h into `stage`, as the pos-th copy of the sequence.  Dense:
+    // every wave issues a scale piece with every half-block (waves without a
+    // scale role load a dummy), so all waves wait alike.  `sparse` (the masked
+    // layout, where the weight stream is the bound): scales change once per
+    // K-block and only its first half reads them, so only the waves with a
+    // scale role load one, with even positions only (h and pos have the same
+    // parity except for the reloads past the end, which are never read).
+    __device__ __forceinline__ void copy(uint8_t* stage, int h, int pos, bool sparse) const {
         const uint32_t koff = uint32_t(h) * W::KS;
 #pragma unroll
         for (int i = 0; i < W::A_PER_WAVE; ++i)
@@ -706,7 +716,9 @@ struct WideBufCopier {
 #pragma unroll
         for (int i = 0; i < W::B_PER_WAVE; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i]), 16, vb[i], koff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs, uint32_t(h >> 1) * s_step, 0, 0);
+        if (!sparse || (has_scale && (pos & 1) == 0))
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs, uint32_t(h >> 1) * s_step,
+                                                     0, 0);
     }
 };
 
@@ -716,6 +728,7 @@ __device__ __forceinline__ WideBufCopier<W> make_wide_buf_copier(const Tile& t, 
     typedef WStage<W> S;
     WideBufCopier<W> c;
     c.K = K;
+    c.has_scale = wave < W::A_SCALE_WAVES + W::B_SCALE_WAVES;
     const int sub = lane >> 2, slot = lane & 3;
     const int64_t tile_rows = t.rows_valid - t.m0 < W::BM ? t.rows_valid - t.m0 : W::BM;   // >= 1
     c.ra = make_rsrc(t.A + t.m0 * K, uint32_t(tile_rows * K));
@@ -881,14 +894,15 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
     const int mlive = left <= 0 ? 0 : (left >= FM * 32 ? FM : int((left + 31) / 32));
     constexpr bool full = FM == 1 || MODE != int(GemmMode::Masked);
     const int r = lane & 31, h = lane >> 5;
-    constexpr int L = W::LOADS_PER_WAVE;
+    constexpr int L = W::A_PER_WAVE + W::B_PER_WAVE;   // data loads per half-block, + a scale piece
+    constexpr bool SPARSE = MODE == int(GemmMode::Masked);
 
     if (tid < 4) st<u32x4>(lds_raw + kZeroLine + tid * 16, u32x4{0u, 0u, 0u, 0u});
     // half-blocks past the end reload the last one (into slots never read
     // again), so every iteration issues the same loads and waits the same
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
-        cp.copy(reinterpret_cast<uint8_t*>(&ring[st]), st < halves ? st : halves - 1);
+        cp.copy(reinterpret_cast<uint8_t*>(&ring[st]), st < halves ? st : halves - 1, st, SPARSE);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the zero line is written before the first barrier
 
     v16f acc[FM][FN];
@@ -912,14 +926,23 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int cur = hb + e;
-            wait_vmcnt<(STAGES - 2) * L>();   // this wave's copy of half-block cur has landed
+            // this wave's copy of half-block cur has landed: only the loads of
+            // the STAGES - 2 later half-blocks may be outstanding
+            if (!SPARSE)
+                wait_vmcnt<(STAGES - 2) * (L + 1)>();
+            else if (!cp.has_scale)
+                wait_vmcnt<(STAGES - 2) * L>();
+            else if (e == 0)
+                wait_vmcnt<(STAGES - 2) * L + later_even(STAGES - 2, 0)>();
+            else
+                wait_vmcnt<(STAGES - 2) * L + later_even(STAGES - 2, 1)>();
             if ((cur + 1) * W::KS > K) {      // partial last K-block (uniform)
                 cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[slot]), cur, lane);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             }
             __builtin_amdgcn_s_barrier();     // ... every wave's; the slot of cur - 1 is free
             const int fill = cur + STAGES - 1;
-            cp.copy(reinterpret_cast<uint8_t*>(&ring[fill_slot]), fill < halves ? fill : halves - 1);
+            cp.copy(reinterpret_cast<uint8_t*>(&ring[fill_slot]), fill < halves ? fill : halves - 1, fill, SPARSE);
             if (mlive > 0) {
                 if (e == 0) {
                     const WideScales<FM> nw = wide_scales<W>(ring[slot], wm, wn, r);
