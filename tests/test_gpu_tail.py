@@ -68,6 +68,8 @@ def test_planned_tail_full_size_matches_full_tiles(monkeypatch, M, N, K):
     w = torch.randn((N, K), generator=g, device=DEV) * 0.02
     qa, sa = fp8.fp8_quant_act_1x128(x)
     qb, sb = fp8.fp8_quant_weight_128x128(w)
-    c = _gemm(monkeypatch, "1", qa, sa, qb, sb, "bf16")
     c0 = _gemm(monkeypatch, "0", qa, sa, qb, sb, "bf16")
-    assert _same_bits(c, c0)
+    # the plan this device makes, and a forced split (tail tiles whatever the
+    # CU count: N = 25 x 256 + 4 x 192)
+    for mode in ("1", "force"):
+        assert _same_bits(_gemm(monkeypatch, mode, qa, sa, qb, sb, "bf16"), c0), mode
