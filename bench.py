@@ -2,15 +2,17 @@
 
 Default workload: the dense Fprop GEMM shaped like a DeepSeek-V3 MoE
 down-projection, M=4096 tokens, K=2048, N=7168, BF16 output.  One step is the
-whole path on one batch: online 1x128 quantization of the fp32 activations,
+whole path on one batch: online 1x128 quantization of the fp32 activations and
 online 128x128 quantization of the fp32 weights (training re-quantizes its
-master weights every step), and the block-scaled FP8 GEMM.  Four independent
+master weights every step), both in one launch (fp8_quant_fprop_operands), and
+the block-scaled FP8 GEMM.  Four independent
 input sets rotate from step to step so that no step finds its inputs in the
 256 MB last-level cache; all inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  `value` = GEMM FLOPs / step time (TFLOPS, whole step).
-A step is three launches on one stream with nothing between them; HIP events
-bracket only the whole timed region.  `kernels_us` holds each kernel's
+A step is two launches on one stream with nothing between them; HIP events
+bracket only the whole timed region.  `step_three_launches_ms` times the same
+step with the two quantizations as separate launches.  `kernels_us` holds each kernel's
 duration alone: the mean of back-to-back launches between two HIP events on
 the bench stream, right after the timed steps, which is what a kernel trace of
 the same command reports per launch.  `roofline` describes the GEMM kernel,
@@ -46,7 +48,9 @@ def parse():
     p.add_argument("--sets", type=int, default=4, help="rotating input sets")
     p.add_argument("--cpu-rows", type=int, default=4096, help="rows of the oracle's timed sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--profile-kernel", choices=["gemm", "quant_act", "quant_weight", "copy"],
+    p.add_argument("--settle-s", type=float, default=0.5,
+                   help="seconds of untimed steps before the warmup steps (clock settling)")
+    p.add_argument("--profile-kernel", choices=["gemm", "quant_act", "quant_weight", "quant_fprop", "copy"],
                    help="counter-collection driver: launch only this kernel `steps` times on the "
                         "dense_fprop inputs (copy: a 1 GiB device-to-device copy, the byte-counter "
                         "calibration); prints no JSON")
@@ -104,10 +108,24 @@ def cpu_baseline(x, w, rows, min_seconds=10.0):
                       f"{dt:.2f} s"}
 
 
-def time_launches(fn, steps, warmup, stream):
+_SETTLED = [False]
+
+
+def time_launches(fn, steps, warmup, stream, settle_s=0.5):
     """Average duration (ms) of fn() from HIP events recorded around each
-    launch on the launch stream."""
+    launch on the launch stream.  The first call of a run first keeps the GPU
+    busy with fn for settle_s seconds, untimed, so the clock has settled."""
     import torch
+    if not _SETTLED[0]:
+        t_end = time.perf_counter() + settle_s
+        n = 0
+        while time.perf_counter() < t_end:
+            fn(n)
+            n += 1
+            if n % 64 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        _SETTLED[0] = True
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
@@ -339,35 +357,56 @@ def main():
                 fp8.fp8_quant_act_1x128(s["x"], q=s["qa"], s=s["sa"])
             elif args.profile_kernel == "quant_weight":
                 fp8.fp8_quant_weight_128x128(s["w"], q=s["qb"], s=s["sb"])
+            elif args.profile_kernel == "quant_fprop":
+                fp8.fp8_quant_fprop_operands(s["x"], s["w"], s["qa"], s["sa"], s["qb"], s["sb"])
             else:
                 dst.copy_(src)
         torch.cuda.synchronize()
         print(f"profiled {args.profile_kernel} x{args.steps}", flush=True)
         return
 
-    # One stream, three launches back to back and nothing between them: an
-    # event or a cross-stream wait costs this stack 5-10 us of idle GPU per use
-    # (seen in the kernel trace), more than overlapping the two quantizations
-    # would save.
+    # One stream, launches back to back and nothing between them: an event or
+    # a cross-stream wait costs this stack 5-10 us of idle GPU per use (seen in
+    # the kernel trace).  The two quantizations share one launch, so their small
+    # grids overlap instead of each ramping up and draining on its own.
     def step(i):
+        s = sets[i % len(sets)]
+        fp8.fp8_quant_fprop_operands(s["x"], s["w"], s["qa"], s["sa"], s["qb"], s["sb"])
+        fp8.fp8_gemm_blockscaled(s["qa"], s["sa"], s["qb"], s["sb"], fp8.BSCALE_128x128, torch.bfloat16, out=s["c"])
+
+    def step_three_launches(i):
         s = sets[i % len(sets)]
         fp8.fp8_quant_act_1x128(s["x"], q=s["qa"], s=s["sa"])
         fp8.fp8_quant_weight_128x128(s["w"], q=s["qb"], s=s["sb"])
         fp8.fp8_gemm_blockscaled(s["qa"], s["sa"], s["qb"], s["sb"], fp8.BSCALE_128x128, torch.bfloat16, out=s["c"])
 
-    for i in range(args.warmup):
+    def timed_steps(fn):
+        for i in range(args.warmup):
+            fn(i)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
+
+    # Untimed settling before the warmup steps: the GPU clock takes a few
+    # hundred milliseconds of load to reach its steady level, and a timed loop
+    # started sooner runs 10-20% slow (seen as a slow first repetition of
+    # otherwise identical loops).
+    t_end = time.perf_counter() + args.settle_s
+    i = 0
+    while time.perf_counter() < t_end:
         step(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
+    ms_step = timed_steps(step)
+    ms_step3 = timed_steps(step_three_launches)
 
     def back_to_back(launch):
         # one kernel alone, `steps` launches between two events on the bench
@@ -387,6 +426,7 @@ def main():
         return back_to_back(lambda s: fp8.fp8_gemm_blockscaled(s["qa"], s["sa"], s["qb"], s["sb"], fp8.BSCALE_128x128,
                                                                torch.bfloat16, out=s["c"]))
 
+    t_fprop = back_to_back(lambda s: fp8.fp8_quant_fprop_operands(s["x"], s["w"], s["qa"], s["sa"], s["qb"], s["sb"]))
     t_act = back_to_back(lambda s: fp8.fp8_quant_act_1x128(s["x"], q=s["qa"], s=s["sa"]))
     t_w = back_to_back(lambda s: fp8.fp8_quant_weight_128x128(s["w"], q=s["qb"], s=s["sb"]))
     t_gemm = gemm_back_to_back()
@@ -418,12 +458,16 @@ def main():
         "dtype": "fp8_e4m3",
         "data": "synthetic (seeded: activations N(0,1) with 0.1% outlier channels x100, weights N(0,0.02))",
         "config": {"workload": "dense_fprop: M=4096 N=7168 K=2048, 1x128 activation / 128x128 weight scales, "
-                               "BF16 out; step = quant_act_1x128 + quant_weight_128x128 + gemm_blockscaled",
+                               "BF16 out; step = quant_fprop_operands (1x128 activation + 128x128 weight "
+                               "quantization, one launch) + gemm_blockscaled",
                    "M": M, "N": N, "K": K, "rotating_input_sets": args.sets},
         "pct_of_fp8_peak_step": round(100 * value / PEAK_FP8_TFLOPS, 2),
-        "kernels_us": {"quant_act_1x128": round(t_act * 1e3, 2), "quant_weight_128x128": round(t_w * 1e3, 2),
+        "step_three_launches_ms": round(ms_step3, 5),
+        "kernels_us": {"quant_fprop_operands": round(t_fprop * 1e3, 2),
+                       "quant_act_1x128": round(t_act * 1e3, 2), "quant_weight_128x128": round(t_w * 1e3, 2),
                        "gemm_blockscaled": round(t_gemm * 1e3, 2)},
-        "quant_gbs": {"act": round(act_bytes / (t_act * 1e-3) / 1e9, 1),
+        "quant_gbs": {"fprop_operands": round((act_bytes + w_bytes) / (t_fprop * 1e-3) / 1e9, 1),
+                      "act": round(act_bytes / (t_act * 1e-3) / 1e9, 1),
                       "weight": round(w_bytes / (t_w * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),

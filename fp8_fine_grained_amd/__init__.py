@@ -22,13 +22,13 @@ BSCALE_1x128 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
            "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
            "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16", "fp8_requant_act_tokenwise",
-           "fp8_quant_mx_1x32", "fp8_gemm_mx", "fp8_gemm_blockscaled_fp8out",
+           "fp8_quant_mx_1x32", "fp8_gemm_mx", "fp8_gemm_blockscaled_fp8out", "fp8_quant_fprop_operands",
            "fp8fg_status_string", "fp8fg_abi_version")
-_COMPUTE = EXPORTS[:11]
+_COMPUTE = EXPORTS[:12]
 
 
 class Fp8fgError(RuntimeError):
@@ -61,6 +61,7 @@ def load_library(path=LIB_PATH):
     lib.fp8_quant_mx_1x32.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.fp8_gemm_mx.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     lib.fp8_gemm_blockscaled_fp8out.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.fp8_quant_fprop_operands.argtypes = [vp, i32, i64, vp, i32, i64, i64, vp, vp, vp, vp, vp]
     for name in _COMPUTE:
         getattr(lib, name).restype = ctypes.c_int
     lib.fp8fg_status_string.argtypes = [ctypes.c_int]
@@ -159,6 +160,31 @@ def fp8_quant_weight_128x128(w, transpose_out=False, q=None, s=None):
 def fp8_quant_weight_128x128_bf16(w, transpose_out=False, q=None, s=None):
     """fp8_quant_weight_128x128 for w bf16 [N][K] (quantizes the exactly widened values)."""
     return _quant_weight("fp8_quant_weight_128x128_bf16", w, torch.bfloat16, transpose_out, q, s)
+
+
+def fp8_quant_fprop_operands(x, w, qa=None, sa=None, qb=None, sb=None):
+    """Both Fprop operands in one launch: x f32 or bf16 [M][K], w f32 or bf16
+    [N][K] -> (qa u8 [M][K], sa f32 [K/128][M], qb u8 [N][K], sb f32
+    [N/128][K/128]), exactly fp8_quant_act_1x128(x) and
+    fp8_quant_weight_128x128(w) (or their bf16 forms)."""
+    M, K = x.shape
+    N = w.shape[0]
+    if x.dtype not in (torch.float32, torch.bfloat16) or w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x and w must be float32 or bfloat16")
+    _need(x, x.dtype, (M, K), "x")
+    _need(w, w.dtype, (N, K), "w")
+    qa = _empty((M, K), torch.uint8, x) if qa is None else qa
+    sa = _empty((_nb(K), M), torch.float32, x) if sa is None else sa
+    qb = _empty((N, K), torch.uint8, w) if qb is None else qb
+    sb = _empty((_nb(N), _nb(K)), torch.float32, w) if sb is None else sb
+    _need(qa, torch.uint8, (M, K), "qa")
+    _need(sa, torch.float32, (_nb(K), M), "sa")
+    _need(qb, torch.uint8, (N, K), "qb")
+    _need(sb, torch.float32, (_nb(N), _nb(K)), "sb")
+    _check("fp8_quant_fprop_operands", load_library().fp8_quant_fprop_operands(
+        _ptr(x), int(x.dtype == torch.bfloat16), M, _ptr(w), int(w.dtype == torch.bfloat16), N, K,
+        _ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), _stream(x)))
+    return qa, sa, qb, sb
 
 
 def fp8_requant_act_tokenwise(q, s, qt=None, st=None):

@@ -41,7 +41,7 @@ const char* fp8fg_status_string(int status) {
 // the quantizers' checks, shared by the fp32 and bf16 entry points
 static int quant_act(const void* x, int bf16, int64_t M, int64_t K, int transpose_out, uint8_t* q, float* s,
                      void* stream) {
-    if (!x || !q || !s) return FP8FG_ERR_NULL;
+    if (M > 0 && K > 0 && (!x || !q || !s)) return FP8FG_ERR_NULL;   // empty arrays may be NULL
     if (M < 0 || K < 0) return FP8FG_ERR_SHAPE;
     if (transpose_out != 0 && transpose_out != 1) return FP8FG_ERR_UNSUPPORTED;
     // the grouped axis: a multiple of 16 (a last partial group is allowed)
@@ -56,7 +56,7 @@ static int quant_act(const void* x, int bf16, int64_t M, int64_t K, int transpos
 
 static int quant_weight(const void* w, int bf16, int64_t N, int64_t K, int transpose_out, uint8_t* q, float* s,
                         void* stream) {
-    if (!w || !q || !s) return FP8FG_ERR_NULL;
+    if (N > 0 && K > 0 && (!w || !q || !s)) return FP8FG_ERR_NULL;   // empty arrays may be NULL
     if (N < 0 || K < 0 || N % 16 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
     if (transpose_out != 0 && transpose_out != 1) return FP8FG_ERR_UNSUPPORTED;
     if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return FP8FG_ERR_ALIGN;
@@ -85,6 +85,25 @@ int fp8_quant_weight_128x128(const float* w, int64_t N, int64_t K, int transpose
 int fp8_quant_weight_128x128_bf16(const uint16_t* w, int64_t N, int64_t K, int transpose_out, uint8_t* q, float* s,
                                   void* stream) {
     return quant_weight(w, 1, N, K, transpose_out, q, s, stream);
+}
+
+int fp8_quant_fprop_operands(const void* x, int x_bf16, int64_t M, const void* w, int w_bf16, int64_t N, int64_t K,
+                             uint8_t* qa, float* sa, uint8_t* qb, float* sb, void* stream) {
+    // an operand with no elements may come with NULL pointers (never touched)
+    if (M > 0 && K > 0 && (!x || !qa || !sa)) return FP8FG_ERR_NULL;
+    if (N > 0 && K > 0 && (!w || !qb || !sb)) return FP8FG_ERR_NULL;
+    if (M < 0 || N < 0 || K < 0 || K % 16 != 0 || N % 16 != 0) return FP8FG_ERR_SHAPE;
+    if ((x_bf16 != 0 && x_bf16 != 1) || (w_bf16 != 0 && w_bf16 != 1)) return FP8FG_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(qa) || !aligned16(sa) || !aligned16(qb) || !aligned16(sb))
+        return FP8FG_ERR_ALIGN;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim || (M > 0 && K > kMaxElems / M) || (N > 0 && K > kMaxElems / N))
+        return FP8FG_ERR_UNSUPPORTED;
+    // one 1-D grid: weight blocks plus rowwise workgroups (at most 65535 row groups)
+    const int64_t kbs = (K + 127) / 128;
+    if (kbs * ((N + 127) / 128) + ((kbs + 3) / 4) * 65535 > 0x7FFFFFFF) return FP8FG_ERR_UNSUPPORTED;
+    if (K == 0 || (M == 0 && N == 0)) return FP8FG_OK;
+    return hip_status(fp8fg::launch_quant_fprop(x, x_bf16, M, w, w_bf16, N, K, qa, sa, qb, sb,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int fp8_requant_act_tokenwise(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt, float* st,

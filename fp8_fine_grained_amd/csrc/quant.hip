@@ -27,11 +27,12 @@ namespace fp8fg {
 // s[kb][m].
 template <int U, class T>
 __device__ __forceinline__ void quant_act_rows_body(const T* __restrict__ x, int64_t M, int64_t K,
-                                                    uint8_t* __restrict__ q, float* __restrict__ s) {
+                                                    uint8_t* __restrict__ q, float* __restrict__ s, int64_t bx,
+                                                    int64_t by, int64_t gy) {
     const int lane = threadIdx.x & 31;
     const int64_t kbs = (K + kBlock - 1) / kBlock;     // a last partial group holds K % 128 elements
-    const int64_t kb0 = int64_t(blockIdx.x) * U;
-    for (int64_t m = int64_t(blockIdx.y) * 8 + (threadIdx.x >> 5); m < M; m += int64_t(gridDim.y) * 8) {
+    const int64_t kb0 = bx * U;
+    for (int64_t m = by * 8 + (threadIdx.x >> 5); m < M; m += gy * 8) {
         const T* xr = x + m * K + kb0 * kBlock + lane * 4;
         uint8_t* qr = q + m * K + kb0 * kBlock + lane * 4;
         v4f v[U];
@@ -67,11 +68,12 @@ __device__ __forceinline__ v4f widen_bf16x4(uint32_t w0, uint32_t w1) {
 
 template <int U>
 __device__ __forceinline__ void quant_act_rows_bf16_body(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                         uint8_t* __restrict__ q, float* __restrict__ s) {
+                                                         uint8_t* __restrict__ q, float* __restrict__ s, int64_t bx,
+                                                         int64_t by, int64_t gy) {
     const int lane = threadIdx.x & 15;
     const int64_t kbs = (K + kBlock - 1) / kBlock;     // a last partial group holds K % 128 elements
-    const int64_t kb0 = int64_t(blockIdx.x) * U;
-    for (int64_t m = int64_t(blockIdx.y) * 16 + (threadIdx.x >> 4); m < M; m += int64_t(gridDim.y) * 16) {
+    const int64_t kb0 = bx * U;
+    for (int64_t m = by * 16 + (threadIdx.x >> 4); m < M; m += gy * 16) {
         const uint16_t* xr = x + m * K + kb0 * kBlock + lane * 8;
         uint8_t* qr = q + m * K + kb0 * kBlock + lane * 8;
         u32x4 v[U];
@@ -276,13 +278,14 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&in)[4], uint32_t (
     out[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
 }
 
+// the 128x128 block (nb, kb)
 template <class T>
 __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64_t N, int64_t K, int transpose_out,
-                                                  uint8_t* __restrict__ q, float* __restrict__ s) {
+                                                  uint8_t* __restrict__ q, float* __restrict__ s, int64_t kb,
+                                                  int64_t nb) {
     __shared__ float red[4];
     __shared__ __align__(16) uint8_t qt[kBlock * (kBlock + 16)];
     const int t = threadIdx.x;
-    const int64_t nb = blockIdx.y, kb = blockIdx.x;
     const int c4 = (t & 31) * 4;
     const int r0 = (t >> 5) * 16;
     const int64_t nbs = (N + kBlock - 1) / kBlock;    // N % 16 == 0: a last partial block of N % 128 rows
@@ -333,14 +336,25 @@ __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64
     if (t == 0) s[kb * nbs + nb] = sc;
 }
 
+// workgroup (bx, by) of a grid with gy row groups
 template <int U>
-__device__ __forceinline__ void quant_act_rows_dispatch(const float* x, int64_t M, int64_t K, uint8_t* q, float* s) {
-    quant_act_rows_body<U>(x, M, K, q, s);
+__device__ __forceinline__ void quant_act_rows_dispatch(const float* x, int64_t M, int64_t K, uint8_t* q, float* s,
+                                                        int64_t bx, int64_t by, int64_t gy) {
+    quant_act_rows_body<U>(x, M, K, q, s, bx, by, gy);
 }
 template <int U>
 __device__ __forceinline__ void quant_act_rows_dispatch(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
-                                                        float* s) {
-    quant_act_rows_bf16_body<U>(x, M, K, q, s);
+                                                        float* s, int64_t bx, int64_t by, int64_t gy) {
+    quant_act_rows_bf16_body<U>(x, M, K, q, s, bx, by, gy);
+}
+// rowwise workgroup grid of an [M][K] activation: (K-block chunks of U, row groups)
+template <class T>
+inline void act_rows_grid(int64_t M, int64_t K, int64_t& chunks, int64_t& row_groups) {
+    constexpr int U = 4;
+    constexpr int rows_per_group = sizeof(T) == 4 ? 8 : 16;   // half-waves (fp32) or quarter-waves (bf16)
+    chunks = ((K + kBlock - 1) / kBlock + U - 1) / U;
+    row_groups = (M + rows_per_group - 1) / rows_per_group;
+    if (row_groups > 65535) row_groups = 65535;      // the kernel strides over the rest
 }
 
 // ---------------------------------------------------------------------------
@@ -403,7 +417,7 @@ hipError_t launch_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q, uin
     __global__ __launch_bounds__(256) void quant_act_rows_##SUFFIX(const T* __restrict__ x, int64_t M,      \
                                                                    int64_t K, uint8_t* __restrict__ q,     \
                                                                    float* __restrict__ s) {                \
-        quant_act_rows_dispatch<4>(x, M, K, q, s);                                                         \
+        quant_act_rows_dispatch<4>(x, M, K, q, s, blockIdx.x, blockIdx.y, gridDim.y);                      \
     }                                                                                                      \
     __global__ __launch_bounds__(256) void quant_act_tokens_##SUFFIX(const T* __restrict__ x, int64_t M,    \
                                                                      int64_t K, uint8_t* __restrict__ q,   \
@@ -414,11 +428,37 @@ hipError_t launch_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q, uin
                                                                  int64_t K, int transpose_out,             \
                                                                  uint8_t* __restrict__ q,                  \
                                                                  float* __restrict__ s) {                  \
-        quant_weight_body(w, N, K, transpose_out, q, s);                                                   \
+        quant_weight_body(w, N, K, transpose_out, q, s, blockIdx.x, blockIdx.y);                           \
     }
 FP8FG_QUANT_KERNELS(float, f32)
 FP8FG_QUANT_KERNELS(uint16_t, bf16)
 #undef FP8FG_QUANT_KERNELS
+
+// ---------------------------------------------------------------------------
+// Both Fprop operands in one launch: the 128x128 weight blocks (the longer
+// workgroups) first, then the rowwise activation workgroups, each running the
+// body of its own kernel, so every byte is what the two separate launches
+// write.  One launch lets the two small grids overlap instead of each paying
+// its own ramp-up and drain.
+#define FP8FG_FPROP_KERNEL(TX, TW, SUFFIX)                                                                   \
+    __global__ __launch_bounds__(256) void quant_fprop_##SUFFIX(                                             \
+        const TX* __restrict__ x, int64_t M, const TW* __restrict__ w, int64_t N, int64_t K,                 \
+        uint8_t* __restrict__ qa, float* __restrict__ sa, uint8_t* __restrict__ qb, float* __restrict__ sb,  \
+        int64_t act_chunks, int64_t act_groups) {                                                            \
+        const int64_t kbs = (K + kBlock - 1) / kBlock, w_blocks = kbs * ((N + kBlock - 1) / kBlock);         \
+        const int64_t b = blockIdx.x;                                                                        \
+        if (b < w_blocks) {                                                                                  \
+            quant_weight_body(w, N, K, 0, qb, sb, b % kbs, b / kbs);                                         \
+        } else {                                                                                             \
+            const int64_t a = b - w_blocks;                                                                  \
+            quant_act_rows_dispatch<4>(x, M, K, qa, sa, a % act_chunks, a / act_chunks, act_groups);         \
+        }                                                                                                    \
+    }
+FP8FG_FPROP_KERNEL(float, float, f32_f32)
+FP8FG_FPROP_KERNEL(uint16_t, float, bf16_f32)
+FP8FG_FPROP_KERNEL(float, uint16_t, f32_bf16)
+FP8FG_FPROP_KERNEL(uint16_t, uint16_t, bf16_bf16)
+#undef FP8FG_FPROP_KERNEL
 
 // FP8 activation cache -> token-wise Wgrad operand
 __global__ __launch_bounds__(256) void requant_act_tokens(const uint8_t* __restrict__ qr, const float* __restrict__ sr,
@@ -432,11 +472,8 @@ static hipError_t launch_act(const T* x, int64_t M, int64_t K, int transpose_out
                              hipStream_t stream, void (*rows)(const T*, int64_t, int64_t, uint8_t*, float*),
                              void (*tokens)(const T*, int64_t, int64_t, uint8_t*, float*)) {
     if (!transpose_out) {
-        constexpr int U = 4;
-        constexpr int rows_per_group = sizeof(T) == 4 ? 8 : 16;   // half-waves (fp32) or quarter-waves (bf16)
-        const int64_t chunks = ((K + kBlock - 1) / kBlock + U - 1) / U;
-        int64_t row_groups = (M + rows_per_group - 1) / rows_per_group;
-        if (row_groups > 65535) row_groups = 65535;      // the kernel strides over the rest
+        int64_t chunks = 0, row_groups = 0;
+        act_rows_grid<T>(M, K, chunks, row_groups);
         hipLaunchKernelGGL(rows, dim3(unsigned(chunks), unsigned(row_groups)), dim3(256), 0, stream, x, M, K, q, s);
     } else {
         const dim3 grid(unsigned((M + kBlock - 1) / kBlock), unsigned((K + kTokCh - 1) / kTokCh));
@@ -459,6 +496,32 @@ hipError_t launch_requant_act_tokens(const uint8_t* qr, const float* sr, int64_t
     const dim3 grid(unsigned((M + kBlock - 1) / kBlock), unsigned((K + kTokCh - 1) / kTokCh));
     hipLaunchKernelGGL(requant_act_tokens, grid, dim3(256), 0, stream, qr, sr, M, K, q, s);
     return hipGetLastError();
+}
+
+template <class TX, class TW>
+static hipError_t launch_fprop(const TX* x, int64_t M, const TW* w, int64_t N, int64_t K, uint8_t* qa, float* sa,
+                               uint8_t* qb, float* sb, hipStream_t stream,
+                               void (*kern)(const TX*, int64_t, const TW*, int64_t, int64_t, uint8_t*, float*,
+                                            uint8_t*, float*, int64_t, int64_t)) {
+    int64_t chunks = 0, row_groups = 0;
+    act_rows_grid<TX>(M, K, chunks, row_groups);
+    const int64_t w_blocks = ((K + kBlock - 1) / kBlock) * ((N + kBlock - 1) / kBlock);
+    const int64_t blocks = w_blocks + chunks * row_groups;
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), 0, stream, x, M, w, N, K, qa, sa, qb, sb, chunks,
+                       row_groups);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_fprop(const void* x, int x_bf16, int64_t M, const void* w, int w_bf16, int64_t N, int64_t K,
+                              uint8_t* qa, float* sa, uint8_t* qb, float* sb, hipStream_t stream) {
+    const float* xf = static_cast<const float*>(x);
+    const uint16_t* xh = static_cast<const uint16_t*>(x);
+    const float* wf = static_cast<const float*>(w);
+    const uint16_t* wh = static_cast<const uint16_t*>(w);
+    if (!x_bf16 && !w_bf16) return launch_fprop(xf, M, wf, N, K, qa, sa, qb, sb, stream, quant_fprop_f32_f32);
+    if (x_bf16 && !w_bf16) return launch_fprop(xh, M, wf, N, K, qa, sa, qb, sb, stream, quant_fprop_bf16_f32);
+    if (!x_bf16) return launch_fprop(xf, M, wh, N, K, qa, sa, qb, sb, stream, quant_fprop_f32_bf16);
+    return launch_fprop(xh, M, wh, N, K, qa, sa, qb, sb, stream, quant_fprop_bf16_bf16);
 }
 
 hipError_t launch_quant_weight(const void* w, int bf16, int64_t N, int64_t K, int transpose_out, uint8_t* q,

@@ -30,7 +30,8 @@
  *   - Return value: FP8FG_OK, or a negative fp8fg_status.  Argument errors are
  *     detected on the host BEFORE anything is enqueued (no partial work);
  *     FP8FG_ERR_HIP means the kernel launch itself failed.  A zero-sized
- *     problem (M == 0, G == 0, ...) is a successful no-op.
+ *     problem (M == 0, G == 0, ...) is a successful no-op.  The quantizers
+ *     also accept NULL for the pointers of an operand with no elements.
  *   - Scale layouts.  A 1x128-scaled operand of logical shape [R][K] (K = the
  *     axis the 128-element groups run along) stores codes u8 [R][K] row-major
  *     and scales f32 [K/128][R] ("kb-major").  A 128x128-scaled [N][K] operand
@@ -66,7 +67,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 5
+#define FP8FG_ABI_VERSION 6
 
 enum fp8fg_status {
     FP8FG_OK = 0,
@@ -125,6 +126,25 @@ int fp8_quant_act_1x128_bf16(const uint16_t* x, int64_t M, int64_t K, int transp
                              uint8_t* q, float* s, void* stream);
 int fp8_quant_weight_128x128_bf16(const uint16_t* w, int64_t N, int64_t K, int transpose_out,
                                   uint8_t* q, float* s, void* stream);
+
+/*
+ * Both operands of a Linear layer's Fprop GEMM in one launch (both are
+ * quantized online each step: "The Insider Secrets Of Deepseek Discovered",
+ * passages on Figure 7(a) and on online quantization): exactly
+ *   fp8_quant_act_1x128(x, M, K, 0, qa, sa)        (or _bf16 when x_bf16 = 1)
+ *   fp8_quant_weight_128x128(w, N, K, 0, qb, sb)   (or _bf16 when w_bf16 = 1)
+ * byte for byte, with the same layouts (qa u8 [M][K], sa f32 [K/128][M],
+ * qb u8 [N][K], sb f32 [N/128][K/128]).  x / w are f32, or bf16 bit patterns
+ * when x_bf16 / w_bf16 is 1.  The two small grids share one launch, so they
+ * overlap instead of each paying its own ramp-up and drain.  Requires
+ * K % 16 == 0, N % 16 == 0, M, N, K >= 0, M * K < 2^40 and N * K < 2^40;
+ * 16-byte aligned pointers; x_bf16 and w_bf16 in {0, 1}.  M = 0 or N = 0
+ * skips that operand only, as the separate call would, and that operand's
+ * pointers may then be NULL; K = 0, or M = N = 0, is a successful no-op.
+ * Errors as for the separate calls.
+ */
+int fp8_quant_fprop_operands(const void* x, int x_bf16, int64_t M, const void* w, int w_bf16, int64_t N,
+                             int64_t K, uint8_t* qa, float* sa, uint8_t* qb, float* sb, void* stream);
 
 /*
  * FP8 activation cache for backward ("The Insider Secrets Of Deepseek

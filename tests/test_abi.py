@@ -51,12 +51,14 @@ def test_quant_argument_errors():
     assert q(P, 128, 128, 2, P, P2, NUL) == EUNSUP
     assert q(P, 0, 128, 0, P, P2, NUL) == OK                # empty: no launch
     assert q(P, 128, 0, 1, P, P2, NUL) == OK
+    assert q(NUL, 0, 128, 0, NUL, NUL, NUL) == OK          # empty arrays may be NULL
     w = lib.fp8_quant_weight_128x128
     assert w(P, 128, 72, 0, P, P2, NUL) == ESHAPE          # K % 16
     assert w(P, 72, 128, 0, P, P2, NUL) == ESHAPE          # N % 16
     assert w(P, 128, 128, 0, NUL, P2, NUL) == ENULL
     assert w(P, 128, 128, 0, P, MIS, NUL) == EALIGN
     assert w(P, 0, 128, 1, P, P2, NUL) == OK
+    assert w(NUL, 128, 0, 0, NUL, NUL, NUL) == OK
 
 
 def test_bf16_quant_argument_errors():
@@ -74,6 +76,23 @@ def test_bf16_quant_argument_errors():
     assert w(MIS, 128, 128, 0, P, P2, NUL) == EALIGN
     assert w(P, 128, 128, 3, P, P2, NUL) == EUNSUP
     assert w(P, 128, 0, 0, P, P2, NUL) == OK
+
+
+def test_fprop_operands_argument_errors():
+    f = fp8.load_library().fp8_quant_fprop_operands
+    #      x  xb  M    w  wb   N    K   qa  sa  qb  sb
+    assert f(NUL, 0, 128, P, 0, 128, 128, P, P2, P, P2, NUL) == ENULL
+    assert f(P, 0, 128, P, 0, 128, 128, P, P2, P, NUL, NUL) == ENULL
+    assert f(P, 0, 128, P, 0, 128, 100, P, P2, P, P2, NUL) == ESHAPE     # K % 16
+    assert f(P, 0, 128, P, 0, 72, 128, P, P2, P, P2, NUL) == ESHAPE      # N % 16
+    assert f(P, 0, -1, P, 0, 128, 128, P, P2, P, P2, NUL) == ESHAPE
+    assert f(P, 2, 128, P, 0, 128, 128, P, P2, P, P2, NUL) == EUNSUP     # x_bf16 not 0 / 1
+    assert f(P, 0, 128, P, -1, 128, 128, P, P2, P, P2, NUL) == EUNSUP
+    assert f(P, 0, 128, MIS, 0, 128, 128, P, P2, P, P2, NUL) == EALIGN
+    assert f(P, 1, 128, P, 1, 128, 0, P, P2, P, P2, NUL) == OK          # K = 0: no launch
+    assert f(P, 0, 0, P, 1, 0, 128, P, P2, P, P2, NUL) == OK            # M = N = 0: no launch
+    assert f(NUL, 0, 0, NUL, 0, 0, 128, NUL, NUL, NUL, NUL, NUL) == OK  # empty operands may be NULL
+    assert f(NUL, 0, 0, P, 0, 128, 128, NUL, NUL, NUL, P2, NUL) == ENULL  # the weight is not empty
 
 
 def test_requant_argument_errors():

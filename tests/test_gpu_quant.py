@@ -246,3 +246,42 @@ def test_requant_full_size_linear_trio():
     q, s = quant.quant_act_1x128(x)
     qt, st = fp8.fp8_requant_act_tokenwise(dev(q), dev(s))
     assert_same(qt, st, *quant.requant_act_tokenwise(q, s), "requant trio X")
+
+
+# ---------------------------------------------------------------------------
+# Both Fprop operands in one launch: byte for byte the two separate calls, and
+# the oracle's codes and scales.
+def _bf16_bits(a):
+    """float32 array -> the bf16 tensor of its upper halves (exact widening back)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+    return t.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,N,K", [(37, 272, 1040), (256, 512, 384), (1, 16, 16), (0, 144, 256), (96, 0, 256)])
+@pytest.mark.parametrize("xb,wb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_fprop_operands_match_separate_calls_and_oracle(M, N, K, xb, wb):
+    rng = np.random.default_rng(M + 3 * N + 7 * K + 11 * xb + 13 * wb)
+    x = workloads.activations(rng, max(M, 1), K, 0.01, 50.0)[:M]
+    w = workloads.weights(rng, max(N, 1), K)[:N]
+    xt = _bf16_bits(x).to(DEV) if xb else dev(x)
+    wt = _bf16_bits(w).to(DEV) if wb else dev(w)
+    qa, sa, qb, sb = fp8.fp8_quant_fprop_operands(xt, wt)
+    ra = (fp8.fp8_quant_act_1x128_bf16 if xb else fp8.fp8_quant_act_1x128)(xt)
+    rb = (fp8.fp8_quant_weight_128x128_bf16 if wb else fp8.fp8_quant_weight_128x128)(wt)
+    for got, ref, what in ((qa, ra[0], "qa"), (sa, ra[1], "sa"), (qb, rb[0], "qb"), (sb, rb[1], "sb")):
+        g, r = host(got), host(ref)
+        assert np.array_equal(g.view(np.uint8), r.view(np.uint8)), what
+    # the oracle on the values the kernels saw (bf16 inputs widen exactly)
+    xo = xt.float().cpu().numpy()
+    wo = wt.float().cpu().numpy()
+    if M > 0:
+        assert_same(qa, sa, *quant.quant_act_1x128(xo), f"fprop act {M}x{K}")
+    if N > 0:
+        assert_same(qb, sb, *quant.quant_weight_128x128(wo), f"fprop weight {N}x{K}")
+
+
+def test_fprop_operands_full_size_dense_fprop():
+    x, w = workloads.dense_fprop()
+    qa, sa, qb, sb = fp8.fp8_quant_fprop_operands(dev(x), dev(w))
+    assert_same(qa, sa, *quant.quant_act_1x128(x), "fprop act full size")
+    assert_same(qb, sb, *quant.quant_weight_128x128(w), "fprop weight full size")
