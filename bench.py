@@ -108,16 +108,16 @@ def cpu_baseline(x, w, rows, min_seconds=10.0):
                       f"{dt:.2f} s"}
 
 
-_SETTLED = [False]
+_SETTLE = {"done": False, "seconds": 0.5}
 
 
-def time_launches(fn, steps, warmup, stream, settle_s=0.5):
+def time_launches(fn, steps, warmup, stream):
     """Average duration (ms) of fn() from HIP events recorded around each
     launch on the launch stream.  The first call of a run first keeps the GPU
-    busy with fn for settle_s seconds, untimed, so the clock has settled."""
+    busy with fn for --settle-s seconds, untimed, so the clock has settled."""
     import torch
-    if not _SETTLED[0]:
-        t_end = time.perf_counter() + settle_s
+    if not _SETTLE["done"]:
+        t_end = time.perf_counter() + _SETTLE["seconds"]
         n = 0
         while time.perf_counter() < t_end:
             fn(n)
@@ -125,7 +125,7 @@ def time_launches(fn, steps, warmup, stream, settle_s=0.5):
             if n % 64 == 0:
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
-        _SETTLED[0] = True
+        _SETTLE["done"] = True
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
@@ -311,6 +311,7 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
         sys.exit(2)
+    _SETTLE["seconds"] = args.settle_s
     if args.workload != "dense_fprop":
         run_extra(args)
         return
@@ -472,9 +473,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": stored_traffic(),
-                     "kernel": "gemm_wide_o0_dense (dense, 128x128 B scales, BF16 out, 256x256 tiles): FP8 "
-                               "operands widened exactly to BF16 in registers, BF16 MFMA, so its peak is the "
-                               "dense BF16 MFMA peak",
+                     "kernel": "gemm_wmix_o0_dense (dense, 128x128 B scales, BF16 out; on 256 CUs a planned "
+                               "grid of 256 256x256 tiles + 256 256x192 tail tiles, gemm_wide_o0_dense's body "
+                               "for the former): FP8 operands widened exactly to BF16 in registers, BF16 MFMA, "
+                               "so its peak is the dense BF16 MFMA peak",
                      "pct_of_fp8_peak": round(100 * gemm_tflops / PEAK_FP8_TFLOPS, 2),
                      "kernel_us": round(t_gemm * 1e3, 2),
                      "duration_source": "mean of `steps` back-to-back launches on the bench stream between two "
