@@ -641,6 +641,19 @@ struct alignas(16) WStage {
 // how many of the n positions after one of parity e are even
 constexpr int later_even(int n, int e) { return n % 2 == 0 ? n / 2 : (e == 1 ? (n + 1) / 2 : (n - 1) / 2); }
 
+// Sparse copies: wait until at most the loads of the LATER later copies are
+// outstanding -- DATA data loads each, plus a scale piece on the even ones
+// when the wave has a scale role; e = the current copy's parity.
+template <int LATER, int DATA>
+__device__ __forceinline__ void wait_sparse(bool has_scale, int e) {
+    if (!has_scale)
+        wait_vmcnt<LATER * DATA>();
+    else if (e == 0)
+        wait_vmcnt<LATER * DATA + later_even(LATER, 0)>();
+    else
+        wait_vmcnt<LATER * DATA + later_even(LATER, 1)>();
+}
+
 // scale s -> (2^t with t = s's exponent clamped to [-124, 118], the range in
 // which the widening cvt scales every code exactly; s / 2^t), with s == 0
 // giving mantissa part 1 (its rows read the zero line instead).  The mantissa part
@@ -687,6 +700,7 @@ struct WideBufCopier {
     int a_c16[W::A_PER_WAVE], b_c16[W::B_PER_WAVE];       // the lane's chunk offset within a stage (bytes)
     int64_t K;
     bool has_scale;            // uniform: this wave copies a scale piece (not the dummy)
+    bool skip_a;               // uniform: its one A piece holds only rows the compute never reads
 
     // After this wave's loads of half-block h have landed: zero its 16-byte
     // slots past K (a partial last K-block).  Those loads read whatever lies
@@ -709,11 +723,15 @@ struct WideBufCopier {
     // K-block and only its first half reads them, so only the waves with a
     // scale role load one, with even positions only (h and pos have the same
     // parity except for the reloads past the end, which are never read).
+    // Sparse also skips an A piece whose rows lie past every m-tile the tile
+    // computes (decode tiles with at most 32 valid rows).
     __device__ __forceinline__ void copy(uint8_t* stage, int h, int pos, bool sparse) const {
         const uint32_t koff = uint32_t(h) * W::KS;
+        if (!(sparse && skip_a)) {
 #pragma unroll
-        for (int i = 0; i < W::A_PER_WAVE; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + a_lds[i]), 16, va[i], koff, 0, 0);
+            for (int i = 0; i < W::A_PER_WAVE; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + a_lds[i]), 16, va[i], koff, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < W::B_PER_WAVE; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i]), 16, vb[i], koff, 0, 0);
@@ -734,6 +752,9 @@ __device__ __forceinline__ WideBufCopier<W> make_wide_buf_copier(const Tile& t, 
     const int64_t tile_rows = t.rows_valid - t.m0 < W::BM ? t.rows_valid - t.m0 : W::BM;   // >= 1
     c.ra = make_rsrc(t.A + t.m0 * K, uint32_t(tile_rows * K));
     c.rb = make_rsrc(t.B + n0 * K, uint32_t(W::BN * K));
+    // one m-row of waves: the compute reads the first ceil(tile_rows / 32) m-tiles
+    c.skip_a = W::A_PER_WAVE == 1 && W::WAVES_M == 1 &&
+               int64_t(wave) * W::ROWS_PER_PIECE >= (tile_rows + 31) / 32 * 32;
 #pragma unroll
     for (int i = 0; i < W::A_PER_WAVE; ++i) {
         const int r0 = (wave * W::A_PER_WAVE + i) * W::ROWS_PER_PIECE, r = r0 + sub;
@@ -933,14 +954,13 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args, uint8_t* ld
             const int cur = hb + e;
             // this wave's copy of half-block cur has landed: only the loads of
             // the STAGES - 2 later half-blocks may be outstanding
+            // (sparse: per role -- a scale piece or not, the A piece skipped or not)
             if (!SPARSE)
                 wait_vmcnt<(STAGES - 2) * (L + 1)>();
-            else if (!cp.has_scale)
-                wait_vmcnt<(STAGES - 2) * L>();
-            else if (e == 0)
-                wait_vmcnt<(STAGES - 2) * L + later_even(STAGES - 2, 0)>();
+            else if (cp.skip_a)
+                wait_sparse<(STAGES - 2), L - W::A_PER_WAVE>(cp.has_scale, e);
             else
-                wait_vmcnt<(STAGES - 2) * L + later_even(STAGES - 2, 1)>();
+                wait_sparse<(STAGES - 2), L>(cp.has_scale, e);
             if ((cur + 1) * W::KS > K) {      // partial last K-block (uniform)
                 cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[slot]), cur, lane);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
