@@ -278,11 +278,76 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&in)[4], uint32_t (
     out[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
 }
 
-// the 128x128 block (nb, kb)
-template <class T>
-__device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64_t N, int64_t K, int transpose_out,
-                                                  uint8_t* __restrict__ q, float* __restrict__ s, int64_t kb,
-                                                  int64_t nb) {
+// bf16 weights: 16 lanes x 8 elements (one 16-byte load) per 128-column row
+// and 8 consecutive rows per thread, so a load moves as many bytes as the fp32
+// body's; the block's codes, scale and transposed layout are the fp32 body's.
+__device__ __forceinline__ void quant_weight_bf16_body(const uint16_t* __restrict__ w, int64_t N, int64_t K,
+                                                       int transpose_out, uint8_t* __restrict__ q,
+                                                       float* __restrict__ s, int64_t kb, int64_t nb) {
+    __shared__ float red[4];
+    __shared__ __align__(16) uint8_t qt[kBlock * (kBlock + 16)];
+    const int t = threadIdx.x;
+    const int c8 = (t & 15) * 8;
+    const int r8 = (t >> 4) * 8;
+    const int64_t nbs = (N + kBlock - 1) / kBlock;
+    const uint16_t* wb = w + nb * kBlock * K + kb * kBlock + c8;
+    const bool cvalid = kb * kBlock + c8 < K;     // K % 16 == 0: eight columns lie wholly inside or past K
+    const int64_t kbs = (K + kBlock - 1) / kBlock;
+    v4f lo[8], hi[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const u32x4 raw = cvalid && nb * kBlock + r8 + i < N ? ld<u32x4>(wb + int64_t(r8 + i) * K)
+                                                              : u32x4{0u, 0u, 0u, 0u};
+        lo[i] = widen_bf16x4(raw[0], raw[1]);
+        hi[i] = widen_bf16x4(raw[2], raw[3]);
+        amax = fmaxf(amax, fmaxf(abs_max4(lo[i]), abs_max4(hi[i])));
+    }
+    amax = wave_max(amax);
+    if ((t & 63) == 0) red[t >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float sc = amax / 448.0f;
+    const float rc = 1.0f / sc;
+    if (!transpose_out) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t row = nb * kBlock + r8 + i;
+            if (cvalid && row < N)
+                st<u32x2_t>(q + row * K + kb * kBlock + c8, u32x2_t{encode4(lo[i], sc, rc), encode4(hi[i], sc, rc)});
+        }
+        if (t == 0) s[nb * kbs + kb] = sc;
+        return;
+    }
+    // 4x4 groups of codes (rows r8 + 4g .., columns c8 + 4hh ..) turned around
+    // in registers, staged as [column][row]
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            uint32_t in[4], out[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) in[i] = encode4(hh ? hi[4 * g + i] : lo[4 * g + i], sc, rc);
+            transpose4x4(in, out);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st<uint32_t>(&qt[qt_off(c8 + 4 * hh + j, r8 + 4 * g)], out[j]);
+        }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int piece = t + 256 * i;          // 1024 pieces of 16 B
+        const int kr = piece >> 3, off = (piece & 7) * 16;
+        if (kb * kBlock + kr < K && nb * kBlock + off < N)
+            st<u32x4>(q + (kb * kBlock + kr) * N + nb * kBlock + off, ld<u32x4>(&qt[qt_off(kr, off)]));
+    }
+    if (t == 0) s[kb * nbs + nb] = sc;
+}
+
+// fp32 weights: 32 lanes x 4 elements per 128-column row, 16 rows per thread
+__device__ __forceinline__ void quant_weight_f32_body(const float* __restrict__ w, int64_t N, int64_t K,
+                                                      int transpose_out, uint8_t* __restrict__ q,
+                                                      float* __restrict__ s, int64_t kb, int64_t nb) {
+    typedef float T;
     __shared__ float red[4];
     __shared__ __align__(16) uint8_t qt[kBlock * (kBlock + 16)];
     const int t = threadIdx.x;
@@ -334,6 +399,16 @@ __device__ __forceinline__ void quant_weight_body(const T* __restrict__ w, int64
             st<u32x4>(q + (kb * kBlock + kr) * N + nb * kBlock + off, ld<u32x4>(&qt[qt_off(kr, off)]));
     }
     if (t == 0) s[kb * nbs + nb] = sc;
+}
+
+// the 128x128 block (nb, kb)
+__device__ __forceinline__ void quant_weight_body(const float* w, int64_t N, int64_t K, int transpose_out, uint8_t* q,
+                                                  float* s, int64_t kb, int64_t nb) {
+    quant_weight_f32_body(w, N, K, transpose_out, q, s, kb, nb);
+}
+__device__ __forceinline__ void quant_weight_body(const uint16_t* w, int64_t N, int64_t K, int transpose_out,
+                                                  uint8_t* q, float* s, int64_t kb, int64_t nb) {
+    quant_weight_bf16_body(w, N, K, transpose_out, q, s, kb, nb);
 }
 
 // workgroup (bx, by) of a grid with gy row groups
