@@ -26,7 +26,18 @@
 //           and this engine is held to a looser bound.  Chosen with
 //           FP8FG_GEMM_ENGINE=fp8mfma.
 //
-// Work decomposition (both engines).  A 512-thread workgroup computes a
+// Kernels, by what they serve:
+//   gemm_wide_*   exact engine, 128x128-scaled B, N % 256 == 0: dense,
+//                 contiguous and long masked buffers (256 x 256 tiles), and
+//                 decode-sized masked buffers (gemm_wdec_*, 64 x 256 tiles);
+//                 the promotion is folded into the MFMA accumulator (below).
+//   gemm_wmix_*   dense grids planned as 256 x 256 tiles plus 256 x 192 tail
+//                 tiles, so both kinds fill whole rounds of the device's CUs.
+//   gemm_big_* / gemm_dec_*   the fold kernels described next: 1x128-scaled
+//                 B (Wgrad), the fp8mfma engine, and N = 128 mod 256.
+//   gemm_mx_*     the MX variant (E8M0 scales applied inside the MFMA).
+//
+// Fold kernels.  A 512-thread workgroup computes a
 // 256 (m) x 128 (n) tile of C; each of its eight waves (two per SIMD) owns a
 // 64 x 64 sub-tile = 2 x 2 MFMA tiles of 32 x 32.  K-blocks stream through a
 // three-stage ring in LDS filled by direct-to-LDS loads
@@ -592,7 +603,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
 // Stages hold half a K-block (64 K: rows of 64 bytes, four 16-byte chunks,
 // chunk c of row r at slot c ^ ((r >> 2) & 3)); four of them (135 KB) keep
 // three half-blocks in flight.  The scales of K-block kb ride with both of
-// its halves; the first half applies them.  Copies are buffer-to-LDS loads
+// its halves (masked layout: with the first only, on the waves that own a
+// scale piece); the first half applies them.  Copies are buffer-to-LDS loads
 // whose per-lane offsets are fixed for the whole tile, the K position riding
 // in the scalar offset, and each half-block is one straight-line block of
 // fragment reads, cvts and MFMAs.  A row whose A scale (or the block's B

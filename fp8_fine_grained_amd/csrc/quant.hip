@@ -10,7 +10,11 @@
 // which E4M3 code it rounds to and divides only when that cannot be decided,
 // so every byte and scale is reproducible bit for bit.
 //
-// All three kernels are HBM-bound: 4 bytes (fp32 input) or 2 bytes (bf16
+// Kernels: rowwise 1x128 (quant_act_rows_*), token-wise 1x128 with
+// transposed output (quant_act_tokens_*), 128x128 weights (quant_weight_*),
+// both Fprop operands in one launch (quant_fprop_*), the FP8 activation cache
+// to the token-wise layout (requant_act_tokens) and the MX variant
+// (quant_mx_rows).  All are HBM-bound: 4 bytes (fp32 input) or 2 bytes (bf16
 // input, widened exactly) read and 1 byte written per element, plus 4 bytes of
 // scale per group.
 #include "device_common.hpp"
@@ -20,11 +24,11 @@ namespace fp8fg {
 
 // ---------------------------------------------------------------------------
 // 1x128 tiles along K.  A workgroup of eight half-waves (32 lanes x float4
-// each) owns eight rows and U consecutive K-blocks of them: half-wave h takes
-// row blockIdx.y*8 + h (grid-strided over rows) and tiles kb0 .. kb0+U-1 with
-// kb0 = blockIdx.x*U, so U independent 16-byte loads per lane are in flight
-// before the first reduction and no index needs a division.  Scales go to
-// s[kb][m].
+// each) owns eight rows and U consecutive K-blocks of them: workgroup (bx, by)
+// of a grid with gy row groups gives half-wave h row by*8 + h (strided by
+// gy*8 over the rows) and tiles kb0 .. kb0+U-1 with kb0 = bx*U, so U
+// independent 16-byte loads per lane are in flight before the first reduction
+// and no index needs a division.  Scales go to s[kb][m].
 template <int U, class T>
 __device__ __forceinline__ void quant_act_rows_body(const T* __restrict__ x, int64_t M, int64_t K,
                                                     uint8_t* __restrict__ q, float* __restrict__ s, int64_t bx,
