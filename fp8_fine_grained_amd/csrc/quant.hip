@@ -29,14 +29,15 @@ namespace fp8fg {
 // gy*8 over the rows) and tiles kb0 .. kb0+U-1 with kb0 = bx*U, so U
 // independent 16-byte loads per lane are in flight before the first reduction
 // and no index needs a division.  Scales go to s[kb][m].
-template <int U, class T>
+template <int U, class T, int NT = 256>
 __device__ __forceinline__ void quant_act_rows_body(const T* __restrict__ x, int64_t M, int64_t K,
                                                     uint8_t* __restrict__ q, float* __restrict__ s, int64_t bx,
                                                     int64_t by, int64_t gy) {
+    constexpr int RW = NT / 32;                        // rows (half-waves) per workgroup
     const int lane = threadIdx.x & 31;
     const int64_t kbs = (K + kBlock - 1) / kBlock;     // a last partial group holds K % 128 elements
     const int64_t kb0 = bx * U;
-    for (int64_t m = by * 8 + (threadIdx.x >> 5); m < M; m += gy * 8) {
+    for (int64_t m = by * RW + (threadIdx.x >> 5); m < M; m += gy * RW) {
         const T* xr = x + m * K + kb0 * kBlock + lane * 4;
         uint8_t* qr = q + m * K + kb0 * kBlock + lane * 4;
         v4f v[U];
@@ -70,14 +71,15 @@ __device__ __forceinline__ v4f widen_bf16x4(uint32_t w0, uint32_t w1) {
                __builtin_bit_cast(float, w1 << 16), __builtin_bit_cast(float, w1 & 0xFFFF0000u)};
 }
 
-template <int U>
+template <int U, int NT = 256>
 __device__ __forceinline__ void quant_act_rows_bf16_body(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                          uint8_t* __restrict__ q, float* __restrict__ s, int64_t bx,
                                                          int64_t by, int64_t gy) {
+    constexpr int RW = NT / 16;                        // rows (quarter-waves) per workgroup
     const int lane = threadIdx.x & 15;
     const int64_t kbs = (K + kBlock - 1) / kBlock;     // a last partial group holds K % 128 elements
     const int64_t kb0 = bx * U;
-    for (int64_t m = by * 16 + (threadIdx.x >> 4); m < M; m += gy * 16) {
+    for (int64_t m = by * RW + (threadIdx.x >> 4); m < M; m += gy * RW) {
         const uint16_t* xr = x + m * K + kb0 * kBlock + lane * 8;
         uint8_t* qr = q + m * K + kb0 * kBlock + lane * 8;
         u32x4 v[U];
@@ -285,22 +287,25 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&in)[4], uint32_t (
 // bf16 weights: 16 lanes x 8 elements (one 16-byte load) per 128-column row
 // and 8 consecutive rows per thread, so a load moves as many bytes as the fp32
 // body's; the block's codes, scale and transposed layout are the fp32 body's.
+template <int NT = 256>
 __device__ __forceinline__ void quant_weight_bf16_body(const uint16_t* __restrict__ w, int64_t N, int64_t K,
                                                        int transpose_out, uint8_t* __restrict__ q,
                                                        float* __restrict__ s, int64_t kb, int64_t nb) {
-    __shared__ float red[4];
+    constexpr int RPT = 2048 / NT;                 // rows per thread: 8 (256 threads) or 4 (512)
+    constexpr int NWV = NT / 64;
+    __shared__ float red[NWV];
     __shared__ __align__(16) uint8_t qt[kBlock * (kBlock + 16)];
     const int t = threadIdx.x;
     const int c8 = (t & 15) * 8;
-    const int r8 = (t >> 4) * 8;
+    const int r8 = (t >> 4) * RPT;
     const int64_t nbs = (N + kBlock - 1) / kBlock;
     const uint16_t* wb = w + nb * kBlock * K + kb * kBlock + c8;
     const bool cvalid = kb * kBlock + c8 < K;     // K % 16 == 0: eight columns lie wholly inside or past K
     const int64_t kbs = (K + kBlock - 1) / kBlock;
-    v4f lo[8], hi[8];
+    v4f lo[RPT], hi[RPT];
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < RPT; ++i) {
         const u32x4 raw = cvalid && nb * kBlock + r8 + i < N ? ld<u32x4>(wb + int64_t(r8 + i) * K)
                                                               : u32x4{0u, 0u, 0u, 0u};
         lo[i] = widen_bf16x4(raw[0], raw[1]);
@@ -310,12 +315,14 @@ __device__ __forceinline__ void quant_weight_bf16_body(const uint16_t* __restric
     amax = wave_max(amax);
     if ((t & 63) == 0) red[t >> 6] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    amax = red[0];
+#pragma unroll
+    for (int i = 1; i < NWV; ++i) amax = fmaxf(amax, red[i]);
     const float sc = amax / 448.0f;
     const float rc = 1.0f / sc;
     if (!transpose_out) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < RPT; ++i) {
             const int64_t row = nb * kBlock + r8 + i;
             if (cvalid && row < N)
                 st<u32x2_t>(q + row * K + kb * kBlock + c8, u32x2_t{encode4(lo[i], sc, rc), encode4(hi[i], sc, rc)});
@@ -326,7 +333,7 @@ __device__ __forceinline__ void quant_weight_bf16_body(const uint16_t* __restric
     // 4x4 groups of codes (rows r8 + 4g .., columns c8 + 4hh ..) turned around
     // in registers, staged as [column][row]
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < RPT / 4; ++g)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             uint32_t in[4], out[4];
@@ -338,8 +345,8 @@ __device__ __forceinline__ void quant_weight_bf16_body(const uint16_t* __restric
         }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int piece = t + 256 * i;          // 1024 pieces of 16 B
+    for (int i = 0; i < 1024 / NT; ++i) {
+        const int piece = t + NT * i;           // 1024 pieces of 16 B
         const int kr = piece >> 3, off = (piece & 7) * 16;
         if (kb * kBlock + kr < K && nb * kBlock + off < N)
             st<u32x4>(q + (kb * kBlock + kr) * N + nb * kBlock + off, ld<u32x4>(&qt[qt_off(kr, off)]));
@@ -348,35 +355,39 @@ __device__ __forceinline__ void quant_weight_bf16_body(const uint16_t* __restric
 }
 
 // fp32 weights: 32 lanes x 4 elements per 128-column row, 16 rows per thread
+template <int NT = 256>
 __device__ __forceinline__ void quant_weight_f32_body(const float* __restrict__ w, int64_t N, int64_t K,
                                                       int transpose_out, uint8_t* __restrict__ q,
                                                       float* __restrict__ s, int64_t kb, int64_t nb) {
-    typedef float T;
-    __shared__ float red[4];
+    constexpr int RPT = 4096 / NT;                 // rows per thread: 16 (256 threads) or 8 (512)
+    constexpr int NWV = NT / 64;
+    __shared__ float red[NWV];
     __shared__ __align__(16) uint8_t qt[kBlock * (kBlock + 16)];
     const int t = threadIdx.x;
     const int c4 = (t & 31) * 4;
-    const int r0 = (t >> 5) * 16;
+    const int r0 = (t >> 5) * RPT;
     const int64_t nbs = (N + kBlock - 1) / kBlock;    // N % 16 == 0: a last partial block of N % 128 rows
-    const T* wb = w + nb * kBlock * K + kb * kBlock + c4;
+    const float* wb = w + nb * kBlock * K + kb * kBlock + c4;
     const bool cvalid = kb * kBlock + c4 < K;     // K % 16 == 0: a last partial block of K % 128 columns
     const int64_t kbs = (K + kBlock - 1) / kBlock;
-    v4f v[16];
+    v4f v[RPT];
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < RPT; ++i) {
         v[i] = cvalid && nb * kBlock + r0 + i < N ? load4(wb + int64_t(r0 + i) * K) : v4f{0.f, 0.f, 0.f, 0.f};
         amax = fmaxf(amax, abs_max4(v[i]));
     }
     amax = wave_max(amax);
     if ((t & 63) == 0) red[t >> 6] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    amax = red[0];
+#pragma unroll
+    for (int i = 1; i < NWV; ++i) amax = fmaxf(amax, red[i]);
     const float sc = amax / 448.0f;
     const float rc = 1.0f / sc;
     if (!transpose_out) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < RPT; ++i) {
             const int64_t row = nb * kBlock + r0 + i;
             if (cvalid && row < N)
                 *reinterpret_cast<uint32_t*>(q + row * K + kb * kBlock + c4) = encode4(v[i], sc, rc);
@@ -385,7 +396,7 @@ __device__ __forceinline__ void quant_weight_f32_body(const float* __restrict__ 
         return;
     }
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < RPT / 4; ++g) {
         uint32_t in[4], out[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) in[i] = encode4(v[4 * g + i], sc, rc);
@@ -396,8 +407,8 @@ __device__ __forceinline__ void quant_weight_f32_body(const float* __restrict__ 
     __syncthreads();
     // row kr of the transposed block: 128 bytes, written by 8 threads x 16 B
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int piece = t + 256 * i;          // 1024 pieces of 16 B
+    for (int i = 0; i < 1024 / NT; ++i) {
+        const int piece = t + NT * i;           // 1024 pieces of 16 B
         const int kr = piece >> 3, off = (piece & 7) * 16;
         if (kb * kBlock + kr < K && nb * kBlock + off < N)
             st<u32x4>(q + (kb * kBlock + kr) * N + nb * kBlock + off, ld<u32x4>(&qt[qt_off(kr, off)]));
@@ -405,32 +416,35 @@ __device__ __forceinline__ void quant_weight_f32_body(const float* __restrict__ 
     if (t == 0) s[kb * nbs + nb] = sc;
 }
 
-// the 128x128 block (nb, kb)
+// the 128x128 block (nb, kb), by a workgroup of NT threads
+template <int NT = 256>
 __device__ __forceinline__ void quant_weight_body(const float* w, int64_t N, int64_t K, int transpose_out, uint8_t* q,
                                                   float* s, int64_t kb, int64_t nb) {
-    quant_weight_f32_body(w, N, K, transpose_out, q, s, kb, nb);
+    quant_weight_f32_body<NT>(w, N, K, transpose_out, q, s, kb, nb);
 }
+template <int NT = 256>
 __device__ __forceinline__ void quant_weight_body(const uint16_t* w, int64_t N, int64_t K, int transpose_out,
                                                   uint8_t* q, float* s, int64_t kb, int64_t nb) {
-    quant_weight_bf16_body(w, N, K, transpose_out, q, s, kb, nb);
+    quant_weight_bf16_body<NT>(w, N, K, transpose_out, q, s, kb, nb);
 }
 
-// workgroup (bx, by) of a grid with gy row groups
-template <int U>
+// workgroup (bx, by) of NT threads in a grid with gy row groups
+template <int U, int NT = 256>
 __device__ __forceinline__ void quant_act_rows_dispatch(const float* x, int64_t M, int64_t K, uint8_t* q, float* s,
                                                         int64_t bx, int64_t by, int64_t gy) {
-    quant_act_rows_body<U>(x, M, K, q, s, bx, by, gy);
+    quant_act_rows_body<U, float, NT>(x, M, K, q, s, bx, by, gy);
 }
-template <int U>
+template <int U, int NT = 256>
 __device__ __forceinline__ void quant_act_rows_dispatch(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
                                                         float* s, int64_t bx, int64_t by, int64_t gy) {
-    quant_act_rows_bf16_body<U>(x, M, K, q, s, bx, by, gy);
+    quant_act_rows_bf16_body<U, NT>(x, M, K, q, s, bx, by, gy);
 }
-// rowwise workgroup grid of an [M][K] activation: (K-block chunks of U, row groups)
-template <class T>
+// rowwise grid of an [M][K] activation for NT-thread workgroups: (K-block
+// chunks of U, row groups)
+template <class T, int NT = 256>
 inline void act_rows_grid(int64_t M, int64_t K, int64_t& chunks, int64_t& row_groups) {
     constexpr int U = 4;
-    constexpr int rows_per_group = sizeof(T) == 4 ? 8 : 16;   // half-waves (fp32) or quarter-waves (bf16)
+    constexpr int rows_per_group = sizeof(T) == 4 ? NT / 32 : NT / 16;   // half-waves (fp32) or quarter-waves (bf16)
     chunks = ((K + kBlock - 1) / kBlock + U - 1) / U;
     row_groups = (M + rows_per_group - 1) / rows_per_group;
     if (row_groups > 65535) row_groups = 65535;      // the kernel strides over the rest
@@ -519,18 +533,20 @@ FP8FG_QUANT_KERNELS(uint16_t, bf16)
 // body of its own kernel, so every byte is what the two separate launches
 // write.  One launch lets the two small grids overlap instead of each paying
 // its own ramp-up and drain.
+constexpr int kFpropThreads = 512;   // eight waves: half the registers per weight thread of a 256-thread block
 #define FP8FG_FPROP_KERNEL(TX, TW, SUFFIX)                                                                   \
-    __global__ __launch_bounds__(256) void quant_fprop_##SUFFIX(                                             \
+    __global__ __launch_bounds__(kFpropThreads) void quant_fprop_##SUFFIX(                                   \
         const TX* __restrict__ x, int64_t M, const TW* __restrict__ w, int64_t N, int64_t K,                 \
         uint8_t* __restrict__ qa, float* __restrict__ sa, uint8_t* __restrict__ qb, float* __restrict__ sb,  \
         int64_t act_chunks, int64_t act_groups) {                                                            \
         const int64_t kbs = (K + kBlock - 1) / kBlock, w_blocks = kbs * ((N + kBlock - 1) / kBlock);         \
         const int64_t b = blockIdx.x;                                                                        \
         if (b < w_blocks) {                                                                                  \
-            quant_weight_body(w, N, K, 0, qb, sb, b % kbs, b / kbs);                                         \
+            quant_weight_body<kFpropThreads>(w, N, K, 0, qb, sb, b % kbs, b / kbs);                          \
         } else {                                                                                             \
             const int64_t a = b - w_blocks;                                                                  \
-            quant_act_rows_dispatch<4>(x, M, K, qa, sa, a % act_chunks, a / act_chunks, act_groups);         \
+            quant_act_rows_dispatch<4, kFpropThreads>(x, M, K, qa, sa, a % act_chunks, a / act_chunks,       \
+                                                      act_groups);                                           \
         }                                                                                                    \
     }
 FP8FG_FPROP_KERNEL(float, float, f32_f32)
@@ -583,11 +599,11 @@ static hipError_t launch_fprop(const TX* x, int64_t M, const TW* w, int64_t N, i
                                void (*kern)(const TX*, int64_t, const TW*, int64_t, int64_t, uint8_t*, float*,
                                             uint8_t*, float*, int64_t, int64_t)) {
     int64_t chunks = 0, row_groups = 0;
-    act_rows_grid<TX>(M, K, chunks, row_groups);
+    act_rows_grid<TX, kFpropThreads>(M, K, chunks, row_groups);
     const int64_t w_blocks = ((K + kBlock - 1) / kBlock) * ((N + kBlock - 1) / kBlock);
     const int64_t blocks = w_blocks + chunks * row_groups;
-    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), 0, stream, x, M, w, N, K, qa, sa, qb, sb, chunks,
-                       row_groups);
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kFpropThreads), 0, stream, x, M, w, N, K, qa, sa, qb, sb,
+                       chunks, row_groups);
     return hipGetLastError();
 }
 
