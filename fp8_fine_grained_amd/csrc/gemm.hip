@@ -183,6 +183,14 @@ __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile, int
     Tile t;
     const int n_tiles = int(((n_ext < 0 ? args.N : n_ext) + BN - 1) / BN);   // a last partial n-tile when N % BN != 0
     const int64_t kbs = (args.K + BK - 1) / BK;
+    if (MODE == int(GemmMode::Masked) && args.xcds > 1) {
+        // Workgroup w runs on XCD w mod xcds (round-robin dispatch).  Give each
+        // XCD whole (expert, m-tile) pairs -- ranks x, x + xcds, ... -- so the
+        // n-tiles sharing a pair's A rows share one L2; the host sets xcds only
+        // when it divides the pair count, which keeps this a bijection.
+        const int64_t x = tile % args.xcds, j = tile / args.xcds;
+        tile = (x + args.xcds * (j / n_tiles)) * n_tiles + j % n_tiles;
+    }
     t.bn = int(tile % n_tiles);
     tile /= n_tiles;
     t.A = args.a;
@@ -1682,6 +1690,14 @@ bool wide_enabled() {
     return !(e && e[0] == '0');
 }
 
+// gfx950 (MI350 series): eight XCDs, each with its own L2
+constexpr int kXcds = 8;
+// FP8FG_GEMM_XCD=0 keeps the masked layout's tiles in plain rank order (comparison runs)
+bool xcd_order_enabled() {
+    const char* e = getenv("FP8FG_GEMM_XCD");
+    return !(e && e[0] == '0');
+}
+
 // compute units of the current device (queried once per device)
 int cu_count() {
     static int cache[64] = {0};
@@ -1771,10 +1787,16 @@ hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, c
                           : tile == 2 ? tile_count<WideTile>(mode, args)
                                       : tile_count<WideDecodeTile>(mode, args);
     if (tiles == 0) return hipSuccess;
+    GemmArgs a = args;
+    if (mode == GemmMode::Masked && xcd_order_enabled()) {
+        const int64_t bm = tile == 0 ? BigTile::BM : tile == 1 ? DecodeTile::BM : tile == 2 ? WideTile::BM
+                                                                                             : WideDecodeTile::BM;
+        if ((args.G * ((args.M + bm - 1) / bm)) % kXcds == 0) a.xcds = kXcds;
+    }
     auto launch = [&](const KernelEntry& k) -> bool {
         if (k.tile == tile && k.engine == engine && k.bscale == bscale_1x128 && k.out_fp32 == out_fp32 &&
             k.mode == int(mode)) {
-            hipLaunchKernelGGL(k.fn, dim3(unsigned(tiles)), dim3(k.threads), 0, stream, args);
+            hipLaunchKernelGGL(k.fn, dim3(unsigned(tiles)), dim3(k.threads), 0, stream, a);
             return true;
         }
         return false;

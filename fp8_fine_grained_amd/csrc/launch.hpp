@@ -32,6 +32,7 @@ struct GemmArgs {
     int64_t N, K;
     int64_t G;              // groups (1 for dense)
     float* cs;              // output scales [N/128][M] of the FP8 output mode (else unused)
+    int xcds = 1;           // masked layout: XCDs whose L2s the tile order groups experts for (1: none)
 };
 
 // MX GEMM: args.sa / args.sb carry the E8M0 scale bytes ([K/32][M], [K/32][N])

@@ -360,6 +360,40 @@ def test_masked_many_experts_every_row_once():
             assert np.all(ch[g, mm[g]:] == -7.0), g
 
 
+# (G, M_max, N, K): the 64 x 256 decode tile (16 pairs), the 256 x 256 tile
+# (M_max > 128: 8 pairs), the fold decode tile (N = 128 mod 256: 16 pairs), and
+# 12 pairs, which the host leaves in rank order
+@pytest.mark.parametrize("G,M_max,N,K", [(8, 128, 768, 384), (4, 300, 512, 256), (8, 96, 384, 256),
+                                         (6, 128, 512, 256)])
+def test_masked_xcd_order_same_bits(monkeypatch, G, M_max, N, K):
+    """The masked layout's tile order groups each (expert, m-tile) pair's
+    n-tiles on one XCD; every tile computes the same thing wherever it runs,
+    so the output must equal, bit for bit, the plain rank order
+    (FP8FG_GEMM_XCD=0), and stay inside the oracle's bound."""
+    rng = np.random.default_rng(G * 1000 + M_max + N + K)
+    mm = rng.integers(0, M_max + 1, G).astype(np.int32)
+    mm[:3] = [M_max, 0, 1]
+    a = np.stack([workloads.activations(rng, M_max, K, 0.01, 50.0) for _ in range(G)])
+    qa, sa = zip(*[quant.quant_act_1x128(a[g]) for g in range(G)])
+    qa, sa = np.stack(qa), np.stack(sa)
+    qs, ss = zip(*[quant.quant_weight_128x128(workloads.weights(rng, N, K)) for _ in range(G)])
+    qb, sb = np.stack(qs), np.stack(ss)
+    args = (dev(qa), dev(sa), dev(qb), dev(sb), dev(mm))
+    outs = []
+    for mode in ("1", "0"):
+        monkeypatch.setenv("FP8FG_GEMM_XCD", mode)
+        c = torch.full((G, M_max, N), -5.0, dtype=torch.bfloat16, device=DEV)
+        fp8.fp8_grouped_gemm_masked(*args, torch.bfloat16, out=c)
+        torch.cuda.synchronize()
+        outs.append(c.cpu())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "tile order changed the bits"
+    res = gemm.grouped_masked_ref(qa, sa, qb, sb, mm)
+    ch = outs[0].double().numpy()
+    for g in range(G):
+        check(ch[g, :mm[g]], res[g][0], res[g][1], "bf16", f"xcd order g={g}")
+        assert np.all(ch[g, mm[g]:] == -5.0), g
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("N,K", [(4096, 7168), (7168, 2048)])
 def test_masked_moe_full_size(N, K):
