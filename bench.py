@@ -112,9 +112,10 @@ _SETTLE = {"done": False, "seconds": 0.5}
 
 
 def time_launches(fn, steps, warmup, stream):
-    """Average duration (ms) of fn() from HIP events recorded around each
-    launch on the launch stream.  The first call of a run first keeps the GPU
-    busy with fn for --settle-s seconds, untimed, so the clock has settled."""
+    """Duration (ms) of one fn(): `steps` back-to-back launches between two HIP
+    events on the launch stream, divided by `steps`; the median of three such
+    runs.  The first call of a run first keeps the GPU busy with fn for
+    --settle-s seconds, untimed, so the clock has settled."""
     import torch
     if not _SETTLE["done"]:
         t_end = time.perf_counter() + _SETTLE["seconds"]
@@ -129,13 +130,16 @@ def time_launches(fn, steps, warmup, stream):
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i, (a, b) in enumerate(evs):
+    runs = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        fn(i)
+        for i in range(steps):
+            fn(i)
         b.record(stream)
-    torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        torch.cuda.synchronize()
+        runs.append(a.elapsed_time(b) / steps)
+    return float(np.median(runs))
 
 
 def extra_line(workload, kernel, ms, flops=None, nbytes=None, args=None, config=None, peak=None):
@@ -299,11 +303,17 @@ def run_extra(args):
             c = torch.empty((G, MMAX, N), dtype=torch.bfloat16, device="cuda")
             valid = int(mm.sum())
             nbytes = G * N * K + G * (N // 128) * (K // 128) * 4 + valid * K + valid * (K // 128) * 4 + valid * N * 2
+            cfg = {"experts": G, "M_max": MMAX, "valid_rows": valid, "N": N, "K": K,
+                   "bytes": "all expert weights + scales + valid A rows + valid C rows"}
             ms = time_launches(lambda i: fp8.fp8_grouped_gemm_masked(qa, sa, qb, sb, mmt, out=c), T, W, stream)
-            extra_line("moe_masked", f"grouped_gemm_masked N={N} K={K}", ms, nbytes=nbytes, args=args,
-                       config={"experts": G, "M_max": MMAX, "valid_rows": valid, "N": N, "K": K,
-                               "bytes": "all expert weights + scales + valid A rows + valid C rows"})
-            del qb, sb, c
+            extra_line("moe_masked", f"grouped_gemm_masked N={N} K={K}", ms, nbytes=nbytes, args=args, config=cfg)
+            # the same GEMM on weights stored in the decode-tiled layout (rearranged
+            # once, when weights are loaded; the rearrangement is not in the timed loop)
+            qt = fp8.fp8_tile_weights_decode(qb)
+            ms = time_launches(lambda i: fp8.fp8_grouped_gemm_masked_tiled(qa, sa, qt, sb, mmt, out=c), T, W, stream)
+            extra_line("moe_masked", f"grouped_gemm_masked_tiled N={N} K={K}", ms, nbytes=nbytes, args=args,
+                       config=dict(cfg, weights="decode-tiled layout (fp8_tile_weights_decode)"))
+            del qb, sb, c, qt
 
 
 def main():

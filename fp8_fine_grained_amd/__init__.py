@@ -22,13 +22,14 @@ BSCALE_1x128 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
            "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
            "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16", "fp8_requant_act_tokenwise",
            "fp8_quant_mx_1x32", "fp8_gemm_mx", "fp8_gemm_blockscaled_fp8out", "fp8_quant_fprop_operands",
+           "fp8_tile_weights_decode", "fp8_grouped_gemm_masked_tiled",
            "fp8fg_status_string", "fp8fg_abi_version")
-_COMPUTE = EXPORTS[:12]
+_COMPUTE = EXPORTS[:14]
 
 
 class Fp8fgError(RuntimeError):
@@ -62,6 +63,8 @@ def load_library(path=LIB_PATH):
     lib.fp8_gemm_mx.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     lib.fp8_gemm_blockscaled_fp8out.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.fp8_quant_fprop_operands.argtypes = [vp, i32, i64, vp, i32, i64, i64, vp, vp, vp, vp, vp]
+    lib.fp8_tile_weights_decode.argtypes = [vp, i64, i64, i64, vp, vp]
+    lib.fp8_grouped_gemm_masked_tiled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     for name in _COMPUTE:
         getattr(lib, name).restype = ctypes.c_int
     lib.fp8fg_status_string.argtypes = [ctypes.c_int]
@@ -297,5 +300,37 @@ def fp8_grouped_gemm_masked(a, sa, b, sb, masked_m, out_dtype=torch.bfloat16, ou
     _need(out, out_dtype, (G, M_max, N), "out")
     _check("fp8_grouped_gemm_masked", load_library().fp8_grouped_gemm_masked(
         _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(masked_m), G, M_max, N, K, _ptr(out),
+        _out_dtype(out_dtype), _stream(a)))
+    return out
+
+
+def fp8_tile_weights_decode(q, out=None):
+    """Experts' codes u8 [G][N][K] -> the decode-tiled layout, returned as u8
+    [G][N/256][K/64][16384]: one 16 KB block per (expert, 256-row n-tile,
+    64-byte K piece), in the order fp8fg.h defines."""
+    G, N, K = q.shape
+    _need(q, torch.uint8, (G, N, K), "q")
+    shape = (G, N // 256, K // 64, 16384)
+    out = _empty(shape, torch.uint8, q) if out is None else out
+    _need(out, torch.uint8, shape, "out")
+    _check("fp8_tile_weights_decode", load_library().fp8_tile_weights_decode(
+        _ptr(q), G, N, K, _ptr(out), _stream(q)))
+    return out
+
+
+def fp8_grouped_gemm_masked_tiled(a, sa, b_tiled, sb, masked_m, out_dtype=torch.bfloat16, out=None):
+    """fp8_grouped_gemm_masked with the experts' codes in the decode-tiled
+    layout (b_tiled u8 [G][N/256][K/64][16384], from fp8_tile_weights_decode)."""
+    G, M_max, K = a.shape
+    N = b_tiled.shape[1] * 256
+    _need(a, torch.uint8, (G, M_max, K), "a")
+    _need(sa, torch.float32, (G, _nb(K), M_max), "sa")
+    _need(b_tiled, torch.uint8, (G, N // 256, K // 64, 16384), "b_tiled")
+    _need(sb, torch.float32, (G, _nb(N), _nb(K)), "sb")
+    _need(masked_m, torch.int32, (G,), "masked_m")
+    out = _empty((G, M_max, N), out_dtype, a) if out is None else out
+    _need(out, out_dtype, (G, M_max, N), "out")
+    _check("fp8_grouped_gemm_masked_tiled", load_library().fp8_grouped_gemm_masked_tiled(
+        _ptr(a), _ptr(sa), _ptr(b_tiled), _ptr(sb), _ptr(masked_m), G, M_max, N, K, _ptr(out),
         _out_dtype(out_dtype), _stream(a)))
     return out

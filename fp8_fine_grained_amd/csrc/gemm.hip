@@ -711,7 +711,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), kRsrcFlags);
 }
 
-template <class W>
+// TB: B is in the decode-tiled layout (fp8_tile_weights_decode): each
+// half-block of a 256-row n-tile is one contiguous 16 KB block, already in
+// the stage's LDS order, so the B pieces are plain contiguous copies.
+template <class W, bool TB = false>
 struct WideBufCopier {
     rsrc_t ra, rb, rs;
     uint32_t va[W::A_PER_WAVE], vb[W::B_PER_WAVE], vs;   // per-lane byte offsets
@@ -754,18 +757,19 @@ struct WideBufCopier {
         }
 #pragma unroll
         for (int i = 0; i < W::B_PER_WAVE; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i]), 16, vb[i], koff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i]), 16, vb[i],
+                                                     TB ? uint32_t(h) * uint32_t(W::BN * W::KS) : koff, 0, 0);
         if (!sparse || (has_scale && (pos & 1) == 0))
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs, uint32_t(h >> 1) * s_step,
                                                      0, 0);
     }
 };
 
-template <class W>
-__device__ __forceinline__ WideBufCopier<W> make_wide_buf_copier(const Tile& t, int wave, int lane, int64_t K,
-                                                                 int64_t n0) {
+template <class W, bool TB = false>
+__device__ __forceinline__ WideBufCopier<W, TB> make_wide_buf_copier(const Tile& t, int wave, int lane, int64_t K,
+                                                                     int64_t n0) {
     typedef WStage<W> S;
-    WideBufCopier<W> c;
+    WideBufCopier<W, TB> c;
     c.K = K;
     c.has_scale = wave < W::A_SCALE_WAVES + W::B_SCALE_WAVES;
     const int sub = lane >> 2, slot = lane & 3;
@@ -788,7 +792,9 @@ __device__ __forceinline__ WideBufCopier<W> make_wide_buf_copier(const Tile& t, 
     for (int i = 0; i < W::B_PER_WAVE; ++i) {
         const int r0 = (wave * W::B_PER_WAVE + i) * W::ROWS_PER_PIECE, r = r0 + sub;
         const int chunk = slot ^ ((r >> 2) & 3);
-        c.vb[i] = uint32_t(int64_t(r) * K + chunk * 16);
+        // tiled: the lane's 16 bytes sit where the stage keeps them (row r,
+        // position slot, holding K chunk `chunk` of the half-block)
+        c.vb[i] = TB ? uint32_t(r0 * W::KS + lane * 16) : uint32_t(int64_t(r) * K + chunk * 16);
         c.b_c16[i] = chunk * 16;
         c.b_lds[i] = int(offsetof(S, b)) + r0 * W::KS;
     }
@@ -915,7 +921,7 @@ constexpr uint32_t wide_lds_bytes() { return uint32_t(W::STAGES * sizeof(WStage<
 // OUT: 0 = BF16, 1 = FP32, 2 = FP8 codes + 1x128 scales along N (dense only).
 // `lds_raw` holds wide_lds_bytes<W>(); the workgroup computes tile `tile` of
 // the n-tiles covering columns [0, n_ext) (n_ext < 0: all N).
-template <class W, int OUT, int MODE>
+template <class W, int OUT, int MODE, bool TB = false>
 __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args, uint8_t* lds_raw, int64_t tile, int64_t n_ext) {
     typedef WStage<W> S;
     constexpr int FM = W::FM, FN = W::FN, STAGES = W::STAGES;
@@ -930,7 +936,8 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args, uint8_t* ld
     const Tile t = map_tile<W, MODE>(args, tile, n_ext);
     if (!t.live) return;
     const int64_t n0 = int64_t(t.bn) * W::BN;
-    const WideBufCopier<W> cp = make_wide_buf_copier<W>(t, wave, lane, K, n0);
+    static_assert(!TB || (W::BN == 256 && W::KS == 64), "the decode-tiled layout has 256-row, 64-K blocks");
+    const WideBufCopier<W, TB> cp = make_wide_buf_copier<W, TB>(t, wave, lane, K, n0);
     const int64_t wrow0 = t.m0 + wm * FM * 32;
     const int64_t left = t.rows_valid - wrow0;
     // m-tiles of this wave holding valid rows (uniform): 0, 1 or FM.  Only the
@@ -1667,6 +1674,34 @@ FP8FG_WIDE_KERNELS(FP8FG_DEFINE_WIDE)
 const KernelEntry kWideKernels[] = {FP8FG_WIDE_KERNELS(FP8FG_WIDE_ENTRY)};
 #undef FP8FG_WIDE_ENTRY
 
+// the masked decode tile on decode-tiled B (fp8_grouped_gemm_masked_tiled)
+__global__ __launch_bounds__(WideDecodeTile::THREADS) void gemm_wdect_o0_masked(GemmArgs args) {
+    __shared__ __align__(16) uint8_t lds[wide_lds_bytes<WideDecodeTile>()];
+    gemm_wide_body<WideDecodeTile, 0, int(GemmMode::Masked), true>(args, lds, blockIdx.x, -1);
+}
+__global__ __launch_bounds__(WideDecodeTile::THREADS) void gemm_wdect_o1_masked(GemmArgs args) {
+    __shared__ __align__(16) uint8_t lds[wide_lds_bytes<WideDecodeTile>()];
+    gemm_wide_body<WideDecodeTile, 1, int(GemmMode::Masked), true>(args, lds, blockIdx.x, -1);
+}
+
+// The decode-tiled weight layout, 16 bytes per thread in output order.  Output
+// byte block blk (16 KB) = (g * N/256 + t) * (K/64) + h holds n-tile t of
+// expert g (rows 256 t .. 256 t + 255) for K bytes 64 h .. 64 h + 63: row r of
+// the n-tile at bytes 64 r .. 64 r + 63, whose 16-byte position s holds K chunk
+// s ^ ((r >> 2) & 3) of the half-block -- the order the decode tile's stage
+// keeps in LDS.
+__global__ __launch_bounds__(256) void tile_weights_decode(const uint8_t* __restrict__ q, int64_t K, int64_t units,
+                                                           uint8_t* __restrict__ out) {
+    const int64_t halves = K / 64;
+    for (int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x; u < units; u += int64_t(gridDim.x) * 256) {
+        const int64_t blk = u >> 10;
+        const int within = int(u & 1023), r = within >> 2, sl = within & 3;
+        const int64_t gt = blk / halves, h = blk - gt * halves;
+        const int c = sl ^ ((r >> 2) & 3);
+        st<u32x4>(out + u * 16, ld<u32x4>(q + (gt * 256 + r) * K + h * 64 + c * 16));
+    }
+}
+
 template <class C>
 int64_t tile_count(GemmMode mode, const GemmArgs& args) {
     const int64_t n_tiles = (args.N + C::BN - 1) / C::BN;
@@ -1696,6 +1731,11 @@ constexpr int kXcds = 8;
 bool xcd_order_enabled() {
     const char* e = getenv("FP8FG_GEMM_XCD");
     return !(e && e[0] == '0');
+}
+// the masked layout's XCD grouping for tiles of bm rows: on when 8 divides the
+// (expert, m-tile) pair count
+int masked_xcds(const GemmArgs& args, int64_t bm) {
+    return xcd_order_enabled() && (args.G * ((args.M + bm - 1) / bm)) % kXcds == 0 ? kXcds : 1;
 }
 
 // compute units of the current device (queried once per device)
@@ -1788,11 +1828,11 @@ hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, c
                                       : tile_count<WideDecodeTile>(mode, args);
     if (tiles == 0) return hipSuccess;
     GemmArgs a = args;
-    if (mode == GemmMode::Masked && xcd_order_enabled()) {
-        const int64_t bm = tile == 0 ? BigTile::BM : tile == 1 ? DecodeTile::BM : tile == 2 ? WideTile::BM
-                                                                                             : WideDecodeTile::BM;
-        if ((args.G * ((args.M + bm - 1) / bm)) % kXcds == 0) a.xcds = kXcds;
-    }
+    if (mode == GemmMode::Masked)
+        a.xcds = masked_xcds(args, tile == 0   ? BigTile::BM
+                                   : tile == 1 ? DecodeTile::BM
+                                   : tile == 2 ? WideTile::BM
+                                               : WideDecodeTile::BM);
     auto launch = [&](const KernelEntry& k) -> bool {
         if (k.tile == tile && k.engine == engine && k.bscale == bscale_1x128 && k.out_fp32 == out_fp32 &&
             k.mode == int(mode)) {
@@ -1822,7 +1862,35 @@ hipError_t launch_mx(int out_fp32, const GemmArgs& args, hipStream_t stream) {
     return hipGetLastError();
 }
 
+hipError_t launch_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream) {
+    const int64_t tiles = tile_count<WideDecodeTile>(GemmMode::Masked, args);
+    if (tiles == 0) return hipSuccess;
+    GemmArgs a = args;
+    a.xcds = masked_xcds(args, WideDecodeTile::BM);
+    hipLaunchKernelGGL(out_fp32 ? gemm_wdect_o1_masked : gemm_wdect_o0_masked, dim3(unsigned(tiles)),
+                       dim3(WideDecodeTile::THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, uint8_t* out, hipStream_t stream) {
+    const int64_t units = G * N * (K / 16);
+    if (units == 0) return hipSuccess;
+    const int64_t blocks = (units + 255) / 256;
+    hipLaunchKernelGGL(tile_weights_decode, dim3(unsigned(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream, q,
+                       K, units, out);
+    return hipGetLastError();
+}
+
 }  // namespace gemm_detail
+
+hipError_t launch_gemm_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream) {
+    return gemm_detail::launch_masked_tiled(out_fp32, args, stream);
+}
+
+hipError_t launch_tile_weights_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, uint8_t* out,
+                                      hipStream_t stream) {
+    return gemm_detail::launch_tile_decode(q, G, N, K, out, stream);
+}
 
 hipError_t launch_gemm_mx(int out_fp32, const GemmArgs& args, hipStream_t stream) {
     return gemm_detail::launch_mx(out_fp32, args, stream);

@@ -39,5 +39,10 @@ struct GemmArgs {
 hipError_t launch_gemm_mx(int out_fp32, const GemmArgs& args, hipStream_t stream);
 hipError_t launch_gemm(GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                        hipStream_t stream);
+// the masked layout on decode-tiled B (M <= 128, N % 256 == 0, K % 64 == 0)
+hipError_t launch_gemm_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream);
+// [G][N][K] codes -> the decode-tiled layout (N % 256 == 0, K % 64 == 0)
+hipError_t launch_tile_weights_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, uint8_t* out,
+                                      hipStream_t stream);
 
 }  // namespace fp8fg

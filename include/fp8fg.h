@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 6
+#define FP8FG_ABI_VERSION 7
 
 enum fp8fg_status {
     FP8FG_OK = 0,
@@ -247,6 +247,38 @@ int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t
 int fp8_grouped_gemm_masked(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                             const int32_t* masked_m, int64_t G, int64_t M_max,
                             int64_t N, int64_t K, void* c, int out_dtype, void* stream);
+
+/*
+ * Decode-tiled weight layout for the masked GEMM (this library's own format;
+ * the pages define the masked layout's operation -- "Deepgemm lançado no dia 4
+ * da semana de código aberto Deepseek", section "Principais características"
+ * -- not a storage order).  Decode streams every expert's weights once per
+ * step, so a storage order in which each step of the kernel reads one
+ * contiguous block raises the HBM rate; weights are static, so the
+ * rearrangement is made once, when they are loaded.
+ * q: u8 [G][N][K] codes, as written by fp8_quant_weight_128x128 per expert.
+ * q_tiled: u8, G*N*K bytes (caller-owned, must not overlap q).  Block
+ *   blk = (g * N/256 + t) * (K/64) + h (16384 bytes at offset 16384 * blk)
+ *   holds rows 256 t .. 256 t + 255 of expert g, K bytes 64 h .. 64 h + 63:
+ *   row r (0..255) at bytes 64 r .. 64 r + 63 of the block, whose 16-byte
+ *   position s (0..3) holds bytes 16 c .. 16 c + 15 of that 64-byte piece,
+ *   c = s ^ ((r >> 2) & 3).  A pure byte permutation; the scales are not
+ *   touched (sb stays [G][N/128][K/128]).
+ * Requires N % 256 == 0, K % 64 == 0, K < 2^24, G >= 0 (empty arrays may be
+ * NULL).
+ */
+int fp8_tile_weights_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, uint8_t* q_tiled, void* stream);
+
+/*
+ * fp8_grouped_gemm_masked on decode-tiled weights: the same operation, the
+ * same arguments and the same result bit for bit, except that b_tiled holds
+ * the experts' codes in the layout written by fp8_tile_weights_decode.
+ * Always the exact engine (FP8FG_GEMM_ENGINE is not read).
+ * Requires M_max <= 128, N % 256 == 0, K % 64 == 0, K > 0, K < 2^24, G >= 0.
+ */
+int fp8_grouped_gemm_masked_tiled(const uint8_t* a, const float* sa, const uint8_t* b_tiled, const float* sb,
+                                  const int32_t* masked_m, int64_t G, int64_t M_max,
+                                  int64_t N, int64_t K, void* c, int out_dtype, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp8fg_status_string(int status);

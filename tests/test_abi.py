@@ -163,6 +163,28 @@ def test_grouped_argument_errors():
     assert m(P, P, P, P, P, 4, 0, 128, 128, P, 0, NUL) == OK
 
 
+def test_decode_tiled_argument_errors():
+    lib = fp8.load_library()
+    t = lib.fp8_tile_weights_decode
+    assert t(NUL, 2, 512, 128, P, NUL) == ENULL
+    assert t(P, 2, 384, 128, P2, NUL) == ESHAPE       # N % 256
+    assert t(P, 2, 512, 96, P2, NUL) == ESHAPE        # K % 64
+    assert t(P, -1, 512, 128, P2, NUL) == ESHAPE
+    assert t(MIS, 2, 512, 128, P2, NUL) == EALIGN
+    assert t(P, 2, 512, 1 << 24, P2, NUL) == EUNSUP
+    assert t(NUL, 0, 512, 128, NUL, NUL) == OK         # empty: NULL allowed
+    m = lib.fp8_grouped_gemm_masked_tiled
+    assert m(P, P, P, P, NUL, 4, 128, 256, 128, P, 0, NUL) == ENULL
+    assert m(P, P, P, P, P, 4, 128, 128, 128, P, 0, NUL) == ESHAPE   # N % 256
+    assert m(P, P, P, P, P, 4, 128, 256, 96, P, 0, NUL) == ESHAPE    # K % 64
+    assert m(P, P, P, P, P, 4, 128, 256, 0, P, 0, NUL) == ESHAPE     # K = 0 with work to do
+    assert m(P, P, MIS, P, P, 4, 128, 256, 128, P, 0, NUL) == EALIGN
+    assert m(P, P, P, P, P, 4, 128, 256, 128, P, 2, NUL) == EUNSUP   # output dtype
+    assert m(P, P, P, P, P, 4, 129, 256, 128, P, 0, NUL) == EUNSUP   # M_max > 128
+    assert m(P, P, P, P, P, 0, 128, 256, 128, P, 0, NUL) == OK       # G = 0
+    assert m(P, P, P, P, P, 4, 0, 256, 128, P, 0, NUL) == OK         # M_max = 0
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
