@@ -108,25 +108,23 @@ def cpu_baseline(x, w, rows, min_seconds=10.0):
                       f"{dt:.2f} s"}
 
 
-_SETTLE = {"done": False, "seconds": 0.5}
+_SETTLE = {"seconds": 0.5}
 
 
 def time_launches(fn, steps, warmup, stream):
     """Duration (ms) of one fn(): `steps` back-to-back launches between two HIP
     events on the launch stream, divided by `steps`; the median of three such
-    runs.  The first call of a run first keeps the GPU busy with fn for
-    --settle-s seconds, untimed, so the clock has settled."""
+    runs.  Each call first keeps the GPU busy with fn for --settle-s seconds,
+    untimed, so the clock has settled after the set-up work between lines."""
     import torch
-    if not _SETTLE["done"]:
-        t_end = time.perf_counter() + _SETTLE["seconds"]
-        n = 0
-        while time.perf_counter() < t_end:
-            fn(n)
-            n += 1
-            if n % 64 == 0:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
-        _SETTLE["done"] = True
+    t_end = time.perf_counter() + _SETTLE["seconds"]
+    n = 0
+    while time.perf_counter() < t_end:
+        fn(n)
+        n += 1
+        if n % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()

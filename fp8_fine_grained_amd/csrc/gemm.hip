@@ -31,6 +31,9 @@
 //                 contiguous and long masked buffers (256 x 256 tiles), and
 //                 decode-sized masked buffers (gemm_wdec_*, 64 x 256 tiles);
 //                 the promotion is folded into the MFMA accumulator (below).
+//   gemm_wdect_*  the decode tile on weights in the decode-tiled layout
+//                 (written by tile_weights_decode): each half-block is one
+//                 contiguous 16 KB block in the stage's LDS order.
 //   gemm_wmix_*   dense grids planned as 256 x 256 tiles plus 256 x 192 tail
 //                 tiles, so both kinds fill whole rounds of the device's CUs.
 //   gemm_big_* / gemm_dec_*   the fold kernels described next: 1x128-scaled
