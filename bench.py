@@ -50,10 +50,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--settle-s", type=float, default=0.5,
                    help="seconds of untimed steps before the warmup steps (clock settling)")
-    p.add_argument("--profile-kernel", choices=["gemm", "quant_act", "quant_weight", "quant_fprop", "copy"],
+    p.add_argument("--profile-kernel", choices=["gemm", "quant_act", "quant_weight", "quant_fprop", "copy", "masked",
+                                                "masked_tiled"],
                    help="counter-collection driver: launch only this kernel `steps` times on the "
                         "dense_fprop inputs (copy: a 1 GiB device-to-device copy, the byte-counter "
-                        "calibration); prints no JSON")
+                        "calibration; masked / masked_tiled: the masked decode gate+up GEMM on plain / "
+                        "decode-tiled weights); prints no JSON")
     p.add_argument("--workload", default="dense_fprop",
                    choices=["dense_fprop", "dense_small", "linear_trio", "moe_contig", "moe_masked", "dense_mx"],
                    help="dense_fprop is the headline step; the others print one line per measured kernel")
@@ -171,6 +173,49 @@ def gpu_acts(gen, rows, K, frac, mult, sigma=1.0):
     return x
 
 
+def masked_inputs(gen, G, MMAX, N, K):
+    """The masked decode workload on the GPU: seeded valid-row counts, 1x128
+    quantized activations and 128x128 quantized expert weights."""
+    import torch
+    import fp8_fine_grained_amd as fp8
+    import workloads
+    mm, _ = workloads.moe_masked_inputs(N, 128, G, MMAX)
+    a = gpu_acts(gen, G * MMAX, K, 0.001, 100.0).reshape(G, MMAX, K).contiguous()
+    qa = torch.empty((G, MMAX, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((G, K // 128, MMAX), dtype=torch.float32, device="cuda")
+    for g in range(G):
+        fp8.fp8_quant_act_1x128(a[g], q=qa[g], s=sa[g])
+    del a
+    qb = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device="cuda")
+    for g in range(G):
+        wg = torch.randn((N, K), generator=gen, device="cuda") * 0.02
+        fp8.fp8_quant_weight_128x128(wg, q=qb[g], s=sb[g])
+    mmt = torch.from_numpy(mm.astype(np.int32)).cuda()
+    c = torch.empty((G, MMAX, N), dtype=torch.bfloat16, device="cuda")
+    return mm, qa, sa, qb, sb, mmt, c
+
+
+def profile_masked(args):
+    """Counter-collection driver for the masked decode GEMM (gate+up shape):
+    launch only that kernel `steps` times, on plain or decode-tiled weights."""
+    import torch
+    import fp8_fine_grained_amd as fp8
+    fp8.load_library()
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    mm, qa, sa, qb, sb, mmt, c = masked_inputs(gen, 32, 128, 4096, 7168)
+    if args.profile_kernel == "masked_tiled":
+        qb = fp8.fp8_tile_weights_decode(qb)
+        fn = fp8.fp8_grouped_gemm_masked_tiled
+    else:
+        fn = fp8.fp8_grouped_gemm_masked
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        fn(qa, sa, qb, sb, mmt, out=c)
+    torch.cuda.synchronize()
+    print(f"profiled {args.profile_kernel} x{args.steps} (valid rows {int(mm.sum())})", flush=True)
+
+
 def run_extra(args):
     import torch
     import fp8_fine_grained_amd as fp8
@@ -286,19 +331,7 @@ def run_extra(args):
     elif args.workload == "moe_masked":
         G, MMAX = 32, 128
         for (N, K) in ((4096, 7168), (7168, 2048)):
-            mm, _ = workloads.moe_masked_inputs(N, 128, G, MMAX)
-            a = gpu_acts(gen, G * MMAX, K, 0.001, 100.0).reshape(G, MMAX, K).contiguous()
-            qa = torch.empty((G, MMAX, K), dtype=torch.uint8, device="cuda")
-            sa = torch.empty((G, K // 128, MMAX), dtype=torch.float32, device="cuda")
-            for g in range(G):
-                fp8.fp8_quant_act_1x128(a[g], q=qa[g], s=sa[g])
-            qb = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
-            sb = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device="cuda")
-            for g in range(G):
-                wg = torch.randn((N, K), generator=gen, device="cuda") * 0.02
-                fp8.fp8_quant_weight_128x128(wg, q=qb[g], s=sb[g])
-            mmt = torch.from_numpy(mm.astype(np.int32)).cuda()
-            c = torch.empty((G, MMAX, N), dtype=torch.bfloat16, device="cuda")
+            mm, qa, sa, qb, sb, mmt, c = masked_inputs(gen, G, MMAX, N, K)
             valid = int(mm.sum())
             nbytes = G * N * K + G * (N // 128) * (K // 128) * 4 + valid * K + valid * (K // 128) * 4 + valid * N * 2
             cfg = {"experts": G, "M_max": MMAX, "valid_rows": valid, "N": N, "K": K,
@@ -320,6 +353,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
         sys.exit(2)
     _SETTLE["seconds"] = args.settle_s
+    if args.profile_kernel in ("masked", "masked_tiled"):
+        profile_masked(args)
+        return
     if args.workload != "dense_fprop":
         run_extra(args)
         return
