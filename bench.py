@@ -484,6 +484,21 @@ def main():
     t_fp8mfma = gemm_back_to_back()
     del os.environ["FP8FG_GEMM_ENGINE"]
 
+    # Measured references on this machine, the same way: the platform's own BF16
+    # GEMM (torch.matmul, no block scales) on the same M x N x K, and a device
+    # copy (read + write bytes).  They put the exact engine's rate next to what
+    # the vendor library reaches with the same matrix cores, and the quantizers'
+    # bytes next to an achievable stream.
+    ab = torch.randn((M, K), device=dev, dtype=torch.bfloat16)
+    bb = torch.randn((K, N), device=dev, dtype=torch.bfloat16)   # contiguous [K][N]: a plain 2-D product
+    cb = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+    t_bf16_lib = back_to_back(lambda s: torch.matmul(ab, bb, out=cb))
+    src = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    t_copy = back_to_back(lambda s: dst.copy_(src))
+    copy_gbs = 2.0 * src.numel() * 4 / (t_copy * 1e-3) / 1e9
+    del ab, bb, cb, src, dst
+
     flops = 2.0 * M * N * K
     value = flops / (ms_step * 1e-3) / 1e12
     gemm_tflops = flops / (t_gemm * 1e-3) / 1e12
@@ -530,6 +545,15 @@ def main():
                           "tflops": round(flops / (t_fp8out * 1e-3) / 1e12, 2),
                           "note": "same GEMM writing FP8 codes + 1x128 scales along N (the next layer's A "
                                   "operand) instead of BF16; not the timed step"},
+        "measured_reference": {
+            "torch_bf16_matmul_us": round(t_bf16_lib * 1e3, 2),
+            "torch_bf16_matmul_tflops": round(flops / (t_bf16_lib * 1e-3) / 1e12, 2),
+            "gemm_frac_of_torch_bf16_matmul": round(t_bf16_lib / t_gemm, 4),
+            "device_copy_gbs": round(copy_gbs, 1),
+            "quant_fprop_frac_of_copy": round((act_bytes + w_bytes) / (t_fprop * 1e-3) / 1e9 / copy_gbs, 4),
+            "note": "same box, same run: torch.matmul on BF16 operands of the same shape (no block scales) and a "
+                    "1 GiB device-to-device copy (read + write bytes), each as back-to-back launches between two "
+                    "HIP events"},
         "fp8mfma_engine": {"gemm_us": round(t_fp8mfma * 1e3, 2),
                            "tflops": round(flops / (t_fp8mfma * 1e-3) / 1e12, 2),
                            "pct_of_fp8_peak": round(100 * flops / (t_fp8mfma * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
