@@ -493,6 +493,19 @@ def main():
     bb = torch.randn((K, N), device=dev, dtype=torch.bfloat16)   # contiguous [K][N]: a plain 2-D product
     cb = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
     t_bf16_lib = back_to_back(lambda s: torch.matmul(ab, bb, out=cb))
+    # the platform's FP8 GEMM with one scale per row of A and per column of B
+    # (torch._scaled_mm, row-wise): no 1x128 / 128x128 blocks, so not this
+    # method, but the FP8 matrix cores as the vendor library drives them
+    t_fp8_lib = None
+    try:
+        af = torch.randn((M, K), device=dev).to(torch.float8_e4m3fn)
+        wf = torch.randn((N, K), device=dev).to(torch.float8_e4m3fn)
+        ra, rb = torch.ones((M, 1), device=dev), torch.ones((1, N), device=dev)
+        t_fp8_lib = back_to_back(lambda s: torch._scaled_mm(af, wf.t(), scale_a=ra, scale_b=rb,
+                                                             out_dtype=torch.bfloat16))
+        del af, wf, ra, rb
+    except (RuntimeError, AttributeError, TypeError):
+        t_fp8_lib = None
     src = torch.empty(1 << 28, device=dev, dtype=torch.float32)
     dst = torch.empty_like(src)
     t_copy = back_to_back(lambda s: dst.copy_(src))
@@ -549,9 +562,12 @@ def main():
             "torch_bf16_matmul_us": round(t_bf16_lib * 1e3, 2),
             "torch_bf16_matmul_tflops": round(flops / (t_bf16_lib * 1e-3) / 1e12, 2),
             "gemm_frac_of_torch_bf16_matmul": round(t_bf16_lib / t_gemm, 4),
+            "torch_fp8_scaled_mm_rowwise_tflops": (round(flops / (t_fp8_lib * 1e-3) / 1e12, 2)
+                                                   if t_fp8_lib else None),
             "device_copy_gbs": round(copy_gbs, 1),
             "quant_fprop_frac_of_copy": round((act_bytes + w_bytes) / (t_fprop * 1e-3) / 1e9 / copy_gbs, 4),
-            "note": "same box, same run: torch.matmul on BF16 operands of the same shape (no block scales) and a "
+            "note": "same box, same run: torch.matmul on BF16 operands of the same shape (no block scales), "
+                    "torch._scaled_mm on FP8 operands with row/column scales (no 1x128 / 128x128 blocks), and a "
                     "1 GiB device-to-device copy (read + write bytes), each as back-to-back launches between two "
                     "HIP events"},
         "fp8mfma_engine": {"gemm_us": round(t_fp8mfma * 1e3, 2),
