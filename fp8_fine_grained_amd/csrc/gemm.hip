@@ -622,11 +622,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
 // scale) is zero reads its codes from a zeroed 64-byte line after the ring,
 // so its products are +0 whatever the codes hold.
 //
-// Measured on this kernel: a SIMD runs its two waves' MFMAs and VALU
-// instructions essentially one after the other (only about two VALU
-// instructions per 32x32x16 MFMA hide under it), so the loop costs MFMA time
-// plus VALU time; the cvts (3 per MFMA) and the rescale (2 per MFMA) are most
-// of the latter.
+// This loop serves the masked layout; the dense and contiguous layouts run
+// the interleaved schedule below (gemm_wide_il_body), same arithmetic.
 // Tile configurations of the kernel: WAVES_M x WAVES_N waves, each owning
 // FM x FN MFMA tiles of 32 x 32, STAGES half-block stages.
 template <int WAVES_M_, int WAVES_N_, int FM_, int FN_, int STAGES_>
@@ -751,8 +748,29 @@ struct WideBufCopier {
     // parity except for the reloads past the end, which are never read).
     // Sparse also skips an A piece whose rows lie past every m-tile the tile
     // computes (decode tiles with at most 32 valid rows).
-    __device__ __forceinline__ void copy(uint8_t* stage, int h, int pos, bool sparse) const {
+    // `ahead` (dense copies only): the scale piece of half-block h carries the
+    // scales of the NEXT K-block, h / 2 + 1, so they sit in LDS a whole
+    // K-block before they are applied (the first block's come another way).
+    // The pieces of the last K-block then lie past the scale array and read
+    // zeros (range-checked buffer loads); they are never used.
+    // Piece i of copy(stage, h, pos, false, true): the A pieces, then the B
+    // pieces, then the scale piece -- so that a copy can be spread over a
+    // half-block's MFMAs instead of issued in one burst.
+    __device__ __forceinline__ void copy_piece(uint8_t* stage, int h, int i) const {
         const uint32_t koff = uint32_t(h) * W::KS;
+        if (i < W::A_PER_WAVE)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + a_lds[i]), 16, va[i], koff, 0, 0);
+        else if (i < W::A_PER_WAVE + W::B_PER_WAVE)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i - W::A_PER_WAVE]), 16,
+                                                     vb[i - W::A_PER_WAVE], koff, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs,
+                                                     uint32_t((h >> 1) + 1) * s_step, 0, 0);
+    }
+
+    __device__ __forceinline__ void copy(uint8_t* stage, int h, int pos, bool sparse, bool ahead = false) const {
+        const uint32_t koff = uint32_t(h) * W::KS;
+        const uint32_t skb = uint32_t(ahead ? (h >> 1) + 1 : h >> 1);
         if (!(sparse && skip_a)) {
 #pragma unroll
             for (int i = 0; i < W::A_PER_WAVE; ++i)
@@ -763,8 +781,7 @@ struct WideBufCopier {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i]), 16, vb[i],
                                                      TB ? uint32_t(h) * uint32_t(W::BN * W::KS) : koff, 0, 0);
         if (!sparse || (has_scale && (pos & 1) == 0))
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs, uint32_t(h >> 1) * s_step,
-                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs, skb * s_step, 0, 0);
     }
 };
 
@@ -1071,6 +1088,400 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args, uint8_t* ld
                 }
             }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Interleaved schedule of the wide exact kernel (dense and contiguous layouts).
+//
+// Measured on gfx950 (one 32x32x16 BF16 MFMA every 32 cycles per SIMD, with
+// one or two waves): up to about six independent VALU instructions issue
+// under each MFMA at no cost -- widening cvts and rescale multiplies alike --
+// and eight cost a third more.  The exact engine needs about six per MFMA
+// (three cvts, two rescale multiplies, scale and address arithmetic), so the
+// schedule must spread them evenly; the loop above bunches them (the rescale
+// multiplies of a whole K-block between a barrier and the first MFMA).  In a
+// timestamped run of that loop on 4096 x 7168 x 2048, waves spent a third of
+// each half-block in the barrier and in issuing the copies right after it.
+// This schedule:
+//   - one barrier per K-block: the ring's four half-block slots hold K-blocks
+//     kb and kb + 1; kb + 1's copies are issued piece by piece between kb's
+//     MFMAs (not in a burst after a barrier) into the slots of kb - 1;
+//   - MFMAs run in groups of IL_GW n-tiles (all four k-steps of a half-block,
+//     the group's FM x IL_GW tiles taking turns): the A fragments of a
+//     half-block are used by every group, a group's B fragments only by it,
+//     so each cvt runs just before its first use;
+//   - a tile's rescale may run anywhere between its last MFMA of K-block kb-1
+//     and its first of kb: the first half of the groups rescale in the odd
+//     half-block of kb-1 (after their MFMAs), the others in the even
+//     half-block of kb (before theirs), 64 multiplies per half-block;
+//   - the scale piece of each stage carries the NEXT K-block's scales
+//     (copy(ahead)), so the ratios and cvt exponents of K-block kb+1 are
+//     computed in the last group of kb's even half-block; the first
+//     K-block's scales are read from global memory before the loop;
+//   - an odd half-block's A fragments and first group's B fragments are read
+//     from LDS during the even half-block (into registers its first group has
+//     finished with), so the odd half-block starts without an LDS burst;
+//   - a compile-time plan (make_il_plan) gives every cvt and multiply a slot,
+//     the gap after one MFMA: at most IL_CAP VALU instructions per slot, cvts
+//     one MFMA before their first use, a tile's multiplies two MFMAs after its
+//     last one; sched_barrier(0) fences keep the program order the plan sets.
+// Same arithmetic in the same order per output element as gemm_wide_body:
+// bit-identical results (tested).
+constexpr int IL_CAP = 6;
+constexpr int IL_GW = 2;   // n-tiles per group: FM x IL_GW accumulators in flight
+
+// slot -1 = before the first MFMA; slot n = right after MFMA n.  MFMA n of a
+// half-block is (group G, k-step k, m-tile mi, n-tile 2G + p) with
+// n = G (4 FM GW) + k (FM GW) + mi GW + p: within a group the FM x GW tiles
+// take turns, so consecutive MFMAs on one accumulator are FM x GW apart.
+template <int FM, int FN>
+struct IlPlan {
+    static constexpr int NS = 4 * FM * FN;
+    signed char a[FM][4][4];      // cvt q (one dword) of A fragment (mi, k)
+    signed char b[FN][4][4];      // cvt q of B fragment (g, k)
+    signed char m[FM][FN][16];    // rescale multiply of element i of tile (mi, g); -2: none in this half
+};
+
+template <int FM, int FN>
+constexpr IlPlan<FM, FN> make_il_plan(bool odd, int scale_slot, int scale_ops) {
+    constexpr int NS = IlPlan<FM, FN>::NS, GW = IL_GW, NG = FN / GW, PG = 4 * FM * GW;
+    IlPlan<FM, FN> p{};
+    int cap[NS] = {};
+    for (int n = 0; n < NS; ++n) cap[n] = IL_CAP;
+    // the scale arithmetic of the next K-block (even half-blocks) takes room in
+    // the slots from scale_slot on
+    for (int n = scale_slot, left = scale_ops; n < NS && left > 0; ++n) {
+        const int take = left < cap[n] ? left : cap[n];
+        cap[n] -= take;
+        left -= take;
+    }
+    // cvts first, each as late as possible but one MFMA before its first use
+    // (latest use first); what finds no room runs before MFMA 0 (slot -1)
+    auto late = [&](int hi) -> int {
+        for (int n = hi; n >= 0; --n)
+            if (cap[n] > 0) {
+                --cap[n];
+                return n;
+            }
+        return -1;
+    };
+    for (int n = NS - 1; n >= 0; --n) {
+        const int G = n / PG, k = (n % PG) / (FM * GW), mi = (n % (FM * GW)) / GW, pp = n % GW;
+        if (mi == 0)
+            for (int q = 3; q >= 0; --q) p.b[G * GW + pp][k][q] = (signed char)late(n - 1);
+        if (G == 0 && pp == 0)
+            for (int q = 3; q >= 0; --q) p.a[mi][k][q] = (signed char)late(n - 1);
+    }
+    // then the multiplies, each tile's sixteen as early as its window allows
+    // in the room left (a window that is full spills to its last slot): the
+    // first NG/2 groups after their last MFMA of an odd half-block, the others
+    // before their first MFMA of an even one
+    auto early = [&](int lo, int hi) -> int {
+        for (int n = lo < 0 ? 0 : lo; n <= hi; ++n)
+            if (cap[n] > 0) {
+                --cap[n];
+                return n;
+            }
+        return hi;
+    };
+    for (int g = 0; g < FN; ++g)
+        for (int mi = 0; mi < FM; ++mi)
+            for (int i = 0; i < 16; ++i) {
+                const int G = g / GW, first = G * PG + mi * GW + g % GW, last = first + 3 * FM * GW;
+                if (odd && G < NG / 2)
+                    p.m[mi][g][i] = (signed char)early(last + 2, NS - 1);
+                else if (!odd && G >= NG / 2)
+                    p.m[mi][g][i] = (signed char)early(0, first - 1);
+                else
+                    p.m[mi][g][i] = -2;
+            }
+    return p;
+}
+
+// one dword (two BF16 values) of a widened fragment: codes of bytes
+// 2 (q & 1) .. +1 of word q >> 1 of the 8-byte half hh of a 16-byte chunk
+__device__ __forceinline__ uint32_t widen_q(const u32x4& raw, int hh, int q, float p2) {
+    const int wd = int(raw[2 * hh + (q >> 1)]);
+    return __builtin_bit_cast(uint32_t, (q & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, p2, true)
+                                                : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, p2, false));
+}
+
+// Even half-blocks also turn the stage's scale piece (the next K-block's
+// scales) into `next`: its LDS reads go out with the fragment reads, its
+// arithmetic runs in four slots of the last group, whose room the plan keeps.
+template <class W, int ODD>
+__device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int wn, int r, int h,
+                                             const WideScales<W::FM>& w, const float (&ratio)[W::FM],
+                                             uint32_t zero_line, v16f (&acc)[W::FM][W::FN],
+                                             WideScales<W::FM>& next, const WideBufCopier<W, false>& cp,
+                                             int fill_slot, int fill_h, int pf_slot, u32x4 (&pfa)[W::FM][2],
+                                             u32x4 (&pfb)[IL_GW][2]) {
+#if defined(__HIP_DEVICE_COMPILE__)   // device code only: the host pass never runs it
+    constexpr int IL_SCALE_OPS = 32;
+    constexpr int FM = W::FM, FN = W::FN, NS = 4 * FM * FN, SS = NS - 12;
+    static_assert(FN % 2 == 0 && FM == 2, "plan shape");
+    constexpr IlPlan<FM, FN> P = make_il_plan<FM, FN>(ODD != 0, SS, ODD ? 0 : IL_SCALE_OPS);
+    const WStage<W>& sg = *reinterpret_cast<const WStage<W>*>(lds + uint32_t(slot) * uint32_t(sizeof(WStage<W>)));
+    float nsa[FM], nsb = 0.0f;
+    if (!ODD) {
+        nsb = sg.sb[((wn * FN * 32) / 128) * 64];
+#pragma clang loop unroll(full)
+        for (int mi = 0; mi < FM; ++mi) nsa[mi] = sg.sa[wm * FM * 32 + mi * 32 + r];
+    }
+    ScaleSplit nb{}, na[FM] = {};
+    uint32_t ch[2];
+#pragma clang loop unroll(full)
+    for (int j = 0; j < 2; ++j) ch[j] = uint32_t(((2 * j + h) ^ ((r >> 2) & 3)) << 4);
+    // fragment reads: the A rows and the B rows of n-tile g from LDS slot `sl`
+    auto read_a = [&](uint32_t sl, int mi, int j) -> u32x4 {
+        const uint32_t at = sl * uint32_t(sizeof(WStage<W>)) + uint32_t(offsetof(WStage<W>, a)) +
+                            uint32_t((wm * FM * 32 + mi * 32 + r) * W::KS) + ch[j];
+        return ld<u32x4>(lds + (w.zero[mi] ? zero_line + ch[j] : at));
+    };
+    auto read_b = [&](uint32_t sl, int g, int j) -> u32x4 {
+        return ld<u32x4>(lds + sl * uint32_t(sizeof(WStage<W>)) + uint32_t(offsetof(WStage<W>, b)) +
+                         uint32_t((wn * FN * 32 + g * 32 + r) * W::KS) + ch[j]);
+    };
+    // An odd half-block's A fragments and its first group's B fragments were
+    // read during the even half-block before it (the K-block's barrier covers
+    // both slots); the rest is read here.  The even one reads all of its own.
+    u32x4 ra[FM][2], rb[FN][2];
+#pragma clang loop unroll(full)
+    for (int mi = 0; mi < FM; ++mi)
+#pragma clang loop unroll(full)
+        for (int j = 0; j < 2; ++j) ra[mi][j] = ODD ? pfa[mi][j] : read_a(uint32_t(slot), mi, j);
+#pragma clang loop unroll(full)
+    for (int g = 0; g < FN; ++g)
+#pragma clang loop unroll(full)
+        for (int j = 0; j < 2; ++j) rb[g][j] = (ODD && g < IL_GW) ? pfb[g][j] : read_b(uint32_t(slot), g, j);
+    u32x4 ca[FM][4], cb[FN][4];
+    // the VALU work planned for slot n
+    auto valu = [&](int n) {
+#pragma clang loop unroll(full)
+        for (int mi = 0; mi < FM; ++mi)
+#pragma clang loop unroll(full)
+            for (int k = 0; k < 4; ++k)
+#pragma clang loop unroll(full)
+                for (int q = 0; q < 4; ++q)
+                    if (P.a[mi][k][q] == n) ca[mi][k][q] = widen_q(ra[mi][k >> 1], k & 1, q, w.pa[mi]);
+#pragma clang loop unroll(full)
+        for (int g = 0; g < FN; ++g)
+#pragma clang loop unroll(full)
+            for (int k = 0; k < 4; ++k)
+#pragma clang loop unroll(full)
+                for (int q = 0; q < 4; ++q)
+                    if (P.b[g][k][q] == n) cb[g][k][q] = widen_q(rb[g][k >> 1], k & 1, q, w.pb);
+#pragma clang loop unroll(full)
+        for (int mi = 0; mi < FM; ++mi)
+#pragma clang loop unroll(full)
+            for (int g = 0; g < FN; ++g)
+#pragma clang loop unroll(full)
+                for (int i = 0; i < 16; ++i)
+                    if (P.m[mi][g][i] == n) acc[mi][g][i] *= ratio[mi];
+    };
+    // the copy of half-block fill_h, one piece every few MFMAs
+    constexpr int PIECES = W::A_PER_WAVE + W::B_PER_WAVE + 1, PSTRIDE = NS / PIECES;
+    uint8_t* fill_stage = lds + uint32_t(fill_slot) * uint32_t(sizeof(WStage<W>));
+    valu(-1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma clang loop unroll(full)
+    for (int n = 0; n < NS; ++n) {
+        constexpr int PG = 4 * FM * IL_GW;
+        const int k = (n % PG) / (FM * IL_GW), mi = (n % (FM * IL_GW)) / IL_GW, g = (n / PG) * IL_GW + n % IL_GW;
+        acc[mi][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, cb[g][k]),
+                                                             __builtin_bit_cast(v8bf, ca[mi][k]), acc[mi][g], 0, 0, 0);
+        if (n % PSTRIDE == 1 && n / PSTRIDE < PIECES) cp.copy_piece(fill_stage, fill_h, n / PSTRIDE);
+        if (!ODD && n == NS / 2 + 2) {
+            // the odd half-block's first fragments, into registers the first
+            // group of this one no longer needs
+#pragma clang loop unroll(full)
+            for (int mi = 0; mi < FM; ++mi)
+#pragma clang loop unroll(full)
+                for (int j = 0; j < 2; ++j) pfa[mi][j] = read_a(uint32_t(pf_slot), mi, j);
+#pragma clang loop unroll(full)
+            for (int g = 0; g < IL_GW; ++g)
+#pragma clang loop unroll(full)
+                for (int j = 0; j < 2; ++j) pfb[g][j] = read_b(uint32_t(pf_slot), g, j);
+        }
+        valu(n);
+        if (!ODD) {
+            // the next K-block's scales, split as wide_scales does
+            if (n == SS) nb = split_scale(nsb);
+            if (n == SS + 1) na[0] = split_scale(nsa[0]);
+            if (n == SS + 2) na[1] = split_scale(nsa[1]);
+            if (n == SS + 3) {
+                next.pb = nb.pow2;
+#pragma clang loop unroll(full)
+                for (int q = 0; q < FM; ++q) {
+                    next.pa[q] = na[q].pow2;
+                    next.unit[q] = clamp_unit(na[q].mant * nb.mant);
+                    next.zero[q] = (nsa[q] == 0.0f || nsb == 0.0f) ? 1 : 0;
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#endif
+}
+
+template <class W, int OUT, int MODE>
+__device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t* lds_raw, int64_t tile, int64_t n_ext) {
+    static_assert(MODE != int(GemmMode::Masked), "dense and contiguous layouts");
+    typedef WStage<W> S;
+    constexpr int FM = W::FM, FN = W::FN, STAGES = W::STAGES;
+    constexpr uint32_t kZeroLine = STAGES * sizeof(S);
+    S* ring = reinterpret_cast<S*>(lds_raw);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / W::WAVES_N, wn = wave % W::WAVES_N;
+    const int64_t N = args.N, K = args.K;
+    const int halves = int(2 * ((K + BK - 1) / BK));
+    const Tile t = map_tile<W, MODE>(args, tile, n_ext);
+    if (!t.live) return;
+    const int64_t n0 = int64_t(t.bn) * W::BN;
+    const WideBufCopier<W, false> cp = make_wide_buf_copier<W, false>(t, wave, lane, K, n0);
+    const int64_t wrow0 = t.m0 + wm * FM * 32;
+    const bool live = wrow0 < t.rows_valid;   // uniform
+    const int r = lane & 31, h = lane >> 5;
+
+    // the first K-block's scales, straight from global memory (rows clamped
+    // as the copier clamps them)
+    float sa0[FM];
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) {
+        int64_t row = wrow0 + mi * 32 + r;
+        row = row < t.rows_valid ? row : t.rows_valid - 1;
+        sa0[mi] = t.SA[row];
+    }
+    const float sb0 = t.SB[((n0 + wn * FN * 32) / 128) * ((K + BK - 1) / BK)];
+
+    if (tid < 4) st<u32x4>(lds_raw + kZeroLine + tid * 16, u32x4{0u, 0u, 0u, 0u});
+    // the ring holds four half-blocks: K-block kb in slots 2kb % 4 and
+    // 2kb % 4 + 1; the copies of K-block kb + 1 run during kb's MFMAs, into
+    // the slots of kb - 1, which every wave has finished by kb's barrier
+    static_assert(STAGES == 4, "two K-blocks of half-block slots");
+    cp.copy(reinterpret_cast<uint8_t*>(&ring[0]), 0, 0, false, true);
+    cp.copy(reinterpret_cast<uint8_t*>(&ring[1]), 1, 1, false, true);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+    v16f acc[FM][FN];
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
+    // w: scales of the current K-block; nw: of the next one.  ratio[mi] moves
+    // a tile from the unit of one K-block to the next's (exactly 1 where no
+    // block follows: multiplying by 1 is exact)
+    WideScales<FM> w, nw;
+    {
+        const ScaleSplit b = split_scale(sb0);
+        nw.pb = b.pow2;
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi) {
+            const ScaleSplit a = split_scale(sa0[mi]);
+            nw.pa[mi] = a.pow2;
+            nw.unit[mi] = clamp_unit(a.mant * b.mant);
+            nw.zero[mi] = (sa0[mi] == 0.0f || sb0 == 0.0f) ? 1 : 0;
+        }
+    }
+    float ratio[FM];
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) ratio[mi] = 1.0f;
+    u32x4 pfa[FM][2], pfb[IL_GW][2];   // an odd half-block's first fragments, read ahead
+
+    for (int hb = 0; hb < halves; hb += 2) {
+        // both halves of this K-block have landed (this wave's copies: the
+        // only loads in flight), then every wave's
+        wait_vmcnt<0>();
+        if ((hb + 2) * W::KS > K) {           // partial last K-block (uniform)
+            cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[hb & 3]), hb, lane);
+            cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[(hb + 1) & 3]), hb + 1, lane);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        __builtin_amdgcn_s_barrier();
+        // the next K-block's halves (past the end: the last half again, into
+        // slots never read again)
+        const int f0 = hb + 2 < halves ? hb + 2 : halves - 1, f1 = hb + 3 < halves ? hb + 3 : halves - 1;
+        if (live) {
+            w = nw;
+            // the even slot's scale piece holds the next K-block's scales
+            wide_il_half<W, 0>(lds_raw, hb & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 2) & 3, f0,
+                               (hb + 1) & 3, pfa, pfb);
+            const bool more = hb + 2 < halves;
+#pragma unroll
+            for (int mi = 0; mi < FM; ++mi)
+                ratio[mi] = more ? clamp_unit(w.unit[mi] * __builtin_amdgcn_rcpf(nw.unit[mi])) : 1.0f;
+            wide_il_half<W, 1>(lds_raw, (hb + 1) & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 3) & 3,
+                               f1, 0, pfa, pfb);
+        } else {
+            cp.copy(reinterpret_cast<uint8_t*>(&ring[(hb + 2) & 3]), f0, f0, false, true);
+            cp.copy(reinterpret_cast<uint8_t*>(&ring[(hb + 3) & 3]), f1, f1, false, true);
+        }
+    }
+    wait_vmcnt<0>();
+
+    const int n_lane = wn * FN * 32 + 4 * h;
+    if constexpr (OUT == 2) {
+        static_assert(FN * 32 == 128, "one 128-column group per wave");
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(acc[mi][ni][i] * w.unit[mi]));
+            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+            const float sc = amax / 448.0f;
+            const float rc = 1.0f / sc;
+            const int64_t m = wrow0 + mi * 32 + r;
+            if (m >= t.rows_valid) continue;
+#pragma unroll
+            for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
+                                      acc[mi][ni][4 * j + 3]} * w.unit[mi];
+                    st<uint32_t>(static_cast<uint8_t*>(args.c) + m * N + n0 + n_lane + ni * 32 + 8 * j,
+                                 encode4(v, sc, rc));
+                }
+            if (h == 0) args.cs[(n0 / 128 + wn) * args.M + m] = sc;
+        }
+        return;
+    }
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) {
+        const int64_t m = wrow0 + mi * 32 + r;
+        if (m >= t.rows_valid) continue;
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
+                const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
+                                  acc[mi][ni][4 * j + 3]} * w.unit[mi];
+                if (OUT == 1) {
+                    st<v4f>(static_cast<float*>(args.c) + idx, v);
+                } else {
+                    const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+                    const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+                    st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
+                }
+            }
+    }
+}
+
+// the wide kernel's body for a layout: the interleaved schedule for the dense
+// and contiguous layouts, the half-block loop for the masked one (whose
+// decode tiles are bound by the weight stream, not by the MFMAs)
+template <class W, int OUT, int MODE>
+__device__ __forceinline__ void gemm_wide_sel(const GemmArgs& args, uint8_t* lds_raw, int64_t tile, int64_t n_ext) {
+    if constexpr (MODE != int(GemmMode::Masked))
+        gemm_wide_il_body<W, OUT, MODE>(args, lds_raw, tile, n_ext);
+    else
+        gemm_wide_body<W, OUT, MODE>(args, lds_raw, tile, n_ext);
 }
 
 // ---------------------------------------------------------------------------
@@ -1392,7 +1803,7 @@ template <int OUT>
 __device__ __forceinline__ void gemm_wmix_body(const GemmArgs& args, int64_t tiles1, int64_t n_split) {
     __shared__ __align__(16) uint8_t lds[wide_lds_bytes<WideTile>()];
     if (int64_t(blockIdx.x) < tiles1)
-        gemm_wide_body<WideTile, OUT, int(GemmMode::Dense)>(args, lds, blockIdx.x, n_split);
+        gemm_wide_sel<WideTile, OUT, int(GemmMode::Dense)>(args, lds, blockIdx.x, n_split);
     else
         gemm_tail_body<OUT>(args, lds, int64_t(blockIdx.x) - tiles1, n_split);
 }
@@ -1669,7 +2080,7 @@ const KernelEntry kKernels[] = {FP8FG_GEMM_KERNELS(FP8FG_ENTRY)};
 #define FP8FG_DEFINE_WIDE(NAME, CFG, TILE, OF, MODE)                                   \
     __global__ __launch_bounds__(CFG::THREADS) void gemm_##NAME(GemmArgs args) {       \
         __shared__ __align__(16) uint8_t lds[wide_lds_bytes<CFG>()];                   \
-        gemm_wide_body<CFG, OF, MODE>(args, lds, blockIdx.x, -1);                     \
+        gemm_wide_sel<CFG, OF, MODE>(args, lds, blockIdx.x, -1);                      \
     }
 FP8FG_WIDE_KERNELS(FP8FG_DEFINE_WIDE)
 #undef FP8FG_DEFINE_WIDE
@@ -1754,14 +2165,16 @@ int cu_count() {
     return cache[dev];
 }
 
-// FP8FG_GEMM_TAIL: unset -> plan tail tiles when they fill whole rounds;
-// "0" -> never; "force" -> whenever the columns split as 256 a + 192 b, b > 0
-// (read at every call; "force" exists to exercise the tail tiles on small shapes)
+// FP8FG_GEMM_TAIL: unset or "0" -> never plan tail tiles (their body has not
+// been given the interleaved schedule, and the plain grid is faster now);
+// "1" -> plan them when they fill whole rounds; "force" -> whenever the
+// columns split as 256 a + 192 b, b > 0 (read at every call; "force" exists to
+// exercise the tail tiles on small shapes)
 int tail_mode() {
     const char* e = getenv("FP8FG_GEMM_TAIL");
-    if (e && strcmp(e, "0") == 0) return 0;
+    if (e && strcmp(e, "1") == 0) return 1;
     if (e && strcmp(e, "force") == 0) return 2;
-    return 1;
+    return 0;
 }
 
 // Split of a dense wide grid into 256 x 256 tiles over columns [0, n_split)
