@@ -52,3 +52,41 @@ def quant_group(vals):
         y = abs(f) if s == 0 else abs(rn32(f / s))
         codes.append(e4m3_rne(neg, y))
     return np.float32(float(s)), codes
+
+
+# E5M2 (OCP): 1 sign, 5 exponent bits with bias 15, 2 mantissa bits; exponent 0
+# holds the subnormals m * 2^-16; exponent 31 is inf / NaN, so the 124 finite
+# non-negative magnitudes are codes 0x00..0x7B, the largest (4 + 3) * 2^13.
+MAGS_E5M2 = [Fraction(c & 3, 1 << 16) if c >> 2 == 0 else Fraction(4 + (c & 3)) * Fraction(2) ** ((c >> 2) - 17)
+             for c in range(124)]
+
+
+def rne_to_grid(mag, mags):
+    """Nearest of the non-negative magnitudes `mags` (ascending, code = index),
+    ties to the even code, saturating at the largest: the code."""
+    if mag >= mags[-1]:
+        return len(mags) - 1
+    c, bd = None, None
+    for k, m in enumerate(mags):
+        d = abs(m - mag)
+        if c is None or d < bd or (d == bd and k % 2 == 0):
+            c, bd = k, d
+    return c
+
+
+def quant_dequant_group(vals, mags):
+    """One group quantized and dequantized exactly as the method does it, in the
+    format whose magnitudes are `mags`: s = RN32(amax / max), y = RN32(x / s),
+    code = RNE(y); returns the exact dequantized values dec(code) * s."""
+    fr = [Fraction(float(v)) for v in vals]
+    amax = max(abs(v) for v in fr)
+    s = rn32(amax / mags[-1])
+    out = []
+    for v, f in zip(vals, fr):
+        if s == 0:
+            out.append(Fraction(0))
+            continue
+        y = rn32(f / s)
+        m = mags[rne_to_grid(abs(y), mags)]
+        out.append((m if y >= 0 else -m) * s)
+    return out

@@ -89,3 +89,22 @@ def test_half_ulp_bound_and_monotone():
     err = np.abs(e4m3.decode(q) - y.astype(np.float64))
     assert np.all(err <= e4m3.ulp_at(y) / 2)
     assert np.all(np.diff(q.astype(np.int64)) >= 0)
+
+
+def test_ulp_at_is_the_code_spacing():
+    """ulp_at(|y|) is the distance from E4M3 value dec(c) to the next one,
+    dec(c + 1), for every code 0x00..0x7D (the subnormal step 2^-9 below 2^-6,
+    2^(e-3) in binade e), and the same anywhere strictly between the two."""
+    codes = np.arange(0x7E, dtype=np.uint8)
+    lo = e4m3.decode(codes)
+    hi = e4m3.decode(codes + 1)
+    step = hi - lo
+    assert np.array_equal(e4m3.ulp_at(lo), step)
+    assert np.array_equal(e4m3.ulp_at((lo + hi) / 2.0), step)
+    assert np.array_equal(e4m3.ulp_at(-lo), step)
+    # closed forms at the edges of the range
+    assert e4m3.ulp_at(0.0) == 2.0 ** -9
+    assert e4m3.ulp_at(2.0 ** -9) == 2.0 ** -9
+    assert e4m3.ulp_at(2.0 ** -6) == 2.0 ** -9          # first normal binade keeps the subnormal step
+    assert e4m3.ulp_at(2.0 ** -5) == 2.0 ** -8
+    assert e4m3.ulp_at(255.0) == 16.0 and e4m3.ulp_at(256.0) == 32.0 and e4m3.ulp_at(448.0) == 32.0

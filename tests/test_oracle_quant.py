@@ -195,3 +195,21 @@ def test_partial_weight_blocks_brute_force():
         bs, bc = quant_group(w[:, lo:hi].reshape(-1))
         assert s[0, kb].view(np.uint32) == bs.view(np.uint32)
         assert q[:, lo:hi].reshape(-1).tolist() == bc
+
+
+def test_per_tensor_scaling_brute_force():
+    """The per-tensor baseline is the method's group step with the whole tensor
+    as one group: checked against the exact rational quantizer on a small tensor
+    with an outlier, negatives and signed zeros, and on an all-zero tensor."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((5, 37)).astype(np.float32)
+    x[2, 3] = 90.0
+    x[1, :4] = [0.0, -0.0, 1e-9, -3e-7]
+    q, s = quant.quant_per_tensor(x)
+    s_ref, codes = quant_group(x.ravel())
+    assert np.float32(s) == s_ref
+    assert np.array_equal(q.ravel(), np.array(codes, dtype=np.uint8))
+    z = np.zeros((3, 4), np.float32)
+    z[0, 1] = -0.0
+    qz, sz = quant.quant_per_tensor(z)
+    assert sz == 0.0 and np.array_equal(qz.ravel(), np.array(quant_group(z.ravel())[1], dtype=np.uint8))

@@ -71,3 +71,29 @@ def test_unified_e4m3_and_fine_groups_win_on_the_linear_layer():
         assert res["tensor_hybrid"][g] > 1.3 * res["tensor_e4m3"][g], (g, res)
     assert res["fine_hybrid"]["fprop"] == res["fine_e4m3"]["fprop"]
     assert res["tensor_e4m3"]["fprop"] > 1.2 * res["fine_e4m3"]["fprop"], res
+
+
+def _exact(vals, mags):
+    from tests.bruteforce import quant_dequant_group
+    return np.array([float(v) for v in quant_dequant_group(vals, mags)], dtype=np.float64)
+
+
+def test_e5m2_groups_and_per_tensor_against_exact_quantizer():
+    """The study's E5M2 1x128 groups (scale amax / 57344) and its per-tensor
+    quantizers (E4M3 and E5M2) equal an exact rational re-implementation: one
+    scale per 128 consecutive values (or per tensor), RN32 division, nearest
+    format value with ties to even."""
+    from tests.bruteforce import MAGS, MAGS_E5M2
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((3, 256)) * np.exp2(rng.integers(-12, 6, size=(3, 256)))).astype(np.float32)
+    x[1, 130] = 700.0                       # an outlier in one group only
+    x[2, 128:256] = 0.0                     # an all-zero group
+    got = study._groups_e5m2(x)
+    ref = np.concatenate([_exact(x[r, 128 * j:128 * j + 128], MAGS_E5M2) for r in range(3) for j in range(2)])
+    assert np.array_equal(got.ravel(), ref)
+    t = x[:2, :64].copy()
+    # values 2^20 .. 2^28 below the max-abs: normal in E5M2 only when the
+    # scale maps the max-abs to 57344, subnormal or zero with a smaller target
+    t[0, :5] = np.max(np.abs(t)) * np.exp2(-np.array([20.0, 22.0, 24.0, 26.0, 28.0])).astype(np.float32)
+    assert np.array_equal(study._tensor(t, e5m2).ravel(), _exact(t.ravel(), MAGS_E5M2))
+    assert np.array_equal(study._tensor(t, e4m3).ravel(), _exact(t.ravel(), MAGS))
