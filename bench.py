@@ -16,7 +16,10 @@ step with the two quantizations as separate launches.  `kernels_us` holds each k
 duration alone: the mean of back-to-back launches between two HIP events on
 the bench stream, right after the timed steps, which is what a kernel trace of
 the same command reports per launch.  `roofline` describes the GEMM kernel,
-with that duration.
+with that duration, as a fraction of the dense FP8 MFMA peak (the metric's
+basis); `frac_of_bf16_peak` is the same rate against the BF16 matrix cores
+the exact engine runs on.  `masked_decode` holds the masked-layout MoE decode
+GEMMs' HBM rates (both shapes, plain and decode-tiled weights).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 import argparse
@@ -113,11 +116,28 @@ def cpu_baseline(x, w, rows, min_seconds=10.0):
 _SETTLE = {"seconds": 0.5}
 
 
+_FLUSH = {}
+
+
+def _flush(stream):
+    """Read a 512 MB buffer (twice the 256 MB last-level cache) on the stream,
+    so the next launch finds none of its inputs in any cache.  Reading, not
+    writing: a write would leave dirty lines whose write-back then competes
+    with the timed kernel for HBM."""
+    import torch
+    if "buf" not in _FLUSH:
+        _FLUSH["buf"] = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
+        _FLUSH["sum"] = torch.empty((), dtype=torch.float32, device="cuda")
+    torch.sum(_FLUSH["buf"], out=_FLUSH["sum"])
+
+
 def time_launches(fn, steps, warmup, stream):
-    """Duration (ms) of one fn(): `steps` back-to-back launches between two HIP
-    events on the launch stream, divided by `steps`; the median of three such
-    runs.  Each call first keeps the GPU busy with fn for --settle-s seconds,
-    untimed, so the clock has settled after the set-up work between lines."""
+    """Duration (ms) of one fn() with its inputs in HBM, not in a cache: each of
+    `steps` launches follows an untimed 512 MB read and is bracketed by its
+    own pair of HIP events on the launch stream; the mean over the launches, the
+    median of three such runs.  Each call first keeps the GPU busy with fn for
+    --settle-s seconds, untimed, so the clock has settled after the set-up
+    work between lines."""
     import torch
     t_end = time.perf_counter() + _SETTLE["seconds"]
     n = 0
@@ -132,13 +152,16 @@ def time_launches(fn, steps, warmup, stream):
     torch.cuda.synchronize()
     runs = []
     for _ in range(3):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
+        ev = []
         for i in range(steps):
+            _flush(stream)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
             fn(i)
-        b.record(stream)
+            b.record(stream)
+            ev.append((a, b))
         torch.cuda.synchronize()
-        runs.append(a.elapsed_time(b) / steps)
+        runs.append(sum(a.elapsed_time(b) for a, b in ev) / steps)
     return float(np.median(runs))
 
 
@@ -148,11 +171,11 @@ def extra_line(workload, kernel, ms, flops=None, nbytes=None, args=None, config=
             "data": "synthetic, seeded (drawn on the GPU)", "config": config or {}}
     if flops:
         tf = flops / (ms * 1e-3) / 1e12
-        pk = peak or PEAK_BF16_TFLOPS
         line.update({"value": round(tf, 2), "unit": "TFLOPS",
-                     "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": pk,
-                                  "unit": "TFLOP/s", "frac": round(tf / pk, 4),
-                                  "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2)}})
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                                  "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                  "matrix_cores": peak or "BF16 (codes widened exactly)"}})
     if nbytes:
         gbs = nbytes / (ms * 1e-3) / 1e9
         line.setdefault("value", round(gbs, 1))
@@ -194,6 +217,41 @@ def masked_inputs(gen, G, MMAX, N, K):
     mmt = torch.from_numpy(mm.astype(np.int32)).cuda()
     c = torch.empty((G, MMAX, N), dtype=torch.bfloat16, device="cuda")
     return mm, qa, sa, qb, sb, mmt, c
+
+
+def masked_decode_rates(args):
+    """HBM rate of the masked-layout decode GEMM on both MoE shapes (gate+up
+    K=7168 N=4096, down K=2048 N=7168; 32 experts, 128-row buffers, U{1..64}
+    valid rows), on plain and on decode-tiled weights.  Bytes: every expert's
+    weights and scales, the valid A rows and their scales, the valid C rows."""
+    import torch
+    import fp8_fine_grained_amd as fp8
+    import workloads
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda").manual_seed(workloads.SEEDS.get("moe_masked", 105))
+    out = {}
+    G, MMAX = 32, 128
+    for name, (N, K) in (("gate_up", (4096, 7168)), ("down", (7168, 2048))):
+        mm, qa, sa, qb, sb, mmt, c = masked_inputs(gen, G, MMAX, N, K)
+        valid = int(mm.sum())
+        nbytes = G * N * K + G * (N // 128) * (K // 128) * 4 + valid * K + valid * (K // 128) * 4 + valid * N * 2
+        ms = time_launches(lambda i: fp8.fp8_grouped_gemm_masked(qa, sa, qb, sb, mmt, out=c), args.steps,
+                           args.warmup, stream)
+        qt = fp8.fp8_tile_weights_decode(qb)
+        ms_t = time_launches(lambda i: fp8.fp8_grouped_gemm_masked_tiled(qa, sa, qt, sb, mmt, out=c), args.steps,
+                             args.warmup, stream)
+        gbs, gbs_t = nbytes / (ms * 1e-3) / 1e9, nbytes / (ms_t * 1e-3) / 1e9
+        out[name] = {"N": N, "K": K, "valid_rows": valid, "algorithmic_bytes": int(nbytes),
+                     "plain_us": round(ms * 1e3, 2), "plain_gbs": round(gbs, 1),
+                     "plain_frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                     "tiled_us": round(ms_t * 1e3, 2), "tiled_gbs": round(gbs_t, 1),
+                     "tiled_frac_of_hbm": round(gbs_t / PEAK_HBM_GBS, 4)}
+        del qa, sa, qb, sb, c, qt
+        torch.cuda.empty_cache()
+    out["note"] = ("each launch after an untimed 512 MB read, between its own HIP events; tiled = weights in "
+                   "the decode-tiled layout (fp8_tile_weights_decode, arranged once at load time); target >= 0.70 "
+                   "of the 8 TB/s HBM peak")
+    return out
 
 
 def profile_masked(args):
@@ -250,7 +308,7 @@ def run_extra(args):
         extra_line("dense_mx", "quant_mx_1x32 W", ms, nbytes=N * K * 5 + N * K // 32, args=args, config=cfg)
         ms = time_launches(lambda i: fp8.fp8_gemm_mx(qa, ea, qb, eb, torch.bfloat16, out=c), T, W, stream)
         extra_line("dense_mx", "gemm_mx 4096x7168x2048 BF16", ms, flops=2.0 * M * N * K, args=args, config=cfg,
-                   peak=PEAK_FP8_TFLOPS)
+                   peak="FP8 (scaled MFMA)")
     elif args.workload == "linear_trio":
         TOK, IN, OUT = 8192, 7168, 2048
         x = gpu_acts(gen, TOK, IN, 0.001, 100.0)
@@ -479,10 +537,13 @@ def main():
     qy = torch.empty((M, N), dtype=torch.uint8, device=dev)
     sy = torch.empty((N // 128, M), dtype=torch.float32, device=dev)
     t_fp8out = back_to_back(lambda s: fp8.fp8_gemm_blockscaled_fp8out(s["qa"], s["sa"], s["qb"], s["sb"], q=qy, s=sy))
-    # the opt-in FP8-MFMA engine (looser error bound), GEMM alone, for comparison
-    os.environ["FP8FG_GEMM_ENGINE"] = "fp8mfma"
-    t_fp8mfma = gemm_back_to_back()
-    del os.environ["FP8FG_GEMM_ENGINE"]
+    # the FP8-MFMA engine (its own entry point, looser error bound), GEMM alone
+    t_fp8mfma = back_to_back(lambda s: fp8.fp8_gemm_blockscaled_fp8mfma(s["qa"], s["sa"], s["qb"], s["sb"],
+                                                                        fp8.BSCALE_128x128, torch.bfloat16,
+                                                                        out=s["c"]))
+    # the masked-layout decode GEMMs (32 experts, 128-row buffers, U{1..64}
+    # valid rows): HBM-bound, so their figure is GB/s against 8 TB/s
+    masked = masked_decode_rates(args)
 
     # Measured references on this machine, the same way: the platform's own BF16
     # GEMM (torch.matmul, no block scales) on the same M x N x K, and a device
@@ -542,13 +603,15 @@ def main():
         "quant_gbs": {"fprop_operands": round((act_bytes + w_bytes) / (t_fprop * 1e-3) / 1e9, 1),
                       "act": round(act_bytes / (t_act * 1e-3) / 1e9, 1),
                       "weight": round(w_bytes / (t_w * 1e-3) / 1e9, 1)},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
                      "traffic": stored_traffic(),
-                     "kernel": "gemm_wmix_o0_dense (dense, 128x128 B scales, BF16 out; on 256 CUs a planned "
-                               "grid of 256 256x256 tiles + 256 256x192 tail tiles, gemm_wide_o0_dense's body "
-                               "for the former): FP8 operands widened exactly to BF16 in registers, BF16 MFMA, "
-                               "so its peak is the dense BF16 MFMA peak",
+                     "kernel": "gemm_wide_o0_dense (dense, 128x128 B scales, BF16 out, 448 tiles of 256x256): "
+                               "FP8 operands widened exactly to BF16 in registers and multiplied on the BF16 "
+                               "matrix cores (gfx950's FP8 MFMA keeps ~14 bits per group of 8 products, outside "
+                               "the 2^-14 contract), so this engine's own ceiling is the BF16 peak, half the FP8 "
+                               "one: frac_of_bf16_peak",
+                     "frac_of_bf16_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                      "pct_of_fp8_peak": round(100 * gemm_tflops / PEAK_FP8_TFLOPS, 2),
                      "kernel_us": round(t_gemm * 1e3, 2),
                      "duration_source": "mean of `steps` back-to-back launches on the bench stream between two "
@@ -573,8 +636,10 @@ def main():
         "fp8mfma_engine": {"gemm_us": round(t_fp8mfma * 1e3, 2),
                            "tflops": round(flops / (t_fp8mfma * 1e-3) / 1e12, 2),
                            "pct_of_fp8_peak": round(100 * flops / (t_fp8mfma * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
-                           "note": "opt-in engine, error bound 2^-9 * sum|ab| (gfx950 FP8 MFMA accumulates "
-                                   "8-product groups with ~14 bits); not the timed step"},
+                           "note": "fp8_gemm_blockscaled_fp8mfma: FP8 matrix cores, error bound 2^-9 * sum|ab| "
+                                   "(gfx950 FP8 MFMA accumulates 8-product groups with ~14 bits); not the timed "
+                                   "step"},
+        "masked_decode": masked,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(host0[0], host0[1], args.cpu_rows)

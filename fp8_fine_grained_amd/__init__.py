@@ -22,14 +22,14 @@ BSCALE_1x128 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
            "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
            "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16", "fp8_requant_act_tokenwise",
            "fp8_quant_mx_1x32", "fp8_gemm_mx", "fp8_gemm_blockscaled_fp8out", "fp8_quant_fprop_operands",
-           "fp8_tile_weights_decode", "fp8_grouped_gemm_masked_tiled",
+           "fp8_tile_weights_decode", "fp8_grouped_gemm_masked_tiled", "fp8_gemm_blockscaled_fp8mfma",
            "fp8fg_status_string", "fp8fg_abi_version")
-_COMPUTE = EXPORTS[:14]
+_COMPUTE = EXPORTS[:15]
 
 
 class Fp8fgError(RuntimeError):
@@ -54,6 +54,7 @@ def load_library(path=LIB_PATH):
     lib.fp8_quant_act_1x128.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.fp8_quant_weight_128x128.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.fp8_gemm_blockscaled.argtypes = [vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp]
+    lib.fp8_gemm_blockscaled_fp8mfma.argtypes = [vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp]
     lib.fp8_grouped_gemm_contiguous.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     lib.fp8_grouped_gemm_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     lib.fp8_quant_act_1x128_bf16.argtypes = [vp, i64, i64, i32, vp, vp, vp]
@@ -236,8 +237,7 @@ def _out_dtype(out_dtype):
     return {torch.bfloat16: OUT_BF16, torch.float32: OUT_FP32}[out_dtype]
 
 
-def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind=BSCALE_128x128, out_dtype=torch.bfloat16, out=None):
-    """C[M][N] = A[M][K] . B[N][K]^T with 1x128 A scales and 128x128 (or 1x128) B scales."""
+def _gemm_dense(fn, a, sa, b, sb, bscale_kind, out_dtype, out):
     M, K = a.shape
     N = b.shape[0]
     _need(a, torch.uint8, (M, K), "a")
@@ -246,10 +246,21 @@ def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind=BSCALE_128x128, out_dtype=tor
     _need(sb, torch.float32, (_nb(N), _nb(K)) if bscale_kind == BSCALE_128x128 else (_nb(K), N), "sb")
     out = _empty((M, N), out_dtype, a) if out is None else out
     _need(out, out_dtype, (M, N), "out")
-    _check("fp8_gemm_blockscaled", load_library().fp8_gemm_blockscaled(
+    _check(fn, getattr(load_library(), fn)(
         _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), int(bscale_kind), _ptr(out), _out_dtype(out_dtype),
         M, N, K, _stream(a)))
     return out
+
+
+def fp8_gemm_blockscaled(a, sa, b, sb, bscale_kind=BSCALE_128x128, out_dtype=torch.bfloat16, out=None):
+    """C[M][N] = A[M][K] . B[N][K]^T with 1x128 A scales and 128x128 (or 1x128) B scales."""
+    return _gemm_dense("fp8_gemm_blockscaled", a, sa, b, sb, bscale_kind, out_dtype, out)
+
+
+def fp8_gemm_blockscaled_fp8mfma(a, sa, b, sb, bscale_kind=BSCALE_128x128, out_dtype=torch.bfloat16, out=None):
+    """fp8_gemm_blockscaled on the FP8 matrix cores: same operands and layouts,
+    accuracy contract 2^-9 * sum|a b| instead of 2^-14 (see fp8fg.h)."""
+    return _gemm_dense("fp8_gemm_blockscaled_fp8mfma", a, sa, b, sb, bscale_kind, out_dtype, out)
 
 
 def fp8_gemm_blockscaled_fp8out(a, sa, b, sb, q=None, s=None):

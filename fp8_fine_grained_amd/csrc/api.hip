@@ -1,8 +1,8 @@
 // C entry points of libfp8fg.so (declared in include/fp8fg.h).
 //
 // Every argument is checked on the host before anything is enqueued, in this
-// order: NULL pointers, sizes and multiple-of-128 rules, 16-byte alignment,
-// enum values.  A zero-sized problem returns FP8FG_OK without touching the
+// order: NULL pointers, sizes and each call's multiple-of rules, 16-byte
+// alignment, enum values.  A zero-sized problem returns FP8FG_OK without touching the
 // HIP runtime, so these checks can be exercised on a machine without a GPU.
 #include "fp8fg.h"
 #include "launch.hpp"
@@ -13,6 +13,9 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+// K-blocks of the calls that always run the wide exact kernel, whose single
+// FP32 accumulator keeps the 2^-14 S contract up to this many (gemm.hip)
+constexpr int64_t kWideMaxKBlocks = 92;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -30,7 +33,7 @@ const char* fp8fg_status_string(int status) {
     switch (status) {
         case FP8FG_OK: return "ok";
         case FP8FG_ERR_NULL: return "null pointer argument";
-        case FP8FG_ERR_SHAPE: return "invalid shape (negative size or not a multiple of 128)";
+        case FP8FG_ERR_SHAPE: return "invalid shape (negative size, or a size that breaks the call's multiple-of rule)";
         case FP8FG_ERR_ALIGN: return "pointer not 16-byte aligned";
         case FP8FG_ERR_UNSUPPORTED: return "unsupported argument value or size";
         case FP8FG_ERR_HIP: return "HIP runtime error at launch";
@@ -142,8 +145,9 @@ int fp8_gemm_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uin
     return hip_status(fp8fg::launch_gemm_mx(out_dtype == FP8FG_OUT_FP32, args, static_cast<hipStream_t>(stream)));
 }
 
-int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int bscale_kind,
-                         void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+// the dense call's checks; engine 0 = exact, 1 = FP8 MFMA
+static int gemm_dense(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int bscale_kind, void* c,
+                      int out_dtype, int64_t M, int64_t N, int64_t K, void* stream, int engine) {
     if (!a || !sa || !b || !sb || !c) return FP8FG_ERR_NULL;
     if (M < 0 || N < 0 || K < 0 || N % 16 != 0 || K % 16 != 0) return FP8FG_ERR_SHAPE;
     if (K == 0 && M > 0 && N > 0) return FP8FG_ERR_SHAPE;
@@ -154,8 +158,19 @@ int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, co
     if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return FP8FG_OK;
     fp8fg::GemmArgs args{a, sa, b, sb, c, nullptr, M, N, K, 1};
-    return hip_status(fp8fg::launch_gemm(fp8fg::GemmMode::Dense, bscale_kind == FP8FG_BSCALE_1x128,
+    return hip_status(fp8fg::launch_gemm(engine, fp8fg::GemmMode::Dense, bscale_kind == FP8FG_BSCALE_1x128,
                                          out_dtype == FP8FG_OUT_FP32, args, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int bscale_kind,
+                         void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+    return gemm_dense(a, sa, b, sb, bscale_kind, c, out_dtype, M, N, K, stream, 0);
+}
+
+int fp8_gemm_blockscaled_fp8mfma(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                 int bscale_kind, void* c, int out_dtype, int64_t M, int64_t N, int64_t K,
+                                 void* stream) {
+    return gemm_dense(a, sa, b, sb, bscale_kind, c, out_dtype, M, N, K, stream, 1);
 }
 
 int fp8_gemm_blockscaled_fp8out(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, uint8_t* q,
@@ -165,12 +180,12 @@ int fp8_gemm_blockscaled_fp8out(const uint8_t* a, const float* sa, const uint8_t
     if (K == 0 && M > 0 && N > 0) return FP8FG_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(q) || !aligned16(s))
         return FP8FG_ERR_ALIGN;
-    if (M > kMaxDim || N > kMaxDim || K >= (int64_t(1) << 24)) return FP8FG_ERR_UNSUPPORTED;
+    if (M > kMaxDim || N > kMaxDim || (K + 127) / 128 > kWideMaxKBlocks) return FP8FG_ERR_UNSUPPORTED;
     if (((K + 127) / 128) * M * 4 > int64_t(0xFFFFFFFF)) return FP8FG_ERR_UNSUPPORTED;
     if (((M + 255) / 256) * (N / 256) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return FP8FG_OK;
     fp8fg::GemmArgs args{a, sa, b, sb, q, nullptr, M, N, K, 1, s};
-    return hip_status(fp8fg::launch_gemm(fp8fg::GemmMode::Dense, 0, 2, args, static_cast<hipStream_t>(stream)));
+    return hip_status(fp8fg::launch_gemm(0, fp8fg::GemmMode::Dense, 0, 2, args, static_cast<hipStream_t>(stream)));
 }
 
 int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
@@ -188,7 +203,7 @@ int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t
     if ((M_total / 128) * ((N + 127) / 128) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
     if (G == 0 || M_total == 0 || N == 0) return FP8FG_OK;
     fp8fg::GemmArgs args{a, sa, b, sb, c, group_offsets, M_total, N, K, G};
-    return hip_status(fp8fg::launch_gemm(fp8fg::GemmMode::Contig, 0, out_dtype == FP8FG_OUT_FP32, args,
+    return hip_status(fp8fg::launch_gemm(0, fp8fg::GemmMode::Contig, 0, out_dtype == FP8FG_OUT_FP32, args,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -206,7 +221,7 @@ int fp8_grouped_gemm_masked(const uint8_t* a, const float* sa, const uint8_t* b,
     if (tiles_per_group > 0 && G > kMaxDim / tiles_per_group) return FP8FG_ERR_UNSUPPORTED;
     if (G == 0 || M_max == 0 || N == 0) return FP8FG_OK;
     fp8fg::GemmArgs args{a, sa, b, sb, c, masked_m, M_max, N, K, G};
-    return hip_status(fp8fg::launch_gemm(fp8fg::GemmMode::Masked, 0, out_dtype == FP8FG_OUT_FP32, args,
+    return hip_status(fp8fg::launch_gemm(0, fp8fg::GemmMode::Masked, 0, out_dtype == FP8FG_OUT_FP32, args,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -231,7 +246,7 @@ int fp8_grouped_gemm_masked_tiled(const uint8_t* a, const float* sa, const uint8
         return FP8FG_ERR_ALIGN;
     if (!valid_out(out_dtype)) return FP8FG_ERR_UNSUPPORTED;
     // the decode tile: buffers of at most 128 rows; 256 K bytes per n-tile stay below 4 GiB
-    if (M_max > 128 || N > kMaxDim || K >= (int64_t(1) << 24) || G > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if (M_max > 128 || N > kMaxDim || (K + 127) / 128 > kWideMaxKBlocks || G > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
     if (N > 0 && G > kMaxDim / (2 * (N / 256))) return FP8FG_ERR_UNSUPPORTED;
     if (G == 0 || M_max == 0 || N == 0) return FP8FG_OK;
     fp8fg::GemmArgs args{a, sa, b_tiled, sb, c, masked_m, M_max, N, K, G};

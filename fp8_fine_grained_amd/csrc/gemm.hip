@@ -11,11 +11,11 @@
 // both K-major; A scales [K/128][rows]; C [rows][N].
 //
 // Two engines compute P_kb:
-//   exact   (default) -- each FP8 fragment is widened to BF16 in registers
-//           (exact: BF16 holds every E4M3 value) and eight chained
-//           v_mfma_f32_32x32x16_bf16 form P_kb.  This MFMA adds exact
-//           products with IEEE FP32 round-to-nearest, so P_kb is an
-//           FP32-accurate block sum, which is what the promotion assumes.
+//   exact   -- each FP8 fragment is widened to BF16 in registers (exact: BF16
+//           holds every E4M3 value) and eight chained v_mfma_f32_32x32x16_bf16
+//           form P_kb.  This MFMA adds exact products with IEEE FP32
+//           round-to-nearest, so P_kb is an FP32-accurate block sum, which is
+//           what the promotion assumes.  Every entry point but one.
 //   fp8mfma -- two chained v_mfma_f32_32x32x64_f8f6f4 per K-block straight
 //           from the FP8 codes, at twice the MFMA rate.  gfx950's FP8 MFMAs
 //           add their products in groups of eight consecutive K, truncating
@@ -23,21 +23,21 @@
 //           exponent (about 14 significant bits: the kind of limited
 //           accumulation the pages measured on H800, here inside a single
 //           instruction), so promotion every 128 cannot restore FP32 accuracy
-//           and this engine is held to a looser bound.  Chosen with
-//           FP8FG_GEMM_ENGINE=fp8mfma.
+//           and this engine is held to a looser bound.  Only the dense entry
+//           point fp8_gemm_blockscaled_fp8mfma runs it.
 //
 // Kernels, by what they serve:
-//   gemm_wide_*   exact engine, 128x128-scaled B, N % 256 == 0: dense,
-//                 contiguous and long masked buffers (256 x 256 tiles), and
+//   gemm_wide_*   exact engine, 128x128-scaled B, N % 256 == 0, at most 92
+//                 K-blocks: dense and contiguous (256 x 256 tiles, the
+//                 interleaved schedule), long masked buffers (256 x 256), and
 //                 decode-sized masked buffers (gemm_wdec_*, 64 x 256 tiles);
 //                 the promotion is folded into the MFMA accumulator (below).
 //   gemm_wdect_*  the decode tile on weights in the decode-tiled layout
 //                 (written by tile_weights_decode): each half-block is one
 //                 contiguous 16 KB block in the stage's LDS order.
-//   gemm_wmix_*   dense grids planned as 256 x 256 tiles plus 256 x 192 tail
-//                 tiles, so both kinds fill whole rounds of the device's CUs.
 //   gemm_big_* / gemm_dec_*   the fold kernels described next: 1x128-scaled
-//                 B (Wgrad), the fp8mfma engine, and N = 128 mod 256.
+//                 B (Wgrad), the fp8mfma engine, N = 128 mod 256, and K
+//                 beyond the wide kernel's limit.
 //   gemm_mx_*     the MX variant (E8M0 scales applied inside the MFMA).
 //
 // Fold kernels.  A 512-thread workgroup computes a
@@ -63,8 +63,6 @@
 #include "launch.hpp"
 
 #include <stddef.h>
-#include <stdlib.h>
-#include <string.h>
 
 namespace fp8fg {
 
@@ -1485,338 +1483,6 @@ __device__ __forceinline__ void gemm_wide_sel(const GemmArgs& args, uint8_t* lds
 }
 
 // ---------------------------------------------------------------------------
-// Tail tiles of a dense grid.  448 tiles of 256 x 256 (4096 x 7168) fill 256
-// CUs 1.75 times, leaving a quarter of the chip idle for the second round.
-// The planner (dispatch) then covers the last columns with 256 x 192 tiles,
-// sized so that each kind fills whole rounds: 256 wide tiles, then 256 tail
-// tiles of three quarters of the work, in one launch.  The tail tile is the
-// wide kernel with waves 4 x 2 of 64 x 96 (FN = 3), so the VALU work per MFMA
-// barely changes.  It starts on a multiple of 64 columns and spans two
-// 128-wide n-blocks, and one wave column straddles them, so the B scale's
-// exponent part, the zero test and the accumulator unit are per 32-column
-// fragment.  12 B pieces per half-block: waves 0-3 copy two, waves 4-7 one.
-struct TailCfg {
-    static constexpr int WAVES_M = 4, WAVES_N = 2, FM = 2, FN = 3, STAGES = 4;
-    static constexpr int NW = WAVES_M * WAVES_N, THREADS = NW * 64;
-    static constexpr int BM = WAVES_M * FM * 32, BN = WAVES_N * FN * 32, KS = 64, ROWS_PER_PIECE = 16;
-    static constexpr int A_PER_WAVE = BM / ROWS_PER_PIECE / NW;
-    static constexpr int A_SCALE_WAVES = BM / 64, B_SCALE_WAVES = 2;   // the two n-blocks a tile touches
-    static_assert(BN == 192 && BN / ROWS_PER_PIECE == 12 && A_PER_WAVE == 2, "piece split below");
-};
-
-struct alignas(16) TStage {
-    uint8_t a[TailCfg::BM * TailCfg::KS];
-    uint8_t b[TailCfg::BN * TailCfg::KS];
-    float sa[TailCfg::BM];
-    float sb[TailCfg::B_SCALE_WAVES * 64];   // 64 copies of each n-block's scale
-    float dummy[64];
-};
-constexpr uint32_t tail_lds_bytes() { return uint32_t(TailCfg::STAGES * sizeof(TStage) + 64); }
-
-struct TailCopier {
-    rsrc_t ra, rb, rs;
-    uint32_t va[2], vb[2], vs;
-    uint32_t s_step;
-    int a_lds[2], b_lds[2], s_lds;
-    int a_c16[2], b_c16[2];
-    bool two_b;              // uniform: this wave copies two B pieces (waves 0-3) or one
-    int64_t K;
-
-    // as WideBufCopier::zero_tail
-    __device__ __forceinline__ void zero_tail(uint8_t* stage, int h, int lane) const {
-        const int64_t koff = int64_t(h) * TailCfg::KS;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            if (koff + a_c16[i] >= K) st<u32x4>(stage + a_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            if ((i == 0 || two_b) && koff + b_c16[i] >= K)
-                st<u32x4>(stage + b_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
-    }
-
-    // half-block h into `stage`: A pieces, B pieces, one scale piece (a dummy
-    // on waves 6 and 7) -- 5 loads on waves 0-3, 4 on waves 4-7
-    __device__ __forceinline__ void copy(uint8_t* stage, int h) const {
-        const uint32_t koff = uint32_t(h) * TailCfg::KS;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + a_lds[i]), 16, va[i], koff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[0]), 16, vb[0], koff, 0, 0);
-        if (two_b) __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[1]), 16, vb[1], koff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs, uint32_t(h >> 1) * s_step, 0, 0);
-    }
-};
-
-// t: dense tile (m0, rows_valid = M); n0: first column (a multiple of 64)
-__device__ __forceinline__ TailCopier make_tail_copier(const Tile& t, int wave, int lane, int64_t K, int64_t N,
-                                                       int64_t n0) {
-    typedef TailCfg W;
-    TailCopier c;
-    c.K = K;
-    c.two_b = wave < 4;
-    const int sub = lane >> 2, slot = lane & 3;
-    const int64_t tile_rows = t.rows_valid - t.m0 < W::BM ? t.rows_valid - t.m0 : W::BM;   // >= 1
-    c.ra = make_rsrc(t.A + t.m0 * K, uint32_t(tile_rows * K));
-    c.rb = make_rsrc(t.B + n0 * K, uint32_t(W::BN * K));
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r0 = (wave * 2 + i) * W::ROWS_PER_PIECE, r = r0 + sub;
-        const int chunk = slot ^ ((r >> 2) & 3);
-        const int64_t row = r < tile_rows ? r : tile_rows - 1;      // clamp: loaded, never stored
-        c.va[i] = uint32_t(row * K + chunk * 16);
-        c.a_c16[i] = chunk * 16;
-        c.a_lds[i] = int(offsetof(TStage, a)) + r0 * W::KS;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int piece = wave < 4 ? wave * 2 + i : 8 + (wave - 4);   // waves 4-7: one piece (i = 1 unused)
-        const int r0 = piece * W::ROWS_PER_PIECE, r = r0 + sub;
-        const int chunk = slot ^ ((r >> 2) & 3);
-        c.vb[i] = uint32_t(int64_t(r) * K + chunk * 16);
-        c.b_c16[i] = chunk * 16;
-        c.b_lds[i] = int(offsetof(TStage, b)) + r0 * W::KS;
-    }
-    const int64_t kbs = (K + BK - 1) / BK, nbs = (N + 127) / 128;
-    if (wave < W::A_SCALE_WAVES) {        // A scales of rows 64 wave .. +63 (clamped)
-        const int64_t rr = int64_t(wave) * 64 + lane;
-        const int64_t row = rr < tile_rows ? rr : tile_rows - 1;
-        c.rs = make_rsrc(t.SA + t.m0, uint32_t(((kbs - 1) * t.lda_s + tile_rows) * 4));
-        c.vs = uint32_t(row * 4);
-        c.s_step = uint32_t(t.lda_s * 4);
-        c.s_lds = int(offsetof(TStage, sa)) + wave * 64 * 4;
-    } else if (wave < W::A_SCALE_WAVES + W::B_SCALE_WAVES) {   // 64 copies of n-block n0/128 + j
-        const int j = wave - W::A_SCALE_WAVES;
-        int64_t nb = n0 / 128 + j;
-        nb = nb < nbs ? nb : nbs - 1;
-        c.rs = make_rsrc(t.SB + nb * kbs, uint32_t(kbs * 4));
-        c.vs = 0;
-        c.s_step = 4;
-        c.s_lds = int(offsetof(TStage, sb)) + j * 64 * 4;
-    } else {                              // padding: the tile's first A scale again
-        c.rs = make_rsrc(t.SA + t.m0, uint32_t(((kbs - 1) * t.lda_s + 1) * 4));
-        c.vs = 0;
-        c.s_step = uint32_t(t.lda_s * 4);
-        c.s_lds = int(offsetof(TStage, dummy));
-    }
-    return c;
-}
-
-// a K-block's scales for one wave of a tail tile, per 32-column fragment
-struct TailScales {
-    float pa[TailCfg::FM], pb[TailCfg::FN];
-    float unit[TailCfg::FM][TailCfg::FN];
-    int za[TailCfg::FM], zb[TailCfg::FN];   // codes read as +0: A scale 0 (per row), B scale 0 (per fragment)
-};
-
-// nsel[ni]: which of the tile's two n-blocks fragment ni lies in (uniform)
-__device__ __forceinline__ TailScales tail_scales(const TStage& sg, int wm, const int (&nsel)[TailCfg::FN], int r) {
-    TailScales w;
-    const float sb0 = sg.sb[0], sb1 = sg.sb[64];
-    const ScaleSplit b0 = split_scale(sb0), b1 = split_scale(sb1);
-    float bm[TailCfg::FN];
-#pragma unroll
-    for (int ni = 0; ni < TailCfg::FN; ++ni) {
-        w.pb[ni] = nsel[ni] ? b1.pow2 : b0.pow2;
-        bm[ni] = nsel[ni] ? b1.mant : b0.mant;
-        w.zb[ni] = (nsel[ni] ? sb1 : sb0) == 0.0f ? 1 : 0;
-    }
-#pragma unroll
-    for (int mi = 0; mi < TailCfg::FM; ++mi) {
-        const float sa = sg.sa[wm * TailCfg::FM * 32 + mi * 32 + r];
-        const ScaleSplit a = split_scale(sa);
-        w.pa[mi] = a.pow2;
-        w.za[mi] = sa == 0.0f ? 1 : 0;
-#pragma unroll
-        for (int ni = 0; ni < TailCfg::FN; ++ni) w.unit[mi][ni] = clamp_unit(a.mant * bm[ni]);
-    }
-    return w;
-}
-
-__device__ __forceinline__ void tail_rescale(v16f (&acc)[TailCfg::FM][TailCfg::FN], const TailScales& w,
-                                             const TailScales& nw) {
-#pragma unroll
-    for (int mi = 0; mi < TailCfg::FM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < TailCfg::FN; ++ni) {
-            const float ratio = clamp_unit(w.unit[mi][ni] * __builtin_amdgcn_rcpf(nw.unit[mi][ni]));
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[mi][ni][i] *= ratio;
-        }
-}
-
-// fragments of chunk column j (32 K) of stage slot `slot`, then its two k-steps
-__device__ __forceinline__ void tail_column(const uint8_t* lds, int slot, int j, int wm, int wn, int r, int h,
-                                            const TailScales& w, uint32_t zero_line,
-                                            v16f (&acc)[TailCfg::FM][TailCfg::FN]) {
-    typedef TailCfg W;
-    const uint32_t base = uint32_t(slot) * uint32_t(sizeof(TStage));
-    const uint32_t chunk = uint32_t(((2 * j + h) ^ ((r >> 2) & 3)) << 4);
-    u32x4 a[W::FM], b[W::FN];
-#pragma unroll
-    for (int mi = 0; mi < W::FM; ++mi) {
-        const uint32_t at = base + uint32_t(offsetof(TStage, a)) + uint32_t((wm * W::FM * 32 + mi * 32 + r) * W::KS) + chunk;
-        a[mi] = ld<u32x4>(lds + (w.za[mi] ? zero_line + chunk : at));
-    }
-#pragma unroll
-    for (int ni = 0; ni < W::FN; ++ni) {
-        const uint32_t bt = base + uint32_t(offsetof(TStage, b)) + uint32_t((wn * W::FN * 32 + ni * 32 + r) * W::KS) + chunk;
-        b[ni] = ld<u32x4>(lds + (w.zb[ni] ? zero_line + chunk : bt));
-    }
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        v8bf a8[W::FM], b8[W::FN];
-#pragma unroll
-        for (int mi = 0; mi < W::FM; ++mi) a8[mi] = widen8_scaled(a[mi][2 * half], a[mi][2 * half + 1], w.pa[mi]);
-#pragma unroll
-        for (int ni = 0; ni < W::FN; ++ni) b8[ni] = widen8_scaled(b[ni][2 * half], b[ni][2 * half + 1], w.pb[ni]);
-#pragma unroll
-        for (int mi = 0; mi < W::FM; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < W::FN; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8[ni], a8[mi], acc[mi][ni], 0, 0, 0);
-    }
-}
-
-// Dense tail tile `tile` of the 256 x 192 tiles covering columns [n_base, N)
-// (N - n_base a multiple of 192, n_base of 64); `lds_raw` holds tail_lds_bytes().
-// OUT: 0 = BF16, 1 = FP32.
-template <int OUT>
-__device__ __forceinline__ void gemm_tail_body(const GemmArgs& args, uint8_t* lds_raw, int64_t tile, int64_t n_base) {
-    typedef TailCfg W;
-    constexpr int FM = W::FM, FN = W::FN, STAGES = W::STAGES;
-    constexpr uint32_t kZeroLine = STAGES * sizeof(TStage);
-    TStage* ring = reinterpret_cast<TStage*>(lds_raw);
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / W::WAVES_N, wn = wave % W::WAVES_N;
-    const int64_t N = args.N, K = args.K;
-    const int halves = int(2 * ((K + BK - 1) / BK));
-    const int64_t n_tiles = (N - n_base) / W::BN;
-    Tile t;
-    t.m0 = (tile / n_tiles) * W::BM;
-    t.rows_valid = args.M;
-    t.lda_s = args.M;
-    t.c_base = 0;
-    t.A = args.a;
-    t.SA = args.sa;
-    t.B = args.b;
-    t.SB = args.sb;
-    t.bn = int(tile % n_tiles);
-    if (t.m0 >= t.rows_valid) return;
-    const int64_t n0 = n_base + int64_t(t.bn) * W::BN;
-    const TailCopier cp = make_tail_copier(t, wave, lane, K, N, n0);
-    const int64_t wrow0 = t.m0 + wm * FM * 32;
-    const bool live = wrow0 < t.rows_valid;   // uniform: this wave has valid rows
-    const int r = lane & 31, h = lane >> 5;
-    int nsel[FN];
-#pragma unroll
-    for (int ni = 0; ni < FN; ++ni) nsel[ni] = int(((n0 & 127) + wn * FN * 32 + ni * 32) >> 7);
-
-    if (tid < 4) st<u32x4>(lds_raw + kZeroLine + tid * 16, u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-    for (int st_ = 0; st_ < STAGES - 1; ++st_)
-        cp.copy(reinterpret_cast<uint8_t*>(&ring[st_]), st_ < halves ? st_ : halves - 1);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
-    v16f acc[FM][FN];
-#pragma unroll
-    for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
-    TailScales w;
-#pragma unroll
-    for (int mi = 0; mi < FM; ++mi) {
-        w.pa[mi] = 1.0f;
-        w.za[mi] = 0;
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni) w.unit[mi][ni] = 1.0f;
-    }
-#pragma unroll
-    for (int ni = 0; ni < FN; ++ni) {
-        w.pb[ni] = 1.0f;
-        w.zb[ni] = 0;
-    }
-
-    int slot = 0, fill_slot = STAGES - 1;
-    for (int hb = 0; hb < halves; hb += 2) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int cur = hb + e;
-            // this wave's copy of half-block cur has landed (5 or 4 loads per half-block)
-            if (cp.two_b)
-                wait_vmcnt<(STAGES - 2) * 5>();
-            else
-                wait_vmcnt<(STAGES - 2) * 4>();
-            if ((cur + 1) * W::KS > K) {      // partial last K-block (uniform)
-                cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[slot]), cur, lane);
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            }
-            __builtin_amdgcn_s_barrier();
-            const int fill = cur + STAGES - 1;
-            cp.copy(reinterpret_cast<uint8_t*>(&ring[fill_slot]), fill < halves ? fill : halves - 1);
-            if (live) {
-                if (e == 0) {
-                    const TailScales nw = tail_scales(ring[slot], wm, nsel, r);
-                    tail_rescale(acc, w, nw);
-                    w = nw;
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j) tail_column(lds_raw, slot, j, wm, wn, r, h, w, kZeroLine, acc);
-            }
-            slot = slot == STAGES - 1 ? 0 : slot + 1;
-            fill_slot = fill_slot == STAGES - 1 ? 0 : fill_slot + 1;
-        }
-    }
-    wait_vmcnt<0>();   // no copy may land after the workgroup's LDS is handed on
-
-    const int n_lane = wn * FN * 32 + 4 * h;
-#pragma unroll
-    for (int mi = 0; mi < FM; ++mi) {
-        const int64_t m = wrow0 + mi * 32 + r;
-        if (m >= t.rows_valid) continue;
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t idx = m * N + n0 + n_lane + ni * 32 + 8 * j;
-                const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
-                                  acc[mi][ni][4 * j + 3]} * w.unit[mi][ni];
-                if (OUT == 1) {
-                    st<v4f>(static_cast<float*>(args.c) + idx, v);
-                } else {
-                    const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-                    const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-                    st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
-                }
-            }
-    }
-}
-
-// One launch of a planned dense grid: workgroups [0, tiles1) take the 256 x
-// 256 tiles over columns [0, n_split), the rest the 256 x 192 tail tiles over
-// [n_split, N).  Both bodies share one LDS array.
-static_assert(tail_lds_bytes() <= wide_lds_bytes<WideTile>(), "the tail body fits the wide body's LDS");
-template <int OUT>
-__device__ __forceinline__ void gemm_wmix_body(const GemmArgs& args, int64_t tiles1, int64_t n_split) {
-    __shared__ __align__(16) uint8_t lds[wide_lds_bytes<WideTile>()];
-    if (int64_t(blockIdx.x) < tiles1)
-        gemm_wide_sel<WideTile, OUT, int(GemmMode::Dense)>(args, lds, blockIdx.x, n_split);
-    else
-        gemm_tail_body<OUT>(args, lds, int64_t(blockIdx.x) - tiles1, n_split);
-}
-__global__ __launch_bounds__(WideTile::THREADS) void gemm_wmix_o0_dense(GemmArgs args, int64_t tiles1,
-                                                                        int64_t n_split) {
-    gemm_wmix_body<0>(args, tiles1, n_split);
-}
-__global__ __launch_bounds__(WideTile::THREADS) void gemm_wmix_o1_dense(GemmArgs args, int64_t tiles1,
-                                                                        int64_t n_split) {
-    gemm_wmix_body<1>(args, tiles1, n_split);
-}
-
-// ---------------------------------------------------------------------------
 // MX GEMM (microscaled operands: E4M3 codes with one power-of-two E8M0 scale
 // per 32 consecutive K; the MX variant of the method, see quant.hip).
 // C = A . B^T, A codes [M][K] with scale bytes [K/32][M], B codes [N][K] with
@@ -2041,13 +1707,7 @@ __global__ __launch_bounds__(MxTile::THREADS) void gemm_mx_o1_dense(GemmArgs arg
     X(big_e1_b0_o0_dense, 0, 4, 2, 2, 2, 3, 1, 0, 0, 0)                    \
     X(big_e1_b0_o1_dense, 0, 4, 2, 2, 2, 3, 1, 0, 1, 0)                    \
     X(big_e1_b1_o0_dense, 0, 4, 2, 2, 2, 3, 1, 1, 0, 0)                    \
-    X(big_e1_b1_o1_dense, 0, 4, 2, 2, 2, 3, 1, 1, 1, 0)                    \
-    X(big_e1_b0_o0_contig, 0, 4, 2, 2, 2, 3, 1, 0, 0, 1)                   \
-    X(big_e1_b0_o1_contig, 0, 4, 2, 2, 2, 3, 1, 0, 1, 1)                   \
-    X(big_e1_b0_o0_masked, 0, 4, 2, 2, 2, 3, 1, 0, 0, 2)                   \
-    X(big_e1_b0_o1_masked, 0, 4, 2, 2, 2, 3, 1, 0, 1, 2)                   \
-    X(dec_e1_b0_o0_masked, 1, 2, 4, 1, 1, 3, 1, 0, 0, 2)                   \
-    X(dec_e1_b0_o1_masked, 1, 2, 4, 1, 1, 3, 1, 0, 1, 2)
+    X(big_e1_b1_o1_dense, 0, 4, 2, 2, 2, 3, 1, 1, 1, 0)
 
 #define FP8FG_DEFINE_KERNEL(NAME, TILE, WM, WN, FM, FN, ST, E, BS, OF, MODE)                  \
     __global__ __launch_bounds__(kThreads) void gemm_##NAME(GemmArgs args) {                  \
@@ -2127,112 +1787,37 @@ int64_t tile_count(GemmMode mode, const GemmArgs& args) {
 // The wide kernel addresses its operands through buffer descriptors with
 // 32-bit byte ranges: a 256-row slice of A or B (256 K bytes) and the A scale
 // array ((K / 128) * rows * 4 bytes) must each stay below 4 GiB, and its n-tile
-// is 256 wide.
+// is 256 wide.  It also keeps one FP32 accumulator over all of K, which takes
+// about eleven roundings per K-block (the eight MFMAs' sums and the unit
+// change, three), each at most 2^-24 of S, the running sum of |a b|: inside
+// the 2^-14 S contract for at most 92 K-blocks (11 * 92 + 1 <= 1024).  Longer
+// contractions run the fold kernel, whose block sums start from zero every
+// K-block (8 roundings of the block's own S, plus one per promotion).
+constexpr int64_t kWideMaxKBlocks = 92;
 bool wide_fits(const GemmArgs& args) {
-    if (args.N % WideTile::BN != 0 || args.K >= (int64_t(1) << 24)) return false;
+    if (args.N % WideTile::BN != 0 || (args.K + BK - 1) / BK > kWideMaxKBlocks) return false;
     return ((args.K + BK - 1) / BK) * args.M * 4 <= int64_t(0xFFFFFFFF);
-}
-
-// FP8FG_GEMM_WIDE=0 keeps the big tile for everything (comparison runs)
-bool wide_enabled() {
-    const char* e = getenv("FP8FG_GEMM_WIDE");
-    return !(e && e[0] == '0');
 }
 
 // gfx950 (MI350 series): eight XCDs, each with its own L2
 constexpr int kXcds = 8;
-// FP8FG_GEMM_XCD=0 keeps the masked layout's tiles in plain rank order (comparison runs)
-bool xcd_order_enabled() {
-    const char* e = getenv("FP8FG_GEMM_XCD");
-    return !(e && e[0] == '0');
-}
 // the masked layout's XCD grouping for tiles of bm rows: on when 8 divides the
-// (expert, m-tile) pair count
+// (expert, m-tile) pair count (the map is then a bijection)
 int masked_xcds(const GemmArgs& args, int64_t bm) {
-    return xcd_order_enabled() && (args.G * ((args.M + bm - 1) / bm)) % kXcds == 0 ? kXcds : 1;
-}
-
-// compute units of the current device (queried once per device)
-int cu_count() {
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cache[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cache[dev] = n;
-    }
-    return cache[dev];
-}
-
-// FP8FG_GEMM_TAIL: unset or "0" -> never plan tail tiles (their body has not
-// been given the interleaved schedule, and the plain grid is faster now);
-// "1" -> plan them when they fill whole rounds; "force" -> whenever the
-// columns split as 256 a + 192 b, b > 0 (read at every call; "force" exists to
-// exercise the tail tiles on small shapes)
-int tail_mode() {
-    const char* e = getenv("FP8FG_GEMM_TAIL");
-    if (e && strcmp(e, "1") == 0) return 1;
-    if (e && strcmp(e, "force") == 0) return 2;
-    return 0;
-}
-
-// Split of a dense wide grid into 256 x 256 tiles over columns [0, n_split)
-// and 256 x 192 tail tiles over [n_split, N).  Planned only when the 256 x 256
-// grid leaves a partial last round and both kinds fill whole rounds on the
-// device's CUs (a tail tile costs about 0.8 of a full one).
-bool plan_tail(const GemmArgs& args, int64_t& tiles1, int64_t& tiles2, int64_t& n_split) {
-    const int mode = tail_mode();
-    if (mode == 0 || args.N % 256 != 0) return false;
-    const int64_t mt = (args.M + WideTile::BM - 1) / WideTile::BM, nt = args.N / 256;
-    bool found = false;
-    if (mode == 2) {
-        for (int64_t a = nt - 1; a >= 0 && !found; --a)
-            if ((args.N - 256 * a) % TailCfg::BN == 0) {
-                tiles1 = mt * a;
-                tiles2 = mt * ((args.N - 256 * a) / TailCfg::BN);
-                n_split = 256 * a;
-                found = true;
-            }
-        return found;
-    }
-    const int64_t cus = cu_count();
-    if (cus <= 0 || (mt * nt) % cus == 0) return false;
-    double best = 0.97 * double((mt * nt + cus - 1) / cus);
-    for (int64_t a = 0; a < nt; ++a) {
-        const int64_t rem = args.N - 256 * a;
-        if (rem % TailCfg::BN) continue;
-        const int64_t t1 = mt * a, t2 = mt * (rem / TailCfg::BN);
-        if (t1 % cus || t2 % cus) continue;
-        const double cost = double(t1 / cus) + 0.8 * double(t2 / cus);
-        if (cost < best) {
-            best = cost;
-            tiles1 = t1;
-            tiles2 = t2;
-            n_split = 256 * a;
-            found = true;
-        }
-    }
-    return found;
+    return (args.G * ((args.M + bm - 1) / bm)) % kXcds == 0 ? kXcds : 1;
 }
 
 hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                     hipStream_t stream) {
-    // the exact engine on 128x128-scaled B with N a multiple of 256 runs the
+    // The exact engine on 128x128-scaled B with N a multiple of 256 runs the
     // wide kernel: 64 x 256 tiles for decode-sized masked buffers (at most
     // 128 rows), 256 x 256 tiles otherwise.  The rest (1x128 B scales, the
-    // FP8-MFMA engine, N = 128 mod 256) runs the fold kernel: 64 x 128 tiles
-    // for decode-sized masked buffers, 256 x 128 tiles otherwise.
-    // the FP8 output mode exists only in the wide exact kernel (the entry point
-    // checks that it fits)
-    const bool wide = out_fp32 == 2 || (engine == 0 && !bscale_1x128 && wide_fits(args) && wide_enabled());
+    // FP8-MFMA engine, N = 128 mod 256, more than kWideMaxKBlocks K-blocks)
+    // runs the fold kernel: 64 x 128 tiles for decode-sized masked buffers,
+    // 256 x 128 tiles otherwise.  The FP8 output mode exists only in the wide
+    // exact kernel (its entry point checks that it fits).
+    const bool wide = out_fp32 == 2 || (engine == 0 && !bscale_1x128 && wide_fits(args));
     if (out_fp32 == 2) engine = 0;
-    int64_t tiles1 = 0, tiles2 = 0, n_split = 0;
-    if (wide && mode == GemmMode::Dense && out_fp32 != 2 && args.M > 0 && plan_tail(args, tiles1, tiles2, n_split)) {
-        hipLaunchKernelGGL(out_fp32 ? gemm_wmix_o1_dense : gemm_wmix_o0_dense, dim3(unsigned(tiles1 + tiles2)),
-                           dim3(WideTile::THREADS), 0, stream, args, tiles1, n_split);
-        return hipGetLastError();
-    }
     int tile = 0;
     if (mode == GemmMode::Masked && args.M <= 128)
         tile = wide ? 3 : 1;
@@ -2249,33 +1834,24 @@ hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, c
                                    : tile == 1 ? DecodeTile::BM
                                    : tile == 2 ? WideTile::BM
                                                : WideDecodeTile::BM);
-    auto launch = [&](const KernelEntry& k) -> bool {
-        if (k.tile == tile && k.engine == engine && k.bscale == bscale_1x128 && k.out_fp32 == out_fp32 &&
-            k.mode == int(mode)) {
-            hipLaunchKernelGGL(k.fn, dim3(unsigned(tiles)), dim3(k.threads), 0, stream, a);
-            return true;
+    for (const KernelEntry* table : {kKernels, kWideKernels}) {
+        const size_t count = table == kKernels ? sizeof(kKernels) / sizeof(kKernels[0])
+                                               : sizeof(kWideKernels) / sizeof(kWideKernels[0]);
+        for (size_t i = 0; i < count; ++i) {
+            const KernelEntry& k = table[i];
+            if (k.tile == tile && k.engine == engine && k.bscale == bscale_1x128 && k.out_fp32 == out_fp32 &&
+                k.mode == int(mode))
+                return launch_kernel(k.fn, dim3(unsigned(tiles)), dim3(unsigned(k.threads)), stream, a);
         }
-        return false;
-    };
-    for (const KernelEntry& k : kKernels)
-        if (launch(k)) return hipGetLastError();
-    for (const KernelEntry& k : kWideKernels)
-        if (launch(k)) return hipGetLastError();
+    }
     return hipErrorInvalidValue;
-}
-
-// FP8FG_GEMM_ENGINE: unset or "exact" -> 0, "fp8mfma" -> 1 (read at every call)
-int engine_from_env() {
-    const char* e = getenv("FP8FG_GEMM_ENGINE");
-    return (e && strcmp(e, "fp8mfma") == 0) ? 1 : 0;
 }
 
 hipError_t launch_mx(int out_fp32, const GemmArgs& args, hipStream_t stream) {
     const int64_t tiles = ((args.M + MxTile::BM - 1) / MxTile::BM) * (args.N / MxTile::BN);
     if (tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(out_fp32 ? gemm_mx_o1_dense : gemm_mx_o0_dense, dim3(unsigned(tiles)), dim3(MxTile::THREADS),
-                       0, stream, args);
-    return hipGetLastError();
+    return launch_kernel(out_fp32 ? gemm_mx_o1_dense : gemm_mx_o0_dense, dim3(unsigned(tiles)),
+                         dim3(MxTile::THREADS), stream, args);
 }
 
 hipError_t launch_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream) {
@@ -2283,18 +1859,16 @@ hipError_t launch_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t s
     if (tiles == 0) return hipSuccess;
     GemmArgs a = args;
     a.xcds = masked_xcds(args, WideDecodeTile::BM);
-    hipLaunchKernelGGL(out_fp32 ? gemm_wdect_o1_masked : gemm_wdect_o0_masked, dim3(unsigned(tiles)),
-                       dim3(WideDecodeTile::THREADS), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(out_fp32 ? gemm_wdect_o1_masked : gemm_wdect_o0_masked, dim3(unsigned(tiles)),
+                         dim3(WideDecodeTile::THREADS), stream, a);
 }
 
 hipError_t launch_tile_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, uint8_t* out, hipStream_t stream) {
     const int64_t units = G * N * (K / 16);
     if (units == 0) return hipSuccess;
     const int64_t blocks = (units + 255) / 256;
-    hipLaunchKernelGGL(tile_weights_decode, dim3(unsigned(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream, q,
-                       K, units, out);
-    return hipGetLastError();
+    return launch_kernel(tile_weights_decode, dim3(unsigned(blocks < 65536 ? blocks : 65536)), dim3(256), stream, q, K,
+                         units, out);
 }
 
 }  // namespace gemm_detail
@@ -2312,9 +1886,9 @@ hipError_t launch_gemm_mx(int out_fp32, const GemmArgs& args, hipStream_t stream
     return gemm_detail::launch_mx(out_fp32, args, stream);
 }
 
-hipError_t launch_gemm(GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
+hipError_t launch_gemm(int engine, GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                        hipStream_t stream) {
-    return gemm_detail::dispatch(gemm_detail::engine_from_env(), mode, bscale_1x128, out_fp32, args, stream);
+    return gemm_detail::dispatch(engine, mode, bscale_1x128, out_fp32, args, stream);
 }
 
 }  // namespace fp8fg

@@ -5,7 +5,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fp8fg {
+
+// Launch `kernel` on `stream` and return the status of this launch itself.
+// (hipGetLastError() after a <<<>>> launch would also report an earlier,
+// unrelated error left in the runtime's last-error slot as this call's.)
+// The arguments are converted to the kernel's parameter types.
+template <typename... P>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                         typename std::common_type<P>::type... args) {
+    void* ptrs[] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, stream);
+}
 
 // x / w: fp32, or bf16 bit patterns when bf16 != 0
 hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, int transpose_out, uint8_t* q,
@@ -37,7 +50,8 @@ struct GemmArgs {
 
 // MX GEMM: args.sa / args.sb carry the E8M0 scale bytes ([K/32][M], [K/32][N])
 hipError_t launch_gemm_mx(int out_fp32, const GemmArgs& args, hipStream_t stream);
-hipError_t launch_gemm(GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
+// engine 0: exact (FP8 codes widened to BF16, BF16 MFMA); 1: FP8 MFMA on the codes
+hipError_t launch_gemm(int engine, GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                        hipStream_t stream);
 // the masked layout on decode-tiled B (M <= 128, N % 256 == 0, K % 64 == 0)
 hipError_t launch_gemm_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream);

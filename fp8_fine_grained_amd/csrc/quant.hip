@@ -499,9 +499,8 @@ hipError_t launch_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q, uin
     const int64_t chunks = (K + 255) / 256;
     int64_t row_groups = (R + 7) / 8;
     if (row_groups > 65535) row_groups = 65535;      // the kernel strides over the rest
-    hipLaunchKernelGGL(quant_mx_rows, dim3(unsigned(chunks), unsigned(row_groups)), dim3(256), 0, stream, x, R, K,
-                       q, e);
-    return hipGetLastError();
+    return launch_kernel(quant_mx_rows, dim3(unsigned(chunks), unsigned(row_groups)), dim3(256), stream, x, R, K, q,
+                         e);
 }
 
 // ---------------------------------------------------------------------------
@@ -569,12 +568,10 @@ static hipError_t launch_act(const T* x, int64_t M, int64_t K, int transpose_out
     if (!transpose_out) {
         int64_t chunks = 0, row_groups = 0;
         act_rows_grid<T>(M, K, chunks, row_groups);
-        hipLaunchKernelGGL(rows, dim3(unsigned(chunks), unsigned(row_groups)), dim3(256), 0, stream, x, M, K, q, s);
-    } else {
-        const dim3 grid(unsigned((M + kBlock - 1) / kBlock), unsigned((K + kTokCh - 1) / kTokCh));
-        hipLaunchKernelGGL(tokens, grid, dim3(256), 0, stream, x, M, K, q, s);
+        return launch_kernel(rows, dim3(unsigned(chunks), unsigned(row_groups)), dim3(256), stream, x, M, K, q, s);
     }
-    return hipGetLastError();
+    const dim3 grid(unsigned((M + kBlock - 1) / kBlock), unsigned((K + kTokCh - 1) / kTokCh));
+    return launch_kernel(tokens, grid, dim3(256), stream, x, M, K, q, s);
 }
 
 hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, int transpose_out, uint8_t* q,
@@ -589,8 +586,7 @@ hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, int t
 hipError_t launch_requant_act_tokens(const uint8_t* qr, const float* sr, int64_t M, int64_t K, uint8_t* q, float* s,
                                      hipStream_t stream) {
     const dim3 grid(unsigned((M + kBlock - 1) / kBlock), unsigned((K + kTokCh - 1) / kTokCh));
-    hipLaunchKernelGGL(requant_act_tokens, grid, dim3(256), 0, stream, qr, sr, M, K, q, s);
-    return hipGetLastError();
+    return launch_kernel(requant_act_tokens, grid, dim3(256), stream, qr, sr, M, K, q, s);
 }
 
 template <class TX, class TW>
@@ -602,9 +598,8 @@ static hipError_t launch_fprop(const TX* x, int64_t M, const TW* w, int64_t N, i
     act_rows_grid<TX, kFpropThreads>(M, K, chunks, row_groups);
     const int64_t w_blocks = ((K + kBlock - 1) / kBlock) * ((N + kBlock - 1) / kBlock);
     const int64_t blocks = w_blocks + chunks * row_groups;
-    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kFpropThreads), 0, stream, x, M, w, N, K, qa, sa, qb, sb,
-                       chunks, row_groups);
-    return hipGetLastError();
+    return launch_kernel(kern, dim3(unsigned(blocks)), dim3(kFpropThreads), stream, x, M, w, N, K, qa, sa, qb, sb,
+                         chunks, row_groups);
 }
 
 hipError_t launch_quant_fprop(const void* x, int x_bf16, int64_t M, const void* w, int w_bf16, int64_t N, int64_t K,
@@ -623,12 +618,10 @@ hipError_t launch_quant_weight(const void* w, int bf16, int64_t N, int64_t K, in
                                float* s, hipStream_t stream) {
     const dim3 grid(unsigned((K + kBlock - 1) / kBlock), unsigned((N + kBlock - 1) / kBlock));
     if (bf16)
-        hipLaunchKernelGGL(quant_weight_bf16, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(w), N, K,
-                           transpose_out, q, s);
-    else
-        hipLaunchKernelGGL(quant_weight_f32, grid, dim3(256), 0, stream, static_cast<const float*>(w), N, K,
-                           transpose_out, q, s);
-    return hipGetLastError();
+        return launch_kernel(quant_weight_bf16, grid, dim3(256), stream, static_cast<const uint16_t*>(w), N, K,
+                             transpose_out, q, s);
+    return launch_kernel(quant_weight_f32, grid, dim3(256), stream, static_cast<const float*>(w), N, K, transpose_out,
+                         q, s);
 }
 
 }  // namespace fp8fg

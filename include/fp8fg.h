@@ -52,11 +52,15 @@
  *     result C*:  |C - C*| <= 2^-14 * S  (FP32 out), with
  *     S = sum_k |decode(a) sA decode(b) sB|, plus one BF16 rounding of C*
  *     for BF16 out.  The codes are widened exactly to BF16 and multiplied on
- *     the BF16 matrix cores (exact products, FP32 sums).  The environment
- *     variable FP8FG_GEMM_ENGINE=fp8mfma (read at every call) selects the
- *     FP8 matrix-core engine instead: faster, but held only to 2^-9 * S,
- *     because gfx950's FP8 MFMA keeps about 14 bits when it sums each group
- *     of 8 products.  Results are deterministic (no atomics, no split-K).
+ *     the BF16 matrix cores (exact products, FP32 sums).  One call,
+ *     fp8_gemm_blockscaled_fp8mfma, runs the FP8 matrix cores instead and
+ *     has its own, looser contract (see there).  Results are deterministic
+ *     (no atomics, no split-K).  The library reads no environment variables.
+ *   - The 2^-14 * S contract is a worst-case bound: it counts at most 1024
+ *     FP32 roundings of quantities no larger than S.  The calls that take any
+ *     K keep it for K <= 114688 (896 K-blocks: fresh FP32 sums per K-block,
+ *     one rounding per promotion); beyond that it holds for the typical
+ *     (random-sign) accumulation, not in the worst case.
  */
 #ifndef FP8FG_H
 #define FP8FG_H
@@ -67,12 +71,12 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 7
+#define FP8FG_ABI_VERSION 8
 
 enum fp8fg_status {
     FP8FG_OK = 0,
     FP8FG_ERR_NULL = -1,         /* a required pointer is NULL                 */
-    FP8FG_ERR_SHAPE = -2,        /* negative size or a multiple-of-128 rule    */
+    FP8FG_ERR_SHAPE = -2,        /* negative size, or a size rule of the call  */
     FP8FG_ERR_ALIGN = -3,        /* a pointer is not 16-byte aligned           */
     FP8FG_ERR_UNSUPPORTED = -4,  /* unknown enum value or size beyond limits   */
     FP8FG_ERR_HIP = -5           /* the HIP runtime refused the launch         */
@@ -200,6 +204,26 @@ int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, co
                          int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * fp8_gemm_blockscaled on the FP8 matrix cores: the same arguments, layouts,
+ * rules and errors, and the same per-K-block promotion with the scale
+ * product applied at it ("The Insider Secrets Of Deepseek Discovered",
+ * passage on Figure 7(b)), but each K-block's partial sum P_kb comes from
+ * gfx950's FP8 MFMA (two 64-deep instructions per block) on the codes
+ * themselves, at twice the rate of the BF16 matrix cores.  That instruction
+ * adds its products in groups of eight consecutive K and keeps about 14
+ * significant bits of each group (every product truncated toward zero to
+ * 13 fractional bits below the group's largest exponent): the limited
+ * accumulation the same passage measures on H800 Tensor Cores, here inside
+ * one instruction, so promoting every 128 cannot remove it.
+ * Accuracy contract: |C - C*| <= 2^-9 * S (FP32 out), plus one BF16
+ * rounding of C* for BF16 out; the 2^-14 contract of every other call does
+ * not hold here.  Deterministic.
+ */
+int fp8_gemm_blockscaled_fp8mfma(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                 int bscale_kind, void* c, int out_dtype,
+                                 int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * Dense GEMM with the next layer's quantization fused into the epilogue
  * ("The Insider Secrets Of Deepseek Discovered", passage on Figure 6: with
  * every Linear in FP8, a layer's output is quantized again before it feeds
@@ -208,8 +232,10 @@ int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, co
  *   q: u8 [M][N], s: f32 [N/128][M] -- exactly fp8_quant_act_1x128 applied to
  *   the FP32 C that out_dtype = FP8FG_OUT_FP32 would write (same values, bit
  *   for bit), i.e. the A operand layout of a following GEMM with K = N.
- * Always the exact engine.  Requires N % 256 == 0, K % 16 == 0, K > 0 when
- * M * N > 0, K < 2^24, ceil(K/128) * M * 4 < 2^32.
+ * Requires N % 256 == 0, K % 16 == 0, K > 0 when M * N > 0, K <= 11776
+ * (92 K-blocks: this kernel keeps one FP32 accumulator over all of K, about
+ * eleven roundings per K-block, within the 2^-14 contract up to there; else
+ * FP8FG_ERR_UNSUPPORTED), ceil(K/128) * M * 4 < 2^32.
  */
 int fp8_gemm_blockscaled_fp8out(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                                 uint8_t* q, float* s, int64_t M, int64_t N, int64_t K, void* stream);
@@ -273,8 +299,8 @@ int fp8_tile_weights_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, u
  * fp8_grouped_gemm_masked on decode-tiled weights: the same operation, the
  * same arguments and the same result bit for bit, except that b_tiled holds
  * the experts' codes in the layout written by fp8_tile_weights_decode.
- * Always the exact engine (FP8FG_GEMM_ENGINE is not read).
- * Requires M_max <= 128, N % 256 == 0, K % 64 == 0, K > 0, K < 2^24, G >= 0.
+ * Requires M_max <= 128, N % 256 == 0, K % 64 == 0, K > 0, K <= 11776 (92
+ * K-blocks, as for fp8_gemm_blockscaled_fp8out), G >= 0.
  */
 int fp8_grouped_gemm_masked_tiled(const uint8_t* a, const float* sa, const uint8_t* b_tiled, const float* sb,
                                   const int32_t* masked_m, int64_t G, int64_t M_max,

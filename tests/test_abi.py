@@ -37,6 +37,7 @@ def test_abi_version_and_status_strings():
     assert fp8.status_string(0) == "ok"
     for code in (-1, -2, -3, -4, -5):
         assert fp8.status_string(code) not in ("ok", "unknown status")
+    assert "128" not in fp8.status_string(-2)            # the size rules differ by call (16, 32, 64, 128, 256)
     assert fp8.status_string(7) == "unknown status"
 
 
@@ -125,8 +126,9 @@ def test_mx_argument_errors():
     assert g(P, P, P, P, P, 0, 0, 256, 64, NUL) == OK
 
 
-def test_gemm_argument_errors():
-    g = fp8.load_library().fp8_gemm_blockscaled
+@pytest.mark.parametrize("name", ["fp8_gemm_blockscaled", "fp8_gemm_blockscaled_fp8mfma"])
+def test_gemm_argument_errors(name):
+    g = getattr(fp8.load_library(), name)
     assert g(P, P, P, NUL, 0, P, 0, 1, 128, 128, NUL) == ENULL
     assert g(P, P, P, P, 0, P, 0, 1, 100, 128, NUL) == ESHAPE     # N % 16
     assert g(P, P, P, P, 0, P, 0, 1, 128, 100, NUL) == ESHAPE     # K % 16
@@ -145,7 +147,8 @@ def test_fp8out_argument_errors():
     assert f(P, P, P, P, P, P2, 4, 256, 72, NUL) == ESHAPE      # K % 16
     assert f(P, P, P, P, P, P2, 4, 256, 0, NUL) == ESHAPE
     assert f(P, P, P, P, MIS, P2, 4, 256, 128, NUL) == EALIGN
-    assert f(P, P, P, P, P, P2, 0, 256, 128, NUL) == OK
+    assert f(P, P, P, P, P, P2, 4, 256, 92 * 128 + 16, NUL) == EUNSUP   # beyond 92 K-blocks (one accumulator)
+    assert f(P, P, P, P, P, P2, 0, 256, 92 * 128, NUL) == OK
 
 
 def test_grouped_argument_errors():
@@ -178,6 +181,7 @@ def test_decode_tiled_argument_errors():
     assert m(P, P, P, P, P, 4, 128, 128, 128, P, 0, NUL) == ESHAPE   # N % 256
     assert m(P, P, P, P, P, 4, 128, 256, 96, P, 0, NUL) == ESHAPE    # K % 64
     assert m(P, P, P, P, P, 4, 128, 256, 0, P, 0, NUL) == ESHAPE     # K = 0 with work to do
+    assert m(P, P, P, P, P, 4, 128, 256, 92 * 128 + 64, P, 0, NUL) == EUNSUP   # beyond 92 K-blocks
     assert m(P, P, MIS, P, P, 4, 128, 256, 128, P, 0, NUL) == EALIGN
     assert m(P, P, P, P, P, 4, 128, 256, 128, P, 2, NUL) == EUNSUP   # output dtype
     assert m(P, P, P, P, P, 4, 129, 256, 128, P, 0, NUL) == EUNSUP   # M_max > 128
@@ -210,8 +214,11 @@ int main(void) {
     int e1 = fp8_quant_act_1x128((const float*)0, 128, 128, 0, (uint8_t*)0, (float*)0, (void*)0);
     int e2 = fp8_gemm_blockscaled((const uint8_t*)16, (const float*)16, (const uint8_t*)16, (const float*)16,
                                   FP8FG_BSCALE_128x128, (void*)16, FP8FG_OUT_BF16, 4, 100, 128, (void*)0);
-    printf("%d %d %d %s\n", v, e1, e2, fp8fg_status_string(e2));
-    return v == FP8FG_ABI_VERSION && e1 == FP8FG_ERR_NULL && e2 == FP8FG_ERR_SHAPE ? 0 : 1;
+    int e3 = fp8_gemm_blockscaled_fp8mfma((const uint8_t*)16, (const float*)16, (const uint8_t*)16,
+                                          (const float*)0, FP8FG_BSCALE_1x128, (void*)16, FP8FG_OUT_FP32,
+                                          4, 128, 128, (void*)0);
+    printf("%d %d %d %d %s\n", v, e1, e2, e3, fp8fg_status_string(e2));
+    return v == FP8FG_ABI_VERSION && e1 == FP8FG_ERR_NULL && e2 == FP8FG_ERR_SHAPE && e3 == FP8FG_ERR_NULL ? 0 : 1;
 }
 """)
     libdir = os.path.dirname(fp8.LIB_PATH)

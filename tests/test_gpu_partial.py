@@ -111,13 +111,12 @@ def test_wgrad_partial_tokens(M, N, K):
     check(host64(c), *gemm.gemm_blockscaled_ref(qa, sa, qb, sb, "1x128"), "fp32", f"wgrad {M}x{N}x{K}")
 
 
-def test_fp8mfma_engine_partial_k(monkeypatch):
-    monkeypatch.setenv("FP8FG_GEMM_ENGINE", "fp8mfma")
+def test_fp8mfma_engine_partial_k():
     rng = np.random.default_rng(77)
     M, N, K = 130, 256, 336
     qa, sa = quant.quant_act_1x128(workloads.activations(rng, M, K, 0.01, 50.0))
     qb, sb = quant.quant_weight_128x128(workloads.weights(rng, N, K))
-    c = fp8.fp8_gemm_blockscaled(dev(qa), dev(sa), dev(qb), dev(sb), fp8.BSCALE_128x128, torch.float32)
+    c = fp8.fp8_gemm_blockscaled_fp8mfma(dev(qa), dev(sa), dev(qb), dev(sb), fp8.BSCALE_128x128, torch.float32)
     check(host64(c), *gemm.gemm_blockscaled_ref(qa, sa, qb, sb, "128x128"), "fp32", "fp8mfma partial",
           u=2.0 ** -9)
 
@@ -210,13 +209,12 @@ def test_wgrad_partial_n_and_tokens():
     check(host64(c), *gemm.gemm_blockscaled_ref(qa, sa, qb, sb, "1x128"), "fp32", "wgrad N=144")
 
 
-def test_fp8mfma_engine_partial_n(monkeypatch):
-    monkeypatch.setenv("FP8FG_GEMM_ENGINE", "fp8mfma")
+def test_fp8mfma_engine_partial_n():
     rng = np.random.default_rng(88)
     M, N, K = 130, 176, 256
     qa, sa = quant.quant_act_1x128(workloads.activations(rng, M, K, 0.01, 50.0))
     qb, sb = quant.quant_weight_128x128(workloads.weights(rng, N, K))
-    c = fp8.fp8_gemm_blockscaled(dev(qa), dev(sa), dev(qb), dev(sb), fp8.BSCALE_128x128, torch.float32)
+    c = fp8.fp8_gemm_blockscaled_fp8mfma(dev(qa), dev(sa), dev(qb), dev(sb), fp8.BSCALE_128x128, torch.float32)
     check(host64(c), *gemm.gemm_blockscaled_ref(qa, sa, qb, sb, "128x128"), "fp32", "fp8mfma N=176",
           u=2.0 ** -9)
 
