@@ -128,7 +128,7 @@ def _flush(stream):
     if "buf" not in _FLUSH:
         _FLUSH["buf"] = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
         _FLUSH["sum"] = torch.empty((), dtype=torch.float32, device="cuda")
-    torch.sum(_FLUSH["buf"], out=_FLUSH["sum"])
+    torch.sum(_FLUSH["buf"], dim=0, out=_FLUSH["sum"])
 
 
 def time_launches(fn, steps, warmup, stream):

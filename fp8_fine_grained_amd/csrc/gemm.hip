@@ -1089,6 +1089,115 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args, uint8_t* ld
 }
 
 // ---------------------------------------------------------------------------
+// Copies of the interleaved schedule.  Only the first CW waves of the
+// workgroup copy operand data (AP A pieces and BP B pieces of 1 KB each per
+// half-block); every wave keeps its scale piece.  The first waves of a
+// workgroup are the older ones on each SIMD, and the SIMD's issue arbiter
+// favours them: measured, they finish a half-block's MFMAs far ahead of the
+// younger waves and wait at the barrier, so a copy stalled on a full address
+// queue costs them slack instead of costing the younger waves MFMA issue.
+template <class W, int CW>
+struct IlCopier {
+    static constexpr int AP = W::BM / W::ROWS_PER_PIECE / CW, BP = W::BN / W::ROWS_PER_PIECE / CW;
+    static_assert(AP * W::ROWS_PER_PIECE * CW == W::BM && BP * W::ROWS_PER_PIECE * CW == W::BN, "whole pieces");
+    rsrc_t ra, rb, rs;
+    uint32_t va[AP], vb[BP], vs, s_step;
+    int a_lds[AP], b_lds[BP], s_lds;
+    int a_c16[AP], b_c16[BP];
+    int64_t K;
+    bool copier;               // uniform: this wave copies operand data
+
+    // piece i of half-block h: A pieces, then B pieces, then the scale piece,
+    // which carries the NEXT K-block's scales (h / 2 + 1; past the end of the
+    // scale array a range-checked load that reads zeros, never used)
+    __device__ __forceinline__ void copy_piece(uint8_t* stage, int h, int i) const {
+        const uint32_t koff = uint32_t(h) * W::KS;
+        if (i < AP)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + a_lds[i]), 16, va[i], koff, 0, 0);
+        else if (i < AP + BP)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i - AP]), 16, vb[i - AP], koff, 0,
+                                                     0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs,
+                                                     uint32_t((h >> 1) + 1) * s_step, 0, 0);
+    }
+    // the whole of this wave's share of half-block h
+    __device__ __forceinline__ void copy(uint8_t* stage, int h) const {
+        if (copier) {
+#pragma unroll
+            for (int i = 0; i < AP + BP; ++i) copy_piece(stage, h, i);
+        }
+        copy_piece(stage, h, AP + BP);
+    }
+    // after this wave's loads of half-block h have landed: zero its 16-byte
+    // slots past K (a partial last K-block; the loads read whatever lies
+    // there -- the next row, or zeros past the buffer's range)
+    __device__ __forceinline__ void zero_tail(uint8_t* stage, int h, int lane) const {
+        if (!copier) return;
+        const int64_t koff = int64_t(h) * W::KS;
+#pragma unroll
+        for (int i = 0; i < AP; ++i)
+            if (koff + a_c16[i] >= K) st<u32x4>(stage + a_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+        for (int i = 0; i < BP; ++i)
+            if (koff + b_c16[i] >= K) st<u32x4>(stage + b_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
+    }
+};
+
+template <class W, int CW>
+__device__ __forceinline__ IlCopier<W, CW> make_il_copier(const Tile& t, int wave, int lane, int64_t K, int64_t n0) {
+    typedef WStage<W> S;
+    typedef IlCopier<W, CW> C;
+    C c;
+    c.K = K;
+    c.copier = wave < CW;
+    const int cw = c.copier ? wave : 0;     // non-copying waves set up (unused) offsets of wave 0
+    const int sub = lane >> 2, slot = lane & 3;
+    const int64_t tile_rows = t.rows_valid - t.m0 < W::BM ? t.rows_valid - t.m0 : W::BM;   // >= 1
+    c.ra = make_rsrc(t.A + t.m0 * K, uint32_t(tile_rows * K));
+    c.rb = make_rsrc(t.B + n0 * K, uint32_t(W::BN * K));
+#pragma unroll
+    for (int i = 0; i < C::AP; ++i) {
+        const int r0 = (cw * C::AP + i) * W::ROWS_PER_PIECE, r = r0 + sub;
+        const int chunk = slot ^ ((r >> 2) & 3);
+        const int64_t row = r < tile_rows ? r : tile_rows - 1;      // clamp: loaded, never stored
+        c.va[i] = uint32_t(row * K + chunk * 16);
+        c.a_c16[i] = chunk * 16;
+        c.a_lds[i] = int(offsetof(S, a)) + r0 * W::KS;
+    }
+#pragma unroll
+    for (int i = 0; i < C::BP; ++i) {
+        const int r0 = (cw * C::BP + i) * W::ROWS_PER_PIECE, r = r0 + sub;
+        const int chunk = slot ^ ((r >> 2) & 3);
+        c.vb[i] = uint32_t(int64_t(r) * K + chunk * 16);
+        c.b_c16[i] = chunk * 16;
+        c.b_lds[i] = int(offsetof(S, b)) + r0 * W::KS;
+    }
+    const int64_t kbs = (K + BK - 1) / BK;
+    if (wave < W::A_SCALE_WAVES) {        // A scales of rows 64 wave .. +63 (clamped)
+        const int64_t rr = int64_t(wave) * 64 + lane;
+        const int64_t row = rr < tile_rows ? rr : tile_rows - 1;
+        c.rs = make_rsrc(t.SA + t.m0, uint32_t(((kbs - 1) * t.lda_s + tile_rows) * 4));
+        c.vs = uint32_t(row * 4);
+        c.s_step = uint32_t(t.lda_s * 4);
+        c.s_lds = int(offsetof(S, sa)) + wave * 64 * 4;
+    } else if (wave < W::A_SCALE_WAVES + W::B_SCALE_WAVES) {   // 64 copies of an n-block's scale
+        const int j = wave - W::A_SCALE_WAVES;
+        c.rs = make_rsrc(t.SB + (n0 / 128 + j) * kbs, uint32_t(kbs * 4));
+        c.vs = 0;
+        c.s_step = 4;
+        c.s_lds = int(offsetof(S, sb)) + j * 64 * 4;
+    } else {                              // padding: the tile's first A scale again
+        c.rs = make_rsrc(t.SA + t.m0, uint32_t(((kbs - 1) * t.lda_s + 1) * 4));
+        c.vs = 0;
+        c.s_step = uint32_t(t.lda_s * 4);
+        c.s_lds = int(offsetof(S, dummy));
+    }
+    return c;
+}
+constexpr int IL_COPY_WAVES = 4;
+
+// ---------------------------------------------------------------------------
 // Interleaved schedule of the wide exact kernel (dense and contiguous layouts).
 //
 // Measured on gfx950 (one 32x32x16 BF16 MFMA every 32 cycles per SIMD, with
@@ -1207,11 +1316,11 @@ __device__ __forceinline__ uint32_t widen_q(const u32x4& raw, int hh, int q, flo
 // Even half-blocks also turn the stage's scale piece (the next K-block's
 // scales) into `next`: its LDS reads go out with the fragment reads, its
 // arithmetic runs in four slots of the last group, whose room the plan keeps.
-template <class W, int ODD>
+template <class W, int ODD, bool COPIER>
 __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int wn, int r, int h,
                                              const WideScales<W::FM>& w, const float (&ratio)[W::FM],
                                              uint32_t zero_line, v16f (&acc)[W::FM][W::FN],
-                                             WideScales<W::FM>& next, const WideBufCopier<W, false>& cp,
+                                             WideScales<W::FM>& next, const IlCopier<W, IL_COPY_WAVES>& cp,
                                              int fill_slot, int fill_h, int pf_slot, u32x4 (&pfa)[W::FM][2],
                                              u32x4 (&pfb)[IL_GW][2]) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device code only: the host pass never runs it
@@ -1277,8 +1386,10 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
                 for (int i = 0; i < 16; ++i)
                     if (P.m[mi][g][i] == n) acc[mi][g][i] *= ratio[mi];
     };
-    // the copy of half-block fill_h, one piece every few MFMAs
-    constexpr int PIECES = W::A_PER_WAVE + W::B_PER_WAVE + 1, PSTRIDE = NS / PIECES;
+    // this wave's share of the copy of half-block fill_h, one piece every few
+    // MFMAs (the last piece is the scale piece; data only on copying waves)
+    typedef IlCopier<W, IL_COPY_WAVES> Cp;
+    constexpr int PIECES = COPIER ? Cp::AP + Cp::BP + 1 : 1, PSTRIDE = NS / PIECES;
     uint8_t* fill_stage = lds + uint32_t(fill_slot) * uint32_t(sizeof(WStage<W>));
     valu(-1);
     __builtin_amdgcn_sched_barrier(0);
@@ -1288,7 +1399,8 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
         const int k = (n % PG) / (FM * IL_GW), mi = (n % (FM * IL_GW)) / IL_GW, g = (n / PG) * IL_GW + n % IL_GW;
         acc[mi][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, cb[g][k]),
                                                              __builtin_bit_cast(v8bf, ca[mi][k]), acc[mi][g], 0, 0, 0);
-        if (n % PSTRIDE == 1 && n / PSTRIDE < PIECES) cp.copy_piece(fill_stage, fill_h, n / PSTRIDE);
+        if (n % PSTRIDE == 1 && n / PSTRIDE < PIECES)
+            cp.copy_piece(fill_stage, fill_h, COPIER ? n / PSTRIDE : Cp::AP + Cp::BP);
         if (!ODD && n == NS / 2 + 2) {
             // the odd half-block's first fragments, into registers the first
             // group of this one no longer needs
@@ -1322,6 +1434,48 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
 #endif
 }
 
+// The K-loop of gemm_wide_il_body for one copy role (a template parameter, so
+// each role's half-blocks are straight-line code with its own copy slots).
+template <class W, bool COPIER>
+__device__ __forceinline__ void il_kloop(uint8_t* lds_raw, WStage<W>* ring, const IlCopier<W, IL_COPY_WAVES>& cp,
+                                         int halves, int64_t K, int wm, int wn, int r, int h, int lane, bool live,
+                                         WideScales<W::FM>& w, WideScales<W::FM>& nw, float (&ratio)[W::FM],
+                                         v16f (&acc)[W::FM][W::FN]) {
+    constexpr int FM = W::FM;
+    constexpr uint32_t kZeroLine = W::STAGES * sizeof(WStage<W>);
+    u32x4 pfa[FM][2], pfb[IL_GW][2];   // an odd half-block's first fragments, read ahead
+
+    for (int hb = 0; hb < halves; hb += 2) {
+        // both halves of this K-block have landed (this wave's copies: the
+        // only loads in flight), then every wave's
+        wait_vmcnt<0>();
+        if ((hb + 2) * W::KS > K) {           // partial last K-block (uniform)
+            cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[hb & 3]), hb, lane);
+            cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[(hb + 1) & 3]), hb + 1, lane);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        __builtin_amdgcn_s_barrier();
+        // the next K-block's halves (past the end: the last half again, into
+        // slots never read again)
+        const int f0 = hb + 2 < halves ? hb + 2 : halves - 1, f1 = hb + 3 < halves ? hb + 3 : halves - 1;
+        if (live) {
+            w = nw;
+            // the even slot's scale piece holds the next K-block's scales
+            wide_il_half<W, 0, COPIER>(lds_raw, hb & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 2) & 3, f0,
+                               (hb + 1) & 3, pfa, pfb);
+            const bool more = hb + 2 < halves;
+#pragma unroll
+            for (int mi = 0; mi < FM; ++mi)
+                ratio[mi] = more ? clamp_unit(w.unit[mi] * __builtin_amdgcn_rcpf(nw.unit[mi])) : 1.0f;
+            wide_il_half<W, 1, COPIER>(lds_raw, (hb + 1) & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 3) & 3,
+                               f1, 0, pfa, pfb);
+        } else {
+            cp.copy(reinterpret_cast<uint8_t*>(&ring[(hb + 2) & 3]), f0);
+            cp.copy(reinterpret_cast<uint8_t*>(&ring[(hb + 3) & 3]), f1);
+        }
+    }
+}
+
 template <class W, int OUT, int MODE>
 __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t* lds_raw, int64_t tile, int64_t n_ext) {
     static_assert(MODE != int(GemmMode::Masked), "dense and contiguous layouts");
@@ -1338,7 +1492,7 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
     const Tile t = map_tile<W, MODE>(args, tile, n_ext);
     if (!t.live) return;
     const int64_t n0 = int64_t(t.bn) * W::BN;
-    const WideBufCopier<W, false> cp = make_wide_buf_copier<W, false>(t, wave, lane, K, n0);
+    const IlCopier<W, IL_COPY_WAVES> cp = make_il_copier<W, IL_COPY_WAVES>(t, wave, lane, K, n0);
     const int64_t wrow0 = t.m0 + wm * FM * 32;
     const bool live = wrow0 < t.rows_valid;   // uniform
     const int r = lane & 31, h = lane >> 5;
@@ -1359,8 +1513,8 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
     // 2kb % 4 + 1; the copies of K-block kb + 1 run during kb's MFMAs, into
     // the slots of kb - 1, which every wave has finished by kb's barrier
     static_assert(STAGES == 4, "two K-blocks of half-block slots");
-    cp.copy(reinterpret_cast<uint8_t*>(&ring[0]), 0, 0, false, true);
-    cp.copy(reinterpret_cast<uint8_t*>(&ring[1]), 1, 1, false, true);
+    cp.copy(reinterpret_cast<uint8_t*>(&ring[0]), 0);
+    cp.copy(reinterpret_cast<uint8_t*>(&ring[1]), 1);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
     v16f acc[FM][FN];
@@ -1388,37 +1542,10 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
     float ratio[FM];
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi) ratio[mi] = 1.0f;
-    u32x4 pfa[FM][2], pfb[IL_GW][2];   // an odd half-block's first fragments, read ahead
-
-    for (int hb = 0; hb < halves; hb += 2) {
-        // both halves of this K-block have landed (this wave's copies: the
-        // only loads in flight), then every wave's
-        wait_vmcnt<0>();
-        if ((hb + 2) * W::KS > K) {           // partial last K-block (uniform)
-            cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[hb & 3]), hb, lane);
-            cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[(hb + 1) & 3]), hb + 1, lane);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        }
-        __builtin_amdgcn_s_barrier();
-        // the next K-block's halves (past the end: the last half again, into
-        // slots never read again)
-        const int f0 = hb + 2 < halves ? hb + 2 : halves - 1, f1 = hb + 3 < halves ? hb + 3 : halves - 1;
-        if (live) {
-            w = nw;
-            // the even slot's scale piece holds the next K-block's scales
-            wide_il_half<W, 0>(lds_raw, hb & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 2) & 3, f0,
-                               (hb + 1) & 3, pfa, pfb);
-            const bool more = hb + 2 < halves;
-#pragma unroll
-            for (int mi = 0; mi < FM; ++mi)
-                ratio[mi] = more ? clamp_unit(w.unit[mi] * __builtin_amdgcn_rcpf(nw.unit[mi])) : 1.0f;
-            wide_il_half<W, 1>(lds_raw, (hb + 1) & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 3) & 3,
-                               f1, 0, pfa, pfb);
-        } else {
-            cp.copy(reinterpret_cast<uint8_t*>(&ring[(hb + 2) & 3]), f0, f0, false, true);
-            cp.copy(reinterpret_cast<uint8_t*>(&ring[(hb + 3) & 3]), f1, f1, false, true);
-        }
-    }
+    if (cp.copier)
+        il_kloop<W, true>(lds_raw, ring, cp, halves, K, wm, wn, r, h, lane, live, w, nw, ratio, acc);
+    else
+        il_kloop<W, false>(lds_raw, ring, cp, halves, K, wm, wn, r, h, lane, live, w, nw, ratio, acc);
     wait_vmcnt<0>();
 
     const int n_lane = wn * FN * 32 + 4 * h;
