@@ -54,11 +54,13 @@ def parse():
     p.add_argument("--settle-s", type=float, default=0.5,
                    help="seconds of untimed steps before the warmup steps (clock settling)")
     p.add_argument("--profile-kernel", choices=["gemm", "quant_act", "quant_weight", "quant_fprop", "copy", "masked",
-                                                "masked_tiled"],
-                   help="counter-collection driver: launch only this kernel `steps` times on the "
-                        "dense_fprop inputs (copy: a 1 GiB device-to-device copy, the byte-counter "
-                        "calibration; masked / masked_tiled: the masked decode gate+up GEMM on plain / "
-                        "decode-tiled weights); prints no JSON")
+                                                "masked_tiled", "masked_down", "masked_down_tiled", "trio_fprop",
+                                                "trio_dgrad", "trio_wgrad", "contig"],
+                   help="counter-collection driver: launch only this kernel `steps` times (gemm, quant_*: on "
+                        "the dense_fprop inputs; copy: a 1 GiB device-to-device copy, the byte-counter "
+                        "calibration; masked*: the masked decode GEMM, gate+up or down shape, on plain / "
+                        "decode-tiled weights; trio_*: the linear_trio GEMMs; contig: the moe_contig "
+                        "gate+up GEMM); prints no JSON")
     p.add_argument("--workload", default="dense_fprop",
                    choices=["dense_fprop", "dense_small", "linear_trio", "moe_contig", "moe_masked", "dense_mx"],
                    help="dense_fprop is the headline step; the others print one line per measured kernel")
@@ -219,6 +221,97 @@ def masked_inputs(gen, G, MMAX, N, K):
     return mm, qa, sa, qb, sb, mmt, c
 
 
+def trio_inputs(gen):
+    """The linear_trio tensors on the GPU (8192 tokens, 7168 in, 2048 out):
+    activations with outlier channels, weights, upstream gradients."""
+    import torch
+    TOK, IN, OUT = 8192, 7168, 2048
+    x = gpu_acts(gen, TOK, IN, 0.001, 100.0)
+    w = torch.randn((OUT, IN), generator=gen, device="cuda") * 0.02
+    dy = torch.randn((TOK, OUT), generator=gen, device="cuda") * 1e-3
+    return x, w, dy
+
+
+def contig_inputs(gen):
+    """The moe_contig gate+up GEMM's operands on the GPU: 32 experts' rows in
+    128-aligned segments (seeded counts), 1x128-quantized, and 32 experts'
+    128x128-quantized 4096x7168 weights."""
+    import torch
+    import fp8_fine_grained_amd as fp8
+    import workloads
+    G, N, K = 32, 4096, 7168
+    counts, off = workloads.moe_contig_layout()
+    mt = int(off[-1])
+    a = torch.zeros((mt, K), device="cuda")
+    xa = gpu_acts(gen, int(counts.sum()), K, 0.001, 100.0)
+    pos = 0
+    for g in range(G):
+        a[int(off[g]):int(off[g]) + int(counts[g])] = xa[pos:pos + int(counts[g])]
+        pos += int(counts[g])
+    del xa
+    qa, sa = fp8.fp8_quant_act_1x128(a)
+    qb = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device="cuda")
+    for g in range(G):
+        wg = torch.randn((N, K), generator=gen, device="cuda") * 0.02
+        fp8.fp8_quant_weight_128x128(wg, q=qb[g], s=sb[g])
+    offs = torch.from_numpy(off.astype(np.int32)).cuda()
+    return a, qa, sa, qb, sb, offs, counts, mt
+
+
+def profile_other(args):
+    """Counter-collection driver for the masked decode GEMMs (both shapes),
+    the linear_trio GEMMs and the contiguous grouped GEMM: build that
+    workload's inputs, then launch only the named kernel `steps` times."""
+    import torch
+    import fp8_fine_grained_amd as fp8
+    import workloads
+    fp8.load_library()
+    k = args.profile_kernel
+    if k.startswith("masked"):
+        gen = torch.Generator(device="cuda").manual_seed(workloads.SEEDS.get("moe_masked", 105))
+        N, K = (7168, 2048) if k.startswith("masked_down") else (4096, 7168)
+        mm, qa, sa, qb, sb, mmt, c = masked_inputs(gen, 32, 128, N, K)
+        if k.endswith("_tiled"):
+            qb = fp8.fp8_tile_weights_decode(qb)
+            fn = lambda: fp8.fp8_grouped_gemm_masked_tiled(qa, sa, qb, sb, mmt, out=c)
+        else:
+            fn = lambda: fp8.fp8_grouped_gemm_masked(qa, sa, qb, sb, mmt, out=c)
+        what = f"N={N} K={K}, valid rows {int(mm.sum())}"
+    elif k.startswith("trio_"):
+        gen = torch.Generator(device="cuda").manual_seed(workloads.SEEDS.get("linear_trio", 1))
+        x, w, dy = trio_inputs(gen)
+        if k == "trio_fprop":
+            qx, sx = fp8.fp8_quant_act_1x128(x)
+            qw, sw = fp8.fp8_quant_weight_128x128(w)
+            c = torch.empty((x.shape[0], w.shape[0]), dtype=torch.bfloat16, device="cuda")
+            fn = lambda: fp8.fp8_gemm_blockscaled(qx, sx, qw, sw, 0, torch.bfloat16, out=c)
+        elif k == "trio_dgrad":
+            qd, sd = fp8.fp8_quant_act_1x128(dy)
+            qwt, swt = fp8.fp8_quant_weight_128x128(w, transpose_out=True)
+            c = torch.empty((x.shape[0], x.shape[1]), dtype=torch.bfloat16, device="cuda")
+            fn = lambda: fp8.fp8_gemm_blockscaled(qd, sd, qwt, swt, 0, torch.bfloat16, out=c)
+        else:
+            qdt, sdt = fp8.fp8_quant_act_1x128(dy, transpose_out=True)
+            qxt, sxt = fp8.fp8_quant_act_1x128(x, transpose_out=True)
+            c = torch.empty((w.shape[0], w.shape[1]), dtype=torch.float32, device="cuda")
+            fn = lambda: fp8.fp8_gemm_blockscaled(qdt, sdt, qxt, sxt, 1, torch.float32, out=c)
+        del x, w, dy
+        what = "8192 tokens, 7168 in, 2048 out"
+    else:
+        gen = torch.Generator(device="cuda").manual_seed(workloads.SEEDS.get("moe_contig", 1))
+        a, qa, sa, qb, sb, offs, counts, mt = contig_inputs(gen)
+        del a
+        c = torch.empty((mt, qb.shape[1]), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: fp8.fp8_grouped_gemm_contiguous(qa, sa, qb, sb, offs, out=c)
+        what = f"{mt} padded rows, {int(counts.sum())} routed"
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        fn()
+    torch.cuda.synchronize()
+    print(f"profiled {k} x{args.steps} ({what})", flush=True)
+
+
 def masked_decode_rates(args):
     """HBM rate of the masked-layout decode GEMM on both MoE shapes (gate+up
     K=7168 N=4096, down K=2048 N=7168; 32 experts, 128-row buffers, U{1..64}
@@ -252,26 +345,6 @@ def masked_decode_rates(args):
                    "the decode-tiled layout (fp8_tile_weights_decode, arranged once at load time); target >= 0.70 "
                    "of the 8 TB/s HBM peak")
     return out
-
-
-def profile_masked(args):
-    """Counter-collection driver for the masked decode GEMM (gate+up shape):
-    launch only that kernel `steps` times, on plain or decode-tiled weights."""
-    import torch
-    import fp8_fine_grained_amd as fp8
-    fp8.load_library()
-    gen = torch.Generator(device="cuda").manual_seed(0)
-    mm, qa, sa, qb, sb, mmt, c = masked_inputs(gen, 32, 128, 4096, 7168)
-    if args.profile_kernel == "masked_tiled":
-        qb = fp8.fp8_tile_weights_decode(qb)
-        fn = fp8.fp8_grouped_gemm_masked_tiled
-    else:
-        fn = fp8.fp8_grouped_gemm_masked
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        fn(qa, sa, qb, sb, mmt, out=c)
-    torch.cuda.synchronize()
-    print(f"profiled {args.profile_kernel} x{args.steps} (valid rows {int(mm.sum())})", flush=True)
 
 
 def run_extra(args):
@@ -311,9 +384,7 @@ def run_extra(args):
                    peak="FP8 (scaled MFMA)")
     elif args.workload == "linear_trio":
         TOK, IN, OUT = 8192, 7168, 2048
-        x = gpu_acts(gen, TOK, IN, 0.001, 100.0)
-        w = torch.randn((OUT, IN), generator=gen, device="cuda") * 0.02
-        dy = torch.randn((TOK, OUT), generator=gen, device="cuda") * 1e-3
+        x, w, dy = trio_inputs(gen)
         qx, sx = fp8.fp8_quant_act_1x128(x)
         qw, sw = fp8.fp8_quant_weight_128x128(w)
         qwt, swt = fp8.fp8_quant_weight_128x128(w, transpose_out=True)
@@ -362,22 +433,7 @@ def run_extra(args):
         extra_line("linear_trio", "gemm Wgrad 2048x7168x8192 FP32 (1x128 B)", ms, flops=fl, args=args, config=cfg)
     elif args.workload == "moe_contig":
         G, N, K = 32, 4096, 7168
-        counts, off = workloads.moe_contig_layout()
-        mt = int(off[-1])
-        a = torch.zeros((mt, K), device="cuda")
-        xa = gpu_acts(gen, int(counts.sum()), K, 0.001, 100.0)
-        pos = 0
-        for g in range(G):
-            a[int(off[g]):int(off[g]) + int(counts[g])] = xa[pos:pos + int(counts[g])]
-            pos += int(counts[g])
-        del xa
-        qa, sa = fp8.fp8_quant_act_1x128(a)
-        qb = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
-        sb = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device="cuda")
-        for g in range(G):
-            wg = torch.randn((N, K), generator=gen, device="cuda") * 0.02
-            fp8.fp8_quant_weight_128x128(wg, q=qb[g], s=sb[g])
-        offs = torch.from_numpy(off.astype(np.int32)).cuda()
+        a, qa, sa, qb, sb, offs, counts, mt = contig_inputs(gen)
         c = torch.empty((mt, N), dtype=torch.bfloat16, device="cuda")
         cfg = {"experts": G, "routed_rows": int(counts.sum()), "padded_rows": mt, "N": N, "K": K}
         ms = time_launches(lambda i: fp8.fp8_quant_act_1x128(a, q=qa, s=sa), T, W, stream)
@@ -411,8 +467,8 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
         sys.exit(2)
     _SETTLE["seconds"] = args.settle_s
-    if args.profile_kernel in ("masked", "masked_tiled"):
-        profile_masked(args)
+    if args.profile_kernel and (args.profile_kernel.startswith(("masked", "trio_")) or args.profile_kernel == "contig"):
+        profile_other(args)
         return
     if args.workload != "dense_fprop":
         run_extra(args)

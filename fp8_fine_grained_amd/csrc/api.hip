@@ -248,6 +248,8 @@ int fp8_grouped_gemm_masked_tiled(const uint8_t* a, const float* sa, const uint8
     // the decode tile: buffers of at most 128 rows; 256 K bytes per n-tile stay below 4 GiB
     if (M_max > 128 || N > kMaxDim || (K + 127) / 128 > kWideMaxKBlocks || G > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
     if (N > 0 && G > kMaxDim / (2 * (N / 256))) return FP8FG_ERR_UNSUPPORTED;
+    // the decode kernel ranks at most 4096 (expert, 64-row m-tile) pairs
+    if (G * ((M_max + 63) / 64) > 4096) return FP8FG_ERR_UNSUPPORTED;
     if (G == 0 || M_max == 0 || N == 0) return FP8FG_OK;
     fp8fg::GemmArgs args{a, sa, b_tiled, sb, c, masked_m, M_max, N, K, G};
     return hip_status(fp8fg::launch_gemm_masked_tiled(out_dtype == FP8FG_OUT_FP32, args,

@@ -32,9 +32,9 @@
 //                 interleaved schedule), long masked buffers (256 x 256), and
 //                 decode-sized masked buffers (gemm_wdec_*, 64 x 256 tiles);
 //                 the promotion is folded into the MFMA accumulator (below).
-//   gemm_wdect_*  the decode tile on weights in the decode-tiled layout
-//                 (written by tile_weights_decode): each half-block is one
-//                 contiguous 16 KB block in the stage's LDS order.
+//   gemm_dreg_*   persistent decode kernel on weights in the decode-tiled
+//                 layout (written by tile_weights_decode): register-streamed
+//                 weight fragments, the wide kernel's arithmetic.
 //   gemm_big_* / gemm_dec_*   the fold kernels described next: 1x128-scaled
 //                 B (Wgrad), the fp8mfma engine, N = 128 mod 256, and K
 //                 beyond the wide kernel's limit.
@@ -643,8 +643,8 @@ struct WCfg {
 };
 // dense / contiguous / long masked buffers: 256 x 256, waves 4 x 2 of 64 x 128
 typedef WCfg<4, 2, 2, 4, 4> WideTile;
-// decode-sized masked buffers: 64 x 256, waves 1 x 4 of 64 x 64, two
-// workgroups per CU; every B code is widened once
+// decode-sized masked buffers on plain weights: 64 x 256, waves 1 x 4 of
+// 64 x 64, two workgroups per CU; every B code is widened once
 typedef WCfg<1, 4, 2, 2, 3> WideDecodeTile;
 
 template <class W>
@@ -709,10 +709,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), kRsrcFlags);
 }
 
-// TB: B is in the decode-tiled layout (fp8_tile_weights_decode): each
-// half-block of a 256-row n-tile is one contiguous 16 KB block, already in
-// the stage's LDS order, so the B pieces are plain contiguous copies.
-template <class W, bool TB = false>
+template <class W>
 struct WideBufCopier {
     rsrc_t ra, rb, rs;
     uint32_t va[W::A_PER_WAVE], vb[W::B_PER_WAVE], vs;   // per-lane byte offsets
@@ -776,18 +773,17 @@ struct WideBufCopier {
         }
 #pragma unroll
         for (int i = 0; i < W::B_PER_WAVE; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i]), 16, vb[i],
-                                                     TB ? uint32_t(h) * uint32_t(W::BN * W::KS) : koff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i]), 16, vb[i], koff, 0, 0);
         if (!sparse || (has_scale && (pos & 1) == 0))
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs, skb * s_step, 0, 0);
     }
 };
 
-template <class W, bool TB = false>
-__device__ __forceinline__ WideBufCopier<W, TB> make_wide_buf_copier(const Tile& t, int wave, int lane, int64_t K,
-                                                                     int64_t n0) {
+template <class W>
+__device__ __forceinline__ WideBufCopier<W> make_wide_buf_copier(const Tile& t, int wave, int lane, int64_t K,
+                                                                 int64_t n0) {
     typedef WStage<W> S;
-    WideBufCopier<W, TB> c;
+    WideBufCopier<W> c;
     c.K = K;
     c.has_scale = wave < W::A_SCALE_WAVES + W::B_SCALE_WAVES;
     const int sub = lane >> 2, slot = lane & 3;
@@ -810,9 +806,7 @@ __device__ __forceinline__ WideBufCopier<W, TB> make_wide_buf_copier(const Tile&
     for (int i = 0; i < W::B_PER_WAVE; ++i) {
         const int r0 = (wave * W::B_PER_WAVE + i) * W::ROWS_PER_PIECE, r = r0 + sub;
         const int chunk = slot ^ ((r >> 2) & 3);
-        // tiled: the lane's 16 bytes sit where the stage keeps them (row r,
-        // position slot, holding K chunk `chunk` of the half-block)
-        c.vb[i] = TB ? uint32_t(r0 * W::KS + lane * 16) : uint32_t(int64_t(r) * K + chunk * 16);
+        c.vb[i] = uint32_t(int64_t(r) * K + chunk * 16);
         c.b_c16[i] = chunk * 16;
         c.b_lds[i] = int(offsetof(S, b)) + r0 * W::KS;
     }
@@ -939,7 +933,7 @@ constexpr uint32_t wide_lds_bytes() { return uint32_t(W::STAGES * sizeof(WStage<
 // OUT: 0 = BF16, 1 = FP32, 2 = FP8 codes + 1x128 scales along N (dense only).
 // `lds_raw` holds wide_lds_bytes<W>(); the workgroup computes tile `tile` of
 // the n-tiles covering columns [0, n_ext) (n_ext < 0: all N).
-template <class W, int OUT, int MODE, bool TB = false>
+template <class W, int OUT, int MODE>
 __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args, uint8_t* lds_raw, int64_t tile, int64_t n_ext) {
     typedef WStage<W> S;
     constexpr int FM = W::FM, FN = W::FN, STAGES = W::STAGES;
@@ -954,8 +948,7 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args, uint8_t* ld
     const Tile t = map_tile<W, MODE>(args, tile, n_ext);
     if (!t.live) return;
     const int64_t n0 = int64_t(t.bn) * W::BN;
-    static_assert(!TB || (W::BN == 256 && W::KS == 64), "the decode-tiled layout has 256-row, 64-K blocks");
-    const WideBufCopier<W, TB> cp = make_wide_buf_copier<W, TB>(t, wave, lane, K, n0);
+    const WideBufCopier<W> cp = make_wide_buf_copier<W>(t, wave, lane, K, n0);
     const int64_t wrow0 = t.m0 + wm * FM * 32;
     const int64_t left = t.rows_valid - wrow0;
     // m-tiles of this wave holding valid rows (uniform): 0, 1 or FM.  Only the
@@ -1875,31 +1868,414 @@ FP8FG_WIDE_KERNELS(FP8FG_DEFINE_WIDE)
 const KernelEntry kWideKernels[] = {FP8FG_WIDE_KERNELS(FP8FG_WIDE_ENTRY)};
 #undef FP8FG_WIDE_ENTRY
 
-// the masked decode tile on decode-tiled B (fp8_grouped_gemm_masked_tiled)
-__global__ __launch_bounds__(WideDecodeTile::THREADS) void gemm_wdect_o0_masked(GemmArgs args) {
-    __shared__ __align__(16) uint8_t lds[wide_lds_bytes<WideDecodeTile>()];
-    gemm_wide_body<WideDecodeTile, 0, int(GemmMode::Masked), true>(args, lds, blockIdx.x, -1);
-}
-__global__ __launch_bounds__(WideDecodeTile::THREADS) void gemm_wdect_o1_masked(GemmArgs args) {
-    __shared__ __align__(16) uint8_t lds[wide_lds_bytes<WideDecodeTile>()];
-    gemm_wide_body<WideDecodeTile, 1, int(GemmMode::Masked), true>(args, lds, blockIdx.x, -1);
+// ---------------------------------------------------------------------------
+// Persistent masked decode kernel on decode-tiled weights (gemm_dreg_*):
+// masked buffers of at most 128 rows per expert, exact engine, 128x128-scaled
+// B, N % 256 == 0.
+//
+// Decode is bound by the weight stream: every expert's N x K codes are read
+// once per call and each meets at most 64 valid rows.  An item is 64 rows of
+// one expert's buffer (an m-tile holding valid rows) times 64 NW columns; a
+// workgroup of NW waves computes it, wave w owning columns 64 w .. 64 w + 63
+// of all 64 rows (2 x 2 MFMA tiles of 32 x 32).  NW is 8 (one workgroup per
+// CU) when N % 512 == 0, else 4 (two per CU): two workgroups on one CU do not
+// share it evenly -- the older one's waves win the SIMDs' issue arbitration
+// and finish well ahead, leaving the younger to stream alone -- while the
+// eight waves of one workgroup stay in step at every half-block's barrier.
+// Workgroup b of P takes items b, b + P, b + 2P, ... and walks them as one
+// flat sequence of half-blocks (64 K), so the weight stream runs on from one
+// item into the next without a pause; the host sizes P so that the
+// workgroups get equal item counts when the experts are about equally full.
+// B never passes through LDS: each lane loads its own MFMA fragments (16
+// bytes per 32 x 32 tile and 32-wide K step) straight into registers, NP - 1
+// half-blocks ahead of the one being multiplied -- an NP-deep register ring,
+// the loop unrolled NP times so that ring positions are fixed registers --
+// with the non-temporal hint: each weight byte is read once, and the hint
+// measurably raised the stream rate (it keeps the weights from displacing
+// the A rows and scales that the items share).  A (64 rows x 64 K per
+// half-block, shared by the waves) rides an NP-slot LDS ring of
+// direct-to-LDS loads, each A byte copied by one wave; each K-block's scales
+// ride into registers with its first half.  Items are the live (expert,
+// m-tile) pairs ranked heaviest first (the ranking of masked_pair_by_work)
+// times the n-tiles; when eight divides the live pair count, all n-tiles of
+// a pair go to one XCD, whose L2 then serves the A rows they share.
+// The arithmetic is the wide kernel's -- same fragments, same map of k to
+// MFMA steps, same unit fold -- so the outputs are bit-identical to it.
+//
+// The decode-tiled layout (written by tile_weights_decode): the 16 KB block
+// of (expert, 256-row n-tile, half-block) holds the fragments in load order,
+// wave-major: bytes 4096 w + 1024 (2 ni + j) + 16 l are what lane l of wave
+// w (of that n-tile's four) loads for MFMA tile ni and K step j, so every
+// load instruction of the stream reads 1 KB of contiguous memory.
+constexpr int kNonTemporal = 2;   // buffer-load cache policy: nt
+
+// The ranking of the live (expert, 64-row m-tile) pairs, built once per
+// workgroup into LDS before any weight is streamed: entry p = the p-th live
+// pair, those with more valid 32-row sub-tiles first and then by index (the
+// order of masked_pair_by_work), packed as pair | rows << 16 with rows the
+// valid rows from the m-tile's first, at most 64; entry kDregMaxPairs = the
+// live count.  One wave, two passes of ballots over the pairs.
+constexpr int kDregMaxPairs = 4096;
+
+__device__ __forceinline__ void dreg_rank_table(const GemmArgs& args, uint32_t* tab, int lane) {
+    const int64_t m_tiles = (args.M + 63) / 64;
+    const int pairs = int(args.G * m_tiles);
+    int n2 = 0, n1 = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        int r2 = 0, r1 = n2;   // pass 1: next rank of each class
+        for (int base = 0; base < pairs; base += 64) {
+            const int pair = base + lane;
+            int rows = 0;
+            if (pair < pairs) {
+                const int64_t g = pair / m_tiles, m0 = (pair - g * m_tiles) * 64;
+                int64_t mm = args.aux[g];
+                mm = mm < 0 ? 0 : (mm > args.M ? args.M : mm);
+                rows = int(mm - m0 <= 0 ? 0 : (mm - m0 < 64 ? mm - m0 : 64));
+            }
+            const uint64_t b2 = __builtin_amdgcn_ballot_w64(rows > 32);
+            const uint64_t b1 = __builtin_amdgcn_ballot_w64(rows > 0 && rows <= 32);
+            if (pass == 0) {
+                n2 += __builtin_popcountll(b2);
+                n1 += __builtin_popcountll(b1);
+            } else {
+                const uint64_t below = (uint64_t(1) << lane) - 1;
+                if (rows > 0) {
+                    const int rank = rows > 32 ? r2 + __builtin_popcountll(b2 & below)
+                                               : r1 + __builtin_popcountll(b1 & below);
+                    tab[rank] = uint32_t(pair) | (uint32_t(rows) << 16);
+                }
+                r2 += __builtin_popcountll(b2);
+                r1 += __builtin_popcountll(b1);
+            }
+        }
+    }
+    if (lane == 0) tab[kDregMaxPairs] = uint32_t(n2 + n1);
 }
 
-// The decode-tiled weight layout, 16 bytes per thread in output order.  Output
-// byte block blk (16 KB) = (g * N/256 + t) * (K/64) + h holds n-tile t of
-// expert g (rows 256 t .. 256 t + 255) for K bytes 64 h .. 64 h + 63: row r of
-// the n-tile at bytes 64 r .. 64 r + 63, whose 16-byte position s holds K chunk
-// s ^ ((r >> 2) & 3) of the half-block -- the order the decode tile's stage
-// keeps in LDS.
+// One item's addressing for this lane: buffer resources over the item's A
+// rows, its n-tile of B, its A scales and the wave's B scale row, and the
+// lane's fixed offsets into them (the half-block or K-block position rides
+// in the scalar offset).
+struct DregSrc {
+    rsrc_t ra, rb, rsa, rsb;
+    uint32_t va, vb[4], vsa[2];
+    uint32_t sa_step;      // bytes between K-blocks of the A scales
+    int64_t c_off;         // element offset of C at (row m0, column n0)
+    int rows;              // valid rows from m0, at most 64
+};
+
+template <int NW>
+__device__ __forceinline__ DregSrc dreg_src(const GemmArgs& args, const uint32_t* tab, int64_t item, int64_t n_tiles,
+                                            bool xgroup, int wave, int lane) {
+    constexpr int BN = 64 * NW;                  // columns of an item
+    int64_t rank, bn;
+    if (xgroup) {   // item i runs on XCD i % 8 (round-robin dispatch, P % 8 == 0): pairs x, x + 8, ...
+        const int64_t x = item % 8, j = item / 8;
+        rank = x + 8 * (j / n_tiles);
+        bn = j % n_tiles;
+    } else {
+        rank = item / n_tiles;
+        bn = item % n_tiles;
+    }
+    const int64_t M = args.M, N = args.N, K = args.K;
+    const int64_t m_tiles = (M + 63) / 64, kbs = (K + BK - 1) / BK;
+    const uint32_t e = __builtin_amdgcn_readfirstlane(tab[rank]);   // rank < live; uniform
+    const int64_t pair = e & 0xFFFF;
+    const int64_t g = pair / m_tiles, m0 = (pair - g * m_tiles) * 64;
+    const int rows = int(e >> 16);                 // 1 .. 64
+    DregSrc s;
+    s.rows = rows;
+    s.c_off = (g * M + m0) * N + bn * BN;
+    const int r = lane & 31, h = lane >> 5, sub = lane >> 2, slot = lane & 3;
+    // A piece of this wave: rows 64 / NW * wave .. of the m-tile (16 rows,
+    // or 8 by the lower half-wave when eight waves share the tile), 16 bytes
+    // per lane in the ring's order (chunk c of row rr at slot
+    // c ^ ((rr >> 2) & 3)); rows past the valid ones re-read the last valid
+    // row (never used)
+    s.ra = make_rsrc(args.a + (g * M + m0) * K, uint32_t(rows * K));
+    {
+        const int rr = wave * (64 / NW) + (NW == 8 ? (sub & 7) : sub);
+        const int64_t row = rr < rows ? rr : rows - 1;
+        s.va = uint32_t(row * K + ((slot ^ ((rr >> 2) & 3)) << 4));
+    }
+    {   // the wave's 64 rows: quarter wave % 4 of 256-row n-tile BN / 256 * bn + wave / 4
+        const int64_t halves_real = K / 64, t = bn * (BN / 256) + (wave >> 2);
+        s.rb = make_rsrc(args.b + (g * (N / 256) + t) * halves_real * 16384, uint32_t(halves_real * 16384));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s.vb[u] = uint32_t((wave & 3) * 4096 + u * 1024 + lane * 16);
+    }
+    s.rsa = make_rsrc(args.sa + g * kbs * M + m0, uint32_t(((kbs - 1) * M + rows) * 4));
+    s.sa_step = uint32_t(M * 4);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const int rr = mi * 32 + r;
+        s.vsa[mi] = uint32_t((rr < rows ? rr : rows - 1) * 4);
+    }
+    s.rsb = make_rsrc(args.sb + (g * (N / 128) + bn * (BN / 128) + wave / 2) * kbs, uint32_t(kbs * 4));
+    return s;
+}
+
+// loads of half-block hb of an item into ring position POS: B fragments,
+// then the A piece, then (first half of a K-block) the scales
+// The groups must leave in program order -- the vmcnt waits count whole
+// groups, and the compiler's own waits on the ring registers are only as
+// tight as the order it sees -- so the scheduler may not move loads across
+// a group's ends.
+template <int NP, int NW, int POS>
+__device__ __forceinline__ void dreg_issue(const DregSrc& s, int hb, uint8_t* lds, int wave, int lane,
+                                           u32x4 (&bq)[NP][4], float (&qa)[NP / 2][2], float (&qb)[NP / 2]) {
+    constexpr int A_BYTES = 4096 / NW;   // this wave's share of the A half-block
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        bq[POS][t] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, s.vb[t], uint32_t(hb) * 16384u, kNonTemporal);
+    // (eight waves: the upper half-wave's lanes are off, so the copy is 512 bytes)
+    if (NW == 4 || lane < 32)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ra, (lds_ptr_t)(lds + POS * 4096 + wave * A_BYTES), 16, s.va,
+                                                 uint32_t(hb) * 64u, 0, 0);
+    if constexpr (POS % 2 == 0) {
+        const uint32_t kb = uint32_t(hb >> 1);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+            qa[POS / 2][mi] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s.rsa, s.vsa[mi],
+                                                                                           kb * s.sa_step, 0));
+        qb[POS / 2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s.rsb, 0u, kb * 4u, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// LDS byte address of a pointer into the workgroup's LDS
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
+}
+
+// loads per half-block: 4 B fragments + 1 A piece, + 3 scales on even ones
+constexpr int dreg_loads(int q) { return 5 + (q % 2 == 0 ? 3 : 0); }
+// loads issued for the `ahead` half-blocks after one at ring position p
+constexpr int dreg_later(int p, int ahead) {
+    int n = 0;
+    for (int d = 1; d <= ahead; ++d) n += dreg_loads(p + d);
+    return n;
+}
+
+template <int OUT>
+__device__ __forceinline__ void dreg_store(const GemmArgs& args, const DregSrc& c, int wave, int lane,
+                                           const v16f (&acc)[2][2], const WideScales<2>& w) {
+    const int r = lane & 31, h = lane >> 5;
+    const int64_t N = args.N;
+    const int n_lane = wave * 64 + 4 * h;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const int m = mi * 32 + r;
+        if (m >= c.rows) continue;
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t idx = c.c_off + int64_t(m) * N + n_lane + ni * 32 + 8 * j;
+                const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
+                                  acc[mi][ni][4 * j + 3]} * w.unit[mi];
+                if (OUT == 1) {
+                    st<v4f>(static_cast<float*>(args.c) + idx, v);
+                } else {
+                    const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+                    const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+                    st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
+                }
+            }
+    }
+}
+
+// One half-block at ring position P of the compute item: scales (first half
+// of a K-block), then the two K steps of 32 from the A slot and the B
+// registers.  `partial`: the K-block runs past K; fragments past K read as 0.
+template <int NP, int P>
+__device__ __forceinline__ void dreg_compute(const uint8_t* lds, int hb, int64_t K, bool partial, int r, int h, const u32x4 (&bq)[NP][4], const float (&qa)[NP / 2][2],
+                                             const float (&qb)[NP / 2], WideScales<2>& w, v16f (&acc)[2][2]) {
+    constexpr uint32_t kZero = NP * 4096;
+    if constexpr (P % 2 == 0) {
+        WideScales<2> nw;
+        const float sb = qb[P / 2];
+        const ScaleSplit b = split_scale(sb);
+        nw.pb = b.pow2;
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+            const float sa = qa[P / 2][mi];
+            const ScaleSplit a = split_scale(sa);
+            nw.pa[mi] = a.pow2;
+            nw.unit[mi] = clamp_unit(a.mant * b.mant);
+            nw.zero[mi] = (sa == 0.0f || sb == 0.0f) ? 1 : 0;
+        }
+        rescale<2, 2, 2>(acc, w, nw);
+        w = nw;
+    }
+    // The A fragments of both K steps, read in one block that also waits for
+    // them.  The reads are written out so that the compiler's own wait
+    // insertion does not see them: it cannot tell the slot read here from the
+    // slot the direct-to-LDS copies are filling, and would wait for those
+    // copies -- and, the counter being in order, for every prefetched B
+    // fragment with them.  The slot's copies are complete: the vmcnt wait and
+    // the barrier above cover every wave's.
+    const uint32_t base = lds_addr(lds) + uint32_t(P) * 4096u;
+    const uint32_t zero = lds_addr(lds) + kZero;
+    uint32_t ad[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t chunk = uint32_t(((2 * j + h) ^ ((r >> 2) & 3)) << 4);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+            ad[j][mi] = w.zero[mi] ? zero + chunk : base + uint32_t((mi * 32 + r) * 64) + chunk;
+    }
+    u32x4 fa[2][2];
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(fa[0][0]), "=&v"(fa[0][1]), "=&v"(fa[1][0]), "=&v"(fa[1][1])
+        : "v"(ad[0][0]), "v"(ad[0][1]), "v"(ad[1][0]), "v"(ad[1][1])
+        : "memory");
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        Frags<2, 2> x;
+        x.a[0] = fa[j][0];
+        x.a[1] = fa[j][1];
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+            x.b[ni] = bq[P][2 * ni + j];
+            if (partial && int64_t(hb) * 64 + 32 * j + 16 * h >= K) x.b[ni] = u32x4{0u, 0u, 0u, 0u};
+        }
+        mfma_column<2, 2, 2>(x, w, acc);
+    }
+}
+
+// a new item: accumulators at 0, unit 1
+__device__ __forceinline__ void dreg_reset(v16f (&acc)[2][2], WideScales<2>& w) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
+        w.pa[mi] = 1.0f;
+        w.unit[mi] = 1.0f;
+        w.zero[mi] = 0;
+    }
+    w.pb = 1.0f;
+}
+
+template <int OUT, int NP, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
+    static_assert(NP % 2 == 0 && NP >= 2 && NP <= 8, "whole K-blocks per ring turn");
+    static_assert(NW == 4 || NW == 8, "items of 256 or 512 columns");
+    __shared__ __align__(16) uint8_t lds[NP * 4096 + 64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 31, h = lane >> 5, sub = lane >> 2, slot = lane & 3;
+    const int64_t K = args.K;
+    const int halves = int(2 * ((K + BK - 1) / BK));   // whole K-blocks; a multiple of NP (host)
+    const int64_t n_tiles = args.N / (64 * NW);
+    __shared__ uint32_t tab[kDregMaxPairs + 1];
+    if (wave == 0) dreg_rank_table(args, tab, lane);
+    __syncthreads();
+    const int64_t live = __builtin_amdgcn_readfirstlane(tab[kDregMaxPairs]);
+    const int64_t items = live * n_tiles, P = gridDim.x, b0 = blockIdx.x;
+    if (b0 >= items) return;
+    const int64_t my = (items - b0 + P - 1) / P;
+    const int64_t F = my * halves;                     // this workgroup's half-blocks
+    const bool xgroup = live % 8 == 0 && P % 8 == 0;
+
+    if (tid < 4) st<u32x4>(lds + NP * 4096 + tid * 16, u32x4{0u, 0u, 0u, 0u});   // the zero line
+    u32x4 bq[NP][4];
+    float qa[NP / 2][2], qb[NP / 2];
+    // issue side: item of the next half-block to load; compute side: item being multiplied
+    int64_t item_k = 0;
+    DregSrc is = dreg_src<NW>(args, tab, b0, n_tiles, xgroup, wave, lane);
+    DregSrc cs = is;
+    // the first NP - 1 half-blocks (F >= halves >= NP, all of the first item)
+#pragma unroll
+    for (int q = 0; q < NP - 1; ++q) {
+        if (q == 0) dreg_issue<NP, NW, 0>(is, 0, lds, wave, lane, bq, qa, qb);
+        if (q == 1) dreg_issue<NP, NW, 1 % NP>(is, 1, lds, wave, lane, bq, qa, qb);
+        if (q == 2) dreg_issue<NP, NW, 2 % NP>(is, 2, lds, wave, lane, bq, qa, qb);
+        if (q == 3) dreg_issue<NP, NW, 3 % NP>(is, 3, lds, wave, lane, bq, qa, qb);
+        if (q == 4) dreg_issue<NP, NW, 4 % NP>(is, 4, lds, wave, lane, bq, qa, qb);
+        if (q == 5) dreg_issue<NP, NW, 5 % NP>(is, 5, lds, wave, lane, bq, qa, qb);
+        if (q == 6) dreg_issue<NP, NW, 6 % NP>(is, 6, lds, wave, lane, bq, qa, qb);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the zero line is written before the first barrier
+
+    v16f acc[2][2];
+    WideScales<2> w;
+    dreg_reset(acc, w);
+
+    int hb0 = 0;                                         // compute side: half-block of position 0
+    for (int64_t f = 0; f < F; f += NP, hb0 = hb0 + NP == halves ? 0 : hb0 + NP) {
+        const bool item_ends = hb0 + NP == halves;       // the compute item's last half-block is at NP - 1
+        const bool partial = (hb0 + NP) * 64 > K;        // this turn holds the K-block that runs past K
+#define FP8FG_DREG_STEP(PP)                                                                                       \
+        if constexpr ((PP) < NP) {                                                                                \
+            constexpr int later = dreg_later((PP), NP - 2);                                                       \
+            wait_vmcnt<later>();                                                                                  \
+            const int hbc = hb0 + (PP);                                                                           \
+            if (partial && (hbc + 1) * 64 > K) {   /* this wave's A chunks past K read as 0 */                    \
+                const int rr = wave * (64 / NW) + (NW == 8 ? (sub & 7) : sub);                                    \
+                if ((NW == 4 || lane < 32) && int64_t(hbc) * 64 + ((slot ^ ((rr >> 2) & 3)) << 4) >= K)           \
+                    st<u32x4>(lds + (PP) * 4096 + wave * (4096 / NW) + lane * 16, u32x4{0u, 0u, 0u, 0u});         \
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                \
+            }                                                                                                     \
+            __builtin_amdgcn_s_barrier();                                                                         \
+            /* every step issues a group (past F: a reload of the item's own half-blocks into ring */            \
+            /* positions never read again), so every path has the same loads in flight */                        \
+            if ((PP) == 1 && item_ends && f + NP < F) {   /* the issue side moves to the next item */             \
+                ++item_k;                                                                                         \
+                is = dreg_src<NW>(args, tab, b0 + item_k * P, n_tiles, xgroup, wave, lane);                       \
+            }                                                                                                     \
+            /* half-block hb0 + PP + NP - 1 of the compute item, or PP - 1 of the next one */                   \
+            dreg_issue<NP, NW, ((PP) + NP - 1) % NP>(is, item_ends && (PP) >= 1 ? (PP) - 1 : hb0 + (PP) + NP - 1, \
+                                                     lds, wave, lane, bq, qa, qb);                                \
+            dreg_compute<NP, (PP)>(lds, hbc, K, partial, r, h, bq, qa, qb, w, acc);                        \
+        }
+        FP8FG_DREG_STEP(0)
+        FP8FG_DREG_STEP(1)
+        FP8FG_DREG_STEP(2)
+        FP8FG_DREG_STEP(3)
+        FP8FG_DREG_STEP(4)
+        FP8FG_DREG_STEP(5)
+        FP8FG_DREG_STEP(6)
+        FP8FG_DREG_STEP(7)
+#undef FP8FG_DREG_STEP
+        if (item_ends) {
+            dreg_store<OUT>(args, cs, wave, lane, acc, w);
+            dreg_reset(acc, w);
+            cs = is;
+        }
+    }
+    wait_vmcnt<0>();   // no copy may land after the workgroup's LDS is handed on
+}
+
+#define FP8FG_DREG_KERNELS(X) \
+    X(0, 4, 4) X(0, 2, 4) X(1, 4, 4) X(1, 2, 4) X(0, 4, 8) X(0, 2, 8) X(1, 4, 8) X(1, 2, 8)
+#define FP8FG_DREG_INST(OUT, NP, NW) template __global__ void gemm_dreg<OUT, NP, NW>(GemmArgs);
+FP8FG_DREG_KERNELS(FP8FG_DREG_INST)
+#undef FP8FG_DREG_INST
+
+// The decode-tiled weight layout, 16 bytes per thread in output order: unit u
+// (16 bytes) of block blk = (g * N/256 + t) * (K/64) + hb holds, at block
+// offset 4096 w + 1024 (2 ni + j) + 16 l, bytes 64 hb + 32 j + 16 (l / 32)
+// .. + 15 of row 256 t + 64 w + 32 ni + l % 32 of expert g -- the fragment
+// that lane l of wave w of gemm_dreg loads for MFMA tile ni and K step j.
 __global__ __launch_bounds__(256) void tile_weights_decode(const uint8_t* __restrict__ q, int64_t K, int64_t units,
                                                            uint8_t* __restrict__ out) {
     const int64_t halves = K / 64;
     for (int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x; u < units; u += int64_t(gridDim.x) * 256) {
         const int64_t blk = u >> 10;
-        const int within = int(u & 1023), r = within >> 2, sl = within & 3;
-        const int64_t gt = blk / halves, h = blk - gt * halves;
-        const int c = sl ^ ((r >> 2) & 3);
-        st<u32x4>(out + u * 16, ld<u32x4>(q + (gt * 256 + r) * K + h * 64 + c * 16));
+        const int within = int(u & 1023);
+        const int wv = within >> 8, t = (within >> 6) & 3, l = within & 63;
+        const int64_t gt = blk / halves, hb = blk - gt * halves;
+        const int64_t row = gt * 256 + wv * 64 + (t >> 1) * 32 + (l & 31);
+        st<u32x4>(out + u * 16, ld<u32x4>(q + row * K + hb * 64 + (t & 1) * 32 + (l >> 5) * 16));
     }
 }
 
@@ -1932,6 +2308,35 @@ constexpr int kXcds = 8;
 // (expert, m-tile) pair count (the map is then a bijection)
 int masked_xcds(const GemmArgs& args, int64_t bm) {
     return (args.G * ((args.M + bm - 1) / bm)) % kXcds == 0 ? kXcds : 1;
+}
+
+// The persistent decode kernel: grid P such that the items of fully live
+// buffers split evenly over at most two workgroups per CU (P a multiple of
+// eight: the item -> XCD grouping assumes it); ring depth NP 4 when it
+// divides the half-block count, else 2.
+hipError_t launch_dreg(int out_fp32, const GemmArgs& args, hipStream_t stream) {
+    // items of 512 columns (one 8-wave workgroup per CU) when N allows, else 256
+    const int nw = args.N % 512 == 0 ? 8 : 4;
+    const int64_t items_max = args.G * ((args.M + 63) / 64) * (args.N / (64 * nw));
+    if (items_max == 0) return hipSuccess;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t slots = (nw == 8 ? 1 : 2) * int64_t(cus > 0 ? cus : 1);
+    const int64_t per = (items_max + slots - 1) / slots;
+    int64_t P = (items_max + per - 1) / per;
+    if (P >= 8) P -= P % 8;
+    const int64_t halves = 2 * ((args.K + BK - 1) / BK);
+    const int np = halves % 4 == 0 ? 4 : 2;
+    void (*k)(GemmArgs) = nullptr;
+#define FP8FG_DREG_PICK(OUT, NP, NW) \
+    if (out_fp32 == OUT && np == NP && nw == NW) k = gemm_dreg<OUT, NP, NW>;
+    FP8FG_DREG_KERNELS(FP8FG_DREG_PICK)
+#undef FP8FG_DREG_PICK
+    if (!k) return hipErrorInvalidValue;
+    return launch_kernel(k, dim3(unsigned(P)), dim3(unsigned(64 * nw)), stream, args);
 }
 
 hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
@@ -1982,12 +2387,7 @@ hipError_t launch_mx(int out_fp32, const GemmArgs& args, hipStream_t stream) {
 }
 
 hipError_t launch_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream) {
-    const int64_t tiles = tile_count<WideDecodeTile>(GemmMode::Masked, args);
-    if (tiles == 0) return hipSuccess;
-    GemmArgs a = args;
-    a.xcds = masked_xcds(args, WideDecodeTile::BM);
-    return launch_kernel(out_fp32 ? gemm_wdect_o1_masked : gemm_wdect_o0_masked, dim3(unsigned(tiles)),
-                         dim3(WideDecodeTile::THREADS), stream, a);
+    return launch_dreg(out_fp32, args, stream);
 }
 
 hipError_t launch_tile_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, uint8_t* out, hipStream_t stream) {

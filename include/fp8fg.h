@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 8
+#define FP8FG_ABI_VERSION 9
 
 enum fp8fg_status {
     FP8FG_OK = 0,
@@ -285,11 +285,13 @@ int fp8_grouped_gemm_masked(const uint8_t* a, const float* sa, const uint8_t* b,
  * q: u8 [G][N][K] codes, as written by fp8_quant_weight_128x128 per expert.
  * q_tiled: u8, G*N*K bytes (caller-owned, must not overlap q).  Block
  *   blk = (g * N/256 + t) * (K/64) + h (16384 bytes at offset 16384 * blk)
- *   holds rows 256 t .. 256 t + 255 of expert g, K bytes 64 h .. 64 h + 63:
- *   row r (0..255) at bytes 64 r .. 64 r + 63 of the block, whose 16-byte
- *   position s (0..3) holds bytes 16 c .. 16 c + 15 of that 64-byte piece,
- *   c = s ^ ((r >> 2) & 3).  A pure byte permutation; the scales are not
- *   touched (sb stays [G][N/128][K/128]).
+ *   holds rows 256 t .. 256 t + 255 of expert g, K bytes 64 h .. 64 h + 63,
+ *   as sixteen 1024-byte units u = 4 w + 2 n + j (w 0..3, n 0..1, j 0..1):
+ *   bytes 16 l .. 16 l + 15 of unit u (l = 0..63) are K bytes
+ *   64 h + 32 j + 16 (l / 32) .. + 15 of row 256 t + 64 w + 32 n + l % 32 --
+ *   the 16-byte MFMA fragments of the decode kernel in the order its lanes
+ *   load them.  A pure byte permutation; the scales are not touched (sb stays
+ *   [G][N/128][K/128]).
  * Requires N % 256 == 0, K % 64 == 0, K < 2^24, G >= 0 (empty arrays may be
  * NULL).
  */
@@ -300,7 +302,8 @@ int fp8_tile_weights_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, u
  * same arguments and the same result bit for bit, except that b_tiled holds
  * the experts' codes in the layout written by fp8_tile_weights_decode.
  * Requires M_max <= 128, N % 256 == 0, K % 64 == 0, K > 0, K <= 11776 (92
- * K-blocks, as for fp8_gemm_blockscaled_fp8out), G >= 0.
+ * K-blocks, as for fp8_gemm_blockscaled_fp8out), G >= 0, and
+ * G * ceil(M_max / 64) <= 4096 (FP8FG_ERR_UNSUPPORTED beyond).
  */
 int fp8_grouped_gemm_masked_tiled(const uint8_t* a, const float* sa, const uint8_t* b_tiled, const float* sb,
                                   const int32_t* masked_m, int64_t G, int64_t M_max,

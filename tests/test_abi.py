@@ -182,6 +182,8 @@ def test_decode_tiled_argument_errors():
     assert m(P, P, P, P, P, 4, 128, 256, 96, P, 0, NUL) == ESHAPE    # K % 64
     assert m(P, P, P, P, P, 4, 128, 256, 0, P, 0, NUL) == ESHAPE     # K = 0 with work to do
     assert m(P, P, P, P, P, 4, 128, 256, 92 * 128 + 64, P, 0, NUL) == EUNSUP   # beyond 92 K-blocks
+    assert m(P, P, P, P, P, 2049, 128, 256, 128, P, 0, NUL) == EUNSUP    # 4098 (expert, 64-row) pairs
+    assert m(P, P, P, P, P, 4097, 64, 256, 128, P, 0, NUL) == EUNSUP     # 4097 pairs
     assert m(P, P, MIS, P, P, 4, 128, 256, 128, P, 0, NUL) == EALIGN
     assert m(P, P, P, P, P, 4, 128, 256, 128, P, 2, NUL) == EUNSUP   # output dtype
     assert m(P, P, P, P, P, 4, 129, 256, 128, P, 0, NUL) == EUNSUP   # M_max > 128

@@ -391,11 +391,12 @@ def test_masked_many_experts_every_row_once():
             assert np.all(ch[g, mm[g]:] == -7.0), g
 
 
-# (G, M_max, N, K): the 64 x 256 decode tile (16 pairs: tiles grouped per XCD),
-# the 256 x 256 tile (M_max > 128: 8 pairs), the fold decode tile (N = 128 mod
-# 256: 16 pairs), and 12 pairs, which the host leaves in rank order
+# (G, M_max, N, K): the persistent decode kernel on 256-wide items (16 pairs:
+# items grouped per XCD when the live pairs allow), the 256 x 256 tile
+# (M_max > 128: 8 pairs), the fold decode tile (N = 128 mod 256: 16 pairs),
+# 12 pairs, and 512-wide items with a last half K-block (K = 192, 320)
 @pytest.mark.parametrize("G,M_max,N,K", [(8, 128, 768, 384), (4, 300, 512, 256), (8, 96, 384, 256),
-                                         (6, 128, 512, 256)])
+                                         (6, 128, 512, 256), (8, 128, 1024, 192), (5, 64, 512, 320)])
 def test_masked_equals_dense_per_expert(G, M_max, N, K):
     """Every expert's valid rows of the masked GEMM equal, bit for bit, the
     dense GEMM of those rows with that expert's weights: where a tile runs and

@@ -2,11 +2,12 @@
 reads it.
 
 fp8_tile_weights_decode is a byte permutation: it must equal the oracle's
-(oracle/layout.py) byte for byte.  fp8_grouped_gemm_masked_tiled runs the
-masked decode tile's arithmetic on the same LDS contents as
-fp8_grouped_gemm_masked, so it must equal that GEMM on the plain layout bit
-for bit, and stay inside the oracle GEMM's bound; rows past masked_m are not
-written."""
+(oracle/layout.py) byte for byte.  fp8_grouped_gemm_masked_tiled runs a
+different kernel (persistent, weight fragments streamed into registers) with
+the same arithmetic as fp8_grouped_gemm_masked -- the same fragments, map of
+k to MFMA steps and unit fold -- so it must equal that GEMM on the plain
+layout bit for bit, and stay inside the oracle GEMM's bound; rows past
+masked_m are not written."""
 import numpy as np
 import pytest
 import torch
@@ -51,9 +52,11 @@ def test_tile_weights_full_size_sampled():
 
 
 # (G, M_max, N, K, out): whole K-blocks; K = 128 q + 64 (a last half K-block);
-# one half-block; 96-row buffers; fp32 out
+# one half-block; 96-row buffers; fp32 out; a last half K-block with N a
+# multiple of 512 (eight-wave items) and with a 256-wide item (N = 256 mod 512)
 @pytest.mark.parametrize("G,M_max,N,K,out", [(8, 128, 512, 384, "bf16"), (5, 64, 768, 320, "fp32"),
-                                             (4, 100, 256, 64, "bf16"), (8, 96, 1024, 1152, "fp32")])
+                                             (4, 100, 256, 64, "bf16"), (8, 96, 1024, 1152, "fp32"),
+                                             (6, 128, 1024, 448, "bf16"), (4, 128, 512, 64, "fp32")])
 def test_masked_tiled_matches_plain_and_oracle(G, M_max, N, K, out):
     rng = np.random.default_rng(G * 100 + M_max + N + K)
     mm = rng.integers(0, M_max + 1, G).astype(np.int32)
