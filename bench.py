@@ -442,6 +442,15 @@ def run_extra(args):
         ms = time_launches(lambda i: fp8.fp8_grouped_gemm_contiguous(qa, sa, qb, sb, offs, out=c), T, W, stream)
         extra_line("moe_contig", "grouped_gemm_contiguous gate+up", ms, flops=2.0 * int(counts.sum()) * N * K,
                    args=args, config=dict(cfg, flops_counted="valid rows only"))
+        del c
+        qy = torch.zeros((mt, N), dtype=torch.uint8, device="cuda")
+        sy = torch.zeros((N // 128, mt), dtype=torch.float32, device="cuda")
+        ms = time_launches(lambda i: fp8.fp8_grouped_gemm_contiguous_fp8out(qa, sa, qb, sb, offs, q=qy, s=sy),
+                           T, W, stream)
+        extra_line("moe_contig", "grouped_gemm_contiguous gate+up, FP8 out (fused 1x128 quantization)", ms,
+                   flops=2.0 * int(counts.sum()) * N * K, args=args,
+                   config=dict(cfg, flops_counted="valid rows only",
+                               output="FP8 codes + 1x128 scales along N: the down projection's A operand"))
     elif args.workload == "moe_masked":
         G, MMAX = 32, 128
         for (N, K) in ((4096, 7168), (7168, 2048)):

@@ -22,14 +22,14 @@ BSCALE_1x128 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
 
-ABI_VERSION = 9
+ABI_VERSION = 10
 EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
            "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
            "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16", "fp8_requant_act_tokenwise",
            "fp8_quant_mx_1x32", "fp8_gemm_mx", "fp8_gemm_blockscaled_fp8out", "fp8_quant_fprop_operands",
            "fp8_tile_weights_decode", "fp8_grouped_gemm_masked_tiled", "fp8_gemm_blockscaled_fp8mfma",
-           "fp8fg_status_string", "fp8fg_abi_version")
-_COMPUTE = EXPORTS[:15]
+           "fp8_grouped_gemm_contiguous_fp8out", "fp8fg_status_string", "fp8fg_abi_version")
+_COMPUTE = EXPORTS[:16]
 
 
 class Fp8fgError(RuntimeError):
@@ -66,6 +66,7 @@ def load_library(path=LIB_PATH):
     lib.fp8_quant_fprop_operands.argtypes = [vp, i32, i64, vp, i32, i64, i64, vp, vp, vp, vp, vp]
     lib.fp8_tile_weights_decode.argtypes = [vp, i64, i64, i64, vp, vp]
     lib.fp8_grouped_gemm_masked_tiled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
+    lib.fp8_grouped_gemm_contiguous_fp8out.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp]
     for name in _COMPUTE:
         getattr(lib, name).restype = ctypes.c_int
     lib.fp8fg_status_string.argtypes = [ctypes.c_int]
@@ -278,6 +279,26 @@ def fp8_gemm_blockscaled_fp8out(a, sa, b, sb, q=None, s=None):
     _need(s, torch.float32, (N // 128, M), "s")
     _check("fp8_gemm_blockscaled_fp8out", load_library().fp8_gemm_blockscaled_fp8out(
         _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(q), _ptr(s), M, N, K, _stream(a)))
+    return q, s
+
+
+def fp8_grouped_gemm_contiguous_fp8out(a, sa, b, sb, group_offsets, q=None, s=None):
+    """Contiguous MoE layout with the output quantized 1x128 along N in the
+    epilogue: returns (q u8 [M_total][N], s f32 [N/128][M_total]); rows in no
+    expert's range are left as they were (zeros when q, s are allocated here)."""
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    _need(a, torch.uint8, (M_total, K), "a")
+    _need(sa, torch.float32, (_nb(K), M_total), "sa")
+    _need(b, torch.uint8, (G, N, K), "b")
+    _need(sb, torch.float32, (G, _nb(N), _nb(K)), "sb")
+    _need(group_offsets, torch.int32, (G + 1,), "group_offsets")
+    q = torch.zeros((M_total, N), dtype=torch.uint8, device=a.device) if q is None else q
+    s = torch.zeros((N // 128, M_total), dtype=torch.float32, device=a.device) if s is None else s
+    _need(q, torch.uint8, (M_total, N), "q")
+    _need(s, torch.float32, (N // 128, M_total), "s")
+    _check("fp8_grouped_gemm_contiguous_fp8out", load_library().fp8_grouped_gemm_contiguous_fp8out(
+        _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(group_offsets), G, M_total, N, K, _ptr(q), _ptr(s), _stream(a)))
     return q, s
 
 

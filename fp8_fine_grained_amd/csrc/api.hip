@@ -207,6 +207,25 @@ int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t
                                          static_cast<hipStream_t>(stream)));
 }
 
+int fp8_grouped_gemm_contiguous_fp8out(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                       const int32_t* group_offsets, int64_t G, int64_t M_total, int64_t N,
+                                       int64_t K, uint8_t* q, float* s, void* stream) {
+    if (!a || !sa || !b || !sb || !group_offsets || !q || !s) return FP8FG_ERR_NULL;
+    if (G < 0 || M_total < 0 || N < 0 || K < 0 || M_total % 128 != 0 || N % 256 != 0 || K % 16 != 0)
+        return FP8FG_ERR_SHAPE;
+    if (K == 0 && M_total > 0 && N > 0 && G > 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(q) || !aligned16(s) ||
+        !aligned16(group_offsets))
+        return FP8FG_ERR_ALIGN;
+    if (M_total > kMaxDim || N > kMaxDim || G > kMaxDim - 1 || (K + 127) / 128 > kWideMaxKBlocks)
+        return FP8FG_ERR_UNSUPPORTED;
+    if (((K + 127) / 128) * M_total * 4 > int64_t(0xFFFFFFFF)) return FP8FG_ERR_UNSUPPORTED;
+    if ((M_total / 128) * ((N + 127) / 128) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if (G == 0 || M_total == 0 || N == 0) return FP8FG_OK;
+    fp8fg::GemmArgs args{a, sa, b, sb, q, group_offsets, M_total, N, K, G, s};
+    return hip_status(fp8fg::launch_gemm(0, fp8fg::GemmMode::Contig, 0, 2, args, static_cast<hipStream_t>(stream)));
+}
+
 int fp8_grouped_gemm_masked(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                             const int32_t* masked_m, int64_t G, int64_t M_max, int64_t N, int64_t K, void* c,
                             int out_dtype, void* stream) {

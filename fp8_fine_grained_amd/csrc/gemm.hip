@@ -1856,7 +1856,8 @@ const KernelEntry kKernels[] = {FP8FG_GEMM_KERNELS(FP8FG_ENTRY)};
     X(wide_o1_masked, WideTile, 2, 1, 2)            \
     X(wdec_o0_masked, WideDecodeTile, 3, 0, 2)      \
     X(wdec_o1_masked, WideDecodeTile, 3, 1, 2)      \
-    X(wide_o2_dense, WideTile, 2, 2, 0)
+    X(wide_o2_dense, WideTile, 2, 2, 0)             \
+    X(wide_o2_contig, WideTile, 2, 2, 1)
 #define FP8FG_DEFINE_WIDE(NAME, CFG, TILE, OF, MODE)                                   \
     __global__ __launch_bounds__(CFG::THREADS) void gemm_##NAME(GemmArgs args) {       \
         __shared__ __align__(16) uint8_t lds[wide_lds_bytes<CFG>()];                   \

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 9
+#define FP8FG_ABI_VERSION 10
 
 enum fp8fg_status {
     FP8FG_OK = 0,
@@ -258,6 +258,26 @@ int fp8_gemm_blockscaled_fp8out(const uint8_t* a, const float* sa, const uint8_t
 int fp8_grouped_gemm_contiguous(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                                 const int32_t* group_offsets, int64_t G, int64_t M_total,
                                 int64_t N, int64_t K, void* c, int out_dtype, void* stream);
+
+/*
+ * fp8_grouped_gemm_contiguous with the next layer's quantization fused into
+ * the epilogue ("The Insider Secrets Of Deepseek Discovered", passage on
+ * Figure 6: with every Linear in FP8, a layer's output is quantized again
+ * before it feeds the next one -- for a MoE layer, the gate+up output that
+ * feeds the down projection).  Computes the FP32 C of
+ * fp8_grouped_gemm_contiguous and writes, instead of C, its 1x128
+ * quantization along N:
+ *   q: u8 [M_total][N], s: f32 [N/128][M_total] -- exactly
+ *   fp8_quant_act_1x128 applied to the FP32 C that out_dtype = FP8FG_OUT_FP32
+ *   would write (same values, bit for bit); rows in no expert's range are not
+ *   written (neither q nor s).
+ * Same arguments and rules as fp8_grouped_gemm_contiguous, and in addition
+ * N % 256 == 0, K <= 11776 (92 K-blocks, as for fp8_gemm_blockscaled_fp8out:
+ * else FP8FG_ERR_UNSUPPORTED), ceil(K/128) * M_total * 4 < 2^32.
+ */
+int fp8_grouped_gemm_contiguous_fp8out(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                       const int32_t* group_offsets, int64_t G, int64_t M_total,
+                                       int64_t N, int64_t K, uint8_t* q, float* s, void* stream);
 
 /*
  * MoE grouped GEMM, masked layout (decode).

@@ -159,6 +159,14 @@ def test_grouped_argument_errors():
     assert c(P, P, P, P, MIS, 4, 512, 128, 128, P, 0, NUL) == EALIGN
     assert c(P, P, P, P, P, 4, 512, 128, 128, P, 3, NUL) == EUNSUP
     assert c(P, P, P, P, P, 0, 512, 128, 128, P, 0, NUL) == OK       # G = 0
+    f = lib.fp8_grouped_gemm_contiguous_fp8out
+    assert f(P, P, P, P, P, 4, 512, 256, 128, NUL, P, NUL) == ENULL
+    assert f(P, P, P, P, P, 4, 512, 128, 128, P, P, NUL) == ESHAPE     # N % 256
+    assert f(P, P, P, P, P, 4, 500, 256, 128, P, P, NUL) == ESHAPE     # M_total % 128
+    assert f(P, P, P, P, P, 4, 512, 256, 0, P, P, NUL) == ESHAPE       # K = 0 with work to do
+    assert f(P, P, P, P, P, 4, 512, 256, 128, MIS, P, NUL) == EALIGN
+    assert f(P, P, P, P, P, 4, 512, 256, 92 * 128 + 16, P, P, NUL) == EUNSUP   # beyond 92 K-blocks
+    assert f(P, P, P, P, P, 0, 512, 256, 128, P, P, NUL) == OK         # G = 0
     m = lib.fp8_grouped_gemm_masked
     assert m(P, P, P, P, NUL, 4, 128, 128, 128, P, 0, NUL) == ENULL
     assert m(P, P, P, P, P, 4, 128, 128, 130, P, 0, NUL) == ESHAPE
@@ -219,8 +227,12 @@ int main(void) {
     int e3 = fp8_gemm_blockscaled_fp8mfma((const uint8_t*)16, (const float*)16, (const uint8_t*)16,
                                           (const float*)0, FP8FG_BSCALE_1x128, (void*)16, FP8FG_OUT_FP32,
                                           4, 128, 128, (void*)0);
-    printf("%d %d %d %d %s\n", v, e1, e2, e3, fp8fg_status_string(e2));
-    return v == FP8FG_ABI_VERSION && e1 == FP8FG_ERR_NULL && e2 == FP8FG_ERR_SHAPE && e3 == FP8FG_ERR_NULL ? 0 : 1;
+    int e4 = fp8_grouped_gemm_contiguous_fp8out((const uint8_t*)16, (const float*)16, (const uint8_t*)16,
+                                                (const float*)16, (const int32_t*)16, 4, 512, 128, 128,
+                                                (uint8_t*)16, (float*)16, (void*)0);
+    printf("%d %d %d %d %d %s\n", v, e1, e2, e3, e4, fp8fg_status_string(e2));
+    return v == FP8FG_ABI_VERSION && e1 == FP8FG_ERR_NULL && e2 == FP8FG_ERR_SHAPE && e3 == FP8FG_ERR_NULL &&
+           e4 == FP8FG_ERR_SHAPE ? 0 : 1;
 }
 """)
     libdir = os.path.dirname(fp8.LIB_PATH)

@@ -100,3 +100,84 @@ def test_full_size_dense_fprop():
     rows = np.concatenate([np.random.default_rng(8).choice(4096, 64, replace=False), [0, 4095]])
     c_ref, s_abs = gemm.gemm_blockscaled_ref(qa, sa, qb, sb, "128x128", rows=rows)
     _check_valid(host(q)[rows], host(s)[:, rows], c_ref, s_abs, "fp8out full size")
+
+
+# ---------------------------------------------------------------------------
+# The contiguous MoE layout with the fused output quantization (the gate+up
+# output feeding the down projection as its 1x128 A operand).
+
+def test_contiguous_exact_outputs_quantize_bit_for_bit():
+    """Identity experts (one nonzero product per output, power-of-two A
+    scales): codes and scales equal the oracle's quantization of the exact C;
+    rows in no expert's range keep the zeros they had."""
+    rng = np.random.default_rng(61)
+    N = K = 512
+    off = np.array([0, 256, 384, 384], np.int32)     # experts of 256, 128 and 0 rows; rows 384-511 in none
+    M = 512
+    qa = rng.integers(0, 256, size=(M, K), dtype=np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0x00
+    sa = (2.0 ** rng.integers(-20, 21, size=(K // 128, M))).astype(np.float32)
+    eye = np.where(np.eye(N, K, dtype=bool), np.uint8(0x38), np.uint8(0)).astype(np.uint8)
+    qb = np.stack([eye] * 3)
+    sb = np.ones((3, N // 128, K // 128), np.float32)
+    c_exact = quant.dequant32(qa, np.repeat(sa.T, 128, axis=1)) + np.float32(0.0)
+    q, s = fp8.fp8_grouped_gemm_contiguous_fp8out(dev(qa), dev(sa), dev(qb), dev(sb), dev(off))
+    oq, os_ = quant.quant_act_1x128(c_exact[:384])
+    gq, gs = host(q), host(s)
+    assert np.array_equal(gs[:, :384].view(np.uint32), os_.view(np.uint32))
+    bad = np.argwhere(gq[:384] != oq)
+    assert bad.size == 0, [(tuple(i), hex(gq[tuple(i)]), hex(oq[tuple(i)])) for i in bad[:6]]
+    assert not gq[384:].any() and not gs[:, 384:].any(), "rows outside every expert were written"
+
+
+@pytest.mark.parametrize("K", [384, 1040])
+def test_contiguous_fp8out_is_the_quantized_fp32_output(K):
+    """Ragged experts (5, 0, 300, 128 and 1 routed rows, each padded to 128),
+    K with and without a partial last K-block: the fused codes and scales are
+    the 1x128 quantizer applied to the FP32 output of the same GEMM, bit for
+    bit, and a valid quantization of the oracle's C within the GEMM bound."""
+    rng = np.random.default_rng(62 + K)
+    counts = np.array([5, 0, 300, 128, 1])
+    off = workloads.pad_offsets(counts)
+    G, N = 5, 512
+    qa, sa = quant.quant_act_1x128(workloads.activations(rng, int(off[-1]), K, 0.01, 100.0))
+    qs, ss = zip(*[quant.quant_weight_128x128(workloads.weights(rng, N, K)) for _ in range(G)])
+    qb, sb = np.stack(qs), np.stack(ss)
+    args = [dev(qa), dev(sa), dev(qb), dev(sb), dev(off.astype(np.int32))]
+    q, s = fp8.fp8_grouped_gemm_contiguous_fp8out(*args)
+    c = fp8.fp8_grouped_gemm_contiguous(*args, torch.float32)
+    rq, rs = fp8.fp8_quant_act_1x128(c)
+    torch.cuda.synchronize()
+    assert torch.equal(q, rq)
+    assert torch.equal(s.view(torch.int32), rs.view(torch.int32))
+    rows, cr, s_abs = gemm.grouped_contiguous_ref(qa, sa, qb, sb, off)
+    _check_valid(host(q)[rows], host(s)[:, rows], cr, s_abs, f"contiguous fp8out K={K}")
+
+
+@pytest.mark.timeout(900)
+def test_contiguous_fp8out_full_size():
+    """The MoE gate+up layer (32 experts, 65536 Zipf-routed rows padded per
+    expert, N=4096, K=7168): equal to the quantized FP32 output everywhere,
+    and sampled rows (each expert's first and last, plus random ones) valid
+    against the oracle."""
+    counts, off = workloads.moe_contig_layout()
+    G, N, K = 32, 4096, 7168
+    a = workloads.moe_contig_rows(counts, off, K)
+    qa, sa = quant.quant_act_1x128(a)
+    del a
+    qs, ss = zip(*[quant.quant_weight_128x128(workloads.expert_weight("moe_gate_up", g, N, K)) for g in range(G)])
+    qb, sb = np.stack(qs), np.stack(ss)
+    del qs, ss
+    args = [dev(qa), dev(sa), dev(qb), dev(sb), dev(off.astype(np.int32))]
+    q, s = fp8.fp8_grouped_gemm_contiguous_fp8out(*args)
+    c = fp8.fp8_grouped_gemm_contiguous(*args, torch.float32)
+    rq, rs = fp8.fp8_quant_act_1x128(c)
+    torch.cuda.synchronize()
+    assert torch.equal(q, rq)
+    assert torch.equal(s.view(torch.int32), rs.view(torch.int32))
+    del c, rq, rs, args
+    rng = np.random.default_rng(63)
+    rows = [[off[g], off[g + 1] - 1] for g in range(G) if off[g + 1] > off[g]]
+    rows = np.unique(np.concatenate([np.concatenate(rows), rng.integers(0, int(off[-1]), 64)]))
+    sel, cr, s_abs = gemm.grouped_contiguous_ref(qa, sa, qb, sb, off, rows=rows)
+    _check_valid(host(q)[sel], host(s)[:, sel], cr, s_abs, "contiguous fp8out full size")
