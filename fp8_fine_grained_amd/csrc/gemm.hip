@@ -652,7 +652,8 @@ struct alignas(16) WStage {
     uint8_t a[W::BM * W::KS];
     uint8_t b[W::BN * W::KS];
     float sa[W::BM];                    // A scales of the stage's K-block
-    float sb[W::B_SCALE_WAVES * 64];    // 64 copies of each n-block's scale
+    float sb[W::BN];                    // 64 copies of each n-block's scale (128x128 B), or
+                                        // one scale per column (1x128 B)
     float dummy[64];
 };
 
@@ -839,6 +840,11 @@ struct WideScales {
     float pa[FM], pb;        // cvt scale operands (exponent parts)
     float unit[FM];          // mantissa-part products: the accumulator unit
     int zero[FM];            // 1 if the row's codes must read as +0 (its A scale or the B scale is 0)
+    // 1x128 B (one scale per column): the exponent part and zero flag of the
+    // column each B fragment of the lane holds (n-tile g: column 32 g + r of
+    // the wave's); `unit` is then the A part alone
+    float pbn[4];
+    int zbm;                 // bit g: that column's scale is 0 (its codes read as +0)
 };
 
 template <class W>
@@ -927,8 +933,9 @@ __device__ __forceinline__ void rescale(v16f (&acc)[FM][FN], const WideScales<FM
     }
 }
 
-template <class W>
-constexpr uint32_t wide_lds_bytes() { return uint32_t(W::STAGES * sizeof(WStage<W>) + 64); }
+// (BS1: plus each wave's column arrays, 1536 bytes)
+template <class W, bool BS1 = false>
+constexpr uint32_t wide_lds_bytes() { return uint32_t(W::STAGES * sizeof(WStage<W>) + 64 + (BS1 ? W::NW * 1536 : 0)); }
 
 // OUT: 0 = BF16, 1 = FP32, 2 = FP8 codes + 1x128 scales along N (dense only).
 // `lds_raw` holds wide_lds_bytes<W>(); the workgroup computes tile `tile` of
@@ -1137,8 +1144,9 @@ struct IlCopier {
     }
 };
 
-template <class W, int CW>
-__device__ __forceinline__ IlCopier<W, CW> make_il_copier(const Tile& t, int wave, int lane, int64_t K, int64_t n0) {
+template <class W, int CW, bool BS1 = false>
+__device__ __forceinline__ IlCopier<W, CW> make_il_copier(const Tile& t, int wave, int lane, int64_t K, int64_t N,
+                                                          int64_t n0) {
     typedef WStage<W> S;
     typedef IlCopier<W, CW> C;
     C c;
@@ -1174,7 +1182,14 @@ __device__ __forceinline__ IlCopier<W, CW> make_il_copier(const Tile& t, int wav
         c.vs = uint32_t(row * 4);
         c.s_step = uint32_t(t.lda_s * 4);
         c.s_lds = int(offsetof(S, sa)) + wave * 64 * 4;
-    } else if (wave < W::A_SCALE_WAVES + W::B_SCALE_WAVES) {   // 64 copies of an n-block's scale
+    } else if (BS1 && wave < W::A_SCALE_WAVES + W::BN / 64) {   // 64 column scales ([K/128][N], 1x128 B)
+        static_assert(!BS1 || W::A_SCALE_WAVES + W::BN / 64 <= W::NW, "a scale piece per wave at most");
+        const int j = wave - W::A_SCALE_WAVES;
+        c.rs = make_rsrc(t.SB + n0 + 64 * j, uint32_t(((kbs - 1) * N + 64) * 4));
+        c.vs = uint32_t(lane * 4);
+        c.s_step = uint32_t(N * 4);
+        c.s_lds = int(offsetof(S, sb)) + j * 64 * 4;
+    } else if (!BS1 && wave < W::A_SCALE_WAVES + W::B_SCALE_WAVES) {   // 64 copies of an n-block's scale
         const int j = wave - W::A_SCALE_WAVES;
         c.rs = make_rsrc(t.SB + (n0 / 128 + j) * kbs, uint32_t(kbs * 4));
         c.vs = 0;
@@ -1240,14 +1255,19 @@ struct IlPlan {
     signed char a[FM][4][4];      // cvt q (one dword) of A fragment (mi, k)
     signed char b[FN][4][4];      // cvt q of B fragment (g, k)
     signed char m[FM][FN][16];    // rescale multiply of element i of tile (mi, g); -2: none in this half
+    signed char rb[FN][4];        // 1x128 B: LDS read of the column ratios of elements 4q .. 4q + 3 of
+                                  // n-tile g (two slots before their first multiply); -2: none
 };
 
+// mul_cost: VALU instructions per rescaled element (2 with 1x128 B: the row
+// ratio and the column ratio)
 template <int FM, int FN>
-constexpr IlPlan<FM, FN> make_il_plan(bool odd, int scale_slot, int scale_ops) {
+constexpr IlPlan<FM, FN> make_il_plan(bool odd, int scale_slot, int scale_ops, int mul_cost = 1,
+                                       int slot_cap = IL_CAP) {
     constexpr int NS = IlPlan<FM, FN>::NS, GW = IL_GW, NG = FN / GW, PG = 4 * FM * GW;
     IlPlan<FM, FN> p{};
     int cap[NS] = {};
-    for (int n = 0; n < NS; ++n) cap[n] = IL_CAP;
+    for (int n = 0; n < NS; ++n) cap[n] = slot_cap;
     // the scale arithmetic of the next K-block (even half-blocks) takes room in
     // the slots from scale_slot on
     for (int n = scale_slot, left = scale_ops; n < NS && left > 0; ++n) {
@@ -1278,15 +1298,18 @@ constexpr IlPlan<FM, FN> make_il_plan(bool odd, int scale_slot, int scale_ops) {
     // before their first MFMA of an even one
     auto early = [&](int lo, int hi) -> int {
         for (int n = lo < 0 ? 0 : lo; n <= hi; ++n)
-            if (cap[n] > 0) {
-                --cap[n];
+            if (cap[n] >= mul_cost) {
+                cap[n] -= mul_cost;
                 return n;
             }
         return hi;
     };
+    // (elements in runs of four columns, both m-tiles of a run together: with
+    // 1x128 B a run shares one LDS read of its column ratios)
     for (int g = 0; g < FN; ++g)
+        for (int qq = 0; qq < 16; qq += 4)
         for (int mi = 0; mi < FM; ++mi)
-            for (int i = 0; i < 16; ++i) {
+            for (int i = qq; i < qq + 4; ++i) {
                 const int G = g / GW, first = G * PG + mi * GW + g % GW, last = first + 3 * FM * GW;
                 if (odd && G < NG / 2)
                     p.m[mi][g][i] = (signed char)early(last + 2, NS - 1);
@@ -1295,6 +1318,14 @@ constexpr IlPlan<FM, FN> make_il_plan(bool odd, int scale_slot, int scale_ops) {
                 else
                     p.m[mi][g][i] = -2;
             }
+    for (int g = 0; g < FN; ++g)
+        for (int q = 0; q < 4; ++q) {
+            int first = NS;
+            for (int mi = 0; mi < FM; ++mi)
+                for (int i = 4 * q; i < 4 * q + 4; ++i)
+                    if (p.m[mi][g][i] != -2 && p.m[mi][g][i] < first) first = p.m[mi][g][i];
+            p.rb[g][q] = (signed char)(first == NS ? -2 : (first - 2 < -1 ? -1 : first - 2));
+        }
     return p;
 }
 
@@ -1309,22 +1340,32 @@ __device__ __forceinline__ uint32_t widen_q(const u32x4& raw, int hh, int q, flo
 // Even half-blocks also turn the stage's scale piece (the next K-block's
 // scales) into `next`: its LDS reads go out with the fragment reads, its
 // arithmetic runs in four slots of the last group, whose room the plan keeps.
-template <class W, int ODD, bool COPIER>
+// With 1x128 B (BS1) the accumulator unit is the A part alone and each
+// column carries its own ratio: every rescaled element takes two multiplies,
+// by its row's ratio and by its column's, read four at a time from this
+// wave's private LDS arrays (`cl`: ratios of two transitions, by parity, then
+// the columns' current mantissa parts); the column ratios of the next
+// transition are computed here (even half-blocks), two columns per lane.  No
+// fragments are read ahead for the odd half-block (no registers for them).
+template <class W, int ODD, bool COPIER, bool BS1 = false>
 __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int wn, int r, int h,
                                              const WideScales<W::FM>& w, const float (&ratio)[W::FM],
                                              uint32_t zero_line, v16f (&acc)[W::FM][W::FN],
                                              WideScales<W::FM>& next, const IlCopier<W, IL_COPY_WAVES>& cp,
                                              int fill_slot, int fill_h, int pf_slot, u32x4 (&pfa)[W::FM][2],
-                                             u32x4 (&pfb)[IL_GW][2]) {
+                                             u32x4 (&pfb)[IL_GW][2], uint32_t cl, int rpar, int wpar, bool more,
+                                             int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device code only: the host pass never runs it
     constexpr int IL_SCALE_OPS = 32;
     constexpr int FM = W::FM, FN = W::FN, NS = 4 * FM * FN, SS = NS - 12;
-    static_assert(FN % 2 == 0 && FM == 2, "plan shape");
-    constexpr IlPlan<FM, FN> P = make_il_plan<FM, FN>(ODD != 0, SS, ODD ? 0 : IL_SCALE_OPS);
+    static_assert(FN % 2 == 0 && FM == 2 && FN <= 4, "plan shape");
+    constexpr IlPlan<FM, FN> P = make_il_plan<FM, FN>(ODD != 0, SS, ODD ? 0 : IL_SCALE_OPS, BS1 ? 2 : 1,
+                                                      BS1 ? 9 : IL_CAP);
+    constexpr bool PREFETCH = !BS1;   // odd half-blocks' first fragments read during the even one
     const WStage<W>& sg = *reinterpret_cast<const WStage<W>*>(lds + uint32_t(slot) * uint32_t(sizeof(WStage<W>)));
     float nsa[FM], nsb = 0.0f;
     if (!ODD) {
-        nsb = sg.sb[((wn * FN * 32) / 128) * 64];
+        if (!BS1) nsb = sg.sb[((wn * FN * 32) / 128) * 64];
 #pragma clang loop unroll(full)
         for (int mi = 0; mi < FM; ++mi) nsa[mi] = sg.sa[wm * FM * 32 + mi * 32 + r];
     }
@@ -1339,8 +1380,10 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
         return ld<u32x4>(lds + (w.zero[mi] ? zero_line + ch[j] : at));
     };
     auto read_b = [&](uint32_t sl, int g, int j) -> u32x4 {
-        return ld<u32x4>(lds + sl * uint32_t(sizeof(WStage<W>)) + uint32_t(offsetof(WStage<W>, b)) +
-                         uint32_t((wn * FN * 32 + g * 32 + r) * W::KS) + ch[j]);
+        const uint32_t bt = sl * uint32_t(sizeof(WStage<W>)) + uint32_t(offsetof(WStage<W>, b)) +
+                            uint32_t((wn * FN * 32 + g * 32 + r) * W::KS) + ch[j];
+        // a column whose 1x128 scale is 0 reads as +0, like a zero-scaled A row
+        return ld<u32x4>(lds + (BS1 && ((w.zbm >> g) & 1) ? zero_line + ch[j] : bt));
     };
     // An odd half-block's A fragments and its first group's B fragments were
     // read during the even half-block before it (the K-block's barrier covers
@@ -1349,12 +1392,14 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
 #pragma clang loop unroll(full)
     for (int mi = 0; mi < FM; ++mi)
 #pragma clang loop unroll(full)
-        for (int j = 0; j < 2; ++j) ra[mi][j] = ODD ? pfa[mi][j] : read_a(uint32_t(slot), mi, j);
+        for (int j = 0; j < 2; ++j) ra[mi][j] = (ODD && PREFETCH) ? pfa[mi][j] : read_a(uint32_t(slot), mi, j);
 #pragma clang loop unroll(full)
     for (int g = 0; g < FN; ++g)
 #pragma clang loop unroll(full)
-        for (int j = 0; j < 2; ++j) rb[g][j] = (ODD && g < IL_GW) ? pfb[g][j] : read_b(uint32_t(slot), g, j);
+        for (int j = 0; j < 2; ++j)
+            rb[g][j] = (ODD && PREFETCH && g < IL_GW) ? pfb[g][j] : read_b(uint32_t(slot), g, j);
     u32x4 ca[FM][4], cb[FN][4];
+    v4f rbq[FN][4];   // 1x128 B: column ratios of elements 4q .. 4q + 3 of n-tile g
     // the VALU work planned for slot n
     auto valu = [&](int n) {
 #pragma clang loop unroll(full)
@@ -1370,14 +1415,27 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
             for (int k = 0; k < 4; ++k)
 #pragma clang loop unroll(full)
                 for (int q = 0; q < 4; ++q)
-                    if (P.b[g][k][q] == n) cb[g][k][q] = widen_q(rb[g][k >> 1], k & 1, q, w.pb);
+                    if (P.b[g][k][q] == n) cb[g][k][q] = widen_q(rb[g][k >> 1], k & 1, q, BS1 ? w.pbn[g] : w.pb);
+        if (BS1) {
+#pragma clang loop unroll(full)
+            for (int g = 0; g < FN; ++g)
+#pragma clang loop unroll(full)
+                for (int q = 0; q < 4; ++q)
+                    if (P.rb[g][q] == n)
+                        rbq[g][q] = ld<v4f>(lds + cl + uint32_t(rpar) * 512u + uint32_t((g * 32 + 8 * q + 4 * h) * 4));
+        }
 #pragma clang loop unroll(full)
         for (int mi = 0; mi < FM; ++mi)
 #pragma clang loop unroll(full)
             for (int g = 0; g < FN; ++g)
 #pragma clang loop unroll(full)
                 for (int i = 0; i < 16; ++i)
-                    if (P.m[mi][g][i] == n) acc[mi][g][i] *= ratio[mi];
+                    if (P.m[mi][g][i] == n) {
+                        if (BS1)
+                            acc[mi][g][i] *= ratio[mi] * rbq[g][i >> 2][i & 3];
+                        else
+                            acc[mi][g][i] *= ratio[mi];
+                    }
     };
     // this wave's share of the copy of half-block fill_h, one piece every few
     // MFMAs (the last piece is the scale piece; data only on copying waves)
@@ -1394,7 +1452,7 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
                                                              __builtin_bit_cast(v8bf, ca[mi][k]), acc[mi][g], 0, 0, 0);
         if (n % PSTRIDE == 1 && n / PSTRIDE < PIECES)
             cp.copy_piece(fill_stage, fill_h, COPIER ? n / PSTRIDE : Cp::AP + Cp::BP);
-        if (!ODD && n == NS / 2 + 2) {
+        if (PREFETCH && !ODD && n == NS / 2 + 2) {
             // the odd half-block's first fragments, into registers the first
             // group of this one no longer needs
 #pragma clang loop unroll(full)
@@ -1407,7 +1465,7 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
                 for (int j = 0; j < 2; ++j) pfb[g][j] = read_b(uint32_t(pf_slot), g, j);
         }
         valu(n);
-        if (!ODD) {
+        if (!ODD && !BS1) {
             // the next K-block's scales, split as wide_scales does
             if (n == SS) nb = split_scale(nsb);
             if (n == SS + 1) na[0] = split_scale(nsa[0]);
@@ -1422,18 +1480,60 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
                 }
             }
         }
+        if (!ODD && BS1) {
+            // the next K-block's row scales (its column scales are taken
+            // between the half-blocks, by dreg_columns)
+            if (n == SS + 1) na[0] = split_scale(nsa[0]);
+            if (n == SS + 2) na[1] = split_scale(nsa[1]);
+            if (n == SS + 3) {
+#pragma clang loop unroll(full)
+                for (int q = 0; q < FM; ++q) {
+                    next.pa[q] = na[q].pow2;
+                    next.unit[q] = clamp_unit(na[q].mant);
+                    next.zero[q] = nsa[q] == 0.0f ? 1 : 0;
+                }
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 #endif
 }
 
+// 1x128 B, between the two half-blocks of K-block kb: the next K-block's
+// column scales (its scale piece sits in the even slot `sg`) -- the B
+// exponents and zero mask of the lane's fragment columns into `nw`, and the
+// ratios of the transition into it for this wave's private array of parity
+// `wpar` (two columns per lane; 1 where no K-block follows), with the
+// columns' new mantissa parts
+template <class W>
+__device__ __forceinline__ void il_columns(const uint8_t* lds, const WStage<W>& sg, uint32_t cl, int wpar, bool more,
+                                           int wn, int r, int lane, WideScales<W::FM>& nw) {
+    constexpr int FN = W::FN;
+    nw.zbm = 0;
+#pragma unroll
+    for (int g = 0; g < FN; ++g) {
+        const float sb = sg.sb[wn * FN * 32 + g * 32 + r];
+        nw.pbn[g] = split_scale(sb).pow2;
+        nw.zbm |= (sb == 0.0f ? 1 : 0) << g;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t col = uint32_t((64 * j + lane) * 4);
+        const float mn = split_scale(sg.sb[wn * FN * 32 + 64 * j + lane]).mant;
+        const float mo = ld<float>(lds + cl + 1024u + col);
+        st<float>(const_cast<uint8_t*>(lds) + cl + uint32_t(wpar) * 512u + col,
+                  more ? clamp_unit(mo * __builtin_amdgcn_rcpf(mn)) : 1.0f);
+        if (more) st<float>(const_cast<uint8_t*>(lds) + cl + 1024u + col, mn);
+    }
+}
+
 // The K-loop of gemm_wide_il_body for one copy role (a template parameter, so
 // each role's half-blocks are straight-line code with its own copy slots).
-template <class W, bool COPIER>
+template <class W, bool COPIER, bool BS1>
 __device__ __forceinline__ void il_kloop(uint8_t* lds_raw, WStage<W>* ring, const IlCopier<W, IL_COPY_WAVES>& cp,
                                          int halves, int64_t K, int wm, int wn, int r, int h, int lane, bool live,
                                          WideScales<W::FM>& w, WideScales<W::FM>& nw, float (&ratio)[W::FM],
-                                         v16f (&acc)[W::FM][W::FN]) {
+                                         v16f (&acc)[W::FM][W::FN], uint32_t cl) {
     constexpr int FM = W::FM;
     constexpr uint32_t kZeroLine = W::STAGES * sizeof(WStage<W>);
     u32x4 pfa[FM][2], pfb[IL_GW][2];   // an odd half-block's first fragments, read ahead
@@ -1454,14 +1554,16 @@ __device__ __forceinline__ void il_kloop(uint8_t* lds_raw, WStage<W>* ring, cons
         if (live) {
             w = nw;
             // the even slot's scale piece holds the next K-block's scales
-            wide_il_half<W, 0, COPIER>(lds_raw, hb & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 2) & 3, f0,
-                               (hb + 1) & 3, pfa, pfb);
             const bool more = hb + 2 < halves;
+            const int par = (hb >> 1) & 1;   // K-block parity: column ratios of the transition into it
+            wide_il_half<W, 0, COPIER, BS1>(lds_raw, hb & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 2) & 3,
+                                            f0, (hb + 1) & 3, pfa, pfb, cl, par, par ^ 1, more, lane);
 #pragma unroll
             for (int mi = 0; mi < FM; ++mi)
                 ratio[mi] = more ? clamp_unit(w.unit[mi] * __builtin_amdgcn_rcpf(nw.unit[mi])) : 1.0f;
-            wide_il_half<W, 1, COPIER>(lds_raw, (hb + 1) & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 3) & 3,
-                               f1, 0, pfa, pfb);
+            if (BS1) il_columns<W>(lds_raw, ring[hb & 3], cl, par ^ 1, more, wn, r, lane, nw);
+            wide_il_half<W, 1, COPIER, BS1>(lds_raw, (hb + 1) & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp,
+                                            (hb + 3) & 3, f1, 0, pfa, pfb, cl, par ^ 1, par ^ 1, more, lane);
         } else {
             cp.copy(reinterpret_cast<uint8_t*>(&ring[(hb + 2) & 3]), f0);
             cp.copy(reinterpret_cast<uint8_t*>(&ring[(hb + 3) & 3]), f1);
@@ -1469,9 +1571,12 @@ __device__ __forceinline__ void il_kloop(uint8_t* lds_raw, WStage<W>* ring, cons
     }
 }
 
-template <class W, int OUT, int MODE>
+// BS1: B is 1x128-scaled (one scale per column and K-block, [K/128][N]: the
+// Wgrad operand); dense layout, BF16 / FP32 out.
+template <class W, int OUT, int MODE, bool BS1 = false>
 __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t* lds_raw, int64_t tile, int64_t n_ext) {
     static_assert(MODE != int(GemmMode::Masked), "dense and contiguous layouts");
+    static_assert(!BS1 || (OUT != 2 && MODE == int(GemmMode::Dense)), "1x128 B: dense, BF16 / FP32 out");
     typedef WStage<W> S;
     constexpr int FM = W::FM, FN = W::FN, STAGES = W::STAGES;
     constexpr uint32_t kZeroLine = STAGES * sizeof(S);
@@ -1485,7 +1590,7 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
     const Tile t = map_tile<W, MODE>(args, tile, n_ext);
     if (!t.live) return;
     const int64_t n0 = int64_t(t.bn) * W::BN;
-    const IlCopier<W, IL_COPY_WAVES> cp = make_il_copier<W, IL_COPY_WAVES>(t, wave, lane, K, n0);
+    const IlCopier<W, IL_COPY_WAVES> cp = make_il_copier<W, IL_COPY_WAVES, BS1>(t, wave, lane, K, N, n0);
     const int64_t wrow0 = t.m0 + wm * FM * 32;
     const bool live = wrow0 < t.rows_valid;   // uniform
     const int r = lane & 31, h = lane >> 5;
@@ -1499,7 +1604,24 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
         row = row < t.rows_valid ? row : t.rows_valid - 1;
         sa0[mi] = t.SA[row];
     }
-    const float sb0 = t.SB[((n0 + wn * FN * 32) / 128) * ((K + BK - 1) / BK)];
+    const float sb0 = BS1 ? 1.0f : t.SB[((n0 + wn * FN * 32) / 128) * ((K + BK - 1) / BK)];
+    // 1x128 B: the first K-block's column scales -- of the lane's B fragments
+    // (column 32 g + r of the wave's) and of its two columns of the ratio
+    // arrays (lane, 64 + lane); this wave's private arrays sit after the zero
+    // line: two K-block parities of column ratios, then the columns' current
+    // mantissa parts
+    const uint32_t cl = kZeroLine + 64u + uint32_t(wave) * 1536u;
+    float sbn0[4] = {};
+    if (BS1) {
+#pragma unroll
+        for (int g = 0; g < FN; ++g) sbn0[g] = t.SB[n0 + wn * FN * 32 + g * 32 + r];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float mb0 = split_scale(t.SB[n0 + wn * FN * 32 + 64 * j + lane]).mant;
+            st<float>(lds_raw + cl + uint32_t((64 * j + lane) * 4), 1.0f);           // parity 0: no transition
+            st<float>(lds_raw + cl + 1024u + uint32_t((64 * j + lane) * 4), mb0);
+        }
+    }
 
     if (tid < 4) st<u32x4>(lds_raw + kZeroLine + tid * 16, u32x4{0u, 0u, 0u, 0u});
     // the ring holds four half-blocks: K-block kb in slots 2kb % 4 and
@@ -1528,17 +1650,23 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
         for (int mi = 0; mi < FM; ++mi) {
             const ScaleSplit a = split_scale(sa0[mi]);
             nw.pa[mi] = a.pow2;
-            nw.unit[mi] = clamp_unit(a.mant * b.mant);
+            nw.unit[mi] = clamp_unit(BS1 ? a.mant : a.mant * b.mant);
             nw.zero[mi] = (sa0[mi] == 0.0f || sb0 == 0.0f) ? 1 : 0;
+        }
+        nw.zbm = 0;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            nw.pbn[g] = split_scale(sbn0[g]).pow2;
+            nw.zbm |= (sbn0[g] == 0.0f ? 1 : 0) << g;
         }
     }
     float ratio[FM];
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi) ratio[mi] = 1.0f;
     if (cp.copier)
-        il_kloop<W, true>(lds_raw, ring, cp, halves, K, wm, wn, r, h, lane, live, w, nw, ratio, acc);
+        il_kloop<W, true, BS1>(lds_raw, ring, cp, halves, K, wm, wn, r, h, lane, live, w, nw, ratio, acc, cl);
     else
-        il_kloop<W, false>(lds_raw, ring, cp, halves, K, wm, wn, r, h, lane, live, w, nw, ratio, acc);
+        il_kloop<W, false, BS1>(lds_raw, ring, cp, halves, K, wm, wn, r, h, lane, live, w, nw, ratio, acc, cl);
     wait_vmcnt<0>();
 
     const int n_lane = wn * FN * 32 + 4 * h;
@@ -1578,8 +1706,10 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
-                const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
-                                  acc[mi][ni][4 * j + 3]} * w.unit[mi];
+                v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
+                            acc[mi][ni][4 * j + 3]} * w.unit[mi];
+                if (BS1)   // the columns' last mantissa parts
+                    v = v * ld<v4f>(lds_raw + cl + 1024u + uint32_t((ni * 32 + 8 * j + 4 * h) * 4));
                 if (OUT == 1) {
                     st<v4f>(static_cast<float*>(args.c) + idx, v);
                 } else {
@@ -1869,6 +1999,18 @@ FP8FG_WIDE_KERNELS(FP8FG_DEFINE_WIDE)
 const KernelEntry kWideKernels[] = {FP8FG_WIDE_KERNELS(FP8FG_WIDE_ENTRY)};
 #undef FP8FG_WIDE_ENTRY
 
+// the interleaved schedule on 1x128-scaled B (dense, Wgrad)
+__global__ __launch_bounds__(WideTile::THREADS) void gemm_wide_b1_o0_dense(GemmArgs args) {
+    __shared__ __align__(16) uint8_t lds[wide_lds_bytes<WideTile, true>()];
+    gemm_wide_il_body<WideTile, 0, int(GemmMode::Dense), true>(args, lds, blockIdx.x, -1);
+}
+__global__ __launch_bounds__(WideTile::THREADS) void gemm_wide_b1_o1_dense(GemmArgs args) {
+    __shared__ __align__(16) uint8_t lds[wide_lds_bytes<WideTile, true>()];
+    gemm_wide_il_body<WideTile, 1, int(GemmMode::Dense), true>(args, lds, blockIdx.x, -1);
+}
+const KernelEntry kWideB1Kernels[] = {{gemm_wide_b1_o0_dense, 2, 0, 1, 0, int(GemmMode::Dense), WideTile::THREADS},
+                                      {gemm_wide_b1_o1_dense, 2, 0, 1, 1, int(GemmMode::Dense), WideTile::THREADS}};
+
 // ---------------------------------------------------------------------------
 // Persistent masked decode kernel on decode-tiled weights (gemm_dreg_*):
 // masked buffers of at most 128 rows per expert, exact engine, 128x128-scaled
@@ -1987,7 +2129,7 @@ __device__ __forceinline__ DregSrc dreg_src(const GemmArgs& args, const uint32_t
     DregSrc s;
     s.rows = rows;
     s.c_off = (g * M + m0) * N + bn * BN;
-    const int r = lane & 31, h = lane >> 5, sub = lane >> 2, slot = lane & 3;
+    const int r = lane & 31, sub = lane >> 2, slot = lane & 3;
     // A piece of this wave: rows 64 / NW * wave .. of the m-tile (16 rows,
     // or 8 by the lower half-wave when eight waves share the tile), 16 bytes
     // per lane in the ring's order (chunk c of row rr at slot
@@ -2302,6 +2444,18 @@ bool wide_fits(const GemmArgs& args) {
     if (args.N % WideTile::BN != 0 || (args.K + BK - 1) / BK > kWideMaxKBlocks) return false;
     return ((args.K + BK - 1) / BK) * args.M * 4 <= int64_t(0xFFFFFFFF);
 }
+// On 1x128-scaled B the unit change costs more roundings: the column ratio
+// (reciprocal and multiply, about three) and its product with the row ratio
+// (one) join the row ratio's three and the accumulator's multiply, about
+// fifteen per K-block with the eight MFMA sums: inside the contract for at
+// most 68 K-blocks (15 * 68 + 1 <= 1024); the column scale array's byte range
+// must also fit 32 bits.
+constexpr int64_t kWideB1MaxKBlocks = 68;
+bool wide_b1_fits(const GemmArgs& args) {
+    const int64_t kbs = (args.K + BK - 1) / BK;
+    if (args.N % WideTile::BN != 0 || kbs > kWideB1MaxKBlocks) return false;
+    return kbs * args.M * 4 <= int64_t(0xFFFFFFFF) && kbs * args.N * 4 <= int64_t(0xFFFFFFFF);
+}
 
 // gfx950 (MI350 series): eight XCDs, each with its own L2
 constexpr int kXcds = 8;
@@ -2349,7 +2503,8 @@ hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, c
     // runs the fold kernel: 64 x 128 tiles for decode-sized masked buffers,
     // 256 x 128 tiles otherwise.  The FP8 output mode exists only in the wide
     // exact kernel (its entry point checks that it fits).
-    const bool wide = out_fp32 == 2 || (engine == 0 && !bscale_1x128 && wide_fits(args));
+    const bool wide = out_fp32 == 2 ||
+                      (engine == 0 && (bscale_1x128 ? mode == GemmMode::Dense && wide_b1_fits(args) : wide_fits(args)));
     if (out_fp32 == 2) engine = 0;
     int tile = 0;
     if (mode == GemmMode::Masked && args.M <= 128)
@@ -2367,9 +2522,10 @@ hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, c
                                    : tile == 1 ? DecodeTile::BM
                                    : tile == 2 ? WideTile::BM
                                                : WideDecodeTile::BM);
-    for (const KernelEntry* table : {kKernels, kWideKernels}) {
-        const size_t count = table == kKernels ? sizeof(kKernels) / sizeof(kKernels[0])
-                                               : sizeof(kWideKernels) / sizeof(kWideKernels[0]);
+    for (const KernelEntry* table : {kKernels, kWideKernels, kWideB1Kernels}) {
+        const size_t count = table == kKernels       ? sizeof(kKernels) / sizeof(kKernels[0])
+                             : table == kWideKernels ? sizeof(kWideKernels) / sizeof(kWideKernels[0])
+                                                     : sizeof(kWideB1Kernels) / sizeof(kWideB1Kernels[0]);
         for (size_t i = 0; i < count; ++i) {
             const KernelEntry& k = table[i];
             if (k.tile == tile && k.engine == engine && k.bscale == bscale_1x128 && k.out_fp32 == out_fp32 &&

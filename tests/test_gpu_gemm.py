@@ -96,7 +96,7 @@ def test_exact_integer_case():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 256, 256), (128, 256, 512), (130, 384, 384),
-                                   (257, 128, 1024), (300, 512, 2048)])
+                                   (257, 128, 1024), (300, 512, 2048), (200, 512, 1040)])
 @pytest.mark.parametrize("kind", ["128x128", "1x128"])
 @pytest.mark.parametrize("out", ["bf16", "fp32"])
 def test_dense_random(M, N, K, kind, out):
@@ -137,7 +137,8 @@ def test_determinism_and_scale_linearity():
 
 
 @pytest.mark.parametrize("out", ["bf16", "fp32"])
-def test_scales_across_many_binades(out):
+@pytest.mark.parametrize("kind", ["128x128", "1x128"])
+def test_scales_across_many_binades(out, kind):
     """Tile scales spread over 2^-64 .. 2^64 (A) and 2^-24 .. 2^24 (B), with
     one subnormal A scale: the promotion must hold for any scale pair, not
     just for quantizer-sized ones (the kernel splits scales into powers of two
@@ -145,34 +146,44 @@ def test_scales_across_many_binades(out):
     rng = np.random.default_rng(50)
     M, N, K = 300, 512, 1024
     qa, sa = quant.quant_act_1x128(workloads.activations(rng, M, K, 0.01, 50.0))
-    qb, sb = quant.quant_weight_128x128(workloads.weights(rng, N, K))
+    b = workloads.weights(rng, N, K) if kind == "128x128" else workloads.activations(rng, N, K, 0.01, 20.0, 1e-2)
+    qb, sb = quant_b(b, kind)
     sa = (sa * np.exp2(rng.integers(-64, 65, sa.shape))).astype(np.float32)
     sb = (sb * np.exp2(rng.integers(-24, 25, sb.shape))).astype(np.float32)
     sa[3, 7] = np.float32(2.0 ** -140)
-    c = host64(run_dense(qa, sa, qb, sb, "128x128", out))
-    c_ref, s_abs = gemm.gemm_blockscaled_ref(qa, sa, qb, sb)
+    if kind == "1x128":
+        sb[2, 9] = np.float32(2.0 ** -135)     # a subnormal column scale
+    c = host64(run_dense(qa, sa, qb, sb, kind, out))
+    c_ref, s_abs = gemm.gemm_blockscaled_ref(qa, sa, qb, sb, kind)
     assert np.all(np.isfinite(c))
-    check(c, c_ref, s_abs, out, f"scales across binades {out}")
+    check(c, c_ref, s_abs, out, f"scales across binades {kind} {out}")
 
 
-def test_zero_scales_with_nonzero_codes():
+@pytest.mark.parametrize("kind", ["128x128", "1x128"])
+def test_zero_scales_with_nonzero_codes(kind):
     """A zero scale removes its block's products whatever the codes say: some
-    A tiles and B blocks get scale 0 over nonzero codes, and row 5 has only
-    zero scales, so its outputs must be exactly zero."""
+    A tiles and B blocks (or, 1x128 B, single columns of a K-block) get scale
+    0 over nonzero codes, and row 5 has only zero scales, so its outputs must
+    be exactly zero; with 1x128 B column 9 too."""
     rng = np.random.default_rng(51)
     M, N, K = 130, 512, 768
     qa, sa = quant.quant_act_1x128(workloads.activations(rng, M, K, 0.01, 50.0))
-    qb, sb = quant.quant_weight_128x128(workloads.weights(rng, N, K))
+    b = workloads.weights(rng, N, K) if kind == "128x128" else workloads.activations(rng, N, K, 0.01, 20.0, 1e-2)
+    qb, sb = quant_b(b, kind)
     sa = sa.copy()
     sb = sb.copy()
     sa[rng.random(sa.shape) < 0.15] = 0.0
     sa[:, 5] = 0.0
     sb[rng.random(sb.shape) < 0.2] = 0.0
+    if kind == "1x128":
+        sb[:, 9] = 0.0
     for out in ("fp32", "bf16"):
-        c = host64(run_dense(qa, sa, qb, sb, "128x128", out))
-        c_ref, s_abs = gemm.gemm_blockscaled_ref(qa, sa, qb, sb)
-        check(c, c_ref, s_abs, out, f"zero scales {out}")
+        c = host64(run_dense(qa, sa, qb, sb, kind, out))
+        c_ref, s_abs = gemm.gemm_blockscaled_ref(qa, sa, qb, sb, kind)
+        check(c, c_ref, s_abs, out, f"zero scales {kind} {out}")
         assert np.all(c[5] == 0.0)
+        if kind == "1x128":
+            assert np.all(c[:, 9] == 0.0)
 
 
 def sample_rows(M, rng, n=64):
