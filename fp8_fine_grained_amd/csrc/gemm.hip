@@ -2369,11 +2369,19 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                \
             }                                                                                                     \
             __builtin_amdgcn_s_barrier();                                                                         \
-            /* every step issues a group (past F: a reload of the item's own half-blocks into ring */            \
-            /* positions never read again), so every path has the same loads in flight */                        \
-            if ((PP) == 1 && item_ends && f + NP < F) {   /* the issue side moves to the next item */             \
-                ++item_k;                                                                                         \
-                is = dreg_src<NW>(args, tab, b0 + item_k * P, n_tiles, xgroup, wave, lane);                       \
+            /* every step issues a group, so every path has the same loads in flight; past F the */              \
+            /* group goes to ring positions never read again, through empty buffer ranges, so those */            \
+            /* loads return zeros without touching memory */                                                      \
+            if ((PP) == 1 && item_ends) {                                                                         \
+                if (f + NP < F) {   /* the issue side moves to the next item */                                   \
+                    ++item_k;                                                                                     \
+                    is = dreg_src<NW>(args, tab, b0 + item_k * P, n_tiles, xgroup, wave, lane);                   \
+                } else {                                                                                          \
+                    is.ra = make_rsrc(args.a, 0u);                                                                \
+                    is.rb = make_rsrc(args.b, 0u);                                                                \
+                    is.rsa = make_rsrc(args.sa, 0u);                                                              \
+                    is.rsb = make_rsrc(args.sb, 0u);                                                              \
+                }                                                                                                 \
             }                                                                                                     \
             /* half-block hb0 + PP + NP - 1 of the compute item, or PP - 1 of the next one */                   \
             dreg_issue<NP, NW, ((PP) + NP - 1) % NP>(is, item_ends && (PP) >= 1 ? (PP) - 1 : hb0 + (PP) + NP - 1, \
