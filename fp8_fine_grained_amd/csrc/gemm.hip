@@ -2020,11 +2020,13 @@ const KernelEntry kWideB1Kernels[] = {{gemm_wide_b1_o0_dense, 2, 0, 1, 0, int(Ge
 // once per call and each meets at most 64 valid rows.  An item is 64 rows of
 // one expert's buffer (an m-tile holding valid rows) times 64 NW columns; a
 // workgroup of NW waves computes it, wave w owning columns 64 w .. 64 w + 63
-// of all 64 rows (2 x 2 MFMA tiles of 32 x 32).  NW is 8 (one workgroup per
-// CU) when N % 512 == 0, else 4 (two per CU): two workgroups on one CU do not
-// share it evenly -- the older one's waves win the SIMDs' issue arbitration
-// and finish well ahead, leaving the younger to stream alone -- while the
-// eight waves of one workgroup stay in step at every half-block's barrier.
+// of all 64 rows (2 x 2 MFMA tiles of 32 x 32).  NW is 8 or 7 (one workgroup
+// per CU; the host takes the one whose items fill more CUs: 7168 columns make
+// 16 items of 448 per expert but 14 of 512) when N allows, else 4 (two per
+// CU): two workgroups on one CU do not share it evenly -- the older one's
+// waves win the SIMDs' issue arbitration and finish well ahead, leaving the
+// younger to stream alone -- while the waves of one workgroup stay in step
+// at every half-block's barrier.
 // Workgroup b of P takes items b, b + P, b + 2P, ... and walks them as one
 // flat sequence of half-blocks (64 K), so the weight stream runs on from one
 // item into the next without a pause; the host sizes P so that the
@@ -2107,6 +2109,17 @@ struct DregSrc {
     int rows;              // valid rows from m0, at most 64
 };
 
+// The A half-block (64 rows x 64 bytes) is copied by the first COPIERS
+// waves, ROWS rows each (16: a whole wave of 16-byte pieces; 8: the lower
+// half-wave, eight waves sharing it).  With seven waves the last three copy
+// nothing; they issue the same direct-to-LDS load through an empty buffer
+// range into a dummy LDS line, so every wave counts the same loads.
+template <int NW>
+struct DregA {
+    static constexpr int ROWS = NW == 8 ? 8 : 16;
+    static constexpr int COPIERS = 64 / ROWS;
+};
+
 template <int NW>
 __device__ __forceinline__ DregSrc dreg_src(const GemmArgs& args, const uint32_t* tab, int64_t item, int64_t n_tiles,
                                             bool xgroup, int wave, int lane) {
@@ -2130,22 +2143,22 @@ __device__ __forceinline__ DregSrc dreg_src(const GemmArgs& args, const uint32_t
     s.rows = rows;
     s.c_off = (g * M + m0) * N + bn * BN;
     const int r = lane & 31, sub = lane >> 2, slot = lane & 3;
-    // A piece of this wave: rows 64 / NW * wave .. of the m-tile (16 rows,
-    // or 8 by the lower half-wave when eight waves share the tile), 16 bytes
-    // per lane in the ring's order (chunk c of row rr at slot
-    // c ^ ((rr >> 2) & 3)); rows past the valid ones re-read the last valid
-    // row (never used)
-    s.ra = make_rsrc(args.a + (g * M + m0) * K, uint32_t(rows * K));
+    // A piece of this wave: rows ROWS * wave .. of the m-tile, 16 bytes per
+    // lane in the ring's order (chunk c of row rr at slot c ^ ((rr >> 2) & 3));
+    // rows past the valid ones re-read the last valid row (never used)
+    s.ra = wave < DregA<NW>::COPIERS ? make_rsrc(args.a + (g * M + m0) * K, uint32_t(rows * K))
+                                     : make_rsrc(args.a, 0u);
     {
-        const int rr = wave * (64 / NW) + (NW == 8 ? (sub & 7) : sub);
+        const int rr = wave * DregA<NW>::ROWS + (DregA<NW>::ROWS == 8 ? (sub & 7) : sub);
         const int64_t row = rr < rows ? rr : rows - 1;
         s.va = uint32_t(row * K + ((slot ^ ((rr >> 2) & 3)) << 4));
     }
-    {   // the wave's 64 rows: quarter wave % 4 of 256-row n-tile BN / 256 * bn + wave / 4
-        const int64_t halves_real = K / 64, t = bn * (BN / 256) + (wave >> 2);
+    {   // the wave's 64 columns: quarter q of 256-row n-tile t of the tiled layout
+        const int64_t col = bn * BN + 64 * wave, t = col / 256, q = (col % 256) / 64;
+        const int64_t halves_real = K / 64;
         s.rb = make_rsrc(args.b + (g * (N / 256) + t) * halves_real * 16384, uint32_t(halves_real * 16384));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) s.vb[u] = uint32_t((wave & 3) * 4096 + u * 1024 + lane * 16);
+        for (int u = 0; u < 4; ++u) s.vb[u] = uint32_t(q * 4096 + u * 1024 + lane * 16);
     }
     s.rsa = make_rsrc(args.sa + g * kbs * M + m0, uint32_t(((kbs - 1) * M + rows) * 4));
     s.sa_step = uint32_t(M * 4);
@@ -2154,7 +2167,7 @@ __device__ __forceinline__ DregSrc dreg_src(const GemmArgs& args, const uint32_t
         const int rr = mi * 32 + r;
         s.vsa[mi] = uint32_t((rr < rows ? rr : rows - 1) * 4);
     }
-    s.rsb = make_rsrc(args.sb + (g * (N / 128) + bn * (BN / 128) + wave / 2) * kbs, uint32_t(kbs * 4));
+    s.rsb = make_rsrc(args.sb + (g * (N / 128) + (bn * BN + 64 * wave) / 128) * kbs, uint32_t(kbs * 4));
     return s;
 }
 
@@ -2167,15 +2180,16 @@ __device__ __forceinline__ DregSrc dreg_src(const GemmArgs& args, const uint32_t
 template <int NP, int NW, int POS>
 __device__ __forceinline__ void dreg_issue(const DregSrc& s, int hb, uint8_t* lds, int wave, int lane,
                                            u32x4 (&bq)[NP][4], float (&qa)[NP / 2][2], float (&qb)[NP / 2]) {
-    constexpr int A_BYTES = 4096 / NW;   // this wave's share of the A half-block
+    constexpr int A_BYTES = DregA<NW>::ROWS * 64;   // a copying wave's share of the A half-block
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
         bq[POS][t] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, s.vb[t], uint32_t(hb) * 16384u, kNonTemporal);
-    // (eight waves: the upper half-wave's lanes are off, so the copy is 512 bytes)
-    if (NW == 4 || lane < 32)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ra, (lds_ptr_t)(lds + POS * 4096 + wave * A_BYTES), 16, s.va,
-                                                 uint32_t(hb) * 64u, 0, 0);
+    // (eight waves: the upper half-wave's lanes are off, so the copy is 512
+    // bytes; waves past the copiers load nothing into the dummy line)
+    uint8_t* dst = wave < DregA<NW>::COPIERS ? lds + POS * 4096 + wave * A_BYTES : lds + NP * 4096 + 64;
+    if (DregA<NW>::ROWS == 16 || lane < 32)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ra, (lds_ptr_t)dst, 16, s.va, uint32_t(hb) * 64u, 0, 0);
     if constexpr (POS % 2 == 0) {
         const uint32_t kb = uint32_t(hb >> 1);
 #pragma unroll
@@ -2311,8 +2325,9 @@ __device__ __forceinline__ void dreg_reset(v16f (&acc)[2][2], WideScales<2>& w) 
 template <int OUT, int NP, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
     static_assert(NP % 2 == 0 && NP >= 2 && NP <= 8, "whole K-blocks per ring turn");
-    static_assert(NW == 4 || NW == 8, "items of 256 or 512 columns");
-    __shared__ __align__(16) uint8_t lds[NP * 4096 + 64];
+    static_assert(NW == 4 || NW == 7 || NW == 8, "items of 256, 448 or 512 columns");
+    // the ring, the zero line and (seven waves) the dummy line of the non-copying waves
+    __shared__ __align__(16) uint8_t lds[NP * 4096 + 64 + (NW == 7 ? 1024 : 0)];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, h = lane >> 5, sub = lane >> 2, slot = lane & 3;
@@ -2363,9 +2378,11 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
             wait_vmcnt<later>();                                                                                  \
             const int hbc = hb0 + (PP);                                                                           \
             if (partial && (hbc + 1) * 64 > K) {   /* this wave's A chunks past K read as 0 */                    \
-                const int rr = wave * (64 / NW) + (NW == 8 ? (sub & 7) : sub);                                    \
-                if ((NW == 4 || lane < 32) && int64_t(hbc) * 64 + ((slot ^ ((rr >> 2) & 3)) << 4) >= K)           \
-                    st<u32x4>(lds + (PP) * 4096 + wave * (4096 / NW) + lane * 16, u32x4{0u, 0u, 0u, 0u});         \
+                constexpr int ROWS = DregA<NW>::ROWS;                                                             \
+                const int rr = wave * ROWS + (ROWS == 8 ? (sub & 7) : sub);                                       \
+                if (wave < DregA<NW>::COPIERS && (ROWS == 16 || lane < 32) &&                                     \
+                    int64_t(hbc) * 64 + ((slot ^ ((rr >> 2) & 3)) << 4) >= K)                                     \
+                    st<u32x4>(lds + (PP) * 4096 + wave * (ROWS * 64) + lane * 16, u32x4{0u, 0u, 0u, 0u});         \
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                \
             }                                                                                                     \
             __builtin_amdgcn_s_barrier();                                                                         \
@@ -2407,7 +2424,8 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
 }
 
 #define FP8FG_DREG_KERNELS(X) \
-    X(0, 4, 4) X(0, 2, 4) X(1, 4, 4) X(1, 2, 4) X(0, 4, 8) X(0, 2, 8) X(1, 4, 8) X(1, 2, 8)
+    X(0, 4, 4) X(0, 2, 4) X(1, 4, 4) X(1, 2, 4) X(0, 4, 8) X(0, 2, 8) X(1, 4, 8) X(1, 2, 8) \
+    X(0, 4, 7) X(0, 2, 7) X(1, 4, 7) X(1, 2, 7)
 #define FP8FG_DREG_INST(OUT, NP, NW) template __global__ void gemm_dreg<OUT, NP, NW>(GemmArgs);
 FP8FG_DREG_KERNELS(FP8FG_DREG_INST)
 #undef FP8FG_DREG_INST
@@ -2474,23 +2492,45 @@ int masked_xcds(const GemmArgs& args, int64_t bm) {
 }
 
 // The persistent decode kernel: grid P such that the items of fully live
-// buffers split evenly over at most two workgroups per CU (P a multiple of
-// eight: the item -> XCD grouping assumes it); ring depth NP 4 when it
-// divides the half-block count, else 2.
+// buffers split evenly over the workgroup slots (P a multiple of eight: the
+// item -> XCD grouping assumes it); ring depth NP 4 when it divides the
+// half-block count, else 2.  Items of 512 or 448 columns (one 8- or 7-wave
+// workgroup per CU), whichever N allows and fills more slots, else 256 (two
+// 4-wave workgroups per CU).
+struct DregGrid {
+    int nw;
+    int64_t P;
+};
+DregGrid dreg_grid(const GemmArgs& args, int cus) {
+    DregGrid best{0, 0};
+    double best_use = -1.0;
+    for (const int nw : {8, 7, 4}) {
+        if (args.N % (64 * nw) != 0) continue;
+        const int64_t items = args.G * ((args.M + 63) / 64) * (args.N / (64 * nw));
+        if (items == 0) return DregGrid{nw, 0};
+        const int64_t slots = (nw == 4 ? 2 : 1) * int64_t(cus > 0 ? cus : 1);
+        const int64_t per = (items + slots - 1) / slots;
+        int64_t P = (items + per - 1) / per;
+        if (P >= 8) P -= P % 8;
+        const double use = double(P) / double(slots);
+        if (use > best_use) {
+            best = DregGrid{nw, P};
+            best_use = use;
+        }
+    }
+    return best;
+}
+
 hipError_t launch_dreg(int out_fp32, const GemmArgs& args, hipStream_t stream) {
-    // items of 512 columns (one 8-wave workgroup per CU) when N allows, else 256
-    const int nw = args.N % 512 == 0 ? 8 : 4;
-    const int64_t items_max = args.G * ((args.M + 63) / 64) * (args.N / (64 * nw));
-    if (items_max == 0) return hipSuccess;
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const int64_t slots = (nw == 8 ? 1 : 2) * int64_t(cus > 0 ? cus : 1);
-    const int64_t per = (items_max + slots - 1) / slots;
-    int64_t P = (items_max + per - 1) / per;
-    if (P >= 8) P -= P % 8;
+    const DregGrid grid = dreg_grid(args, cus);
+    const int nw = grid.nw;
+    const int64_t P = grid.P;
+    if (P == 0) return hipSuccess;
     const int64_t halves = 2 * ((args.K + BK - 1) / BK);
     const int np = halves % 4 == 0 ? 4 : 2;
     void (*k)(GemmArgs) = nullptr;

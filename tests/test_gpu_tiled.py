@@ -56,7 +56,10 @@ def test_tile_weights_full_size_sampled():
 # multiple of 512 (eight-wave items) and with a 256-wide item (N = 256 mod 512)
 @pytest.mark.parametrize("G,M_max,N,K,out", [(8, 128, 512, 384, "bf16"), (5, 64, 768, 320, "fp32"),
                                              (4, 100, 256, 64, "bf16"), (8, 96, 1024, 1152, "fp32"),
-                                             (6, 128, 1024, 448, "bf16"), (4, 128, 512, 64, "fp32")])
+                                             (6, 128, 1024, 448, "bf16"), (4, 128, 512, 64, "fp32"),
+                                             # items of 448 columns (seven-wave workgroups)
+                                             (8, 128, 1792, 448, "bf16"), (8, 128, 1792, 384, "fp32"),
+                                             (4, 128, 3584, 192, "fp32")])
 def test_masked_tiled_matches_plain_and_oracle(G, M_max, N, K, out):
     rng = np.random.default_rng(G * 100 + M_max + N + K)
     mm = rng.integers(0, M_max + 1, G).astype(np.int32)
