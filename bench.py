@@ -167,6 +167,37 @@ def time_launches(fn, steps, warmup, stream):
     return float(np.median(runs))
 
 
+def rotating_launches(fns, steps, warmup, stream):
+    """Duration (ms) of one launch in a stream of back-to-back launches that
+    cycle through len(fns) input sets, each larger than the 256 MB last-level
+    cache, so that every launch reads its inputs from HBM while the next
+    launch's dispatch overlaps the current one (as in a model's decode step).
+    `steps` launches between two HIP events on the launch stream; the median
+    of three such runs, after --settle-s seconds of untimed launches and
+    `warmup` more."""
+    import torch
+    t_end = time.perf_counter() + _SETTLE["seconds"]
+    n = 0
+    while time.perf_counter() < t_end:
+        fns[n % len(fns)]()
+        n += 1
+        if n % 64 == 0:
+            torch.cuda.synchronize()
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            fns[i % len(fns)]()
+        b.record(stream)
+        torch.cuda.synchronize()
+        runs.append(a.elapsed_time(b) / steps)
+    return float(np.median(runs))
+
+
 def extra_line(workload, kernel, ms, flops=None, nbytes=None, args=None, config=None, peak=None):
     line = {"metric": METRIC if flops else "HBM GB/s of " + kernel, "workload": workload, "kernel": kernel,
             "us": round(ms * 1e3, 2), "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -312,42 +343,77 @@ def profile_other(args):
     print(f"profiled {k} x{args.steps} ({what})", flush=True)
 
 
+MASKED_SETS = 3   # rotating input sets of the masked decode timing (each >= 470 MB of weights)
+
+
+def masked_sets(gen, G, MMAX, N, K):
+    """MASKED_SETS independent masked-decode input sets (same valid-row
+    counts, fresh activations and weights), each with its decode-tiled copy."""
+    import fp8_fine_grained_amd as fp8
+    out = []
+    for _ in range(MASKED_SETS):
+        mm, qa, sa, qb, sb, mmt, c = masked_inputs(gen, G, MMAX, N, K)
+        out.append(dict(mm=mm, qa=qa, sa=sa, qb=qb, sb=sb, mmt=mmt, c=c, qt=fp8.fp8_tile_weights_decode(qb)))
+    return out
+
+
+def masked_times(sets, args, stream):
+    """(plain, tiled) per-launch ms of the masked GEMM: back to back over the
+    rotating sets (rotating_launches), and single launches after a cache
+    flush, each between its own events (time_launches; the events add their
+    dispatch gap, about 5 us)."""
+    import fp8_fine_grained_amd as fp8
+    plain = [lambda s=s: fp8.fp8_grouped_gemm_masked(s["qa"], s["sa"], s["qb"], s["sb"], s["mmt"], out=s["c"])
+             for s in sets]
+    tiled = [lambda s=s: fp8.fp8_grouped_gemm_masked_tiled(s["qa"], s["sa"], s["qt"], s["sb"], s["mmt"], out=s["c"])
+             for s in sets]
+    return {"plain": rotating_launches(plain, args.steps, args.warmup, stream),
+            "tiled": rotating_launches(tiled, args.steps, args.warmup, stream),
+            "plain_single": time_launches(lambda i: plain[0](), args.steps, args.warmup, stream),
+            "tiled_single": time_launches(lambda i: tiled[0](), args.steps, args.warmup, stream)}
+
+
 def masked_decode_rates(args):
     """HBM rate of the masked-layout decode GEMM on both MoE shapes (gate+up
     K=7168 N=4096, down K=2048 N=7168; 32 experts, 128-row buffers, U{1..64}
     valid rows), on plain and on decode-tiled weights.  Bytes: every expert's
     weights and scales, the valid A rows and their scales, the valid C rows."""
     import torch
-    import fp8_fine_grained_amd as fp8
     import workloads
     stream = torch.cuda.current_stream()
     gen = torch.Generator(device="cuda").manual_seed(workloads.SEEDS.get("moe_masked", 105))
     out = {}
     G, MMAX = 32, 128
     for name, (N, K) in (("gate_up", (4096, 7168)), ("down", (7168, 2048))):
-        mm, qa, sa, qb, sb, mmt, c = masked_inputs(gen, G, MMAX, N, K)
-        valid = int(mm.sum())
+        sets = masked_sets(gen, G, MMAX, N, K)
+        valid = int(sets[0]["mm"].sum())
         nbytes = G * N * K + G * (N // 128) * (K // 128) * 4 + valid * K + valid * (K // 128) * 4 + valid * N * 2
-        ms = time_launches(lambda i: fp8.fp8_grouped_gemm_masked(qa, sa, qb, sb, mmt, out=c), args.steps,
-                           args.warmup, stream)
-        qt = fp8.fp8_tile_weights_decode(qb)
-        ms_t = time_launches(lambda i: fp8.fp8_grouped_gemm_masked_tiled(qa, sa, qt, sb, mmt, out=c), args.steps,
-                             args.warmup, stream)
-        gbs, gbs_t = nbytes / (ms * 1e-3) / 1e9, nbytes / (ms_t * 1e-3) / 1e9
+        t = masked_times(sets, args, stream)
+        gbs = {k: nbytes / (v * 1e-3) / 1e9 for k, v in t.items()}
         out[name] = {"N": N, "K": K, "valid_rows": valid, "algorithmic_bytes": int(nbytes),
-                     "plain_us": round(ms * 1e3, 2), "plain_gbs": round(gbs, 1),
-                     "plain_frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                     "tiled_us": round(ms_t * 1e3, 2), "tiled_gbs": round(gbs_t, 1),
-                     "tiled_frac_of_hbm": round(gbs_t / PEAK_HBM_GBS, 4)}
-        del qa, sa, qb, sb, c, qt
+                     "plain_us": round(t["plain"] * 1e3, 2), "plain_gbs": round(gbs["plain"], 1),
+                     "plain_frac_of_hbm": round(gbs["plain"] / PEAK_HBM_GBS, 4),
+                     "tiled_us": round(t["tiled"] * 1e3, 2), "tiled_gbs": round(gbs["tiled"], 1),
+                     "tiled_frac_of_hbm": round(gbs["tiled"] / PEAK_HBM_GBS, 4),
+                     "single_launch": {"plain_us": round(t["plain_single"] * 1e3, 2),
+                                       "plain_frac_of_hbm": round(gbs["plain_single"] / PEAK_HBM_GBS, 4),
+                                       "tiled_us": round(t["tiled_single"] * 1e3, 2),
+                                       "tiled_frac_of_hbm": round(gbs["tiled_single"] / PEAK_HBM_GBS, 4)}}
+        del sets
         torch.cuda.empty_cache()
-    out["note"] = ("each launch after an untimed 512 MB read, between its own HIP events; tiled = weights in "
-                   "the decode-tiled layout (fp8_tile_weights_decode, arranged once at load time); target >= 0.70 "
-                   "of the 8 TB/s HBM peak")
+    out["note"] = (f"back-to-back launches cycling through {MASKED_SETS} input sets (each set's weights exceed "
+                   "the 256 MB last-level cache, so every launch streams them from HBM) between two HIP events; "
+                   "single_launch: each launch after an untimed 512 MB read, between its own events (which add "
+                   "their dispatch gap, about 5 us); tiled = weights in the decode-tiled layout "
+                   "(fp8_tile_weights_decode, arranged once at load time); target >= 0.70 of the 8 TB/s HBM peak")
     return out
 
 
 def run_extra(args):
+    """The --workload lines.  Every kernel line is timed back to back over
+    rotating input sets whose bytes together exceed the 256 MB last-level
+    cache (rotating_launches), with one launch after a cache flush between
+    its own events beside it (time_launches: `single_launch_us`)."""
     import torch
     import fp8_fine_grained_amd as fp8
     import workloads
@@ -355,119 +421,153 @@ def run_extra(args):
     stream = torch.cuda.current_stream()
     gen = torch.Generator(device="cuda").manual_seed(workloads.SEEDS.get(args.workload, 1))
     T, W = args.steps, args.warmup
+
+    def line(workload, kernel, fn, sets, config, **kw):
+        fns = [lambda s=s: fn(s) for s in sets]
+        ms = rotating_launches(fns, T, W, stream)
+        ms1 = time_launches(lambda i: fns[0](), T, W, stream)
+        extra_line(workload, kernel, ms, args=args, config=dict(
+            config, timing=f"back to back over {len(sets)} rotating input sets",
+            single_launch_us=round(ms1 * 1e3, 2)), **kw)
+
     if args.workload == "dense_small":
+        # launch-latency bound: one small set, back-to-back launches
         M, N, K = 128, 256, 512
         x = gpu_acts(gen, M, K, 0.005, 50.0)
         w = torch.randn((N, K), generator=gen, device="cuda") * 0.02
         qa, sa = fp8.fp8_quant_act_1x128(x)
         qb, sb = fp8.fp8_quant_weight_128x128(w)
-        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled(qa, sa, qb, sb, 0, torch.bfloat16, out=c), T, W, stream)
-        extra_line("dense_small 128x256x512", "gemm_blockscaled", ms, flops=2.0 * M * N * K, args=args,
-                   config={"M": M, "N": N, "K": K, "note": "launch-latency bound"})
+        sets = [dict(qa=qa, sa=sa, qb=qb, sb=sb, c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"))]
+        line("dense_small 128x256x512", "gemm_blockscaled",
+             lambda s: fp8.fp8_gemm_blockscaled(s["qa"], s["sa"], s["qb"], s["sb"], 0, torch.bfloat16, out=s["c"]),
+             sets, {"M": M, "N": N, "K": K, "note": "launch-latency bound"}, flops=2.0 * M * N * K)
     elif args.workload == "dense_mx":
         # the MX variant on the dense Fprop shapes: 1x32 blocks with E8M0 scales,
         # scales applied inside the FP8 MFMA, so its peak is the FP8 one
         M, N, K = 4096, 7168, 2048
-        x = gpu_acts(gen, M, K, 0.001, 100.0)
-        w = torch.randn((N, K), generator=gen, device="cuda") * 0.02
-        qa, ea = fp8.fp8_quant_mx_1x32(x)
-        qb, eb = fp8.fp8_quant_mx_1x32(w)
-        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        sets = []
+        for _ in range(6):   # ~200 MB each
+            x = gpu_acts(gen, M, K, 0.001, 100.0)
+            w = torch.randn((N, K), generator=gen, device="cuda") * 0.02
+            qa, ea = fp8.fp8_quant_mx_1x32(x)
+            qb, eb = fp8.fp8_quant_mx_1x32(w)
+            sets.append(dict(x=x, w=w, qa=qa, ea=ea, qb=qb, eb=eb,
+                             c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
         cfg = {"M": M, "N": N, "K": K, "scales": "E8M0 per 1x32 block"}
-        ms = time_launches(lambda i: fp8.fp8_quant_mx_1x32(x, q=qa, e=ea), T, W, stream)
-        extra_line("dense_mx", "quant_mx_1x32 X", ms, nbytes=M * K * 5 + M * K // 32, args=args, config=cfg)
-        ms = time_launches(lambda i: fp8.fp8_quant_mx_1x32(w, q=qb, e=eb), T, W, stream)
-        extra_line("dense_mx", "quant_mx_1x32 W", ms, nbytes=N * K * 5 + N * K // 32, args=args, config=cfg)
-        ms = time_launches(lambda i: fp8.fp8_gemm_mx(qa, ea, qb, eb, torch.bfloat16, out=c), T, W, stream)
-        extra_line("dense_mx", "gemm_mx 4096x7168x2048 BF16", ms, flops=2.0 * M * N * K, args=args, config=cfg,
-                   peak="FP8 (scaled MFMA)")
+        line("dense_mx", "quant_mx_1x32 X", lambda s: fp8.fp8_quant_mx_1x32(s["x"], q=s["qa"], e=s["ea"]), sets,
+             cfg, nbytes=M * K * 5 + M * K // 32)
+        line("dense_mx", "quant_mx_1x32 W", lambda s: fp8.fp8_quant_mx_1x32(s["w"], q=s["qb"], e=s["eb"]), sets,
+             cfg, nbytes=N * K * 5 + N * K // 32)
+        line("dense_mx", "gemm_mx 4096x7168x2048 BF16",
+             lambda s: fp8.fp8_gemm_mx(s["qa"], s["ea"], s["qb"], s["eb"], torch.bfloat16, out=s["c"]), sets, cfg,
+             flops=2.0 * M * N * K, peak="FP8 (scaled MFMA)")
     elif args.workload == "linear_trio":
         TOK, IN, OUT = 8192, 7168, 2048
-        x, w, dy = trio_inputs(gen)
-        qx, sx = fp8.fp8_quant_act_1x128(x)
-        qw, sw = fp8.fp8_quant_weight_128x128(w)
-        qwt, swt = fp8.fp8_quant_weight_128x128(w, transpose_out=True)
-        qd, sd = fp8.fp8_quant_act_1x128(dy)
-        qdt, sdt = fp8.fp8_quant_act_1x128(dy, transpose_out=True)
-        qxt, sxt = fp8.fp8_quant_act_1x128(x, transpose_out=True)
+        bf = torch.bfloat16
+        sets = []
+        for _ in range(4):   # ~1.3 GB each
+            x, w, dy = trio_inputs(gen)
+            s = dict(x=x, w=w, dy=dy, xh=x.to(bf), dyh=dy.to(bf), wh=w.to(bf))
+            s["qx"], s["sx"] = fp8.fp8_quant_act_1x128(x)
+            s["qxt"], s["sxt"] = fp8.fp8_quant_act_1x128(x, transpose_out=True)
+            s["qd"], s["sd"] = fp8.fp8_quant_act_1x128(dy)
+            s["qdt"], s["sdt"] = fp8.fp8_quant_act_1x128(dy, transpose_out=True)
+            s["qw"], s["sw"] = fp8.fp8_quant_weight_128x128(w)
+            s["qwt"], s["swt"] = fp8.fp8_quant_weight_128x128(w, transpose_out=True)
+            # outputs of the timed quantizer launches other than the operands' own
+            # (those rewrite the same bytes): requantization and the bf16 inputs
+            for k in ("qx", "qxt", "qdt", "qw", "qwt"):
+                s["o" + k] = torch.empty_like(s[k])
+                s["o" + k.replace("q", "s", 1)] = torch.empty_like(s[k.replace("q", "s", 1)])
+            s["yb"] = torch.empty((TOK, OUT), dtype=bf, device="cuda")
+            s["qy"] = torch.empty((TOK, OUT), dtype=torch.uint8, device="cuda")
+            s["sy"] = torch.empty((OUT // 128, TOK), dtype=torch.float32, device="cuda")
+            s["dxb"] = torch.empty((TOK, IN), dtype=bf, device="cuda")
+            s["dwf"] = torch.empty((OUT, IN), dtype=torch.float32, device="cuda")
+            sets.append(s)
         cfg = {"tokens": TOK, "in": IN, "out": OUT}
-        for name, src, tr in (("quant_act_1x128 X rowwise", x, False), ("quant_act_1x128 X token-wise", x, True),
-                              ("quant_act_1x128 dY rowwise", dy, False), ("quant_act_1x128 dY token-wise", dy, True)):
-            ms = time_launches(lambda i, src=src, tr=tr: fp8.fp8_quant_act_1x128(src, transpose_out=tr), T, W, stream)
-            n = src.numel()
-            extra_line("linear_trio", name, ms, nbytes=n * 5 + (n // 128) * 4, args=args, config=cfg)
-        for name, tr in (("quant_weight_128x128 W", False), ("quant_weight_128x128 W transposed", True)):
-            ms = time_launches(lambda i, tr=tr: fp8.fp8_quant_weight_128x128(w, transpose_out=tr), T, W, stream)
-            extra_line("linear_trio", name, ms, nbytes=w.numel() * 5, args=args, config=cfg)
-        ms = time_launches(lambda i: fp8.fp8_requant_act_tokenwise(qx, sx, qt=qxt, st=sxt), T, W, stream)
-        n = x.numel()
-        extra_line("linear_trio", "requant_act_tokenwise X (rowwise FP8 cache -> token-wise)", ms,
-                   nbytes=n * 2 + (n // 128) * 8, args=args, config=cfg)
-        xh, dyh, wh = x.to(torch.bfloat16), dy.to(torch.bfloat16), w.to(torch.bfloat16)
-        for name, src, tr in (("quant_act_1x128_bf16 X rowwise", xh, False),
-                              ("quant_act_1x128_bf16 X token-wise", xh, True),
-                              ("quant_act_1x128_bf16 dY token-wise", dyh, True)):
-            ms = time_launches(lambda i, src=src, tr=tr: fp8.fp8_quant_act_1x128_bf16(src, transpose_out=tr),
-                               T, W, stream)
-            n = src.numel()
-            extra_line("linear_trio", name, ms, nbytes=n * 3 + (n // 128) * 4, args=args, config=cfg)
-        for name, tr in (("quant_weight_128x128_bf16 W", False), ("quant_weight_128x128_bf16 W transposed", True)):
-            ms = time_launches(lambda i, tr=tr: fp8.fp8_quant_weight_128x128_bf16(wh, transpose_out=tr), T, W, stream)
-            extra_line("linear_trio", name, ms, nbytes=wh.numel() * 3, args=args, config=cfg)
-        del xh, dyh, wh
-        yb = torch.empty((TOK, OUT), dtype=torch.bfloat16, device="cuda")
-        dxb = torch.empty((TOK, IN), dtype=torch.bfloat16, device="cuda")
-        dwf = torch.empty((OUT, IN), dtype=torch.float32, device="cuda")
+        q1 = fp8.fp8_quant_act_1x128
+        for name, src, tr, q, sc in (("quant_act_1x128 X rowwise", "x", False, "qx", "sx"),
+                                     ("quant_act_1x128 X token-wise", "x", True, "qxt", "sxt"),
+                                     ("quant_act_1x128 dY rowwise", "dy", False, "qd", "sd"),
+                                     ("quant_act_1x128 dY token-wise", "dy", True, "qdt", "sdt")):
+            n = sets[0][src].numel()
+            line("linear_trio", name, lambda s, src=src, tr=tr, q=q, sc=sc: q1(s[src], transpose_out=tr, q=s[q],
+                                                                                s=s[sc]),
+                 sets, cfg, nbytes=n * 5 + (n // 128) * 4)
+        for name, tr, q, sc in (("quant_weight_128x128 W", False, "qw", "sw"),
+                                ("quant_weight_128x128 W transposed", True, "qwt", "swt")):
+            line("linear_trio", name, lambda s, tr=tr, q=q, sc=sc: fp8.fp8_quant_weight_128x128(
+                s["w"], transpose_out=tr, q=s[q], s=s[sc]), sets, cfg, nbytes=sets[0]["w"].numel() * 5)
+        n = sets[0]["x"].numel()
+        line("linear_trio", "requant_act_tokenwise X (rowwise FP8 cache -> token-wise)",
+             lambda s: fp8.fp8_requant_act_tokenwise(s["qx"], s["sx"], qt=s["oqxt"], st=s["osxt"]), sets, cfg,
+             nbytes=n * 2 + (n // 128) * 8)
+        qh = fp8.fp8_quant_act_1x128_bf16
+        for name, src, tr, q, sc in (("quant_act_1x128_bf16 X rowwise", "xh", False, "oqx", "osx"),
+                                     ("quant_act_1x128_bf16 X token-wise", "xh", True, "oqxt", "osxt"),
+                                     ("quant_act_1x128_bf16 dY token-wise", "dyh", True, "oqdt", "osdt")):
+            n = sets[0][src].numel()
+            line("linear_trio", name, lambda s, src=src, tr=tr, q=q, sc=sc: qh(s[src], transpose_out=tr, q=s[q],
+                                                                                s=s[sc]),
+                 sets, cfg, nbytes=n * 3 + (n // 128) * 4)
+        for name, tr, q, sc in (("quant_weight_128x128_bf16 W", False, "oqw", "osw"),
+                                ("quant_weight_128x128_bf16 W transposed", True, "oqwt", "oswt")):
+            line("linear_trio", name, lambda s, tr=tr, q=q, sc=sc: fp8.fp8_quant_weight_128x128_bf16(
+                s["wh"], transpose_out=tr, q=s[q], s=s[sc]), sets, cfg, nbytes=sets[0]["wh"].numel() * 3)
         fl = 2.0 * TOK * IN * OUT
-        ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled(qx, sx, qw, sw, 0, torch.bfloat16, out=yb), T, W, stream)
-        extra_line("linear_trio", "gemm Fprop 8192x2048x7168 BF16", ms, flops=fl, args=args, config=cfg)
-        qy = torch.empty((TOK, OUT), dtype=torch.uint8, device="cuda")
-        sy = torch.empty((OUT // 128, TOK), dtype=torch.float32, device="cuda")
-        ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled_fp8out(qx, sx, qw, sw, q=qy, s=sy), T, W, stream)
-        extra_line("linear_trio", "gemm Fprop 8192x2048x7168, FP8 out (fused 1x128 quantization)", ms, flops=fl,
-                   args=args, config=cfg)
-        ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled(qd, sd, qwt, swt, 0, torch.bfloat16, out=dxb), T, W, stream)
-        extra_line("linear_trio", "gemm Dgrad 8192x7168x2048 BF16", ms, flops=fl, args=args, config=cfg)
-        ms = time_launches(lambda i: fp8.fp8_gemm_blockscaled(qdt, sdt, qxt, sxt, 1, torch.float32, out=dwf), T, W, stream)
-        extra_line("linear_trio", "gemm Wgrad 2048x7168x8192 FP32 (1x128 B)", ms, flops=fl, args=args, config=cfg)
+        g = fp8.fp8_gemm_blockscaled
+        line("linear_trio", "gemm Fprop 8192x2048x7168 BF16",
+             lambda s: g(s["qx"], s["sx"], s["qw"], s["sw"], 0, bf, out=s["yb"]), sets, cfg, flops=fl)
+        line("linear_trio", "gemm Fprop 8192x2048x7168, FP8 out (fused 1x128 quantization)",
+             lambda s: fp8.fp8_gemm_blockscaled_fp8out(s["qx"], s["sx"], s["qw"], s["sw"], q=s["qy"], s=s["sy"]),
+             sets, cfg, flops=fl)
+        line("linear_trio", "gemm Dgrad 8192x7168x2048 BF16",
+             lambda s: g(s["qd"], s["sd"], s["qwt"], s["swt"], 0, bf, out=s["dxb"]), sets, cfg, flops=fl)
+        line("linear_trio", "gemm Wgrad 2048x7168x8192 FP32 (1x128 B)",
+             lambda s: g(s["qdt"], s["sdt"], s["qxt"], s["sxt"], 1, torch.float32, out=s["dwf"]), sets, cfg,
+             flops=fl)
     elif args.workload == "moe_contig":
         G, N, K = 32, 4096, 7168
-        a, qa, sa, qb, sb, offs, counts, mt = contig_inputs(gen)
-        c = torch.empty((mt, N), dtype=torch.bfloat16, device="cuda")
+        sets = []
+        for _ in range(2):   # ~2.9 GB each
+            a, qa, sa, qb, sb, offs, counts, mt = contig_inputs(gen)
+            sets.append(dict(a=a, qa=qa, sa=sa, qb=qb, sb=sb, offs=offs,
+                             c=torch.empty((mt, N), dtype=torch.bfloat16, device="cuda"),
+                             qy=torch.zeros((mt, N), dtype=torch.uint8, device="cuda"),
+                             sy=torch.zeros((N // 128, mt), dtype=torch.float32, device="cuda")))
         cfg = {"experts": G, "routed_rows": int(counts.sum()), "padded_rows": mt, "N": N, "K": K}
-        ms = time_launches(lambda i: fp8.fp8_quant_act_1x128(a, q=qa, s=sa), T, W, stream)
-        extra_line("moe_contig", "quant_act_1x128 A rows", ms, nbytes=a.numel() * 5 + (a.numel() // 128) * 4,
-                   args=args, config=cfg)
-        ms = time_launches(lambda i: fp8.fp8_grouped_gemm_contiguous(qa, sa, qb, sb, offs, out=c), T, W, stream)
-        extra_line("moe_contig", "grouped_gemm_contiguous gate+up", ms, flops=2.0 * int(counts.sum()) * N * K,
-                   args=args, config=dict(cfg, flops_counted="valid rows only"))
-        del c
-        qy = torch.zeros((mt, N), dtype=torch.uint8, device="cuda")
-        sy = torch.zeros((N // 128, mt), dtype=torch.float32, device="cuda")
-        ms = time_launches(lambda i: fp8.fp8_grouped_gemm_contiguous_fp8out(qa, sa, qb, sb, offs, q=qy, s=sy),
-                           T, W, stream)
-        extra_line("moe_contig", "grouped_gemm_contiguous gate+up, FP8 out (fused 1x128 quantization)", ms,
-                   flops=2.0 * int(counts.sum()) * N * K, args=args,
-                   config=dict(cfg, flops_counted="valid rows only",
-                               output="FP8 codes + 1x128 scales along N: the down projection's A operand"))
+        na = sets[0]["a"].numel()
+        line("moe_contig", "quant_act_1x128 A rows",
+             lambda s: fp8.fp8_quant_act_1x128(s["a"], q=s["qa"], s=s["sa"]), sets, cfg,
+             nbytes=na * 5 + (na // 128) * 4)
+        fl = 2.0 * int(counts.sum()) * N * K
+        line("moe_contig", "grouped_gemm_contiguous gate+up",
+             lambda s: fp8.fp8_grouped_gemm_contiguous(s["qa"], s["sa"], s["qb"], s["sb"], s["offs"], out=s["c"]),
+             sets, dict(cfg, flops_counted="valid rows only"), flops=fl)
+        line("moe_contig", "grouped_gemm_contiguous gate+up, FP8 out (fused 1x128 quantization)",
+             lambda s: fp8.fp8_grouped_gemm_contiguous_fp8out(s["qa"], s["sa"], s["qb"], s["sb"], s["offs"],
+                                                              q=s["qy"], s=s["sy"]),
+             sets, dict(cfg, flops_counted="valid rows only",
+                        output="FP8 codes + 1x128 scales along N: the down projection's A operand"), flops=fl)
     elif args.workload == "moe_masked":
         G, MMAX = 32, 128
         for (N, K) in ((4096, 7168), (7168, 2048)):
-            mm, qa, sa, qb, sb, mmt, c = masked_inputs(gen, G, MMAX, N, K)
-            valid = int(mm.sum())
+            # the decode-tiled copies are rearranged once, when weights are
+            # loaded; the rearrangement is not in the timed loop
+            sets = masked_sets(gen, G, MMAX, N, K)
+            valid = int(sets[0]["mm"].sum())
             nbytes = G * N * K + G * (N // 128) * (K // 128) * 4 + valid * K + valid * (K // 128) * 4 + valid * N * 2
             cfg = {"experts": G, "M_max": MMAX, "valid_rows": valid, "N": N, "K": K,
                    "bytes": "all expert weights + scales + valid A rows + valid C rows"}
-            ms = time_launches(lambda i: fp8.fp8_grouped_gemm_masked(qa, sa, qb, sb, mmt, out=c), T, W, stream)
-            extra_line("moe_masked", f"grouped_gemm_masked N={N} K={K}", ms, nbytes=nbytes, args=args, config=cfg)
-            # the same GEMM on weights stored in the decode-tiled layout (rearranged
-            # once, when weights are loaded; the rearrangement is not in the timed loop)
-            qt = fp8.fp8_tile_weights_decode(qb)
-            ms = time_launches(lambda i: fp8.fp8_grouped_gemm_masked_tiled(qa, sa, qt, sb, mmt, out=c), T, W, stream)
-            extra_line("moe_masked", f"grouped_gemm_masked_tiled N={N} K={K}", ms, nbytes=nbytes, args=args,
-                       config=dict(cfg, weights="decode-tiled layout (fp8_tile_weights_decode)"))
-            del qb, sb, c, qt
+            line("moe_masked", f"grouped_gemm_masked N={N} K={K}",
+                 lambda s: fp8.fp8_grouped_gemm_masked(s["qa"], s["sa"], s["qb"], s["sb"], s["mmt"], out=s["c"]),
+                 sets, cfg, nbytes=nbytes)
+            line("moe_masked", f"grouped_gemm_masked_tiled N={N} K={K}",
+                 lambda s: fp8.fp8_grouped_gemm_masked_tiled(s["qa"], s["sa"], s["qt"], s["sb"], s["mmt"],
+                                                             out=s["c"]),
+                 sets, dict(cfg, weights="decode-tiled layout (fp8_tile_weights_decode)"), nbytes=nbytes)
+            del sets
 
 
 def main():
