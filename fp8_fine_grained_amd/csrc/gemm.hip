@@ -1575,6 +1575,24 @@ __device__ __forceinline__ void il_kloop(uint8_t* lds_raw, WStage<W>* ring, cons
     constexpr uint32_t kZeroLine = W::STAGES * sizeof(WStage<W>);
     u32x4 pfa[FM][2], pfb[IL_GW][2];   // an odd half-block's first fragments, read ahead
 
+    // Waves whose rows all lie past the tile's valid rows only copy.  Their
+    // loop is separate (`live` is uniform per wave), so the computing loop
+    // carries no values merged from a path that skips the compute.
+    if (!live) {
+        for (int hb = 0; hb < halves; hb += 2) {
+            wait_vmcnt<0>();
+            if ((hb + 2) * W::KS > K) {
+                cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[hb & 3]), hb, lane);
+                cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[(hb + 1) & 3]), hb + 1, lane);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+            __builtin_amdgcn_s_barrier();
+            const int f0 = hb + 2 < halves ? hb + 2 : halves - 1, f1 = hb + 3 < halves ? hb + 3 : halves - 1;
+            cp.copy(reinterpret_cast<uint8_t*>(&ring[(hb + 2) & 3]), f0);
+            cp.copy(reinterpret_cast<uint8_t*>(&ring[(hb + 3) & 3]), f1);
+        }
+        return;
+    }
     for (int hb = 0; hb < halves; hb += 2) {
         // both halves of this K-block have landed (this wave's copies: the
         // only loads in flight), then every wave's
@@ -1588,23 +1606,18 @@ __device__ __forceinline__ void il_kloop(uint8_t* lds_raw, WStage<W>* ring, cons
         // the next K-block's halves (past the end: the last half again, into
         // slots never read again)
         const int f0 = hb + 2 < halves ? hb + 2 : halves - 1, f1 = hb + 3 < halves ? hb + 3 : halves - 1;
-        if (live) {
-            w = nw;
-            // the even slot's scale piece holds the next K-block's scales
-            const bool more = hb + 2 < halves;
-            const int par = (hb >> 1) & 1;   // K-block parity: column ratios of the transition into it
-            wide_il_half<W, 0, COPIER, BS1>(lds_raw, hb & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 2) & 3,
-                                            f0, (hb + 3) & 3, f1, (hb + 1) & 3, pfa, pfb, cl, par, par ^ 1, more, lane);
+        w = nw;
+        // the even slot's scale piece holds the next K-block's scales
+        const bool more = hb + 2 < halves;
+        const int par = (hb >> 1) & 1;   // K-block parity: column ratios of the transition into it
+        wide_il_half<W, 0, COPIER, BS1>(lds_raw, hb & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 2) & 3,
+                                        f0, (hb + 3) & 3, f1, (hb + 1) & 3, pfa, pfb, cl, par, par ^ 1, more, lane);
 #pragma unroll
-            for (int mi = 0; mi < FM; ++mi)
-                ratio[mi] = more ? clamp_unit(w.unit[mi] * __builtin_amdgcn_rcpf(nw.unit[mi])) : 1.0f;
-            if (BS1) il_columns<W>(lds_raw, ring[hb & 3], cl, par ^ 1, more, wn, r, lane, nw);
-            wide_il_half<W, 1, COPIER, BS1>(lds_raw, (hb + 1) & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp,
-                                            0, 0, 0, 0, 0, pfa, pfb, cl, par ^ 1, par ^ 1, more, lane);
-        } else {
-            cp.copy(reinterpret_cast<uint8_t*>(&ring[(hb + 2) & 3]), f0);
-            cp.copy(reinterpret_cast<uint8_t*>(&ring[(hb + 3) & 3]), f1);
-        }
+        for (int mi = 0; mi < FM; ++mi)
+            ratio[mi] = more ? clamp_unit(w.unit[mi] * __builtin_amdgcn_rcpf(nw.unit[mi])) : 1.0f;
+        if (BS1) il_columns<W>(lds_raw, ring[hb & 3], cl, par ^ 1, more, wn, r, lane, nw);
+        wide_il_half<W, 1, COPIER, BS1>(lds_raw, (hb + 1) & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp,
+                                        0, 0, 0, 0, 0, pfa, pfb, cl, par ^ 1, par ^ 1, more, lane);
     }
 }
 
@@ -2048,6 +2061,7 @@ __global__ __launch_bounds__(WideTile::THREADS) void gemm_wide_b1_o1_dense(GemmA
 }
 const KernelEntry kWideB1Kernels[] = {{gemm_wide_b1_o0_dense, 2, 0, 1, 0, int(GemmMode::Dense), WideTile::THREADS},
                                       {gemm_wide_b1_o1_dense, 2, 0, 1, 1, int(GemmMode::Dense), WideTile::THREADS}};
+
 
 // ---------------------------------------------------------------------------
 // Persistent masked decode kernel on decode-tiled weights (gemm_dreg_*):
