@@ -85,7 +85,7 @@ __device__ __forceinline__ void quant_act_rows_bf16_body(const uint16_t* __restr
         u32x4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            v[u] = (kb0 + u) * kBlock + lane * 8 < K ? ld<u32x4>(xr + u * kBlock) : u32x4{0u, 0u, 0u, 0u};
+            v[u] = (kb0 + u) * kBlock + lane * 8 < K ? ld_once<u32x4>(xr + u * kBlock) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (kb0 + u >= kbs) break;
@@ -124,13 +124,13 @@ struct DenseSrc {
         const T* p = x + m * K + k;
         {
             if constexpr (E == 4) {
-                const v4f v = ld<v4f>(p);
+                const v4f v = ld_once<v4f>(p);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) e[j] = v[j];
             } else {
                 // (a bit_cast of a vector element would read element 0: shift
                 // and mask work on values)
-                const u32x4 w = ld<u32x4>(p);
+                const u32x4 w = ld_once<u32x4>(p);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     e[2 * j] = __builtin_bit_cast(float, w[j] << 16);
@@ -306,7 +306,7 @@ __device__ __forceinline__ void quant_weight_bf16_body(const uint16_t* __restric
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const u32x4 raw = cvalid && nb * kBlock + r8 + i < N ? ld<u32x4>(wb + int64_t(r8 + i) * K)
+        const u32x4 raw = cvalid && nb * kBlock + r8 + i < N ? ld_once<u32x4>(wb + int64_t(r8 + i) * K)
                                                               : u32x4{0u, 0u, 0u, 0u};
         lo[i] = widen_bf16x4(raw[0], raw[1]);
         hi[i] = widen_bf16x4(raw[2], raw[3]);
@@ -473,8 +473,8 @@ __global__ __launch_bounds__(256) void quant_mx_rows(const float* __restrict__ x
     for (int64_t m = int64_t(blockIdx.y) * 8 + (threadIdx.x >> 5); m < R; m += int64_t(gridDim.y) * 8) {
         v4f v0 = v4f{0.f, 0.f, 0.f, 0.f}, v1 = v0;
         if (valid) {
-            v0 = ld<v4f>(x + m * K + k);
-            v1 = ld<v4f>(x + m * K + k + 4);
+            v0 = ld_once<v4f>(x + m * K + k);
+            v1 = ld_once<v4f>(x + m * K + k + 4);
         }
         float amax = fmaxf(abs_max4(v0), abs_max4(v1));
         amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
