@@ -1474,11 +1474,13 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
         acc[mi][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, cb[g][k]),
                                                              __builtin_bit_cast(v8bf, ca[mi][k]), acc[mi][g], 0, 0, 0);
         // The waves that do not copy are the younger ones on each SIMD, which
-        // lose issue arbitration to the older; for the rest of the half-block
-        // they take the higher wave priority (measured: Wgrad 2% faster, the
-        // dense GEMM unchanged).
-        if (!COPIER && n == 0) __builtin_amdgcn_s_setprio(1);
-        if (!COPIER && n == NS - 1) __builtin_amdgcn_s_setprio(0);
+        // lose issue arbitration to the older.  In the even half-block, while
+        // the older waves issue the next K-block's copies, they take the
+        // higher wave priority (measured: Wgrad 2% and the dense GEMM 1%
+        // faster; raising it in the odd half-block as well gains nothing for
+        // Wgrad and costs the dense GEMM 1%, in the odd one only 3%).
+        if (!COPIER && !ODD && n == 0) __builtin_amdgcn_s_setprio(1);
+        if (!COPIER && !ODD && n == NS - 1) __builtin_amdgcn_s_setprio(0);
         if (n == RB_AT) {
 #pragma clang loop unroll(full)
             for (int g = IL_GW; g < FN; ++g)
