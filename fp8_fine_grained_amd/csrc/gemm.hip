@@ -1330,6 +1330,21 @@ constexpr IlPlan<FM, FN> make_il_plan(bool odd, int scale_slot, int scale_ops, i
     return p;
 }
 
+// the first slot of any cvt of k-steps 2 and 3 (chunk column 1) of A or of
+// the first group's B (the plan's)
+template <int FM, int FN>
+constexpr int il_first_k2_cvt(const IlPlan<FM, FN>& p) {
+    int first = IlPlan<FM, FN>::NS;
+    for (int k = 2; k < 4; ++k)
+        for (int q = 0; q < 4; ++q) {
+            for (int mi = 0; mi < FM; ++mi)
+                if (p.a[mi][k][q] < first) first = p.a[mi][k][q];
+            for (int g = 0; g < IL_GW; ++g)
+                if (p.b[g][k][q] < first) first = p.b[g][k][q];
+        }
+    return first;
+}
+
 // the first slot of any B cvt of n-tiles g0 and later (the plan's)
 template <int FM, int FN>
 constexpr int il_first_b_cvt(const IlPlan<FM, FN>& p, int g0) {
@@ -1407,15 +1422,23 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
     // plan's first cvt of a later group comes well after RB_AT).
     constexpr int RB_AT = 6;
     static_assert(il_first_b_cvt(P, IL_GW) > RB_AT, "later groups' B read before their first cvt");
+    // Of the fragments read here, only chunk column 0 (k-steps 0 and 1, the
+    // first eight MFMAs) is read before MFMA 0; chunk column 1 follows it (the
+    // plan's first cvt of k-steps 2 and 3 comes later), which halves the
+    // eight waves' read burst that every wave waits on after the barrier.
+    constexpr bool READ_HERE = !(ODD && PREFETCH);
+    static_assert(il_first_k2_cvt(P) > 0, "chunk column 1 read before its first cvt");
     u32x4 ra[FM][2], rb[FN][2];
 #pragma clang loop unroll(full)
-    for (int mi = 0; mi < FM; ++mi)
+    for (int mi = 0; mi < FM; ++mi) {
+        ra[mi][0] = READ_HERE ? read_a(uint32_t(slot), mi, 0) : pfa[mi][0];
+        if (!READ_HERE) ra[mi][1] = pfa[mi][1];
+    }
 #pragma clang loop unroll(full)
-        for (int j = 0; j < 2; ++j) ra[mi][j] = (ODD && PREFETCH) ? pfa[mi][j] : read_a(uint32_t(slot), mi, j);
-#pragma clang loop unroll(full)
-    for (int g = 0; g < IL_GW; ++g)
-#pragma clang loop unroll(full)
-        for (int j = 0; j < 2; ++j) rb[g][j] = (ODD && PREFETCH) ? pfb[g][j] : read_b(uint32_t(slot), g, j);
+    for (int g = 0; g < IL_GW; ++g) {
+        rb[g][0] = READ_HERE ? read_b(uint32_t(slot), g, 0) : pfb[g][0];
+        if (!READ_HERE) rb[g][1] = pfb[g][1];
+    }
     u32x4 ca[FM][4], cb[FN][4];
     v4f rbq[FN][4];   // 1x128 B: column ratios of elements 4q .. 4q + 3 of n-tile g
     // the VALU work planned for slot n
@@ -1481,6 +1504,12 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
         // Wgrad and costs the dense GEMM 1%, in the odd one only 3%).
         if (!COPIER && !ODD && n == 0) __builtin_amdgcn_s_setprio(1);
         if (!COPIER && !ODD && n == NS - 1) __builtin_amdgcn_s_setprio(0);
+        if (READ_HERE && n == 0) {
+#pragma clang loop unroll(full)
+            for (int mi = 0; mi < FM; ++mi) ra[mi][1] = read_a(uint32_t(slot), mi, 1);
+#pragma clang loop unroll(full)
+            for (int g = 0; g < IL_GW; ++g) rb[g][1] = read_b(uint32_t(slot), g, 1);
+        }
         if (n == RB_AT) {
 #pragma clang loop unroll(full)
             for (int g = IL_GW; g < FN; ++g)
