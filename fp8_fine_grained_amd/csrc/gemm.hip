@@ -1784,7 +1784,8 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
         const int64_t m = wrow0 + mi * 32 + r;
         if (m >= t.rows_valid) continue;
 #pragma unroll
-        for (int ni = 0; ni < FN; ++ni)
+        for (int ni = 0; ni < FN; ++ni) {
+            uint32_t d[4][2];   // BF16 out: the four runs of four columns, two dwords each
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
@@ -1795,11 +1796,30 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
                 if (OUT == 1) {
                     st<v4f>(static_cast<float*>(args.c) + idx, v);
                 } else {
-                    const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-                    const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-                    st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
+                    d[j][0] = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+                    d[j][1] = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
                 }
             }
+            if (OUT == 0) {
+                // Lanes r and r + 32 hold the two halves of every run of eight
+                // columns (8 j .. 8 j + 3 and 8 j + 4 .. 8 j + 7 of the row).
+                // One swap across the wave's halves gives lane r both halves of
+                // runs j = 0, 2 and lane r + 32 both halves of runs 1, 3: one
+                // 16-byte store per run of eight, half the store instructions.
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const auto sw = __builtin_amdgcn_permlane32_swap(d[2 * pr][q], d[2 * pr + 1][q], false, false);
+                        d[2 * pr][q] = sw[0];
+                        d[2 * pr + 1][q] = sw[1];
+                    }
+                    const int64_t idx = t.c_base + m * N + n0 + wn * FN * 32 + ni * 32 + 16 * pr + 8 * h;
+                    st<u32x4>(static_cast<uint16_t*>(args.c) + idx,
+                              u32x4{d[2 * pr][0], d[2 * pr][1], d[2 * pr + 1][0], d[2 * pr + 1][1]});
+                }
+            }
+        }
     }
 }
 
