@@ -472,6 +472,49 @@ __device__ __forceinline__ void wait_copies(int later) {
     }
 }
 
+// C stores of one 32x32 MFMA tile row.  Lane l holds row l % 32 and, for
+// j = 0..3, the run of four columns 8 j + 4 (l / 32) .. + 3, so lanes r and
+// r + 32 hold the two halves of each run of eight columns 8 j .. 8 j + 7.  One
+// swap across the wave's halves gives lane r both halves of runs 0 and 2 and
+// lane r + 32 both halves of runs 1 and 3: each lane then writes two runs of
+// eight columns (at 16 pr + 8 h) in place of four runs of four, half the
+// store instructions, each twice as wide.  Both lanes of a pair hold the same
+// row, so a per-row mask keeps the pair together; every lane of the wave that
+// is still active must take part in the swap.  d[j] holds the lane's packed
+// words of run j; p points at the tile's column 0 in the lane's row; runs at
+// or past `cols` are not written (`cols` a multiple of 8).
+template <int W>
+__device__ __forceinline__ void pair_runs(uint32_t (&d)[4][W]) {
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(d[2 * pr][q], d[2 * pr + 1][q], false, false);
+            d[2 * pr][q] = sw[0];
+            d[2 * pr + 1][q] = sw[1];
+        }
+}
+
+__device__ __forceinline__ void store_bf16_runs(uint16_t* p, int h, uint32_t (&d)[4][2], int cols = 32) {
+    pair_runs<2>(d);
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr)
+        if (16 * pr + 8 * h < cols)
+            st<u32x4>(p + 16 * pr + 8 * h, u32x4{d[2 * pr][0], d[2 * pr][1], d[2 * pr + 1][0], d[2 * pr + 1][1]});
+}
+
+__device__ __forceinline__ void store_fp8_runs(uint8_t* p, int h, uint32_t (&d)[4][1]) {
+    pair_runs<1>(d);
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) st<u32x2>(p + 16 * pr + 8 * h, u32x2{d[2 * pr][0], d[2 * pr + 1][0]});
+}
+
+// BF16 bits of four accumulator values, two to a word
+__device__ __forceinline__ void bf16_words(v4f v, uint32_t (&w)[2]) {
+    w[0] = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+    w[1] = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+}
+
 template <int WAVES_M, int WAVES_N, int FM_, int FN_, int STAGES_, int ENGINE, int BSCALE_1x128, int OUT_FP32, int MODE>
 __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
     typedef Cfg<WAVES_M, WAVES_N, FM_, FN_, STAGES_> C;
@@ -562,23 +605,28 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& args) {
         const int64_t m = wrow0 + mi * 32 + (lane & 31);
         if (m >= t.rows_valid) continue;
 #pragma unroll
-        for (int ni = 0; ni < FN; ++ni)
+        for (int ni = 0; ni < FN; ++ni) {
+            // runs of four or eight columns start on multiples of 4 and N % 16 == 0:
+            // a run lies wholly before N or wholly after it
+            const int64_t col0 = n0 + wn * FN * 32 + ni * 32;   // the 32x32 tile's column 0
+            const int64_t cols = N - col0;                      // the same on every lane
+            if (cols <= 0) continue;
+            const int hh = lane >> 5;
+            uint32_t d[4][2];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                // a run of four columns starts on a multiple of 4 and N % 16 == 0:
-                // the run lies wholly before N or wholly after it
-                if (n0 + n_lane + ni * 32 + 8 * j >= N) continue;
-                const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
                 const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
                                   acc[mi][ni][4 * j + 3]};
                 if (OUT_FP32) {
-                    st<v4f>(static_cast<float*>(args.c) + idx, v);
+                    if (8 * j + 4 * hh < cols) st<v4f>(static_cast<float*>(args.c) + t.c_base + m * N + col0 + 8 * j + 4 * hh, v);
                 } else {
-                    const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-                    const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-                    st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
+                    bf16_words(v, d[j]);
                 }
             }
+            if (!OUT_FP32)
+                store_bf16_runs(static_cast<uint16_t*>(args.c) + t.c_base + m * N + col0, hh, d,
+                                cols < 32 ? int(cols) : 32);
+        }
     }
 }
 
@@ -1054,14 +1102,16 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args, uint8_t* ld
             const int64_t m = wrow0 + mi * 32 + r;
             if (m >= t.rows_valid) continue;
 #pragma unroll
-            for (int ni = 0; ni < FN; ++ni)
+            for (int ni = 0; ni < FN; ++ni) {
+                uint32_t d[4][1];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
                                       acc[mi][ni][4 * j + 3]} * w.unit[mi];
-                    st<uint32_t>(static_cast<uint8_t*>(args.c) + m * N + n0 + n_lane + ni * 32 + 8 * j,
-                                 encode4(v, sc, rc));
+                    d[j][0] = encode4(v, sc, rc);
                 }
+                store_fp8_runs(static_cast<uint8_t*>(args.c) + m * N + n0 + wn * FN * 32 + ni * 32, h, d);
+            }
             if (h == 0) args.cs[(n0 / 128 + wn) * args.M + m] = sc;
         }
         return;
@@ -1071,20 +1121,20 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& args, uint8_t* ld
         const int64_t m = wrow0 + mi * 32 + r;
         if (m >= t.rows_valid) continue;
 #pragma unroll
-        for (int ni = 0; ni < FN; ++ni)
+        for (int ni = 0; ni < FN; ++ni) {
+            uint32_t d[4][2];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
                 const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
                                   acc[mi][ni][4 * j + 3]} * w.unit[mi];
-                if (OUT == 1) {
+                if (OUT == 1)
                     st<v4f>(static_cast<float*>(args.c) + idx, v);
-                } else {
-                    const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-                    const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-                    st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
-                }
+                else
+                    bf16_words(v, d[j]);
             }
+            if (OUT == 0) store_bf16_runs(static_cast<uint16_t*>(args.c) + t.c_base + m * N + n0 + wn * FN * 32 + ni * 32, h, d);
+        }
     }
 }
 
@@ -1767,14 +1817,16 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
             const int64_t m = wrow0 + mi * 32 + r;
             if (m >= t.rows_valid) continue;
 #pragma unroll
-            for (int ni = 0; ni < FN; ++ni)
+            for (int ni = 0; ni < FN; ++ni) {
+                uint32_t d[4][1];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
                                       acc[mi][ni][4 * j + 3]} * w.unit[mi];
-                    st<uint32_t>(static_cast<uint8_t*>(args.c) + m * N + n0 + n_lane + ni * 32 + 8 * j,
-                                 encode4(v, sc, rc));
+                    d[j][0] = encode4(v, sc, rc);
                 }
+                store_fp8_runs(static_cast<uint8_t*>(args.c) + m * N + n0 + wn * FN * 32 + ni * 32, h, d);
+            }
             if (h == 0) args.cs[(n0 / 128 + wn) * args.M + m] = sc;
         }
         return;
@@ -1793,32 +1845,12 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
                             acc[mi][ni][4 * j + 3]} * w.unit[mi];
                 if (BS1)   // the columns' last mantissa parts
                     v = v * ld<v4f>(lds_raw + cl + 1024u + uint32_t((ni * 32 + 8 * j + 4 * h) * 4));
-                if (OUT == 1) {
+                if (OUT == 1)
                     st<v4f>(static_cast<float*>(args.c) + idx, v);
-                } else {
-                    d[j][0] = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-                    d[j][1] = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-                }
+                else
+                    bf16_words(v, d[j]);
             }
-            if (OUT == 0) {
-                // Lanes r and r + 32 hold the two halves of every run of eight
-                // columns (8 j .. 8 j + 3 and 8 j + 4 .. 8 j + 7 of the row).
-                // One swap across the wave's halves gives lane r both halves of
-                // runs j = 0, 2 and lane r + 32 both halves of runs 1, 3: one
-                // 16-byte store per run of eight, half the store instructions.
-#pragma unroll
-                for (int pr = 0; pr < 2; ++pr) {
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const auto sw = __builtin_amdgcn_permlane32_swap(d[2 * pr][q], d[2 * pr + 1][q], false, false);
-                        d[2 * pr][q] = sw[0];
-                        d[2 * pr + 1][q] = sw[1];
-                    }
-                    const int64_t idx = t.c_base + m * N + n0 + wn * FN * 32 + ni * 32 + 16 * pr + 8 * h;
-                    st<u32x4>(static_cast<uint16_t*>(args.c) + idx,
-                              u32x4{d[2 * pr][0], d[2 * pr][1], d[2 * pr + 1][0], d[2 * pr + 1][1]});
-                }
-            }
+            if (OUT == 0) store_bf16_runs(static_cast<uint16_t*>(args.c) + t.c_base + m * N + n0 + wn * FN * 32 + ni * 32, h, d);
         }
     }
 }
@@ -2022,20 +2054,20 @@ __device__ __forceinline__ void gemm_mx_body(const GemmArgs& args) {
         const int64_t m = wrow0 + mi * 32 + r;
         if (m >= t.rows_valid) continue;
 #pragma unroll
-        for (int ni = 0; ni < FN; ++ni)
+        for (int ni = 0; ni < FN; ++ni) {
+            uint32_t d[4][2];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t idx = m * N + n0 + n_lane + ni * 32 + 8 * j;
                 const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
                                   acc[mi][ni][4 * j + 3]};
-                if (OUT_FP32) {
+                if (OUT_FP32)
                     st<v4f>(static_cast<float*>(args.c) + idx, v);
-                } else {
-                    const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-                    const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-                    st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
-                }
+                else
+                    bf16_words(v, d[j]);
             }
+            if (!OUT_FP32) store_bf16_runs(static_cast<uint16_t*>(args.c) + m * N + n0 + wn * FN * 32 + ni * 32, h, d);
+        }
     }
 }
 
@@ -2329,20 +2361,20 @@ __device__ __forceinline__ void dreg_store(const GemmArgs& args, const DregSrc& 
         const int m = mi * 32 + r;
         if (m >= c.rows) continue;
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < 2; ++ni) {
+            uint32_t d[4][2];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t idx = c.c_off + int64_t(m) * N + n_lane + ni * 32 + 8 * j;
                 const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
                                   acc[mi][ni][4 * j + 3]} * w.unit[mi];
-                if (OUT == 1) {
+                if (OUT == 1)
                     st<v4f>(static_cast<float*>(args.c) + idx, v);
-                } else {
-                    const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-                    const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-                    st<u32x2>(static_cast<uint16_t*>(args.c) + idx, u32x2{lo, hi});
-                }
+                else
+                    bf16_words(v, d[j]);
             }
+            if (OUT == 0) store_bf16_runs(static_cast<uint16_t*>(args.c) + c.c_off + int64_t(m) * N + wave * 64 + ni * 32, h, d);
+        }
     }
 }
 
