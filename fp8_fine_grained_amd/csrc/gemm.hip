@@ -1151,9 +1151,11 @@ struct IlCopier {
     static constexpr int AP = W::BM / W::ROWS_PER_PIECE / CW, BP = W::BN / W::ROWS_PER_PIECE / CW;
     static_assert(AP * W::ROWS_PER_PIECE * CW == W::BM && BP * W::ROWS_PER_PIECE * CW == W::BN, "whole pieces");
     rsrc_t ra, rb, rs;
-    uint32_t va[AP], vb[BP], vs, s_step;
+    // B pieces: every row lies in range, so piece i's offset is piece 0's
+    // plus a uniform step, carried in the scalar offset (one VGPR, not BP)
+    uint32_t va[AP], vb0, b_step, vs, s_step;
     int a_lds[AP], b_lds[BP], s_lds;
-    int a_c16[AP], b_c16[BP];
+    int c16;   // the lane's 16-byte chunk within a row (the same in every piece: r0 % 16 == 0)
     int64_t K;
     bool copier;               // uniform: this wave copies operand data
 
@@ -1165,8 +1167,8 @@ struct IlCopier {
         if (i < AP)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + a_lds[i]), 16, va[i], koff, 0, 0);
         else if (i < AP + BP)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i - AP]), 16, vb[i - AP], koff, 0,
-                                                     0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i - AP]), 16, vb0,
+                                                     koff + uint32_t(i - AP) * b_step, 0, 0);
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs,
                                                      uint32_t((h >> 1) + 1) * s_step, 0, 0);
@@ -1184,13 +1186,11 @@ struct IlCopier {
     // there -- the next row, or zeros past the buffer's range)
     __device__ __forceinline__ void zero_tail(uint8_t* stage, int h, int lane) const {
         if (!copier) return;
-        const int64_t koff = int64_t(h) * W::KS;
+        if (int64_t(h) * W::KS + c16 < K) return;
 #pragma unroll
-        for (int i = 0; i < AP; ++i)
-            if (koff + a_c16[i] >= K) st<u32x4>(stage + a_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
+        for (int i = 0; i < AP; ++i) st<u32x4>(stage + a_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
-        for (int i = 0; i < BP; ++i)
-            if (koff + b_c16[i] >= K) st<u32x4>(stage + b_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
+        for (int i = 0; i < BP; ++i) st<u32x4>(stage + b_lds[i] + lane * 16, u32x4{0u, 0u, 0u, 0u});
     }
 };
 
@@ -1207,23 +1207,24 @@ __device__ __forceinline__ IlCopier<W, CW> make_il_copier(const Tile& t, int wav
     const int64_t tile_rows = t.rows_valid - t.m0 < W::BM ? t.rows_valid - t.m0 : W::BM;   // >= 1
     c.ra = make_rsrc(t.A + t.m0 * K, uint32_t(tile_rows * K));
     c.rb = make_rsrc(t.B + n0 * K, uint32_t(W::BN * K));
+    // row r = r0 + sub of a piece holds the lane's chunk at slot ^ ((r >> 2) & 3),
+    // and with r0 % 16 == 0 (sub < 16) that is slot ^ ((sub >> 2) & 3) in every piece
+    static_assert(W::ROWS_PER_PIECE % 16 == 0, "one swizzle phase per piece");
+    c.c16 = (slot ^ ((sub >> 2) & 3)) * 16;
 #pragma unroll
     for (int i = 0; i < C::AP; ++i) {
         const int r0 = (cw * C::AP + i) * W::ROWS_PER_PIECE, r = r0 + sub;
-        const int chunk = slot ^ ((r >> 2) & 3);
         const int64_t row = r < tile_rows ? r : tile_rows - 1;      // clamp: loaded, never stored
-        c.va[i] = uint32_t(row * K + chunk * 16);
-        c.a_c16[i] = chunk * 16;
+        c.va[i] = uint32_t(row * K + c.c16);
         c.a_lds[i] = int(offsetof(S, a)) + r0 * W::KS;
     }
 #pragma unroll
     for (int i = 0; i < C::BP; ++i) {
         const int r0 = (cw * C::BP + i) * W::ROWS_PER_PIECE, r = r0 + sub;
-        const int chunk = slot ^ ((r >> 2) & 3);
-        c.vb[i] = uint32_t(int64_t(r) * K + chunk * 16);
-        c.b_c16[i] = chunk * 16;
+        if (i == 0) c.vb0 = uint32_t(int64_t(r) * K + c.c16);
         c.b_lds[i] = int(offsetof(S, b)) + r0 * W::KS;
     }
+    c.b_step = uint32_t(W::ROWS_PER_PIECE * K);
     const int64_t kbs = (K + BK - 1) / BK;
     if (wave < W::A_SCALE_WAVES) {        // A scales of rows 64 wave .. +63 (clamped)
         const int64_t rr = int64_t(wave) * 64 + lane;
@@ -1287,6 +1288,11 @@ constexpr int IL_COPY_WAVES = 4;
 //   - an odd half-block's A fragments and first group's B fragments are read
 //     from LDS during the even half-block (into registers its first group has
 //     finished with), so the odd half-block starts without an LDS burst;
+//   - the K-block's barrier itself sits in the odd half-block before it, 12
+//     MFMAs before its end, and each wave reads the new K-block's first
+//     fragments right after it: the even half-block starts without an LDS
+//     burst too (1x128 B keeps the barrier at the K-block's start: its loop
+//     has no registers for the fragments read ahead);
 //   - a compile-time plan (make_il_plan) gives every cvt and multiply a slot,
 //     the gap after one MFMA: at most IL_CAP VALU instructions per slot, cvts
 //     one MFMA before their first use, a tile's multiplies two MFMAs after its
@@ -1414,6 +1420,17 @@ __device__ __forceinline__ uint32_t widen_q(const u32x4& raw, int hh, int q, flo
                                                 : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, p2, false));
 }
 
+// The 16-byte chunk j (k-steps 2 j and 2 j + 1) of fragment row `row` (of
+// the A part at `part` = offsetof(WStage, a), or of B) from LDS slot sl, as
+// the lane reads it in a half-block; `zero`: the zero line instead.
+template <class W>
+__device__ __forceinline__ u32x4 il_frag(const uint8_t* lds, uint32_t sl, uint32_t part, int row, int r, int h,
+                                         int j, bool zero, uint32_t zero_line) {
+    const uint32_t ch = uint32_t(((2 * j + h) ^ ((r >> 2) & 3)) << 4);
+    const uint32_t at = sl * uint32_t(sizeof(WStage<W>)) + part + uint32_t(row * W::KS) + ch;
+    return ld<u32x4>(lds + (zero ? zero_line + ch : at));
+}
+
 // Even half-blocks also turn the stage's scale piece (the next K-block's
 // scales) into `next`: its LDS reads go out with the fragment reads, its
 // arithmetic runs in four slots of the last group, whose room the plan keeps.
@@ -1424,7 +1441,7 @@ __device__ __forceinline__ uint32_t widen_q(const u32x4& raw, int hh, int q, flo
 // the columns' current mantissa parts); the column ratios of the next
 // transition are computed here (even half-blocks), two columns per lane.  No
 // fragments are read ahead for the odd half-block (no registers for them).
-template <class W, int ODD, bool COPIER, bool BS1 = false>
+template <class W, int ODD, bool COPIER, bool BS1, class Sync>
 __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int wn, int r, int h,
                                              const WideScales<W::FM>& w, const float (&ratio)[W::FM],
                                              uint32_t zero_line, v16f (&acc)[W::FM][W::FN],
@@ -1432,7 +1449,7 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
                                              int fill_slot, int fill_h, int fill2_slot, int fill2_h, int pf_slot,
                                              u32x4 (&pfa)[W::FM][2],
                                              u32x4 (&pfb)[IL_GW][2], uint32_t cl, int rpar, int wpar, bool more,
-                                             int lane) {
+                                             int lane, u32x4 (&ea)[W::FM], u32x4 (&eb)[IL_GW], const Sync& sync) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device code only: the host pass never runs it
     constexpr int IL_SCALE_OPS = 32;
     constexpr int FM = W::FM, FN = W::FN, NS = 4 * FM * FN, SS = NS - 12;
@@ -1440,10 +1457,22 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
     constexpr IlPlan<FM, FN> P = make_il_plan<FM, FN>(ODD != 0, SS, ODD ? 0 : IL_SCALE_OPS, BS1 ? 2 : 1,
                                                       BS1 ? 9 : IL_CAP);
     constexpr bool PREFETCH = !BS1;   // odd half-blocks' first fragments read during the even one
+    // Without 1x128 B the K-block's barrier sits in the odd half-block before
+    // it, after MFMA SYNC_AT: there each wave waits for its copies of the next
+    // K-block, meets the others, and reads that K-block's first fragments
+    // (chunk column 0 of A and of the first group's B, into ea / eb) while the
+    // last MFMAs of this one run on registers.  So no wave starts a K-block
+    // waiting on LDS.  Every read of this K-block's slots comes before
+    // SYNC_AT (the odd half-block's own reads at RB_AT, the rest during the
+    // even one), so the copies that follow the barrier may overwrite them.
+    constexpr bool LOB = !BS1;
+    constexpr int SYNC_AT = 4 * FM * FN - 12;
     const WStage<W>& sg = *reinterpret_cast<const WStage<W>*>(lds + uint32_t(slot) * uint32_t(sizeof(WStage<W>)));
     float nsa[FM], nsb = 0.0f;
     if (!ODD) {
-        if (!BS1) nsb = sg.sb[((wn * FN * 32) / 128) * 64];
+        // (the wave's n-block scale: one value, kept in a scalar register)
+        if (!BS1) nsb = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                            __builtin_bit_cast(int, sg.sb[((wn * FN * 32) / 128) * 64])));
 #pragma clang loop unroll(full)
         for (int mi = 0; mi < FM; ++mi) nsa[mi] = sg.sa[wm * FM * 32 + mi * 32 + r];
     }
@@ -1481,12 +1510,12 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
     u32x4 ra[FM][2], rb[FN][2];
 #pragma clang loop unroll(full)
     for (int mi = 0; mi < FM; ++mi) {
-        ra[mi][0] = READ_HERE ? read_a(uint32_t(slot), mi, 0) : pfa[mi][0];
+        ra[mi][0] = READ_HERE ? (LOB ? ea[mi] : read_a(uint32_t(slot), mi, 0)) : pfa[mi][0];
         if (!READ_HERE) ra[mi][1] = pfa[mi][1];
     }
 #pragma clang loop unroll(full)
     for (int g = 0; g < IL_GW; ++g) {
-        rb[g][0] = READ_HERE ? read_b(uint32_t(slot), g, 0) : pfb[g][0];
+        rb[g][0] = READ_HERE ? (LOB ? eb[g] : read_b(uint32_t(slot), g, 0)) : pfb[g][0];
         if (!READ_HERE) rb[g][1] = pfb[g][1];
     }
     u32x4 ca[FM][4], cb[FN][4];
@@ -1554,6 +1583,22 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
         // Wgrad and costs the dense GEMM 1%, in the odd one only 3%).
         if (!COPIER && !ODD && n == 0) __builtin_amdgcn_s_setprio(1);
         if (!COPIER && !ODD && n == NS - 1) __builtin_amdgcn_s_setprio(0);
+        if (LOB && ODD && n == SYNC_AT) {
+            static_assert(!LOB || SYNC_AT > RB_AT, "this K-block's slots read after the barrier");
+            // (after the last K-block the reads still go out, of a slot no
+            // one uses again: ea / eb are then dead once the even half-block
+            // has taken them, not held through it)
+            if (more) sync();
+            const uint32_t nsl = uint32_t((slot + 1) & 3);   // the next K-block's even slot
+#pragma clang loop unroll(full)
+            for (int mi = 0; mi < FM; ++mi)
+                ea[mi] = il_frag<W>(lds, nsl, uint32_t(offsetof(WStage<W>, a)), wm * FM * 32 + mi * 32 + r, r, h,
+                                    0, next.zero[mi] != 0, zero_line);
+#pragma clang loop unroll(full)
+            for (int g = 0; g < IL_GW; ++g)
+                eb[g] = il_frag<W>(lds, nsl, uint32_t(offsetof(WStage<W>, b)), wn * FN * 32 + g * 32 + r, r, h, 0,
+                                   false, zero_line);
+        }
         if (READ_HERE && n == 0) {
 #pragma clang loop unroll(full)
             for (int mi = 0; mi < FM; ++mi) ra[mi][1] = read_a(uint32_t(slot), mi, 1);
@@ -1674,16 +1719,36 @@ __device__ __forceinline__ void il_kloop(uint8_t* lds_raw, WStage<W>* ring, cons
         }
         return;
     }
-    for (int hb = 0; hb < halves; hb += 2) {
-        // both halves of this K-block have landed (this wave's copies: the
-        // only loads in flight), then every wave's
+    // Both halves of K-block kb have landed (this wave's copies: the only
+    // loads in flight), then every wave's; a partial last K-block's slots
+    // are zeroed past K first.  Without 1x128 B this runs in the odd
+    // half-block of kb - 1 (wide_il_half), and before the loop for kb = 0.
+    auto kblock_sync = [&](int hbk) {
         wait_vmcnt<0>();
-        if ((hb + 2) * W::KS > K) {           // partial last K-block (uniform)
-            cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[hb & 3]), hb, lane);
-            cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[(hb + 1) & 3]), hb + 1, lane);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const bool partial = (hbk + 2) * W::KS > K;   // partial last K-block (uniform)
+        if (partial) {
+            cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[hbk & 3]), hbk, lane);
+            cp.zero_tail(reinterpret_cast<uint8_t*>(&ring[(hbk + 1) & 3]), hbk + 1, lane);
         }
+        // (mid-K-block, this wave's reads of the slots the copies after the
+        // barrier refill are all done as well)
+        if (!BS1 || partial) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
+    };
+    u32x4 ea[FM], eb[IL_GW];   // the next K-block's first fragments, read at its barrier
+    if (!BS1) {
+        kblock_sync(0);
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi)
+            ea[mi] = il_frag<W>(lds_raw, 0u, uint32_t(offsetof(WStage<W>, a)), wm * FM * 32 + mi * 32 + r, r, h, 0,
+                                nw.zero[mi] != 0, kZeroLine);
+#pragma unroll
+        for (int g = 0; g < IL_GW; ++g)
+            eb[g] = il_frag<W>(lds_raw, 0u, uint32_t(offsetof(WStage<W>, b)), wn * W::FN * 32 + g * 32 + r, r, h, 0,
+                               false, kZeroLine);
+    }
+    for (int hb = 0; hb < halves; hb += 2) {
+        if (BS1) kblock_sync(hb);
         // the next K-block's halves (past the end: the last half again, into
         // slots never read again)
         const int f0 = hb + 2 < halves ? hb + 2 : halves - 1, f1 = hb + 3 < halves ? hb + 3 : halves - 1;
@@ -1691,14 +1756,17 @@ __device__ __forceinline__ void il_kloop(uint8_t* lds_raw, WStage<W>* ring, cons
         // the even slot's scale piece holds the next K-block's scales
         const bool more = hb + 2 < halves;
         const int par = (hb >> 1) & 1;   // K-block parity: column ratios of the transition into it
+        const auto no_sync = [] {};
+        const auto next_sync = [&] { kblock_sync(hb + 2); };
         wide_il_half<W, 0, COPIER, BS1>(lds_raw, hb & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 2) & 3,
-                                        f0, (hb + 3) & 3, f1, (hb + 1) & 3, pfa, pfb, cl, par, par ^ 1, more, lane);
+                                        f0, (hb + 3) & 3, f1, (hb + 1) & 3, pfa, pfb, cl, par, par ^ 1, more, lane,
+                                        ea, eb, no_sync);
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi)
             ratio[mi] = more ? clamp_unit(w.unit[mi] * __builtin_amdgcn_rcpf(nw.unit[mi])) : 1.0f;
         if (BS1) il_columns<W>(lds_raw, ring[hb & 3], cl, par ^ 1, more, wn, r, lane, nw);
         wide_il_half<W, 1, COPIER, BS1>(lds_raw, (hb + 1) & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp,
-                                        0, 0, 0, 0, 0, pfa, pfb, cl, par ^ 1, par ^ 1, more, lane);
+                                        0, 0, 0, 0, 0, pfa, pfb, cl, par ^ 1, par ^ 1, more, lane, ea, eb, next_sync);
     }
 }
 
