@@ -192,6 +192,30 @@ __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile, int
         const int64_t x = tile % args.xcds, j = tile / args.xcds;
         tile = (x + args.xcds * (j / n_tiles)) * n_tiles + j % n_tiles;
     }
+    if (MODE == int(GemmMode::Dense) && args.xcds > 1 && tile < ((args.M + BM - 1) / BM) * n_tiles) {
+        // Workgroup w runs on XCD w mod xcds, and the workgroups of one XCD
+        // start in order of w.  XCD x takes the x-th run of Q = T / xcds
+        // consecutive tiles (T tiles in all; the last T mod xcds keep their
+        // index) of an order that walks groups of GM m-tiles column by
+        // column, so the tiles an XCD runs at once form a compact block
+        // (4 x 8 for 32 CUs) whose A and B rows its L2 shares.  A bijection
+        // on [0, T): the bits are those of the plain order.
+        constexpr int64_t GM = 4;
+        const int64_t m_tiles = (args.M + BM - 1) / BM, T = m_tiles * n_tiles, X = args.xcds, Q = T / X;
+        const int64_t L = tile < Q * X ? (tile % X) * Q + tile / X : tile;
+        const int64_t full = (m_tiles / GM) * GM * n_tiles;   // tiles in whole groups
+        int64_t mt, bn;
+        if (L < full) {
+            const int64_t rem = L % (GM * n_tiles);
+            bn = rem / GM;
+            mt = (L / (GM * n_tiles)) * GM + rem % GM;
+        } else {
+            const int64_t h = m_tiles - (m_tiles / GM) * GM, rem = L - full;   // the last, shorter group
+            bn = rem / h;
+            mt = (m_tiles / GM) * GM + rem % h;
+        }
+        tile = mt * n_tiles + bn;
+    }
     t.bn = int(tile % n_tiles);
     tile /= n_tiles;
     t.A = args.a;
@@ -2773,6 +2797,8 @@ hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, c
                                    : tile == 1 ? DecodeTile::BM
                                    : tile == 2 ? WideTile::BM
                                                : WideDecodeTile::BM);
+    else if (mode == GemmMode::Dense)
+        a.xcds = kXcds;
     for (const KernelEntry* table : {kKernels, kWideKernels, kWideB1Kernels}) {
         const size_t count = table == kKernels       ? sizeof(kKernels) / sizeof(kKernels[0])
                              : table == kWideKernels ? sizeof(kWideKernels) / sizeof(kWideKernels[0])
@@ -2790,8 +2816,10 @@ hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, c
 hipError_t launch_mx(int out_fp32, const GemmArgs& args, hipStream_t stream) {
     const int64_t tiles = ((args.M + MxTile::BM - 1) / MxTile::BM) * (args.N / MxTile::BN);
     if (tiles == 0) return hipSuccess;
+    GemmArgs a = args;
+    a.xcds = kXcds;
     return launch_kernel(out_fp32 ? gemm_mx_o1_dense : gemm_mx_o0_dense, dim3(unsigned(tiles)),
-                         dim3(MxTile::THREADS), stream, args);
+                         dim3(MxTile::THREADS), stream, a);
 }
 
 hipError_t launch_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream) {

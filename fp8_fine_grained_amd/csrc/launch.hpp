@@ -45,7 +45,7 @@ struct GemmArgs {
     int64_t N, K;
     int64_t G;              // groups (1 for dense)
     float* cs;              // output scales [N/128][M] of the FP8 output mode (else unused)
-    int xcds = 1;           // masked layout: XCDs whose L2s the tile order groups experts for (1: none)
+    int xcds = 1;           // XCDs whose L2s the tile order groups tiles for (1: the plain order)
 };
 
 // MX GEMM: args.sa / args.sb carry the E8M0 scale bytes ([K/32][M], [K/32][N])
