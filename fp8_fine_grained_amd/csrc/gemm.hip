@@ -1312,7 +1312,7 @@ constexpr int IL_COPY_WAVES = 4;
 //   - an odd half-block's A fragments and first group's B fragments are read
 //     from LDS during the even half-block (into registers its first group has
 //     finished with), so the odd half-block starts without an LDS burst;
-//   - the K-block's barrier itself sits in the odd half-block before it, 12
+//   - the K-block's barrier itself sits in the odd half-block before it, 14
 //     MFMAs before its end, and each wave reads the new K-block's first
 //     fragments right after it: the even half-block starts without an LDS
 //     burst too (1x128 B keeps the barrier at the K-block's start: its loop
@@ -1490,7 +1490,7 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
     // SYNC_AT (the odd half-block's own reads at RB_AT, the rest during the
     // even one), so the copies that follow the barrier may overwrite them.
     constexpr bool LOB = !BS1;
-    constexpr int SYNC_AT = 4 * FM * FN - 12;
+    constexpr int SYNC_AT = 4 * FM * FN - 14;
     const WStage<W>& sg = *reinterpret_cast<const WStage<W>*>(lds + uint32_t(slot) * uint32_t(sizeof(WStage<W>)));
     float nsa[FM], nsb = 0.0f;
     if (!ODD) {
