@@ -934,7 +934,8 @@ template <int FM>
 struct WideScales {
     float pa[FM], pb;        // cvt scale operands (exponent parts)
     float unit[FM];          // mantissa-part products: the accumulator unit
-    int zero[FM];            // 1 if the row's codes must read as +0 (its A scale or the B scale is 0)
+    bool zero[FM];           // the row's codes must read as +0 (its A scale or the B scale is 0); a
+                             // lane mask, so it takes scalar registers, not vector ones
     // 1x128 B (one scale per column): the exponent part and zero flag of the
     // column each B fragment of the lane holds (n-tile g: column 32 g + r of
     // the wave's); `unit` is then the A part alone
@@ -1448,6 +1449,17 @@ constexpr int il_first_k2_cvt(const IlPlan<FM, FN>& p) {
     return first;
 }
 
+// the last slot of any rescale multiply (the plan's; -1 if none)
+template <int FM, int FN>
+constexpr int il_last_mul(const IlPlan<FM, FN>& p) {
+    int last = -1;
+    for (int mi = 0; mi < FM; ++mi)
+        for (int g = 0; g < FN; ++g)
+            for (int i = 0; i < 16; ++i)
+                if (p.m[mi][g][i] > last) last = p.m[mi][g][i];
+    return last;
+}
+
 // the first slot of any B cvt of n-tiles g0 and later (the plan's)
 template <int FM, int FN>
 constexpr int il_first_b_cvt(const IlPlan<FM, FN>& p, int g0) {
@@ -1490,7 +1502,7 @@ __device__ __forceinline__ u32x4 il_frag(const uint8_t* lds, uint32_t sl, uint32
 // fragments are read ahead for the odd half-block (no registers for them).
 template <class W, int ODD, bool COPIER, bool BS1, class Sync>
 __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int wn, int r, int h,
-                                             const WideScales<W::FM>& w, const float (&ratio)[W::FM],
+                                             const WideScales<W::FM>& w, float (&ratio)[W::FM],
                                              uint32_t zero_line, v16f (&acc)[W::FM][W::FN],
                                              WideScales<W::FM>& next, const IlCopier<W, IL_COPY_WAVES>& cp,
                                              int fill_slot, int fill_h, int fill2_slot, int fill2_h, int pf_slot,
@@ -1504,6 +1516,9 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
     constexpr IlPlan<FM, FN> P = make_il_plan<FM, FN>(ODD != 0, SS, ODD ? 0 : IL_SCALE_OPS, BS1 ? 2 : 1,
                                                       BS1 ? 9 : IL_CAP);
     constexpr bool PREFETCH = !BS1;   // odd half-blocks' first fragments read during the even one
+    // the even half-block turns `ratio` into the next transition's at slot
+    // SS + 3, after its own multiplies (by the current one) are all done
+    static_assert(ODD || il_last_mul(P) <= SS + 3, "ratio replaced before the even half-block's last multiply");
     // Without 1x128 B the K-block's barrier sits in the odd half-block before
     // it, after MFMA SYNC_AT: there each wave waits for its copies of the next
     // K-block, meets the others, and reads that K-block's first fragments
@@ -1644,7 +1659,7 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
 #pragma clang loop unroll(full)
             for (int g = 0; g < IL_GW; ++g)
                 eb[g] = il_frag<W>(lds, nsl, uint32_t(offsetof(WStage<W>, b)), wn * FN * 32 + g * 32 + r, r, h, 0,
-                                   false, zero_line);
+                                   BS1 && ((next.zbm >> g) & 1), zero_line);
         }
         if (READ_HERE && n == 0) {
 #pragma clang loop unroll(full)
@@ -1687,6 +1702,7 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
                     next.pa[q] = na[q].pow2;
                     next.unit[q] = clamp_unit(na[q].mant * nb.mant);
                     next.zero[q] = (nsa[q] == 0.0f || nsb == 0.0f) ? 1 : 0;
+                    ratio[q] = more ? clamp_unit(w.unit[q] * __builtin_amdgcn_rcpf(next.unit[q])) : 1.0f;
                 }
             }
         }
@@ -1701,6 +1717,7 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
                     next.pa[q] = na[q].pow2;
                     next.unit[q] = clamp_unit(na[q].mant);
                     next.zero[q] = nsa[q] == 0.0f ? 1 : 0;
+                    ratio[q] = more ? clamp_unit(w.unit[q] * __builtin_amdgcn_rcpf(next.unit[q])) : 1.0f;
                 }
             }
         }
@@ -1792,7 +1809,7 @@ __device__ __forceinline__ void il_kloop(uint8_t* lds_raw, WStage<W>* ring, cons
 #pragma unroll
         for (int g = 0; g < IL_GW; ++g)
             eb[g] = il_frag<W>(lds_raw, 0u, uint32_t(offsetof(WStage<W>, b)), wn * W::FN * 32 + g * 32 + r, r, h, 0,
-                               false, kZeroLine);
+                               BS1 && ((nw.zbm >> g) & 1), kZeroLine);
     }
     for (int hb = 0; hb < halves; hb += 2) {
         if (BS1) kblock_sync(hb);
@@ -1808,9 +1825,6 @@ __device__ __forceinline__ void il_kloop(uint8_t* lds_raw, WStage<W>* ring, cons
         wide_il_half<W, 0, COPIER, BS1>(lds_raw, hb & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp, (hb + 2) & 3,
                                         f0, (hb + 3) & 3, f1, (hb + 1) & 3, pfa, pfb, cl, par, par ^ 1, more, lane,
                                         ea, eb, no_sync);
-#pragma unroll
-        for (int mi = 0; mi < FM; ++mi)
-            ratio[mi] = more ? clamp_unit(w.unit[mi] * __builtin_amdgcn_rcpf(nw.unit[mi])) : 1.0f;
         if (BS1) il_columns<W>(lds_raw, ring[hb & 3], cl, par ^ 1, more, wn, r, lane, nw);
         wide_il_half<W, 1, COPIER, BS1>(lds_raw, (hb + 1) & 3, wm, wn, r, h, w, ratio, kZeroLine, acc, nw, cp,
                                         0, 0, 0, 0, 0, pfa, pfb, cl, par ^ 1, par ^ 1, more, lane, ea, eb, next_sync);
