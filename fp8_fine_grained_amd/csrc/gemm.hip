@@ -1339,8 +1339,8 @@ constexpr int IL_COPY_WAVES = 4;
 //   - the K-block's barrier itself sits in the odd half-block before it, 14
 //     MFMAs before its end, and each wave reads the new K-block's first
 //     fragments right after it: the even half-block starts without an LDS
-//     burst too (1x128 B keeps the barrier at the K-block's start: its loop
-//     has no registers for the fragments read ahead);
+//     burst too (with 1x128 B only A's are read there: its loop has no
+//     registers for B's);
 //   - a compile-time plan (make_il_plan) gives every cvt and multiply a slot,
 //     the gap after one MFMA: at most IL_CAP VALU instructions per slot, cvts
 //     one MFMA before their first use, a tile's multiplies two MFMAs after its
@@ -1519,15 +1519,16 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
     // the even half-block turns `ratio` into the next transition's at slot
     // SS + 3, after its own multiplies (by the current one) are all done
     static_assert(ODD || il_last_mul(P) <= SS + 3, "ratio replaced before the even half-block's last multiply");
-    // Without 1x128 B the K-block's barrier sits in the odd half-block before
-    // it, after MFMA SYNC_AT: there each wave waits for its copies of the next
-    // K-block, meets the others, and reads that K-block's first fragments
-    // (chunk column 0 of A and of the first group's B, into ea / eb) while the
-    // last MFMAs of this one run on registers.  So no wave starts a K-block
-    // waiting on LDS.  Every read of this K-block's slots comes before
-    // SYNC_AT (the odd half-block's own reads at RB_AT, the rest during the
+    // The K-block's barrier sits in the odd half-block before it, after MFMA
+    // SYNC_AT: there each wave waits for its copies of the next K-block,
+    // meets the others, and reads that K-block's first fragments (chunk
+    // column 0 of A, into ea, and without 1x128 B of the first group's B, into
+    // eb; the 1x128-B loop has no registers for eb) while the last MFMAs of
+    // this one run on registers.  So no wave starts a K-block waiting on all
+    // of its first reads.  Every read of this K-block's slots comes before
+    // SYNC_AT (the odd half-block's own reads by RB_AT, the rest during the
     // even one), so the copies that follow the barrier may overwrite them.
-    constexpr bool LOB = !BS1;
+    constexpr bool LOB_B = !BS1;
     constexpr int SYNC_AT = 4 * FM * FN - 14;
     const WStage<W>& sg = *reinterpret_cast<const WStage<W>*>(lds + uint32_t(slot) * uint32_t(sizeof(WStage<W>)));
     float nsa[FM], nsb = 0.0f;
@@ -1572,12 +1573,12 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
     u32x4 ra[FM][2], rb[FN][2];
 #pragma clang loop unroll(full)
     for (int mi = 0; mi < FM; ++mi) {
-        ra[mi][0] = READ_HERE ? (LOB ? ea[mi] : read_a(uint32_t(slot), mi, 0)) : pfa[mi][0];
+        ra[mi][0] = READ_HERE ? (!ODD ? ea[mi] : read_a(uint32_t(slot), mi, 0)) : pfa[mi][0];
         if (!READ_HERE) ra[mi][1] = pfa[mi][1];
     }
 #pragma clang loop unroll(full)
     for (int g = 0; g < IL_GW; ++g) {
-        rb[g][0] = READ_HERE ? (LOB ? eb[g] : read_b(uint32_t(slot), g, 0)) : pfb[g][0];
+        rb[g][0] = READ_HERE ? (LOB_B && !ODD ? eb[g] : read_b(uint32_t(slot), g, 0)) : pfb[g][0];
         if (!READ_HERE) rb[g][1] = pfb[g][1];
     }
     u32x4 ca[FM][4], cb[FN][4];
@@ -1645,8 +1646,8 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
         // Wgrad and costs the dense GEMM 1%, in the odd one only 3%).
         if (!COPIER && !ODD && n == 0) __builtin_amdgcn_s_setprio(1);
         if (!COPIER && !ODD && n == NS - 1) __builtin_amdgcn_s_setprio(0);
-        if (LOB && ODD && n == SYNC_AT) {
-            static_assert(!LOB || SYNC_AT > RB_AT, "this K-block's slots read after the barrier");
+        if (ODD && n == SYNC_AT) {
+            static_assert(SYNC_AT > RB_AT, "this K-block's slots read after the barrier");
             // (after the last K-block the reads still go out, of a slot no
             // one uses again: ea / eb are then dead once the even half-block
             // has taken them, not held through it)
@@ -1657,9 +1658,9 @@ __device__ __forceinline__ void wide_il_half(uint8_t* lds, int slot, int wm, int
                 ea[mi] = il_frag<W>(lds, nsl, uint32_t(offsetof(WStage<W>, a)), wm * FM * 32 + mi * 32 + r, r, h,
                                     0, next.zero[mi] != 0, zero_line);
 #pragma clang loop unroll(full)
-            for (int g = 0; g < IL_GW; ++g)
+            for (int g = 0; g < (LOB_B ? IL_GW : 0); ++g)
                 eb[g] = il_frag<W>(lds, nsl, uint32_t(offsetof(WStage<W>, b)), wn * FN * 32 + g * 32 + r, r, h, 0,
-                                   BS1 && ((next.zbm >> g) & 1), zero_line);
+                                   false, zero_line);
         }
         if (READ_HERE && n == 0) {
 #pragma clang loop unroll(full)
@@ -1785,8 +1786,8 @@ __device__ __forceinline__ void il_kloop(uint8_t* lds_raw, WStage<W>* ring, cons
     }
     // Both halves of K-block kb have landed (this wave's copies: the only
     // loads in flight), then every wave's; a partial last K-block's slots
-    // are zeroed past K first.  Without 1x128 B this runs in the odd
-    // half-block of kb - 1 (wide_il_half), and before the loop for kb = 0.
+    // are zeroed past K first.  This runs in the odd half-block of kb - 1
+    // (wide_il_half), and before the loop for kb = 0.
     auto kblock_sync = [&](int hbk) {
         wait_vmcnt<0>();
         const bool partial = (hbk + 2) * W::KS > K;   // partial last K-block (uniform)
@@ -1796,23 +1797,22 @@ __device__ __forceinline__ void il_kloop(uint8_t* lds_raw, WStage<W>* ring, cons
         }
         // (mid-K-block, this wave's reads of the slots the copies after the
         // barrier refill are all done as well)
-        if (!BS1 || partial) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
     };
     u32x4 ea[FM], eb[IL_GW];   // the next K-block's first fragments, read at its barrier
-    if (!BS1) {
+    {
         kblock_sync(0);
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi)
             ea[mi] = il_frag<W>(lds_raw, 0u, uint32_t(offsetof(WStage<W>, a)), wm * FM * 32 + mi * 32 + r, r, h, 0,
                                 nw.zero[mi] != 0, kZeroLine);
 #pragma unroll
-        for (int g = 0; g < IL_GW; ++g)
+        for (int g = 0; g < (BS1 ? 0 : IL_GW); ++g)
             eb[g] = il_frag<W>(lds_raw, 0u, uint32_t(offsetof(WStage<W>, b)), wn * W::FN * 32 + g * 32 + r, r, h, 0,
-                               BS1 && ((nw.zbm >> g) & 1), kZeroLine);
+                               false, kZeroLine);
     }
     for (int hb = 0; hb < halves; hb += 2) {
-        if (BS1) kblock_sync(hb);
         // the next K-block's halves (past the end: the last half again, into
         // slots never read again)
         const int f0 = hb + 2 < halves ? hb + 2 : halves - 1, f1 = hb + 3 < halves ? hb + 3 : halves - 1;
