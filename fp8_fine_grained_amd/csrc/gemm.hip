@@ -556,6 +556,30 @@ __device__ __forceinline__ void store_bf16_rows64(uint16_t* p, int64_t ldc, int 
     if (i + 16 < rows) st<u32x4>(p + (i + 16) * ldc + col, u32x4{c1[0], c1[1], c1[2], c1[3]});
 }
 
+// FP32 C of one 32x32 MFMA tile written as 64-byte row segments.  Lane l
+// holds, of tile row l % 32, the four runs j of four columns 8 j + 4 (l / 32)
+// .. + 3 (v[j]).  A swap of 16-lane rows between runs 2 p and 2 p + 1 gives
+// the lanes with l % 16 = i columns 16 p .. 16 p + 15 of tile row i in one
+// chunk and of row i + 16 in the other: each store writes 64 contiguous bytes
+// of 16 rows, not 32 bytes of 32.  p points at the tile's row 0, column 0;
+// `rows` of its rows exist.  Every lane of the wave must take part.
+__device__ __forceinline__ void store_f32_rows64(float* p, int64_t ldc, int lane, int64_t rows, v4f (&v)[4]) {
+    const int i = lane & 15, col = 4 * (lane >> 5) + 8 * ((lane >> 4) & 1);
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+        const u32x4 a = __builtin_bit_cast(u32x4, v[2 * pr]), b = __builtin_bit_cast(u32x4, v[2 * pr + 1]);
+        uint32_t x[4], y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(a[q], b[q], false, false);
+            x[q] = sw[0];
+            y[q] = sw[1];
+        }
+        if (i < rows) st<u32x4>(p + i * ldc + 16 * pr + col, u32x4{x[0], x[1], x[2], x[3]});
+        if (i + 16 < rows) st<u32x4>(p + (i + 16) * ldc + 16 * pr + col, u32x4{y[0], y[1], y[2], y[3]});
+    }
+}
+
 // BF16 bits of four accumulator values, two to a word
 __device__ __forceinline__ void bf16_words(v4f v, uint32_t (&w)[2]) {
     w[0] = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
@@ -1930,7 +1954,6 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
         il_kloop<W, false, BS1>(lds_raw, ring, cp, halves, K, wm, wn, r, h, lane, live, w, nw, ratio, acc, cl);
     wait_vmcnt<0>();
 
-    const int n_lane = wn * FN * 32 + 4 * h;
     if constexpr (OUT == 2) {
         static_assert(FN * 32 == 128, "one 128-column group per wave");
 #pragma unroll
@@ -1980,22 +2003,24 @@ __device__ __forceinline__ void gemm_wide_il_body(const GemmArgs& args, uint8_t*
                                   lane, t.rows_valid - m0, d);
             }
         }
-    } else {
+    } else {   // FP32, in 64-byte row segments
 #pragma unroll
-        for (int mi = 0; mi < FM; ++mi) {   // FP32
-            const int64_t m = wrow0 + mi * 32 + r;
-            if (m >= t.rows_valid) continue;
+        for (int mi = 0; mi < FM; ++mi) {
+            const int64_t m0 = wrow0 + mi * 32;
+            if (m0 >= t.rows_valid) continue;   // uniform
 #pragma unroll
-            for (int ni = 0; ni < FN; ++ni)
+            for (int ni = 0; ni < FN; ++ni) {
+                v4f v[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
-                    v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
-                                acc[mi][ni][4 * j + 3]} * w.unit[mi];
+                    v[j] = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
+                               acc[mi][ni][4 * j + 3]} * w.unit[mi];
                     if (BS1)   // the columns' last mantissa parts
-                        v = v * ld<v4f>(lds_raw + cl + 1024u + uint32_t((ni * 32 + 8 * j + 4 * h) * 4));
-                    st<v4f>(static_cast<float*>(args.c) + idx, v);
+                        v[j] = v[j] * ld<v4f>(lds_raw + cl + 1024u + uint32_t((ni * 32 + 8 * j + 4 * h) * 4));
                 }
+                store_f32_rows64(static_cast<float*>(args.c) + t.c_base + m0 * N + n0 + wn * FN * 32 + ni * 32, N, lane,
+                                 t.rows_valid - m0, v);
+            }
         }
     }
 }
