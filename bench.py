@@ -290,6 +290,19 @@ def contig_inputs(gen):
     return a, qa, sa, qb, sb, offs, counts, mt
 
 
+def mx_experts(gen, G, N, K):
+    """G experts' fresh N(0, 0.02) weights [N][K], MX-quantized one by one on
+    the GPU: codes [G][N][K] and E8M0 bytes [G][K/32][N]."""
+    import torch
+    import fp8_fine_grained_amd as fp8
+    qb = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    eb = torch.empty((G, K // 32, N), dtype=torch.uint8, device="cuda")
+    for g in range(G):
+        wg = torch.randn((N, K), generator=gen, device="cuda") * 0.02
+        fp8.fp8_quant_mx_1x32(wg, q=qb[g], e=eb[g])
+    return qb, eb
+
+
 def profile_other(args):
     """Counter-collection driver for the masked decode GEMMs (both shapes),
     the linear_trio GEMMs and the contiguous grouped GEMM: build that
@@ -550,6 +563,15 @@ def run_extra(args):
                                                               q=s["qy"], s=s["sy"]),
              sets, dict(cfg, flops_counted="valid rows only",
                         output="FP8 codes + 1x128 scales along N: the down projection's A operand"), flops=fl)
+        # the MX variant on the same rows (1x32 blocks, E8M0 scales applied in the FP8 MFMA)
+        for s in sets:
+            s["qam"], s["eam"] = fp8.fp8_quant_mx_1x32(s["a"])
+            s["qbm"], s["ebm"] = mx_experts(gen, G, N, K)
+        line("moe_contig", "grouped_gemm_contiguous_mx gate+up (MX operands)",
+             lambda s: fp8.fp8_grouped_gemm_contiguous_mx(s["qam"], s["eam"], s["qbm"], s["ebm"], s["offs"],
+                                                          out=s["c"]),
+             sets, dict(cfg, flops_counted="valid rows only", scales="E8M0 per 1x32 block"), flops=fl,
+             peak="FP8 (scaled MFMA)")
     elif args.workload == "moe_masked":
         G, MMAX = 32, 128
         for (N, K) in ((4096, 7168), (7168, 2048)):
@@ -567,6 +589,21 @@ def run_extra(args):
                  lambda s: fp8.fp8_grouped_gemm_masked_tiled(s["qa"], s["sa"], s["qt"], s["sb"], s["mmt"],
                                                              out=s["c"]),
                  sets, dict(cfg, weights="decode-tiled layout (fp8_tile_weights_decode)"), nbytes=nbytes)
+            # the MX variant: the same valid-row counts, fresh MX operands
+            for s in sets:
+                a = gpu_acts(gen, G * MMAX, K, 0.001, 100.0).reshape(G, MMAX, K)
+                s["qam"] = torch.empty((G, MMAX, K), dtype=torch.uint8, device="cuda")
+                s["eam"] = torch.empty((G, K // 32, MMAX), dtype=torch.uint8, device="cuda")
+                for g in range(G):
+                    fp8.fp8_quant_mx_1x32(a[g], q=s["qam"][g], e=s["eam"][g])
+                del a
+                s["qbm"], s["ebm"] = mx_experts(gen, G, N, K)
+            nbytes_mx = G * N * K + G * (K // 32) * N + valid * K + valid * (K // 32) + valid * N * 2
+            line("moe_masked", f"grouped_gemm_masked_mx N={N} K={K} (MX operands)",
+                 lambda s: fp8.fp8_grouped_gemm_masked_mx(s["qam"], s["eam"], s["qbm"], s["ebm"], s["mmt"],
+                                                          out=s["c"]),
+                 sets, dict(cfg, scales="E8M0 per 1x32 block", bytes="all expert weights + E8M0 scales + valid A "
+                            "rows + scales + valid C rows"), nbytes=nbytes_mx)
             del sets
 
 

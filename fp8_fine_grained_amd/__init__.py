@@ -22,14 +22,15 @@ BSCALE_1x128 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
 
-ABI_VERSION = 10
+ABI_VERSION = 11
 EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
            "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
            "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16", "fp8_requant_act_tokenwise",
            "fp8_quant_mx_1x32", "fp8_gemm_mx", "fp8_gemm_blockscaled_fp8out", "fp8_quant_fprop_operands",
            "fp8_tile_weights_decode", "fp8_grouped_gemm_masked_tiled", "fp8_gemm_blockscaled_fp8mfma",
-           "fp8_grouped_gemm_contiguous_fp8out", "fp8fg_status_string", "fp8fg_abi_version")
-_COMPUTE = EXPORTS[:16]
+           "fp8_grouped_gemm_contiguous_fp8out", "fp8_grouped_gemm_contiguous_mx", "fp8_grouped_gemm_masked_mx",
+           "fp8fg_status_string", "fp8fg_abi_version")
+_COMPUTE = EXPORTS[:18]
 
 
 class Fp8fgError(RuntimeError):
@@ -67,6 +68,8 @@ def load_library(path=LIB_PATH):
     lib.fp8_tile_weights_decode.argtypes = [vp, i64, i64, i64, vp, vp]
     lib.fp8_grouped_gemm_masked_tiled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     lib.fp8_grouped_gemm_contiguous_fp8out.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp]
+    lib.fp8_grouped_gemm_contiguous_mx.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
+    lib.fp8_grouped_gemm_masked_mx.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     for name in _COMPUTE:
         getattr(lib, name).restype = ctypes.c_int
     lib.fp8fg_status_string.argtypes = [ctypes.c_int]
@@ -231,6 +234,43 @@ def fp8_gemm_mx(a, ea, b, eb, out_dtype=torch.bfloat16, out=None):
     _need(out, out_dtype, (M, N), "out")
     _check("fp8_gemm_mx", load_library().fp8_gemm_mx(_ptr(a), _ptr(ea), _ptr(b), _ptr(eb), _ptr(out),
                                                       _out_dtype(out_dtype), M, N, K, _stream(a)))
+    return out
+
+
+def fp8_grouped_gemm_contiguous_mx(a, ea, b, eb, group_offsets, out_dtype=torch.bfloat16, out=None):
+    """fp8_grouped_gemm_contiguous on MX operands: a u8 [M_total][K] / ea u8
+    [K/32][M_total], b u8 [G][N][K] / eb u8 [G][K/32][N]; off device int32 [G+1]."""
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    _need(a, torch.uint8, (M_total, K), "a")
+    _need(ea, torch.uint8, (K // 32, M_total), "ea")
+    _need(b, torch.uint8, (G, N, K), "b")
+    _need(eb, torch.uint8, (G, K // 32, N), "eb")
+    _need(group_offsets, torch.int32, (G + 1,), "group_offsets")
+    out = _empty((M_total, N), out_dtype, a) if out is None else out
+    _need(out, out_dtype, (M_total, N), "out")
+    _check("fp8_grouped_gemm_contiguous_mx", load_library().fp8_grouped_gemm_contiguous_mx(
+        _ptr(a), _ptr(ea), _ptr(b), _ptr(eb), _ptr(group_offsets), G, M_total, N, K, _ptr(out),
+        _out_dtype(out_dtype), _stream(a)))
+    return out
+
+
+def fp8_grouped_gemm_masked_mx(a, ea, b, eb, masked_m, out_dtype=torch.bfloat16, out=None):
+    """fp8_grouped_gemm_masked on MX operands: a u8 [G][M_max][K] / ea u8
+    [G][K/32][M_max], b u8 [G][N][K] / eb u8 [G][K/32][N]; rows >= masked_m[g]
+    of out are not written."""
+    G, M_max, K = a.shape
+    N = b.shape[1]
+    _need(a, torch.uint8, (G, M_max, K), "a")
+    _need(ea, torch.uint8, (G, K // 32, M_max), "ea")
+    _need(b, torch.uint8, (G, N, K), "b")
+    _need(eb, torch.uint8, (G, K // 32, N), "eb")
+    _need(masked_m, torch.int32, (G,), "masked_m")
+    out = _empty((G, M_max, N), out_dtype, a) if out is None else out
+    _need(out, out_dtype, (G, M_max, N), "out")
+    _check("fp8_grouped_gemm_masked_mx", load_library().fp8_grouped_gemm_masked_mx(
+        _ptr(a), _ptr(ea), _ptr(b), _ptr(eb), _ptr(masked_m), G, M_max, N, K, _ptr(out),
+        _out_dtype(out_dtype), _stream(a)))
     return out
 
 

@@ -142,7 +142,50 @@ int fp8_gemm_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uin
     if (M == 0 || N == 0) return FP8FG_OK;
     fp8fg::GemmArgs args{a, reinterpret_cast<const float*>(ea), b, reinterpret_cast<const float*>(eb), c,
                          nullptr, M, N, K, 1};
-    return hip_status(fp8fg::launch_gemm_mx(out_dtype == FP8FG_OUT_FP32, args, static_cast<hipStream_t>(stream)));
+    return hip_status(fp8fg::launch_gemm_mx(out_dtype == FP8FG_OUT_FP32, fp8fg::GemmMode::Dense, args,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int fp8_grouped_gemm_contiguous_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb,
+                                   const int32_t* group_offsets, int64_t G, int64_t M_total, int64_t N, int64_t K,
+                                   void* c, int out_dtype, void* stream) {
+    if (!a || !ea || !b || !eb || !group_offsets || !c) return FP8FG_ERR_NULL;
+    if (G < 0 || M_total < 0 || N < 0 || K < 0 || M_total % 128 != 0 || N % 256 != 0 || K % 64 != 0)
+        return FP8FG_ERR_SHAPE;
+    if (K == 0 && M_total > 0 && N > 0 && G > 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(ea) || !aligned16(b) || !aligned16(eb) || !aligned16(c) ||
+        !aligned16(group_offsets))
+        return FP8FG_ERR_ALIGN;
+    if (!valid_out(out_dtype)) return FP8FG_ERR_UNSUPPORTED;
+    if (M_total > kMaxDim || N > kMaxDim || K >= (int64_t(1) << 24) || G > kMaxDim - 1) return FP8FG_ERR_UNSUPPORTED;
+    if ((K / 32) * M_total > int64_t(0xFFFFFF00) || (K / 32) * N > int64_t(0xFFFFFF00)) return FP8FG_ERR_UNSUPPORTED;
+    if ((M_total / 256 + G) * (N / 256) > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if (G == 0 || M_total == 0 || N == 0) return FP8FG_OK;
+    fp8fg::GemmArgs args{a, reinterpret_cast<const float*>(ea), b, reinterpret_cast<const float*>(eb), c,
+                         group_offsets, M_total, N, K, G};
+    return hip_status(fp8fg::launch_gemm_mx(out_dtype == FP8FG_OUT_FP32, fp8fg::GemmMode::Contig, args,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int fp8_grouped_gemm_masked_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb,
+                               const int32_t* masked_m, int64_t G, int64_t M_max, int64_t N, int64_t K, void* c,
+                               int out_dtype, void* stream) {
+    if (!a || !ea || !b || !eb || !masked_m || !c) return FP8FG_ERR_NULL;
+    if (G < 0 || M_max < 0 || N < 0 || K < 0 || M_max % 4 != 0 || N % 256 != 0 || K % 64 != 0)
+        return FP8FG_ERR_SHAPE;
+    if (K == 0 && M_max > 0 && N > 0 && G > 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(ea) || !aligned16(b) || !aligned16(eb) || !aligned16(c) || !aligned16(masked_m))
+        return FP8FG_ERR_ALIGN;
+    if (!valid_out(out_dtype)) return FP8FG_ERR_UNSUPPORTED;
+    if (M_max > kMaxDim || N > kMaxDim || K >= (int64_t(1) << 24) || G > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if ((K / 32) * M_max > int64_t(0xFFFFFF00) || (K / 32) * N > int64_t(0xFFFFFF00)) return FP8FG_ERR_UNSUPPORTED;
+    const int64_t tiles_per_group = ((M_max + 255) / 256) * (N / 256);
+    if (tiles_per_group > 0 && G > kMaxDim / tiles_per_group) return FP8FG_ERR_UNSUPPORTED;
+    if (G == 0 || M_max == 0 || N == 0) return FP8FG_OK;
+    fp8fg::GemmArgs args{a, reinterpret_cast<const float*>(ea), b, reinterpret_cast<const float*>(eb), c, masked_m,
+                         M_max, N, K, G};
+    return hip_status(fp8fg::launch_gemm_mx(out_dtype == FP8FG_OUT_FP32, fp8fg::GemmMode::Masked, args,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 // the dense call's checks; engine 0 = exact, 1 = FP8 MFMA

@@ -122,6 +122,7 @@ struct Tile {
     const float* SA;
     const uint8_t* B;
     const float* SB;
+    int64_t g;            // the tile's expert (0 in the dense layout)
     int bn;
     bool live;
 };
@@ -264,6 +265,7 @@ __device__ __forceinline__ Tile map_tile(const GemmArgs& args, int64_t tile, int
         t.SA += g * kbs * args.M;
         t.c_base = g * args.M * args.N;
     }
+    t.g = g;
     if (t.m0 >= t.rows_valid) t.live = false;
     if (MODE != int(GemmMode::Dense)) {
         t.B += g * args.N * args.K;
@@ -2089,6 +2091,10 @@ struct MxCopier {
 
 // Waves 0-1 copy the A scale runs of blocks 2 st + w, waves 2-3 those of B,
 // waves 4-7 repeat wave 0's run into the dummy line (equal load counts).
+// Grouped layouts: expert g's B codes (t.B) and scale bytes [K/32][N] follow
+// one another; in the masked layout so do its A rows (t.A) and A scale bytes
+// [K/32][M_max], while the contiguous layout's A rows and scales are shared.
+template <int MODE>
 __device__ __forceinline__ MxCopier make_mx_copier(const GemmArgs& args, const Tile& t, int wave, int lane,
                                                    int64_t n0) {
     typedef MxTile W;
@@ -2109,8 +2115,8 @@ __device__ __forceinline__ MxCopier make_mx_copier(const GemmArgs& args, const T
         c.b_lds[i] = int(offsetof(MxStage, b)) + r0 * W::KS;
     }
     const int64_t kblocks = K / 32;
-    const uint8_t* ea = reinterpret_cast<const uint8_t*>(args.sa);
-    const uint8_t* eb = reinterpret_cast<const uint8_t*>(args.sb);
+    const uint8_t* ea = reinterpret_cast<const uint8_t*>(args.sa) + (MODE == int(GemmMode::Masked) ? t.g * kblocks * M : 0);
+    const uint8_t* eb = reinterpret_cast<const uint8_t*>(args.sb) + t.g * kblocks * N;
     if (wave < 2) {           // A: bytes of rows m0 + 4 lane .. +3 in block 2 st + wave
         c.rs = make_rsrc(ea, uint32_t(kblocks * M));
         c.vs = uint32_t(t.m0 + 4 * lane);
@@ -2133,7 +2139,7 @@ __device__ __forceinline__ MxCopier make_mx_copier(const GemmArgs& args, const T
     return c;
 }
 
-template <int OUT_FP32>
+template <int OUT_FP32, int MODE>
 __device__ __forceinline__ void gemm_mx_body(const GemmArgs& args) {
     typedef MxTile W;
     constexpr int FM = W::FM, FN = W::FN, STAGES = W::STAGES, L = W::LOADS_PER_WAVE;
@@ -2145,10 +2151,10 @@ __device__ __forceinline__ void gemm_mx_body(const GemmArgs& args) {
     const int wm = wave / W::WAVES_N, wn = wave % W::WAVES_N;
     const int64_t N = args.N, K = args.K;
     const int stages = int(K / W::KS);
-    const Tile t = map_tile<W, int(GemmMode::Dense)>(args, blockIdx.x);
+    const Tile t = map_tile<W, MODE>(args, blockIdx.x);
     if (!t.live) return;
     const int64_t n0 = int64_t(t.bn) * W::BN;
-    const MxCopier cp = make_mx_copier(args, t, wave, lane, n0);
+    const MxCopier cp = make_mx_copier<MODE>(args, t, wave, lane, n0);
     const int64_t wrow0 = t.m0 + wm * FM * 32;
     const bool live = wrow0 < t.rows_valid;
     const int r = lane & 31, h = lane >> 5;
@@ -2228,7 +2234,7 @@ __device__ __forceinline__ void gemm_mx_body(const GemmArgs& args) {
             uint32_t d[4][2];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int64_t idx = m * N + n0 + n_lane + ni * 32 + 8 * j;
+                const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
                 const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
                                   acc[mi][ni][4 * j + 3]};
                 if (OUT_FP32) {
@@ -2238,14 +2244,23 @@ __device__ __forceinline__ void gemm_mx_body(const GemmArgs& args) {
                 }
             }
             if (!OUT_FP32)
-                store_bf16_rows64(static_cast<uint16_t*>(args.c) + m0 * N + n0 + wn * FN * 32 + ni * 32, N, lane,
-                                  t.rows_valid - m0, d);
+                store_bf16_rows64(static_cast<uint16_t*>(args.c) + t.c_base + m0 * N + n0 + wn * FN * 32 + ni * 32, N,
+                                  lane, t.rows_valid - m0, d);
         }
     }
 }
 
-__global__ __launch_bounds__(MxTile::THREADS) void gemm_mx_o0_dense(GemmArgs args) { gemm_mx_body<0>(args); }
-__global__ __launch_bounds__(MxTile::THREADS) void gemm_mx_o1_dense(GemmArgs args) { gemm_mx_body<1>(args); }
+#define FP8FG_MX_KERNEL(OUT, NAME, MODE)                                                                  \
+    __global__ __launch_bounds__(MxTile::THREADS) void gemm_mx_o##OUT##_##NAME(GemmArgs args) {          \
+        gemm_mx_body<OUT, int(GemmMode::MODE)>(args);                                                    \
+    }
+FP8FG_MX_KERNEL(0, dense, Dense)
+FP8FG_MX_KERNEL(1, dense, Dense)
+FP8FG_MX_KERNEL(0, contig, Contig)
+FP8FG_MX_KERNEL(1, contig, Contig)
+FP8FG_MX_KERNEL(0, masked, Masked)
+FP8FG_MX_KERNEL(1, masked, Masked)
+#undef FP8FG_MX_KERNEL
 
 // One plain __global__ function per instantiation (kernel templates whose
 // instantiations differ only in the tile shape lost their host stubs).
@@ -2894,13 +2909,19 @@ hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, c
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_mx(int out_fp32, const GemmArgs& args, hipStream_t stream) {
-    const int64_t tiles = ((args.M + MxTile::BM - 1) / MxTile::BM) * (args.N / MxTile::BN);
+// The MX GEMM in any layout: 256 x 256 tiles; the dense layout in the
+// XCD-grouped order, the masked one ranked heaviest first (one XCD per
+// (expert, m-tile) pair when eight divides their count), the contiguous one
+// walking the group offsets over a grid that bounds its tile count.
+hipError_t launch_mx(int out_fp32, GemmMode mode, const GemmArgs& args, hipStream_t stream) {
+    const int64_t tiles = tile_count<MxTile>(mode, args);
     if (tiles == 0) return hipSuccess;
     GemmArgs a = args;
-    a.xcds = kXcds;
-    return launch_kernel(out_fp32 ? gemm_mx_o1_dense : gemm_mx_o0_dense, dim3(unsigned(tiles)),
-                         dim3(MxTile::THREADS), stream, a);
+    a.xcds = mode == GemmMode::Dense ? kXcds : mode == GemmMode::Masked ? masked_xcds(args, MxTile::BM) : 1;
+    void (*k)(GemmArgs) = mode == GemmMode::Dense    ? (out_fp32 ? gemm_mx_o1_dense : gemm_mx_o0_dense)
+                          : mode == GemmMode::Contig ? (out_fp32 ? gemm_mx_o1_contig : gemm_mx_o0_contig)
+                                                     : (out_fp32 ? gemm_mx_o1_masked : gemm_mx_o0_masked);
+    return launch_kernel(k, dim3(unsigned(tiles)), dim3(MxTile::THREADS), stream, a);
 }
 
 hipError_t launch_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream) {
@@ -2926,8 +2947,8 @@ hipError_t launch_tile_weights_decode(const uint8_t* q, int64_t G, int64_t N, in
     return gemm_detail::launch_tile_decode(q, G, N, K, out, stream);
 }
 
-hipError_t launch_gemm_mx(int out_fp32, const GemmArgs& args, hipStream_t stream) {
-    return gemm_detail::launch_mx(out_fp32, args, stream);
+hipError_t launch_gemm_mx(int out_fp32, GemmMode mode, const GemmArgs& args, hipStream_t stream) {
+    return gemm_detail::launch_mx(out_fp32, mode, args, stream);
 }
 
 hipError_t launch_gemm(int engine, GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,

@@ -48,8 +48,10 @@ struct GemmArgs {
     int xcds = 1;           // XCDs whose L2s the tile order groups tiles for (1: the plain order)
 };
 
-// MX GEMM: args.sa / args.sb carry the E8M0 scale bytes ([K/32][M], [K/32][N])
-hipError_t launch_gemm_mx(int out_fp32, const GemmArgs& args, hipStream_t stream);
+// MX GEMM: args.sa / args.sb carry the E8M0 scale bytes ([K/32][M], [K/32][N];
+// per expert in the grouped layouts: A's [G][K/32][M_max] when masked, B's
+// [G][K/32][N])
+hipError_t launch_gemm_mx(int out_fp32, GemmMode mode, const GemmArgs& args, hipStream_t stream);
 // engine 0: exact (FP8 codes widened to BF16, BF16 MFMA); 1: FP8 MFMA on the codes
 hipError_t launch_gemm(int engine, GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                        hipStream_t stream);

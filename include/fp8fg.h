@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 10
+#define FP8FG_ABI_VERSION 11
 
 enum fp8fg_status {
     FP8FG_OK = 0,
@@ -189,6 +189,34 @@ int fp8_requant_act_tokenwise(const uint8_t* q, const float* s, int64_t M, int64
 int fp8_quant_mx_1x32(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e, void* stream);
 int fp8_gemm_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb,
                 void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * The MX GEMM in the two MoE layouts ("Deepgemm lançado no dia 4 da semana de
+ * código aberto Deepseek", section "Principais características": dense plus a
+ * contiguous and a masked grouped layout), with fp8_gemm_mx's arithmetic and
+ * accuracy contract for each expert's rows:
+ *   b u8 [G][N][K] with eb u8 [G][K/32][N] (each expert's weight quantized by
+ *   fp8_quant_mx_1x32).
+ * fp8_grouped_gemm_contiguous_mx: a u8 [M_total][K] with ea u8 [K/32][M_total]
+ *   (all rows quantized together), group_offsets as for
+ *   fp8_grouped_gemm_contiguous (DEVICE int32 [G+1], non-decreasing, from 0 to
+ *   M_total, multiples of 128); c [M_total][N].  Rows in no expert's range are
+ *   not written.  Requires M_total % 128 == 0, N % 256 == 0, K % 64 == 0,
+ *   K > 0 when there is work, K < 2^24, (K / 32) * max(M_total, N) < 2^32.
+ * fp8_grouped_gemm_masked_mx: a u8 [G][M_max][K] with ea u8 [G][K/32][M_max],
+ *   masked_m as for fp8_grouped_gemm_masked (DEVICE int32 [G], clamped to
+ *   [0, M_max] on the device); c [G][M_max][N], rows at or beyond masked_m[g]
+ *   NOT written.  Requires M_max % 4 == 0, N % 256 == 0, K % 64 == 0, K > 0
+ *   when there is work, K < 2^24, (K / 32) * max(M_max, N) < 2^32.
+ * Each expert's rows come out bit for bit as fp8_gemm_mx gives them for that
+ * expert's operands.
+ */
+int fp8_grouped_gemm_contiguous_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb,
+                                   const int32_t* group_offsets, int64_t G, int64_t M_total,
+                                   int64_t N, int64_t K, void* c, int out_dtype, void* stream);
+int fp8_grouped_gemm_masked_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb,
+                               const int32_t* masked_m, int64_t G, int64_t M_max,
+                               int64_t N, int64_t K, void* c, int out_dtype, void* stream);
 
 /*
  * Dense block-scaled FP8 GEMM: C[M][N] = A[M][K] . B[N][K]^T.

@@ -124,6 +124,26 @@ def test_mx_argument_errors():
     assert g(P, MIS, P, P, P, 0, 4, 256, 64, NUL) == EALIGN
     assert g(P, P, P, P, P, 7, 4, 256, 64, NUL) == EUNSUP
     assert g(P, P, P, P, P, 0, 0, 256, 64, NUL) == OK
+    c = lib.fp8_grouped_gemm_contiguous_mx
+    #        a  ea  b  eb off  G  M_total N   K   c  out
+    assert c(P, P, P, P, NUL, 4, 512, 256, 64, P, 0, NUL) == ENULL
+    assert c(P, P, P, P, P, 4, 500, 256, 64, P, 0, NUL) == ESHAPE      # M_total % 128
+    assert c(P, P, P, P, P, 4, 512, 128, 64, P, 0, NUL) == ESHAPE      # N % 256
+    assert c(P, P, P, P, P, 4, 512, 256, 96, P, 0, NUL) == ESHAPE      # K % 64
+    assert c(P, P, P, P, P, 4, 512, 256, 0, P, 0, NUL) == ESHAPE       # K = 0 with work to do
+    assert c(P, P, P, P, MIS, 4, 512, 256, 64, P, 0, NUL) == EALIGN
+    assert c(P, P, P, P, P, 4, 512, 256, 64, P, 2, NUL) == EUNSUP      # output dtype
+    assert c(P, P, P, P, P, 4, 512, 256, 1 << 24, P, 0, NUL) == EUNSUP
+    assert c(P, P, P, P, P, 0, 512, 256, 64, P, 0, NUL) == OK          # G = 0
+    m = lib.fp8_grouped_gemm_masked_mx
+    assert m(P, P, P, NUL, P, 4, 128, 256, 64, P, 0, NUL) == ENULL
+    assert m(P, P, P, P, P, 4, 126, 256, 64, P, 0, NUL) == ESHAPE      # M_max % 4
+    assert m(P, P, P, P, P, 4, 128, 384, 64, P, 0, NUL) == ESHAPE      # N % 256
+    assert m(P, P, P, P, P, 4, 128, 256, 32, P, 0, NUL) == ESHAPE      # K % 64
+    assert m(P, P, P, P, P, -1, 128, 256, 64, P, 0, NUL) == ESHAPE
+    assert m(P, MIS, P, P, P, 4, 128, 256, 64, P, 0, NUL) == EALIGN
+    assert m(P, P, P, P, P, 4, 128, 256, 64, P, 5, NUL) == EUNSUP
+    assert m(P, P, P, P, P, 4, 0, 256, 64, P, 0, NUL) == OK            # M_max = 0
 
 
 @pytest.mark.parametrize("name", ["fp8_gemm_blockscaled", "fp8_gemm_blockscaled_fp8mfma"])
@@ -230,9 +250,12 @@ int main(void) {
     int e4 = fp8_grouped_gemm_contiguous_fp8out((const uint8_t*)16, (const float*)16, (const uint8_t*)16,
                                                 (const float*)16, (const int32_t*)16, 4, 512, 128, 128,
                                                 (uint8_t*)16, (float*)16, (void*)0);
-    printf("%d %d %d %d %d %s\n", v, e1, e2, e3, e4, fp8fg_status_string(e2));
+    int e5 = fp8_grouped_gemm_masked_mx((const uint8_t*)16, (const uint8_t*)16, (const uint8_t*)16,
+                                        (const uint8_t*)16, (const int32_t*)16, 4, 128, 256, 96, (void*)16,
+                                        FP8FG_OUT_BF16, (void*)0);
+    printf("%d %d %d %d %d %d %s\n", v, e1, e2, e3, e4, e5, fp8fg_status_string(e2));
     return v == FP8FG_ABI_VERSION && e1 == FP8FG_ERR_NULL && e2 == FP8FG_ERR_SHAPE && e3 == FP8FG_ERR_NULL &&
-           e4 == FP8FG_ERR_SHAPE ? 0 : 1;
+           e4 == FP8FG_ERR_SHAPE && e5 == FP8FG_ERR_SHAPE ? 0 : 1;
 }
 """)
     libdir = os.path.dirname(fp8.LIB_PATH)

@@ -100,3 +100,102 @@ def test_gemm_mx_full_size_dense_fprop():
     # the GPU quantizer gives the same operands
     gq, ge = fp8.fp8_quant_mx_1x32(dev(x))
     assert np.array_equal(host(gq), qa) and np.array_equal(host(ge), ea)
+
+
+# ---------------------------------------------------------------------------
+# The MX GEMM in the MoE layouts.  Each expert's rows must be exactly what the
+# dense MX call gives for that expert's operands (same arithmetic, same tile
+# origin), and within the MX bound of the oracle.
+
+def _mx_experts(rng, G, N, K):
+    qs, es = zip(*[mx.quant_mx_1x32(workloads.weights(rng, N, K)) for _ in range(G)])
+    return np.stack(qs), np.stack(es)
+
+
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_mx_contiguous_equals_dense_per_group(out):
+    """Groups of 256, 0, 128 and 384 rows (tiles of 256 rows straddle a group
+    end), N = 512, K = 320 (five 64-K stages)."""
+    rng = np.random.default_rng(91)
+    off = np.array([0, 256, 256, 384, 768], np.int32)
+    G, N, K = 4, 512, 320
+    qa, ea = mx.quant_mx_1x32(workloads.activations(rng, int(off[-1]), K, 0.01, 50.0))
+    qb, eb = _mx_experts(rng, G, N, K)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    c = fp8.fp8_grouped_gemm_contiguous_mx(dev(qa), dev(ea), dev(qb), dev(eb), dev(off), od)
+    ch = c.float().cpu().numpy().astype(np.float64)
+    for g in range(G):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi == lo:
+            continue
+        cd = fp8.fp8_gemm_mx(dev(qa[lo:hi]), dev(ea[:, lo:hi]), dev(qb[g]), dev(eb[g]), od)
+        torch.cuda.synchronize()
+        assert torch.equal(cd, c[lo:hi]), g
+        _check(ch[lo:hi], mx.dequant_mx(qa[lo:hi], ea[:, lo:hi]), mx.dequant_mx(qb[g], eb[g]), out,
+               f"mx contiguous g={g} {out}")
+
+
+def test_mx_contiguous_rows_outside_offsets_untouched():
+    rng = np.random.default_rng(92)
+    off = np.array([0, 128, 256], np.int32)          # M_total = 512: rows 256.. belong to no group
+    G, N, K = 2, 256, 128
+    qa, ea = mx.quant_mx_1x32(workloads.activations(rng, 512, K))
+    qb, eb = _mx_experts(rng, G, N, K)
+    c = torch.full((512, N), 7.0, dtype=torch.float32, device=DEV)
+    fp8.fp8_grouped_gemm_contiguous_mx(dev(qa), dev(ea), dev(qb), dev(eb), dev(off), torch.float32, out=c)
+    torch.cuda.synchronize()
+    assert torch.all(c[256:] == 7.0)
+    assert not torch.any(c[:256] == 7.0)
+
+
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_mx_masked_equals_dense_per_expert(out):
+    """Buffers of 320 rows (two 256-row m-tiles), valid counts 0, 1, 257, 320,
+    77 and two out-of-range values that the device clamps (-3 -> 0, 999 -> 320);
+    rows past the count keep their sentinel."""
+    rng = np.random.default_rng(93)
+    G, M_max, N, K = 7, 320, 512, 192
+    mm_dev = np.array([0, 1, 257, 320, 77, -3, 999], np.int32)
+    mm = np.clip(mm_dev, 0, M_max)
+    qa, ea = zip(*[mx.quant_mx_1x32(workloads.activations(rng, M_max, K, 0.01, 50.0)) for _ in range(G)])
+    qa, ea = np.stack(qa), np.stack(ea)
+    qb, eb = _mx_experts(rng, G, N, K)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    c = torch.full((G, M_max, N), 9.0, dtype=od, device=DEV)
+    fp8.fp8_grouped_gemm_masked_mx(dev(qa), dev(ea), dev(qb), dev(eb), dev(mm_dev), od, out=c)
+    torch.cuda.synchronize()
+    for g in range(G):
+        m = int(mm[g])
+        assert bool(torch.all(c[g, m:] == 9.0)), g
+        if m == 0:
+            continue
+        cd = fp8.fp8_gemm_mx(dev(qa[g]), dev(ea[g]), dev(qb[g]), dev(eb[g]), od)
+        torch.cuda.synchronize()
+        assert torch.equal(cd[:m], c[g, :m]), g
+        _check(c[g, :m].float().cpu().numpy().astype(np.float64), mx.dequant_mx(qa[g], ea[g])[:m],
+               mx.dequant_mx(qb[g], eb[g]), out, f"mx masked g={g} {out}")
+
+
+@pytest.mark.timeout(900)
+def test_mx_masked_decode_full_size():
+    """The masked decode workload's down projection (32 experts, 128-row
+    buffers, valid rows U{1..64}, K = 2048, N = 7168), MX-quantized by the
+    oracle: sampled valid rows of every expert within the MX bound, every row
+    past masked_m keeps its sentinel."""
+    G, M_max, N, K = 32, 128, 7168, 2048
+    mm, a = workloads.moe_masked_inputs(N, K, G, M_max)
+    qa, ea = zip(*[mx.quant_mx_1x32(a[g]) for g in range(G)])
+    qa, ea = np.stack(qa), np.stack(ea)
+    del a
+    qb, eb = zip(*[mx.quant_mx_1x32(workloads.expert_weight("moe_down", g, N, K)) for g in range(G)])
+    qb, eb = np.stack(qb), np.stack(eb)
+    c = torch.full((G, M_max, N), 5.0, dtype=torch.bfloat16, device=DEV)
+    fp8.fp8_grouped_gemm_masked_mx(dev(qa), dev(ea), dev(qb), dev(eb), dev(mm.astype(np.int32)), out=c)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(94)
+    for g in range(G):
+        m = int(mm[g])
+        assert bool(torch.all(c[g, m:] == 5.0)), g
+        rows = np.unique(np.concatenate([[0, m - 1], rng.integers(0, m, 3)]))
+        cg = c[g][torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
+        _check(cg, mx.dequant_mx(qa[g], ea[g])[rows], mx.dequant_mx(qb[g], eb[g]), "bf16", f"mx masked full g={g}")
