@@ -540,6 +540,29 @@ def run_extra(args):
         line("linear_trio", "gemm Wgrad 2048x7168x8192 FP32 (1x128 B)",
              lambda s: g(s["qdt"], s["sdt"], s["qxt"], s["sxt"], 1, torch.float32, out=s["dwf"]), sets, cfg,
              flops=fl)
+        # the MX variant of the trio: every operand MX-quantized along its GEMM's contraction
+        for s in sets:
+            s["mqx"], s["mex"] = fp8.fp8_quant_mx_1x32(s["x"])
+            s["mqw"], s["mew"] = fp8.fp8_quant_mx_1x32(s["w"])
+            s["mqd"], s["med"] = fp8.fp8_quant_mx_1x32(s["dy"])
+            s["mqwt"], s["mewt"] = fp8.fp8_quant_mx_1x32_transposed(s["w"])
+            s["mqdt"], s["medt"] = fp8.fp8_quant_mx_1x32_transposed(s["dy"])
+            s["mqxt"], s["mext"] = fp8.fp8_quant_mx_1x32_transposed(s["x"])
+        n = sets[0]["x"].numel()
+        line("linear_trio", "quant_mx_1x32_transposed X (blocks of 32 tokens)",
+             lambda s: fp8.fp8_quant_mx_1x32_transposed(s["x"], q=s["mqxt"], e=s["mext"]), sets,
+             dict(cfg, scales="E8M0 per 32 tokens"), nbytes=n * 5 + n // 32)
+        mcfg = dict(cfg, scales="E8M0 per 1x32 block along each GEMM's contraction")
+        gm = fp8.fp8_gemm_mx
+        line("linear_trio", "gemm_mx Fprop 8192x2048x7168 BF16 (MX operands)",
+             lambda s: gm(s["mqx"], s["mex"], s["mqw"], s["mew"], bf, out=s["yb"]), sets, mcfg, flops=fl,
+             peak="FP8 (scaled MFMA)")
+        line("linear_trio", "gemm_mx Dgrad 8192x7168x2048 BF16 (MX operands)",
+             lambda s: gm(s["mqd"], s["med"], s["mqwt"], s["mewt"], bf, out=s["dxb"]), sets, mcfg, flops=fl,
+             peak="FP8 (scaled MFMA)")
+        line("linear_trio", "gemm_mx Wgrad 2048x7168x8192 FP32 (MX operands)",
+             lambda s: gm(s["mqdt"], s["medt"], s["mqxt"], s["mext"], torch.float32, out=s["dwf"]), sets, mcfg,
+             flops=fl, peak="FP8 (scaled MFMA)")
     elif args.workload == "moe_contig":
         G, N, K = 32, 4096, 7168
         sets = []

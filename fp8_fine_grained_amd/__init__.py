@@ -22,15 +22,15 @@ BSCALE_1x128 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
 
-ABI_VERSION = 11
+ABI_VERSION = 12
 EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
            "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
            "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16", "fp8_requant_act_tokenwise",
            "fp8_quant_mx_1x32", "fp8_gemm_mx", "fp8_gemm_blockscaled_fp8out", "fp8_quant_fprop_operands",
            "fp8_tile_weights_decode", "fp8_grouped_gemm_masked_tiled", "fp8_gemm_blockscaled_fp8mfma",
            "fp8_grouped_gemm_contiguous_fp8out", "fp8_grouped_gemm_contiguous_mx", "fp8_grouped_gemm_masked_mx",
-           "fp8fg_status_string", "fp8fg_abi_version")
-_COMPUTE = EXPORTS[:18]
+           "fp8_quant_mx_1x32_transposed", "fp8fg_status_string", "fp8fg_abi_version")
+_COMPUTE = EXPORTS[:19]
 
 
 class Fp8fgError(RuntimeError):
@@ -62,6 +62,7 @@ def load_library(path=LIB_PATH):
     lib.fp8_quant_weight_128x128_bf16.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.fp8_requant_act_tokenwise.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     lib.fp8_quant_mx_1x32.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.fp8_quant_mx_1x32_transposed.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.fp8_gemm_mx.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     lib.fp8_gemm_blockscaled_fp8out.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.fp8_quant_fprop_operands.argtypes = [vp, i32, i64, vp, i32, i64, i64, vp, vp, vp, vp, vp]
@@ -219,6 +220,20 @@ def fp8_quant_mx_1x32(x, q=None, e=None):
     _need(q, torch.uint8, (R, K), "q")
     _need(e, torch.uint8, (K // 32, R), "e")
     _check("fp8_quant_mx_1x32", load_library().fp8_quant_mx_1x32(_ptr(x), R, K, _ptr(q), _ptr(e), _stream(x)))
+    return q, e
+
+
+def fp8_quant_mx_1x32_transposed(x, q=None, e=None):
+    """MX quantization of x f32 [M][K] in blocks of 32 rows, transposed:
+    (codes u8 [K][M], E8M0 scale bytes u8 [M/32][K]) = fp8_quant_mx_1x32(x^T)."""
+    M, K = x.shape
+    _need(x, torch.float32, (M, K), "x")
+    q = _empty((K, M), torch.uint8, x) if q is None else q
+    e = _empty((M // 32, K), torch.uint8, x) if e is None else e
+    _need(q, torch.uint8, (K, M), "q")
+    _need(e, torch.uint8, (M // 32, K), "e")
+    _check("fp8_quant_mx_1x32_transposed", load_library().fp8_quant_mx_1x32_transposed(
+        _ptr(x), M, K, _ptr(q), _ptr(e), _stream(x)))
     return q, e
 
 

@@ -129,6 +129,16 @@ int fp8_quant_mx_1x32(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t*
     return hip_status(fp8fg::launch_quant_mx(x, R, K, q, e, static_cast<hipStream_t>(stream)));
 }
 
+int fp8_quant_mx_1x32_transposed(const float* x, int64_t M, int64_t K, uint8_t* q, uint8_t* e, void* stream) {
+    if (M > 0 && K > 0 && (!x || !q || !e)) return FP8FG_ERR_NULL;   // empty arrays may be NULL
+    if (M < 0 || K < 0 || M % 32 != 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(e)) return FP8FG_ERR_ALIGN;
+    if (M > kMaxDim || K > kMaxDim || (M > 0 && K > kMaxElems / M)) return FP8FG_ERR_UNSUPPORTED;
+    if ((K + 63) / 64 > 65535) return FP8FG_ERR_UNSUPPORTED;
+    if (M == 0 || K == 0) return FP8FG_OK;
+    return hip_status(fp8fg::launch_quant_mx_tokens(x, M, K, q, e, static_cast<hipStream_t>(stream)));
+}
+
 int fp8_gemm_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb, void* c, int out_dtype,
                 int64_t M, int64_t N, int64_t K, void* stream) {
     if (!a || !ea || !b || !eb || !c) return FP8FG_ERR_NULL;

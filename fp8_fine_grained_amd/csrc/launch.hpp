@@ -26,6 +26,8 @@ hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, int t
 hipError_t launch_requant_act_tokens(const uint8_t* qr, const float* sr, int64_t M, int64_t K, uint8_t* q, float* s,
                                      hipStream_t stream);
 hipError_t launch_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e, hipStream_t stream);
+// MX blocks of 32 along M, codes transposed: q [K][M], e [M/32][K]
+hipError_t launch_quant_mx_tokens(const float* x, int64_t M, int64_t K, uint8_t* q, uint8_t* e, hipStream_t stream);
 // both Fprop operands (rowwise activation, 128x128 weight, no transpose) in one launch
 hipError_t launch_quant_fprop(const void* x, int x_bf16, int64_t M, const void* w, int w_bf16, int64_t N, int64_t K,
                               uint8_t* qa, float* sa, uint8_t* qb, float* sb, hipStream_t stream);

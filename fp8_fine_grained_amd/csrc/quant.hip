@@ -183,9 +183,12 @@ struct CacheSrc {
     }
 };
 
-template <class Src>
+// MX = true: the MX rule instead (blocks of 32 tokens, E8M0 scale bytes
+// e [M/32][K]; see quant_mx_rows): each lane's 32 tokens of its channel are
+// one whole block, so no partial maxima are exchanged.
+template <class Src, bool MX = false, class S = float>
 __device__ __forceinline__ void quant_tokens_core(const Src& src, int64_t M, int64_t K, uint8_t* __restrict__ q,
-                                                  float* __restrict__ s) {
+                                                  S* __restrict__ s) {
     __shared__ __align__(16) float tile[kBlock][kTokCh + 1];
     __shared__ float part[4][kTokCh];
     // the codes reuse the tile's memory: every read of the tile precedes the
@@ -234,21 +237,36 @@ __device__ __forceinline__ void quant_tokens_core(const Src& src, int64_t M, int
         v[i] = tile[quarter * 32 + i][c];
         amax = fmaxf(amax, fabsf(v[i]));
     }
-    part[quarter][c] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(part[0][c], part[1][c]), fmaxf(part[2][c], part[3][c]));
-    const float sc = amax / 448.0f;
-    const float rc = 1.0f / sc;
     const int64_t k = k0 + c;
     uint32_t w[8];
+    if constexpr (MX) {
+        const int field = int((__float_as_uint(amax) >> 23) & 0xFF);
+        const int sh = field - 135 < -127 ? -127 : field - 135;
+        const float mul = __uint_as_float(uint32_t(127 - sh) << 23);   // 2^-s, a normal float
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = encode4(v4f{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]}, sc, rc);
+        for (int i = 0; i < 8; ++i) {
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = fmaxf(fminf(v[4 * i + j] * mul, 448.0f), -448.0f);
+            w[i] = cvt4(y[0], y[1], y[2], y[3]);
+        }
+        if (k < K && mb * kBlock + quarter * 32 < M) s[(mb * 4 + quarter) * K + k] = S(sh + 127);
+        __syncthreads();   // every read of the tile is done before the codes overwrite it
+    } else {
+        part[quarter][c] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(part[0][c], part[1][c]), fmaxf(part[2][c], part[3][c]));
+        const float sc = amax / 448.0f;
+        const float rc = 1.0f / sc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = encode4(v4f{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]}, sc, rc);
+        if (quarter == 0 && k < K) s[mb * K + k] = sc;
+    }
     // the codes go through LDS as [channel][token], so that each store
     // instruction below writes eight whole 128-byte row segments of q^T
     // instead of 64 scattered 16-byte pieces
     st<u32x4>(&codes[c][quarter * 32], u32x4{w[0], w[1], w[2], w[3]});
     st<u32x4>(&codes[c][quarter * 32 + 16], u32x4{w[4], w[5], w[6], w[7]});
-    if (quarter == 0 && k < K) s[mb * K + k] = sc;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -493,6 +511,18 @@ __global__ __launch_bounds__(256) void quant_mx_rows(const float* __restrict__ x
             if ((lane & 3) == 0) e[(k / kMxBlock) * R + m] = uint8_t(sh + 127);
         }
     }
+}
+
+// MX blocks of 32 tokens, codes written transposed: q [K][M], e [M/32][K]
+// (exactly quant_mx_rows of x^T), through the token-wise kernel's staging
+__global__ __launch_bounds__(256) void quant_mx_tokens(const float* __restrict__ x, int64_t M, int64_t K,
+                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ e) {
+    quant_tokens_core<DenseSrc<float>, true>(DenseSrc<float>{x, K}, M, K, q, e);
+}
+
+hipError_t launch_quant_mx_tokens(const float* x, int64_t M, int64_t K, uint8_t* q, uint8_t* e, hipStream_t stream) {
+    const dim3 grid(unsigned((M + kBlock - 1) / kBlock), unsigned((K + kTokCh - 1) / kTokCh));
+    return launch_kernel(quant_mx_tokens, grid, dim3(256), stream, x, M, K, q, e);
 }
 
 hipError_t launch_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e, hipStream_t stream) {

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 11
+#define FP8FG_ABI_VERSION 12
 
 enum fp8fg_status {
     FP8FG_OK = 0,
@@ -179,6 +179,14 @@ int fp8_requant_act_tokenwise(const uint8_t* q, const float* s, int64_t M, int64
  *   e u8 [K/32][R]:  s = clamp(floor(log2(amax)) - 8, -127, 127) per block
  *   (amax = 0 gives -127), code = E4M3_RNE_SAT(RN32(x * 2^-s)), e = s + 127.
  *   Requires K % 32 == 0; R * K < 2^40.
+ * fp8_quant_mx_1x32_transposed: the same rule on blocks of 32 consecutive
+ *   rows (tokens) of one column, codes written transposed -- exactly
+ *   fp8_quant_mx_1x32 applied to x^T: x f32 [M][K] -> q u8 [K][M], e u8
+ *   [M/32][K].  The operands of the MX Wgrad (X and dY, contraction over
+ *   tokens) and the MX Dgrad weight (W [N][K] -> W^T blocked along N; "The
+ *   Insider Secrets Of Deepseek Discovered", Figure 6: all three GEMMs of a
+ *   Linear in FP8).  Requires M % 32 == 0 (any K); M * K < 2^40,
+ *   ceil(K / 64) <= 65535.  Empty arrays may be NULL.
  * fp8_gemm_mx: C[M][N] = sum_k decode(a) 2^(ea-127) decode(b) 2^(eb-127) with
  *   a u8 [M][K], ea u8 [K/32][M], b u8 [N][K], eb u8 [K/32][N]; c BF16 or FP32
  *   [M][N].  Accuracy: |C - C*| <= 2^-9 * S (S = sum_k |a_k b_k| of the
@@ -187,6 +195,7 @@ int fp8_requant_act_tokenwise(const uint8_t* q, const float* s, int64_t M, int64
  *   K % 64 == 0, K > 0 when M * N > 0, K < 2^24, (K / 32) * max(M, N) < 2^32.
  */
 int fp8_quant_mx_1x32(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e, void* stream);
+int fp8_quant_mx_1x32_transposed(const float* x, int64_t M, int64_t K, uint8_t* q, uint8_t* e, void* stream);
 int fp8_gemm_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb,
                 void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream);
 

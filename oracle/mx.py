@@ -52,3 +52,13 @@ def scales_of(e):
 def dequant_mx(q, e):
     """Exact float64 values of MX-quantized rows: q u8 [R][K], e u8 [K/32][R]."""
     return e4m3.decode(q) * np.repeat(scales_of(e).T, BLOCK, axis=1)
+
+
+def quant_mx_1x32_transposed(x):
+    """x float32 [M][K] (M % 32 == 0) -> (codes u8 [K][M], scale bytes u8 [M/32][K]):
+    the same rule on blocks of 32 consecutive rows of one column, i.e. the
+    rowwise quantizer applied to x^T.  These are the MX operands whose
+    contraction runs over x's rows: X and dY of the Wgrad GEMM (tokens), and W
+    of the Dgrad GEMM (output features)."""
+    x = np.asarray(x, dtype=np.float32)
+    return quant_mx_1x32(np.ascontiguousarray(x.T))

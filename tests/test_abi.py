@@ -115,6 +115,13 @@ def test_mx_argument_errors():
     assert q(P, 4, 48, P, P2, NUL) == ESHAPE            # K % 32
     assert q(MIS, 4, 64, P, P2, NUL) == EALIGN
     assert q(P, 0, 64, P, P2, NUL) == OK
+    t = lib.fp8_quant_mx_1x32_transposed
+    assert t(NUL, 64, 8, P, P2, NUL) == ENULL
+    assert t(P, 48, 8, P, P2, NUL) == ESHAPE             # M % 32 (the blocked axis)
+    assert t(P, -32, 8, P, P2, NUL) == ESHAPE
+    assert t(P, 64, 8, MIS, P2, NUL) == EALIGN
+    assert t(P, 64, 64 * 65535 + 1, P, P2, NUL) == EUNSUP
+    assert t(NUL, 0, 8, NUL, NUL, NUL) == OK             # empty: NULL allowed
     g = lib.fp8_gemm_mx
     assert g(P, P, P, NUL, P, 0, 4, 256, 64, NUL) == ENULL
     assert g(P, P, P, P, P, 0, 6, 256, 64, NUL) == ESHAPE     # M % 4

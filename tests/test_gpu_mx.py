@@ -199,3 +199,73 @@ def test_mx_masked_decode_full_size():
         rows = np.unique(np.concatenate([[0, m - 1], rng.integers(0, m, 3)]))
         cg = c[g][torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
         _check(cg, mx.dequant_mx(qa[g], ea[g])[rows], mx.dequant_mx(qb[g], eb[g]), "bf16", f"mx masked full g={g}")
+
+
+# ---------------------------------------------------------------------------
+# MX operands blocked along the rows (tokens for Wgrad, output features for
+# the Dgrad weight): the transposed quantizer and the MX trio of a Linear.
+
+def _inputs_t(rng, M, K):
+    x = (rng.standard_normal((M, K)) * np.exp(rng.uniform(-6, 6, size=(1, K)))).astype(np.float32)
+    if M >= 96 and K > 2:
+        x[:32, 0] = 0.0
+        x[5, 0] = -0.0
+        x[32:64, 1] = np.float32(1.9)                           # saturation
+        x[64:96, 2] = np.float32(2.0 ** -130) * np.arange(32)   # subnormal block: scale clamps
+    return x
+
+
+@pytest.mark.parametrize("M,K", [(32, 1), (96, 70), (128, 64), (160, 300), (4096, 33)])
+def test_quant_mx_transposed_bit_exact(M, K):
+    x = _inputs_t(np.random.default_rng(M + 5 * K), M, K)
+    q, e = fp8.fp8_quant_mx_1x32_transposed(dev(x))
+    oq, oe = mx.quant_mx_1x32_transposed(x)
+    assert np.array_equal(host(e), oe)
+    bad = np.argwhere(host(q) != oq)
+    assert bad.size == 0, bad[:5].tolist()
+
+
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_mx_linear_trio_small(out):
+    """Fprop, Dgrad and Wgrad of a 512 -> 256 Linear at 192 tokens, every
+    operand MX-quantized by the oracle along its GEMM's contraction; the GPU
+    quantizers give the same bytes."""
+    rng = np.random.default_rng(95)
+    T, IN, OUT = 192, 512, 256
+    x = workloads.activations(rng, T, IN, 0.01, 50.0)
+    w = workloads.weights(rng, OUT, IN)
+    dy = workloads.activations(rng, T, OUT, sigma=1e-3)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    qx, ex = mx.quant_mx_1x32(x)
+    qw, ew = mx.quant_mx_1x32(w)
+    qd, ed = mx.quant_mx_1x32(dy)
+    qwt, ewt = mx.quant_mx_1x32_transposed(w)       # W^T [IN][OUT], blocks along OUT
+    qdt, edt = mx.quant_mx_1x32_transposed(dy)      # dY^T [OUT][T], blocks along tokens
+    qxt, ext = mx.quant_mx_1x32_transposed(x)       # X^T [IN][T]
+    for src, (oq, oe) in ((w, (qwt, ewt)), (dy, (qdt, edt)), (x, (qxt, ext))):
+        gq, ge = fp8.fp8_quant_mx_1x32_transposed(dev(src))
+        assert np.array_equal(host(gq), oq) and np.array_equal(host(ge), oe)
+    for name, (qa, ea, qb, eb) in (("fprop", (qx, ex, qw, ew)), ("dgrad", (qd, ed, qwt, ewt)),
+                                   ("wgrad", (qdt, edt, qxt, ext))):
+        c = fp8.fp8_gemm_mx(dev(qa), dev(ea), dev(qb), dev(eb), od)
+        _check(c.float().cpu().numpy().astype(np.float64), mx.dequant_mx(qa, ea), mx.dequant_mx(qb, eb), out,
+               f"mx trio {name} {out}")
+
+
+@pytest.mark.timeout(900)
+def test_mx_wgrad_full_size():
+    """dW = dY^T . X of the 7168 -> 2048 Linear at 8192 tokens (M = 2048,
+    N = 7168, K = 8192), both operands MX along tokens: the GPU quantizer's
+    bytes equal the oracle's, and sampled rows of the FP32 dW are within the
+    MX bound."""
+    x, _, dy = workloads.linear_trio()
+    qdt, edt = mx.quant_mx_1x32_transposed(dy)
+    qxt, ext = mx.quant_mx_1x32_transposed(x)
+    gq, ge = fp8.fp8_quant_mx_1x32_transposed(dev(x))
+    assert np.array_equal(host(ge), ext) and np.array_equal(host(gq), qxt)
+    del gq, ge
+    c = fp8.fp8_gemm_mx(dev(qdt), dev(edt), dev(qxt), dev(ext), torch.float32)
+    rows = np.unique(np.concatenate([np.random.default_rng(96).choice(2048, 24, replace=False), [0, 2047]]))
+    torch.cuda.synchronize()
+    cg = c[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    _check(cg, mx.dequant_mx(qdt, edt)[rows], mx.dequant_mx(qxt, ext), "fp32", "mx wgrad full size")

@@ -103,3 +103,21 @@ def test_dequant_error_bound():
     y = np.abs(x.astype(np.float64)) / scale
     lim = np.where(y > 448, y - 448 + 1e-12, e4m3.ulp_at(y) / 2) * scale
     assert np.all(np.abs(back - x) <= lim * (1 + 1e-12))
+
+
+def test_transposed_blocks_run_down_the_columns():
+    """The transposed quantizer's blocks are 32 consecutive rows of one column:
+    against the exact brute force on x^T, and a column whose 32-row blocks have
+    maxima 2^j (j = 0, 1, 2) gets scale bytes 127 + j - 8 in rows j of e."""
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((96, 5)) * np.exp(rng.uniform(-4, 4, size=(1, 5)))).astype(np.float32)
+    q, e = mx.quant_mx_1x32_transposed(x)
+    bq, be = _brute(np.ascontiguousarray(x.T))
+    assert q.shape == (5, 96) and e.shape == (3, 5)
+    assert np.array_equal(q, bq) and np.array_equal(e, be)
+    y = np.full((96, 2), 0.25, np.float32)
+    for j in range(3):
+        y[32 * j + 7, 0] = np.float32(2.0 ** j)
+    _, ey = mx.quant_mx_1x32_transposed(y)
+    assert ey[:, 0].tolist() == [119, 120, 121]
+    assert ey[:, 1].tolist() == [117, 117, 117]          # amax 2^-2: s = -2 - 8
