@@ -612,6 +612,16 @@ def run_extra(args):
                  lambda s: fp8.fp8_grouped_gemm_masked_tiled(s["qa"], s["sa"], s["qt"], s["sb"], s["mmt"],
                                                              out=s["c"]),
                  sets, dict(cfg, weights="decode-tiled layout (fp8_tile_weights_decode)"), nbytes=nbytes)
+            # the same GEMM writing the down projection's (or next layer's) FP8 operand
+            for s in sets:
+                s["qy"] = torch.zeros((G, MMAX, N), dtype=torch.uint8, device="cuda")
+                s["sy"] = torch.zeros((G, N // 128, MMAX), dtype=torch.float32, device="cuda")
+            nbytes_q = nbytes - valid * N * 2 + valid * N + valid * (N // 128) * 4
+            line("moe_masked", f"grouped_gemm_masked_tiled_fp8out N={N} K={K} (fused 1x128 output quantization)",
+                 lambda s: fp8.fp8_grouped_gemm_masked_tiled_fp8out(s["qa"], s["sa"], s["qt"], s["sb"], s["mmt"],
+                                                                    q=s["qy"], s=s["sy"]),
+                 sets, dict(cfg, weights="decode-tiled layout", output="FP8 codes + 1x128 scales along N"),
+                 nbytes=nbytes_q)
             # the MX variant: the same valid-row counts, fresh MX operands
             for s in sets:
                 a = gpu_acts(gen, G * MMAX, K, 0.001, 100.0).reshape(G, MMAX, K)

@@ -22,15 +22,16 @@ BSCALE_1x128 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
 
-ABI_VERSION = 12
+ABI_VERSION = 13
 EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
            "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
            "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16", "fp8_requant_act_tokenwise",
            "fp8_quant_mx_1x32", "fp8_gemm_mx", "fp8_gemm_blockscaled_fp8out", "fp8_quant_fprop_operands",
            "fp8_tile_weights_decode", "fp8_grouped_gemm_masked_tiled", "fp8_gemm_blockscaled_fp8mfma",
            "fp8_grouped_gemm_contiguous_fp8out", "fp8_grouped_gemm_contiguous_mx", "fp8_grouped_gemm_masked_mx",
-           "fp8_quant_mx_1x32_transposed", "fp8fg_status_string", "fp8fg_abi_version")
-_COMPUTE = EXPORTS[:19]
+           "fp8_quant_mx_1x32_transposed", "fp8_grouped_gemm_masked_tiled_fp8out", "fp8fg_status_string",
+           "fp8fg_abi_version")
+_COMPUTE = EXPORTS[:20]
 
 
 class Fp8fgError(RuntimeError):
@@ -69,6 +70,7 @@ def load_library(path=LIB_PATH):
     lib.fp8_tile_weights_decode.argtypes = [vp, i64, i64, i64, vp, vp]
     lib.fp8_grouped_gemm_masked_tiled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     lib.fp8_grouped_gemm_contiguous_fp8out.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp]
+    lib.fp8_grouped_gemm_masked_tiled_fp8out.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp]
     lib.fp8_grouped_gemm_contiguous_mx.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     lib.fp8_grouped_gemm_masked_mx.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     for name in _COMPUTE:
@@ -389,6 +391,26 @@ def fp8_grouped_gemm_masked(a, sa, b, sb, masked_m, out_dtype=torch.bfloat16, ou
         _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(masked_m), G, M_max, N, K, _ptr(out),
         _out_dtype(out_dtype), _stream(a)))
     return out
+
+
+def fp8_grouped_gemm_masked_tiled_fp8out(a, sa, b_tiled, sb, masked_m, q=None, s=None):
+    """fp8_grouped_gemm_masked_tiled with the output quantized 1x128 along N in
+    the epilogue: returns (q u8 [G][M_max][N], s f32 [G][N/128][M_max]); rows
+    past masked_m[g] are left as they were (zeros when q, s are allocated here)."""
+    G, M_max, K = a.shape
+    N = b_tiled.shape[1] * 256
+    _need(a, torch.uint8, (G, M_max, K), "a")
+    _need(sa, torch.float32, (G, _nb(K), M_max), "sa")
+    _need(b_tiled, torch.uint8, (G, N // 256, K // 64, 16384), "b_tiled")
+    _need(sb, torch.float32, (G, _nb(N), _nb(K)), "sb")
+    _need(masked_m, torch.int32, (G,), "masked_m")
+    q = torch.zeros((G, M_max, N), dtype=torch.uint8, device=a.device) if q is None else q
+    s = torch.zeros((G, N // 128, M_max), dtype=torch.float32, device=a.device) if s is None else s
+    _need(q, torch.uint8, (G, M_max, N), "q")
+    _need(s, torch.float32, (G, N // 128, M_max), "s")
+    _check("fp8_grouped_gemm_masked_tiled_fp8out", load_library().fp8_grouped_gemm_masked_tiled_fp8out(
+        _ptr(a), _ptr(sa), _ptr(b_tiled), _ptr(sb), _ptr(masked_m), G, M_max, N, K, _ptr(q), _ptr(s), _stream(a)))
+    return q, s
 
 
 def fp8_tile_weights_decode(q, out=None):

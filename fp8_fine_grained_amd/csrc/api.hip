@@ -307,6 +307,23 @@ int fp8_tile_weights_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, u
     return hip_status(fp8fg::launch_tile_weights_decode(q, G, N, K, q_tiled, static_cast<hipStream_t>(stream)));
 }
 
+int fp8_grouped_gemm_masked_tiled_fp8out(const uint8_t* a, const float* sa, const uint8_t* b_tiled, const float* sb,
+                                         const int32_t* masked_m, int64_t G, int64_t M_max, int64_t N, int64_t K,
+                                         uint8_t* q, float* s, void* stream) {
+    if (!a || !sa || !b_tiled || !sb || !masked_m || !q || !s) return FP8FG_ERR_NULL;
+    if (G < 0 || M_max < 0 || N < 0 || K < 0 || N % 256 != 0 || K % 64 != 0) return FP8FG_ERR_SHAPE;
+    if (K == 0 && M_max > 0 && N > 0 && G > 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(sa) || !aligned16(b_tiled) || !aligned16(sb) || !aligned16(q) || !aligned16(s) ||
+        !aligned16(masked_m))
+        return FP8FG_ERR_ALIGN;
+    if (M_max > 128 || N > kMaxDim || (K + 127) / 128 > kWideMaxKBlocks || G > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if (N > 0 && G > kMaxDim / (2 * (N / 256))) return FP8FG_ERR_UNSUPPORTED;
+    if (G * ((M_max + 63) / 64) > 4096) return FP8FG_ERR_UNSUPPORTED;
+    if (G == 0 || M_max == 0 || N == 0) return FP8FG_OK;
+    fp8fg::GemmArgs args{a, sa, b_tiled, sb, q, masked_m, M_max, N, K, G, s};
+    return hip_status(fp8fg::launch_gemm_masked_tiled(2, args, static_cast<hipStream_t>(stream)));
+}
+
 int fp8_grouped_gemm_masked_tiled(const uint8_t* a, const float* sa, const uint8_t* b_tiled, const float* sb,
                                   const int32_t* masked_m, int64_t G, int64_t M_max, int64_t N, int64_t K, void* c,
                                   int out_dtype, void* stream) {

@@ -2429,6 +2429,7 @@ struct DregSrc {
     uint32_t va, vb[4], vsa[2];
     uint32_t sa_step;      // bytes between K-blocks of the A scales
     int64_t c_off;         // element offset of C at (row m0, column n0)
+    int64_t s_off;         // FP8 output: offset of the scale of (row m0, 128-column group of n0)
     int rows;              // valid rows from m0, at most 64
 };
 
@@ -2465,6 +2466,7 @@ __device__ __forceinline__ DregSrc dreg_src(const GemmArgs& args, const uint32_t
     DregSrc s;
     s.rows = rows;
     s.c_off = (g * M + m0) * N + bn * BN;
+    s.s_off = (g * (N / 128) + bn * BN / 128) * M + m0;
     const int r = lane & 31, sub = lane >> 2, slot = lane & 3;
     // A piece of this wave: rows ROWS * wave .. of the m-tile, 16 bytes per
     // lane in the ring's order (chunk c of row rr at slot c ^ ((rr >> 2) & 3));
@@ -2538,11 +2540,53 @@ constexpr int dreg_later(int p, int ahead) {
     return n;
 }
 
+// OUT 2 (FP8 output): C's 1x128 quantization along N -- exactly the rowwise
+// quantizer on the FP32 C that OUT 1 writes.  A 128-column group is the
+// columns of waves 2p and 2p + 1 (items of 256 or 512 columns); each wave
+// takes its rows' max-abs over its 64 columns, the pair meets in `xch`.
 template <int OUT>
 __device__ __forceinline__ void dreg_store(const GemmArgs& args, const DregSrc& c, int wave, int lane,
-                                           const v16f (&acc)[2][2], const WideScales<2>& w) {
+                                           const v16f (&acc)[2][2], const WideScales<2>& w, float* xch) {
     const int r = lane & 31, h = lane >> 5;
     const int64_t N = args.N;
+    if constexpr (OUT == 2) {
+        float am[2];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+            am[mi] = 0.0f;
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) am[mi] = fmaxf(am[mi], fabsf(acc[mi][ni][i] * w.unit[mi]));
+            am[mi] = fmaxf(am[mi], __shfl_xor(am[mi], 32, 64));
+            if (h == 0) xch[wave * 64 + mi * 32 + r] = am[mi];
+        }
+        // LDS only: the weight loads in flight for the next item keep going
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");   // the partner's maxima are read after the barrier
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+            const float amax = fmaxf(am[mi], xch[(wave ^ 1) * 64 + mi * 32 + r]);
+            const float sc = amax / 448.0f;
+            const float rc = 1.0f / sc;
+            const int m = mi * 32 + r;
+            if (m >= c.rows) continue;
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                uint32_t d[4][1];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
+                                      acc[mi][ni][4 * j + 3]} * w.unit[mi];
+                    d[j][0] = encode4(v, sc, rc);
+                }
+                store_fp8_runs(static_cast<uint8_t*>(args.c) + c.c_off + int64_t(m) * N + wave * 64 + ni * 32, h, d);
+            }
+            if (h == 0 && (wave & 1) == 0) args.cs[c.s_off + (wave >> 1) * args.M + m] = sc;
+        }
+        return;
+    }
     const int n_lane = wave * 64 + 4 * h;
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
@@ -2649,6 +2693,8 @@ template <int OUT, int NP, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
     static_assert(NP % 2 == 0 && NP >= 2 && NP <= 8, "whole K-blocks per ring turn");
     static_assert(NW == 4 || NW == 7 || NW == 8, "items of 256, 448 or 512 columns");
+    static_assert(OUT != 2 || NW % 2 == 0, "FP8 output: 128-column groups are wave pairs");
+    __shared__ float xch[OUT == 2 ? 64 * NW : 1];   // FP8 output: the waves' row maxima
     // the ring, the zero line and (seven waves) the dummy line of the non-copying waves
     __shared__ __align__(16) uint8_t lds[NP * 4096 + 64 + (NW == 7 ? 1024 : 0)];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -2738,7 +2784,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
         FP8FG_DREG_STEP(7)
 #undef FP8FG_DREG_STEP
         if (item_ends) {
-            dreg_store<OUT>(args, cs, wave, lane, acc, w);
+            dreg_store<OUT>(args, cs, wave, lane, acc, w, xch);
             dreg_reset(acc, w);
             cs = is;
         }
@@ -2748,7 +2794,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
 
 #define FP8FG_DREG_KERNELS(X) \
     X(0, 4, 4) X(0, 2, 4) X(1, 4, 4) X(1, 2, 4) X(0, 4, 8) X(0, 2, 8) X(1, 4, 8) X(1, 2, 8) \
-    X(0, 4, 7) X(0, 2, 7) X(1, 4, 7) X(1, 2, 7)
+    X(0, 4, 7) X(0, 2, 7) X(1, 4, 7) X(1, 2, 7) X(2, 4, 4) X(2, 2, 4) X(2, 4, 8) X(2, 2, 8)
 #define FP8FG_DREG_INST(OUT, NP, NW) template __global__ void gemm_dreg<OUT, NP, NW>(GemmArgs);
 FP8FG_DREG_KERNELS(FP8FG_DREG_INST)
 #undef FP8FG_DREG_INST
@@ -2819,16 +2865,17 @@ int masked_xcds(const GemmArgs& args, int64_t bm) {
 // item -> XCD grouping assumes it); ring depth NP 4 when it divides the
 // half-block count, else 2.  Items of 512 or 448 columns (one 8- or 7-wave
 // workgroup per CU), whichever N allows and fills more slots, else 256 (two
-// 4-wave workgroups per CU).
+// 4-wave workgroups per CU).  `pairs` (the FP8 output) leaves out 448: its
+// 128-column groups must be wave pairs of one item.
 struct DregGrid {
     int nw;
     int64_t P;
 };
-DregGrid dreg_grid(const GemmArgs& args, int cus) {
+DregGrid dreg_grid(const GemmArgs& args, int cus, bool pairs) {
     DregGrid best{0, 0};
     double best_use = -1.0;
     for (const int nw : {8, 7, 4}) {
-        if (args.N % (64 * nw) != 0) continue;
+        if (args.N % (64 * nw) != 0 || (pairs && nw % 2 != 0)) continue;
         const int64_t items = args.G * ((args.M + 63) / 64) * (args.N / (64 * nw));
         if (items == 0) return DregGrid{nw, 0};
         const int64_t slots = (nw == 4 ? 2 : 1) * int64_t(cus > 0 ? cus : 1);
@@ -2850,7 +2897,7 @@ hipError_t launch_dreg(int out_fp32, const GemmArgs& args, hipStream_t stream) {
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const DregGrid grid = dreg_grid(args, cus);
+    const DregGrid grid = dreg_grid(args, cus, out_fp32 == 2);   // FP8 output: wave pairs own 128 columns
     const int nw = grid.nw;
     const int64_t P = grid.P;
     if (P == 0) return hipSuccess;

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 12
+#define FP8FG_ABI_VERSION 13
 
 enum fp8fg_status {
     FP8FG_OK = 0,
@@ -365,6 +365,24 @@ int fp8_tile_weights_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, u
 int fp8_grouped_gemm_masked_tiled(const uint8_t* a, const float* sa, const uint8_t* b_tiled, const float* sb,
                                   const int32_t* masked_m, int64_t G, int64_t M_max,
                                   int64_t N, int64_t K, void* c, int out_dtype, void* stream);
+
+/*
+ * fp8_grouped_gemm_masked_tiled with the next layer's quantization fused into
+ * the epilogue ("The Insider Secrets Of Deepseek Discovered", passage on
+ * Figure 6: every Linear runs in FP8, so a layer's output is quantized again
+ * before the next GEMM reads it), the decode counterpart of
+ * fp8_grouped_gemm_contiguous_fp8out.  Computes the FP32 C of
+ * fp8_grouped_gemm_masked_tiled and writes, instead of C, its 1x128
+ * quantization along N, in the masked A operand's own layout:
+ *   q: u8 [G][M_max][N], s: f32 [G][N/128][M_max] -- for every valid row,
+ *   exactly fp8_quant_act_1x128 applied to the FP32 C that out_dtype =
+ *   FP8FG_OUT_FP32 would write (same values, bit for bit); rows at or beyond
+ *   masked_m[g] are not written (neither q nor s).
+ * Same arguments and rules as fp8_grouped_gemm_masked_tiled.
+ */
+int fp8_grouped_gemm_masked_tiled_fp8out(const uint8_t* a, const float* sa, const uint8_t* b_tiled, const float* sb,
+                                         const int32_t* masked_m, int64_t G, int64_t M_max,
+                                         int64_t N, int64_t K, uint8_t* q, float* s, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp8fg_status_string(int status);

@@ -224,6 +224,16 @@ def test_decode_tiled_argument_errors():
     assert m(P, P, P, P, P, 4, 129, 256, 128, P, 0, NUL) == EUNSUP   # M_max > 128
     assert m(P, P, P, P, P, 0, 128, 256, 128, P, 0, NUL) == OK       # G = 0
     assert m(P, P, P, P, P, 4, 0, 256, 128, P, 0, NUL) == OK         # M_max = 0
+    f = lib.fp8_grouped_gemm_masked_tiled_fp8out
+    #        a  sa  b  sb  mm  G  M_max N    K    q  s
+    assert f(P, P, P, P, P, 4, 128, 256, 128, P, NUL, NUL) == ENULL
+    assert f(P, P, P, P, P, 4, 128, 128, 128, P, P2, NUL) == ESHAPE     # N % 256
+    assert f(P, P, P, P, P, 4, 128, 256, 96, P, P2, NUL) == ESHAPE      # K % 64
+    assert f(P, P, P, P, P, 4, 128, 256, 0, P, P2, NUL) == ESHAPE       # K = 0 with work to do
+    assert f(P, P, P, P, P, 4, 128, 256, 128, P, MIS, NUL) == EALIGN
+    assert f(P, P, P, P, P, 4, 129, 256, 128, P, P2, NUL) == EUNSUP     # M_max > 128
+    assert f(P, P, P, P, P, 4, 128, 256, 92 * 128 + 64, P, P2, NUL) == EUNSUP   # beyond 92 K-blocks
+    assert f(P, P, P, P, P, 0, 128, 256, 128, P, P2, NUL) == OK         # G = 0
 
 
 def test_python_binding_refuses_cpu_tensors():

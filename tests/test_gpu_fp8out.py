@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import fp8_fine_grained_amd as fp8
-from oracle import e4m3, gemm, quant
+from oracle import e4m3, gemm, layout, quant
 import workloads
 
 pytestmark = pytest.mark.gpu
@@ -181,3 +181,98 @@ def test_contiguous_fp8out_full_size():
     rows = np.unique(np.concatenate([np.concatenate(rows), rng.integers(0, int(off[-1]), 64)]))
     sel, cr, s_abs = gemm.grouped_contiguous_ref(qa, sa, qb, sb, off, rows=rows)
     _check_valid(host(q)[sel], host(s)[:, sel], cr, s_abs, "contiguous fp8out full size")
+
+
+# ---------------------------------------------------------------------------
+# The masked decode layout on decode-tiled weights with the fused output
+# quantization (fp8_grouped_gemm_masked_tiled_fp8out): codes u8 [G][M_max][N],
+# scales f32 [G][N/128][M_max], the masked A operand's own layout.
+
+def _masked_tiled_fp8out(qa, sa, qb, sb, mm):
+    args = [dev(qa), dev(sa), dev(layout.tile_weights_decode(qb)), dev(sb), dev(np.asarray(mm, np.int32))]
+    q, s = fp8.fp8_grouped_gemm_masked_tiled_fp8out(*args)
+    return args, q, s
+
+
+@pytest.mark.parametrize("N", [512, 768])
+def test_masked_tiled_exact_outputs_quantize_bit_for_bit(N):
+    """Identity experts (one nonzero product per output, power-of-two A
+    scales), 512-column items (N = 512) and 256-column items (N = 768): the
+    valid rows' codes and scales equal the oracle's quantization of the exact
+    C; rows past masked_m keep the zeros they had."""
+    rng = np.random.default_rng(64 + N)
+    G, M_max, K = 4, 128, N
+    mm = np.array([128, 0, 1, 77])
+    qa = rng.integers(0, 256, size=(G, M_max, K), dtype=np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0x00
+    sa = (2.0 ** rng.integers(-20, 21, size=(G, K // 128, M_max))).astype(np.float32)
+    eye = np.where(np.eye(N, K, dtype=bool), np.uint8(0x38), np.uint8(0)).astype(np.uint8)
+    qb = np.stack([eye] * G)
+    sb = np.ones((G, N // 128, K // 128), np.float32)
+    _, q, s = _masked_tiled_fp8out(qa, sa, qb, sb, mm)
+    gq, gs = host(q), host(s)
+    for g in range(G):
+        m = int(mm[g])
+        c_exact = quant.dequant32(qa[g], np.repeat(sa[g].T, 128, axis=1)) + np.float32(0.0)
+        if m:
+            oq, os_ = quant.quant_act_1x128(c_exact[:m])
+            assert np.array_equal(gs[g][:, :m].view(np.uint32), os_.view(np.uint32)), g
+            bad = np.argwhere(gq[g, :m] != oq)
+            assert bad.size == 0, (g, [(tuple(i), hex(gq[g][tuple(i)]), hex(oq[tuple(i)])) for i in bad[:6]])
+        assert not gq[g, m:].any() and not gs[g][:, m:].any(), f"g={g}: rows past masked_m were written"
+
+
+@pytest.mark.parametrize("G,M_max,N,K", [(6, 128, 1024, 448), (5, 96, 768, 320), (3, 64, 256, 64)])
+def test_masked_tiled_fp8out_is_the_quantized_fp32_output(G, M_max, N, K):
+    """Ragged valid counts (M_max, 0, 1, 33, ...): the fused codes and scales
+    are the 1x128 quantizer applied to the FP32 output of the same GEMM, bit
+    for bit, on every valid row, and a valid quantization of the oracle's C."""
+    rng = np.random.default_rng(G * 10 + M_max + N + K)
+    mm = rng.integers(0, M_max + 1, G)
+    mm[:min(G, 4)] = [M_max, 0, 1, 33][:min(G, 4)]
+    qa, sa = zip(*[quant.quant_act_1x128(workloads.activations(rng, M_max, K, 0.01, 50.0)) for _ in range(G)])
+    qa, sa = np.stack(qa), np.stack(sa)
+    qs, ss = zip(*[quant.quant_weight_128x128(workloads.weights(rng, N, K)) for _ in range(G)])
+    qb, sb = np.stack(qs), np.stack(ss)
+    args, q, s = _masked_tiled_fp8out(qa, sa, qb, sb, mm)
+    c = fp8.fp8_grouped_gemm_masked_tiled(*args, torch.float32)
+    res = gemm.grouped_masked_ref(qa, sa, qb, sb, mm)
+    for g in range(G):
+        m = int(mm[g])
+        if m == 0:
+            assert not bool(q[g].any()) and not bool(s[g].any()), g
+            continue
+        rq, rs = fp8.fp8_quant_act_1x128(c[g, :m].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(q[g, :m], rq), g
+        assert torch.equal(s[g][:, :m].contiguous().view(torch.int32), rs.view(torch.int32)), g
+        assert not bool(q[g, m:].any()) and not bool(s[g][:, m:].any()), g
+        _check_valid(host(q[g, :m]), host(s[g][:, :m]), res[g][0], res[g][1], f"masked fp8out g={g}")
+
+
+@pytest.mark.timeout(900)
+def test_masked_tiled_fp8out_full_size_down():
+    """The masked decode down projection (32 experts, 128-row buffers, rows
+    U{1..64}, N = 7168, K = 2048): equal to the quantized FP32 output on every
+    valid row, and sampled rows of every expert valid against the oracle."""
+    G, M_max, N, K = 32, 128, 7168, 2048
+    mm, a = workloads.moe_masked_inputs(N, K, G, M_max)
+    qa, sa = zip(*[quant.quant_act_1x128(a[g]) for g in range(G)])
+    qa, sa = np.stack(qa), np.stack(sa)
+    del a
+    qs, ss = zip(*[quant.quant_weight_128x128(workloads.expert_weight("moe_down", g, N, K)) for g in range(G)])
+    qb, sb = np.stack(qs), np.stack(ss)
+    del qs, ss
+    args, q, s = _masked_tiled_fp8out(qa, sa, qb, sb, mm)
+    c = fp8.fp8_grouped_gemm_masked_tiled(*args, torch.float32)
+    rng = np.random.default_rng(65)
+    for g in range(G):
+        m = int(mm[g])
+        rq, rs = fp8.fp8_quant_act_1x128(c[g, :m].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(q[g, :m], rq), g
+        assert torch.equal(s[g][:, :m].contiguous().view(torch.int32), rs.view(torch.int32)), g
+        assert not bool(q[g, m:].any()) and not bool(s[g][:, m:].any()), g
+        rows = np.unique(np.concatenate([[0, m - 1], rng.integers(0, m, 3)]))
+        cr, s_abs = gemm.gemm_blockscaled_ref(qa[g], sa[g], qb[g], sb[g], rows=rows)
+        _check_valid(host(q[g])[rows], host(s[g])[:, rows], cr, s_abs, f"masked fp8out full g={g}")
