@@ -637,6 +637,14 @@ def run_extra(args):
                                                           out=s["c"]),
                  sets, dict(cfg, scales="E8M0 per 1x32 block", bytes="all expert weights + E8M0 scales + valid A "
                             "rows + scales + valid C rows"), nbytes=nbytes_mx)
+            for s in sets:
+                s["qbmt"] = fp8.fp8_tile_weights_decode(s["qbm"])
+            line("moe_masked", f"grouped_gemm_masked_tiled_mx N={N} K={K} (MX operands, decode-tiled weights)",
+                 lambda s: fp8.fp8_grouped_gemm_masked_tiled_mx(s["qam"], s["eam"], s["qbmt"], s["ebm"], s["mmt"],
+                                                                out=s["c"]),
+                 sets, dict(cfg, scales="E8M0 per 1x32 block", weights="decode-tiled layout",
+                            bytes="all expert weights + E8M0 scales + valid A rows + scales + valid C rows"),
+                 nbytes=nbytes_mx)
             del sets
 
 

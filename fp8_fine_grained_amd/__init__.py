@@ -22,16 +22,16 @@ BSCALE_1x128 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
 
-ABI_VERSION = 13
+ABI_VERSION = 14
 EXPORTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_gemm_blockscaled",
            "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked",
            "fp8_quant_act_1x128_bf16", "fp8_quant_weight_128x128_bf16", "fp8_requant_act_tokenwise",
            "fp8_quant_mx_1x32", "fp8_gemm_mx", "fp8_gemm_blockscaled_fp8out", "fp8_quant_fprop_operands",
            "fp8_tile_weights_decode", "fp8_grouped_gemm_masked_tiled", "fp8_gemm_blockscaled_fp8mfma",
            "fp8_grouped_gemm_contiguous_fp8out", "fp8_grouped_gemm_contiguous_mx", "fp8_grouped_gemm_masked_mx",
-           "fp8_quant_mx_1x32_transposed", "fp8_grouped_gemm_masked_tiled_fp8out", "fp8fg_status_string",
-           "fp8fg_abi_version")
-_COMPUTE = EXPORTS[:20]
+           "fp8_quant_mx_1x32_transposed", "fp8_grouped_gemm_masked_tiled_fp8out",
+           "fp8_grouped_gemm_masked_tiled_mx", "fp8fg_status_string", "fp8fg_abi_version")
+_COMPUTE = EXPORTS[:21]
 
 
 class Fp8fgError(RuntimeError):
@@ -71,6 +71,7 @@ def load_library(path=LIB_PATH):
     lib.fp8_grouped_gemm_masked_tiled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     lib.fp8_grouped_gemm_contiguous_fp8out.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp]
     lib.fp8_grouped_gemm_masked_tiled_fp8out.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp]
+    lib.fp8_grouped_gemm_masked_tiled_mx.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     lib.fp8_grouped_gemm_contiguous_mx.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     lib.fp8_grouped_gemm_masked_mx.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     for name in _COMPUTE:
@@ -389,6 +390,24 @@ def fp8_grouped_gemm_masked(a, sa, b, sb, masked_m, out_dtype=torch.bfloat16, ou
     _need(out, out_dtype, (G, M_max, N), "out")
     _check("fp8_grouped_gemm_masked", load_library().fp8_grouped_gemm_masked(
         _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(masked_m), G, M_max, N, K, _ptr(out),
+        _out_dtype(out_dtype), _stream(a)))
+    return out
+
+
+def fp8_grouped_gemm_masked_tiled_mx(a, ea, b_tiled, eb, masked_m, out_dtype=torch.bfloat16, out=None):
+    """fp8_grouped_gemm_masked_mx with the experts' codes in the decode-tiled
+    layout (b_tiled u8 [G][N/256][K/64][16384], from fp8_tile_weights_decode)."""
+    G, M_max, K = a.shape
+    N = b_tiled.shape[1] * 256
+    _need(a, torch.uint8, (G, M_max, K), "a")
+    _need(ea, torch.uint8, (G, K // 32, M_max), "ea")
+    _need(b_tiled, torch.uint8, (G, N // 256, K // 64, 16384), "b_tiled")
+    _need(eb, torch.uint8, (G, K // 32, N), "eb")
+    _need(masked_m, torch.int32, (G,), "masked_m")
+    out = _empty((G, M_max, N), out_dtype, a) if out is None else out
+    _need(out, out_dtype, (G, M_max, N), "out")
+    _check("fp8_grouped_gemm_masked_tiled_mx", load_library().fp8_grouped_gemm_masked_tiled_mx(
+        _ptr(a), _ptr(ea), _ptr(b_tiled), _ptr(eb), _ptr(masked_m), G, M_max, N, K, _ptr(out),
         _out_dtype(out_dtype), _stream(a)))
     return out
 

@@ -307,6 +307,27 @@ int fp8_tile_weights_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, u
     return hip_status(fp8fg::launch_tile_weights_decode(q, G, N, K, q_tiled, static_cast<hipStream_t>(stream)));
 }
 
+int fp8_grouped_gemm_masked_tiled_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b_tiled, const uint8_t* eb,
+                                     const int32_t* masked_m, int64_t G, int64_t M_max, int64_t N, int64_t K, void* c,
+                                     int out_dtype, void* stream) {
+    if (!a || !ea || !b_tiled || !eb || !masked_m || !c) return FP8FG_ERR_NULL;
+    if (G < 0 || M_max < 0 || N < 0 || K < 0 || M_max % 4 != 0 || N % 256 != 0 || K % 64 != 0) return FP8FG_ERR_SHAPE;
+    if (K == 0 && M_max > 0 && N > 0 && G > 0) return FP8FG_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(ea) || !aligned16(b_tiled) || !aligned16(eb) || !aligned16(c) ||
+        !aligned16(masked_m))
+        return FP8FG_ERR_ALIGN;
+    if (!valid_out(out_dtype)) return FP8FG_ERR_UNSUPPORTED;
+    if (M_max > 128 || N > kMaxDim || K >= (int64_t(1) << 24) || G > kMaxDim) return FP8FG_ERR_UNSUPPORTED;
+    if ((K / 32) * N > int64_t(0xFFFFFF00)) return FP8FG_ERR_UNSUPPORTED;
+    if (N > 0 && G > kMaxDim / (2 * (N / 256))) return FP8FG_ERR_UNSUPPORTED;
+    if (G * ((M_max + 63) / 64) > 4096) return FP8FG_ERR_UNSUPPORTED;
+    if (G == 0 || M_max == 0 || N == 0) return FP8FG_OK;
+    fp8fg::GemmArgs args{a, reinterpret_cast<const float*>(ea), b_tiled, reinterpret_cast<const float*>(eb), c,
+                         masked_m, M_max, N, K, G};
+    return hip_status(fp8fg::launch_gemm_masked_tiled(out_dtype == FP8FG_OUT_FP32, args,
+                                                      static_cast<hipStream_t>(stream), true));
+}
+
 int fp8_grouped_gemm_masked_tiled_fp8out(const uint8_t* a, const float* sa, const uint8_t* b_tiled, const float* sb,
                                          const int32_t* masked_m, int64_t G, int64_t M_max, int64_t N, int64_t K,
                                          uint8_t* q, float* s, void* stream) {

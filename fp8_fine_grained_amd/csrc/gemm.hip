@@ -2426,8 +2426,9 @@ __device__ __forceinline__ void dreg_rank_table(const GemmArgs& args, uint32_t* 
 // in the scalar offset).
 struct DregSrc {
     rsrc_t ra, rb, rsa, rsb;
-    uint32_t va, vb[4], vsa[2];
-    uint32_t sa_step;      // bytes between K-blocks of the A scales
+    uint32_t va, vb[4], vsa[2], vsb[2];
+    uint32_t sa_step;      // bytes between K-blocks of the A scales (MX: between 32-K blocks)
+    uint32_t sb_step;      // MX: bytes between 32-K blocks of the B scale bytes
     int64_t c_off;         // element offset of C at (row m0, column n0)
     int64_t s_off;         // FP8 output: offset of the scale of (row m0, 128-column group of n0)
     int rows;              // valid rows from m0, at most 64
@@ -2444,7 +2445,7 @@ struct DregA {
     static constexpr int COPIERS = 64 / ROWS;
 };
 
-template <int NW>
+template <int NW, bool MX = false>
 __device__ __forceinline__ DregSrc dreg_src(const GemmArgs& args, const uint32_t* tab, int64_t item, int64_t n_tiles,
                                             bool xgroup, int wave, int lane) {
     constexpr int BN = 64 * NW;                  // columns of an item
@@ -2485,6 +2486,27 @@ __device__ __forceinline__ DregSrc dreg_src(const GemmArgs& args, const uint32_t
 #pragma unroll
         for (int u = 0; u < 4; ++u) s.vb[u] = uint32_t(q * 4096 + u * 1024 + lane * 16);
     }
+    if constexpr (MX) {
+        // E8M0 bytes: A [G][K/32][M], B [G][K/32][N]; lane (r, h) loads the
+        // bytes of 32-K block 2 hb + h of its rows mi * 32 + r and of its
+        // columns ni * 32 + r (the scaled MFMA takes block h from lanes
+        // r + 32 h)
+        const int64_t k32 = K / 32;
+        const uint8_t* ea = reinterpret_cast<const uint8_t*>(args.sa);
+        const uint8_t* eb = reinterpret_cast<const uint8_t*>(args.sb);
+        s.rsa = make_rsrc(ea + g * k32 * M + m0, uint32_t((k32 - 1) * M + rows));
+        s.sa_step = uint32_t(M);
+        s.rsb = make_rsrc(eb + g * k32 * N, uint32_t(k32 * N));
+        s.sb_step = uint32_t(N);
+        const int h = lane >> 5;
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+            const int rr = mi * 32 + r;
+            s.vsa[mi] = uint32_t((rr < rows ? rr : rows - 1) + h * M);
+            s.vsb[mi] = uint32_t(bn * BN + 64 * wave + mi * 32 + r + h * N);
+        }
+        return s;
+    }
     s.rsa = make_rsrc(args.sa + g * kbs * M + m0, uint32_t(((kbs - 1) * M + rows) * 4));
     s.sa_step = uint32_t(M * 4);
 #pragma unroll
@@ -2502,26 +2524,56 @@ __device__ __forceinline__ DregSrc dreg_src(const GemmArgs& args, const uint32_t
 // groups, and the compiler's own waits on the ring registers are only as
 // tight as the order it sees -- so the scheduler may not move loads across
 // a group's ends.
-template <int NP, int NW, int POS>
+// The scales in flight: FP32 scales of each K-block (loaded with its first
+// half), or (MX) the E8M0 bytes of every half-block's two 32-K blocks.
+template <int NP, bool MX>
+struct DregScales {
+    float qa[NP / 2][2], qb[NP / 2];
+};
+template <int NP>
+struct DregScales<NP, true> {
+    uint32_t ea[NP][2], eb[NP][2];
+    v8i b8[NP][2];   // MX: the B ring itself, both K steps of tile ni as one operand
+};
+
+template <int NP, int NW, int POS, bool MX>
 __device__ __forceinline__ void dreg_issue(const DregSrc& s, int hb, uint8_t* lds, int wave, int lane,
-                                           u32x4 (&bq)[NP][4], float (&qa)[NP / 2][2], float (&qb)[NP / 2]) {
+                                           u32x4 (&bq)[NP][4], DregScales<NP, MX>& sc) {
     constexpr int A_BYTES = DregA<NW>::ROWS * 64;   // a copying wave's share of the A half-block
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MX) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-        bq[POS][t] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, s.vb[t], uint32_t(hb) * 16384u, kNonTemporal);
+        for (int ni = 0; ni < 2; ++ni) {
+            const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(s.rb, s.vb[2 * ni], uint32_t(hb) * 16384u,
+                                                                   kNonTemporal);
+            const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(s.rb, s.vb[2 * ni + 1], uint32_t(hb) * 16384u,
+                                                                   kNonTemporal);
+            sc.b8[POS][ni] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            bq[POS][t] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, s.vb[t], uint32_t(hb) * 16384u, kNonTemporal);
+    }
     // (eight waves: the upper half-wave's lanes are off, so the copy is 512
     // bytes; waves past the copiers load nothing into the dummy line)
     uint8_t* dst = wave < DregA<NW>::COPIERS ? lds + POS * 4096 + wave * A_BYTES : lds + NP * 4096 + 64;
     if (DregA<NW>::ROWS == 16 || lane < 32)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ra, (lds_ptr_t)dst, 16, s.va, uint32_t(hb) * 64u, 0, 0);
-    if constexpr (POS % 2 == 0) {
+    if constexpr (MX) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+            sc.ea[POS][mi] = __builtin_amdgcn_raw_buffer_load_b8(s.rsa, s.vsa[mi], uint32_t(2 * hb) * s.sa_step, 0);
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+            sc.eb[POS][ni] = __builtin_amdgcn_raw_buffer_load_b8(s.rsb, s.vsb[ni], uint32_t(2 * hb) * s.sb_step, 0);
+    } else if constexpr (POS % 2 == 0) {
         const uint32_t kb = uint32_t(hb >> 1);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
-            qa[POS / 2][mi] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s.rsa, s.vsa[mi],
-                                                                                           kb * s.sa_step, 0));
-        qb[POS / 2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s.rsb, 0u, kb * 4u, 0));
+            sc.qa[POS / 2][mi] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s.rsa, s.vsa[mi],
+                                                                                              kb * s.sa_step, 0));
+        sc.qb[POS / 2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s.rsb, 0u, kb * 4u, 0));
     }
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -2532,11 +2584,12 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 }
 
 // loads per half-block: 4 B fragments + 1 A piece, + 3 scales on even ones
-constexpr int dreg_loads(int q) { return 5 + (q % 2 == 0 ? 3 : 0); }
+// (MX: + 4 scale bytes on every one)
+constexpr int dreg_loads(int q, bool mx) { return mx ? 9 : 5 + (q % 2 == 0 ? 3 : 0); }
 // loads issued for the `ahead` half-blocks after one at ring position p
-constexpr int dreg_later(int p, int ahead) {
+constexpr int dreg_later(int p, int ahead, bool mx) {
     int n = 0;
-    for (int d = 1; d <= ahead; ++d) n += dreg_loads(p + d);
+    for (int d = 1; d <= ahead; ++d) n += dreg_loads(p + d, mx);
     return n;
 }
 
@@ -2613,18 +2666,58 @@ __device__ __forceinline__ void dreg_store(const GemmArgs& args, const DregSrc& 
 // One half-block at ring position P of the compute item: scales (first half
 // of a K-block), then the two K steps of 32 from the A slot and the B
 // registers.  `partial`: the K-block runs past K; fragments past K read as 0.
-template <int NP, int P>
-__device__ __forceinline__ void dreg_compute(const uint8_t* lds, int hb, int64_t K, bool partial, int r, int h, const u32x4 (&bq)[NP][4], const float (&qa)[NP / 2][2],
-                                             const float (&qb)[NP / 2], WideScales<2>& w, v16f (&acc)[2][2]) {
+// MX: one scaled FP8 MFMA per 32 x 32 tile and half-block on the codes
+// themselves (A chunks h and 2 + h, the two B pieces of the K steps), with
+// the lane's scale bytes; no unit, no rescale.
+template <int NP, int P, bool MX>
+__device__ __forceinline__ void dreg_compute(const uint8_t* lds, int hb, int64_t K, bool partial, int r, int h,
+                                             const u32x4 (&bq)[NP][4], const DregScales<NP, MX>& sc, WideScales<2>& w,
+                                             v16f (&acc)[2][2]) {
     constexpr uint32_t kZero = NP * 4096;
-    if constexpr (P % 2 == 0) {
+    if constexpr (MX) {
+        // K % 64 == 0: a half-block lies wholly inside K or wholly past it;
+        // one past K contributes nothing (uniform branch)
+        if (partial && int64_t(hb) * 64 >= K) return;
+        const uint32_t base = lds_addr(lds) + uint32_t(P) * 4096u;
+        uint32_t ad[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t chunk = uint32_t(((2 * j + h) ^ ((r >> 2) & 3)) << 4);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) ad[j][mi] = base + uint32_t((mi * 32 + r) * 64) + chunk;
+        }
+        u32x4 fa[2][2];
+        asm volatile(   // as below: waits for these reads only
+            "ds_read_b128 %0, %4\n\t"
+            "ds_read_b128 %1, %5\n\t"
+            "ds_read_b128 %2, %6\n\t"
+            "ds_read_b128 %3, %7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(fa[0][0]), "=&v"(fa[0][1]), "=&v"(fa[1][0]), "=&v"(fa[1][1])
+            : "v"(ad[0][0]), "v"(ad[0][1]), "v"(ad[1][0]), "v"(ad[1][1])
+            : "memory");
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+            const v8i b8 = sc.b8[P][ni];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) {
+                const v8i a8 = v8i{int(fa[0][mi][0]), int(fa[0][mi][1]), int(fa[0][mi][2]), int(fa[0][mi][3]),
+                                   int(fa[1][mi][0]), int(fa[1][mi][1]), int(fa[1][mi][2]), int(fa[1][mi][3])};
+                // formats 0/0 = E4M3 x E4M3; B is the instruction's first operand
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    b8, a8, acc[mi][ni], 0, 0, 0, int(sc.eb[P][ni]), 0, int(sc.ea[P][mi]));
+            }
+        }
+        return;
+    }
+    if constexpr (!MX && P % 2 == 0) {
         WideScales<2> nw;
-        const float sb = qb[P / 2];
+        const float sb = sc.qb[P / 2];
         const ScaleSplit b = split_scale(sb);
         nw.pb = b.pow2;
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
-            const float sa = qa[P / 2][mi];
+            const float sa = sc.qa[P / 2][mi];
             const ScaleSplit a = split_scale(sa);
             nw.pa[mi] = a.pow2;
             nw.unit[mi] = clamp_unit(a.mant * b.mant);
@@ -2689,7 +2782,7 @@ __device__ __forceinline__ void dreg_reset(v16f (&acc)[2][2], WideScales<2>& w) 
     w.pb = 1.0f;
 }
 
-template <int OUT, int NP, int NW>
+template <int OUT, int NP, int NW, bool MX>
 __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
     static_assert(NP % 2 == 0 && NP >= 2 && NP <= 8, "whole K-blocks per ring turn");
     static_assert(NW == 4 || NW == 7 || NW == 8, "items of 256, 448 or 512 columns");
@@ -2715,21 +2808,21 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
 
     if (tid < 4) st<u32x4>(lds + NP * 4096 + tid * 16, u32x4{0u, 0u, 0u, 0u});   // the zero line
     u32x4 bq[NP][4];
-    float qa[NP / 2][2], qb[NP / 2];
+    DregScales<NP, MX> sc;
     // issue side: item of the next half-block to load; compute side: item being multiplied
     int64_t item_k = 0;
-    DregSrc is = dreg_src<NW>(args, tab, b0, n_tiles, xgroup, wave, lane);
+    DregSrc is = dreg_src<NW, MX>(args, tab, b0, n_tiles, xgroup, wave, lane);
     DregSrc cs = is;
     // the first NP - 1 half-blocks (F >= halves >= NP, all of the first item)
 #pragma unroll
     for (int q = 0; q < NP - 1; ++q) {
-        if (q == 0) dreg_issue<NP, NW, 0>(is, 0, lds, wave, lane, bq, qa, qb);
-        if (q == 1) dreg_issue<NP, NW, 1 % NP>(is, 1, lds, wave, lane, bq, qa, qb);
-        if (q == 2) dreg_issue<NP, NW, 2 % NP>(is, 2, lds, wave, lane, bq, qa, qb);
-        if (q == 3) dreg_issue<NP, NW, 3 % NP>(is, 3, lds, wave, lane, bq, qa, qb);
-        if (q == 4) dreg_issue<NP, NW, 4 % NP>(is, 4, lds, wave, lane, bq, qa, qb);
-        if (q == 5) dreg_issue<NP, NW, 5 % NP>(is, 5, lds, wave, lane, bq, qa, qb);
-        if (q == 6) dreg_issue<NP, NW, 6 % NP>(is, 6, lds, wave, lane, bq, qa, qb);
+        if (q == 0) dreg_issue<NP, NW, 0, MX>(is, 0, lds, wave, lane, bq, sc);
+        if (q == 1) dreg_issue<NP, NW, 1 % NP, MX>(is, 1, lds, wave, lane, bq, sc);
+        if (q == 2) dreg_issue<NP, NW, 2 % NP, MX>(is, 2, lds, wave, lane, bq, sc);
+        if (q == 3) dreg_issue<NP, NW, 3 % NP, MX>(is, 3, lds, wave, lane, bq, sc);
+        if (q == 4) dreg_issue<NP, NW, 4 % NP, MX>(is, 4, lds, wave, lane, bq, sc);
+        if (q == 5) dreg_issue<NP, NW, 5 % NP, MX>(is, 5, lds, wave, lane, bq, sc);
+        if (q == 6) dreg_issue<NP, NW, 6 % NP, MX>(is, 6, lds, wave, lane, bq, sc);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the zero line is written before the first barrier
 
@@ -2743,7 +2836,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
         const bool partial = (hb0 + NP) * 64 > K;        // this turn holds the K-block that runs past K
 #define FP8FG_DREG_STEP(PP)                                                                                       \
         if constexpr ((PP) < NP) {                                                                                \
-            constexpr int later = dreg_later((PP), NP - 2);                                                       \
+            constexpr int later = dreg_later((PP), NP - 2, MX);                                                   \
             wait_vmcnt<later>();                                                                                  \
             const int hbc = hb0 + (PP);                                                                           \
             if (partial && (hbc + 1) * 64 > K) {   /* this wave's A chunks past K read as 0 */                    \
@@ -2761,7 +2854,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
             if ((PP) == 1 && item_ends) {                                                                         \
                 if (f + NP < F) {   /* the issue side moves to the next item */                                   \
                     ++item_k;                                                                                     \
-                    is = dreg_src<NW>(args, tab, b0 + item_k * P, n_tiles, xgroup, wave, lane);                   \
+                    is = dreg_src<NW, MX>(args, tab, b0 + item_k * P, n_tiles, xgroup, wave, lane);               \
                 } else {                                                                                          \
                     is.ra = make_rsrc(args.a, 0u);                                                                \
                     is.rb = make_rsrc(args.b, 0u);                                                                \
@@ -2770,9 +2863,9 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
                 }                                                                                                 \
             }                                                                                                     \
             /* half-block hb0 + PP + NP - 1 of the compute item, or PP - 1 of the next one */                   \
-            dreg_issue<NP, NW, ((PP) + NP - 1) % NP>(is, item_ends && (PP) >= 1 ? (PP) - 1 : hb0 + (PP) + NP - 1, \
-                                                     lds, wave, lane, bq, qa, qb);                                \
-            dreg_compute<NP, (PP)>(lds, hbc, K, partial, r, h, bq, qa, qb, w, acc);                        \
+            dreg_issue<NP, NW, ((PP) + NP - 1) % NP, MX>(is, item_ends && (PP) >= 1 ? (PP) - 1 : hb0 + (PP) + NP - 1, \
+                                                         lds, wave, lane, bq, sc);                            \
+            dreg_compute<NP, (PP), MX>(lds, hbc, K, partial, r, h, bq, sc, w, acc);                        \
         }
         FP8FG_DREG_STEP(0)
         FP8FG_DREG_STEP(1)
@@ -2793,9 +2886,11 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_dreg(GemmArgs args) {
 }
 
 #define FP8FG_DREG_KERNELS(X) \
-    X(0, 4, 4) X(0, 2, 4) X(1, 4, 4) X(1, 2, 4) X(0, 4, 8) X(0, 2, 8) X(1, 4, 8) X(1, 2, 8) \
-    X(0, 4, 7) X(0, 2, 7) X(1, 4, 7) X(1, 2, 7) X(2, 4, 4) X(2, 2, 4) X(2, 4, 8) X(2, 2, 8)
-#define FP8FG_DREG_INST(OUT, NP, NW) template __global__ void gemm_dreg<OUT, NP, NW>(GemmArgs);
+    X(0, 4, 4, 0) X(0, 2, 4, 0) X(1, 4, 4, 0) X(1, 2, 4, 0) X(0, 4, 8, 0) X(0, 2, 8, 0) X(1, 4, 8, 0) X(1, 2, 8, 0) \
+    X(0, 4, 7, 0) X(0, 2, 7, 0) X(1, 4, 7, 0) X(1, 2, 7, 0) X(2, 4, 4, 0) X(2, 2, 4, 0) X(2, 4, 8, 0) X(2, 2, 8, 0) \
+    X(0, 4, 4, 1) X(0, 2, 4, 1) X(1, 4, 4, 1) X(1, 2, 4, 1) X(0, 4, 8, 1) X(0, 2, 8, 1) X(1, 4, 8, 1) X(1, 2, 8, 1) \
+    X(0, 4, 7, 1) X(0, 2, 7, 1) X(1, 4, 7, 1) X(1, 2, 7, 1)
+#define FP8FG_DREG_INST(OUT, NP, NW, MX) template __global__ void gemm_dreg<OUT, NP, NW, MX>(GemmArgs);
 FP8FG_DREG_KERNELS(FP8FG_DREG_INST)
 #undef FP8FG_DREG_INST
 
@@ -2891,7 +2986,7 @@ DregGrid dreg_grid(const GemmArgs& args, int cus, bool pairs) {
     return best;
 }
 
-hipError_t launch_dreg(int out_fp32, const GemmArgs& args, hipStream_t stream) {
+hipError_t launch_dreg(int out_fp32, bool mx, const GemmArgs& args, hipStream_t stream) {
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -2904,8 +2999,8 @@ hipError_t launch_dreg(int out_fp32, const GemmArgs& args, hipStream_t stream) {
     const int64_t halves = 2 * ((args.K + BK - 1) / BK);
     const int np = halves % 4 == 0 ? 4 : 2;
     void (*k)(GemmArgs) = nullptr;
-#define FP8FG_DREG_PICK(OUT, NP, NW) \
-    if (out_fp32 == OUT && np == NP && nw == NW) k = gemm_dreg<OUT, NP, NW>;
+#define FP8FG_DREG_PICK(OUT, NP, NW, MX) \
+    if (out_fp32 == OUT && np == NP && nw == NW && mx == bool(MX)) k = gemm_dreg<OUT, NP, NW, MX>;
     FP8FG_DREG_KERNELS(FP8FG_DREG_PICK)
 #undef FP8FG_DREG_PICK
     if (!k) return hipErrorInvalidValue;
@@ -2971,8 +3066,8 @@ hipError_t launch_mx(int out_fp32, GemmMode mode, const GemmArgs& args, hipStrea
     return launch_kernel(k, dim3(unsigned(tiles)), dim3(MxTile::THREADS), stream, a);
 }
 
-hipError_t launch_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream) {
-    return launch_dreg(out_fp32, args, stream);
+hipError_t launch_masked_tiled(int out_fp32, bool mx, const GemmArgs& args, hipStream_t stream) {
+    return launch_dreg(out_fp32, mx, args, stream);
 }
 
 hipError_t launch_tile_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, uint8_t* out, hipStream_t stream) {
@@ -2985,8 +3080,8 @@ hipError_t launch_tile_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K,
 
 }  // namespace gemm_detail
 
-hipError_t launch_gemm_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream) {
-    return gemm_detail::launch_masked_tiled(out_fp32, args, stream);
+hipError_t launch_gemm_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream, bool mx) {
+    return gemm_detail::launch_masked_tiled(out_fp32, mx, args, stream);
 }
 
 hipError_t launch_tile_weights_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, uint8_t* out,

@@ -58,8 +58,9 @@ hipError_t launch_gemm_mx(int out_fp32, GemmMode mode, const GemmArgs& args, hip
 hipError_t launch_gemm(int engine, GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                        hipStream_t stream);
 // the masked layout on decode-tiled B (M <= 128, N % 256 == 0, K % 64 == 0);
-// out_fp32 2: FP8 codes to args.c with their 1x128 scales to args.cs
-hipError_t launch_gemm_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream);
+// out_fp32 2: FP8 codes to args.c with their 1x128 scales to args.cs;
+// mx: MX operands (args.sa / args.sb carry E8M0 bytes [G][K/32][M], [G][K/32][N])
+hipError_t launch_gemm_masked_tiled(int out_fp32, const GemmArgs& args, hipStream_t stream, bool mx = false);
 // [G][N][K] codes -> the decode-tiled layout (N % 256 == 0, K % 64 == 0)
 hipError_t launch_tile_weights_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, uint8_t* out,
                                       hipStream_t stream);

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 13
+#define FP8FG_ABI_VERSION 14
 
 enum fp8fg_status {
     FP8FG_OK = 0,
@@ -365,6 +365,23 @@ int fp8_tile_weights_decode(const uint8_t* q, int64_t G, int64_t N, int64_t K, u
 int fp8_grouped_gemm_masked_tiled(const uint8_t* a, const float* sa, const uint8_t* b_tiled, const float* sb,
                                   const int32_t* masked_m, int64_t G, int64_t M_max,
                                   int64_t N, int64_t K, void* c, int out_dtype, void* stream);
+
+/*
+ * fp8_grouped_gemm_masked_mx on decode-tiled weights: the same operation,
+ * arguments and result bit for bit (each expert's valid rows as
+ * fp8_gemm_mx gives them), with the experts' codes in the layout written by
+ * fp8_tile_weights_decode (which the scaled FP8 MFMA reads as it stands: a
+ * lane's two 16-byte pieces of a 64-K step are one operand).
+ * a u8 [G][M_max][K], ea u8 [G][K/32][M_max], b_tiled (decode-tiled [G][N][K]
+ * codes), eb u8 [G][K/32][N], masked_m DEVICE int32 [G] (clamped to
+ * [0, M_max]); c [G][M_max][N] BF16 or FP32, rows past masked_m[g] NOT
+ * written.  Requires M_max <= 128, M_max % 4 == 0, N % 256 == 0, K % 64 == 0,
+ * K > 0 when there is work, K < 2^24, (K / 32) * N < 2^32,
+ * G * ceil(M_max / 64) <= 4096 (FP8FG_ERR_UNSUPPORTED beyond).
+ */
+int fp8_grouped_gemm_masked_tiled_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b_tiled, const uint8_t* eb,
+                                     const int32_t* masked_m, int64_t G, int64_t M_max,
+                                     int64_t N, int64_t K, void* c, int out_dtype, void* stream);
 
 /*
  * fp8_grouped_gemm_masked_tiled with the next layer's quantization fused into

@@ -224,6 +224,17 @@ def test_decode_tiled_argument_errors():
     assert m(P, P, P, P, P, 4, 129, 256, 128, P, 0, NUL) == EUNSUP   # M_max > 128
     assert m(P, P, P, P, P, 0, 128, 256, 128, P, 0, NUL) == OK       # G = 0
     assert m(P, P, P, P, P, 4, 0, 256, 128, P, 0, NUL) == OK         # M_max = 0
+    x = lib.fp8_grouped_gemm_masked_tiled_mx
+    assert x(P, P, P, NUL, P, 4, 128, 256, 128, P, 0, NUL) == ENULL
+    assert x(P, P, P, P, P, 4, 126, 256, 128, P, 0, NUL) == ESHAPE    # M_max % 4
+    assert x(P, P, P, P, P, 4, 128, 128, 128, P, 0, NUL) == ESHAPE    # N % 256
+    assert x(P, P, P, P, P, 4, 128, 256, 96, P, 0, NUL) == ESHAPE     # K % 64
+    assert x(P, P, P, P, P, 4, 128, 256, 0, P, 0, NUL) == ESHAPE      # K = 0 with work to do
+    assert x(P, MIS, P, P, P, 4, 128, 256, 128, P, 0, NUL) == EALIGN
+    assert x(P, P, P, P, P, 4, 128, 256, 128, P, 2, NUL) == EUNSUP    # output dtype
+    assert x(P, P, P, P, P, 4, 132, 256, 128, P, 0, NUL) == EUNSUP    # M_max > 128
+    assert x(P, P, P, P, P, 4097, 64, 256, 128, P, 0, NUL) == EUNSUP  # 4097 (expert, 64-row) pairs
+    assert x(P, P, P, P, P, 0, 128, 256, 128, P, 0, NUL) == OK        # G = 0
     f = lib.fp8_grouped_gemm_masked_tiled_fp8out
     #        a  sa  b  sb  mm  G  M_max N    K    q  s
     assert f(P, P, P, P, P, 4, 128, 256, 128, P, NUL, NUL) == ENULL

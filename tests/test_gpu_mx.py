@@ -269,3 +269,63 @@ def test_mx_wgrad_full_size():
     torch.cuda.synchronize()
     cg = c[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
     _check(cg, mx.dequant_mx(qdt, edt)[rows], mx.dequant_mx(qxt, ext), "fp32", "mx wgrad full size")
+
+
+# The MX masked GEMM on decode-tiled weights: the persistent register-stream
+# kernel, bit for bit the plain-weight MX call.
+
+@pytest.mark.parametrize("G,M_max,N,K,out", [(8, 128, 512, 384, "bf16"), (5, 64, 768, 320, "fp32"),
+                                             (4, 100, 256, 64, "bf16"), (8, 96, 1024, 1152, "fp32"),
+                                             (8, 128, 1792, 448, "bf16"), (4, 128, 3584, 192, "fp32")])
+def test_mx_masked_tiled_equals_plain(G, M_max, N, K, out):
+    """Ragged valid counts (M_max, 0, 1, 33, ...), K with a half K-block past
+    the last whole one, items of 256, 448 and 512 columns; rows past masked_m
+    keep their sentinel; the valid rows are within the MX bound of the oracle."""
+    from oracle import layout
+    if M_max % 4:
+        M_max += 4 - M_max % 4
+    rng = np.random.default_rng(G * 100 + M_max + N + K + 7)
+    mm = rng.integers(0, M_max + 1, G).astype(np.int32)
+    mm[:4] = [M_max, 0, 1, 33]
+    qa, ea = zip(*[mx.quant_mx_1x32(workloads.activations(rng, M_max, K, 0.01, 50.0)) for _ in range(G)])
+    qa, ea = np.stack(qa), np.stack(ea)
+    qb, eb = _mx_experts(rng, G, N, K)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    args = [dev(qa), dev(ea)]
+    c_t = torch.full((G, M_max, N), -9.0, dtype=od, device=DEV)
+    fp8.fp8_grouped_gemm_masked_tiled_mx(*args, dev(layout.tile_weights_decode(qb)), dev(eb), dev(mm), od, out=c_t)
+    c_p = torch.full((G, M_max, N), -9.0, dtype=od, device=DEV)
+    fp8.fp8_grouped_gemm_masked_mx(*args, dev(qb), dev(eb), dev(mm), od, out=c_p)
+    torch.cuda.synchronize()
+    assert torch.equal(c_t.view(torch.int16 if out == "bf16" else torch.int32),
+                       c_p.view(torch.int16 if out == "bf16" else torch.int32)), "the tiled layout changed the result"
+    ch = c_t.float().cpu().numpy().astype(np.float64)
+    for g in range(G):
+        m = int(mm[g])
+        assert np.all(ch[g, m:] == -9.0), g
+        if m:
+            _check(ch[g, :m], mx.dequant_mx(qa[g], ea[g])[:m], mx.dequant_mx(qb[g], eb[g]), out, f"mx tiled g={g}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("N,K", [(4096, 7168), (7168, 2048)])
+def test_mx_masked_tiled_full_size_equals_plain(N, K):
+    """The masked decode shapes (32 experts, 128-row buffers, rows U{1..64}),
+    MX-quantized and tiled by the GPU: the same bits as the plain-weight MX
+    call (whose oracle parity at this size is test_mx_masked_decode_full_size)."""
+    G, M_max = 32, 128
+    g = torch.Generator(device=DEV).manual_seed(N + 5 * K)
+    qa = torch.empty((G, M_max, K), dtype=torch.uint8, device=DEV)
+    ea = torch.empty((G, K // 32, M_max), dtype=torch.uint8, device=DEV)
+    qb = torch.empty((G, N, K), dtype=torch.uint8, device=DEV)
+    eb = torch.empty((G, K // 32, N), dtype=torch.uint8, device=DEV)
+    for e in range(G):
+        fp8.fp8_quant_mx_1x32(torch.randn((M_max, K), generator=g, device=DEV), q=qa[e], e=ea[e])
+        fp8.fp8_quant_mx_1x32(torch.randn((N, K), generator=g, device=DEV) * 0.02, q=qb[e], e=eb[e])
+    mm = torch.randint(1, 65, (G,), generator=g, device=DEV, dtype=torch.int32)
+    c_t = torch.full((G, M_max, N), 5.0, dtype=torch.bfloat16, device=DEV)
+    fp8.fp8_grouped_gemm_masked_tiled_mx(qa, ea, fp8.fp8_tile_weights_decode(qb), eb, mm, out=c_t)
+    c_p = torch.full((G, M_max, N), 5.0, dtype=torch.bfloat16, device=DEV)
+    fp8.fp8_grouped_gemm_masked_mx(qa, ea, qb, eb, mm, out=c_p)
+    torch.cuda.synchronize()
+    assert torch.equal(c_t.view(torch.int16), c_p.view(torch.int16))
