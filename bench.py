@@ -55,12 +55,12 @@ def parse():
                    help="seconds of untimed steps before the warmup steps (clock settling)")
     p.add_argument("--profile-kernel", choices=["gemm", "quant_act", "quant_weight", "quant_fprop", "copy", "masked",
                                                 "masked_tiled", "masked_down", "masked_down_tiled", "trio_fprop",
-                                                "trio_dgrad", "trio_wgrad", "contig"],
+                                                "trio_dgrad", "trio_wgrad", "contig", "mx"],
                    help="counter-collection driver: launch only this kernel `steps` times (gemm, quant_*: on "
                         "the dense_fprop inputs; copy: a 1 GiB device-to-device copy, the byte-counter "
                         "calibration; masked*: the masked decode GEMM, gate+up or down shape, on plain / "
                         "decode-tiled weights; trio_*: the linear_trio GEMMs; contig: the moe_contig "
-                        "gate+up GEMM); prints no JSON")
+                        "gate+up GEMM; mx: the MX GEMM on the dense_fprop shape); prints no JSON")
     p.add_argument("--workload", default="dense_fprop",
                    choices=["dense_fprop", "dense_small", "linear_trio", "moe_contig", "moe_masked", "dense_mx"],
                    help="dense_fprop is the headline step; the others print one line per measured kernel")
@@ -342,6 +342,14 @@ def profile_other(args):
             fn = lambda: fp8.fp8_gemm_blockscaled(qdt, sdt, qxt, sxt, 1, torch.float32, out=c)
         del x, w, dy
         what = "8192 tokens, 7168 in, 2048 out"
+    elif k == "mx":
+        gen = torch.Generator(device="cuda").manual_seed(workloads.SEEDS.get("dense_mx", 1))
+        M, N, K = 4096, 7168, 2048
+        qa, ea = fp8.fp8_quant_mx_1x32(gpu_acts(gen, M, K, 0.001, 100.0))
+        qb, eb = fp8.fp8_quant_mx_1x32(torch.randn((N, K), generator=gen, device="cuda") * 0.02)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: fp8.fp8_gemm_mx(qa, ea, qb, eb, torch.bfloat16, out=c)
+        what = f"{M}x{N}x{K}"
     else:
         gen = torch.Generator(device="cuda").manual_seed(workloads.SEEDS.get("moe_contig", 1))
         a, qa, sa, qb, sb, offs, counts, mt = contig_inputs(gen)
@@ -654,7 +662,8 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
         sys.exit(2)
     _SETTLE["seconds"] = args.settle_s
-    if args.profile_kernel and (args.profile_kernel.startswith(("masked", "trio_")) or args.profile_kernel == "contig"):
+    if args.profile_kernel and (args.profile_kernel.startswith(("masked", "trio_")) or
+                                args.profile_kernel in ("contig", "mx")):
         profile_other(args)
         return
     if args.workload != "dense_fprop":
