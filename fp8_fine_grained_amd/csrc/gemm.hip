@@ -34,11 +34,13 @@
 //                 the promotion is folded into the MFMA accumulator (below).
 //   gemm_dreg_*   persistent decode kernel on weights in the decode-tiled
 //                 layout (written by tile_weights_decode): register-streamed
-//                 weight fragments, the wide kernel's arithmetic.
+//                 weight fragments, the wide kernel's arithmetic; also with
+//                 the fused FP8 output and with MX operands.
 //   gemm_big_* / gemm_dec_*   the fold kernels described next: 1x128-scaled
 //                 B (Wgrad), the fp8mfma engine, N = 128 mod 256, and K
 //                 beyond the wide kernel's limit.
-//   gemm_mx_*     the MX variant (E8M0 scales applied inside the MFMA).
+//   gemm_mx_*     the MX variant (E8M0 scales applied inside the MFMA), dense,
+//                 contiguous and masked.
 //
 // Fold kernels.  A 512-thread workgroup computes a
 // 256 (m) x 128 (n) tile of C; each of its eight waves (two per SIMD) owns a

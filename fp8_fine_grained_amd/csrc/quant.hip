@@ -14,7 +14,7 @@
 // transposed output (quant_act_tokens_*), 128x128 weights (quant_weight_*),
 // both Fprop operands in one launch (quant_fprop_*), the FP8 activation cache
 // to the token-wise layout (requant_act_tokens) and the MX variant
-// (quant_mx_rows).  All are HBM-bound: 4 bytes (fp32 input) or 2 bytes (bf16
+// (quant_mx_rows; quant_mx_tokens, blocks along M with transposed output).  All are HBM-bound: 4 bytes (fp32 input) or 2 bytes (bf16
 // input, widened exactly) read and 1 byte written per element, plus 4 bytes of
 // scale per group.
 #include "device_common.hpp"
