@@ -2073,11 +2073,25 @@ struct alignas(16) MxStage {
     uint8_t dummy[256];
 };
 
+// The same ring on block-scaled operands (the FP8-MFMA engine of
+// fp8_gemm_blockscaled_fp8mfma): each stage carries its K-block's FP32 A
+// scales (256 rows) and the two 128-column B scales instead of E8M0 bytes.
+struct alignas(16) MxbsStage {
+    uint8_t a[MxTile::BM * MxTile::KS];
+    uint8_t b[MxTile::BN * MxTile::KS];
+    float sa[MxTile::BM];
+    float sb[64];                  // lanes 0, 1 of one load: n-blocks 2 bn, 2 bn + 1
+    uint8_t dummy[256];
+};
+
 struct MxCopier {
     rsrc_t ra, rb, rs;
     uint32_t va[2], vb[2], vs, s_base, s_step;
     int a_lds[2], b_lds[2], s_lds;
 
+    // BS: the scale run of stage st is that of K-block st / 2 (two 64-K
+    // stages per block); MX: of the 32-K blocks 2 st and 2 st + 1
+    template <bool BS = false>
     __device__ __forceinline__ void copy(uint8_t* stage, int st) const {
         const uint32_t koff = uint32_t(st) * MxTile::KS;
 #pragma unroll
@@ -2087,7 +2101,7 @@ struct MxCopier {
         for (int i = 0; i < 2; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + b_lds[i]), 16, vb[i], koff, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + s_lds), 4, vs,
-                                                 s_base + uint32_t(2 * st) * s_step, 0, 0);
+                                                 s_base + uint32_t(BS ? st >> 1 : 2 * st) * s_step, 0, 0);
     }
 };
 
@@ -2096,7 +2110,7 @@ struct MxCopier {
 // Grouped layouts: expert g's B codes (t.B) and scale bytes [K/32][N] follow
 // one another; in the masked layout so do its A rows (t.A) and A scale bytes
 // [K/32][M_max], while the contiguous layout's A rows and scales are shared.
-template <int MODE>
+template <int MODE, bool BS = false>
 __device__ __forceinline__ MxCopier make_mx_copier(const GemmArgs& args, const Tile& t, int wave, int lane,
                                                    int64_t n0) {
     typedef MxTile W;
@@ -2115,6 +2129,27 @@ __device__ __forceinline__ MxCopier make_mx_copier(const GemmArgs& args, const T
         c.vb[i] = uint32_t(int64_t(r) * K + chunk * 16);
         c.a_lds[i] = int(offsetof(MxStage, a)) + r0 * W::KS;
         c.b_lds[i] = int(offsetof(MxStage, b)) + r0 * W::KS;
+    }
+    if constexpr (BS) {   // dense: waves 0-3 the A scales of rows 64 w .., wave 4 the two B scales
+        const int64_t kbs = (K + 127) / 128;
+        if (wave < 4) {
+            c.rs = make_rsrc(args.sa, uint32_t(kbs * M * 4));
+            c.vs = uint32_t((t.m0 + 64 * wave + lane) * 4);
+            c.s_step = uint32_t(M * 4);
+            c.s_lds = int(offsetof(MxbsStage, sa)) + wave * 256;
+        } else if (wave == 4) {
+            c.rs = make_rsrc(args.sb, uint32_t((N / 128) * kbs * 4));
+            c.vs = uint32_t(((n0 / 128) + (lane < 2 ? lane : 0)) * kbs * 4);
+            c.s_step = 4u;
+            c.s_lds = int(offsetof(MxbsStage, sb));
+        } else {
+            c.rs = make_rsrc(args.sa, uint32_t(kbs * M * 4));
+            c.vs = uint32_t((t.m0 + lane) * 4);
+            c.s_step = uint32_t(M * 4);
+            c.s_lds = int(offsetof(MxbsStage, dummy));
+        }
+        c.s_base = 0;
+        return c;
     }
     const int64_t kblocks = K / 32;
     const uint8_t* ea = reinterpret_cast<const uint8_t*>(args.sa) + (MODE == int(GemmMode::Masked) ? t.g * kblocks * M : 0);
@@ -2141,12 +2176,23 @@ __device__ __forceinline__ MxCopier make_mx_copier(const GemmArgs& args, const T
     return c;
 }
 
-template <int OUT_FP32, int MODE>
+// BS: block-scaled operands (1x128 A, 128x128 B, FP32 scales) on the FP8
+// MFMA, the FP8-MFMA engine.  As in the exact wide kernel, each scale splits
+// into a power of two and a mantissa part: the powers of two go to the
+// instruction as E8M0 scale bytes, and the accumulator is kept in the unit of
+// the mantissa parts' product, moved to the next K-block's unit at every
+// K-block (the promotion folded into the accumulator).  Rows whose A scale
+// (or whose B scale) is 0 read a zero line.
+template <int OUT_FP32, int MODE, bool BS = false>
 __device__ __forceinline__ void gemm_mx_body(const GemmArgs& args) {
     typedef MxTile W;
+    typedef typename std::conditional<BS, MxbsStage, MxStage>::type Stage;
+    static_assert(offsetof(MxbsStage, a) == offsetof(MxStage, a) && offsetof(MxbsStage, b) == offsetof(MxStage, b),
+                  "one copier layout for the codes");
     constexpr int FM = W::FM, FN = W::FN, STAGES = W::STAGES, L = W::LOADS_PER_WAVE;
-    __shared__ __align__(16) uint8_t lds_raw[STAGES * sizeof(MxStage)];
-    MxStage* ring = reinterpret_cast<MxStage*>(lds_raw);
+    constexpr uint32_t kZeroLine = STAGES * sizeof(Stage);
+    __shared__ __align__(16) uint8_t lds_raw[STAGES * sizeof(Stage) + (BS ? 64 : 0)];
+    Stage* ring = reinterpret_cast<Stage*>(lds_raw);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2156,7 +2202,7 @@ __device__ __forceinline__ void gemm_mx_body(const GemmArgs& args) {
     const Tile t = map_tile<W, MODE>(args, blockIdx.x);
     if (!t.live) return;
     const int64_t n0 = int64_t(t.bn) * W::BN;
-    const MxCopier cp = make_mx_copier<MODE>(args, t, wave, lane, n0);
+    const MxCopier cp = make_mx_copier<MODE, BS>(args, t, wave, lane, n0);
     const int64_t wrow0 = t.m0 + wm * FM * 32;
     const bool live = wrow0 < t.rows_valid;
     const int r = lane & 31, h = lane >> 5;
@@ -2167,21 +2213,27 @@ __device__ __forceinline__ void gemm_mx_body(const GemmArgs& args) {
         const int row = wm * FM * 32 + mi * 32 + r;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-            oa[mi][c] = uint32_t(offsetof(MxStage, a)) + uint32_t(row * W::KS + (((2 * c + h) ^ ((row >> 2) & 3)) << 4));
-        osa[mi] = uint32_t(offsetof(MxStage, sa)) + uint32_t(h * W::BM + row);
+            oa[mi][c] = uint32_t(offsetof(Stage, a)) + uint32_t(row * W::KS + (((2 * c + h) ^ ((row >> 2) & 3)) << 4));
+        osa[mi] = BS ? uint32_t(offsetof(MxbsStage, sa)) + uint32_t(row * 4)
+                     : uint32_t(offsetof(MxStage, sa)) + uint32_t(h * W::BM + row);
     }
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) {
         const int row = wn * FN * 32 + ni * 32 + r;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-            ob[ni][c] = uint32_t(offsetof(MxStage, b)) + uint32_t(row * W::KS + (((2 * c + h) ^ ((row >> 2) & 3)) << 4));
-        osb[ni] = uint32_t(offsetof(MxStage, sb)) + uint32_t(h * W::BN + row);
+            ob[ni][c] = uint32_t(offsetof(Stage, b)) + uint32_t(row * W::KS + (((2 * c + h) ^ ((row >> 2) & 3)) << 4));
+        osb[ni] = BS ? 0u : uint32_t(offsetof(MxStage, sb)) + uint32_t(h * W::BN + row);
+    }
+    if constexpr (BS) {   // the zero line, written before the first barrier
+        if (tid < 4) st<u32x4>(lds_raw + kZeroLine + tid * 16, u32x4{0u, 0u, 0u, 0u});
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
-        cp.copy(reinterpret_cast<uint8_t*>(&ring[st]), st < stages ? st : stages - 1);
+        cp.template copy<BS>(reinterpret_cast<uint8_t*>(&ring[st]), st < stages ? st : stages - 1);
+    WideScales<FM> w;   // BS: the current K-block's exponent parts and unit
 
     v16f acc[FM][FN];
 #pragma unroll
@@ -2196,22 +2248,45 @@ __device__ __forceinline__ void gemm_mx_body(const GemmArgs& args) {
         wait_vmcnt<(STAGES - 2) * L>();   // this wave's copy of stage cur has landed
         __builtin_amdgcn_s_barrier();     // ... every wave's; the slot of cur - 1 is free
         const int fill = cur + STAGES - 1;
-        cp.copy(reinterpret_cast<uint8_t*>(&ring[fill_slot]), fill < stages ? fill : stages - 1);
+        cp.template copy<BS>(reinterpret_cast<uint8_t*>(&ring[fill_slot]), fill < stages ? fill : stages - 1);
         if (live) {
-            const uint8_t* sg = lds_raw + uint32_t(slot) * uint32_t(sizeof(MxStage));
+            const uint8_t* sg = lds_raw + uint32_t(slot) * uint32_t(sizeof(Stage));
             v8i a8[FM], b8[FN];
             int ea[FM], eb[FN];
+            if constexpr (BS) {
+                if ((cur & 1) == 0) {   // a new K-block: its scales came with this stage
+                    WideScales<FM> nw;
+                    const float sb = ld<float>(sg + offsetof(MxbsStage, sb) + wn * 4);
+                    const ScaleSplit b = split_scale(sb);
+                    nw.pb = b.pow2;
+#pragma unroll
+                    for (int mi = 0; mi < FM; ++mi) {
+                        const float sa = ld<float>(sg + osa[mi]);
+                        const ScaleSplit a = split_scale(sa);
+                        nw.pa[mi] = a.pow2;
+                        nw.unit[mi] = clamp_unit(a.mant * b.mant);
+                        nw.zero[mi] = (sa == 0.0f || sb == 0.0f) ? 1 : 0;
+                    }
+                    if (cur > 0) rescale<FM, FN, FM>(acc, w, nw);
+                    w = nw;
+                }
+            }
 #pragma unroll
             for (int mi = 0; mi < FM; ++mi) {
-                const u32x4 lo = ld<u32x4>(sg + oa[mi][0]), hi = ld<u32x4>(sg + oa[mi][1]);
+                uint32_t o0 = oa[mi][0], o1 = oa[mi][1];
+                if (BS && w.zero[mi]) {   // the chunk offsets within the zero line
+                    o0 = kZeroLine - uint32_t(slot) * uint32_t(sizeof(Stage)) + (o0 & 63u);
+                    o1 = kZeroLine - uint32_t(slot) * uint32_t(sizeof(Stage)) + (o1 & 63u);
+                }
+                const u32x4 lo = ld<u32x4>(sg + o0), hi = ld<u32x4>(sg + o1);
                 a8[mi] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
-                ea[mi] = sg[osa[mi]];
+                ea[mi] = BS ? int((__builtin_bit_cast(uint32_t, w.pa[mi]) >> 23) & 0xFF) : int(sg[osa[mi]]);
             }
 #pragma unroll
             for (int ni = 0; ni < FN; ++ni) {
                 const u32x4 lo = ld<u32x4>(sg + ob[ni][0]), hi = ld<u32x4>(sg + ob[ni][1]);
                 b8[ni] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
-                eb[ni] = sg[osb[ni]];
+                eb[ni] = BS ? int((__builtin_bit_cast(uint32_t, w.pb) >> 23) & 0xFF) : int(sg[osb[ni]]);
             }
 #pragma unroll
             for (int mi = 0; mi < FM; ++mi)
@@ -2237,8 +2312,9 @@ __device__ __forceinline__ void gemm_mx_body(const GemmArgs& args) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t idx = t.c_base + m * N + n0 + n_lane + ni * 32 + 8 * j;
-                const v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
-                                  acc[mi][ni][4 * j + 3]};
+                v4f v = v4f{acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2],
+                            acc[mi][ni][4 * j + 3]};
+                if (BS) v = v * w.unit[mi];
                 if (OUT_FP32) {
                     if (m < t.rows_valid) st<v4f>(static_cast<float*>(args.c) + idx, v);
                 } else {
@@ -2263,6 +2339,13 @@ FP8FG_MX_KERNEL(1, contig, Contig)
 FP8FG_MX_KERNEL(0, masked, Masked)
 FP8FG_MX_KERNEL(1, masked, Masked)
 #undef FP8FG_MX_KERNEL
+// the FP8-MFMA engine on 128x128-scaled B in this tiling (dense)
+__global__ __launch_bounds__(MxTile::THREADS) void gemm_mxbs_o0_dense(GemmArgs args) {
+    gemm_mx_body<0, int(GemmMode::Dense), true>(args);
+}
+__global__ __launch_bounds__(MxTile::THREADS) void gemm_mxbs_o1_dense(GemmArgs args) {
+    gemm_mx_body<1, int(GemmMode::Dense), true>(args);
+}
 
 // One plain __global__ function per instantiation (kernel templates whose
 // instantiations differ only in the tile shape lost their host stubs).
@@ -3009,8 +3092,24 @@ hipError_t launch_dreg(int out_fp32, bool mx, const GemmArgs& args, hipStream_t 
     return launch_kernel(k, dim3(unsigned(P)), dim3(unsigned(64 * nw)), stream, args);
 }
 
+// The FP8-MFMA engine on the MX kernel's tiling: dense, 128x128-scaled B,
+// N % 256 == 0, K % 64 == 0, and byte ranges that fit the buffer descriptors
+bool mxbs_fits(const GemmArgs& args) {
+    const int64_t kbs = (args.K + 127) / 128;
+    return args.N % MxTile::BN == 0 && args.K % MxTile::KS == 0 && args.K > 0 && args.K < (int64_t(1) << 24) &&
+           kbs * args.M * 4 <= int64_t(0xFFFFFFFF) && (args.N / 128) * kbs * 4 <= int64_t(0xFFFFFFFF);
+}
+
 hipError_t dispatch(int engine, GemmMode mode, int bscale_1x128, int out_fp32, const GemmArgs& args,
                     hipStream_t stream) {
+    if (engine == 1 && mode == GemmMode::Dense && !bscale_1x128 && out_fp32 != 2 && mxbs_fits(args)) {
+        const int64_t tiles = ((args.M + MxTile::BM - 1) / MxTile::BM) * (args.N / MxTile::BN);
+        if (tiles == 0) return hipSuccess;
+        GemmArgs a = args;
+        a.xcds = kXcds;
+        return launch_kernel(out_fp32 ? gemm_mxbs_o1_dense : gemm_mxbs_o0_dense, dim3(unsigned(tiles)),
+                             dim3(MxTile::THREADS), stream, a);
+    }
     // The exact engine on 128x128-scaled B with N a multiple of 256 runs the
     // wide kernel: 64 x 256 tiles for decode-sized masked buffers (at most
     // 128 rows), 256 x 256 tiles otherwise.  The rest (1x128 B scales, the
