@@ -57,12 +57,13 @@ def parse():
                    help="seconds of untimed steps before the warmup steps (clock settling)")
     p.add_argument("--profile-kernel", choices=["gemm", "quant_act", "quant_weight", "quant_fprop", "copy", "masked",
                                                 "masked_tiled", "masked_down", "masked_down_tiled", "trio_fprop",
-                                                "trio_dgrad", "trio_wgrad", "contig", "mx"],
+                                                "trio_dgrad", "trio_wgrad", "contig", "mx", "fp8mfma"],
                    help="counter-collection driver: launch only this kernel `steps` times (gemm, quant_*: on "
                         "the dense_fprop inputs; copy: a 1 GiB device-to-device copy, the byte-counter "
                         "calibration; masked*: the masked decode GEMM, gate+up or down shape, on plain / "
                         "decode-tiled weights; trio_*: the linear_trio GEMMs; contig: the moe_contig "
-                        "gate+up GEMM; mx: the MX GEMM on the dense_fprop shape); prints no JSON")
+                        "gate+up GEMM; mx: the MX GEMM on the dense_fprop shape; fp8mfma: the FP8-MFMA engine on "
+                        "the dense_fprop inputs); prints no JSON")
     p.add_argument("--workload", default="dense_fprop",
                    choices=["dense_fprop", "dense_small", "linear_trio", "moe_contig", "moe_masked", "dense_mx"],
                    help="dense_fprop is the headline step; the others print one line per measured kernel")
@@ -710,6 +711,9 @@ def main():
             if args.profile_kernel == "gemm":
                 fp8.fp8_gemm_blockscaled(s["qa"], s["sa"], s["qb"], s["sb"], fp8.BSCALE_128x128, torch.bfloat16,
                                          out=s["c"])
+            elif args.profile_kernel == "fp8mfma":
+                fp8.fp8_gemm_blockscaled_fp8mfma(s["qa"], s["sa"], s["qb"], s["sb"], fp8.BSCALE_128x128,
+                                                 torch.bfloat16, out=s["c"])
             elif args.profile_kernel == "quant_act":
                 fp8.fp8_quant_act_1x128(s["x"], q=s["qa"], s=s["sa"])
             elif args.profile_kernel == "quant_weight":
